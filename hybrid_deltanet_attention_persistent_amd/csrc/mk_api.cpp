@@ -1,0 +1,602 @@
+// mk_api.cpp -- host side of the C ABI declared in include/mk.h: validation, arena
+// layout, weight re-tiling, state reset and the persistent-kernel launches.
+//
+// Validation of a call (config, tensors, sizes, context length, call order) is
+// finished before the first HIP call of that call, so every rejection is
+// side-effect free and can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "mk.h"
+#include "mk_layout.h"
+
+extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, hipStream_t stream);
+extern "C" hipError_t mk_forward_occupancy(int ncol_template, int *blocks_per_cu);
+
+static thread_local std::string g_err;
+
+static int fail(int code, const std::string &msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIPCHECK(expr)                                                                        \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) return fail(MK_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+static const uint32_t MK_MAGIC = 0x6d6b4d44u;
+
+struct mk_model {
+  uint32_t magic;
+  int device;
+  mk_config cfg;
+  std::vector<uint8_t> kinds;
+  MkDev dev;
+  char *arena;
+  size_t arena_bytes;
+  // regions cleared by mk_reset_state
+  std::vector<std::pair<size_t, size_t>> state_regions;
+  int32_t pos_hi;  // upper bound of the device position (exact unless a verify ran)
+  uint32_t tag;    // next exchange tag
+};
+
+// ------------------------------------------------------------------------------ layout
+namespace {
+
+struct Region {
+  size_t off = 0, bytes = 0;
+};
+
+struct Layout {
+  size_t total = 0;
+  Region add(size_t bytes) {
+    Region r;
+    r.off = (total + 255) & ~size_t(255);
+    r.bytes = bytes;
+    total = r.off + bytes;
+    return r;
+  }
+};
+
+struct LayerRegions {
+  Region ln1, ln2;
+  Region dn_in, dn_conv, dn_gnorm, dn_out, S, ring, pend;
+  Region at_q, at_k, at_v, at_o, kc, vc;
+  Region ffn_gu, ffn_dn;
+  Region x_in, x_o, x_mix, x_r1, x_m, x_ffn, x_r2;
+};
+
+struct Plan {
+  int H, V, I, J, nh, dk, dv, C, r_in, nq, nkv, hd, r_in_max, x_o_len, max_pages;
+  Region embed, lnf, rope, page_table, layer_table, ctl, x_arg;
+  std::vector<LayerRegions> layers;
+  size_t total;
+};
+
+int check_config(const mk_config *c, std::string &why) {
+  if (!c) { why = "config is NULL"; return MK_EINVAL; }
+  if (c->n_layers <= 0 || c->n_layers > 256) { why = "n_layers out of range"; return MK_EINVAL; }
+  if (!c->layer_kind) { why = "layer_kind is NULL"; return MK_EINVAL; }
+  int nd = 0, na = 0;
+  for (int i = 0; i < c->n_layers; ++i) {
+    if (c->layer_kind[i] == MK_LAYER_DELTANET) ++nd;
+    else if (c->layer_kind[i] == MK_LAYER_ATTENTION) ++na;
+    else { why = "layer_kind[" + std::to_string(i) + "] is neither DeltaNet nor attention"; return MK_EINVAL; }
+  }
+  if (!(c->hidden == 256 || c->hidden == 512 || c->hidden == 1024)) { why = "hidden must be 256, 512 or 1024"; return MK_EINVAL; }
+  if (c->vocab <= 0 || c->vocab % 2 != 0) { why = "vocab must be positive and even"; return MK_EINVAL; }
+  if (c->ffn <= 0 || c->ffn % 64 != 0) { why = "ffn must be a positive multiple of 64"; return MK_EINVAL; }
+  {
+    const int J = c->ffn / MK_NX;
+    const int G = mk_tile_G(J);
+    if (J / 8 / G > 8) { why = "ffn / 8 has too few power-of-two factors for the down-projection tiles"; return MK_EINVAL; }
+  }
+  if (nd > 0) {
+    if (c->dn_heads < 1 || c->dn_heads > MK_NX) { why = "dn_heads must be in [1, 8]"; return MK_EINVAL; }
+    if (!(c->dn_dk == 64 || c->dn_dk == 128) || c->dn_dv != c->dn_dk) { why = "dn_dk == dn_dv in {64, 128} required"; return MK_EINVAL; }
+    if (c->conv_k != 4) { why = "conv_k must be 4"; return MK_EINVAL; }
+  }
+  if (na > 0) {
+    if (c->at_q_heads < 1 || c->at_q_heads > MK_NX) { why = "at_q_heads must be in [1, 8]"; return MK_EINVAL; }
+    if (c->at_kv_heads < 1 || c->at_q_heads % c->at_kv_heads != 0) { why = "at_q_heads must be a multiple of at_kv_heads"; return MK_EINVAL; }
+    if (!(c->at_head_dim == 64 || c->at_head_dim == 128)) { why = "at_head_dim must be 64 or 128"; return MK_EINVAL; }
+    if (!(c->rope_theta > 0.f)) { why = "rope_theta must be positive"; return MK_EINVAL; }
+  }
+  if (!(c->rms_eps >= 0.f) || !(c->l2_eps >= 0.f)) { why = "eps must be >= 0"; return MK_EINVAL; }
+  if (c->tied_embedding != 1) { why = "only a tied LM head is supported"; return MK_EINVAL; }
+  if (c->max_ctx <= 0 || c->max_ctx % MK_PAGE != 0 || c->max_ctx > 10240) { why = "max_ctx must be a multiple of 64 in [64, 10240]"; return MK_EINVAL; }
+  if (c->prefill_chunk != 64) { why = "prefill_chunk must be 64"; return MK_EINVAL; }
+  if (c->max_verify < 1 || c->max_verify > MK_MAXCOL) { why = "max_verify must be in [1, 5]"; return MK_EINVAL; }
+  return MK_OK;
+}
+
+Plan make_plan(const mk_config *c) {
+  Plan p;
+  p.H = c->hidden; p.V = c->vocab; p.I = c->ffn; p.J = c->ffn / MK_NX;
+  p.nh = c->dn_heads; p.dk = c->dn_dk; p.dv = c->dn_dv;
+  p.C = 2 * c->dn_heads * c->dn_dk + c->dn_heads * c->dn_dv;
+  p.r_in = 2 * p.dk + 2 * p.dv + 2;
+  p.nq = c->at_q_heads; p.nkv = c->at_kv_heads; p.hd = c->at_head_dim;
+  bool has_dn = false, has_at = false;
+  for (int i = 0; i < c->n_layers; ++i) (c->layer_kind[i] == MK_LAYER_DELTANET ? has_dn : has_at) = true;
+  p.r_in_max = std::max(has_dn ? p.r_in : 0, has_at ? 3 * p.hd : 0);
+  p.r_in_max = (p.r_in_max + 31) & ~31;  // 256-byte aligned per-column blocks: no cache line is shared
+
+  p.x_o_len = std::max(has_dn ? p.dv : 0, has_at ? MK_NL * (p.hd + 2) : 0);
+  p.x_o_len = (p.x_o_len + 31) & ~31;
+  p.max_pages = c->max_ctx / MK_PAGE;
+  const size_t H = p.H;
+  Layout L;
+  p.embed = L.add((size_t)p.V * H * 2);
+  p.lnf = L.add(H * 4);
+  p.rope = L.add(has_at ? (size_t)c->max_ctx * (p.hd / 2) * 2 * 4 : 0);
+  p.page_table = L.add((size_t)p.max_pages * 4);
+  p.layer_table = L.add(sizeof(MkLayerDev) * c->n_layers);
+  p.ctl = L.add(MK_CTL_WORDS * 4);
+  p.x_arg = L.add((size_t)MK_MAXCOL * MK_NWG * 16);
+  p.layers.resize(c->n_layers);
+  for (int i = 0; i < c->n_layers; ++i) {
+    LayerRegions &r = p.layers[i];
+    r.ln1 = L.add(H * 4);
+    r.ln2 = L.add(H * 4);
+    if (c->layer_kind[i] == MK_LAYER_DELTANET) {
+      r.dn_in = L.add((size_t)p.nh * p.r_in * H * 2);
+      r.dn_conv = L.add((size_t)p.C * 4 * 4);
+      r.dn_gnorm = L.add((size_t)p.dv * 4);
+      r.dn_out = L.add((size_t)p.nh * H * p.dv * 2);
+      r.S = L.add((size_t)p.nh * p.dv * p.dk * 4);
+      r.ring = L.add((size_t)MK_RING * p.C * 4);
+      r.pend = L.add((size_t)2 * p.nh * MK_MAXCOL * (p.dk + p.dv + 2) * 4);
+    } else {
+      r.at_q = L.add((size_t)p.nq * p.hd * H * 2);
+      r.at_k = L.add((size_t)p.nkv * p.hd * H * 2);
+      r.at_v = L.add((size_t)p.nkv * p.hd * H * 2);
+      r.at_o = L.add((size_t)p.nq * H * p.hd * 2);
+      r.kc = L.add((size_t)p.max_pages * p.nkv * MK_PAGE * p.hd * 2);
+      r.vc = L.add((size_t)p.max_pages * p.nkv * MK_PAGE * p.hd * 2);
+    }
+    r.ffn_gu = L.add((size_t)2 * p.I * H * 2);
+    r.ffn_dn = L.add((size_t)H * p.I * 2);
+  }
+  for (int i = 0; i < c->n_layers; ++i) {
+    LayerRegions &r = p.layers[i];
+    r.x_in = L.add((size_t)MK_NX * MK_MAXCOL * p.r_in_max * 8);
+    r.x_o = L.add((size_t)MK_NX * MK_MAXCOL * p.x_o_len * 8);
+    r.x_mix = L.add((size_t)MK_MAXCOL * MK_NX * H * 8);
+    r.x_r1 = L.add((size_t)MK_NX * MK_MAXCOL * H * 8);
+    r.x_m = L.add((size_t)MK_NX * MK_MAXCOL * p.J * 8);
+    r.x_ffn = L.add((size_t)MK_MAXCOL * MK_NX * H * 8);
+    r.x_r2 = L.add((size_t)MK_NX * MK_MAXCOL * H * 8);
+  }
+  p.total = (L.total + 255) & ~size_t(255);
+  return p;
+}
+
+struct Expect {
+  std::vector<int64_t> shape;
+  const mk_tensor *t = nullptr;
+};
+
+std::map<std::string, Expect> expected_tensors(const mk_config *c) {
+  std::map<std::string, Expect> e;
+  const int64_t H = c->hidden, V = c->vocab, I = c->ffn;
+  e["embed"].shape = {V, H};
+  e["lnf"].shape = {H};
+  for (int i = 0; i < c->n_layers; ++i) {
+    const std::string p = "layers." + std::to_string(i) + ".";
+    e[p + "ln1"].shape = {H};
+    e[p + "ln2"].shape = {H};
+    if (c->layer_kind[i] == MK_LAYER_DELTANET) {
+      const int64_t qk = (int64_t)c->dn_heads * c->dn_dk, vv = (int64_t)c->dn_heads * c->dn_dv;
+      e[p + "dn.wq"].shape = {qk, H};
+      e[p + "dn.wk"].shape = {qk, H};
+      e[p + "dn.wv"].shape = {vv, H};
+      e[p + "dn.wz"].shape = {vv, H};
+      e[p + "dn.wa"].shape = {c->dn_heads, H};
+      e[p + "dn.wb"].shape = {c->dn_heads, H};
+      e[p + "dn.conv"].shape = {2 * qk + vv, c->conv_k};
+      e[p + "dn.gnorm"].shape = {c->dn_dv};
+      e[p + "dn.wo"].shape = {H, vv};
+    } else {
+      const int64_t q = (int64_t)c->at_q_heads * c->at_head_dim, kv = (int64_t)c->at_kv_heads * c->at_head_dim;
+      e[p + "attn.wq"].shape = {q, H};
+      e[p + "attn.wk"].shape = {kv, H};
+      e[p + "attn.wv"].shape = {kv, H};
+      e[p + "attn.wo"].shape = {H, q};
+    }
+    e[p + "ffn.wg"].shape = {I, H};
+    e[p + "ffn.wu"].shape = {I, H};
+    e[p + "ffn.wd"].shape = {H, I};
+  }
+  return e;
+}
+
+// Re-tile rows [rows][K] (row stride src_stride elements) into the tile format of mk_layout.h.
+void tile_pack(const uint16_t *src, int rows, int K, size_t src_stride, uint16_t *dst) {
+  const int G = mk_tile_G(K), L = K / 8 / G, RG = 64 / G;
+  for (int rg = 0; rg < rows / RG; ++rg)
+    for (int i = 0; i < L; ++i)
+      for (int l = 0; l < 64; ++l) {
+        const int row = rg * RG + l / G, chunk = i * G + (l % G);
+        std::memcpy(dst + (((size_t)rg * L + i) * 64 + l) * 8, src + (size_t)row * src_stride + (size_t)chunk * 8, 16);
+      }
+}
+
+inline float bf2f(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------ ABI
+extern "C" const char *mk_status_string(int s) {
+  switch (s) {
+    case MK_OK: return "ok";
+    case MK_EINVAL: return "invalid argument";
+    case MK_EDTYPE: return "weight tensor is not BF16";
+    case MK_ESHAPE: return "weight tensor missing, duplicated, unknown or mis-shaped";
+    case MK_ECTX: return "context length exceeded";
+    case MK_ESTATE: return "model not loaded";
+    case MK_ELAUNCH: return "device cannot host the persistent grid";
+    case MK_EHIP: return "HIP runtime error";
+    case MK_EHANG: return "device wait timed out";
+    case MK_ETOKEN: return "token id out of range";
+    case MK_ENAN: return "non-finite logits";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char *mk_last_error(void) { return g_err.c_str(); }
+
+extern "C" int mk_required_bytes(const mk_config *cfg, size_t *arena_bytes) {
+  std::string why;
+  if (!arena_bytes) return fail(MK_EINVAL, "arena_bytes is NULL");
+  int s = check_config(cfg, why);
+  if (s != MK_OK) return fail(s, why);
+  *arena_bytes = make_plan(cfg).total;
+  return MK_OK;
+}
+
+static int validate_tensors(const mk_config *cfg, const mk_tensor *t, int32_t n,
+                            std::map<std::string, Expect> &exp) {
+  if (n < 0 || (n > 0 && !t)) return fail(MK_EINVAL, "tensor list is NULL or has a negative length");
+  for (int i = 0; i < n; ++i) {
+    if (!t[i].name) return fail(MK_EINVAL, "tensor " + std::to_string(i) + " has no name");
+    const std::string name = t[i].name;
+    auto it = exp.find(name);
+    if (it == exp.end()) return fail(MK_ESHAPE, "unknown tensor '" + name + "'");
+    if (t[i].dtype != MK_DTYPE_BF16) return fail(MK_EDTYPE, "tensor '" + name + "' is not BF16");
+    if (it->second.t) return fail(MK_ESHAPE, "tensor '" + name + "' given twice");
+    const auto &sh = it->second.shape;
+    bool ok = t[i].ndim == (int32_t)sh.size();
+    for (size_t d = 0; ok && d < sh.size(); ++d) ok = t[i].shape[d] == sh[d];
+    if (!ok) return fail(MK_ESHAPE, "tensor '" + name + "' has the wrong shape");
+    if (!t[i].data) return fail(MK_EINVAL, "tensor '" + name + "' has no data");
+    it->second.t = &t[i];
+  }
+  for (auto &kv : exp)
+    if (!kv.second.t) return fail(MK_ESHAPE, "tensor '" + kv.first + "' is missing");
+  (void)cfg;
+  return MK_OK;
+}
+
+static int check_device(int *dev) {
+  HIPCHECK(hipGetDevice(dev));
+  hipDeviceProp_t prop;
+  HIPCHECK(hipGetDeviceProperties(&prop, *dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MK_ELAUNCH, std::string("device is ") + prop.gcnArchName + ", need gfx950 (MI355X)");
+  if (prop.multiProcessorCount != MK_NWG)
+    return fail(MK_ELAUNCH, "device has " + std::to_string(prop.multiProcessorCount) + " CUs, need 256 (8 XCDs x 32)");
+  if (!prop.cooperativeLaunch) return fail(MK_ELAUNCH, "device has no cooperative launch");
+  for (int tmpl : {1, MK_MAXCOL}) {
+    int per_cu = 0;
+    HIPCHECK(mk_forward_occupancy(tmpl, &per_cu));
+    if (per_cu < 1) return fail(MK_ELAUNCH, "persistent kernel does not fit on a CU");
+  }
+  return MK_OK;
+}
+
+extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, int32_t n_tensors, void *d_arena,
+                               size_t arena_bytes, void *stream, mk_model **out) {
+  std::string why;
+  if (!out) return fail(MK_EINVAL, "out is NULL");
+  *out = nullptr;
+  int s = check_config(cfg, why);
+  if (s != MK_OK) return fail(s, why);
+  auto exp = expected_tensors(cfg);
+  s = validate_tensors(cfg, tensors, n_tensors, exp);
+  if (s != MK_OK) return s;
+  Plan p = make_plan(cfg);
+  if (!d_arena) return fail(MK_EINVAL, "arena is NULL");
+  if (((uintptr_t)d_arena & 255) != 0) return fail(MK_EINVAL, "arena is not 256-byte aligned");
+  if (arena_bytes < p.total) return fail(MK_EINVAL, "arena too small: need " + std::to_string(p.total) + " bytes");
+
+  int dev = 0;
+  s = check_device(&dev);
+  if (s != MK_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char *A = (char *)d_arena;
+  auto T = [&](const std::string &name) { return (const uint16_t *)exp[name].t->data; };
+  auto put = [&](const Region &r, const void *host) -> hipError_t {
+    hipError_t e = hipMemcpyAsync(A + r.off, host, r.bytes, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return e;
+    return hipStreamSynchronize(st);  // the staging buffer is reused right after
+  };
+  auto gains = [&](const uint16_t *src, size_t n) {
+    std::vector<float> g(n);
+    for (size_t i = 0; i < n; ++i) g[i] = bf2f(src[i]);
+    return g;
+  };
+  const size_t H = p.H;
+  std::vector<uint16_t> stage;
+  // embedding / LM head: tile format with one row group per G-lane segment == row-major for H <= 1024
+  HIPCHECK(put(p.embed, T("embed")));
+  { auto g = gains(T("lnf"), H); HIPCHECK(put(p.lnf, g.data())); }
+
+  MkDev d{};
+  d.n_layers = cfg->n_layers; d.H = p.H; d.V = p.V; d.I = p.I; d.J = p.J;
+  d.nh = p.nh; d.dk = p.dk; d.dv = p.dv; d.C = p.C; d.r_in = p.r_in;
+  d.nq = p.nq; d.nkv = p.nkv; d.hd = p.hd; d.r_in_max = p.r_in_max; d.x_o_len = p.x_o_len;
+  d.max_ctx = cfg->max_ctx; d.max_pages = p.max_pages;
+  d.rms_eps = cfg->rms_eps; d.l2_eps = cfg->l2_eps;
+  d.embed = (const uint16_t *)(A + p.embed.off);
+  d.lnf = (const float *)(A + p.lnf.off);
+  d.rope = (const float *)(A + p.rope.off);
+  d.page_table = (const int32_t *)(A + p.page_table.off);
+  d.layers = (const MkLayerDev *)(A + p.layer_table.off);
+  d.ctl = (int32_t *)(A + p.ctl.off);
+  d.x_arg = (uint4 *)(A + p.x_arg.off);
+
+  if (p.rope.bytes) {  // rotary table in double precision, stored as float
+    std::vector<float> rt((size_t)cfg->max_ctx * (p.hd / 2) * 2);
+    for (int pos = 0; pos < cfg->max_ctx; ++pos)
+      for (int i = 0; i < p.hd / 2; ++i) {
+        const double invf = std::pow((double)cfg->rope_theta, -2.0 * i / (double)p.hd);
+        const double ang = (double)pos * invf;
+        rt[((size_t)pos * (p.hd / 2) + i) * 2 + 0] = (float)std::cos(ang);
+        rt[((size_t)pos * (p.hd / 2) + i) * 2 + 1] = (float)std::sin(ang);
+      }
+    HIPCHECK(put(p.rope, rt.data()));
+  }
+  {
+    std::vector<int32_t> pt(p.max_pages);
+    for (int i = 0; i < p.max_pages; ++i) pt[i] = i;  // one sequence: identity page map
+    HIPCHECK(put(p.page_table, pt.data()));
+  }
+
+  std::vector<MkLayerDev> lt(cfg->n_layers);
+  std::vector<std::pair<size_t, size_t>> state;
+  int nd = 0, na = 0;
+  for (int li = 0; li < cfg->n_layers; ++li) {
+    const LayerRegions &r = p.layers[li];
+    MkLayerDev &L = lt[li];
+    std::memset(&L, 0, sizeof(L));
+    const std::string pre = "layers." + std::to_string(li) + ".";
+    L.kind = cfg->layer_kind[li] == MK_LAYER_DELTANET ? 0 : 1;
+    L.idx = L.kind == 0 ? nd++ : na++;
+    { auto g = gains(T(pre + "ln1"), H); HIPCHECK(put(r.ln1, g.data())); }
+    { auto g = gains(T(pre + "ln2"), H); HIPCHECK(put(r.ln2, g.data())); }
+    L.ln1 = (const float *)(A + r.ln1.off);
+    L.ln2 = (const float *)(A + r.ln2.off);
+    if (L.kind == 0) {
+      const int nh = p.nh, dk = p.dk, dv = p.dv;
+      stage.assign(r.dn_in.bytes / 2, 0);
+      std::vector<uint16_t> rows((size_t)p.r_in * H);
+      for (int h = 0; h < nh; ++h) {
+        size_t o = 0;
+        auto take = [&](const uint16_t *src, int r0, int nr) {
+          std::memcpy(rows.data() + o * H, src + (size_t)r0 * H, (size_t)nr * H * 2);
+          o += nr;
+        };
+        take(T(pre + "dn.wq"), h * dk, dk);
+        take(T(pre + "dn.wk"), h * dk, dk);
+        take(T(pre + "dn.wv"), h * dv, dv);
+        take(T(pre + "dn.wz"), h * dv, dv);
+        take(T(pre + "dn.wa"), h, 1);
+        take(T(pre + "dn.wb"), h, 1);
+        tile_pack(rows.data(), p.r_in, p.H, H, stage.data() + (size_t)h * p.r_in * H);
+      }
+      HIPCHECK(put(r.dn_in, stage.data()));
+      { auto g = gains(T(pre + "dn.conv"), (size_t)p.C * 4); HIPCHECK(put(r.dn_conv, g.data())); }
+      { auto g = gains(T(pre + "dn.gnorm"), dv); HIPCHECK(put(r.dn_gnorm, g.data())); }
+      stage.assign(r.dn_out.bytes / 2, 0);
+      for (int h = 0; h < nh; ++h)
+        tile_pack(T(pre + "dn.wo") + (size_t)h * dv, p.H, dv, (size_t)nh * dv, stage.data() + (size_t)h * H * dv);
+      HIPCHECK(put(r.dn_out, stage.data()));
+      L.dn_in = (const uint16_t *)(A + r.dn_in.off);
+      L.dn_conv = (const float *)(A + r.dn_conv.off);
+      L.dn_gnorm = (const float *)(A + r.dn_gnorm.off);
+      L.dn_out = (const uint16_t *)(A + r.dn_out.off);
+      L.S = (float *)(A + r.S.off);
+      L.ring = (float *)(A + r.ring.off);
+      L.pend = (float *)(A + r.pend.off);
+      state.push_back({r.S.off, r.S.bytes});
+      state.push_back({r.ring.off, r.ring.bytes});
+      state.push_back({r.pend.off, r.pend.bytes});
+    } else {
+      const int nq = p.nq, nkv = p.nkv, hd = p.hd;
+      stage.assign(r.at_q.bytes / 2, 0);
+      for (int i = 0; i < nq; ++i) tile_pack(T(pre + "attn.wq") + (size_t)i * hd * H, hd, p.H, H, stage.data() + (size_t)i * hd * H);
+      HIPCHECK(put(r.at_q, stage.data()));
+      stage.assign(r.at_k.bytes / 2, 0);
+      for (int i = 0; i < nkv; ++i) tile_pack(T(pre + "attn.wk") + (size_t)i * hd * H, hd, p.H, H, stage.data() + (size_t)i * hd * H);
+      HIPCHECK(put(r.at_k, stage.data()));
+      stage.assign(r.at_v.bytes / 2, 0);
+      for (int i = 0; i < nkv; ++i) tile_pack(T(pre + "attn.wv") + (size_t)i * hd * H, hd, p.H, H, stage.data() + (size_t)i * hd * H);
+      HIPCHECK(put(r.at_v, stage.data()));
+      stage.assign(r.at_o.bytes / 2, 0);
+      for (int i = 0; i < nq; ++i) tile_pack(T(pre + "attn.wo") + (size_t)i * hd, p.H, hd, (size_t)nq * hd, stage.data() + (size_t)i * H * hd);
+      HIPCHECK(put(r.at_o, stage.data()));
+      L.at_q = (const uint16_t *)(A + r.at_q.off);
+      L.at_k = (const uint16_t *)(A + r.at_k.off);
+      L.at_v = (const uint16_t *)(A + r.at_v.off);
+      L.at_o = (const uint16_t *)(A + r.at_o.off);
+      L.kc = (uint16_t *)(A + r.kc.off);
+      L.vc = (uint16_t *)(A + r.vc.off);
+    }
+    {
+      const int J = p.J;
+      stage.assign(r.ffn_gu.bytes / 2, 0);
+      std::vector<uint16_t> rows((size_t)2 * J * H);
+      for (int xg = 0; xg < MK_NX; ++xg) {
+        for (int j = 0; j < J; ++j) {
+          std::memcpy(rows.data() + (size_t)(2 * j) * H, T(pre + "ffn.wg") + (size_t)(xg * J + j) * H, H * 2);
+          std::memcpy(rows.data() + (size_t)(2 * j + 1) * H, T(pre + "ffn.wu") + (size_t)(xg * J + j) * H, H * 2);
+        }
+        tile_pack(rows.data(), 2 * J, p.H, H, stage.data() + (size_t)xg * 2 * J * H);
+      }
+      HIPCHECK(put(r.ffn_gu, stage.data()));
+      stage.assign(r.ffn_dn.bytes / 2, 0);
+      for (int xg = 0; xg < MK_NX; ++xg)
+        tile_pack(T(pre + "ffn.wd") + (size_t)xg * J, p.H, J, (size_t)p.I, stage.data() + (size_t)xg * H * J);
+      HIPCHECK(put(r.ffn_dn, stage.data()));
+      L.ffn_gu = (const uint16_t *)(A + r.ffn_gu.off);
+      L.ffn_dn = (const uint16_t *)(A + r.ffn_dn.off);
+    }
+    L.x_in = (uint2 *)(A + r.x_in.off);
+    L.x_o = (uint2 *)(A + r.x_o.off);
+    L.x_mix = (uint2 *)(A + r.x_mix.off);
+    L.x_r1 = (uint2 *)(A + r.x_r1.off);
+    L.x_m = (uint2 *)(A + r.x_m.off);
+    L.x_ffn = (uint2 *)(A + r.x_ffn.off);
+    L.x_r2 = (uint2 *)(A + r.x_r2.off);
+  }
+  HIPCHECK(put(p.layer_table, lt.data()));
+  // exchange slots start with tag 0 (never used); control words and state start at zero
+  HIPCHECK(hipMemsetAsync(A + p.x_arg.off, 0, p.x_arg.bytes, st));
+  {
+    const size_t x0 = p.layers[0].x_in.off;
+    HIPCHECK(hipMemsetAsync(A + x0, 0, p.total - x0, st));
+  }
+  state.push_back({p.ctl.off, p.ctl.bytes});
+  for (auto &r : state) HIPCHECK(hipMemsetAsync(A + r.first, 0, r.second, st));
+  HIPCHECK(hipStreamSynchronize(st));
+
+  mk_model *mm = new mk_model();
+  mm->magic = MK_MAGIC;
+  mm->device = dev;
+  mm->cfg = *cfg;
+  mm->kinds.assign(cfg->layer_kind, cfg->layer_kind + cfg->n_layers);
+  mm->cfg.layer_kind = mm->kinds.data();
+  mm->dev = d;
+  mm->arena = A;
+  mm->arena_bytes = arena_bytes;
+  mm->state_regions = state;
+  mm->pos_hi = 0;
+  mm->tag = 1;
+  *out = mm;
+  return MK_OK;
+}
+
+static bool live(const mk_model *m) { return m && m->magic == MK_MAGIC; }
+
+extern "C" int mk_reset_state(mk_model *m, void *stream) {
+  if (!live(m)) return fail(MK_ESTATE, "model not loaded");
+  hipStream_t st = (hipStream_t)stream;
+  for (auto &r : m->state_regions) HIPCHECK(hipMemsetAsync(m->arena + r.first, 0, r.second, st));
+  m->pos_hi = 0;
+  return MK_OK;
+}
+
+static int sync_pos(mk_model *m, hipStream_t st, int32_t *ctl_out) {
+  int32_t ctl[MK_CTL_WORDS];
+  HIPCHECK(hipStreamSynchronize(st));
+  HIPCHECK(hipMemcpy(ctl, m->dev.ctl, sizeof(ctl), hipMemcpyDeviceToHost));
+  m->pos_hi = ctl[MK_CTL_POS];
+  if (ctl_out) std::memcpy(ctl_out, ctl, sizeof(ctl));
+  return MK_OK;
+}
+
+static int ensure_ctx(mk_model *m, int32_t n, hipStream_t st) {
+  if ((int64_t)m->pos_hi + n <= m->cfg.max_ctx) return MK_OK;
+  int s = sync_pos(m, st, nullptr);  // the bound is loose after a verify: read the real position
+  if (s != MK_OK) return s;
+  if ((int64_t)m->pos_hi + n > m->cfg.max_ctx)
+    return fail(MK_ECTX, "position " + std::to_string(m->pos_hi) + " + " + std::to_string(n) + " tokens exceeds max_ctx");
+  return MK_OK;
+}
+
+extern "C" int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_next_token,
+                          float *d_last_logits, void *stream) {
+  if (!live(m)) return fail(MK_ESTATE, "model not loaded");
+  if (!d_tokens || !d_next_token) return fail(MK_EINVAL, "token buffers must not be NULL");
+  if (n_tokens < 1 || n_tokens > m->cfg.max_ctx) return fail(MK_EINVAL, "n_tokens out of range");
+  hipStream_t st = (hipStream_t)stream;
+  int s = ensure_ctx(m, n_tokens, st);
+  if (s != MK_OK) return s;
+  MkLaunch a;
+  a.m = m->dev;
+  a.tokens = d_tokens;
+  a.n = n_tokens;
+  a.prefill = 1;
+  a.tag0 = m->tag;
+  a.argmax = d_next_token;
+  a.logits = d_last_logits;
+  a.n_acc = nullptr;
+  HIPCHECK(mk_launch_forward(&a, 1, st));
+  m->tag += (uint32_t)n_tokens;
+  m->pos_hi += n_tokens;
+  return MK_OK;
+}
+
+extern "C" int mk_decode_step(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_argmax,
+                              float *d_logits, int32_t *d_n_accepted, void *stream) {
+  if (!live(m)) return fail(MK_ESTATE, "model not loaded");
+  if (!d_tokens || !d_argmax) return fail(MK_EINVAL, "token buffers must not be NULL");
+  if (n_tokens < 1 || n_tokens > m->cfg.max_verify) return fail(MK_EINVAL, "n_tokens must be in [1, max_verify]");
+  hipStream_t st = (hipStream_t)stream;
+  int s = ensure_ctx(m, n_tokens, st);
+  if (s != MK_OK) return s;
+  MkLaunch a;
+  a.m = m->dev;
+  a.tokens = d_tokens;
+  a.n = n_tokens;
+  a.prefill = 0;
+  a.tag0 = m->tag;
+  a.argmax = d_argmax;
+  a.logits = d_logits;
+  a.n_acc = d_n_accepted;
+  HIPCHECK(mk_launch_forward(&a, n_tokens == 1 ? 1 : MK_MAXCOL, st));
+  m->tag += 1;
+  m->pos_hi += n_tokens;
+  return MK_OK;
+}
+
+extern "C" int mk_sync_status(mk_model *m, void *stream, int32_t *pos) {
+  if (!live(m)) return fail(MK_ESTATE, "model not loaded");
+  int32_t ctl[MK_CTL_WORDS];
+  int s = sync_pos(m, (hipStream_t)stream, ctl);
+  if (s != MK_OK) return s;
+  if (pos) *pos = ctl[MK_CTL_POS];
+  const int e = ctl[MK_CTL_ERR];
+  if (e & MK_DERR_XCD) return fail(MK_ELAUNCH, "workgroups were not placed round-robin over the XCDs");
+  if (e & MK_DERR_HANG) {
+    char buf[160];
+    std::snprintf(buf, sizeof(buf), "a device-side wait timed out (step %d layer %d phase %d, block %d thread %d, tag seen %u wanted %u)",
+                  (ctl[MK_CTL_WHERE] >> 16) & 16383, (ctl[MK_CTL_WHERE] >> 8) & 255, ctl[MK_CTL_WHERE] & 255,
+                  ctl[MK_CTL_WHERE + 1] >> 16, ctl[MK_CTL_WHERE + 1] & 65535, (unsigned)ctl[MK_CTL_WHERE + 2],
+                  (unsigned)ctl[MK_CTL_WHERE + 3]);
+    return fail(MK_EHANG, buf);
+  }
+  if (e & MK_DERR_TOKEN) return fail(MK_ETOKEN, "a token id was out of range");
+  if (e & MK_DERR_NAN) return fail(MK_ENAN, "non-finite logits");
+  return MK_OK;
+}
+
+extern "C" void mk_free(mk_model *m) {
+  if (!live(m)) return;
+  m->magic = 0;
+  delete m;
+}
