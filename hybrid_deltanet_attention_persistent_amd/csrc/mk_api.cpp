@@ -130,6 +130,7 @@ Plan make_plan(const mk_config *c) {
   p.r_in_max = std::max(has_dn ? p.r_in : 0, has_at ? 3 * p.hd : 0);
   p.r_in_max = (p.r_in_max + 31) & ~31;  // 256-byte aligned per-column blocks: no cache line is shared
 
+  // attention: 32 partials {max, sum, acc[hd]}
   p.x_o_len = std::max(has_dn ? p.dv : 0, has_at ? MK_NL * (p.hd + 2) : 0);
   p.x_o_len = (p.x_o_len + 31) & ~31;
   p.max_pages = c->max_ctx / MK_PAGE;

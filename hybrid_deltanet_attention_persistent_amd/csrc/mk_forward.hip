@@ -198,10 +198,9 @@ __device__ __forceinline__ void rg_dot(const u32x4 (&w)[LMAX], int L, int G, con
   for (int c = 0; c < NCOL; ++c) out[c] = group_sum(out[c], G);
 }
 
-// RMSNorm of src[c][H] into dst[c][H] with gain g; optionally rounded to bf16.
+// RMSNorm of src[c][H] into dst[c][H] with gain g.
 template <int NCOL>
-__device__ void rmsnorm_cols(const float *src, float *dst, const float *g, int H, float eps, int n, bool round,
-                             float *red) {
+__device__ void rmsnorm_cols(const float *src, float *dst, const float *g, int H, float eps, int n, float *red) {
   for (int c = 0; c < NCOL; ++c) {
     if (c >= n) break;
     float s = 0.f;
@@ -209,8 +208,7 @@ __device__ void rmsnorm_cols(const float *src, float *dst, const float *g, int H
     const float tot = block_sum(s, red);
     const float den = sqrtf(tot / (float)H + eps);
     for (int k = threadIdx.x; k < H; k += MK_THREADS) {
-      float v = src[c * H + k] / den * g[k];
-      dst[c * H + k] = round ? rbf(v) : v;
+      dst[c * H + k] = src[c * H + k] / den * g[k];
     }
   }
   __syncthreads();
@@ -264,7 +262,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   const bool verify = !a.prefill && a.n > 1;
   const int nsteps = a.prefill ? a.n : 1;
   const int ncol = a.prefill ? 1 : a.n;
-  const bool rmm = a.prefill != 0;
+  // prompts written in this launch are read back by other XCDs in later steps of it
+  const bool kv_live = a.prefill != 0;
   const int G_h = mk_tile_G(H), L_h = H / 8 / G_h, RG_h = 64 / G_h;
   const int SL = H / MK_NL;  // residual slice per workgroup in the reductions
 
@@ -292,7 +291,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       ConstLayer &ly = ((ConstLayer *)(uintptr_t)m.layers)[li];
       const uint32_t tg = tag;
       // ================================================================ mixer
-      rmsnorm_cols<NCOL>(L.xres, L.hn, ly.ln1, H, m.rms_eps, ncol, rmm, L.red);
+      rmsnorm_cols<NCOL>(L.xres, L.hn, ly.ln1, H, m.rms_eps, ncol, L.red);
       if (ly.kind == 0) {
         // ------------------------------------------------ D1: in-projection rows of head x
         const int nh = m.nh, dk = m.dk, dv = m.dv, r_in = m.r_in;
@@ -473,8 +472,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               for (int i = tid; i < dv; i += MK_THREADS) sq = fmaf(o[c * dv + i], o[c * dv + i], sq);
               const float den = sqrtf(block_sum(sq, L.red) / (float)dv + m.rms_eps);
               for (int i = tid; i < dv; i += MK_THREADS) {
-                float y = o[c * dv + i] / den * ly.dn_gnorm[i] * siluf_(z[c * dv + i]);
-                o[c * dv + i] = rmm ? rbf(y) : y;
+                o[c * dv + i] = o[c * dv + i] / den * ly.dn_gnorm[i] * siluf_(z[c * dv + i]);
               }
             }
             __syncthreads();
@@ -532,9 +530,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               const float sn = m.rope[((size_t)(pos0 + c) * half + d) * 2 + 1];
               float *q = qkv + c * 3 * hd, *k = q + hd, *v = k + hd;
               const float q1 = q[d], q2 = q[d + half], k1 = k[d], k2 = k[d + half];
-              float qa = q1 * cs - q2 * sn, qb = q2 * cs + q1 * sn;
-              if (rmm) { qa = rbf(qa); qb = rbf(qb); }
-              q[d] = qa; q[d + half] = qb;
+              q[d] = q1 * cs - q2 * sn;
+              q[d + half] = q2 * cs + q1 * sn;
               k[d] = rbf(k1 * cs - k2 * sn); k[d + half] = rbf(k2 * cs + k1 * sn);
               v[d] = rbf(v[d]); v[d + half] = rbf(v[d + half]);
             }
@@ -557,13 +554,13 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           {
             float *sc = L.work + NCOL * 3 * hd;   // scores of my keys [<= 320]
             float *pv = sc + 320;                  // [MK_WAVES][hd] partial P.V per wave
-            float *mx = pv + MK_WAVES * hd;        // [2]
+            float *mx = pv + MK_WAVES * hd;        // [2]: max, sum
             const float scale = 1.f / sqrtf((float)hd);
             const int lpk = hd / 8;                // lanes per key
             const int kpw = 64 / lpk;              // keys per wave step
             const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
             const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
-            const int kaux = rmm ? AUX_DEV : 0;
+            const int kaux = kv_live ? AUX_DEV : 0;
             for (int c = 0; c < ncol; ++c) {
               const int P = pos0 + c;             // query position; keys 0..P
               const int nblk = P / MK_KBLK + 1;
@@ -600,6 +597,11 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 for (int i = lane; i < nk; i += 64) mv = fmaxf(mv, sc[i]);
 #pragma unroll
                 for (int off = 32; off > 0; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off, 64));
+                if (lane == 0) mx[0] = mv;
+              }
+              __syncthreads();
+              if (w8 == 0) {
+                const float mv = mx[0];
                 float ls = 0.f;
                 for (int i = lane; i < nk; i += 64) {
                   const float p = expf(sc[i] - mv);
@@ -607,7 +609,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                   ls += p;
                 }
                 ls = wave_sum(ls);
-                if (lane == 0) { mx[0] = mv; mx[1] = ls; }
+                if (lane == 0) mx[1] = ls;
               }
               __syncthreads();
               // P.V: wave w takes keys w, w+8, ...; lanes take dims
@@ -662,8 +664,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                     acc = fmaf(part[ww * plen + 2 + d], sc, acc);
                   }
                 }
-                const float o = acc / Ls;
-                ov[c * hd + d] = rmm ? rbf(o) : o;
+                ov[c * hd + d] = acc / Ls;
               }
               __syncthreads();
             }
@@ -701,7 +702,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         if (!gather2d<AUX_L2>(xr, ncol, H, H, tg, L.xres, L.flag, m.ctl, (step << 16) | (li << 8) | 9)) MK_BAIL();
       }
       // ================================================================ FFN
-      rmsnorm_cols<NCOL>(L.xres, L.hn, ly.ln2, H, m.rms_eps, ncol, rmm, L.red);
+      rmsnorm_cols<NCOL>(L.xres, L.hn, ly.ln2, H, m.rms_eps, ncol, L.red);
       {
         const int J = m.J;
         uint2 *xm = ly.x_m + (size_t)x * MK_MAXCOL * J;
@@ -724,8 +725,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           }
           if (lane == 0)
             FOR_COL(c) {
-              const float mm = siluf_(g[c]) * u[c];
-              pub_l2(xm + c * J + j, rmm ? rbf(mm) : mm, tg);
+              pub_l2(xm + c * J + j, siluf_(g[c]) * u[c], tg);
             }
         }
         // F2: down-projection slice (columns x*J .. x*J+J of W_d)
@@ -766,7 +766,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       continue;
     }
     // ================================================================ LM head + greedy argmax
-    rmsnorm_cols<NCOL>(L.xres, L.hn, m.lnf, H, m.rms_eps, ncol, false, L.red);
+    rmsnorm_cols<NCOL>(L.xres, L.hn, m.lnf, H, m.rms_eps, ncol, L.red);
     {
       const int nrg_all = m.V / RG_h;
       const int g0 = (int)((long long)b * nrg_all / MK_NWG), g1 = (int)((long long)(b + 1) * nrg_all / MK_NWG);
@@ -830,6 +830,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                            ((unsigned long long)rec.w << 32) | rec.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+    __syncthreads();  // the candidate above was read from the scratch the final gather reuses
     if (b == 0) {
       // final argmax over the 256 workgroup candidates; the tag word is written after the
       // value/index word by the same thread, so a matching tag implies the record is complete

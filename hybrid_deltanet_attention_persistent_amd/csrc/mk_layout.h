@@ -93,7 +93,7 @@ struct MkLaunch {
   MkDev m;
   const int32_t *tokens;  // device: [n] (decode / verify) or the prompt (prefill)
   int32_t n;              // columns (decode / verify) or prompt tokens (prefill)
-  int32_t prefill;        // 1: process the tokens one by one with bf16 matmul operands
+  int32_t prefill;        // 1: process the tokens one by one (prompt), 0: decode / verify columns
   uint32_t tag0;          // exchange tag of the first forward pass of this launch
   int32_t *argmax;        // device: [n] (prefill: [1])
   float *logits;          // device, nullable: [n][V] (prefill: [V])

@@ -14,4 +14,4 @@ accumulation and the fused attention) for what the path computes.  Where the
 pages are silent the readings used are written next to each function.
 """
 from .ops import *  # noqa: F401,F403
-from .model import OracleModel, Contract, EXACT, C1  # noqa: F401
+from .model import OracleModel, Contract, EXACT, C1, C2  # noqa: F401

@@ -15,15 +15,19 @@ over a block of tokens, which changes nothing: the projections act on each
 token separately, and the sequence mixers (short conv, delta rule, causal
 attention) walk the tokens in order.
 
-Precision.  In ``EXACT`` mode nothing is rounded beyond the bfloat16 weights.
-In ``C1`` mode (used for GPU parity) values are rounded to bfloat16 exactly
-where the GPU stores or multiplies them in bfloat16: the K and V cache always,
-and during prefill (where the projections are matrix-core GEMMs) the activation
-operand of every projection, the attention queries and the attention
-probabilities (normalised to the row maximum, rounded before they weight V; the
-softmax denominator sums the unrounded values).  Decode and verify keep their
-activations unrounded (the weights stream from memory either way).  The LM head
-input is never rounded.
+Precision.  ``EXACT`` rounds nothing beyond the bfloat16 weights.  ``C2`` (the
+contract the GPU path implements) also stores the attention K and V cache in
+bfloat16, and keeps every activation in full precision in every mode: the
+weights and the KV cache are what the forward pass streams from memory, the
+activations are a few kilobytes per token.  ``C1`` additionally rounds, during
+prefill, the activation operand of every projection, the attention queries and
+the attention probabilities (normalised to the row maximum, rounded before they
+weight V; the denominator sums the unrounded values) to bfloat16.  On the
+seeded random-init models C1 is not a usable parity contract: a relative
+perturbation of 1e-7 at the input changes its prefill logits by about 1%
+(each perturbation flips some bfloat16 roundings, which cascade), while under
+C2 the same perturbation changes them by about 2e-5.  The LM head input is
+never rounded.
 """
 from __future__ import annotations
 
@@ -45,6 +49,7 @@ class Contract:
 
 EXACT = Contract(kv_bf16=False, prefill_bf16=False)
 C1 = Contract(kv_bf16=True, prefill_bf16=True)
+C2 = Contract(kv_bf16=True, prefill_bf16=False)
 
 
 def attention_causal(Q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, q_pos: np.ndarray,
@@ -78,7 +83,7 @@ def attention_causal(Q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, q_pos: np.nd
 class OracleModel:
     """Float64 forward pass of the synthetic hybrid decoder with its recurrent state."""
 
-    def __init__(self, cfg: ModelConfig, weight_bits: Dict[str, np.ndarray], contract: Contract = C1):
+    def __init__(self, cfg: ModelConfig, weight_bits: Dict[str, np.ndarray], contract: Contract = C2):
         self.cfg = cfg
         self.contract = contract
         self.w = {name: bf16_bits_to_f64(bits) for name, bits in weight_bits.items()}

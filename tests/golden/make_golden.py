@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 sys.path.insert(0, ROOT)
 
 import workloads as W  # noqa: E402
-from oracle import OracleModel, C1, argmax_lowest  # noqa: E402
+from oracle import OracleModel, C2, argmax_lowest  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 N_SAMPLE = 512
@@ -42,7 +42,7 @@ def run_generate(wl: W.Workload):
     weights = W.make_weights(cfg, seed=wl.weight_seed)
     prompt = W.make_prompt(cfg, wl.prompt_len, seed=wl.prompt_seed)
     ids = sample_ids(cfg.vocab)
-    m = OracleModel(cfg, weights, C1)
+    m = OracleModel(cfg, weights, C2)
     del weights
     rows = []
     t0 = time.time()
@@ -70,8 +70,8 @@ def run_verify(wl: W.Workload, max_forwards: int = 160):
     weights = W.make_weights(cfg, seed=wl.weight_seed)
     prompt = W.make_prompt(cfg, wl.prompt_len, seed=wl.prompt_seed)
     drafts = W.make_drafts(cfg, max_forwards, wl.verify_width, seed=wl.draft_seed)
-    ids = sample_ids(cfg.vocab)
-    m = OracleModel(cfg, weights, C1)
+    ids = sample_ids(cfg.vocab)[::4]
+    m = OracleModel(cfg, weights, C2)
     del weights
     t0 = time.time()
     g0 = argmax_lowest(m.prefill(prompt))

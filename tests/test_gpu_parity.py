@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from oracle import OracleModel, C1, argmax_lowest
+from oracle import OracleModel, C2, argmax_lowest
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +84,7 @@ def tiny():
 def test_tiny_generate_matches_oracle(dev, tiny):
     cfg = W.TINY
     prompt = W.make_prompt(cfg, 16, seed=1)
-    ref_toks, ref_logits = OracleModel(cfg, tiny, C1).generate(prompt, 16)
+    ref_toks, ref_logits = OracleModel(cfg, tiny, C2).generate(prompt, 16)
     r = Runner(cfg, tiny, dev)
     # greedy decode chained on the device: each step reads the previous step's argmax buffer
     nxt = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -107,7 +107,7 @@ def test_tiny_teacher_forced_random_tokens(dev, tiny):
     cfg = W.TINY
     prompt = W.make_prompt(cfg, 5, seed=21)
     feed = W.make_prompt(cfg, 40, seed=22)
-    ref = OracleModel(cfg, tiny, C1)
+    ref = OracleModel(cfg, tiny, C2)
     r = Runner(cfg, tiny, dev)
     g, lg = r.prefill(prompt)
     rl = ref.prefill(prompt)
@@ -125,7 +125,7 @@ def test_tiny_nonunit_gains(dev):
     cfg = W.TINY
     w = W.make_weights(cfg, seed=3, gain_std=0.1)
     prompt = W.make_prompt(cfg, 9, seed=4)
-    ref_toks, ref_logits = OracleModel(cfg, w, C1).generate(prompt, 6)
+    ref_toks, ref_logits = OracleModel(cfg, w, C2).generate(prompt, 6)
     r = Runner(cfg, w, dev)
     g, lg = r.prefill(prompt)
     toks, lgs = [g], [lg]
@@ -141,7 +141,7 @@ def test_tiny_nonunit_gains(dev):
 
 def test_tiny_single_token_prefill_and_full_context(dev, tiny):
     cfg = W.TINY
-    ref = OracleModel(cfg, tiny, C1)
+    ref = OracleModel(cfg, tiny, C2)
     r = Runner(cfg, tiny, dev)
     g, lg = r.prefill([7])
     rl = ref.prefill([7])
@@ -210,7 +210,7 @@ def test_tiny_verify_is_bit_identical_to_sequential_decode(dev, tiny, n_good):
     seq = Runner(cfg, tiny, dev)
     g0, _ = seq.prefill(prompt)
     # drafts: the greedy continuation, corrupted at position n_good (none if n_good == 4)
-    ref = OracleModel(cfg, tiny, C1)
+    ref = OracleModel(cfg, tiny, C2)
     ref.prefill(prompt)
     greedy_ref, t = [], g0
     for _ in range(4):
