@@ -233,7 +233,7 @@ struct Lds {
     return;                                                                                         \
   } while (0)
 
-template <int NCOL>
+template <int NCOL, bool PROMPT>
 __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   extern __shared__ float lds_raw[];
   const MkDev &m = a.m;
@@ -903,14 +903,21 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
 }
 
 // ------------------------------------------------------------------------------ host-side launchers
+// Instantiations: one decode column, up to MK_MAXCOL verify columns, and the prompt
+// processed token by token (a distinct kernel so that profiles separate it).
+static const void *forward_fn(int ncol_template, int prompt) {
+  if (prompt) return (const void *)mk_forward<1, true>;
+  return (ncol_template == 1) ? (const void *)mk_forward<1, false> : (const void *)mk_forward<MK_MAXCOL, false>;
+}
+
 extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, hipStream_t stream) {
   void *args[] = {const_cast<MkLaunch *>(a)};
-  const void *fn = (ncol_template == 1) ? (const void *)mk_forward<1> : (const void *)mk_forward<MK_MAXCOL>;
-  return hipLaunchCooperativeKernel(fn, dim3(MK_NWG), dim3(MK_THREADS), args, MK_LDS_BYTES, stream);
+  return hipLaunchCooperativeKernel(forward_fn(ncol_template, a->prefill), dim3(MK_NWG), dim3(MK_THREADS), args,
+                                    MK_LDS_BYTES, stream);
 }
 
 extern "C" hipError_t mk_forward_occupancy(int ncol_template, int *blocks_per_cu) {
-  const void *fn = (ncol_template == 1) ? (const void *)mk_forward<1> : (const void *)mk_forward<MK_MAXCOL>;
+  const void *fn = forward_fn(ncol_template, ncol_template == 0);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, MK_LDS_BYTES);
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, MK_THREADS, MK_LDS_BYTES);
