@@ -20,8 +20,9 @@
 //     inside one XCD; the out-projection and the FFN down-projection are split
 //     over XCDs along their input dimension, and the residual stream is rebuilt
 //     by a reduce-scatter (over XCDs) + all-gather (inside the XCD) per sublayer.
-//   * Weights are streamed once per forward in a tile layout that makes every
-//     wave load a contiguous 1 KiB (see mk_layout.h).
+//   * Weights stream once per forward in a tile layout that makes every wave load
+//     a contiguous 1 KiB (mk_layout.h), and each phase's weight rows are loaded
+//     into registers one phase ahead, so HBM latency overlaps the hand-off wait.
 //   * Decode and verify use the same per-column arithmetic in the same order, so
 //     a verify forward's logits are bit-identical to sequential decode steps.
 #include <hip/hip_runtime.h>
@@ -31,11 +32,14 @@
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define MK_WAIT_TICKS 20000000ull   // watchdog: 0.2 s of the 100 MHz device wall clock
-// Hand-offs inside one XCD use the same device-coherent (sc1) loads as those between XCDs:
-// polling through the XCD's L2 alone (sc0) did not observe peers' stores reliably here.
-#define AUX_L2 16
 #define AUX_DEV 16                  // sc1: device-coherent
 #define RSRC_W3 0x00020000
+
+// per-wave register budgets of the prefetched weight rows (checked against the model on the host)
+#define NRG_IN 3   // in-projection / QKV row groups per wave
+#define NPAIR 2    // gate/up row pairs per wave
+#define LMAX_D 8   // loads per lane of one down-projection row group
+#define LM_BATCH(NCOL) ((NCOL) == 1 ? 8 : 4)
 
 // ------------------------------------------------------------------------------ helpers
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -65,13 +69,39 @@ __device__ __forceinline__ float sigmoidf_(float x) {
 __device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
 __device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// Cross-lane sums with DPP (no LDS traffic).  Within a 16-lane row: xor 1 and xor 2 (quad
+// permutes), then the half-row and row mirrors pair up 4- and 8-lane groups; every lane of the
+// group ends with the same value (a + b == b + a).  Across rows the four row totals are added in
+// a fixed order.
+#define DPP_XOR1 0xB1       // quad_perm [1,0,3,2]
+#define DPP_XOR2 0x4E       // quad_perm [2,3,0,1]
+#define DPP_HALF_MIRROR 0x141
+#define DPP_MIRROR 0x140
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float group_sum(float v, int G) {  // butterfly over aligned groups of G lanes
-  for (int off = G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+__device__ __forceinline__ float row_sum16(float v) {
+  v = dpp_add<DPP_XOR1>(v);
+  v = dpp_add<DPP_XOR2>(v);
+  v = dpp_add<DPP_HALF_MIRROR>(v);
+  return dpp_add<DPP_MIRROR>(v);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ float group_sum(float v, int G) {  // sum over aligned groups of G lanes
+  if (G == 64) return wave_sum(v);
+  if (G >= 2) v = dpp_add<DPP_XOR1>(v);
+  if (G >= 4) v = dpp_add<DPP_XOR2>(v);
+  if (G >= 8) v = dpp_add<DPP_HALF_MIRROR>(v);
+  if (G >= 16) v = dpp_add<DPP_MIRROR>(v);
+  if (G == 32) v += __shfl_xor(v, 16, 64);
   return v;
 }
 // Sum of one value per thread over the workgroup, fixed order; red: >= MK_WAVES floats of LDS.
@@ -87,65 +117,154 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 }
 
 // tagged exchange slot: 8 bytes {float bits, tag}, written with one device-coherent 64-bit store
-__device__ __forceinline__ void pub_l2(uint2 *p, float v, uint32_t tag) {
+__device__ __forceinline__ void pub(uint2 *p, float v, uint32_t tag) {
   __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), ((unsigned long long)tag << 32) | __float_as_uint(v),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void pub_dev(uint2 *p, float v, uint32_t tag) {
-  __hip_atomic_store(reinterpret_cast<unsigned long long *>(p),
-                     ((unsigned long long)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
 
-// Gather a [nrow][ncol] block of tagged slots (row stride `stride` slots, ncol even)
-// into dst[nrow][ncol] (LDS), polling until every tag equals `tag`.  All threads
-// call it; ends with a barrier.  Returns false on watchdog expiry.
-template <int AUX>
-__device__ bool gather2d(const uint2 *src, int nrow, int ncol, int stride, uint32_t tag, float *dst,
-                         int *fail, int32_t *ctl, int site) {
+// Gather a [nrow][ncol] block of tagged slots (row stride `stride` slots, ncol even) into
+// dst[nrow][ncol] (LDS), polling until every tag equals `tag`.  Thread t polls 16-byte chunks
+// t, t + 512, ... (at most MAXC).  All threads call it; ends with a barrier.  On watchdog
+// expiry records the first failing site in the control block and returns false.
+template <int MAXC>
+__device__ bool gather2d(const uint2 *src, int nrow, int ncol, int stride, uint32_t tag, float *dst, int *fail,
+                         int32_t *ctl, int site, int tid) {
   const int half = ncol >> 1;
   const int nchunk = nrow * half;
   const uint32_t bytes = (uint32_t)(((nrow - 1) * stride + ncol) * 8);
-  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, bytes, RSRC_W3);
-  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, bytes, RSRC_W3);
+  if (nchunk > MAXC * MK_THREADS) {  // more slots than this call site polls: a layout bug, never a hang
+    if (tid == 0) {
+      *fail = 1;
+      int expect = 0;
+      __hip_atomic_compare_exchange_strong(ctl + MK_CTL_WHERE, &expect, site | (1 << 29), __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return false;
+  }
+  uint32_t off[MAXC];
+  int di[MAXC];
   uint32_t pend = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (tid + j * MK_THREADS < nchunk) pend |= 1u << j;
+  for (int j = 0; j < MAXC; ++j) {
+    const int c = tid + j * MK_THREADS;
+    const int r = c / half, q = c - r * half;
+    off[j] = (uint32_t)((r * stride + 2 * q) * 8);
+    di[j] = r * ncol + 2 * q;
+    if (c < nchunk) pend |= 1u << j;
+  }
   if (pend) {
     const unsigned long long deadline = wall_clock64() + MK_WAIT_TICKS;
     while (true) {
-      u32x4 v[8];
+      u32x4 v[MAXC];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (pend & (1u << j)) {
-          const int c = tid + j * MK_THREADS;
-          const int r = c / half, q = c - r * half;
-          v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (r * stride + 2 * q) * 8, 0, AUX);
-        }
-      }
+      for (int j = 0; j < MAXC; ++j)
+        if (pend & (1u << j)) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[j], 0, AUX_DEV);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < MAXC; ++j) {
         if ((pend & (1u << j)) && v[j].y == tag && v[j].w == tag) {
-          const int c = tid + j * MK_THREADS;
-          const int r = c / half, q = c - r * half;
-          dst[r * ncol + 2 * q] = __uint_as_float(v[j].x);
-          dst[r * ncol + 2 * q + 1] = __uint_as_float(v[j].z);
+          dst[di[j]] = __uint_as_float(v[j].x);
+          dst[di[j] + 1] = __uint_as_float(v[j].z);
           pend &= ~(1u << j);
         }
       }
       if (!pend) break;
       if (wall_clock64() > deadline) {
         *fail = 1;
-        // record the first expiry on the device: where, who, and the tag still found there
         uint32_t seen = 0;
 #pragma unroll
-        for (int j = 7; j >= 0; --j)
+        for (int j = MAXC - 1; j >= 0; --j)
           if (pend & (1u << j)) seen = v[j].y;
         int expect = 0;
         if (__hip_atomic_compare_exchange_strong(ctl + MK_CTL_WHERE, &expect, site | (1 << 30), __ATOMIC_RELAXED,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-          __hip_atomic_store(ctl + MK_CTL_WHERE + 1, (int)(blockIdx.x * 65536 + threadIdx.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(ctl + MK_CTL_WHERE + 1, (int)(blockIdx.x * 65536 + tid), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(ctl + MK_CTL_WHERE + 2, (int)seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(ctl + MK_CTL_WHERE + 3, (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+  return *fail == 0;
+}
+
+// One segment of a multi-segment gather: nrow rows of ncol (even) slots starting `off` slots
+// after the common base, row stride `stride` slots, into dst[nrow][ncol].
+struct GSeg {
+  int off, nrow, ncol, stride;
+  float *dst;
+};
+
+// Gather several blocks (all addressed from one base) in one polling loop and one barrier.
+template <int MAXC, int NSEG>
+__device__ bool gather_segs(const uint2 *base, const GSeg (&sg)[NSEG], uint32_t tag, int *fail, int32_t *ctl,
+                            int site, int tid) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, 0x7fffffff, RSRC_W3);
+  int total = 0;
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) total += sg[s].nrow * (sg[s].ncol >> 1);
+  if (total > MAXC * MK_THREADS) {
+    if (tid == 0) {
+      *fail = 1;
+      int expect = 0;
+      __hip_atomic_compare_exchange_strong(ctl + MK_CTL_WHERE, &expect, site | (1 << 29), __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return false;
+  }
+  uint32_t off[MAXC];
+  float *dp[MAXC];
+  uint32_t pend = 0;
+#pragma unroll
+  for (int j = 0; j < MAXC; ++j) {
+    int c = tid + j * MK_THREADS;
+    off[j] = 0;
+    dp[j] = nullptr;
+    if (c < total) {
+      pend |= 1u << j;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) {
+        const int half = sg[s].ncol >> 1, n = sg[s].nrow * half;
+        if (c >= 0 && c < n) {
+          const int r = c / half, q = c - r * half;
+          off[j] = (uint32_t)((sg[s].off + r * sg[s].stride + 2 * q) * 8);
+          dp[j] = sg[s].dst + r * sg[s].ncol + 2 * q;
+        }
+        c -= n;
+      }
+    }
+  }
+  if (pend) {
+    const unsigned long long deadline = wall_clock64() + MK_WAIT_TICKS;
+    while (true) {
+      u32x4 v[MAXC];
+#pragma unroll
+      for (int j = 0; j < MAXC; ++j)
+        if (pend & (1u << j)) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[j], 0, AUX_DEV);
+#pragma unroll
+      for (int j = 0; j < MAXC; ++j) {
+        if ((pend & (1u << j)) && v[j].y == tag && v[j].w == tag) {
+          dp[j][0] = __uint_as_float(v[j].x);
+          dp[j][1] = __uint_as_float(v[j].z);
+          pend &= ~(1u << j);
+        }
+      }
+      if (!pend) break;
+      if (wall_clock64() > deadline) {
+        *fail = 1;
+        uint32_t seen = 0;
+#pragma unroll
+        for (int j = MAXC - 1; j >= 0; --j)
+          if (pend & (1u << j)) seen = v[j].y;
+        int expect = 0;
+        if (__hip_atomic_compare_exchange_strong(ctl + MK_CTL_WHERE, &expect, site | (1 << 30), __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          __hip_atomic_store(ctl + MK_CTL_WHERE + 1, (int)(blockIdx.x * 65536 + tid), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(ctl + MK_CTL_WHERE + 2, (int)seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(ctl + MK_CTL_WHERE + 3, (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -159,19 +278,27 @@ __device__ bool gather2d(const uint2 *src, int nrow, int ncol, int stride, uint3
 }
 
 // ------------------------------------------------------------------------------ GEMV on tiles
-template <int LMAX>
-__device__ __forceinline__ void rg_load(const uint16_t *tile, int rg, int L, u32x4 (&w)[LMAX]) {
-  const u32x4 *p = reinterpret_cast<const u32x4 *>(tile) + (size_t)rg * L * 64 + lane_id();
+// Issue the loads of up to NRG row groups rg = first + i*stride (< end) of a tile: L loads per lane each.
+template <int NRG, int LMAX>
+__device__ __forceinline__ void rg_issue(const uint16_t *tile, int first, int stride, int end, int L,
+                                         u32x4 (&w)[NRG][LMAX]) {
 #pragma unroll
-  for (int i = 0; i < LMAX; ++i)
-    if (i < L) w[i] = __builtin_nontemporal_load(p + i * 64);
+  for (int r = 0; r < NRG; ++r) {
+    const int rg = first + r * stride;
+    if (rg < end) {
+      const u32x4 *p = reinterpret_cast<const u32x4 *>(tile) + (size_t)rg * L * 64 + lane_id();
+#pragma unroll
+      for (int i = 0; i < LMAX; ++i)
+        if (i < L) w[r][i] = __builtin_nontemporal_load(p + i * 64);
+    }
+  }
 }
 
-// Dot products of one row group with NCOL activation vectors act[c*astride + k];
-// returns each lane's row result (valid in every lane of the row's G-lane segment).
+// Dot products of one loaded row group with NCOL activation vectors act[c*astride + k]; returns each
+// lane's row result (valid in every lane of the row's G-lane segment).
 template <int NCOL, int LMAX>
-__device__ __forceinline__ void rg_dot(const u32x4 (&w)[LMAX], int L, int G, const float *act, int astride,
-                                       int n, float (&out)[NCOL]) {
+__device__ __forceinline__ void rg_dot(const u32x4 (&w)[LMAX], int L, int G, const float *act, int astride, int n,
+                                       float (&out)[NCOL]) {
   const int kl = (lane_id() & (G - 1)) * 8;
 #pragma unroll
   for (int c = 0; c < NCOL; ++c) out[c] = 0.f;
@@ -198,6 +325,55 @@ __device__ __forceinline__ void rg_dot(const u32x4 (&w)[LMAX], int L, int G, con
   for (int c = 0; c < NCOL; ++c) out[c] = group_sum(out[c], G);
 }
 
+// Per-lane partial dot of 16 bf16 weights (two 16-byte loads) with 16 cached activations.
+__device__ __forceinline__ float dot16(const u32x4 &w0, const u32x4 &w1, const float (&a)[16]) {
+  float f[8], s = 0.f;
+  unpack8(w0, f);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = fmaf(f[e], a[e], s);
+  unpack8(w1, f);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = fmaf(f[e], a[8 + e], s);
+  return s;
+}
+
+// Sum each of 8 per-lane partials over the 64 lanes: a transposing butterfly that moves half of
+// the partials at each of the first three steps.  Returns, in lane l, the total of partial l >> 3.
+__device__ __forceinline__ float reduce8(const float (&p)[8]) {
+  const int lane = lane_id();
+  const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8;
+  float q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // offset 32: the upper half keeps partials 4..7, the lower half 0..3
+    const float send = hi32 ? p[i] : p[i + 4];
+    const float keep = hi32 ? p[i + 4] : p[i];
+    q[i] = keep + __shfl_xor(send, 32, 64);
+  }
+  float r[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // offset 16
+    const float send = hi16 ? q[i] : q[i + 2];
+    const float keep = hi16 ? q[i + 2] : q[i];
+    r[i] = keep + __shfl_xor(send, 16, 64);
+  }
+  const float send = hi8 ? r[0] : r[1];  // offset 8
+  float t = (hi8 ? r[1] : r[0]) + __shfl_xor(send, 8, 64);
+  t = dpp_add<DPP_XOR1>(t);
+  t = dpp_add<DPP_XOR2>(t);
+  return dpp_add<DPP_HALF_MIRROR>(t);
+}
+
+// The same sum as reduce8 for a single partial: identical additions in identical order
+// (offsets 32, 16, 8, then 1, 2 and the half-row mirror), so decode and verify agree bit for bit.
+__device__ __forceinline__ float wave_sum_lm(float t) {
+  t += __shfl_xor(t, 32, 64);
+  t += __shfl_xor(t, 16, 64);
+  t += __shfl_xor(t, 8, 64);
+  t = dpp_add<DPP_XOR1>(t);
+  t = dpp_add<DPP_XOR2>(t);
+  return dpp_add<DPP_HALF_MIRROR>(t);
+}
+
 // RMSNorm of src[c][H] into dst[c][H] with gain g.
 template <int NCOL>
 __device__ void rmsnorm_cols(const float *src, float *dst, const float *g, int H, float eps, int n, float *red) {
@@ -207,9 +383,24 @@ __device__ void rmsnorm_cols(const float *src, float *dst, const float *g, int H
     for (int k = threadIdx.x; k < H; k += MK_THREADS) s = fmaf(src[c * H + k], src[c * H + k], s);
     const float tot = block_sum(s, red);
     const float den = sqrtf(tot / (float)H + eps);
-    for (int k = threadIdx.x; k < H; k += MK_THREADS) {
-      dst[c * H + k] = src[c * H + k] / den * g[k];
-    }
+    for (int k = threadIdx.x; k < H; k += MK_THREADS) dst[c * H + k] = src[c * H + k] / den * g[k];
+  }
+  __syncthreads();
+}
+
+// RMSNorm with the gains already in registers: thread t owns elements t and t + 512 (H <= 1024).
+template <int NCOL>
+__device__ void rmsnorm_cols_r(const float *src, float *dst, float g0, float g1, int H, float eps, int n,
+                               float *red, int tid) {
+  for (int c = 0; c < NCOL; ++c) {
+    if (c >= n) break;
+    float s = 0.f;
+    if (tid < H) s = fmaf(src[c * H + tid], src[c * H + tid], s);
+    if (tid + MK_THREADS < H) s = fmaf(src[c * H + tid + MK_THREADS], src[c * H + tid + MK_THREADS], s);
+    const float tot = block_sum(s, red);
+    const float den = sqrtf(tot / (float)H + eps);
+    if (tid < H) dst[c * H + tid] = src[c * H + tid] / den * g0;
+    if (tid + MK_THREADS < H) dst[c * H + tid + MK_THREADS] = src[c * H + tid + MK_THREADS] / den * g1;
   }
   __syncthreads();
 }
@@ -217,13 +408,6 @@ __device__ void rmsnorm_cols(const float *src, float *dst, const float *g, int H
 // loop over the live columns with compile-time indices (register arrays stay in registers)
 #define FOR_COL(c) _Pragma("unroll") for (int c = 0; c < NCOL; ++c) if (c < ncol)
 
-// ------------------------------------------------------------------------------ shared memory map
-struct Lds {
-  float *xres, *hn, *work, *red;
-  int *flag;
-};
-
-// ------------------------------------------------------------------------------ the kernel
 // On a watchdog expiry the whole workgroup records the error and leaves; the other
 // workgroups then time out on its missing outputs and leave too.
 #define MK_BAIL()                                                                                   \
@@ -232,24 +416,34 @@ struct Lds {
       __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_HANG, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); \
     return;                                                                                         \
   } while (0)
+#define SITE(ph) ((step << 16) | (li << 8) | (ph))
 
+typedef const __attribute__((address_space(4))) MkLayerDev ConstLayer;
+
+// ------------------------------------------------------------------------------ the kernel
 template <int NCOL, bool PROMPT>
 __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   extern __shared__ float lds_raw[];
   const MkDev &m = a.m;
   const int b = blockIdx.x, x = b & (MK_NX - 1), lw = b >> 3;
-  const int w8 = wave_id(), lane = lane_id(), tid = threadIdx.x;
-  const int wx = lw * MK_WAVES + w8;  // wave index inside the XCD, 0..255
+  // the wave index is wave-uniform: read it into a scalar register so that every row-group
+  // index derived from it is scalar too
+  const int w8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id(), tid = threadIdx.x, tid0 = threadIdx.x;
+  const int wx = lw * MK_WAVES + w8;          // wave index inside the XCD, 0..255
+  const int XW = MK_NL * MK_WAVES;            // waves per XCD
   const int H = m.H;
+  // the layer table is read-only: reading it through the constant address space gives
+  // scalar loads, so every pointer taken from it is known to be wave-uniform
+  ConstLayer *const layers = (ConstLayer *)(uintptr_t)m.layers;
 
-  Lds L;
-  L.xres = lds_raw;
-  L.hn = L.xres + NCOL * H;
-  L.work = L.hn + NCOL * H;
-  L.red = L.work + 8192;
-  L.flag = reinterpret_cast<int *>(L.red + 64);
+  float *xres = lds_raw;                        // [NCOL][H] residual stream
+  float *hn = xres + NCOL * H;                  // [NCOL][H] normalised activations
+  float *work = hn + NCOL * H;                  // [8192] phase scratch
+  float *red = work + 8192;                     // [64] reductions
+  int *flag = reinterpret_cast<int *>(red + 64);
   if (tid == 0) {
-    L.flag[0] = 0;
+    flag[0] = 0;
     uint32_t xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
     if ((int)(xcc & 7) != x) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_XCD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -259,116 +453,169 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   const int ctl_pos = __hip_atomic_load(m.ctl + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int pend_n = __hip_atomic_load(m.ctl + MK_CTL_PEND, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int par = __hip_atomic_load(m.ctl + MK_CTL_PAR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool verify = !a.prefill && a.n > 1;
-  const int nsteps = a.prefill ? a.n : 1;
-  const int ncol = a.prefill ? 1 : a.n;
-  // prompts written in this launch are read back by other XCDs in later steps of it
-  const bool kv_live = a.prefill != 0;
+  const bool verify = !PROMPT && a.n > 1;
+  const int nsteps = PROMPT ? a.n : 1;
+  const int ncol = PROMPT ? 1 : a.n;
   const int G_h = mk_tile_G(H), L_h = H / 8 / G_h, RG_h = 64 / G_h;
   const int SL = H / MK_NL;  // residual slice per workgroup in the reductions
+  const int nh = m.nh, dk = m.dk, dv = m.dv, nq = m.nq, nkv = m.nkv, hd = m.hd, J = m.J;
+  const int G_o = mk_tile_G(dv), RG_o = 64 / G_o;        // out-projection columns of one head: L == 1
+  const int G_a = mk_tile_G(hd), RG_a = 64 / G_a;        // o-projection columns of one head: L == 1
+  const int G_d = mk_tile_G(J), L_d = J / 8 / G_d, RG_d = 64 / G_d;
+  constexpr int MC2 = NCOL == 1 ? 1 : 2;                 // polled chunks per thread of the larger gathers
+
+  // prefetched weight rows (registers), one phase ahead of their use
+  u32x4 w_in[NRG_IN][2];      // D1 / A1
+  u32x4 w_out[1][1];          // D3 / A3
+  u32x4 w_gu[NPAIR * 2][2];   // F1 (gate, up of up to NPAIR pairs)
+  u32x4 w_dn[1][LMAX_D];      // F2
+
+  // in-projection (DeltaNet) or QKV (attention) rows of layer li for this wave
+  auto issue_in = [&](int li) {
+    ConstLayer &ly = layers[li];
+    if (ly.kind == 0) {
+      if (x < nh) rg_issue<NRG_IN, 2>(ly.dn_in + (size_t)x * m.r_in * H, wx, XW, m.r_in / RG_h, L_h, w_in);
+    } else if (x < nq) {
+      const int per = hd / RG_h;
+#pragma unroll
+      for (int r = 0; r < NRG_IN; ++r) {
+        const int u = wx + r * XW;
+        if (u < 3 * per) {
+          const int t = u / per, rg = u - t * per;
+          const uint16_t *tile = (t == 0) ? ly.at_q + (size_t)x * hd * H
+                               : (t == 1) ? ly.at_k + (size_t)(x * nkv / nq) * hd * H
+                                          : ly.at_v + (size_t)(x * nkv / nq) * hd * H;
+          const u32x4 *p = reinterpret_cast<const u32x4 *>(tile) + (size_t)rg * L_h * 64 + lane;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            if (i < L_h) w_in[r][i] = __builtin_nontemporal_load(p + i * 64);
+        }
+      }
+    }
+  };
 
   for (int step = 0; step < nsteps; ++step) {
-    const uint32_t tag = a.tag0 + step;
+    const uint32_t tg = a.tag0 + step;
     const int pos0 = ctl_pos + step;       // position of column 0
     const bool last_step = step == nsteps - 1;
+    int li = 0;
 
+    issue_in(0);
+    float g1a = (tid < H) ? layers[0].ln1[tid] : 0.f;      // gains of the next RMSNorm
+    float g1b = (tid + MK_THREADS < H) ? layers[0].ln1[tid + MK_THREADS] : 0.f;
     // ---- embedding rows
     for (int c = 0; c < ncol; ++c) {
-      int t = a.tokens[a.prefill ? step : c];
+      int t = a.tokens[PROMPT ? step : c];
       if (t < 0 || t >= m.V) {
         if (tid == 0) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         t = 0;
       }
       const uint16_t *row = m.embed + (size_t)t * H;
-      for (int k = tid; k < H; k += MK_THREADS) L.xres[c * H + k] = bfv(row[k]);
+      for (int k = tid; k < H; k += MK_THREADS) xres[c * H + k] = bfv(row[k]);
     }
     __syncthreads();
 
-    for (int li = 0; li < m.n_layers; ++li) {
-      // the layer table is read-only: reading it through the constant address space gives
-      // scalar loads, so every pointer below is known to be wave-uniform
-      typedef const __attribute__((address_space(4))) MkLayerDev ConstLayer;
-      ConstLayer &ly = ((ConstLayer *)(uintptr_t)m.layers)[li];
-      const uint32_t tg = tag;
-      // ================================================================ mixer
-      rmsnorm_cols<NCOL>(L.xres, L.hn, ly.ln1, H, m.rms_eps, ncol, L.red);
+    for (li = 0; li < m.n_layers; ++li) {
+      ConstLayer &ly = layers[li];
+      // A per-layer copy of the thread index the compiler cannot see through: address
+      // arithmetic derived from it stays inside the layer loop instead of being hoisted out
+      // (and spilled) for the whole loop.
+      int tid = tid0;
+      asm volatile("" : "+v"(tid));
+      const int lane = tid & 63;
+      // gains of this layer's FFN norm, needed after the mixer
+      const float g2a = (tid < H) ? ly.ln2[tid] : 0.f;
+      const float g2b = (tid + MK_THREADS < H) ? ly.ln2[tid + MK_THREADS] : 0.f;
+      rmsnorm_cols_r<NCOL>(xres, hn, g1a, g1b, H, m.rms_eps, ncol, red, tid);
       if (ly.kind == 0) {
-        // ------------------------------------------------ D1: in-projection rows of head x
-        const int nh = m.nh, dk = m.dk, dv = m.dv, r_in = m.r_in;
+        // ================================================ DeltaNet layer
         uint2 *xin = ly.x_in + (size_t)x * MK_MAXCOL * m.r_in_max;
+        uint2 *xo = ly.x_o + (size_t)x * MK_MAXCOL * m.x_o_len;
+        const int RW = dv / MK_NL, r0 = lw * RW;
+        // ---- D1: in-projection rows of head x (weights already in flight)
         if (x < nh) {
-          const uint16_t *tile = ly.dn_in + (size_t)x * r_in * H;
-          const int nrg = r_in / RG_h;
-          for (int rg = wx; rg < nrg; rg += MK_NL * MK_WAVES) {
-            u32x4 wr[2];
-            rg_load<2>(tile, rg, L_h, wr);
-            float o[NCOL];
-            rg_dot<NCOL, 2>(wr, L_h, G_h, L.hn, H, ncol, o);
-            if ((lane & (G_h - 1)) == 0) {
-              const int row = rg * RG_h + lane / G_h;
-              FOR_COL(c) pub_l2(xin + c * m.r_in_max + row, o[c], tg);
+          const int nrg = m.r_in / RG_h;
+#pragma unroll
+          for (int r = 0; r < NRG_IN; ++r) {
+            const int rg = wx + r * XW;
+            if (rg < nrg) {
+              float o[NCOL];
+              rg_dot<NCOL, 2>(w_in[r], L_h, G_h, hn, H, ncol, o);
+              if ((lane & (G_h - 1)) == 0) {
+                const int row = rg * RG_h + lane / G_h;
+                FOR_COL(c) pub(xin + c * m.r_in_max + row, o[c], tg);
+              }
             }
           }
+          // prefetch: the out-projection rows (D3)
+          if (wx < H / RG_o) rg_issue<1, 1>(ly.dn_out + (size_t)x * H * dv, wx, XW, H / RG_o, 1, w_out);
         }
-        // ------------------------------------------------ D2: conv, norms, gates, delta rule
-        const int RW = dv / MK_NL, r0 = lw * RW;
-        const int HPR = dk / 64;  // waves per state row
-        float *qk = L.work;                       // [NCOL][2dk]
-        float *vr = qk + NCOL * 2 * dk;           // [NCOL][RWp]
-        const int RWp = RW < 2 ? 2 : RW;
-        float *ab = vr + NCOL * RWp;              // [NCOL][2]
-        float *nrm = ab + NCOL * 2;               // [NCOL][2] 1/den of q, k
+        // ---- D2: conv, norms, gates, delta rule on my RW rows of S
+        float *qk = work;                         // [NCOL][2dk]
+        float *vr = qk + NCOL * 2 * dk;           // [NCOL][RW] (RW even)
+        float *ab = vr + NCOL * RW;               // [NCOL][2]
+        float *nrm = ab + NCOL * 2;               // [NCOL][2]
         float *gts = nrm + NCOL * 2;              // [NCOL][2] alpha, beta
-        float *ored = gts + NCOL * 2;             // [16] row-partial exchange
+        float *outo = gts + NCOL * 2;             // [NCOL][RW]
+        float gn = 0.f;
         if (x < nh) {
-          for (int c = 0; c < ncol; ++c) {
-            if (!gather2d<AUX_L2>(xin + c * m.r_in_max, 1, 2 * dk, 0, tg, qk + c * 2 * dk, L.flag, m.ctl, (step << 16) | (li << 8) | 1)) MK_BAIL();
-            if (!gather2d<AUX_L2>(xin + c * m.r_in_max + 2 * dk + r0, 1, RWp, 0, tg, vr + c * RWp, L.flag, m.ctl, (step << 16) | (li << 8) | 2)) MK_BAIL();
-            if (!gather2d<AUX_L2>(xin + c * m.r_in_max + 2 * dk + 2 * dv, 1, 2, 0, tg, ab + c * 2, L.flag, m.ctl, (step << 16) | (li << 8) | 3)) MK_BAIL();
+          // this wave's row of S (wave w < RW owns row r0 + w; lane holds elements lane + 64 j)
+          const bool act = w8 < RW;
+          float *Srow = ly.S + ((size_t)x * dv + r0 + (act ? w8 : 0)) * dk;
+          float s[2] = {0.f, 0.f};
+          if (act) {
+            s[0] = Srow[lane];
+            if (dk > 64) s[1] = Srow[64 + lane];
           }
-          // conv + SiLU: threads [0, 2dk) are q/k channels of head x, [2dk, 2dk+RW) my v channels
+          // conv history of my channels (positions pos0-3 .. pos0-1), loaded before the waits
+          const int nch = 2 * dk + RW;
+          int ch = 0;
+          if (tid < 2 * dk) ch = (tid < dk) ? x * dk + tid : nh * dk + x * dk + (tid - dk);
+          else if (tid < nch) ch = 2 * nh * dk + x * dv + r0 + (tid - 2 * dk);
+          float hist[3] = {0.f, 0.f, 0.f};
+          float4 wt = make_float4(0.f, 0.f, 0.f, 0.f);
+          gn = (tid < dv) ? ly.dn_gnorm[tid] : 0.f;   // gated-norm gain, used in D3
+          if (tid < nch) {
+            wt = *reinterpret_cast<const float4 *>(ly.dn_conv + ch * 4);
+            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(ly.ring, 0, MK_RING * m.C * 4, RSRC_W3);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+              const int pp = pos0 - 3 + i;
+              if (pp >= 0)
+                hist[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, ((pp & (MK_RING - 1)) * m.C + ch) * 4, 0, AUX_DEV));
+            }
+          }
           {
-            const int nch = 2 * dk + RW;
+            const GSeg sg[3] = {{0, ncol, 2 * dk, m.r_in_max, qk},                 // q, k pre-conv
+                                {2 * dk + r0, ncol, RW, m.r_in_max, vr},           // my v rows
+                                {2 * dk + 2 * dv, ncol, 2, m.r_in_max, ab}};       // a, b
+            if (!gather_segs<MC2, 3>(xin, sg, tg, flag, m.ctl, SITE(1), tid)) MK_BAIL();
+          }
+          // conv + SiLU: threads [0, 2dk) are the q/k channels of head x, [2dk, 2dk+RW) my v channels
+          {
             if (tid < nch) {
-              int ch;
-              float *cur;  // column stride cstride
               int cstride;
+              float *cur;
               if (tid < 2 * dk) {
-                ch = (tid < dk) ? x * dk + tid : nh * dk + x * dk + (tid - dk);
                 cur = qk + tid;
                 cstride = 2 * dk;
               } else {
-                ch = 2 * nh * dk + x * dv + r0 + (tid - 2 * dk);
                 cur = vr + (tid - 2 * dk);
-                cstride = RWp;
+                cstride = RW;
               }
-              const float w0 = ly.dn_conv[ch * 4 + 0], w1 = ly.dn_conv[ch * 4 + 1];
-              const float w2 = ly.dn_conv[ch * 4 + 2], w3 = ly.dn_conv[ch * 4 + 3];
               float raw[NCOL];
 #pragma unroll
               for (int c = 0; c < NCOL; ++c) raw[c] = (c < ncol) ? cur[c * cstride] : 0.f;
-              float hist[3];
-              {
-                __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(ly.ring, 0, MK_RING * m.C * 4, RSRC_W3);
-#pragma unroll
-                for (int i = 0; i < 3; ++i) {
-                  const int pp = pos0 - 3 + i;
-                  hist[i] = (pp >= 0) ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                            rr, ((pp & (MK_RING - 1)) * m.C + ch) * 4, 0, AUX_L2))
-                                      : 0.f;
-                }
-              }
-              const float wt[4] = {w0, w1, w2, w3};
+              const float wv[4] = {wt.x, wt.y, wt.z, wt.w};
               FOR_COL(c) {
-                float s = 0.f;
+                float sacc = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  const int back = 3 - i;              // tap i meets the token `back` steps before column c
-                  const int cc = c - back;
+                  const int cc = c - (3 - i);              // tap i meets the token 3 - i steps before column c
                   const float v = (cc >= 0) ? raw[cc < 0 ? 0 : cc] : hist[cc + 3 < 0 ? 0 : cc + 3];
-                  s = fmaf(wt[i], v, s);
+                  sacc = fmaf(wv[i], v, sacc);
                 }
-                cur[c * cstride] = siluf_(s);
+                cur[c * cstride] = siluf_(sacc);
               }
               if (tid >= 2 * dk || lw == 0)
                 FOR_COL(c) ly.ring[((pos0 + c) & (MK_RING - 1)) * m.C + ch] = raw[c];
@@ -379,149 +626,128 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           for (int r = w8; r < 2 * ncol; r += MK_WAVES) {
             const int c = r >> 1, which = r & 1;
             const float *p = qk + c * 2 * dk + which * dk;
-            float s = 0.f;
-            for (int i = lane; i < dk; i += 64) s = fmaf(p[i], p[i], s);
-            s = wave_sum(s);
-            if (lane == 0) nrm[c * 2 + which] = sqrtf(s + m.l2_eps);
+            float sq = 0.f;
+            for (int i = lane; i < dk; i += 64) sq = fmaf(p[i], p[i], sq);
+            sq = wave_sum(sq);
+            if (lane == 0) nrm[c * 2 + which] = sqrtf(sq + m.l2_eps);
           }
           if (tid < ncol) {
             gts[tid * 2 + 0] = expf(-softplusf_(ab[tid * 2 + 0]));
             gts[tid * 2 + 1] = sigmoidf_(ab[tid * 2 + 1]);
           }
           __syncthreads();
-          for (int i = tid; i < ncol * 2 * dk; i += MK_THREADS) qk[i] = qk[i] / nrm[(i / (2 * dk)) * 2 + ((i % (2 * dk)) >= dk)];
+          for (int i = tid; i < ncol * 2 * dk; i += MK_THREADS)
+            qk[i] = qk[i] / nrm[(i / (2 * dk)) * 2 + ((i % (2 * dk)) >= dk)];
           __syncthreads();
-
-          // delta rule on my RW rows: wave w -> row w / HPR, lanes -> element (w % HPR)*64 + lane
-          const int rr = w8 / HPR, e = (w8 % HPR) * 64 + lane;
-          const bool act = rr < RW;
-          float *Srow = ly.S + ((size_t)x * dv + r0 + (act ? rr : 0)) * dk;
-          float s = act ? Srow[e] : 0.f;
-          const float *pk_base = ly.pend + (size_t)par * nh * MK_MAXCOL * (dk + dv + 2) + (size_t)x * MK_MAXCOL * (dk + dv + 2);
-          auto rowsum = [&](float v) -> float {
-            v = wave_sum(v);
-            if (lane == 0) ored[w8] = v;
-            __syncthreads();
-            float t = 0.f;
-            if (act) {
-              t = ored[rr * HPR];
-              for (int hh = 1; hh < HPR; ++hh) t += ored[rr * HPR + hh];
+          // delta rule: S_r <- alpha S_r + beta (v_r - alpha S_r.k) k ; o_r = S_r.q (rows are independent)
+          if (act) {
+            const int J2 = dk / 64;
+            auto rowdot = [&](const float *vec) {  // S_r . vec (vec: dk values)
+              float p = fmaf(s[0], vec[lane], 0.f);
+              if (J2 > 1) p = fmaf(s[1], vec[64 + lane], p);
+              return wave_sum(p);
+            };
+            const float *pk_base = ly.pend + ((size_t)par * nh + x) * MK_MAXCOL * (dk + dv + 2);
+            for (int j = 0; j < pend_n; ++j) {  // pending updates left by a verify forward
+              const float *pk = pk_base + j * (dk + dv + 2);
+              const float aj = pk[dk + dv], bj = pk[dk + dv + 1], vj = pk[dk + r0 + w8];
+              const float sk = rowdot(pk);
+              const float u = bj * (vj - aj * sk);
+              s[0] = fmaf(u, pk[lane], aj * s[0]);
+              if (J2 > 1) s[1] = fmaf(u, pk[64 + lane], aj * s[1]);
             }
-            __syncthreads();
-            return t;
-          };
-          // pending updates left by a verify forward: replay the accepted ones
-          for (int j = 0; j < pend_n; ++j) {
-            const float *pk = pk_base + j * (dk + dv + 2);
-            const float kj = pk[e < dk ? e : 0];
-            const float vj = pk[dk + r0 + (act ? rr : 0)];
-            const float aj = pk[dk + dv], bj = pk[dk + dv + 1];
-            const float sk = rowsum(act ? s * kj : 0.f);
-            const float u = bj * (vj - aj * sk);
-            s = fmaf(u, kj, aj * s);
+            if (verify) {  // S after the accepted tokens; this forward's tokens become pending
+              Srow[lane] = s[0];
+              if (J2 > 1) Srow[64 + lane] = s[1];
+            }
+            FOR_COL(c) {
+              const float *kc = qk + c * 2 * dk + dk, *qc = qk + c * 2 * dk;
+              const float al = gts[c * 2 + 0], be = gts[c * 2 + 1];
+              const float sk = rowdot(kc);
+              const float u = be * (vr[c * RW + w8] - al * sk);
+              s[0] = fmaf(u, kc[lane], al * s[0]);
+              if (J2 > 1) s[1] = fmaf(u, kc[64 + lane], al * s[1]);
+              const float o = rowdot(qc);
+              if (lane == 0) outo[c * RW + w8] = o;
+            }
+            if (!verify) {
+              Srow[lane] = s[0];
+              if (J2 > 1) Srow[64 + lane] = s[1];
+            }
           }
-          if (verify && act) Srow[e] = s;  // S after the accepted tokens; this forward's tokens become pending
-          float *outo = L.work + 4096;     // [NCOL][RWp] o rows
-          for (int c = 0; c < ncol; ++c) {
-            const float kc = qk[c * 2 * dk + dk + (e < dk ? e : 0)];
-            const float qc = qk[c * 2 * dk + (e < dk ? e : 0)];
-            const float al = gts[c * 2 + 0], be = gts[c * 2 + 1];
-            const float vv = act ? vr[c * RWp + rr] : 0.f;
-            const float sk = rowsum(act ? s * kc : 0.f);
-            const float u = be * (vv - al * sk);
-            s = fmaf(u, kc, al * s);
-            const float o = rowsum(act ? s * qc : 0.f);
-            if (act && (w8 % HPR) == 0 && lane == 0) outo[c * RWp + rr] = o;
-          }
-          if (!verify && act) Srow[e] = s;
           if (verify) {  // this forward's (k, v, alpha, beta) become the pending updates
-            float *pw = ly.pend + (size_t)(par ^ 1) * nh * MK_MAXCOL * (dk + dv + 2) + (size_t)x * MK_MAXCOL * (dk + dv + 2);
+            float *pw = ly.pend + ((size_t)(par ^ 1) * nh + x) * MK_MAXCOL * (dk + dv + 2);
             for (int c = 0; c < ncol; ++c) {
               float *pc = pw + c * (dk + dv + 2);
               if (lw == 0) {
                 for (int i = tid; i < dk; i += MK_THREADS) pc[i] = qk[c * 2 * dk + dk + i];
                 if (tid == 0) { pc[dk + dv] = gts[c * 2]; pc[dk + dv + 1] = gts[c * 2 + 1]; }
               }
-              if (tid < RW) pc[dk + r0 + tid] = vr[c * RWp + tid];
+              if (tid < RW) pc[dk + r0 + tid] = vr[c * RW + tid];
             }
           }
           __syncthreads();
-          wait_stores();
-          {
-            uint2 *xo = ly.x_o + (size_t)x * MK_MAXCOL * m.x_o_len;
-            if (tid < ncol * RW) {
-              const int c = tid / RW, r = tid % RW;
-              pub_l2(xo + c * m.x_o_len + r0 + r, outo[c * RWp + r], tg);
-            }
+          // a prompt's next token reads the ring written here (other workgroups of the XCD); decode
+          // and verify state is read by the next launch only
+          if (PROMPT) wait_stores();
+          if (tid < ncol * RW) {
+            const int c = tid / RW, r = tid - (tid / RW) * RW;
+            pub(xo + c * m.x_o_len + r0 + r, outo[c * RW + r], tg);
           }
         }
-        // ------------------------------------------------ D3: gated RMSNorm + out-projection slice
-        {
-          uint2 *xmix = ly.x_mix;
-          const int G_o = mk_tile_G(dv), L_o = dv / 8 / G_o, RG_o = 64 / G_o;
-          if (x < nh) {
-            float *o = L.work;              // [NCOL][dv]
-            float *z = o + NCOL * dv;       // [NCOL][dv]
-            uint2 *xo = ly.x_o + (size_t)x * MK_MAXCOL * m.x_o_len;
-            for (int c = 0; c < ncol; ++c) {
-              if (!gather2d<AUX_L2>(xo + c * m.x_o_len, 1, dv, 0, tg, o + c * dv, L.flag, m.ctl, (step << 16) | (li << 8) | 4)) MK_BAIL();
-              if (!gather2d<AUX_L2>(xin + c * m.r_in_max + 2 * dk + dv, 1, dv, 0, tg, z + c * dv, L.flag, m.ctl, (step << 16) | (li << 8) | 5)) MK_BAIL();
-            }
-            for (int c = 0; c < ncol; ++c) {
-              float sq = 0.f;
-              for (int i = tid; i < dv; i += MK_THREADS) sq = fmaf(o[c * dv + i], o[c * dv + i], sq);
-              const float den = sqrtf(block_sum(sq, L.red) / (float)dv + m.rms_eps);
-              for (int i = tid; i < dv; i += MK_THREADS) {
-                o[c * dv + i] = o[c * dv + i] / den * ly.dn_gnorm[i] * siluf_(z[c * dv + i]);
-              }
-            }
-            __syncthreads();
-            const uint16_t *tile = ly.dn_out + (size_t)x * H * dv;
-            const int nrg = H / RG_o;
-            for (int rg = wx; rg < nrg; rg += MK_NL * MK_WAVES) {
-              u32x4 wr[2];
-              rg_load<2>(tile, rg, L_o, wr);
-              float oo[NCOL];
-              rg_dot<NCOL, 2>(wr, L_o, G_o, o, dv, ncol, oo);
-              if ((lane & (G_o - 1)) == 0) {
-                const int row = rg * RG_o + lane / G_o;
-                FOR_COL(c) pub_dev(xmix + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
-              }
-            }
-          } else {
-            for (int i = tid + lw * MK_THREADS; i < H; i += MK_NL * MK_THREADS)
-              for (int c = 0; c < ncol; ++c) pub_dev(xmix + ((size_t)c * MK_NX + x) * H + i, 0.f, tg);
+        // ---- D3: gated RMSNorm + out-projection columns of head x
+        if (x < nh) {
+          float *o = work;                 // [NCOL][dv]
+          float *z = o + NCOL * dv;        // [NCOL][dv]
+          {
+            const GSeg sg[2] = {{(int)(xo - xin), ncol, dv, m.x_o_len, o},       // o rows of the head
+                                {2 * dk + dv, ncol, dv, m.r_in_max, z}};         // z of the head
+            if (!gather_segs<MC2, 2>(xin, sg, tg, flag, m.ctl, SITE(4), tid)) MK_BAIL();
           }
+          for (int c = 0; c < ncol; ++c) {
+            float sq = 0.f;
+            for (int i = tid; i < dv; i += MK_THREADS) sq = fmaf(o[c * dv + i], o[c * dv + i], sq);
+            const float den = sqrtf(block_sum(sq, red) / (float)dv + m.rms_eps);
+            if (tid < dv) o[c * dv + tid] = o[c * dv + tid] / den * gn * siluf_(z[c * dv + tid]);
+          }
+          __syncthreads();
+          if (wx < H / RG_o) {
+            float oo[NCOL];
+            rg_dot<NCOL, 1>(w_out[0], 1, G_o, o, dv, ncol, oo);
+            if ((lane & (G_o - 1)) == 0) {
+              const int row = wx * RG_o + lane / G_o;
+              FOR_COL(c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
+            }
+          }
+        } else {
+          for (int i = tid + lw * MK_THREADS; i < H; i += MK_NL * MK_THREADS)
+            for (int c = 0; c < ncol; ++c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + i, 0.f, tg);
         }
       } else {
         // ================================================ attention layer
-        const int nq = m.nq, nkv = m.nkv, hd = m.hd;
-        const int kvh = x * nkv / (nq > 0 ? nq : 1);
+        const int kvh = x * nkv / nq;
         uint2 *xin = ly.x_in + (size_t)x * MK_MAXCOL * m.r_in_max;
         uint2 *xo = ly.x_o + (size_t)x * MK_MAXCOL * m.x_o_len;
-        uint2 *xmix = ly.x_mix;
         if (x < nq) {
-          // ------------------------------------------------ A1: q rows of head x, k/v rows of its kv head
+          // ---- A1: q rows of head x, k/v rows of its kv head (weights already in flight)
           const int per = hd / RG_h;
-          const int nunits = 3 * per;
-          for (int u = wx; u < nunits; u += MK_NL * MK_WAVES) {
-            const int t = u / per, rg = u - t * per;
-            const uint16_t *tile = (t == 0) ? ly.at_q + (size_t)x * hd * H
-                                 : (t == 1) ? ly.at_k + (size_t)kvh * hd * H
-                                            : ly.at_v + (size_t)kvh * hd * H;
-            u32x4 wr[2];
-            rg_load<2>(tile, rg, L_h, wr);
-            float o[NCOL];
-            rg_dot<NCOL, 2>(wr, L_h, G_h, L.hn, H, ncol, o);
-            if ((lane & (G_h - 1)) == 0) {
-              const int row = t * hd + rg * RG_h + lane / G_h;
-              FOR_COL(c) pub_l2(xin + c * m.r_in_max + row, o[c], tg);
+#pragma unroll
+          for (int r = 0; r < NRG_IN; ++r) {
+            const int u = wx + r * XW;
+            if (u < 3 * per) {
+              const int t = u / per, rg = u - t * per;
+              float o[NCOL];
+              rg_dot<NCOL, 2>(w_in[r], L_h, G_h, hn, H, ncol, o);
+              if ((lane & (G_h - 1)) == 0) {
+                const int row = t * hd + rg * RG_h + lane / G_h;
+                FOR_COL(c) pub(xin + c * m.r_in_max + row, o[c], tg);
+              }
             }
           }
-          // ------------------------------------------------ A2: RoPE, KV append, split-KV partials
-          float *qkv = L.work;                    // [NCOL][3hd]
-          for (int c = 0; c < ncol; ++c)
-            if (!gather2d<AUX_L2>(xin + c * m.r_in_max, 1, 3 * hd, 0, tg, qkv + c * 3 * hd, L.flag, m.ctl, (step << 16) | (li << 8) | 6)) MK_BAIL();
+          if (wx < H / RG_a) rg_issue<1, 1>(ly.at_o + (size_t)x * H * hd, wx, XW, H / RG_a, 1, w_out);
+          // ---- A2: RoPE, KV append, split-KV partials
+          float *qkv = work;                    // [NCOL][3hd]
+          if (!gather2d<2>(xin, ncol, 3 * hd, m.r_in_max, tg, qkv, flag, m.ctl, SITE(6), tid)) MK_BAIL();
           {
             const int half = hd / 2;
             for (int i = tid; i < ncol * half; i += MK_THREADS) {
@@ -552,7 +778,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             wait_stores();
           }
           {
-            float *sc = L.work + NCOL * 3 * hd;   // scores of my keys [<= 320]
+            float *sc = work + NCOL * 3 * hd;      // scores of my keys [<= 320]
             float *pv = sc + 320;                  // [MK_WAVES][hd] partial P.V per wave
             float *mx = pv + MK_WAVES * hd;        // [2]: max, sum
             const float scale = 1.f / sqrtf((float)hd);
@@ -560,7 +786,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             const int kpw = 64 / lpk;              // keys per wave step
             const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
             const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
-            const int kaux = kv_live ? AUX_DEV : 0;
+#pragma unroll 1
             for (int c = 0; c < ncol; ++c) {
               const int P = pos0 + c;             // query position; keys 0..P
               const int nblk = P / MK_KBLK + 1;
@@ -568,6 +794,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               const int nk = (myblk == 0) ? 0 : (myblk - 1) * MK_KBLK + min(MK_KBLK, P + 1 - (lw + (myblk - 1) * MK_NL) * MK_KBLK);
               const float *q = qkv + c * 3 * hd;
               // scores: key slot ks -> block lw + (ks / 32) * 32, offset ks % 32
+#pragma unroll 1
               for (int base = w8 * kpw; base < nk; base += MK_WAVES * kpw) {
                 const int ks = base + lane / lpk;
                 float sdot = 0.f;
@@ -577,8 +804,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                   float kf[8];
                   if (tpos < pos0) {
                     const uint32_t off = (uint32_t)((((size_t)m.page_table[tpos / MK_PAGE] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + d0) * 2;
-                    u32x4 kw = (kaux == AUX_DEV) ? __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, AUX_DEV)
-                                                 : __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+                    const u32x4 kw = PROMPT ? __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, AUX_DEV)
+                                            : __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
                     unpack8(kw, kf);
                   } else {
                     const float *kk = qkv + (tpos - pos0) * 3 * hd + hd + d0;
@@ -597,11 +824,6 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 for (int i = lane; i < nk; i += 64) mv = fmaxf(mv, sc[i]);
 #pragma unroll
                 for (int off = 32; off > 0; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off, 64));
-                if (lane == 0) mx[0] = mv;
-              }
-              __syncthreads();
-              if (w8 == 0) {
-                const float mv = mx[0];
                 float ls = 0.f;
                 for (int i = lane; i < nk; i += 64) {
                   const float p = expf(sc[i] - mv);
@@ -609,19 +831,20 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                   ls += p;
                 }
                 ls = wave_sum(ls);
-                if (lane == 0) mx[1] = ls;
+                if (lane == 0) { mx[0] = mv; mx[1] = ls; }
               }
               __syncthreads();
               // P.V: wave w takes keys w, w+8, ...; lanes take dims
               for (int d = lane; d < hd; d += 64) {
                 float acc = 0.f;
+#pragma unroll 1
                 for (int ks = w8; ks < nk; ks += MK_WAVES) {
                   const int tpos = (lw + (ks / MK_KBLK) * MK_NL) * MK_KBLK + (ks % MK_KBLK);
                   float vvv;
                   if (tpos < pos0) {
                     const uint32_t off = (uint32_t)((((size_t)m.page_table[tpos / MK_PAGE] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + d) * 2;
-                    const uint32_t raw = (kaux == AUX_DEV) ? __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, AUX_DEV)
-                                                           : __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, 0);
+                    const uint32_t raw = PROMPT ? __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, AUX_DEV)
+                                                : __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, 0);
                     vvv = __uint_as_float(raw << 16);
                   } else {
                     vvv = qkv[(tpos - pos0) * 3 * hd + 2 * hd + d];
@@ -635,129 +858,159 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               uint2 *dst = xo + c * m.x_o_len + lw * plen;
               for (int d = tid; d < hd; d += MK_THREADS) {
                 float acc = pv[d];
+#pragma unroll 1
                 for (int ww = 1; ww < MK_WAVES; ++ww) acc += pv[ww * hd + d];
-                pub_l2(dst + 2 + d, acc, tg);
+                pub(dst + 2 + d, acc, tg);
               }
               if (tid == 0) {
-                pub_l2(dst + 0, nk > 0 ? mx[0] : -INFINITY, tg);
-                pub_l2(dst + 1, nk > 0 ? mx[1] : 0.f, tg);
+                pub(dst + 0, nk > 0 ? mx[0] : -INFINITY, tg);
+                pub(dst + 1, nk > 0 ? mx[1] : 0.f, tg);
               }
               __syncthreads();
             }
           }
-          // ------------------------------------------------ A3: merge partials + o-projection slice
+          // ---- A3: merge the 32 partials + o-projection columns of head x
           {
             const int plen = hd + 2;
-            float *part = L.work + 2048;           // [32][plen]
-            float *ov = L.work;                    // [NCOL][hd]
+            float *part = work + 2048;             // [32][plen]
+            float *ov = work;                      // [NCOL][hd]
             for (int c = 0; c < ncol; ++c) {
-              if (!gather2d<AUX_L2>(xo + c * m.x_o_len, 1, MK_NL * plen, 0, tg, part, L.flag, m.ctl, (step << 16) | (li << 8) | 7)) MK_BAIL();
-              for (int d = tid; d < hd; d += MK_THREADS) {
-                float M = -INFINITY;
-                for (int ww = 0; ww < MK_NL; ++ww)
-                  if (part[ww * plen + 1] > 0.f) M = fmaxf(M, part[ww * plen]);
-                float Ls = 0.f, acc = 0.f;
-                for (int ww = 0; ww < MK_NL; ++ww) {
-                  if (part[ww * plen + 1] > 0.f) {
-                    const float sc = expf(part[ww * plen] - M);
-                    Ls = fmaf(part[ww * plen + 1], sc, Ls);
-                    acc = fmaf(part[ww * plen + 2 + d], sc, acc);
-                  }
+              if (!gather2d<5>(xo + c * m.x_o_len, 1, MK_NL * plen, 0, tg, part, flag, m.ctl, SITE(7), tid)) MK_BAIL();
+              // per-partial scale exp(m_w - M) (0 for workgroups without keys), once, in wave 0
+              float *scl = part + MK_NL * plen;     // [32] scales, [32] = sum of l_w * scale
+              if (w8 == 0) {
+                const bool has = lane < MK_NL && part[lane * plen + 1] > 0.f;
+                float M = has ? part[lane * plen] : -INFINITY;
+#pragma unroll
+                for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+                const float sv = has ? expf(part[lane * plen] - M) : 0.f;
+                if (lane < MK_NL) scl[lane] = sv;
+                if (lane == 0) {  // (LDS writes of one wave are seen by its later reads)
+                  float Ls = 0.f;
+                  for (int ww = 0; ww < MK_NL; ++ww) Ls = fmaf(part[ww * plen + 1], scl[ww], Ls);
+                  scl[MK_NL] = Ls;
                 }
-                ov[c * hd + d] = acc / Ls;
+              }
+              __syncthreads();
+              for (int d = tid; d < hd; d += MK_THREADS) {
+                float acc = 0.f;
+#pragma unroll 8
+                for (int ww = 0; ww < MK_NL; ++ww) acc = fmaf(part[ww * plen + 2 + d], scl[ww], acc);
+                ov[c * hd + d] = acc / scl[MK_NL];
               }
               __syncthreads();
             }
-            const int G_o = mk_tile_G(hd), L_o = hd / 8 / G_o, RG_o = 64 / G_o;
-            const uint16_t *tile = ly.at_o + (size_t)x * H * hd;
-            const int nrg = H / RG_o;
-            for (int rg = wx; rg < nrg; rg += MK_NL * MK_WAVES) {
-              u32x4 wr[2];
-              rg_load<2>(tile, rg, L_o, wr);
+            if (wx < H / RG_a) {
               float oo[NCOL];
-              rg_dot<NCOL, 2>(wr, L_o, G_o, ov, hd, ncol, oo);
-              if ((lane & (G_o - 1)) == 0) {
-                const int row = rg * RG_o + lane / G_o;
-                FOR_COL(c) pub_dev(xmix + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
+              rg_dot<NCOL, 1>(w_out[0], 1, G_a, ov, hd, ncol, oo);
+              if ((lane & (G_a - 1)) == 0) {
+                const int row = wx * RG_a + lane / G_a;
+                FOR_COL(c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
               }
             }
           }
         } else {
           for (int i = tid + lw * MK_THREADS; i < H; i += MK_NL * MK_THREADS)
-            for (int c = 0; c < ncol; ++c) pub_dev(xmix + ((size_t)c * MK_NX + x) * H + i, 0.f, tg);
+            for (int c = 0; c < ncol; ++c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + i, 0.f, tg);
         }
       }
-      // ---------------------------------------------------- R1: residual += sum of the 8 mixer slices
+      // prefetch: gate/up rows of FFN slice x (F1), in flight during the residual reduction
       {
-        float *tmp = L.work;  // [NCOL*8][SL]
-        if (!gather2d<AUX_DEV>(ly.x_mix + lw * SL, ncol * MK_NX, SL, H, tg, tmp, L.flag, m.ctl, (step << 16) | (li << 8) | 8)) MK_BAIL();
+        const uint16_t *gu = ly.ffn_gu + (size_t)x * 2 * J * H;
+#pragma unroll
+        for (int pr = 0; pr < NPAIR; ++pr) {
+          const int j = wx + pr * XW;
+          if (j < J) {
+            if (RG_h == 1) {  // rows 2j (gate) and 2j+1 (up) are row groups of their own
+              const u32x4 *p = reinterpret_cast<const u32x4 *>(gu) + (size_t)(2 * j) * L_h * 64 + lane;
+#pragma unroll
+              for (int i = 0; i < 2; ++i)
+                if (i < L_h) {
+                  w_gu[2 * pr][i] = __builtin_nontemporal_load(p + i * 64);
+                  w_gu[2 * pr + 1][i] = __builtin_nontemporal_load(p + (L_h + i) * 64);
+                }
+            } else {          // RG_h == 2: one row group holds the pair
+              const u32x4 *p = reinterpret_cast<const u32x4 *>(gu) + (size_t)j * L_h * 64 + lane;
+#pragma unroll
+              for (int i = 0; i < 2; ++i)
+                if (i < L_h) w_gu[2 * pr][i] = __builtin_nontemporal_load(p + i * 64);
+            }
+          }
+        }
+      }
+      // ---- R1: residual += sum of the 8 mixer slices (reduce-scatter over XCDs, all-gather in the XCD)
+      {
+        float *tmp = work;  // [NCOL*8][SL]
+        if (!gather2d<MC2>(ly.x_mix + lw * SL, ncol * MK_NX, SL, H, tg, tmp, flag, m.ctl, SITE(8), tid)) MK_BAIL();
         uint2 *xr = ly.x_r1 + (size_t)x * MK_MAXCOL * H;
         for (int i = tid; i < ncol * SL; i += MK_THREADS) {
           const int c = i / SL, k = i - c * SL;
-          float s = tmp[(c * MK_NX) * SL + k];
+          float sm = tmp[(c * MK_NX) * SL + k];
 #pragma unroll
-          for (int g = 1; g < MK_NX; ++g) s += tmp[(c * MK_NX + g) * SL + k];
-          pub_l2(xr + c * H + lw * SL + k, L.xres[c * H + lw * SL + k] + s, tg);
+          for (int g = 1; g < MK_NX; ++g) sm += tmp[(c * MK_NX + g) * SL + k];
+          pub(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, tg);
         }
-        if (!gather2d<AUX_L2>(xr, ncol, H, H, tg, L.xres, L.flag, m.ctl, (step << 16) | (li << 8) | 9)) MK_BAIL();
+        if (!gather2d<NCOL>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(9), tid)) MK_BAIL();
       }
       // ================================================================ FFN
-      rmsnorm_cols<NCOL>(L.xres, L.hn, ly.ln2, H, m.rms_eps, ncol, L.red);
+      rmsnorm_cols_r<NCOL>(xres, hn, g2a, g2b, H, m.rms_eps, ncol, red, tid);
       {
-        const int J = m.J;
         uint2 *xm = ly.x_m + (size_t)x * MK_MAXCOL * J;
-        const uint16_t *gu = ly.ffn_gu + (size_t)x * 2 * J * H;
-        // F1: gate/up pairs j -> m_j = SiLU(g_j) * u_j
-        for (int j = wx; j < J; j += MK_NL * MK_WAVES) {
-          float g[NCOL], u[NCOL];
-          if (RG_h == 1) {
-            u32x4 wg[2], wu[2];
-            rg_load<2>(gu, 2 * j, L_h, wg);
-            rg_load<2>(gu, 2 * j + 1, L_h, wu);
-            rg_dot<NCOL, 2>(wg, L_h, G_h, L.hn, H, ncol, g);
-            rg_dot<NCOL, 2>(wu, L_h, G_h, L.hn, H, ncol, u);
-          } else {  // RG_h == 2: lanes [0,32) compute g_j, lanes [32,64) u_j
-            u32x4 wr[2];
-            rg_load<2>(gu, j, L_h, wr);
-            rg_dot<NCOL, 2>(wr, L_h, G_h, L.hn, H, ncol, g);
+        // ---- F1: gate/up pairs j -> m_j = SiLU(g_j) * u_j (weights already in flight)
 #pragma unroll
-            for (int c = 0; c < NCOL; ++c) u[c] = __shfl_xor(g[c], 32, 64);
-          }
-          if (lane == 0)
-            FOR_COL(c) {
-              pub_l2(xm + c * J + j, siluf_(g[c]) * u[c], tg);
+        for (int pr = 0; pr < NPAIR; ++pr) {
+          const int j = wx + pr * XW;
+          if (j < J) {
+            float g[NCOL], u[NCOL];
+            if (RG_h == 1) {
+              rg_dot<NCOL, 2>(w_gu[2 * pr], L_h, G_h, hn, H, ncol, g);
+              rg_dot<NCOL, 2>(w_gu[2 * pr + 1], L_h, G_h, hn, H, ncol, u);
+            } else {  // lanes [0,32) compute g_j, lanes [32,64) u_j
+              rg_dot<NCOL, 2>(w_gu[2 * pr], L_h, G_h, hn, H, ncol, g);
+#pragma unroll
+              for (int c = 0; c < NCOL; ++c) u[c] = __shfl_xor(g[c], 32, 64);
             }
+            if (lane == 0) FOR_COL(c) pub(xm + c * J + j, siluf_(g[c]) * u[c], tg);
+          }
         }
-        // F2: down-projection slice (columns x*J .. x*J+J of W_d)
-        float *mv = L.work;  // [NCOL][J]
-        if (!gather2d<AUX_L2>(xm, ncol, J, J, tg, mv, L.flag, m.ctl, (step << 16) | (li << 8) | 11)) MK_BAIL();
-        const int G_d = mk_tile_G(J), L_d = J / 8 / G_d, RG_d = 64 / G_d;
+        // prefetch: down-projection rows (F2), in flight during the m hand-off
         const uint16_t *tile = ly.ffn_dn + (size_t)x * H * J;
         const int nrg = H / RG_d;
-        for (int rg = wx; rg < nrg; rg += MK_NL * MK_WAVES) {
-          u32x4 wr[8];
-          rg_load<8>(tile, rg, L_d, wr);
+        if (wx < nrg) rg_issue<1, LMAX_D>(tile, wx, XW, nrg, L_d, w_dn);
+        // ---- F2: down-projection columns of slice x
+        float *mv = work;  // [NCOL][J]
+        if (!gather2d<NCOL>(xm, ncol, J, J, tg, mv, flag, m.ctl, SITE(11), tid)) MK_BAIL();
+        if (wx < nrg) {
           float oo[NCOL];
-          rg_dot<NCOL, 8>(wr, L_d, G_d, mv, J, ncol, oo);
+          rg_dot<NCOL, LMAX_D>(w_dn[0], L_d, G_d, mv, J, ncol, oo);
           if ((lane & (G_d - 1)) == 0) {
-            const int row = rg * RG_d + lane / G_d;
-            FOR_COL(c) pub_dev(ly.x_ffn + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
+            const int row = wx * RG_d + lane / G_d;
+            FOR_COL(c) pub(ly.x_ffn + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
           }
         }
       }
-      // ---------------------------------------------------- R2: residual += sum of the 8 FFN slices
+      // prefetch: the next layer's in-projection / QKV rows, in flight during the reduction
+      if (li + 1 < m.n_layers) {
+        issue_in(li + 1);
+        g1a = (tid < H) ? layers[li + 1].ln1[tid] : 0.f;
+        g1b = (tid + MK_THREADS < H) ? layers[li + 1].ln1[tid + MK_THREADS] : 0.f;
+      } else {
+        g1a = (tid < H) ? m.lnf[tid] : 0.f;     // the final norm's gains
+        g1b = (tid + MK_THREADS < H) ? m.lnf[tid + MK_THREADS] : 0.f;
+      }
+      // ---- R2: residual += sum of the 8 FFN slices
       {
-        float *tmp = L.work;
-        if (!gather2d<AUX_DEV>(ly.x_ffn + lw * SL, ncol * MK_NX, SL, H, tg, tmp, L.flag, m.ctl, (step << 16) | (li << 8) | 12)) MK_BAIL();
+        float *tmp = work;
+        if (!gather2d<MC2>(ly.x_ffn + lw * SL, ncol * MK_NX, SL, H, tg, tmp, flag, m.ctl, SITE(12), tid)) MK_BAIL();
         uint2 *xr = ly.x_r2 + (size_t)x * MK_MAXCOL * H;
         for (int i = tid; i < ncol * SL; i += MK_THREADS) {
           const int c = i / SL, k = i - c * SL;
-          float s = tmp[(c * MK_NX) * SL + k];
+          float sm = tmp[(c * MK_NX) * SL + k];
 #pragma unroll
-          for (int g = 1; g < MK_NX; ++g) s += tmp[(c * MK_NX + g) * SL + k];
-          pub_l2(xr + c * H + lw * SL + k, L.xres[c * H + lw * SL + k] + s, tg);
+          for (int g = 1; g < MK_NX; ++g) sm += tmp[(c * MK_NX + g) * SL + k];
+          pub(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, tg);
         }
-        if (!gather2d<AUX_L2>(xr, ncol, H, H, tg, L.xres, L.flag, m.ctl, (step << 16) | (li << 8) | 9)) MK_BAIL();
+        if (!gather2d<NCOL>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(13), tid)) MK_BAIL();
       }
     }  // layers
 
@@ -766,38 +1019,77 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       continue;
     }
     // ================================================================ LM head + greedy argmax
-    rmsnorm_cols<NCOL>(L.xres, L.hn, m.lnf, H, m.rms_eps, ncol, L.red);
+    rmsnorm_cols_r<NCOL>(xres, hn, g1a, g1b, H, m.rms_eps, ncol, red, tid0);
     {
       const int nrg_all = m.V / RG_h;
       const int g0 = (int)((long long)b * nrg_all / MK_NWG), g1 = (int)((long long)(b + 1) * nrg_all / MK_NWG);
       const int cnt = g1 - g0;
       const int wg0 = g0 + w8 * cnt / MK_WAVES, wg1 = g0 + (w8 + 1) * cnt / MK_WAVES;
+      constexpr int B = LM_BATCH(NCOL);
       float best[NCOL];
       int bidx[NCOL];
       int nanf = 0;
 #pragma unroll
       for (int c = 0; c < NCOL; ++c) { best[c] = -INFINITY; bidx[c] = 0x7fffffff; }
-      for (int rg = wg0; rg < wg1; ++rg) {
-        u32x4 wr[2];
-        rg_load<2>(m.embed, rg, L_h, wr);
-        float o[NCOL];
-        rg_dot<NCOL, 2>(wr, L_h, G_h, L.hn, H, ncol, o);
-        if ((lane & (G_h - 1)) == 0) {
-          const int row = rg * RG_h + lane / G_h;
+      // this lane's activations: elements (i*G_h + lane % G_h)*8 + e of load i (L_h <= 2)
+      float av[NCOL][16];
+      {
+        const int kl = (lane & (G_h - 1)) * 8;
 #pragma unroll
-          for (int c = 0; c < NCOL; ++c) {
-            if (c < ncol) {
-              if (a.logits) a.logits[(size_t)c * m.V + row] = o[c];
-              if (!(o[c] == o[c]) || isinf(o[c])) nanf = 1;
-              if (o[c] > best[c] || (o[c] == best[c] && row < bidx[c])) { best[c] = o[c]; bidx[c] = row; }
+        for (int c = 0; c < NCOL; ++c)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              av[c][i * 8 + e] = (c < ncol && i < L_h) ? hn[c * H + i * G_h * 8 + kl + e] : 0.f;
+      }
+      for (int rb = wg0; rb < wg1; rb += B) {
+        u32x4 wr[B][2];
+#pragma unroll
+        for (int r = 0; r < B; ++r) {
+          const u32x4 *p = reinterpret_cast<const u32x4 *>(m.embed) + (size_t)(rb + r) * L_h * 64 + lane;
+          if (rb + r < wg1) {
+            wr[r][0] = __builtin_nontemporal_load(p);
+            wr[r][1] = (L_h > 1) ? __builtin_nontemporal_load(p + 64) : u32x4{0u, 0u, 0u, 0u};
+          } else {
+            wr[r][0] = u32x4{0u, 0u, 0u, 0u};
+            wr[r][1] = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < NCOL; ++c) {
+          if (c >= ncol) break;
+          if (G_h == 64 && B == 8) {
+            float part[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) part[r] = dot16(wr[r][0], wr[r][1], av[c]);
+            const float tot = reduce8(part);           // lane l: row rb + (l >> 3)
+            const int row = rb + (lane >> 3);
+            if ((lane & 7) == 0 && row < wg1) {
+              if (a.logits) a.logits[(size_t)c * m.V + row] = tot;
+              if (!(tot == tot) || isinf(tot)) nanf = 1;
+              if (tot > best[c] || (tot == best[c] && row < bidx[c])) { best[c] = tot; bidx[c] = row; }
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < B; ++r) {
+              const int rg = rb + r;
+              const float pl = dot16(wr[r][0], wr[r][1], av[c]);
+              const float tot = (G_h == 64) ? wave_sum_lm(pl) : group_sum(pl, G_h);
+              const int row = rg * RG_h + lane / G_h;
+              if ((lane & (G_h - 1)) == 0 && rg < wg1) {
+                if (a.logits) a.logits[(size_t)c * m.V + row] = tot;
+                if (!(tot == tot) || isinf(tot)) nanf = 1;
+                if (tot > best[c] || (tot == best[c] && row < bidx[c])) { best[c] = tot; bidx[c] = row; }
+              }
             }
           }
         }
       }
       // wave reduce (value desc, index asc), then across waves
-      float *rv = L.work;                  // [NCOL][8]
-      int *ri = reinterpret_cast<int *>(L.work + 64);
-      int *rn = reinterpret_cast<int *>(L.work + 128);
+      float *rv = work;                  // [NCOL][8]
+      int *ri = reinterpret_cast<int *>(work + 64);
+      int *rn = reinterpret_cast<int *>(work + 128);
 #pragma unroll
       for (int c = 0; c < NCOL; ++c) {
         float bv = best[c];
@@ -810,7 +1102,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         }
         if (lane == 0) { rv[c * 8 + w8] = bv; ri[c * 8 + w8] = bi; }
       }
-      int anynan = __any(nanf) ? 1 : 0;
+      const int anynan = __any(nanf) ? 1 : 0;
       if (lane == 0) rn[w8] = anynan;
       __syncthreads();
       if (tid < ncol) {
@@ -822,37 +1114,37 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           nn |= rn[ww];
           if (rv[c * 8 + ww] > bv || (rv[c * 8 + ww] == bv && ri[c * 8 + ww] < bi)) { bv = rv[c * 8 + ww]; bi = ri[c * 8 + ww]; }
         }
-        uint4 rec = make_uint4(__float_as_uint(bv), (uint32_t)bi, tag, (uint32_t)nn);
-        __hip_atomic_store(reinterpret_cast<unsigned long long *>(m.x_arg + c * MK_NWG + b),
-                           ((unsigned long long)rec.y << 32) | rec.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        wait_stores();
-        __hip_atomic_store(reinterpret_cast<unsigned long long *>(m.x_arg + c * MK_NWG + b) + 1,
-                           ((unsigned long long)rec.w << 32) | rec.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned long long *rec = reinterpret_cast<unsigned long long *>(m.x_arg + c * MK_NWG + b);
+        __hip_atomic_store(rec, ((unsigned long long)(uint32_t)bi << 32) | __float_as_uint(bv), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        wait_stores();  // value and index land before the tag word
+        __hip_atomic_store(rec + 1, ((unsigned long long)(uint32_t)nn << 32) | tg, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();  // the candidate above was read from the scratch the final gather reuses
     if (b == 0) {
       // final argmax over the 256 workgroup candidates; the tag word is written after the
       // value/index word by the same thread, so a matching tag implies the record is complete
-      float *cv = L.work;                         // [NCOL][256]
-      int *ci = reinterpret_cast<int *>(L.work + NCOL * MK_NWG);
-      int *cn = reinterpret_cast<int *>(L.work + 2 * NCOL * MK_NWG);
-      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(m.x_arg, 0, MK_MAXCOL * MK_NWG * 16, RSRC_W3);
+      float *cv = work;                         // [NCOL][256]
+      int *ci = reinterpret_cast<int *>(work + NCOL * MK_NWG);
+      int *cn = reinterpret_cast<int *>(work + 2 * NCOL * MK_NWG);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(m.x_arg, 0, MK_MAXCOL * MK_NWG * 16, RSRC_W3);
       for (int i = tid; i < ncol * MK_NWG; i += MK_THREADS) {
         const unsigned long long deadline = wall_clock64() + MK_WAIT_TICKS;
         while (true) {
           const uint32_t tw = __builtin_amdgcn_raw_buffer_load_b32(rs, i * 16 + 8, 0, AUX_DEV);
-          if (tw == tag) break;
-          if (wall_clock64() > deadline) { L.flag[0] = 1; break; }
+          if (tw == tg) break;
+          if (wall_clock64() > deadline) { flag[0] = 1; break; }
           __builtin_amdgcn_s_sleep(1);
         }
-        u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, 0, AUX_DEV);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, 0, AUX_DEV);
         cv[i] = __uint_as_float(v.x);
         ci[i] = (int)v.y;
         cn[i] = (int)v.w;
       }
       __syncthreads();
-      if (L.flag[0]) MK_BAIL();
+      if (flag[0]) MK_BAIL();
       if (w8 == 0) {
         int gsel[MK_MAXCOL];
         int anynan = 0;
@@ -892,7 +1184,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             if (c < ncol) a.argmax[c] = gsel[c];
           if (a.n_acc) a.n_acc[0] = nacc;
           if (anynan) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_NAN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const int consumed = a.prefill ? a.n : (verify ? nacc : 1);
+          const int consumed = PROMPT ? a.n : (verify ? nacc : 1);
           __hip_atomic_store(m.ctl + MK_CTL_POS, ctl_pos + consumed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(m.ctl + MK_CTL_PEND, verify ? nacc : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(m.ctl + MK_CTL_PAR, verify ? (par ^ 1) : par, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
