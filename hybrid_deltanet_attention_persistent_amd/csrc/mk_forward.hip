@@ -46,6 +46,21 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// Workgroup barrier that orders LDS only.  A full barrier also waits for the wave's outstanding
+// global stores, and with them (one in-order counter) for every weight load issued before them;
+// no global data is handed between the waves of a workgroup, so an LDS-scope fence is enough and
+// prefetched weights stay in flight across the barrier.
+// Compiler-only memory barrier: keeps prefetch loads where they are issued.  The LDS-scope
+// barriers do not order global loads, so without it the compiler may sink a prefetch down to
+// its use and nothing is in flight during the hand-offs.
+__device__ __forceinline__ void keep_issued() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ void lbar() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ uint32_t f2bf(float f) {  // round to nearest even
   uint32_t u = __float_as_uint(f);
   u += 0x7fffu + ((u >> 16) & 1u);
@@ -108,11 +123,11 @@ __device__ __forceinline__ float group_sum(float v, int G) {  // sum over aligne
 __device__ __forceinline__ float block_sum(float v, float *red) {
   v = wave_sum(v);
   if (lane_id() == 0) red[wave_id()] = v;
-  __syncthreads();
+  lbar();
   float s = red[0];
 #pragma unroll
   for (int w = 1; w < MK_WAVES; ++w) s += red[w];
-  __syncthreads();
+  lbar();
   return s;
 }
 
@@ -122,73 +137,81 @@ __device__ __forceinline__ void pub(uint2 *p, float v, uint32_t tag) {
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Gather a [nrow][ncol] block of tagged slots (row stride `stride` slots, ncol even) into
-// dst[nrow][ncol] (LDS), polling until every tag equals `tag`.  Thread t polls 16-byte chunks
-// t, t + 512, ... (at most MAXC).  All threads call it; ends with a barrier.  On watchdog
-// expiry records the first failing site in the control block and returns false.
+// Watchdog expiry inside a gather: flag the workgroup and record the first failing site.
+__device__ __noinline__ void gather_timeout(int *fail, int32_t *ctl, int site, int tid, uint32_t seen, uint32_t tag) {
+  *fail = 1;
+  int expect = 0;
+  if (__hip_atomic_compare_exchange_strong(ctl + MK_CTL_WHERE, &expect, site | (1 << 30), __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(ctl + MK_CTL_WHERE + 1, (int)(blockIdx.x * 65536 + tid), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ctl + MK_CTL_WHERE + 2, (int)seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ctl + MK_CTL_WHERE + 3, (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Poll up to MAXC 16-byte chunks per lane (two tagged slots each) until both tags equal `tag`,
+// then store the two values to LDS.  Returns false on watchdog expiry.
 template <int MAXC>
+__device__ __forceinline__ bool poll_chunks(__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[MAXC], float *const (&dp)[MAXC],
+                                            uint32_t pend, uint32_t tag, int *fail, int32_t *ctl, int site, int tid) {
+  if (!pend) return true;
+  const unsigned long long deadline = wall_clock64() + MK_WAIT_TICKS;
+  while (true) {
+    u32x4 v[MAXC];
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j)
+      if (pend & (1u << j)) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[j], 0, AUX_DEV);
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+      if ((pend & (1u << j)) && v[j].y == tag && v[j].w == tag) {
+        dp[j][0] = __uint_as_float(v[j].x);
+        dp[j][1] = __uint_as_float(v[j].z);
+        pend &= ~(1u << j);
+      }
+    }
+    if (!pend) return true;
+    if (wall_clock64() > deadline) {
+      uint32_t seen = 0;
+#pragma unroll
+      for (int j = MAXC - 1; j >= 0; --j)
+        if (pend & (1u << j)) seen = v[j].y;
+      gather_timeout(fail, ctl, site, tid, seen, tag);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Gather a [nrow][ncol] block of tagged slots (row stride `stride` slots, ncol even) into
+// dst[nrow][ncol] (LDS), polling until every tag equals `tag`.  Only the last NPW waves poll, in
+// rounds of MAXC chunks per lane: a wave that polls waits for every older load of its own, so the
+// waves that keep weight loads in flight stay out of it.  Every thread calls it; it ends with a
+// barrier.  On watchdog expiry records the first failing site in the control block and returns false.
+template <int MAXC, int NPW>
 __device__ bool gather2d(const uint2 *src, int nrow, int ncol, int stride, uint32_t tag, float *dst, int *fail,
                          int32_t *ctl, int site, int tid) {
   const int half = ncol >> 1;
   const int nchunk = nrow * half;
-  const uint32_t bytes = (uint32_t)(((nrow - 1) * stride + ncol) * 8);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, bytes, RSRC_W3);
-  if (nchunk > MAXC * MK_THREADS) {  // more slots than this call site polls: a layout bug, never a hang
-    if (tid == 0) {
-      *fail = 1;
-      int expect = 0;
-      __hip_atomic_compare_exchange_strong(ctl + MK_CTL_WHERE, &expect, site | (1 << 29), __ATOMIC_RELAXED,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    return false;
-  }
-  uint32_t off[MAXC];
-  int di[MAXC];
-  uint32_t pend = 0;
-#pragma unroll
-  for (int j = 0; j < MAXC; ++j) {
-    const int c = tid + j * MK_THREADS;
-    const int r = c / half, q = c - r * half;
-    off[j] = (uint32_t)((r * stride + 2 * q) * 8);
-    di[j] = r * ncol + 2 * q;
-    if (c < nchunk) pend |= 1u << j;
-  }
-  if (pend) {
-    const unsigned long long deadline = wall_clock64() + MK_WAIT_TICKS;
-    while (true) {
-      u32x4 v[MAXC];
-#pragma unroll
-      for (int j = 0; j < MAXC; ++j)
-        if (pend & (1u << j)) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[j], 0, AUX_DEV);
+  const int pt = tid - (MK_WAVES - NPW) * 64;   // index among the polling threads
+  if (pt >= 0) {
+    const uint32_t bytes = (uint32_t)(((nrow - 1) * stride + ncol) * 8);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, bytes, RSRC_W3);
+    for (int base = 0; base < nchunk; base += MAXC * NPW * 64) {
+      uint32_t off[MAXC];
+      float *dp[MAXC];
+      uint32_t pend = 0;
 #pragma unroll
       for (int j = 0; j < MAXC; ++j) {
-        if ((pend & (1u << j)) && v[j].y == tag && v[j].w == tag) {
-          dst[di[j]] = __uint_as_float(v[j].x);
-          dst[di[j] + 1] = __uint_as_float(v[j].z);
-          pend &= ~(1u << j);
-        }
+        const int c = base + pt + j * NPW * 64;
+        const int r = c / half, q = c - r * half;
+        off[j] = (uint32_t)((r * stride + 2 * q) * 8);
+        dp[j] = dst + r * ncol + 2 * q;
+        if (c < nchunk) pend |= 1u << j;
       }
-      if (!pend) break;
-      if (wall_clock64() > deadline) {
-        *fail = 1;
-        uint32_t seen = 0;
-#pragma unroll
-        for (int j = MAXC - 1; j >= 0; --j)
-          if (pend & (1u << j)) seen = v[j].y;
-        int expect = 0;
-        if (__hip_atomic_compare_exchange_strong(ctl + MK_CTL_WHERE, &expect, site | (1 << 30), __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-          __hip_atomic_store(ctl + MK_CTL_WHERE + 1, (int)(blockIdx.x * 65536 + tid), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(ctl + MK_CTL_WHERE + 2, (int)seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(ctl + MK_CTL_WHERE + 3, (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+      if (!poll_chunks<MAXC>(rs, off, dp, pend, tag, fail, ctl, site, tid)) break;
     }
   }
-  __syncthreads();
+  lbar();
   return *fail == 0;
 }
 
@@ -200,96 +223,75 @@ struct GSeg {
 };
 
 // Gather several blocks (all addressed from one base) in one polling loop and one barrier.
-template <int MAXC, int NSEG>
+template <int MAXC, int NPW, int NSEG>
 __device__ bool gather_segs(const uint2 *base, const GSeg (&sg)[NSEG], uint32_t tag, int *fail, int32_t *ctl,
                             int site, int tid) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, 0x7fffffff, RSRC_W3);
   int total = 0;
 #pragma unroll
   for (int s = 0; s < NSEG; ++s) total += sg[s].nrow * (sg[s].ncol >> 1);
-  if (total > MAXC * MK_THREADS) {
-    if (tid == 0) {
-      *fail = 1;
-      int expect = 0;
-      __hip_atomic_compare_exchange_strong(ctl + MK_CTL_WHERE, &expect, site | (1 << 29), __ATOMIC_RELAXED,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    return false;
-  }
-  uint32_t off[MAXC];
-  float *dp[MAXC];
-  uint32_t pend = 0;
-#pragma unroll
-  for (int j = 0; j < MAXC; ++j) {
-    int c = tid + j * MK_THREADS;
-    off[j] = 0;
-    dp[j] = nullptr;
-    if (c < total) {
-      pend |= 1u << j;
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s) {
-        const int half = sg[s].ncol >> 1, n = sg[s].nrow * half;
-        if (c >= 0 && c < n) {
-          const int r = c / half, q = c - r * half;
-          off[j] = (uint32_t)((sg[s].off + r * sg[s].stride + 2 * q) * 8);
-          dp[j] = sg[s].dst + r * sg[s].ncol + 2 * q;
-        }
-        c -= n;
-      }
-    }
-  }
-  if (pend) {
-    const unsigned long long deadline = wall_clock64() + MK_WAIT_TICKS;
-    while (true) {
-      u32x4 v[MAXC];
-#pragma unroll
-      for (int j = 0; j < MAXC; ++j)
-        if (pend & (1u << j)) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[j], 0, AUX_DEV);
+  const int pt = tid - (MK_WAVES - NPW) * 64;
+  if (pt >= 0) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, 0x7fffffff, RSRC_W3);
+    for (int b0 = 0; b0 < total; b0 += MAXC * NPW * 64) {
+      uint32_t off[MAXC];
+      float *dp[MAXC];
+      uint32_t pend = 0;
 #pragma unroll
       for (int j = 0; j < MAXC; ++j) {
-        if ((pend & (1u << j)) && v[j].y == tag && v[j].w == tag) {
-          dp[j][0] = __uint_as_float(v[j].x);
-          dp[j][1] = __uint_as_float(v[j].z);
-          pend &= ~(1u << j);
-        }
-      }
-      if (!pend) break;
-      if (wall_clock64() > deadline) {
-        *fail = 1;
-        uint32_t seen = 0;
+        int c = b0 + pt + j * NPW * 64;
+        off[j] = 0;
+        dp[j] = nullptr;
+        if (c < total) {
+          pend |= 1u << j;
 #pragma unroll
-        for (int j = MAXC - 1; j >= 0; --j)
-          if (pend & (1u << j)) seen = v[j].y;
-        int expect = 0;
-        if (__hip_atomic_compare_exchange_strong(ctl + MK_CTL_WHERE, &expect, site | (1 << 30), __ATOMIC_RELAXED,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-          __hip_atomic_store(ctl + MK_CTL_WHERE + 1, (int)(blockIdx.x * 65536 + tid), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(ctl + MK_CTL_WHERE + 2, (int)seen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(ctl + MK_CTL_WHERE + 3, (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int s = 0; s < NSEG; ++s) {
+            const int half = sg[s].ncol >> 1, n = sg[s].nrow * half;
+            if (c >= 0 && c < n) {
+              const int r = c / half, q = c - r * half;
+              off[j] = (uint32_t)((sg[s].off + r * sg[s].stride + 2 * q) * 8);
+              dp[j] = sg[s].dst + r * sg[s].ncol + 2 * q;
+            }
+            c -= n;
+          }
         }
-        break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      if (!poll_chunks<MAXC>(rs, off, dp, pend, tag, fail, ctl, site, tid)) break;
     }
   }
-  __syncthreads();
+  lbar();
   return *fail == 0;
 }
 
 // ------------------------------------------------------------------------------ GEMV on tiles
-// Issue the loads of up to NRG row groups rg = first + i*stride (< end) of a tile: L loads per lane each.
+#define AUX_NT 2                    // non-temporal: weights are streamed once per token
+#define OOB_OFF 0x80000000u         // a buffer offset beyond every tile: the load reads zeros, touches no memory
+
+// Buffer descriptor of a weight tile of `bytes` bytes (0: every load reads zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, RSRC_W3);
+}
+
+// Element i of a float vector of n elements, branch-free (0 for i >= n).
+__device__ __forceinline__ float ld_gain(const float *p, int n, int i) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(p, (uint32_t)(n * 4)), (uint32_t)(i * 4), 0, 0));
+}
+
+// Prefetch up to NRG row groups rg = first + r*stride (valid below `end`) of a tile, L (<= LMAX)
+// 16-byte loads per lane each.  Branch-free: every slot issues one load, an invalid slot with an
+// out-of-range offset.  Straight-line loads let the compiler count exactly how many younger loads
+// may stay in flight when one is consumed; a branch around a load makes it wait for all of them.
 template <int NRG, int LMAX>
-__device__ __forceinline__ void rg_issue(const uint16_t *tile, int first, int stride, int end, int L,
+__device__ __forceinline__ void rg_issue(__amdgpu_buffer_rsrc_t rs, int first, int stride, int end, int L,
                                          u32x4 (&w)[NRG][LMAX]) {
+  const int lane = lane_id();
 #pragma unroll
   for (int r = 0; r < NRG; ++r) {
     const int rg = first + r * stride;
-    if (rg < end) {
-      const u32x4 *p = reinterpret_cast<const u32x4 *>(tile) + (size_t)rg * L * 64 + lane_id();
 #pragma unroll
-      for (int i = 0; i < LMAX; ++i)
-        if (i < L) w[r][i] = __builtin_nontemporal_load(p + i * 64);
+    for (int i = 0; i < LMAX; ++i) {
+      const bool ok = rg < end && i < L;
+      const uint32_t off = ok ? (uint32_t)(((rg * L + i) * 64 + lane) * 16) : OOB_OFF;
+      w[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, AUX_NT);
     }
   }
 }
@@ -385,7 +387,7 @@ __device__ void rmsnorm_cols(const float *src, float *dst, const float *g, int H
     const float den = sqrtf(tot / (float)H + eps);
     for (int k = threadIdx.x; k < H; k += MK_THREADS) dst[c * H + k] = src[c * H + k] / den * g[k];
   }
-  __syncthreads();
+  lbar();
 }
 
 // RMSNorm with the gains already in registers: thread t owns elements t and t + 512 (H <= 1024).
@@ -402,7 +404,7 @@ __device__ void rmsnorm_cols_r(const float *src, float *dst, float g0, float g1,
     if (tid < H) dst[c * H + tid] = src[c * H + tid] / den * g0;
     if (tid + MK_THREADS < H) dst[c * H + tid + MK_THREADS] = src[c * H + tid + MK_THREADS] / den * g1;
   }
-  __syncthreads();
+  lbar();
 }
 
 // loop over the live columns with compile-time indices (register arrays stay in registers)
@@ -430,8 +432,13 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // index derived from it is scalar too
   const int w8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id(), tid = threadIdx.x, tid0 = threadIdx.x;
-  const int wx = lw * MK_WAVES + w8;          // wave index inside the XCD, 0..255
-  const int XW = MK_NL * MK_WAVES;            // waves per XCD
+  // Decode and prompt: waves 0..6 stream weight rows, wave 7 polls the hand-offs (it holds no
+  // weight loads, so its polls never wait behind them).  Verify: all 8 waves do both.
+  constexpr int CW = (NCOL == 1) ? MK_WAVES - 1 : MK_WAVES;   // weight-streaming waves
+  constexpr int NPW = (CW < MK_WAVES) ? MK_WAVES - CW : MK_WAVES;   // polling waves
+  constexpr int NRG_O = (CW < MK_WAVES) ? 2 : 1;               // out-projection row groups per wave
+  const int wx = (w8 < CW) ? lw * CW + w8 : (1 << 24);        // streaming-wave index inside the XCD
+  const int XW = MK_NL * CW;                                   // streaming waves per XCD
   const int H = m.H;
   // the layer table is read-only: reading it through the constant address space gives
   // scalar loads, so every pointer taken from it is known to be wave-uniform
@@ -448,7 +455,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
     if ((int)(xcc & 7) != x) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_XCD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
+  lbar();
 
   const int ctl_pos = __hip_atomic_load(m.ctl + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int pend_n = __hip_atomic_load(m.ctl + MK_CTL_PEND, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -462,36 +469,57 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   const int G_o = mk_tile_G(dv), RG_o = 64 / G_o;        // out-projection columns of one head: L == 1
   const int G_a = mk_tile_G(hd), RG_a = 64 / G_a;        // o-projection columns of one head: L == 1
   const int G_d = mk_tile_G(J), L_d = J / 8 / G_d, RG_d = 64 / G_d;
-  constexpr int MC2 = NCOL == 1 ? 1 : 2;                 // polled chunks per thread of the larger gathers
+  constexpr int MCS = (NPW == 1) ? 4 : (NCOL == 1 ? 1 : 2);   // polled chunks per lane and round: small gathers
+  constexpr int MCL = (NPW == 1) ? 8 : NCOL;                  // ... gathers of whole hidden vectors
 
   // prefetched weight rows (registers), one phase ahead of their use
   u32x4 w_in[NRG_IN][2];      // D1 / A1
-  u32x4 w_out[1][1];          // D3 / A3
-  u32x4 w_gu[NPAIR * 2][2];   // F1 (gate, up of up to NPAIR pairs)
+  u32x4 w_out[NRG_O][1];      // D3 / A3
+  u32x4 w_gu[NPAIR][4];       // F1 (gate and up rows of up to NPAIR pairs)
   u32x4 w_dn[1][LMAX_D];      // F2
 
-  // in-projection (DeltaNet) or QKV (attention) rows of layer li for this wave
-  auto issue_in = [&](int li) {
-    ConstLayer &ly = layers[li];
-    if (ly.kind == 0) {
-      if (x < nh) rg_issue<NRG_IN, 2>(ly.dn_in + (size_t)x * m.r_in * H, wx, XW, m.r_in / RG_h, L_h, w_in);
-    } else if (x < nq) {
-      const int per = hd / RG_h;
+  // in-projection (DeltaNet) or QKV (attention) rows of layer li for this wave, branch-free: the
+  // tile of each slot is selected with scalar selects and absent rows read as zeros
+  auto issue_in = [&](int li) {   // li == n_layers: nothing to load (every slot reads zeros)
+    const bool live = li < m.n_layers;
+    ConstLayer &ly = layers[live ? li : 0];
+    const bool dn = ly.kind == 0;
+    const int per = hd / RG_h;                     // row groups of one attention head
+    const int nrg = !live ? 0 : dn ? ((x < nh) ? m.r_in / RG_h : 0) : ((x < nq) ? 3 * per : 0);
 #pragma unroll
-      for (int r = 0; r < NRG_IN; ++r) {
-        const int u = wx + r * XW;
-        if (u < 3 * per) {
-          const int t = u / per, rg = u - t * per;
-          const uint16_t *tile = (t == 0) ? ly.at_q + (size_t)x * hd * H
-                               : (t == 1) ? ly.at_k + (size_t)(x * nkv / nq) * hd * H
-                                          : ly.at_v + (size_t)(x * nkv / nq) * hd * H;
-          const u32x4 *p = reinterpret_cast<const u32x4 *>(tile) + (size_t)rg * L_h * 64 + lane;
+    for (int r = 0; r < NRG_IN; ++r) {
+      const int u = wx + r * XW;
+      const int t = dn ? 0 : min(u / per, 2), rg = dn ? u : u - t * per;
+      const uint16_t *tile = dn ? ly.dn_in + (size_t)x * m.r_in * H
+                           : (t == 0) ? ly.at_q + (size_t)x * hd * H
+                           : (t == 1) ? ly.at_k + (size_t)(x * nkv / nq) * hd * H
+                                      : ly.at_v + (size_t)(x * nkv / nq) * hd * H;
+      const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, (u < nrg) ? (uint32_t)((rg + 1) * L_h * 1024) : 0u);
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-            if (i < L_h) w_in[r][i] = __builtin_nontemporal_load(p + i * 64);
-        }
+      for (int i = 0; i < 2; ++i) {
+        const bool ok = u < nrg && i < L_h;
+        const uint32_t off = ok ? (uint32_t)(((rg * L_h + i) * 64 + lane) * 16) : OOB_OFF;
+        w_in[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, AUX_NT);
       }
     }
+    keep_issued();
+  };
+  // gate/up rows of FFN slice x for this wave: pair j = rows 2j, 2j+1, contiguous in the tile
+  // (two row groups when a row group is one row, one when it is two), 2 L_h / RG_h loads
+  auto issue_gu = [&](ConstLayer &ly) {
+    const int nl = 2 * L_h / RG_h;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(ly.ffn_gu + (size_t)x * 2 * J * H, (uint32_t)(2 * J * H * 2));
+#pragma unroll
+    for (int pr = 0; pr < NPAIR; ++pr) {
+      const int j = wx + pr * XW;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = j < J && i < nl;
+        const uint32_t off = ok ? (uint32_t)(((j * nl + i) * 64 + lane) * 16) : OOB_OFF;
+        w_gu[pr][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, AUX_NT);
+      }
+    }
+    keep_issued();
   };
 
   for (int step = 0; step < nsteps; ++step) {
@@ -500,9 +528,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     const bool last_step = step == nsteps - 1;
     int li = 0;
 
+    float g1a = ld_gain(layers[0].ln1, H, tid);            // gains of the next RMSNorm
+    float g1b = ld_gain(layers[0].ln1, H, tid + MK_THREADS);
     issue_in(0);
-    float g1a = (tid < H) ? layers[0].ln1[tid] : 0.f;      // gains of the next RMSNorm
-    float g1b = (tid + MK_THREADS < H) ? layers[0].ln1[tid + MK_THREADS] : 0.f;
     // ---- embedding rows
     for (int c = 0; c < ncol; ++c) {
       int t = a.tokens[PROMPT ? step : c];
@@ -513,7 +541,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       const uint16_t *row = m.embed + (size_t)t * H;
       for (int k = tid; k < H; k += MK_THREADS) xres[c * H + k] = bfv(row[k]);
     }
-    __syncthreads();
+    lbar();
 
     for (li = 0; li < m.n_layers; ++li) {
       ConstLayer &ly = layers[li];
@@ -524,8 +552,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       asm volatile("" : "+v"(tid));
       const int lane = tid & 63;
       // gains of this layer's FFN norm, needed after the mixer
-      const float g2a = (tid < H) ? ly.ln2[tid] : 0.f;
-      const float g2b = (tid + MK_THREADS < H) ? ly.ln2[tid + MK_THREADS] : 0.f;
+      const float g2a = ld_gain(ly.ln2, H, tid);
+      const float g2b = ld_gain(ly.ln2, H, tid + MK_THREADS);
       rmsnorm_cols_r<NCOL>(xres, hn, g1a, g1b, H, m.rms_eps, ncol, red, tid);
       if (ly.kind == 0) {
         // ================================================ DeltaNet layer
@@ -548,7 +576,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             }
           }
           // prefetch: the out-projection rows (D3)
-          if (wx < H / RG_o) rg_issue<1, 1>(ly.dn_out + (size_t)x * H * dv, wx, XW, H / RG_o, 1, w_out);
+          rg_issue<NRG_O, 1>(tile_rsrc(ly.dn_out + (size_t)x * H * dv, (uint32_t)(H * dv * 2)), wx, XW, H / RG_o, 1, w_out);
+          keep_issued();
         }
         // ---- D2: conv, norms, gates, delta rule on my RW rows of S
         float *qk = work;                         // [NCOL][2dk]
@@ -589,7 +618,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             const GSeg sg[3] = {{0, ncol, 2 * dk, m.r_in_max, qk},                 // q, k pre-conv
                                 {2 * dk + r0, ncol, RW, m.r_in_max, vr},           // my v rows
                                 {2 * dk + 2 * dv, ncol, 2, m.r_in_max, ab}};       // a, b
-            if (!gather_segs<MC2, 3>(xin, sg, tg, flag, m.ctl, SITE(1), tid)) MK_BAIL();
+            if (!gather_segs<MCS, NPW, 3>(xin, sg, tg, flag, m.ctl, SITE(1), tid)) MK_BAIL();
           }
           // conv + SiLU: threads [0, 2dk) are the q/k channels of head x, [2dk, 2dk+RW) my v channels
           {
@@ -621,7 +650,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 FOR_COL(c) ly.ring[((pos0 + c) & (MK_RING - 1)) * m.C + ch] = raw[c];
             }
           }
-          __syncthreads();
+          lbar();
           // L2 norms of q and k (wave w handles ranges w, w+8, ...), gates
           for (int r = w8; r < 2 * ncol; r += MK_WAVES) {
             const int c = r >> 1, which = r & 1;
@@ -635,10 +664,10 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             gts[tid * 2 + 0] = expf(-softplusf_(ab[tid * 2 + 0]));
             gts[tid * 2 + 1] = sigmoidf_(ab[tid * 2 + 1]);
           }
-          __syncthreads();
+          lbar();
           for (int i = tid; i < ncol * 2 * dk; i += MK_THREADS)
             qk[i] = qk[i] / nrm[(i / (2 * dk)) * 2 + ((i % (2 * dk)) >= dk)];
-          __syncthreads();
+          lbar();
           // delta rule: S_r <- alpha S_r + beta (v_r - alpha S_r.k) k ; o_r = S_r.q (rows are independent)
           if (act) {
             const int J2 = dk / 64;
@@ -686,7 +715,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               if (tid < RW) pc[dk + r0 + tid] = vr[c * RW + tid];
             }
           }
-          __syncthreads();
+          lbar();
           // a prompt's next token reads the ring written here (other workgroups of the XCD); decode
           // and verify state is read by the next launch only
           if (PROMPT) wait_stores();
@@ -702,7 +731,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           {
             const GSeg sg[2] = {{(int)(xo - xin), ncol, dv, m.x_o_len, o},       // o rows of the head
                                 {2 * dk + dv, ncol, dv, m.r_in_max, z}};         // z of the head
-            if (!gather_segs<MC2, 2>(xin, sg, tg, flag, m.ctl, SITE(4), tid)) MK_BAIL();
+            if (!gather_segs<MCS, NPW, 2>(xin, sg, tg, flag, m.ctl, SITE(4), tid)) MK_BAIL();
           }
           for (int c = 0; c < ncol; ++c) {
             float sq = 0.f;
@@ -710,13 +739,17 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             const float den = sqrtf(block_sum(sq, red) / (float)dv + m.rms_eps);
             if (tid < dv) o[c * dv + tid] = o[c * dv + tid] / den * gn * siluf_(z[c * dv + tid]);
           }
-          __syncthreads();
-          if (wx < H / RG_o) {
-            float oo[NCOL];
-            rg_dot<NCOL, 1>(w_out[0], 1, G_o, o, dv, ncol, oo);
-            if ((lane & (G_o - 1)) == 0) {
-              const int row = wx * RG_o + lane / G_o;
-              FOR_COL(c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
+          lbar();
+#pragma unroll
+          for (int r = 0; r < NRG_O; ++r) {
+            const int rg = wx + r * XW;
+            if (rg < H / RG_o) {
+              float oo[NCOL];
+              rg_dot<NCOL, 1>(w_out[r], 1, G_o, o, dv, ncol, oo);
+              if ((lane & (G_o - 1)) == 0) {
+                const int row = rg * RG_o + lane / G_o;
+                FOR_COL(c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
+              }
             }
           }
         } else {
@@ -744,10 +777,11 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               }
             }
           }
-          if (wx < H / RG_a) rg_issue<1, 1>(ly.at_o + (size_t)x * H * hd, wx, XW, H / RG_a, 1, w_out);
+          rg_issue<NRG_O, 1>(tile_rsrc(ly.at_o + (size_t)x * H * hd, (uint32_t)(H * hd * 2)), wx, XW, H / RG_a, 1, w_out);
+          keep_issued();
           // ---- A2: RoPE, KV append, split-KV partials
           float *qkv = work;                    // [NCOL][3hd]
-          if (!gather2d<2>(xin, ncol, 3 * hd, m.r_in_max, tg, qkv, flag, m.ctl, SITE(6), tid)) MK_BAIL();
+          if (!gather2d<MCS, NPW>(xin, ncol, 3 * hd, m.r_in_max, tg, qkv, flag, m.ctl, SITE(6), tid)) MK_BAIL();
           {
             const int half = hd / 2;
             for (int i = tid; i < ncol * half; i += MK_THREADS) {
@@ -762,11 +796,13 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               v[d] = rbf(v[d]); v[d + half] = rbf(v[d + half]);
             }
           }
-          __syncthreads();
-          if (lw == 0 && (x * nkv) % nq == 0) {   // first query head of the kv group appends K, V
+          lbar();
+          // first query head of the kv group appends K, V; with a polling wave, that wave does it
+          // (its wait for the stores then waits for no weight loads)
+          if (lw == 0 && (x * nkv) % nq == 0 && w8 >= MK_WAVES - NPW) {
             const __amdgpu_buffer_rsrc_t kst = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
             const __amdgpu_buffer_rsrc_t vst = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
-            for (int i = tid; i < ncol * hd; i += MK_THREADS) {
+            for (int i = tid - (MK_WAVES - NPW) * 64; i < ncol * hd; i += NPW * 64) {
               const int c = i / hd, d = i - c * hd;
               const int p = pos0 + c;
               const size_t off = (((size_t)m.page_table[p / MK_PAGE] * nkv + kvh) * MK_PAGE + (p % MK_PAGE)) * hd + d;
@@ -818,7 +854,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 sdot = group_sum(sdot, lpk);
                 if (ks < nk && (lane % lpk) == 0) sc[ks] = sdot * scale;
               }
-              __syncthreads();
+              lbar();
               if (w8 == 0) {
                 float mv = -INFINITY;
                 for (int i = lane; i < nk; i += 64) mv = fmaxf(mv, sc[i]);
@@ -833,7 +869,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 ls = wave_sum(ls);
                 if (lane == 0) { mx[0] = mv; mx[1] = ls; }
               }
-              __syncthreads();
+              lbar();
               // P.V: wave w takes keys w, w+8, ...; lanes take dims
               for (int d = lane; d < hd; d += 64) {
                 float acc = 0.f;
@@ -853,7 +889,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 }
                 pv[w8 * hd + d] = acc;
               }
-              __syncthreads();
+              lbar();
               const int plen = hd + 2;
               uint2 *dst = xo + c * m.x_o_len + lw * plen;
               for (int d = tid; d < hd; d += MK_THREADS) {
@@ -866,7 +902,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 pub(dst + 0, nk > 0 ? mx[0] : -INFINITY, tg);
                 pub(dst + 1, nk > 0 ? mx[1] : 0.f, tg);
               }
-              __syncthreads();
+              lbar();
             }
           }
           // ---- A3: merge the 32 partials + o-projection columns of head x
@@ -875,7 +911,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             float *part = work + 2048;             // [32][plen]
             float *ov = work;                      // [NCOL][hd]
             for (int c = 0; c < ncol; ++c) {
-              if (!gather2d<5>(xo + c * m.x_o_len, 1, MK_NL * plen, 0, tg, part, flag, m.ctl, SITE(7), tid)) MK_BAIL();
+              if (!gather2d<5, MK_WAVES>(xo + c * m.x_o_len, 1, MK_NL * plen, 0, tg, part, flag, m.ctl, SITE(7), tid)) MK_BAIL();
               // per-partial scale exp(m_w - M) (0 for workgroups without keys), once, in wave 0
               float *scl = part + MK_NL * plen;     // [32] scales, [32] = sum of l_w * scale
               if (w8 == 0) {
@@ -891,21 +927,25 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                   scl[MK_NL] = Ls;
                 }
               }
-              __syncthreads();
+              lbar();
               for (int d = tid; d < hd; d += MK_THREADS) {
                 float acc = 0.f;
 #pragma unroll 8
                 for (int ww = 0; ww < MK_NL; ++ww) acc = fmaf(part[ww * plen + 2 + d], scl[ww], acc);
                 ov[c * hd + d] = acc / scl[MK_NL];
               }
-              __syncthreads();
+              lbar();
             }
-            if (wx < H / RG_a) {
-              float oo[NCOL];
-              rg_dot<NCOL, 1>(w_out[0], 1, G_a, ov, hd, ncol, oo);
-              if ((lane & (G_a - 1)) == 0) {
-                const int row = wx * RG_a + lane / G_a;
-                FOR_COL(c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
+#pragma unroll
+            for (int r = 0; r < NRG_O; ++r) {
+              const int rg = wx + r * XW;
+              if (rg < H / RG_a) {
+                float oo[NCOL];
+                rg_dot<NCOL, 1>(w_out[r], 1, G_a, ov, hd, ncol, oo);
+                if ((lane & (G_a - 1)) == 0) {
+                  const int row = rg * RG_a + lane / G_a;
+                  FOR_COL(c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
+                }
               }
             }
           }
@@ -915,33 +955,13 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         }
       }
       // prefetch: gate/up rows of FFN slice x (F1), in flight during the residual reduction
-      {
-        const uint16_t *gu = ly.ffn_gu + (size_t)x * 2 * J * H;
-#pragma unroll
-        for (int pr = 0; pr < NPAIR; ++pr) {
-          const int j = wx + pr * XW;
-          if (j < J) {
-            if (RG_h == 1) {  // rows 2j (gate) and 2j+1 (up) are row groups of their own
-              const u32x4 *p = reinterpret_cast<const u32x4 *>(gu) + (size_t)(2 * j) * L_h * 64 + lane;
-#pragma unroll
-              for (int i = 0; i < 2; ++i)
-                if (i < L_h) {
-                  w_gu[2 * pr][i] = __builtin_nontemporal_load(p + i * 64);
-                  w_gu[2 * pr + 1][i] = __builtin_nontemporal_load(p + (L_h + i) * 64);
-                }
-            } else {          // RG_h == 2: one row group holds the pair
-              const u32x4 *p = reinterpret_cast<const u32x4 *>(gu) + (size_t)j * L_h * 64 + lane;
-#pragma unroll
-              for (int i = 0; i < 2; ++i)
-                if (i < L_h) w_gu[2 * pr][i] = __builtin_nontemporal_load(p + i * 64);
-            }
-          }
-        }
-      }
+      issue_gu(ly);
       // ---- R1: residual += sum of the 8 mixer slices (reduce-scatter over XCDs, all-gather in the XCD)
       {
-        float *tmp = work;  // [NCOL*8][SL]
-        if (!gather2d<MC2>(ly.x_mix + lw * SL, ncol * MK_NX, SL, H, tg, tmp, flag, m.ctl, SITE(8), tid)) MK_BAIL();
+        // [NCOL*8][SL], apart from everything the mixer phases read: the polling wave fills it
+        // while the other waves may still be reading the out-projection operand
+        float *tmp = work + 6400;
+        if (!gather2d<MCS, NPW>(ly.x_mix + lw * SL, ncol * MK_NX, SL, H, tg, tmp, flag, m.ctl, SITE(8), tid)) MK_BAIL();
         uint2 *xr = ly.x_r1 + (size_t)x * MK_MAXCOL * H;
         for (int i = tid; i < ncol * SL; i += MK_THREADS) {
           const int c = i / SL, k = i - c * SL;
@@ -950,7 +970,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           for (int g = 1; g < MK_NX; ++g) sm += tmp[(c * MK_NX + g) * SL + k];
           pub(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, tg);
         }
-        if (!gather2d<NCOL>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(9), tid)) MK_BAIL();
+        if (!gather2d<MCL, NPW>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(9), tid)) MK_BAIL();
       }
       // ================================================================ FFN
       rmsnorm_cols_r<NCOL>(xres, hn, g2a, g2b, H, m.rms_eps, ncol, red, tid);
@@ -962,11 +982,14 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           const int j = wx + pr * XW;
           if (j < J) {
             float g[NCOL], u[NCOL];
-            if (RG_h == 1) {
-              rg_dot<NCOL, 2>(w_gu[2 * pr], L_h, G_h, hn, H, ncol, g);
-              rg_dot<NCOL, 2>(w_gu[2 * pr + 1], L_h, G_h, hn, H, ncol, u);
-            } else {  // lanes [0,32) compute g_j, lanes [32,64) u_j
-              rg_dot<NCOL, 2>(w_gu[2 * pr], L_h, G_h, hn, H, ncol, g);
+            if (RG_h == 1) {  // gate = loads [0, L_h), up = loads [L_h, 2 L_h)
+              const u32x4 wg[2] = {w_gu[pr][0], w_gu[pr][1]};
+              const u32x4 wu[2] = {L_h == 2 ? w_gu[pr][2] : w_gu[pr][1], w_gu[pr][3]};
+              rg_dot<NCOL, 2>(wg, L_h, G_h, hn, H, ncol, g);
+              rg_dot<NCOL, 2>(wu, L_h, G_h, hn, H, ncol, u);
+            } else {  // one row group holds the pair: lanes [0,32) compute g_j, lanes [32,64) u_j
+              const u32x4 wg[2] = {w_gu[pr][0], w_gu[pr][1]};
+              rg_dot<NCOL, 2>(wg, L_h, G_h, hn, H, ncol, g);
 #pragma unroll
               for (int c = 0; c < NCOL; ++c) u[c] = __shfl_xor(g[c], 32, 64);
             }
@@ -976,10 +999,11 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         // prefetch: down-projection rows (F2), in flight during the m hand-off
         const uint16_t *tile = ly.ffn_dn + (size_t)x * H * J;
         const int nrg = H / RG_d;
-        if (wx < nrg) rg_issue<1, LMAX_D>(tile, wx, XW, nrg, L_d, w_dn);
+        rg_issue<1, LMAX_D>(tile_rsrc(tile, (uint32_t)(H * J * 2)), wx, XW, nrg, L_d, w_dn);
+        keep_issued();
         // ---- F2: down-projection columns of slice x
         float *mv = work;  // [NCOL][J]
-        if (!gather2d<NCOL>(xm, ncol, J, J, tg, mv, flag, m.ctl, SITE(11), tid)) MK_BAIL();
+        if (!gather2d<MCS, NPW>(xm, ncol, J, J, tg, mv, flag, m.ctl, SITE(11), tid)) MK_BAIL();
         if (wx < nrg) {
           float oo[NCOL];
           rg_dot<NCOL, LMAX_D>(w_dn[0], L_d, G_d, mv, J, ncol, oo);
@@ -990,18 +1014,18 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         }
       }
       // prefetch: the next layer's in-projection / QKV rows, in flight during the reduction
-      if (li + 1 < m.n_layers) {
+      // (gains first: the in-order wait for them at the next norm then excludes the weights)
+      {
+        const bool more = li + 1 < m.n_layers;
+        const float *gsrc = more ? layers[li + 1].ln1 : m.lnf;   // else the final norm's gains
+        g1a = ld_gain(gsrc, H, tid);
+        g1b = ld_gain(gsrc, H, tid + MK_THREADS);
         issue_in(li + 1);
-        g1a = (tid < H) ? layers[li + 1].ln1[tid] : 0.f;
-        g1b = (tid + MK_THREADS < H) ? layers[li + 1].ln1[tid + MK_THREADS] : 0.f;
-      } else {
-        g1a = (tid < H) ? m.lnf[tid] : 0.f;     // the final norm's gains
-        g1b = (tid + MK_THREADS < H) ? m.lnf[tid + MK_THREADS] : 0.f;
       }
       // ---- R2: residual += sum of the 8 FFN slices
       {
-        float *tmp = work;
-        if (!gather2d<MC2>(ly.x_ffn + lw * SL, ncol * MK_NX, SL, H, tg, tmp, flag, m.ctl, SITE(12), tid)) MK_BAIL();
+        float *tmp = work + 6400;  // [NCOL*8][SL], apart from the down-projection operand mv
+        if (!gather2d<MCS, NPW>(ly.x_ffn + lw * SL, ncol * MK_NX, SL, H, tg, tmp, flag, m.ctl, SITE(12), tid)) MK_BAIL();
         uint2 *xr = ly.x_r2 + (size_t)x * MK_MAXCOL * H;
         for (int i = tid; i < ncol * SL; i += MK_THREADS) {
           const int c = i / SL, k = i - c * SL;
@@ -1010,7 +1034,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           for (int g = 1; g < MK_NX; ++g) sm += tmp[(c * MK_NX + g) * SL + k];
           pub(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, tg);
         }
-        if (!gather2d<NCOL>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(13), tid)) MK_BAIL();
+        if (!gather2d<MCL, NPW>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(13), tid)) MK_BAIL();
       }
     }  // layers
 
@@ -1104,7 +1128,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       }
       const int anynan = __any(nanf) ? 1 : 0;
       if (lane == 0) rn[w8] = anynan;
-      __syncthreads();
+      lbar();
       if (tid < ncol) {
         const int c = tid;
         float bv = rv[c * 8];
@@ -1122,7 +1146,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                            __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    __syncthreads();  // the candidate above was read from the scratch the final gather reuses
+    lbar();  // the candidate above was read from the scratch the final gather reuses
     if (b == 0) {
       // final argmax over the 256 workgroup candidates; the tag word is written after the
       // value/index word by the same thread, so a matching tag implies the record is complete
@@ -1143,7 +1167,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         ci[i] = (int)v.y;
         cn[i] = (int)v.w;
       }
-      __syncthreads();
+      lbar();
       if (flag[0]) MK_BAIL();
       if (w8 == 0) {
         int gsel[MK_MAXCOL];
