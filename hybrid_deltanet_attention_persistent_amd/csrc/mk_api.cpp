@@ -18,6 +18,9 @@
 
 extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, hipStream_t stream);
 extern "C" hipError_t mk_forward_occupancy(int ncol_template, int *blocks_per_cu);
+extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
+                                         const int32_t *tokens, int n, int32_t *argmax, float *logits,
+                                         hipStream_t st);
 
 static thread_local std::string g_err;
 
@@ -40,6 +43,8 @@ struct mk_model {
   mk_config cfg;
   std::vector<uint8_t> kinds;
   MkDev dev;
+  std::vector<MkLayerDev> layers_host;  // the layer table (host copy) for the prefill driver
+  MkPf pf;                              // prefill scratch
   char *arena;
   size_t arena_bytes;
   // regions cleared by mk_reset_state
@@ -78,6 +83,10 @@ struct Plan {
   int H, V, I, J, nh, dk, dv, C, r_in, nq, nkv, hd, r_in_max, x_o_len, max_pages;
   Region embed, lnf, rope, page_table, layer_table, ctl, x_arg;
   std::vector<LayerRegions> layers;
+  // prefill scratch (one pass of MK_PT tokens)
+  int K1, NP;
+  Region pf_X, pf_a1h, pf_a1l, pf_a2h, pf_a2l, pf_P, pf_q, pf_k, pf_v, pf_z, pf_la, pf_be, pf_cT, pf_cM, pf_cg, pf_cd,
+      pf_o, pf_aq, pf_lmbest;
   size_t total;
 };
 
@@ -187,6 +196,31 @@ Plan make_plan(const mk_config *c) {
     r.x_m = L.add((size_t)MK_NX * MK_MAXCOL * p.J * 8);
     r.x_ffn = L.add((size_t)MK_MAXCOL * MK_NX * H * 8);
     r.x_r2 = L.add((size_t)MK_NX * MK_MAXCOL * H * 8);
+  }
+  {
+    const size_t T = MK_PT, nch = MK_PT / MK_CHUNK;
+    p.K1 = std::max(p.H, std::max(p.nh * p.dv, p.nq * p.hd));
+    p.NP = std::max(has_dn ? p.nh * p.r_in : 0, has_at ? (p.nq + 2 * p.nkv) * p.hd : 0);
+    p.pf_X = L.add(T * H * 4);
+    p.pf_a1h = L.add(T * p.K1 * 2);
+    p.pf_a1l = L.add(T * p.K1 * 2);
+    p.pf_a2h = L.add(T * p.I * 2);
+    p.pf_a2l = L.add(T * p.I * 2);
+    p.pf_P = L.add(T * p.NP * 4);
+    const size_t nhd = has_dn ? p.nh : 0;
+    p.pf_q = L.add(nhd * T * p.dk * 4);
+    p.pf_k = L.add(nhd * T * p.dk * 4);
+    p.pf_v = L.add(nhd * T * p.dv * 4);
+    p.pf_z = L.add(nhd * T * p.dv * 4);
+    p.pf_la = L.add(nhd * T * 4);
+    p.pf_be = L.add(nhd * T * 4);
+    p.pf_cT = L.add(nhd * nch * MK_CHUNK * MK_CHUNK * 4);
+    p.pf_cM = L.add(nhd * nch * MK_CHUNK * MK_CHUNK * 4);
+    p.pf_cg = L.add(nhd * nch * MK_CHUNK * 4);
+    p.pf_cd = L.add(nhd * nch * MK_CHUNK * 4);
+    p.pf_o = L.add(nhd * T * p.dv * 4);
+    p.pf_aq = L.add(has_at ? T * p.nq * p.hd * 4 : 0);
+    p.pf_lmbest = L.add((size_t)MK_NWG * 8);
   }
   p.total = (L.total + 255) & ~size_t(255);
   return p;
@@ -503,6 +537,21 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   mm->kinds.assign(cfg->layer_kind, cfg->layer_kind + cfg->n_layers);
   mm->cfg.layer_kind = mm->kinds.data();
   mm->dev = d;
+  mm->layers_host = lt;
+  {
+    MkPf &f = mm->pf;
+    auto P = [&](const Region &r) { return (void *)(A + r.off); };
+    f.X = (float *)P(p.pf_X);
+    f.a1h = (uint16_t *)P(p.pf_a1h); f.a1l = (uint16_t *)P(p.pf_a1l);
+    f.a2h = (uint16_t *)P(p.pf_a2h); f.a2l = (uint16_t *)P(p.pf_a2l);
+    f.P = (float *)P(p.pf_P);
+    f.q = (float *)P(p.pf_q); f.k = (float *)P(p.pf_k); f.v = (float *)P(p.pf_v); f.z = (float *)P(p.pf_z);
+    f.la = (float *)P(p.pf_la); f.be = (float *)P(p.pf_be);
+    f.cT = (float *)P(p.pf_cT); f.cM = (float *)P(p.pf_cM); f.cg = (float *)P(p.pf_cg); f.cd = (float *)P(p.pf_cd);
+    f.o = (float *)P(p.pf_o); f.aq = (float *)P(p.pf_aq);
+    f.lmbest = (unsigned long long *)P(p.pf_lmbest);
+    f.K1 = p.K1; f.NP = p.NP;
+  }
   mm->arena = A;
   mm->arena_bytes = arena_bytes;
   mm->state_regions = state;
@@ -548,17 +597,7 @@ extern "C" int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens
   hipStream_t st = (hipStream_t)stream;
   int s = ensure_ctx(m, n_tokens, st);
   if (s != MK_OK) return s;
-  MkLaunch a;
-  a.m = m->dev;
-  a.tokens = d_tokens;
-  a.n = n_tokens;
-  a.prefill = 1;
-  a.tag0 = m->tag;
-  a.argmax = d_next_token;
-  a.logits = d_last_logits;
-  a.n_acc = nullptr;
-  HIPCHECK(mk_launch_forward(&a, 1, st));
-  m->tag += (uint32_t)n_tokens;
+  HIPCHECK(mk_prefill_enqueue(&m->dev, m->layers_host.data(), &m->pf, d_tokens, n_tokens, d_next_token, d_last_logits, st));
   m->pos_hi += n_tokens;
   return MK_OK;
 }

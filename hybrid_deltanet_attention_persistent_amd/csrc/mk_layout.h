@@ -105,3 +105,26 @@ __host__ __device__ static inline int mk_tile_G(int K) {
   while (g > 1 && (c % g) != 0) g >>= 1;
   return g;
 }
+
+// ------------------------------------------------------------------------------ chunked prefill
+// A prompt is processed in passes of up to MK_PT tokens by a stream-ordered sequence of
+// kernels (projections as MFMA GEMMs, the delta rule in chunks of MK_CHUNK tokens).  Scratch
+// for one pass lives in the arena.
+#define MK_PT 1024                   // tokens per prefill pass (multiple of MK_CHUNK)
+#define MK_CHUNK 64                  // delta-rule chunk
+
+struct MkPf {
+  float *X;                           // [PT][H] residual stream (FP32)
+  uint16_t *a1h, *a1l;                // [PT][K1] GEMM operand as bf16 hi + lo, K1 = max(H, nh dv, nq hd)
+  uint16_t *a2h, *a2l;                // [PT][I]  SwiGLU activations as bf16 hi + lo
+  float *P;                           // [PT][NP] projection outputs, NP = max(nh r_in, (nq + 2 nkv) hd)
+  float *q, *k, *v;                   // [nh][PT][dk|dv] conv + SiLU (+ L2 norm for q, k), head-major
+  float *z;                           // [PT][nh dv] output-gate inputs
+  float *la, *be;                     // [nh][PT] log alpha, beta
+  float *cT, *cM;                     // [nh][PT/CHUNK][CHUNK][CHUNK] (I + A)^-1 and decay-weighted q.k
+  float *cg, *cd;                     // [nh][PT/CHUNK][CHUNK] exp(G_i), exp(G_last - G_i)
+  float *o;                           // [PT][nh dv] delta-rule output
+  float *aq;                          // [PT][nq hd] queries after RoPE
+  unsigned long long *lmbest;         // [MK_NWG] packed (ordered value, ~index) candidates
+  int32_t K1, NP;
+};

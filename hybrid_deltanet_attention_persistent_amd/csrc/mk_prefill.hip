@@ -1,0 +1,831 @@
+// mk_prefill.hip -- chunked prefill of the hybrid Gated-DeltaNet + attention decoder on
+// MI355X (gfx950).
+//
+// A prompt is processed in passes of up to MK_PT tokens.  Each pass is a stream-ordered
+// sequence of kernels per layer (launch page "OS Megakernel that match M5 Max Tok/w at 2x the
+// Throughput on RTX 3090", section "We wrote a single CUDA kernel ...": prefill turns the
+// projections into dense products over all prompt rows):
+//
+//   RMSNorm -> MFMA GEMM (in-projection / QKV) -> conv + SiLU + L2 norm + gates ->
+//   chunked delta rule (chunk precompute in parallel, then one sequential scan over the
+//   chunks per state row block) -> gated RMSNorm -> MFMA GEMM (out-projection, + residual) ->
+//   RMSNorm -> MFMA GEMM (gate/up, SwiGLU epilogue) -> MFMA GEMM (down, + residual)
+//
+// and for attention layers RoPE + KV append and causal attention over the cache.
+//
+// Precision.  Weights are BF16 and activations FP32 (the contract of the decode kernel).  A
+// GEMM operand a (FP32) enters the bf16 MFMA as two terms, hi = bf16(a) and lo = bf16(a - hi),
+// both multiplied by the exact bf16 weight and accumulated in FP32: the operand keeps 16
+// significant bits (relative error below 2^-17).  The delta rule, conv, norms and attention
+// run in FP32 on the vector ALUs.
+//
+// The chunked delta rule follows from unrolling the recurrence S_i = alpha_i S_{i-1} +
+// u_i k_i^T, u_i = beta_i (v_i - alpha_i S_{i-1} k_i) over a chunk that starts from S0.  With
+// G_i the in-chunk prefix sum of log alpha and gamma_i = exp(G_i):
+//   (I + A) U = B,  A_ij = beta_i exp(G_i - G_j) k_i.k_j (j < i),  B_i = beta_i (v_i - gamma_i S0 k_i)
+//   o_i = gamma_i S0 q_i + sum_{j <= i} exp(G_i - G_j) (k_j.q_i) u_j
+//   S_end = gamma_last S0 + sum_j exp(G_last - G_j) u_j k_j^T
+// Everything but S0 is computed for all chunks in parallel; the scan carries S0 through the
+// chunks, one block of state rows per workgroup (rows of S evolve independently).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "mk_layout.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int PF_THREADS = 256;
+constexpr int RB = 8;          // state rows per scan workgroup
+constexpr int QB = 16;         // queries per attention workgroup
+constexpr int KB = 64;         // keys per attention block
+
+__device__ __forceinline__ uint32_t f2bf(float f) {  // round to nearest even
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ void split_store(float v, uint16_t *hi, uint16_t *lo) {
+  const uint32_t h = f2bf(v);
+  *hi = (uint16_t)h;
+  *lo = (uint16_t)f2bf(v - bf2f(h));
+}
+__device__ __forceinline__ float sigmoidf_(float x) {
+  if (x >= 0.f) return 1.f / (1.f + expf(-x));
+  const float e = expf(x);
+  return e / (1.f + e);
+}
+__device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
+__device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// sum over the 256-thread workgroup; red: >= 4 floats of LDS
+__device__ __forceinline__ float block_sum(float v, float *red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float s = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return s;
+}
+
+// ------------------------------------------------------------------------------ row kernels
+__global__ void __launch_bounds__(PF_THREADS) pf_embed(const uint16_t *embed, const int32_t *tok, int H, int V,
+                                                       float *X, int32_t *ctl) {
+  const int t = blockIdx.x;
+  int id = tok[t];
+  if (id < 0 || id >= V) {
+    if (threadIdx.x == 0) __hip_atomic_fetch_or(ctl + MK_CTL_ERR, MK_DERR_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    id = 0;
+  }
+  for (int i = threadIdx.x; i < H; i += PF_THREADS) X[(size_t)t * H + i] = bf2f(embed[(size_t)id * H + i]);
+}
+
+// h = x / sqrt(mean(x^2) + eps) * g, written as a bf16 hi + lo pair (row stride ld)
+__global__ void __launch_bounds__(PF_THREADS) pf_norm_split(const float *X, const float *g, int H, float eps,
+                                                            uint16_t *oh, uint16_t *ol, int ld) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const float *x = X + (size_t)t * H;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < H; i += PF_THREADS) s = fmaf(x[i], x[i], s);
+  const float den = sqrtf(block_sum(s, red) / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += PF_THREADS)
+    split_store(x[i] / den * g[i], oh + (size_t)t * ld + i, ol + (size_t)t * ld + i);
+}
+
+// ------------------------------------------------------------------------------ MFMA GEMM
+// C[M][N] = A[M][K] . W[N][K]^T with A given as bf16 hi + lo ([M][lda]) and W in the tile
+// format of mk_layout.h.  W rows come from up to three row segments (tile wb[s] holds rows
+// [wend[s-1], wend[s]) ), and along K from segments of ks columns, kstride elements apart
+// (one tile [rows][ks] per segment).  One wave computes MT x NT 16x16 blocks with
+// v_mfma_f32_16x16x32_bf16 (lane l: A row l%16 and B column l%16 with k = 8 (l/16) .. +8;
+// result rows 4 (l/16) .. +4 of column l%16).
+struct PfGemm {
+  const uint16_t *ah, *al;
+  int lda, M, N, K;
+  const uint16_t *wb[3];
+  int wend[3];
+  int ks, kstride;
+  float *c;
+  int ldc;
+  uint16_t *oh, *ol;
+  int ldo;
+};
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+
+__device__ __forceinline__ int tileG(int K) {
+  int c = K / 8, g = 64;
+  while (g > 1 && (c % g) != 0) g >>= 1;
+  return g;
+}
+
+template <int EPI, int MT, int NT>
+__global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m0 = blockIdx.y * MT * 16;
+  const int n0 = (blockIdx.x * 4 + w) * NT * 16;
+  if (n0 >= g.N) return;  // no barriers in this kernel
+  const int G = tileG(g.ks), L = g.ks / 8 / G, RG = 64 / G, G8 = G * 8;
+  const uint16_t *bb[NT];
+  int rowpart[NT];
+#pragma unroll
+  for (int ni = 0; ni < NT; ++ni) {
+    const int n = min(n0 + ni * 16 + (lane & 15), g.N - 1);
+    const int s = n < g.wend[0] ? 0 : (n < g.wend[1] ? 1 : 2);
+    const int r = n - (s == 0 ? 0 : g.wend[s - 1]);
+    bb[ni] = g.wb[s];
+    rowpart[ni] = (r / RG) * L * 512 + (r % RG) * G8;
+  }
+  const uint16_t *pah[MT], *pal[MT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi) {
+    const size_t row = (size_t)(m0 + mi * 16 + (lane & 15));
+    pah[mi] = g.ah + row * g.lda;
+    pal[mi] = g.al + row * g.lda;
+  }
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this lane's k: segment kseg, offset j inside it
+  int kk = (lane >> 4) * 8, kseg = 0, j = kk;
+  while (j >= g.ks) { j -= g.ks; ++kseg; }
+  auto load = [&](int kcur, int ksg, int jj, bf16x8 (&fa)[MT], bf16x8 (&fl)[MT], bf16x8 (&fb)[NT]) {
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+      fa[mi] = *reinterpret_cast<const bf16x8 *>(pah[mi] + kcur);
+      fl[mi] = *reinterpret_cast<const bf16x8 *>(pal[mi] + kcur);
+    }
+    const int kpart = ksg * g.kstride + (jj / G8) * 512 + (jj & (G8 - 1));
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) fb[ni] = *reinterpret_cast<const bf16x8 *>(bb[ni] + rowpart[ni] + kpart);
+  };
+  bf16x8 fa[MT], fl[MT], fb[NT];
+  load(kk, kseg, j, fa, fl, fb);
+  for (int k0 = 0; k0 < g.K; k0 += 32) {
+    // advance to the next k step (the last iteration reloads the current one: branch-free)
+    int kn = kk, ksn = kseg, jn = j;
+    if (k0 + 32 < g.K) {
+      kn = kk + 32;
+      jn = j + 32;
+      while (jn >= g.ks) { jn -= g.ks; ++ksn; }
+    }
+    bf16x8 na[MT], nl[MT], nb[NT];
+    load(kn, ksn, jn, na, nl, nb);
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) {
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+      }
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) { fa[mi] = na[mi]; fl[mi] = nl[mi]; }
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) fb[ni] = nb[ni];
+    kk = kn; kseg = ksn; j = jn;
+  }
+  // epilogue
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + mi * 16 + (lane >> 4) * 4 + i;
+        const int col = n0 + ni * 16 + (lane & 15);
+        const float v = acc[mi][ni][i];
+        if (EPI == EPI_SWIGLU) {
+          // columns 2j (gate) and 2j+1 (up) of one intermediate index sit in lanes l, l^1
+          const float u = __shfl_xor(v, 1, 64);
+          if ((lane & 1) == 0 && row < g.M && col < g.N) {
+            const size_t o = (size_t)row * g.ldo + (col >> 1);
+            split_store(siluf_(v) * u, g.oh + o, g.ol + o);
+          }
+        } else if (row < g.M && col < g.N) {
+          float *cp = g.c + (size_t)row * g.ldc + col;
+          if (EPI == EPI_RESID) *cp = *cp + v;
+          else *cp = v;
+        }
+      }
+}
+
+// ------------------------------------------------------------------------------ DeltaNet
+struct PfDn {
+  const float *P;        // [T][NP]: per head x, columns x*r_in + [q | k | v | z | a | b]
+  int NP, T;
+  const float *conv;     // [C][4] taps
+  float *ring;           // [MK_RING][C] pre-conv inputs by position
+  const int32_t *ctl;
+  int nh, dk, dv, r_in, C;
+  float l2_eps;
+  float *q, *k, *v, *z, *la, *be;
+};
+
+// source column in P of conv channel ch (q channels, then k, then v)
+__device__ __forceinline__ int dn_col(const PfDn &d, int ch) {
+  const int nqk = d.nh * d.dk;
+  if (ch < nqk) return (ch / d.dk) * d.r_in + (ch % d.dk);
+  if (ch < 2 * nqk) return ((ch - nqk) / d.dk) * d.r_in + d.dk + ((ch - nqk) % d.dk);
+  const int c2 = ch - 2 * nqk;
+  return (c2 / d.dv) * d.r_in + 2 * d.dk + (c2 % d.dv);
+}
+
+// causal conv (taps over positions p-3..p) + SiLU, L2 norms of q and k per head, gates
+__global__ void __launch_bounds__(PF_THREADS) pf_dn_prep(PfDn d) {
+  extern __shared__ float buf[];  // [C] conv outputs, then [2 nh] norms
+  const int t = blockIdx.x;
+  const int p0 = d.ctl[MK_CTL_POS];
+  for (int ch = threadIdx.x; ch < d.C; ch += PF_THREADS) {
+    const int col = dn_col(d, ch);
+    const float4 wt = *reinterpret_cast<const float4 *>(d.conv + ch * 4);
+    const float wv[4] = {wt.x, wt.y, wt.z, wt.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = t - 3 + i;     // tap i meets the token 3 - i steps before
+      float x = 0.f;
+      if (tt >= 0) x = d.P[(size_t)tt * d.NP + col];
+      else if (p0 + tt >= 0) x = d.ring[((p0 + tt) & (MK_RING - 1)) * d.C + ch];
+      acc = fmaf(wv[i], x, acc);
+    }
+    buf[ch] = siluf_(acc);
+  }
+  __syncthreads();
+  float *nrm = buf + d.C;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int r = w; r < 2 * d.nh; r += PF_THREADS / 64) {  // r = 2 head + (0: q, 1: k)
+    const float *p = buf + (r & 1) * d.nh * d.dk + (r >> 1) * d.dk;
+    float sq = 0.f;
+    for (int i = lane; i < d.dk; i += 64) sq = fmaf(p[i], p[i], sq);
+    sq = wave_sum(sq);
+    if (lane == 0) nrm[r] = sqrtf(sq + d.l2_eps);
+  }
+  __syncthreads();
+  const int nqk = d.nh * d.dk;
+  for (int ch = threadIdx.x; ch < d.C; ch += PF_THREADS) {
+    if (ch < nqk) {
+      const int h = ch / d.dk, i = ch % d.dk;
+      d.q[((size_t)h * MK_PT + t) * d.dk + i] = buf[ch] / nrm[2 * h];
+    } else if (ch < 2 * nqk) {
+      const int h = (ch - nqk) / d.dk, i = (ch - nqk) % d.dk;
+      d.k[((size_t)h * MK_PT + t) * d.dk + i] = buf[ch] / nrm[2 * h + 1];
+    } else {
+      const int h = (ch - 2 * nqk) / d.dv, i = (ch - 2 * nqk) % d.dv;
+      d.v[((size_t)h * MK_PT + t) * d.dv + i] = buf[ch];
+    }
+  }
+  for (int i = threadIdx.x; i < d.nh * d.dv; i += PF_THREADS) {
+    const int h = i / d.dv, e = i % d.dv;
+    d.z[(size_t)t * d.nh * d.dv + i] = d.P[(size_t)t * d.NP + h * d.r_in + 2 * d.dk + d.dv + e];
+  }
+  if (threadIdx.x < d.nh) {
+    const int h = threadIdx.x;
+    const float a = d.P[(size_t)t * d.NP + h * d.r_in + 2 * d.dk + 2 * d.dv];
+    const float b = d.P[(size_t)t * d.NP + h * d.r_in + 2 * d.dk + 2 * d.dv + 1];
+    d.la[(size_t)h * MK_PT + t] = -softplusf_(a);   // log alpha, alpha = exp(-softplus(a))
+    d.be[(size_t)h * MK_PT + t] = sigmoidf_(b);
+  }
+}
+
+// keep the pre-conv inputs of the last positions for the decode kernel's conv
+__global__ void __launch_bounds__(PF_THREADS) pf_dn_ring(PfDn d) {
+  const int p0 = d.ctl[MK_CTL_POS];
+  const int first = max(0, d.T - MK_RING);
+  const int t = first + blockIdx.x;
+  if (t >= d.T) return;
+  for (int ch = threadIdx.x; ch < d.C; ch += PF_THREADS)
+    d.ring[((p0 + t) & (MK_RING - 1)) * d.C + ch] = d.P[(size_t)t * d.NP + dn_col(d, ch)];
+}
+
+struct PfChunk {
+  const float *q, *k, *la, *be;   // head-major [nh][PT][dk], [nh][PT]
+  float *cT, *cM, *cg, *cd;       // [nh][PT/CHUNK][CHUNK][CHUNK], [nh][PT/CHUNK][CHUNK]
+  int T, dk;
+};
+
+// per (chunk, head): (I + A)^-1, the decay-weighted q.k matrix and the decays
+__global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
+  extern __shared__ float sm[];
+  const int ch = blockIdx.x, h = blockIdx.y, nch = MK_PT / MK_CHUNK;
+  const int t0 = ch * MK_CHUNK, Cn = min(MK_CHUNK, c.T - t0);
+  const int dk = c.dk, ks = dk + 1;           // padded rows: conflict-free column reads
+  float *Ks = sm, *Qs = Ks + MK_CHUNK * ks;
+  float *A = Qs + MK_CHUNK * ks;              // [64][65]
+  float *X = A + MK_CHUNK * 65;               // [64][65]
+  float *Gs = X + MK_CHUNK * 65, *bs = Gs + MK_CHUNK;
+  const size_t hb = (size_t)h * MK_PT;
+  for (int i = threadIdx.x; i < MK_CHUNK * dk; i += PF_THREADS) {
+    const int r = i / dk, e = i % dk;
+    Ks[r * ks + e] = r < Cn ? c.k[(hb + t0 + r) * dk + e] : 0.f;
+    Qs[r * ks + e] = r < Cn ? c.q[(hb + t0 + r) * dk + e] : 0.f;
+  }
+  if (threadIdx.x < MK_CHUNK) bs[threadIdx.x] = threadIdx.x < Cn ? c.be[hb + t0 + threadIdx.x] : 0.f;
+  if (threadIdx.x == 0) {
+    float G = 0.f;
+    for (int i = 0; i < MK_CHUNK; ++i) {
+      if (i < Cn) G += c.la[hb + t0 + i];
+      Gs[i] = G;
+    }
+  }
+  __syncthreads();
+  float *cT = c.cT + ((size_t)h * nch + ch) * MK_CHUNK * MK_CHUNK;
+  float *cM = c.cM + ((size_t)h * nch + ch) * MK_CHUNK * MK_CHUNK;
+  for (int e = threadIdx.x; e < MK_CHUNK * MK_CHUNK; e += PF_THREADS) {
+    const int i = e / MK_CHUNK, j = e % MK_CHUNK;
+    float kk = 0.f, qk = 0.f;
+    if (j <= i && i < Cn) {
+      for (int d = 0; d < dk; ++d) {
+        kk = fmaf(Ks[i * ks + d], Ks[j * ks + d], kk);
+        qk = fmaf(Qs[i * ks + d], Ks[j * ks + d], qk);
+      }
+    }
+    const float dec = (j <= i && i < Cn) ? expf(Gs[i] - Gs[j]) : 0.f;
+    A[i * 65 + j] = (j < i) ? bs[i] * dec * kk : 0.f;
+    cM[e] = dec * qk;
+  }
+  __syncthreads();
+  // X = (I + A)^-1 (unit lower triangular), one row at a time: X_i = e_i - sum_{m<i} A_im X_m
+  for (int i = 0; i < MK_CHUNK; ++i) {
+    if (threadIdx.x < MK_CHUNK) {
+      const int jj = threadIdx.x;
+      float s = (jj == i) ? 1.f : 0.f;
+      for (int m = jj; m < i; ++m) s = fmaf(-A[i * 65 + m], X[m * 65 + jj], s);
+      X[i * 65 + jj] = (jj <= i) ? s : 0.f;
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < MK_CHUNK * MK_CHUNK; e += PF_THREADS) cT[e] = X[(e / MK_CHUNK) * 65 + e % MK_CHUNK];
+  if (threadIdx.x < MK_CHUNK) {
+    const int i = threadIdx.x;
+    const size_t o = ((size_t)h * nch + ch) * MK_CHUNK + i;
+    c.cg[o] = i < Cn ? expf(Gs[i]) : 0.f;
+    c.cd[o] = i < Cn ? expf(Gs[Cn - 1] - Gs[i]) : 0.f;
+  }
+}
+
+struct PfScan {
+  float *S;                        // [nh][dv][dk] layer state
+  const float *pend;               // [2][nh][MAXCOL][dk + dv + 2] pending updates (k | v | alpha beta)
+  const int32_t *ctl;
+  const float *q, *k, *v, *be;     // head-major
+  const float *cT, *cM, *cg, *cd;
+  float *o;                        // [PT][nh dv]
+  int T, nh, dk, dv;
+};
+
+// carry RB rows of one head's state through every chunk of the pass
+__global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
+  extern __shared__ float sm[];
+  const int h = blockIdx.y, r0 = blockIdx.x * RB, dk = s.dk, dv = s.dv, ks = dk + 1;
+  const int nch = MK_PT / MK_CHUNK, nchunk = (s.T + MK_CHUNK - 1) / MK_CHUNK;
+  float *Sr = sm;                                  // [RB][dk]
+  float *Ks = Sr + RB * dk, *Qs = Ks + MK_CHUNK * ks;
+  float *Tm = Qs + MK_CHUNK * ks, *Mm = Tm + MK_CHUNK * 65;
+  float *SK = Mm + MK_CHUNK * 65, *SQ = SK + RB * MK_CHUNK, *Bm = SQ + RB * MK_CHUNK, *U = Bm + RB * MK_CHUNK;
+  float *Vr = U + RB * MK_CHUNK;                   // [RB][64]
+  float *gs = Vr + RB * MK_CHUNK, *ds = gs + MK_CHUNK, *bs = ds + MK_CHUNK;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  float *Sg = s.S + ((size_t)h * dv + r0) * dk;
+  for (int i = tid; i < RB * dk; i += PF_THREADS) Sr[i] = Sg[i];
+  __syncthreads();
+  // pending updates left by a verify forward (same arithmetic as the decode kernel's step)
+  const int pend_n = s.ctl[MK_CTL_PEND], par = s.ctl[MK_CTL_PAR];
+  for (int jp = 0; jp < pend_n; ++jp) {
+    const float *pk = s.pend + (((size_t)par * s.nh + h) * MK_MAXCOL + jp) * (dk + dv + 2);
+    const float a = pk[dk + dv], b = pk[dk + dv + 1];
+    for (int r = w; r < RB; r += PF_THREADS / 64) {
+      float p = 0.f;
+      for (int e = lane; e < dk; e += 64) p = fmaf(Sr[r * dk + e], pk[e], p);
+      const float sk = wave_sum(p);
+      const float u = b * (pk[dk + r0 + r] - a * sk);
+      for (int e = lane; e < dk; e += 64) Sr[r * dk + e] = fmaf(u, pk[e], a * Sr[r * dk + e]);
+    }
+  }
+  __syncthreads();
+  const size_t hb = (size_t)h * MK_PT;
+  for (int c = 0; c < nchunk; ++c) {
+    const int t0 = c * MK_CHUNK, Cn = min(MK_CHUNK, s.T - t0);
+    const size_t cb = ((size_t)h * nch + c);
+    for (int i = tid; i < MK_CHUNK * dk; i += PF_THREADS) {
+      const int r = i / dk, e = i % dk;
+      Ks[r * ks + e] = r < Cn ? s.k[(hb + t0 + r) * dk + e] : 0.f;
+      Qs[r * ks + e] = r < Cn ? s.q[(hb + t0 + r) * dk + e] : 0.f;
+    }
+    for (int i = tid; i < MK_CHUNK * MK_CHUNK; i += PF_THREADS) {
+      Tm[(i / MK_CHUNK) * 65 + i % MK_CHUNK] = s.cT[cb * MK_CHUNK * MK_CHUNK + i];
+      Mm[(i / MK_CHUNK) * 65 + i % MK_CHUNK] = s.cM[cb * MK_CHUNK * MK_CHUNK + i];
+    }
+    for (int i = tid; i < RB * MK_CHUNK; i += PF_THREADS) {
+      const int r = i / MK_CHUNK, t = i % MK_CHUNK;
+      Vr[i] = t < Cn ? s.v[(hb + t0 + t) * dv + r0 + r] : 0.f;
+    }
+    if (tid < MK_CHUNK) {
+      gs[tid] = s.cg[cb * MK_CHUNK + tid];
+      ds[tid] = s.cd[cb * MK_CHUNK + tid];
+      bs[tid] = tid < Cn ? s.be[hb + t0 + tid] : 0.f;
+    }
+    __syncthreads();
+    // S0 k_i and S0 q_i for my rows
+    for (int e = tid; e < RB * MK_CHUNK; e += PF_THREADS) {
+      const int r = e / MK_CHUNK, i = e % MK_CHUNK;
+      float a = 0.f, b = 0.f;
+      for (int d = 0; d < dk; ++d) {
+        const float sv = Sr[r * dk + d];
+        a = fmaf(sv, Ks[i * ks + d], a);
+        b = fmaf(sv, Qs[i * ks + d], b);
+      }
+      SK[e] = a;
+      SQ[e] = b;
+      Bm[e] = bs[i] * (Vr[e] - gs[i] * a);
+    }
+    __syncthreads();
+    for (int e = tid; e < RB * MK_CHUNK; e += PF_THREADS) {  // U = (I + A)^-1 B
+      const int r = e / MK_CHUNK, i = e % MK_CHUNK;
+      float u = 0.f;
+      for (int jj = 0; jj <= i; ++jj) u = fmaf(Tm[i * 65 + jj], Bm[r * MK_CHUNK + jj], u);
+      U[e] = u;
+    }
+    __syncthreads();
+    for (int e = tid; e < RB * MK_CHUNK; e += PF_THREADS) {  // outputs
+      const int r = e / MK_CHUNK, i = e % MK_CHUNK;
+      if (i < Cn) {
+        float o = gs[i] * SQ[e];
+        for (int jj = 0; jj <= i; ++jj) o = fmaf(Mm[i * 65 + jj], U[r * MK_CHUNK + jj], o);
+        s.o[(size_t)(t0 + i) * s.nh * dv + h * dv + r0 + r] = o;
+      }
+    }
+    const float gl = gs[Cn - 1];
+    for (int e = tid; e < RB * dk; e += PF_THREADS) {  // end-of-chunk state
+      const int r = e / dk, d = e % dk;
+      float acc = 0.f;
+      for (int jj = 0; jj < Cn; ++jj) acc = fmaf(ds[jj] * U[r * MK_CHUNK + jj], Ks[jj * ks + d], acc);
+      Sr[e] = fmaf(gl, Sr[e], acc);
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < RB * dk; i += PF_THREADS) Sg[i] = Sr[i];
+}
+
+// gated RMSNorm per (token, head): y = o / sqrt(mean(o^2) + eps) * g * SiLU(z), as bf16 hi + lo
+__global__ void __launch_bounds__(PF_THREADS) pf_dn_gnorm(const float *o, const float *z, const float *gn, int nh, int dv,
+                                                          float eps, uint16_t *oh, uint16_t *ol, int ld) {
+  const int t = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int h = w; h < nh; h += PF_THREADS / 64) {
+    const float *oo = o + (size_t)t * nh * dv + h * dv;
+    const float *zz = z + (size_t)t * nh * dv + h * dv;
+    float sq = 0.f;
+    for (int i = lane; i < dv; i += 64) sq = fmaf(oo[i], oo[i], sq);
+    const float den = sqrtf(wave_sum(sq) / (float)dv + eps);
+    for (int i = lane; i < dv; i += 64)
+      split_store(oo[i] / den * gn[i] * siluf_(zz[i]), oh + (size_t)t * ld + h * dv + i, ol + (size_t)t * ld + h * dv + i);
+  }
+}
+
+// ------------------------------------------------------------------------------ attention
+struct PfAtt {
+  const float *P;             // [T][NP]: q (nq hd) | k (nkv hd) | v (nkv hd)
+  int NP, T;
+  const float *rope;          // [max_ctx][hd/2][2]
+  const int32_t *page_table;
+  const int32_t *ctl;
+  uint16_t *kc, *vc;          // [pages][nkv][PAGE][hd]
+  float *aq;                  // [PT][nq hd]
+  int nq, nkv, hd;
+  uint16_t *oh, *ol;          // [PT][ld]
+  int ld;
+};
+
+__device__ __forceinline__ size_t kv_off(const PfAtt &a, int p, int kvh) {
+  return (((size_t)a.page_table[p / MK_PAGE] * a.nkv + kvh) * MK_PAGE + (p % MK_PAGE)) * a.hd;
+}
+
+// RoPE on q and k at position p0 + t; K and V appended to the cache as bf16
+__global__ void __launch_bounds__(PF_THREADS) pf_att_rope(PfAtt a) {
+  const int t = blockIdx.x, p = a.ctl[MK_CTL_POS] + t, half = a.hd / 2;
+  const float *row = a.P + (size_t)t * a.NP;
+  for (int e = threadIdx.x; e < (a.nq + a.nkv) * half; e += PF_THREADS) {
+    const int hh = e / half, d = e % half;
+    const float cs = a.rope[((size_t)p * half + d) * 2 + 0], sn = a.rope[((size_t)p * half + d) * 2 + 1];
+    if (hh < a.nq) {
+      const float q1 = row[hh * a.hd + d], q2 = row[hh * a.hd + d + half];
+      a.aq[(size_t)t * a.nq * a.hd + hh * a.hd + d] = q1 * cs - q2 * sn;
+      a.aq[(size_t)t * a.nq * a.hd + hh * a.hd + d + half] = q2 * cs + q1 * sn;
+    } else {
+      const int kvh = hh - a.nq;
+      const float *kr = row + a.nq * a.hd + kvh * a.hd;
+      const float k1 = kr[d], k2 = kr[d + half];
+      const size_t o = kv_off(a, p, kvh);
+      a.kc[o + d] = (uint16_t)f2bf(k1 * cs - k2 * sn);
+      a.kc[o + d + half] = (uint16_t)f2bf(k2 * cs + k1 * sn);
+    }
+  }
+  for (int e = threadIdx.x; e < a.nkv * a.hd; e += PF_THREADS) {
+    const int kvh = e / a.hd, d = e % a.hd;
+    a.vc[kv_off(a, p, kvh) + d] = (uint16_t)f2bf(row[(a.nq + a.nkv) * a.hd + e]);
+  }
+}
+
+// causal attention of QB queries of one head over keys 0 .. position, online softmax (FP32)
+__global__ void __launch_bounds__(PF_THREADS) pf_att(PfAtt a) {
+  extern __shared__ float sm[];
+  const int qb = blockIdx.x, hq = blockIdx.y, hd = a.hd, kvh = hq * a.nkv / a.nq;
+  const int p0 = a.ctl[MK_CTL_POS];
+  const int t0 = qb * QB, nqr = min(QB, a.T - t0);
+  const int kh = hd + 1;
+  float *Qs = sm;                       // [QB][hd]
+  float *Ks = Qs + QB * hd;             // [KB][hd+1]
+  float *Vs = Ks + KB * kh;             // [KB][hd]
+  float *Ps = Vs + KB * hd;             // [QB][KB]
+  float *mrow = Ps + QB * KB, *lrow = mrow + QB, *alpha = lrow + QB;
+  const int tid = threadIdx.x;
+  const float scale = 1.f / sqrtf((float)hd);
+  for (int e = tid; e < QB * hd; e += PF_THREADS) {
+    const int r = e / hd, d = e % hd;
+    Qs[e] = r < nqr ? a.aq[(size_t)(t0 + r) * a.nq * hd + hq * hd + d] : 0.f;
+  }
+  if (tid < QB) { mrow[tid] = -INFINITY; lrow[tid] = 0.f; }
+  // accumulator: thread -> query tid / 16, dims (tid % 16) + 16 j
+  const int aq_ = tid / 16, ad = tid % 16;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  const int last = p0 + t0 + nqr - 1;   // largest query position
+  const int nkb = last / KB + 1;
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int k0 = kb * KB;
+    for (int e = tid; e < KB * hd; e += PF_THREADS) {
+      const int r = e / hd, d = e % hd, p = k0 + r;
+      float kv = 0.f, vv = 0.f;
+      if (p <= last) {
+        const size_t o = kv_off(a, p, kvh) + d;
+        kv = bf2f(a.kc[o]);
+        vv = bf2f(a.vc[o]);
+      }
+      Ks[r * kh + d] = kv;
+      Vs[r * hd + d] = vv;
+    }
+    __syncthreads();
+    for (int e = tid; e < QB * KB; e += PF_THREADS) {
+      const int r = e / KB, j = e % KB;
+      const int qp = p0 + t0 + r, kp = k0 + j;
+      float s = -INFINITY;
+      if (r < nqr && kp <= qp) {
+        float d0 = 0.f;
+        for (int d = 0; d < hd; ++d) d0 = fmaf(Qs[r * hd + d], Ks[j * kh + d], d0);
+        s = d0 * scale;
+      }
+      Ps[e] = s;
+    }
+    __syncthreads();
+    if (tid < QB) {  // online softmax bookkeeping for row tid
+      const int r = tid;
+      float mx = mrow[r];
+      for (int j = 0; j < KB; ++j) mx = fmaxf(mx, Ps[r * KB + j]);
+      const float al = (mx == -INFINITY) ? 1.f : expf(mrow[r] - mx);
+      float l = lrow[r] * al;
+      for (int j = 0; j < KB; ++j) {
+        const float p = (Ps[r * KB + j] == -INFINITY) ? 0.f : expf(Ps[r * KB + j] - mx);
+        Ps[r * KB + j] = p;
+        l += p;
+      }
+      mrow[r] = mx;
+      lrow[r] = l;
+      alpha[r] = al;
+    }
+    __syncthreads();
+    {
+      const float al = alpha[aq_];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = ad + 16 * j;
+        if (d < hd) {
+          float s = acc[j] * al;
+          for (int kk = 0; kk < KB; ++kk) s = fmaf(Ps[aq_ * KB + kk], Vs[kk * hd + d], s);
+          acc[j] = s;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (aq_ < nqr) {
+    const float inv = lrow[aq_];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = ad + 16 * j;
+      if (d < hd) {
+        const size_t o = (size_t)(t0 + aq_) * a.ld + hq * hd + d;
+        split_store(acc[j] / inv, a.oh + o, a.ol + o);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ LM head
+__device__ __forceinline__ unsigned long long pack_best(float v, int idx) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // order-preserving
+  return ((unsigned long long)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+// logits of the last row (final RMSNorm + tied embedding) and each workgroup's best
+__global__ void __launch_bounds__(PF_THREADS) pf_lm(const float *X, int row, const float *lnf, float eps,
+                                                    const uint16_t *embed, int V, int H, float *logits,
+                                                    unsigned long long *best, int32_t *ctl) {
+  __shared__ float hn[1024];
+  __shared__ float red[4];
+  __shared__ unsigned long long wb[4];
+  const float *x = X + (size_t)row * H;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < H; i += PF_THREADS) s = fmaf(x[i], x[i], s);
+  const float den = sqrtf(block_sum(s, red) / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += PF_THREADS) hn[i] = x[i] / den * lnf[i];
+  __syncthreads();
+  const int b = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = (int)((long long)b * V / gridDim.x), r1 = (int)((long long)(b + 1) * V / gridDim.x);
+  unsigned long long mybest = 0;
+  int bad = 0;
+  for (int r = r0 + w; r < r1; r += PF_THREADS / 64) {
+    const uint16_t *er = embed + (size_t)r * H;
+    float p = 0.f;
+    for (int i = lane * 8; i < H; i += 512) {
+      const uint4 wv = *reinterpret_cast<const uint4 *>(er + i);
+      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p = fmaf(__uint_as_float(ww[e] << 16), hn[i + 2 * e], p);
+        p = fmaf(__uint_as_float(ww[e] & 0xffff0000u), hn[i + 2 * e + 1], p);
+      }
+    }
+    const float tot = wave_sum(p);
+    if (lane == 0) {
+      if (logits) logits[r] = tot;
+      if (!(tot == tot) || isinf(tot)) bad = 1;
+      const unsigned long long k = pack_best(tot, r);
+      if (k > mybest) mybest = k;
+    }
+  }
+  if (lane == 0) wb[w] = mybest;
+  if (bad) __hip_atomic_fetch_or(ctl + MK_CTL_ERR, MK_DERR_NAN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long m = wb[0];
+    for (int i = 1; i < 4; ++i) m = wb[i] > m ? wb[i] : m;
+    best[b] = m;
+  }
+}
+
+// end of a pass: the greedy token (last pass), the position, pending updates consumed
+__global__ void pf_finish(const unsigned long long *best, int nbest, int32_t *argmax, int32_t *ctl, int T) {
+  if (threadIdx.x != 0) return;
+  if (argmax) {
+    unsigned long long m = 0;
+    for (int i = 0; i < nbest; ++i) m = best[i] > m ? best[i] : m;
+    argmax[0] = (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFu));
+  }
+  ctl[MK_CTL_POS] += T;
+  ctl[MK_CTL_PEND] = 0;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------ host driver
+struct MkPfHost {
+  const MkDev *d;
+  const MkLayerDev *layers;   // host copy of the layer table
+  MkPf pf;
+};
+
+static hipError_t launch_gemm(int epi, bool small, const PfGemm &g, hipStream_t st) {
+  const int MT = small ? 2 : 4, NT = small ? 2 : 4;
+  dim3 grid((g.N + 4 * NT * 16 - 1) / (4 * NT * 16), (g.M + MT * 16 - 1) / (MT * 16));
+  if (epi == EPI_STORE) {
+    if (small) hipLaunchKernelGGL((pf_gemm<EPI_STORE, 2, 2>), grid, dim3(PF_THREADS), 0, st, g);
+    else hipLaunchKernelGGL((pf_gemm<EPI_STORE, 4, 4>), grid, dim3(PF_THREADS), 0, st, g);
+  } else if (epi == EPI_RESID) {
+    if (small) hipLaunchKernelGGL((pf_gemm<EPI_RESID, 2, 2>), grid, dim3(PF_THREADS), 0, st, g);
+    else hipLaunchKernelGGL((pf_gemm<EPI_RESID, 4, 4>), grid, dim3(PF_THREADS), 0, st, g);
+  } else {
+    if (small) hipLaunchKernelGGL((pf_gemm<EPI_SWIGLU, 2, 2>), grid, dim3(PF_THREADS), 0, st, g);
+    else hipLaunchKernelGGL((pf_gemm<EPI_SWIGLU, 4, 4>), grid, dim3(PF_THREADS), 0, st, g);
+  }
+  return hipGetLastError();
+}
+
+static size_t chunk_prep_lds(int dk) { return (size_t)(2 * MK_CHUNK * (dk + 1) + 2 * MK_CHUNK * 65 + 2 * MK_CHUNK) * 4; }
+static size_t scan_lds(int dk) {
+  return (size_t)(RB * dk + 2 * MK_CHUNK * (dk + 1) + 2 * MK_CHUNK * 65 + 5 * RB * MK_CHUNK + 3 * MK_CHUNK) * 4;
+}
+static size_t att_lds(int hd) { return (size_t)(QB * hd + KB * (hd + 1) + KB * hd + QB * KB + 3 * QB) * 4; }
+
+// Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table.
+extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
+                                         const int32_t *tokens, int n, int32_t *argmax, float *logits,
+                                         hipStream_t st) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e;
+    if ((e = hipFuncSetAttribute((const void *)pf_dn_chunk_prep, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)pf_dn_scan, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)pf_att, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess) return e;
+    attr_done = true;
+  }
+  const int H = d->H, nh = d->nh, dk = d->dk, dv = d->dv, nq = d->nq, nkv = d->nkv, hd = d->hd, J = d->J, I = d->I;
+  for (int s0 = 0; s0 < n; s0 += MK_PT) {
+    const int T = n - s0 < MK_PT ? n - s0 : MK_PT;
+    const bool last = s0 + T == n;
+    hipLaunchKernelGGL(pf_embed, dim3(T), dim3(PF_THREADS), 0, st, d->embed, tokens + s0, H, d->V, pf->X, d->ctl);
+    for (int li = 0; li < d->n_layers; ++li) {
+      const MkLayerDev &L = layers_host[li];
+      hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->X, L.ln1, H, d->rms_eps,
+                         pf->a1h, pf->a1l, pf->K1);
+      PfGemm g{};
+      g.ah = pf->a1h; g.al = pf->a1l; g.lda = pf->K1; g.M = T;
+      if (L.kind == 0) {
+        g.N = nh * d->r_in; g.K = H;
+        g.wb[0] = g.wb[1] = g.wb[2] = L.dn_in; g.wend[0] = g.wend[1] = g.wend[2] = g.N;
+        g.ks = H; g.kstride = 0;
+        g.c = pf->P; g.ldc = pf->NP;
+        hipError_t e = launch_gemm(EPI_STORE, false, g, st);
+        if (e != hipSuccess) return e;
+        PfDn dn{};
+        dn.P = pf->P; dn.NP = pf->NP; dn.T = T; dn.conv = L.dn_conv; dn.ring = L.ring; dn.ctl = d->ctl;
+        dn.nh = nh; dn.dk = dk; dn.dv = dv; dn.r_in = d->r_in; dn.C = d->C; dn.l2_eps = d->l2_eps;
+        dn.q = pf->q; dn.k = pf->k; dn.v = pf->v; dn.z = pf->z; dn.la = pf->la; dn.be = pf->be;
+        hipLaunchKernelGGL(pf_dn_prep, dim3(T), dim3(PF_THREADS), (size_t)(d->C + 2 * nh) * 4, st, dn);
+        hipLaunchKernelGGL(pf_dn_ring, dim3(T < MK_RING ? T : MK_RING), dim3(PF_THREADS), 0, st, dn);
+        const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
+        PfChunk ck{pf->q, pf->k, pf->la, pf->be, pf->cT, pf->cM, pf->cg, pf->cd, T, dk};
+        hipLaunchKernelGGL(pf_dn_chunk_prep, dim3(nchunk, nh), dim3(PF_THREADS), chunk_prep_lds(dk), st, ck);
+        PfScan sc{L.S, L.pend, d->ctl, pf->q, pf->k, pf->v, pf->be, pf->cT, pf->cM, pf->cg, pf->cd, pf->o, T, nh, dk, dv};
+        hipLaunchKernelGGL(pf_dn_scan, dim3(dv / RB, nh), dim3(PF_THREADS), scan_lds(dk), st, sc);
+        hipLaunchKernelGGL(pf_dn_gnorm, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->o, (const float *)pf->z,
+                           L.dn_gnorm, nh, dv, d->rms_eps, pf->a1h, pf->a1l, pf->K1);
+        PfGemm go{};
+        go.ah = pf->a1h; go.al = pf->a1l; go.lda = pf->K1; go.M = T; go.N = H; go.K = nh * dv;
+        go.wb[0] = go.wb[1] = go.wb[2] = L.dn_out; go.wend[0] = go.wend[1] = go.wend[2] = H;
+        go.ks = dv; go.kstride = H * dv;
+        go.c = pf->X; go.ldc = H;
+        if ((e = launch_gemm(EPI_RESID, true, go, st)) != hipSuccess) return e;
+      } else {
+        g.N = (nq + 2 * nkv) * hd; g.K = H;
+        g.wb[0] = L.at_q; g.wend[0] = nq * hd;
+        g.wb[1] = L.at_k; g.wend[1] = (nq + nkv) * hd;
+        g.wb[2] = L.at_v; g.wend[2] = g.N;
+        g.ks = H; g.kstride = 0;
+        g.c = pf->P; g.ldc = pf->NP;
+        hipError_t e = launch_gemm(EPI_STORE, false, g, st);
+        if (e != hipSuccess) return e;
+        PfAtt at{};
+        at.P = pf->P; at.NP = pf->NP; at.T = T; at.rope = d->rope; at.page_table = d->page_table; at.ctl = d->ctl;
+        at.kc = L.kc; at.vc = L.vc; at.aq = pf->aq; at.nq = nq; at.nkv = nkv; at.hd = hd;
+        at.oh = pf->a1h; at.ol = pf->a1l; at.ld = pf->K1;
+        hipLaunchKernelGGL(pf_att_rope, dim3(T), dim3(PF_THREADS), 0, st, at);
+        hipLaunchKernelGGL(pf_att, dim3((T + QB - 1) / QB, nq), dim3(PF_THREADS), att_lds(hd), st, at);
+        PfGemm go{};
+        go.ah = pf->a1h; go.al = pf->a1l; go.lda = pf->K1; go.M = T; go.N = H; go.K = nq * hd;
+        go.wb[0] = go.wb[1] = go.wb[2] = L.at_o; go.wend[0] = go.wend[1] = go.wend[2] = H;
+        go.ks = hd; go.kstride = H * hd;
+        go.c = pf->X; go.ldc = H;
+        if ((e = launch_gemm(EPI_RESID, true, go, st)) != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->X, L.ln2, H, d->rms_eps,
+                         pf->a1h, pf->a1l, pf->K1);
+      PfGemm gu{};
+      gu.ah = pf->a1h; gu.al = pf->a1l; gu.lda = pf->K1; gu.M = T; gu.N = 2 * I; gu.K = H;
+      gu.wb[0] = gu.wb[1] = gu.wb[2] = L.ffn_gu; gu.wend[0] = gu.wend[1] = gu.wend[2] = 2 * I;
+      gu.ks = H; gu.kstride = 0;
+      gu.oh = pf->a2h; gu.ol = pf->a2l; gu.ldo = I;
+      hipError_t e = launch_gemm(EPI_SWIGLU, false, gu, st);
+      if (e != hipSuccess) return e;
+      PfGemm gd{};
+      gd.ah = pf->a2h; gd.al = pf->a2l; gd.lda = I; gd.M = T; gd.N = H; gd.K = I;
+      gd.wb[0] = gd.wb[1] = gd.wb[2] = L.ffn_dn; gd.wend[0] = gd.wend[1] = gd.wend[2] = H;
+      gd.ks = J; gd.kstride = H * J;
+      gd.c = pf->X; gd.ldc = H;
+      if ((e = launch_gemm(EPI_RESID, true, gd, st)) != hipSuccess) return e;
+    }
+    if (last) {
+      hipLaunchKernelGGL(pf_lm, dim3(MK_NWG), dim3(PF_THREADS), 0, st, (const float *)pf->X, T - 1, d->lnf, d->rms_eps,
+                         d->embed, d->V, H, logits, pf->lmbest, d->ctl);
+      hipLaunchKernelGGL(pf_finish, dim3(1), dim3(64), 0, st, (const unsigned long long *)pf->lmbest, MK_NWG, argmax,
+                         d->ctl, T);
+    } else {
+      hipLaunchKernelGGL(pf_finish, dim3(1), dim3(64), 0, st, (const unsigned long long *)pf->lmbest, 0,
+                         (int32_t *)nullptr, d->ctl, T);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
