@@ -75,6 +75,36 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
   return s;
 }
 
+// Copy a [rows][cols] FP32 matrix (source row stride sstride) into LDS (row stride dstride; both
+// multiples of 4 floats).  Rows >= nvalid read as zero.  Every thread of the workgroup calls it;
+// each issues NB 16-byte loads before storing any, so the loads overlap instead of each paying
+// the full memory latency.
+template <int NB>
+__device__ __forceinline__ void g2l(float *dst, int dstride, const float *src, size_t sstride, int rows, int cols,
+                                    int nvalid) {
+  const int c4 = cols >> 2, total = rows * c4;
+  for (int base = 0; base < total; base += NB * PF_THREADS) {
+    float4 v[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int e = base + b * PF_THREADS + (int)threadIdx.x;
+      const int r = e / c4, c = e - r * c4;
+      v[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < total && r < nvalid) v[b] = *reinterpret_cast<const float4 *>(src + (size_t)r * sstride + c * 4);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int e = base + b * PF_THREADS + (int)threadIdx.x;
+      const int r = e / c4, c = e - r * c4;
+      if (e < total) *reinterpret_cast<float4 *>(dst + r * dstride + c * 4) = v[b];
+    }
+  }
+}
+__device__ __forceinline__ float dot4(const float4 a, const float4 b, float s) {
+  s = fmaf(a.x, b.x, s); s = fmaf(a.y, b.y, s); s = fmaf(a.z, b.z, s); return fmaf(a.w, b.w, s);
+}
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+
 // ------------------------------------------------------------------------------ row kernels
 __global__ void __launch_bounds__(PF_THREADS) pf_embed(const uint16_t *embed, const int32_t *tok, int H, int V,
                                                        float *X, int32_t *ctl) {
@@ -314,59 +344,80 @@ struct PfChunk {
 };
 
 // per (chunk, head): (I + A)^-1, the decay-weighted q.k matrix and the decays
+constexpr int CS = MK_CHUNK + 4;   // padded row stride of the chunk matrices in LDS
 __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
   extern __shared__ float sm[];
   const int ch = blockIdx.x, h = blockIdx.y, nch = MK_PT / MK_CHUNK;
   const int t0 = ch * MK_CHUNK, Cn = min(MK_CHUNK, c.T - t0);
-  const int dk = c.dk, ks = dk + 1;           // padded rows: conflict-free column reads
+  const int dk = c.dk, ks = dk + 4;           // padded rows keep float4 reads conflict-free
   float *Ks = sm, *Qs = Ks + MK_CHUNK * ks;
-  float *A = Qs + MK_CHUNK * ks;              // [64][65]
-  float *X = A + MK_CHUNK * 65;               // [64][65]
-  float *Gs = X + MK_CHUNK * 65, *bs = Gs + MK_CHUNK;
+  float *A = Qs + MK_CHUNK * ks;              // [64][CS]
+  float *X = A + MK_CHUNK * CS;               // [64][CS]
+  float *Gs = X + MK_CHUNK * CS, *bs = Gs + MK_CHUNK;
   const size_t hb = (size_t)h * MK_PT;
-  for (int i = threadIdx.x; i < MK_CHUNK * dk; i += PF_THREADS) {
-    const int r = i / dk, e = i % dk;
-    Ks[r * ks + e] = r < Cn ? c.k[(hb + t0 + r) * dk + e] : 0.f;
-    Qs[r * ks + e] = r < Cn ? c.q[(hb + t0 + r) * dk + e] : 0.f;
+  const int tid = threadIdx.x;
+  g2l<8>(Ks, ks, c.k + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
+  g2l<8>(Qs, ks, c.q + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
+  if (tid < MK_CHUNK) bs[tid] = tid < Cn ? c.be[hb + t0 + tid] : 0.f;
+  if (tid < 64) {  // in-chunk prefix sums of log alpha (one wave, Hillis-Steele)
+    float G = tid < Cn ? c.la[hb + t0 + tid] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(G, o, 64);
+      if (tid >= o) G += y;
+    }
+    Gs[tid] = G;
   }
-  if (threadIdx.x < MK_CHUNK) bs[threadIdx.x] = threadIdx.x < Cn ? c.be[hb + t0 + threadIdx.x] : 0.f;
-  if (threadIdx.x == 0) {
-    float G = 0.f;
+  __syncthreads();
+  float *cM = c.cM + ((size_t)h * nch + ch) * MK_CHUNK * MK_CHUNK;
+  {  // thread -> 4x4 block of (i, j): k_i.k_j and q_i.k_j
+    const int i0 = (tid >> 4) * 4, j0 = (tid & 15) * 4;
+    float kk[4][4], qk[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) { kk[a][b] = 0.f; qk[a][b] = 0.f; }
+    if (j0 <= i0 + 3) {
+      for (int d = 0; d < dk; d += 4) {
+        float4 ki[4], qi[4], kj[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) { ki[a] = ld4(Ks + (i0 + a) * ks + d); qi[a] = ld4(Qs + (i0 + a) * ks + d); kj[a] = ld4(Ks + (j0 + a) * ks + d); }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) { kk[a][b] = dot4(ki[a], kj[b], kk[a][b]); qk[a][b] = dot4(qi[a], kj[b], qk[a][b]); }
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int i = i0 + a, j = j0 + b;
+        const bool lower = j <= i && i < Cn;
+        const float dec = lower ? expf(Gs[i] - Gs[j]) : 0.f;
+        A[i * CS + j] = (lower && j < i) ? bs[i] * dec * kk[a][b] : 0.f;
+        cM[i * MK_CHUNK + j] = dec * qk[a][b];
+      }
+  }
+  __syncthreads();
+  // X = (I + A)^-1 (unit lower triangular).  Column jj depends only on itself:
+  // X_ij = [i == j] - sum_{j <= m < i} A_im X_mj, so lane jj of wave 0 builds it alone.
+  if (tid < 64) {
+    const int jj = tid;
     for (int i = 0; i < MK_CHUNK; ++i) {
-      if (i < Cn) G += c.la[hb + t0 + i];
-      Gs[i] = G;
+      float s = (jj == i) ? 1.f : 0.f;
+      for (int m = jj; m < i; ++m) s = fmaf(-A[i * CS + m], X[m * CS + jj], s);
+      X[i * CS + jj] = (jj <= i) ? s : 0.f;
     }
   }
   __syncthreads();
   float *cT = c.cT + ((size_t)h * nch + ch) * MK_CHUNK * MK_CHUNK;
-  float *cM = c.cM + ((size_t)h * nch + ch) * MK_CHUNK * MK_CHUNK;
-  for (int e = threadIdx.x; e < MK_CHUNK * MK_CHUNK; e += PF_THREADS) {
-    const int i = e / MK_CHUNK, j = e % MK_CHUNK;
-    float kk = 0.f, qk = 0.f;
-    if (j <= i && i < Cn) {
-      for (int d = 0; d < dk; ++d) {
-        kk = fmaf(Ks[i * ks + d], Ks[j * ks + d], kk);
-        qk = fmaf(Qs[i * ks + d], Ks[j * ks + d], qk);
-      }
-    }
-    const float dec = (j <= i && i < Cn) ? expf(Gs[i] - Gs[j]) : 0.f;
-    A[i * 65 + j] = (j < i) ? bs[i] * dec * kk : 0.f;
-    cM[e] = dec * qk;
+  for (int e4 = tid; e4 < MK_CHUNK * MK_CHUNK / 4; e4 += PF_THREADS) {
+    const int i = e4 / (MK_CHUNK / 4), j = (e4 % (MK_CHUNK / 4)) * 4;
+    *reinterpret_cast<float4 *>(cT + i * MK_CHUNK + j) = ld4(X + i * CS + j);
   }
-  __syncthreads();
-  // X = (I + A)^-1 (unit lower triangular), one row at a time: X_i = e_i - sum_{m<i} A_im X_m
-  for (int i = 0; i < MK_CHUNK; ++i) {
-    if (threadIdx.x < MK_CHUNK) {
-      const int jj = threadIdx.x;
-      float s = (jj == i) ? 1.f : 0.f;
-      for (int m = jj; m < i; ++m) s = fmaf(-A[i * 65 + m], X[m * 65 + jj], s);
-      X[i * 65 + jj] = (jj <= i) ? s : 0.f;
-    }
-    __syncthreads();
-  }
-  for (int e = threadIdx.x; e < MK_CHUNK * MK_CHUNK; e += PF_THREADS) cT[e] = X[(e / MK_CHUNK) * 65 + e % MK_CHUNK];
-  if (threadIdx.x < MK_CHUNK) {
-    const int i = threadIdx.x;
+  if (tid < MK_CHUNK) {
+    const int i = tid;
     const size_t o = ((size_t)h * nch + ch) * MK_CHUNK + i;
     c.cg[o] = i < Cn ? expf(Gs[i]) : 0.f;
     c.cd[o] = i < Cn ? expf(Gs[Cn - 1] - Gs[i]) : 0.f;
@@ -386,17 +437,17 @@ struct PfScan {
 // carry RB rows of one head's state through every chunk of the pass
 __global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
   extern __shared__ float sm[];
-  const int h = blockIdx.y, r0 = blockIdx.x * RB, dk = s.dk, dv = s.dv, ks = dk + 1;
+  const int h = blockIdx.y, r0 = blockIdx.x * RB, dk = s.dk, dv = s.dv, ks = dk + 4;
   const int nch = MK_PT / MK_CHUNK, nchunk = (s.T + MK_CHUNK - 1) / MK_CHUNK;
   float *Sr = sm;                                  // [RB][dk]
   float *Ks = Sr + RB * dk, *Qs = Ks + MK_CHUNK * ks;
-  float *Tm = Qs + MK_CHUNK * ks, *Mm = Tm + MK_CHUNK * 65;
-  float *SK = Mm + MK_CHUNK * 65, *SQ = SK + RB * MK_CHUNK, *Bm = SQ + RB * MK_CHUNK, *U = Bm + RB * MK_CHUNK;
-  float *Vr = U + RB * MK_CHUNK;                   // [RB][64]
-  float *gs = Vr + RB * MK_CHUNK, *ds = gs + MK_CHUNK, *bs = ds + MK_CHUNK;
+  float *Tm = Qs + MK_CHUNK * ks, *Mm = Tm + MK_CHUNK * CS;
+  float *SQ = Mm + MK_CHUNK * CS, *Bm = SQ + RB * CS, *U = Bm + RB * CS;
+  float *Vr = U + RB * CS;                         // [64][RB]: token-major, as stored
+  float *gs = Vr + MK_CHUNK * RB, *ds = gs + MK_CHUNK, *bs = ds + MK_CHUNK;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float *Sg = s.S + ((size_t)h * dv + r0) * dk;
-  for (int i = tid; i < RB * dk; i += PF_THREADS) Sr[i] = Sg[i];
+  g2l<4>(Sr, dk, Sg, dk, RB, dk, RB);
   __syncthreads();
   // pending updates left by a verify forward (same arithmetic as the decode kernel's step)
   const int pend_n = s.ctl[MK_CTL_PEND], par = s.ctl[MK_CTL_PAR];
@@ -413,67 +464,77 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
   }
   __syncthreads();
   const size_t hb = (size_t)h * MK_PT;
+  const int ti = tid & 63, rp = (tid >> 6) * 2;    // token of this thread, its first state row (RB == 8)
   for (int c = 0; c < nchunk; ++c) {
     const int t0 = c * MK_CHUNK, Cn = min(MK_CHUNK, s.T - t0);
     const size_t cb = ((size_t)h * nch + c);
-    for (int i = tid; i < MK_CHUNK * dk; i += PF_THREADS) {
-      const int r = i / dk, e = i % dk;
-      Ks[r * ks + e] = r < Cn ? s.k[(hb + t0 + r) * dk + e] : 0.f;
-      Qs[r * ks + e] = r < Cn ? s.q[(hb + t0 + r) * dk + e] : 0.f;
-    }
-    for (int i = tid; i < MK_CHUNK * MK_CHUNK; i += PF_THREADS) {
-      Tm[(i / MK_CHUNK) * 65 + i % MK_CHUNK] = s.cT[cb * MK_CHUNK * MK_CHUNK + i];
-      Mm[(i / MK_CHUNK) * 65 + i % MK_CHUNK] = s.cM[cb * MK_CHUNK * MK_CHUNK + i];
-    }
-    for (int i = tid; i < RB * MK_CHUNK; i += PF_THREADS) {
-      const int r = i / MK_CHUNK, t = i % MK_CHUNK;
-      Vr[i] = t < Cn ? s.v[(hb + t0 + t) * dv + r0 + r] : 0.f;
-    }
+    g2l<8>(Ks, ks, s.k + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
+    g2l<8>(Qs, ks, s.q + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
+    g2l<4>(Tm, CS, s.cT + cb * MK_CHUNK * MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK);
+    g2l<4>(Mm, CS, s.cM + cb * MK_CHUNK * MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK);
+    g2l<1>(Vr, RB, s.v + (hb + t0) * dv + r0, dv, MK_CHUNK, RB, Cn);
     if (tid < MK_CHUNK) {
       gs[tid] = s.cg[cb * MK_CHUNK + tid];
       ds[tid] = s.cd[cb * MK_CHUNK + tid];
       bs[tid] = tid < Cn ? s.be[hb + t0 + tid] : 0.f;
     }
     __syncthreads();
-    // S0 k_i and S0 q_i for my rows
-    for (int e = tid; e < RB * MK_CHUNK; e += PF_THREADS) {
-      const int r = e / MK_CHUNK, i = e % MK_CHUNK;
-      float a = 0.f, b = 0.f;
-      for (int d = 0; d < dk; ++d) {
-        const float sv = Sr[r * dk + d];
-        a = fmaf(sv, Ks[i * ks + d], a);
-        b = fmaf(sv, Qs[i * ks + d], b);
+    {  // S0 k_i and S0 q_i for rows rp, rp+1 -> B and SQ
+      float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+      for (int d = 0; d < dk; d += 4) {
+        const float4 k4 = ld4(Ks + ti * ks + d), q4 = ld4(Qs + ti * ks + d);
+        const float4 s0 = ld4(Sr + rp * dk + d), s1 = ld4(Sr + (rp + 1) * dk + d);
+        a0 = dot4(s0, k4, a0); b0 = dot4(s0, q4, b0);
+        a1 = dot4(s1, k4, a1); b1 = dot4(s1, q4, b1);
       }
-      SK[e] = a;
-      SQ[e] = b;
-      Bm[e] = bs[i] * (Vr[e] - gs[i] * a);
+      Bm[rp * CS + ti] = bs[ti] * (Vr[ti * RB + rp] - gs[ti] * a0);
+      Bm[(rp + 1) * CS + ti] = bs[ti] * (Vr[ti * RB + rp + 1] - gs[ti] * a1);
+      SQ[rp * CS + ti] = b0;
+      SQ[(rp + 1) * CS + ti] = b1;
     }
     __syncthreads();
-    for (int e = tid; e < RB * MK_CHUNK; e += PF_THREADS) {  // U = (I + A)^-1 B
-      const int r = e / MK_CHUNK, i = e % MK_CHUNK;
-      float u = 0.f;
-      for (int jj = 0; jj <= i; ++jj) u = fmaf(Tm[i * 65 + jj], Bm[r * MK_CHUNK + jj], u);
-      U[e] = u;
+    {  // U = (I + A)^-1 B  (the inverse is zero above the diagonal)
+      float u0 = 0.f, u1 = 0.f;
+      for (int j = 0; j <= ti; j += 4) {
+        const float4 t4 = ld4(Tm + ti * CS + j);
+        u0 = dot4(t4, ld4(Bm + rp * CS + j), u0);
+        u1 = dot4(t4, ld4(Bm + (rp + 1) * CS + j), u1);
+      }
+      U[rp * CS + ti] = u0;
+      U[(rp + 1) * CS + ti] = u1;
     }
     __syncthreads();
-    for (int e = tid; e < RB * MK_CHUNK; e += PF_THREADS) {  // outputs
-      const int r = e / MK_CHUNK, i = e % MK_CHUNK;
-      if (i < Cn) {
-        float o = gs[i] * SQ[e];
-        for (int jj = 0; jj <= i; ++jj) o = fmaf(Mm[i * 65 + jj], U[r * MK_CHUNK + jj], o);
-        s.o[(size_t)(t0 + i) * s.nh * dv + h * dv + r0 + r] = o;
+    if (ti < Cn) {  // outputs (the decay-weighted q.k matrix is zero above the diagonal)
+      float o0 = gs[ti] * SQ[rp * CS + ti], o1 = gs[ti] * SQ[(rp + 1) * CS + ti];
+      for (int j = 0; j <= ti; j += 4) {
+        const float4 m4 = ld4(Mm + ti * CS + j);
+        o0 = dot4(m4, ld4(U + rp * CS + j), o0);
+        o1 = dot4(m4, ld4(U + (rp + 1) * CS + j), o1);
       }
+      float *op = s.o + (size_t)(t0 + ti) * s.nh * dv + h * dv + r0 + rp;
+      op[0] = o0;
+      op[1] = o1;
     }
-    const float gl = gs[Cn - 1];
-    for (int e = tid; e < RB * dk; e += PF_THREADS) {  // end-of-chunk state
-      const int r = e / dk, d = e % dk;
-      float acc = 0.f;
-      for (int jj = 0; jj < Cn; ++jj) acc = fmaf(ds[jj] * U[r * MK_CHUNK + jj], Ks[jj * ks + d], acc);
-      Sr[e] = fmaf(gl, Sr[e], acc);
+    {  // end-of-chunk state: thread -> row tid / 32, columns 4 (tid % 32) .. +4
+      const float gl = gs[Cn - 1];
+      for (int e = tid; e < RB * (dk / 4); e += PF_THREADS) {
+        const int r = e / (dk / 4), d = (e % (dk / 4)) * 4;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < Cn; ++j) {
+          const float cf = ds[j] * U[r * CS + j];
+          const float4 k4 = ld4(Ks + j * ks + d);
+          acc.x = fmaf(cf, k4.x, acc.x); acc.y = fmaf(cf, k4.y, acc.y);
+          acc.z = fmaf(cf, k4.z, acc.z); acc.w = fmaf(cf, k4.w, acc.w);
+        }
+        float4 *sp = reinterpret_cast<float4 *>(Sr + r * dk + d);
+        const float4 sv = *sp;
+        *sp = make_float4(fmaf(gl, sv.x, acc.x), fmaf(gl, sv.y, acc.y), fmaf(gl, sv.z, acc.z), fmaf(gl, sv.w, acc.w));
+      }
     }
     __syncthreads();
   }
-  for (int i = tid; i < RB * dk; i += PF_THREADS) Sg[i] = Sr[i];
+  for (int i = tid; i < RB * dk / 4; i += PF_THREADS)
+    reinterpret_cast<float4 *>(Sg)[i] = reinterpret_cast<const float4 *>(Sr)[i];
 }
 
 // gated RMSNorm per (token, head): y = o / sqrt(mean(o^2) + eps) * g * SiLU(z), as bf16 hi + lo
@@ -541,39 +602,53 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att(PfAtt a) {
   const int qb = blockIdx.x, hq = blockIdx.y, hd = a.hd, kvh = hq * a.nkv / a.nq;
   const int p0 = a.ctl[MK_CTL_POS];
   const int t0 = qb * QB, nqr = min(QB, a.T - t0);
-  const int kh = hd + 1;
+  const int kh = hd + 4;                // padded rows: float4 reads stay conflict-free
   float *Qs = sm;                       // [QB][hd]
-  float *Ks = Qs + QB * hd;             // [KB][hd+1]
+  float *Ks = Qs + QB * hd;             // [KB][hd+4]
   float *Vs = Ks + KB * kh;             // [KB][hd]
   float *Ps = Vs + KB * hd;             // [QB][KB]
   float *mrow = Ps + QB * KB, *lrow = mrow + QB, *alpha = lrow + QB;
   const int tid = threadIdx.x;
   const float scale = 1.f / sqrtf((float)hd);
-  for (int e = tid; e < QB * hd; e += PF_THREADS) {
-    const int r = e / hd, d = e % hd;
-    Qs[e] = r < nqr ? a.aq[(size_t)(t0 + r) * a.nq * hd + hq * hd + d] : 0.f;
-  }
+  g2l<2>(Qs, hd, a.aq + (size_t)t0 * a.nq * hd + hq * hd, (size_t)a.nq * hd, QB, hd, nqr);
   if (tid < QB) { mrow[tid] = -INFINITY; lrow[tid] = 0.f; }
-  // accumulator: thread -> query tid / 16, dims (tid % 16) + 16 j
-  const int aq_ = tid / 16, ad = tid % 16;
+  // accumulator: thread -> query tid / 16, dims dpt (tid % 16) .. +dpt, dpt = hd / 16
+  const int aq_ = tid / 16, dpt = hd / 16, d0 = (tid % 16) * dpt;
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
   const int last = p0 + t0 + nqr - 1;   // largest query position
   const int nkb = last / KB + 1;
+  const int cpr = hd / 8;               // 16-byte chunks per K/V row
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
     const int k0 = kb * KB;
-    for (int e = tid; e < KB * hd; e += PF_THREADS) {
-      const int r = e / hd, d = e % hd, p = k0 + r;
-      float kv = 0.f, vv = 0.f;
-      if (p <= last) {
-        const size_t o = kv_off(a, p, kvh) + d;
-        kv = bf2f(a.kc[o]);
-        vv = bf2f(a.vc[o]);
+    {  // K and V rows of this block: 16-byte loads, all issued before any store
+      constexpr int NL = 4;             // chunks per thread (KB * 128 / 8 / 256)
+      uint4 kr[NL], vr[NL];
+#pragma unroll
+      for (int b = 0; b < NL; ++b) {
+        const int e = b * PF_THREADS + tid, r = e / cpr, cc = e % cpr, p = k0 + r;
+        kr[b] = make_uint4(0u, 0u, 0u, 0u);
+        vr[b] = make_uint4(0u, 0u, 0u, 0u);
+        if (r < KB && p <= last) {
+          const size_t o = kv_off(a, p, kvh) + cc * 8;
+          kr[b] = *reinterpret_cast<const uint4 *>(a.kc + o);
+          vr[b] = *reinterpret_cast<const uint4 *>(a.vc + o);
+        }
       }
-      Ks[r * kh + d] = kv;
-      Vs[r * hd + d] = vv;
+#pragma unroll
+      for (int b = 0; b < NL; ++b) {
+        const int e = b * PF_THREADS + tid, r = e / cpr, cc = e % cpr;
+        if (r < KB) {
+          float *kd = Ks + r * kh + cc * 8, *vd = Vs + r * hd + cc * 8;
+          const uint32_t kw[4] = {kr[b].x, kr[b].y, kr[b].z, kr[b].w}, vw[4] = {vr[b].x, vr[b].y, vr[b].z, vr[b].w};
+          *reinterpret_cast<float4 *>(kd) = make_float4(bf2f(kw[0] & 0xffffu), bf2f(kw[0] >> 16), bf2f(kw[1] & 0xffffu), bf2f(kw[1] >> 16));
+          *reinterpret_cast<float4 *>(kd + 4) = make_float4(bf2f(kw[2] & 0xffffu), bf2f(kw[2] >> 16), bf2f(kw[3] & 0xffffu), bf2f(kw[3] >> 16));
+          *reinterpret_cast<float4 *>(vd) = make_float4(bf2f(vw[0] & 0xffffu), bf2f(vw[0] >> 16), bf2f(vw[1] & 0xffffu), bf2f(vw[1] >> 16));
+          *reinterpret_cast<float4 *>(vd + 4) = make_float4(bf2f(vw[2] & 0xffffu), bf2f(vw[2] >> 16), bf2f(vw[3] & 0xffffu), bf2f(vw[3] >> 16));
+        }
+      }
     }
     __syncthreads();
     for (int e = tid; e < QB * KB; e += PF_THREADS) {
@@ -581,9 +656,9 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att(PfAtt a) {
       const int qp = p0 + t0 + r, kp = k0 + j;
       float s = -INFINITY;
       if (r < nqr && kp <= qp) {
-        float d0 = 0.f;
-        for (int d = 0; d < hd; ++d) d0 = fmaf(Qs[r * hd + d], Ks[j * kh + d], d0);
-        s = d0 * scale;
+        float dd = 0.f;
+        for (int d = 0; d < hd; d += 4) dd = dot4(ld4(Qs + r * hd + d), ld4(Ks + j * kh + d), dd);
+        s = dd * scale;
       }
       Ps[e] = s;
     }
@@ -607,12 +682,17 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att(PfAtt a) {
     {
       const float al = alpha[aq_];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = ad + 16 * j;
-        if (d < hd) {
-          float s = acc[j] * al;
-          for (int kk = 0; kk < KB; ++kk) s = fmaf(Ps[aq_ * KB + kk], Vs[kk * hd + d], s);
-          acc[j] = s;
+      for (int j = 0; j < 8; ++j) acc[j] *= al;
+      for (int kk = 0; kk < KB; ++kk) {
+        const float pk = Ps[aq_ * KB + kk];
+        const float *vp = Vs + kk * hd + d0;
+        const float4 v0 = ld4(vp);
+        acc[0] = fmaf(pk, v0.x, acc[0]); acc[1] = fmaf(pk, v0.y, acc[1]);
+        acc[2] = fmaf(pk, v0.z, acc[2]); acc[3] = fmaf(pk, v0.w, acc[3]);
+        if (dpt == 8) {
+          const float4 v1 = ld4(vp + 4);
+          acc[4] = fmaf(pk, v1.x, acc[4]); acc[5] = fmaf(pk, v1.y, acc[5]);
+          acc[6] = fmaf(pk, v1.z, acc[6]); acc[7] = fmaf(pk, v1.w, acc[7]);
         }
       }
     }
@@ -622,9 +702,8 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att(PfAtt a) {
     const float inv = lrow[aq_];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int d = ad + 16 * j;
-      if (d < hd) {
-        const size_t o = (size_t)(t0 + aq_) * a.ld + hq * hd + d;
+      if (j < dpt) {
+        const size_t o = (size_t)(t0 + aq_) * a.ld + hq * hd + d0 + j;
         split_store(acc[j] / inv, a.oh + o, a.ol + o);
       }
     }
@@ -722,11 +801,11 @@ static hipError_t launch_gemm(int epi, bool small, const PfGemm &g, hipStream_t 
   return hipGetLastError();
 }
 
-static size_t chunk_prep_lds(int dk) { return (size_t)(2 * MK_CHUNK * (dk + 1) + 2 * MK_CHUNK * 65 + 2 * MK_CHUNK) * 4; }
+static size_t chunk_prep_lds(int dk) { return (size_t)(2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 2 * MK_CHUNK) * 4; }
 static size_t scan_lds(int dk) {
-  return (size_t)(RB * dk + 2 * MK_CHUNK * (dk + 1) + 2 * MK_CHUNK * 65 + 5 * RB * MK_CHUNK + 3 * MK_CHUNK) * 4;
+  return (size_t)(RB * dk + 2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 3 * RB * CS + MK_CHUNK * RB + 3 * MK_CHUNK) * 4;
 }
-static size_t att_lds(int hd) { return (size_t)(QB * hd + KB * (hd + 1) + KB * hd + QB * KB + 3 * QB) * 4; }
+static size_t att_lds(int hd) { return (size_t)(QB * hd + KB * (hd + 4) + KB * hd + QB * KB + 3 * QB) * 4; }
 
 // Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table.
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
