@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 BASELINE_DECODE_TOKS = 413.0    # the pages' megakernel decode figure (tg128, RTX 3090)
 WORKLOAD_CHOICES = ["24L-pp520-tg128", "24L-pp8192-tg128", "tiny-pp16-tg16"]
 
@@ -48,6 +49,25 @@ def decode_bytes_per_token(cfg: W.ModelConfig, ctx: float) -> dict:
     kv_row = cfg.at_kv_heads * cfg.at_head_dim * 2 * 2      # K and V of one position, bf16
     kv = n_at * kv_row * (ctx + 1)
     return dict(weights=weights, all=weights + small + state + conv + kv)
+
+
+def prefill_flops(cfg: W.ModelConfig, T: int, p0: int = 0) -> dict:
+    """Algorithmic FLOPs of one prefill of T tokens starting at position p0.
+
+    Projections: 2 T x (every weight matrix but the embedding); causal attention: QK^T and
+    P.V over keys 0..p for each query (4 hd (p + 1) per query and head); delta rule:
+    6 dk dv per token and head (decay, S k, rank-1 update, S q); LM head of the last row."""
+    n_dn = sum(1 for k in cfg.layer_kinds if k == "D")
+    n_at = cfg.n_layers - n_dn
+    H, I = cfg.hidden, cfg.ffn
+    dn_mat = (2 * cfg.dn_qk + 2 * cfg.dn_v + 2 * cfg.dn_heads) * H + H * cfg.dn_v
+    at_mat = (cfg.at_q_heads + 2 * cfg.at_kv_heads) * cfg.at_head_dim * H + H * cfg.at_q_heads * cfg.at_head_dim
+    proj = 2.0 * T * (n_dn * dn_mat + n_at * at_mat + cfg.n_layers * 3 * H * I)
+    keys = sum(p0 + t + 1 for t in range(T))
+    att = 4.0 * cfg.at_head_dim * keys * cfg.at_q_heads * n_at
+    delta = 6.0 * cfg.dn_dk * cfg.dn_dv * cfg.dn_heads * T * n_dn
+    lm = 2.0 * cfg.vocab * H
+    return dict(projections=proj, attention=att, delta_rule=delta, lm_head=lm, all=proj + att + delta + lm)
 
 
 def source_hash() -> str:
@@ -166,6 +186,9 @@ def main():
     ctx_mid = wl.prompt_len + (T - 1) / 2.0
     by = decode_bytes_per_token(cfg, ctx_mid)
     achieved = by["all"] / (launch_us * 1e-6) / 1e9
+    pf = prefill_flops(cfg, wl.prompt_len)
+    pf_s = float(np.median(pre_ms)) * 1e-3
+    pf_tflops = pf["all"] / pf_s / 1e12
     kernel = "mk_forward<1>"
     traffic = load_traffic(kernel)
     line = {
@@ -184,6 +207,10 @@ def main():
         "config": {"workload": f"{cfg.name} pp{wl.prompt_len} tg{T} batch 1 (seeded random weights and prompt)",
                    "prompt_tokens": wl.prompt_len, "decode_tokens": T, "batch": 1},
         "prefill_tok_s": round(prefill_tok_s, 1),
+        "prefill_roofline": {"bound": "mfma", "achieved": round(pf_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(pf_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "flops_per_prefill": int(pf["all"]), "prefill_ms_median": round(pf_s * 1e3, 3),
+                             "weights_hbm_frac": round(by["weights"] / pf_s / 1e9 / HBM_PEAK_GBS, 4)},
         "decode_us_per_token": round(launch_us, 2),
         "hbm_weights_only_frac": round(by["weights"] / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

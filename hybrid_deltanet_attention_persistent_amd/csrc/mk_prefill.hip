@@ -33,6 +33,7 @@
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -100,6 +101,29 @@ __device__ __forceinline__ void g2l(float *dst, int dstride, const float *src, s
     }
   }
 }
+// The two halves of g2l for one batch of NB float4 per thread, so that a batch can be loaded
+// into registers well before it is stored (software prefetch).
+template <int NB>
+__device__ __forceinline__ void g2r(float4 (&v)[NB], const float *src, size_t sstride, int rows, int cols, int nvalid) {
+  const int c4 = cols >> 2, total = rows * c4;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int e = b * PF_THREADS + (int)threadIdx.x;
+    const int r = e / c4, c = e - r * c4;
+    v[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e < total && r < nvalid) v[b] = *reinterpret_cast<const float4 *>(src + (size_t)r * sstride + c * 4);
+  }
+}
+template <int NB>
+__device__ __forceinline__ void r2l(const float4 (&v)[NB], float *dst, int dstride, int rows, int cols) {
+  const int c4 = cols >> 2, total = rows * c4;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int e = b * PF_THREADS + (int)threadIdx.x;
+    const int r = e / c4, c = e - r * c4;
+    if (e < total) *reinterpret_cast<float4 *>(dst + r * dstride + c * 4) = v[b];
+  }
+}
 __device__ __forceinline__ float dot4(const float4 a, const float4 b, float s) {
   s = fmaf(a.x, b.x, s); s = fmaf(a.y, b.y, s); s = fmaf(a.z, b.z, s); return fmaf(a.w, b.w, s);
 }
@@ -156,75 +180,102 @@ __device__ __forceinline__ int tileG(int K) {
   return g;
 }
 
-template <int EPI, int MT, int NT>
+// Workgroup tile BM x BN (BM = WGM*MT*16, BN = WGN*NT*16, WGM*WGN = 4 waves), K in stages of 64.
+// Each stage of A (hi and lo) and W is copied into LDS once per workgroup (16-byte loads: 128
+// contiguous bytes per row), double-buffered: the next stage's loads are in flight while the
+// MFMAs of the current one run.  LDS rows are padded to 72 elements so the 16-byte fragment
+// reads of 8 consecutive rows hit distinct banks.
+constexpr int GBK = 64, GLD = GBK + 8;
+
+template <int EPI, int MT, int NT, int WGM, int WGN>
 __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int m0 = blockIdx.y * MT * 16;
-  const int n0 = (blockIdx.x * 4 + w) * NT * 16;
-  if (n0 >= g.N) return;  // no barriers in this kernel
+  constexpr int BM = WGM * MT * 16, BN = WGN * NT * 16;
+  constexpr int NA = 2 * BM * 8 / PF_THREADS, NB = BN * 8 / PF_THREADS;   // 16-byte loads per thread and stage
+  extern __shared__ uint16_t gsm[];
+  // stage buffer b: A at gsm + b * 2 BM GLD ([hi/lo][BM][GLD]), W at gsm + 4 BM GLD + b * BN GLD
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  const int bm0 = blockIdx.y * BM, bn0 = blockIdx.x * BN;
   const int G = tileG(g.ks), L = g.ks / 8 / G, RG = 64 / G, G8 = G * 8;
-  const uint16_t *bb[NT];
-  int rowpart[NT];
+  // staging: thread -> chunks c = tid + i*256 of A ([hi/lo][row][kg]) and of B ([row][kg])
+  const uint16_t *asrc[NA];
+  int aoff[NA];
 #pragma unroll
-  for (int ni = 0; ni < NT; ++ni) {
-    const int n = min(n0 + ni * 16 + (lane & 15), g.N - 1);
+  for (int i = 0; i < NA; ++i) {
+    const int c = tid + i * PF_THREADS, hl = c / (BM * 8), rem = c % (BM * 8), row = rem / 8, kg = rem % 8;
+    asrc[i] = (hl ? g.al : g.ah) + (size_t)(bm0 + row) * g.lda + kg * 8;
+    aoff[i] = (hl * BM + row) * GLD + kg * 8;
+  }
+  const uint16_t *bsrc[NB];
+  int brow[NB], bkg[NB], boff[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int c = tid + i * PF_THREADS, row = c / 8, kg = c % 8;
+    const int n = min(bn0 + row, g.N - 1);
     const int s = n < g.wend[0] ? 0 : (n < g.wend[1] ? 1 : 2);
     const int r = n - (s == 0 ? 0 : g.wend[s - 1]);
-    bb[ni] = g.wb[s];
-    rowpart[ni] = (r / RG) * L * 512 + (r % RG) * G8;
+    bsrc[i] = g.wb[s] + (r / RG) * L * 512 + (r % RG) * G8;
+    brow[i] = r;
+    bkg[i] = kg * 8;
+    boff[i] = row * GLD + kg * 8;
   }
-  const uint16_t *pah[MT], *pal[MT];
+  (void)brow;
+  u32x4 ra[NA], rb[NB];
+  auto fetch = [&](int k0) {
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi) {
-    const size_t row = (size_t)(m0 + mi * 16 + (lane & 15));
-    pah[mi] = g.ah + row * g.lda;
-    pal[mi] = g.al + row * g.lda;
-  }
+    for (int i = 0; i < NA; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(asrc[i] + k0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int k = k0 + bkg[i];
+      const int ksg = k / g.ks, j = k - ksg * g.ks;
+      rb[i] = *reinterpret_cast<const u32x4 *>(bsrc[i] + (size_t)ksg * g.kstride + (j / G8) * 512 + (j & (G8 - 1)));
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) *reinterpret_cast<u32x4 *>(gsm + buf * 2 * BM * GLD + aoff[i]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4 *>(gsm + 4 * BM * GLD + buf * BN * GLD + boff[i]) = rb[i];
+  };
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // this lane's k: segment kseg, offset j inside it
-  int kk = (lane >> 4) * 8, kseg = 0, j = kk;
-  while (j >= g.ks) { j -= g.ks; ++kseg; }
-  auto load = [&](int kcur, int ksg, int jj, bf16x8 (&fa)[MT], bf16x8 (&fl)[MT], bf16x8 (&fb)[NT]) {
+  const int nst = g.K / GBK;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    fetch((st + 1 < nst ? st + 1 : st) * GBK);   // branch-free: the last stage re-reads itself
+    const uint16_t *Ab = gsm + cur * 2 * BM * GLD, *Bb = gsm + 4 * BM * GLD + cur * BN * GLD;
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-      fa[mi] = *reinterpret_cast<const bf16x8 *>(pah[mi] + kcur);
-      fl[mi] = *reinterpret_cast<const bf16x8 *>(pal[mi] + kcur);
-    }
-    const int kpart = ksg * g.kstride + (jj / G8) * 512 + (jj & (G8 - 1));
+    for (int kk = 0; kk < GBK; kk += 32) {
+      const int kc = kk + (lane >> 4) * 8;
+      bf16x8 fa[MT], fl[MT], fb[NT];
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) fb[ni] = *reinterpret_cast<const bf16x8 *>(bb[ni] + rowpart[ni] + kpart);
-  };
-  bf16x8 fa[MT], fl[MT], fb[NT];
-  load(kk, kseg, j, fa, fl, fb);
-  for (int k0 = 0; k0 < g.K; k0 += 32) {
-    // advance to the next k step (the last iteration reloads the current one: branch-free)
-    int kn = kk, ksn = kseg, jn = j;
-    if (k0 + 32 < g.K) {
-      kn = kk + 32;
-      jn = j + 32;
-      while (jn >= g.ks) { jn -= g.ks; ++ksn; }
-    }
-    bf16x8 na[MT], nl[MT], nb[NT];
-    load(kn, ksn, jn, na, nl, nb);
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NT; ++ni) {
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+      for (int mi = 0; mi < MT; ++mi) {
+        const int row = wm * MT * 16 + mi * 16 + (lane & 15);
+        fa[mi] = *reinterpret_cast<const bf16x8 *>(Ab + row * GLD + kc);
+        fl[mi] = *reinterpret_cast<const bf16x8 *>(Ab + (BM + row) * GLD + kc);
       }
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) { fa[mi] = na[mi]; fl[mi] = nl[mi]; }
+      for (int ni = 0; ni < NT; ++ni)
+        fb[ni] = *reinterpret_cast<const bf16x8 *>(Bb + (wn * NT * 16 + ni * 16 + (lane & 15)) * GLD + kc);
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) fb[ni] = nb[ni];
-    kk = kn; kseg = ksn; j = jn;
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni) {
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+        }
+    }
+    if (st + 1 < nst) stash(cur ^ 1);
+    __syncthreads();
   }
   // epilogue
+  const int m0 = bm0 + wm * MT * 16, n0 = bn0 + wn * NT * 16;
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
@@ -395,20 +446,34 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
         const int i = i0 + a, j = j0 + b;
         const bool lower = j <= i && i < Cn;
         const float dec = lower ? expf(Gs[i] - Gs[j]) : 0.f;
-        A[i * CS + j] = (lower && j < i) ? bs[i] * dec * kk[a][b] : 0.f;
+        A[j * CS + i] = (lower && j < i) ? bs[i] * dec * kk[a][b] : 0.f;   // transposed: A[j][i] holds A_ij
         cM[i * MK_CHUNK + j] = dec * qk[a][b];
       }
   }
   __syncthreads();
-  // X = (I + A)^-1 (unit lower triangular).  Column jj depends only on itself:
-  // X_ij = [i == j] - sum_{j <= m < i} A_im X_mj, so lane jj of wave 0 builds it alone.
+  // X = (I + A)^-1 (unit lower triangular).  Column jj depends only on itself, so lane jj of
+  // wave 0 builds it alone, right-looking and held in registers: once row m of the column is
+  // final, it is eliminated from every row below (col_i -= A_im col_m).
   if (tid < 64) {
     const int jj = tid;
-    for (int i = 0; i < MK_CHUNK; ++i) {
-      float s = (jj == i) ? 1.f : 0.f;
-      for (int m = jj; m < i; ++m) s = fmaf(-A[i * CS + m], X[m * CS + jj], s);
-      X[i * CS + jj] = (jj <= i) ? s : 0.f;
+    float col[MK_CHUNK];
+#pragma unroll
+    for (int i = 0; i < MK_CHUNK; ++i) col[i] = (i == jj) ? 1.f : 0.f;
+#pragma unroll
+    for (int m = 0; m < MK_CHUNK - 1; ++m) {
+      const float xm = col[m];
+      const float *am = A + m * CS;            // A[m][i] = A_im (transposed)
+#pragma unroll
+      for (int i4 = ((m + 1) & ~3); i4 < MK_CHUNK; i4 += 4) {
+        const float4 a4 = ld4(am + i4);
+        if (i4 + 0 > m) col[i4 + 0] = fmaf(-a4.x, xm, col[i4 + 0]);
+        if (i4 + 1 > m) col[i4 + 1] = fmaf(-a4.y, xm, col[i4 + 1]);
+        if (i4 + 2 > m) col[i4 + 2] = fmaf(-a4.z, xm, col[i4 + 2]);
+        if (i4 + 3 > m) col[i4 + 3] = fmaf(-a4.w, xm, col[i4 + 3]);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < MK_CHUNK; ++i) X[i * CS + jj] = col[i];
   }
   __syncthreads();
   float *cT = c.cT + ((size_t)h * nch + ch) * MK_CHUNK * MK_CHUNK;
@@ -465,20 +530,34 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
   __syncthreads();
   const size_t hb = (size_t)h * MK_PT;
   const int ti = tid & 63, rp = (tid >> 6) * 2;    // token of this thread, its first state row (RB == 8)
-  for (int c = 0; c < nchunk; ++c) {
+  // the next chunk's inputs, loaded into registers while the current chunk is computed
+  float4 pK[8], pQ[8], pT[4], pM[4], pV[1];
+  float pg = 0.f, pd = 0.f, pb = 0.f;
+  auto fetch = [&](int c) {
     const int t0 = c * MK_CHUNK, Cn = min(MK_CHUNK, s.T - t0);
     const size_t cb = ((size_t)h * nch + c);
-    g2l<8>(Ks, ks, s.k + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
-    g2l<8>(Qs, ks, s.q + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
-    g2l<4>(Tm, CS, s.cT + cb * MK_CHUNK * MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK);
-    g2l<4>(Mm, CS, s.cM + cb * MK_CHUNK * MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK);
-    g2l<1>(Vr, RB, s.v + (hb + t0) * dv + r0, dv, MK_CHUNK, RB, Cn);
+    g2r<8>(pK, s.k + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
+    g2r<8>(pQ, s.q + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
+    g2r<4>(pT, s.cT + cb * MK_CHUNK * MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK);
+    g2r<4>(pM, s.cM + cb * MK_CHUNK * MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK);
+    g2r<1>(pV, s.v + (hb + t0) * dv + r0, dv, MK_CHUNK, RB, Cn);
     if (tid < MK_CHUNK) {
-      gs[tid] = s.cg[cb * MK_CHUNK + tid];
-      ds[tid] = s.cd[cb * MK_CHUNK + tid];
-      bs[tid] = tid < Cn ? s.be[hb + t0 + tid] : 0.f;
+      pg = s.cg[cb * MK_CHUNK + tid];
+      pd = s.cd[cb * MK_CHUNK + tid];
+      pb = tid < Cn ? s.be[hb + t0 + tid] : 0.f;
     }
+  };
+  fetch(0);
+  for (int c = 0; c < nchunk; ++c) {
+    const int t0 = c * MK_CHUNK, Cn = min(MK_CHUNK, s.T - t0);
+    r2l<8>(pK, Ks, ks, MK_CHUNK, dk);
+    r2l<8>(pQ, Qs, ks, MK_CHUNK, dk);
+    r2l<4>(pT, Tm, CS, MK_CHUNK, MK_CHUNK);
+    r2l<4>(pM, Mm, CS, MK_CHUNK, MK_CHUNK);
+    r2l<1>(pV, Vr, RB, MK_CHUNK, RB);
+    if (tid < MK_CHUNK) { gs[tid] = pg; ds[tid] = pd; bs[tid] = pb; }
     __syncthreads();
+    if (c + 1 < nchunk) fetch(c + 1);
     {  // S0 k_i and S0 q_i for rows rp, rp+1 -> B and SQ
       float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
       for (int d = 0; d < dk; d += 4) {
@@ -785,20 +864,26 @@ struct MkPfHost {
   MkPf pf;
 };
 
-static hipError_t launch_gemm(int epi, bool small, const PfGemm &g, hipStream_t st) {
-  const int MT = small ? 2 : 4, NT = small ? 2 : 4;
-  dim3 grid((g.N + 4 * NT * 16 - 1) / (4 * NT * 16), (g.M + MT * 16 - 1) / (MT * 16));
-  if (epi == EPI_STORE) {
-    if (small) hipLaunchKernelGGL((pf_gemm<EPI_STORE, 2, 2>), grid, dim3(PF_THREADS), 0, st, g);
-    else hipLaunchKernelGGL((pf_gemm<EPI_STORE, 4, 4>), grid, dim3(PF_THREADS), 0, st, g);
-  } else if (epi == EPI_RESID) {
-    if (small) hipLaunchKernelGGL((pf_gemm<EPI_RESID, 2, 2>), grid, dim3(PF_THREADS), 0, st, g);
-    else hipLaunchKernelGGL((pf_gemm<EPI_RESID, 4, 4>), grid, dim3(PF_THREADS), 0, st, g);
-  } else {
-    if (small) hipLaunchKernelGGL((pf_gemm<EPI_SWIGLU, 2, 2>), grid, dim3(PF_THREADS), 0, st, g);
-    else hipLaunchKernelGGL((pf_gemm<EPI_SWIGLU, 4, 4>), grid, dim3(PF_THREADS), 0, st, g);
+// wide projections: 64 x 256 workgroup tiles (4 waves of 64 x 64); 1024-wide outputs: 64 x 64
+template <int EPI, int MT, int NT, int WGM, int WGN>
+static hipError_t launch_gemm_t(const PfGemm &g, hipStream_t st) {
+  constexpr int BM = WGM * MT * 16, BN = WGN * NT * 16;
+  const size_t lds = (size_t)(4 * BM + 2 * BN) * GLD * 2;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void *)pf_gemm<EPI, MT, NT, WGM, WGN>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
   }
+  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
+  hipLaunchKernelGGL((pf_gemm<EPI, MT, NT, WGM, WGN>), grid, dim3(PF_THREADS), lds, st, g);
   return hipGetLastError();
+}
+static hipError_t launch_gemm(int epi, bool small, const PfGemm &g, hipStream_t st) {
+  if (g.K % GBK != 0) return hipErrorInvalidValue;
+  if (epi == EPI_STORE) return small ? launch_gemm_t<EPI_STORE, 2, 2, 2, 2>(g, st) : launch_gemm_t<EPI_STORE, 4, 4, 1, 4>(g, st);
+  if (epi == EPI_RESID) return small ? launch_gemm_t<EPI_RESID, 2, 2, 2, 2>(g, st) : launch_gemm_t<EPI_RESID, 4, 4, 1, 4>(g, st);
+  return small ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2>(g, st) : launch_gemm_t<EPI_SWIGLU, 4, 4, 1, 4>(g, st);
 }
 
 static size_t chunk_prep_lds(int dk) { return (size_t)(2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 2 * MK_CHUNK) * 4; }

@@ -251,6 +251,92 @@ def test_tiny_verify_is_bit_identical_to_sequential_decode(dev, tiny, n_good):
         x.close()
 
 
+def test_tiny_prefill_after_partial_verify(dev, tiny):
+    """A prefill right after a verify applies the verify's pending delta-rule updates first
+    (the state must be "after the accepted tokens"), then continues from there."""
+    cfg = W.TINY
+    prompt = W.make_prompt(cfg, 13, seed=31)
+    ref = OracleModel(cfg, tiny, C2)
+    r = Runner(cfg, tiny, dev)
+    g, _ = r.prefill(prompt)
+    t = argmax_lowest(ref.prefill(prompt))
+    assert g == t
+    # drafts: two correct greedy tokens, then a wrong one -> 3 accepted, 2 pending updates
+    probe = OracleModel(cfg, tiny, C2)
+    probe.prefill(prompt)
+    d1 = argmax_lowest(probe.decode(t))
+    d2 = argmax_lowest(probe.decode(d1))
+    toks = [t, d1, d2, (d2 + 7) % cfg.vocab, 11]
+    vg, n_acc, vl = r.verify(toks)
+    rg, rn, rl = ref.verify(toks)
+    assert n_acc == rn == 3 and vg == rg
+    for i in range(5):
+        close(vl[i], rl[i], f"verify column {i}")
+    more = W.make_prompt(cfg, 21, seed=32)
+    g, lg = r.prefill(more)
+    rl = ref.prefill(more)
+    close(lg, rl, "prefill after verify")
+    gr = argmax_lowest(rl)
+    assert g == gr
+    for i in range(3):
+        g, lg = r.decode(gr)
+        rl = ref.decode(gr)
+        close(lg, rl, f"decode {i}")
+        gr = argmax_lowest(rl)
+        assert g == gr
+    r.close()
+
+
+@pytest.mark.parametrize("lens", [[63], [64], [65, 1], [129, 70]])
+def test_tiny_prefill_ragged_chunks(dev, tiny, lens):
+    """Prompt lengths around the 64-token delta-rule chunk, in one or two calls."""
+    cfg = dataclasses_replace(W.TINY, max_ctx=256)
+    ref = OracleModel(cfg, tiny, C2)
+    r = Runner(cfg, tiny, dev)
+    for j, n in enumerate(lens):
+        prompt = W.make_prompt(cfg, n, seed=40 + j)
+        g, lg = r.prefill(prompt)
+        rl = ref.prefill(prompt)
+        close(lg, rl, f"prefill {j} ({n} tokens)")
+        assert g == argmax_lowest(rl)
+    g, lg = r.decode(g)
+    rl = ref.decode(argmax_lowest(rl))
+    close(lg, rl, "decode after prefill")
+    r.close()
+
+
+def dataclasses_replace(cfg, **kw):
+    import dataclasses
+    return dataclasses.replace(cfg, **kw)
+
+
+def test_tiny_prompt_spanning_two_passes(dev, tiny):
+    """1100 prompt tokens: two prefill passes (1024 + 76) in one call, then a second call whose
+    start is not chunk aligned, then decode."""
+    cfg = dataclasses_replace(W.TINY, max_ctx=1536)
+    ref = OracleModel(cfg, tiny, C2)
+    r = Runner(cfg, tiny, dev)
+    prompt = W.make_prompt(cfg, 1100, seed=51)
+    g, lg = r.prefill(prompt)
+    rl = ref.prefill(prompt)
+    close(lg, rl, "1100-token prefill")
+    assert g == argmax_lowest(rl)
+    more = W.make_prompt(cfg, 300, seed=52)
+    g, lg = r.prefill(more)
+    rl = ref.prefill(more)
+    close(lg, rl, "300-token prefill at position 1100")
+    gr = argmax_lowest(rl)
+    assert g == gr
+    for i in range(3):
+        g, lg = r.decode(gr)
+        rl = ref.decode(gr)
+        close(lg, rl, f"decode {i}")
+        gr = argmax_lowest(rl)
+        assert g == gr
+    assert r.m.sync() == 1403
+    r.close()
+
+
 # ---------------------------------------------------------------------------------- 24-layer model
 def golden(name):
     path = os.path.join(GOLDEN, name + ".npz")
