@@ -86,7 +86,7 @@ struct Plan {
   // prefill scratch (one pass of MK_PT tokens)
   int K1, NP;
   Region pf_X, pf_a1h, pf_a1l, pf_a2h, pf_a2l, pf_P, pf_q, pf_k, pf_v, pf_z, pf_la, pf_be, pf_cT, pf_cM, pf_cg, pf_cd,
-      pf_o, pf_aq, pf_lmbest;
+      pf_o, pf_aq, pf_lmbest, pf_part;
   size_t total;
 };
 
@@ -221,6 +221,7 @@ Plan make_plan(const mk_config *c) {
     p.pf_o = L.add(nhd * T * p.dv * 4);
     p.pf_aq = L.add(has_at ? T * p.nq * p.hd * 4 : 0);
     p.pf_lmbest = L.add((size_t)MK_NWG * 8);
+    p.pf_part = L.add((size_t)4 * T * H * 4);
   }
   p.total = (L.total + 255) & ~size_t(255);
   return p;
@@ -550,6 +551,7 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
     f.cT = (float *)P(p.pf_cT); f.cM = (float *)P(p.pf_cM); f.cg = (float *)P(p.pf_cg); f.cd = (float *)P(p.pf_cd);
     f.o = (float *)P(p.pf_o); f.aq = (float *)P(p.pf_aq);
     f.lmbest = (unsigned long long *)P(p.pf_lmbest);
+    f.part = (float *)P(p.pf_part);
     f.K1 = p.K1; f.NP = p.NP;
   }
   mm->arena = A;

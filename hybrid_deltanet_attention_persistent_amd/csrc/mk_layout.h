@@ -126,5 +126,6 @@ struct MkPf {
   float *o;                           // [PT][nh dv] delta-rule output
   float *aq;                          // [PT][nq hd] queries after RoPE
   unsigned long long *lmbest;         // [MK_NWG] packed (ordered value, ~index) candidates
+  float *part;                        // [4][PT][H] split-K partial sums
   int32_t K1, NP;
 };

@@ -171,8 +171,11 @@ struct PfGemm {
   int ldc;
   uint16_t *oh, *ol;
   int ldo;
+  int kper;            // K columns per split (blockIdx.z); == K without split-K
+  float *part;         // EPI_PART: split z writes part[z][row][ldc]
+  size_t part_stride;  // elements per split
 };
-enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PART = 3 };
 
 __device__ __forceinline__ int tileG(int K) {
   int c = K / 8, g = 64;
@@ -220,8 +223,8 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
     boff[i] = row * GLD + kg * 8;
   }
   (void)brow;
-  u32x4 ra[NA], rb[NB];
-  auto fetch = [&](int k0) {
+  u32x4 ra0[NA], rb0[NB], ra1[NA], rb1[NB];
+  auto fetch = [&](int k0, u32x4 (&ra)[NA], u32x4 (&rb)[NB]) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(asrc[i] + k0);
 #pragma unroll
@@ -231,7 +234,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
       rb[i] = *reinterpret_cast<const u32x4 *>(bsrc[i] + (size_t)ksg * g.kstride + (j / G8) * 512 + (j & (G8 - 1)));
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, const u32x4 (&ra)[NA], const u32x4 (&rb)[NB]) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) *reinterpret_cast<u32x4 *>(gsm + buf * 2 * BM * GLD + aoff[i]) = ra[i];
 #pragma unroll
@@ -242,14 +245,8 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
   for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nst = g.K / GBK;
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st & 1;
-    fetch((st + 1 < nst ? st + 1 : st) * GBK);   // branch-free: the last stage re-reads itself
-    const uint16_t *Ab = gsm + cur * 2 * BM * GLD, *Bb = gsm + 4 * BM * GLD + cur * BN * GLD;
+  auto compute = [&](int buf) {
+    const uint16_t *Ab = gsm + buf * 2 * BM * GLD, *Bb = gsm + 4 * BM * GLD + buf * BN * GLD;
 #pragma unroll
     for (int kk = 0; kk < GBK; kk += 32) {
       const int kc = kk + (lane >> 4) * 8;
@@ -271,7 +268,25 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[mi], fb[ni], acc[mi][ni], 0, 0, 0);
         }
     }
-    if (st + 1 < nst) stash(cur ^ 1);
+  };
+  // Stage st sits in LDS buffer st & 1 while stage st + 1 is in one register set and stage st + 2
+  // is being loaded into the other: each load has two stages of MFMAs to land.  Past the last
+  // stage the fetches re-read it (branch-free) and are never used.
+  const int kbeg = blockIdx.z * g.kper, nst = g.kper / GBK;
+  auto kof = [&](int st) { return kbeg + min(st, nst - 1) * GBK; };
+  fetch(kof(0), ra0, rb0);
+  stash(0, ra0, rb0);
+  fetch(kof(1), ra1, rb1);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    fetch(kof(st + 2), ra0, rb0);
+    compute(0);
+    stash(1, ra1, rb1);
+    __syncthreads();
+    if (st + 1 >= nst) break;
+    fetch(kof(st + 3), ra1, rb1);
+    compute(1);
+    stash(0, ra0, rb0);
     __syncthreads();
   }
   // epilogue
@@ -293,11 +308,32 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
             split_store(siluf_(v) * u, g.oh + o, g.ol + o);
           }
         } else if (row < g.M && col < g.N) {
-          float *cp = g.c + (size_t)row * g.ldc + col;
-          if (EPI == EPI_RESID) *cp = *cp + v;
-          else *cp = v;
+          if (EPI == EPI_PART) {
+            g.part[blockIdx.z * g.part_stride + (size_t)row * g.ldc + col] = v;
+          } else {
+            float *cp = g.c + (size_t)row * g.ldc + col;
+            if (EPI == EPI_RESID) *cp = *cp + v;
+            else *cp = v;
+          }
         }
       }
+}
+
+// X += sum over the splits of the split-K partials, in split order (deterministic)
+__global__ void __launch_bounds__(PF_THREADS) pf_split_reduce(float *X, const float *part, int nsplit, size_t stride,
+                                                              int N, int M) {
+  const int row = blockIdx.x;
+  if (row >= M) return;
+  for (int n4 = threadIdx.x; n4 < N / 4; n4 += PF_THREADS) {
+    float4 acc = reinterpret_cast<const float4 *>(part + (size_t)row * N)[n4];
+    for (int z = 1; z < nsplit; ++z) {
+      const float4 p = reinterpret_cast<const float4 *>(part + z * stride + (size_t)row * N)[n4];
+      acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+    float4 *xp = reinterpret_cast<float4 *>(X + (size_t)row * N) + n4;
+    const float4 xv = *xp;
+    *xp = make_float4(xv.x + acc.x, xv.y + acc.y, xv.z + acc.z, xv.w + acc.w);
+  }
 }
 
 // ------------------------------------------------------------------------------ DeltaNet
@@ -866,7 +902,7 @@ struct MkPfHost {
 
 // wide projections: 64 x 256 workgroup tiles (4 waves of 64 x 64); 1024-wide outputs: 64 x 64
 template <int EPI, int MT, int NT, int WGM, int WGN>
-static hipError_t launch_gemm_t(const PfGemm &g, hipStream_t st) {
+static hipError_t launch_gemm_t(const PfGemm &g, int nsplit, hipStream_t st) {
   constexpr int BM = WGM * MT * 16, BN = WGN * NT * 16;
   const size_t lds = (size_t)(4 * BM + 2 * BN) * GLD * 2;
   static bool attr = false;
@@ -875,15 +911,28 @@ static hipError_t launch_gemm_t(const PfGemm &g, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
+  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, nsplit);
   hipLaunchKernelGGL((pf_gemm<EPI, MT, NT, WGM, WGN>), grid, dim3(PF_THREADS), lds, st, g);
   return hipGetLastError();
 }
-static hipError_t launch_gemm(int epi, bool small, const PfGemm &g, hipStream_t st) {
+// Wide projections: 64 x 256 workgroup tiles (4 waves of 64 x 64).  The 1024-wide outputs that
+// add into the residual stream: 64 x 64 tiles and split-K (partials reduced in split order), so
+// that the grid fills the chip and each K stream is short.
+static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStream_t st) {
   if (g.K % GBK != 0) return hipErrorInvalidValue;
-  if (epi == EPI_STORE) return small ? launch_gemm_t<EPI_STORE, 2, 2, 2, 2>(g, st) : launch_gemm_t<EPI_STORE, 4, 4, 1, 4>(g, st);
-  if (epi == EPI_RESID) return small ? launch_gemm_t<EPI_RESID, 2, 2, 2, 2>(g, st) : launch_gemm_t<EPI_RESID, 4, 4, 1, 4>(g, st);
-  return small ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2>(g, st) : launch_gemm_t<EPI_SWIGLU, 4, 4, 1, 4>(g, st);
+  g.kper = g.K;
+  if (epi == EPI_STORE) return small ? launch_gemm_t<EPI_STORE, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_STORE, 4, 4, 1, 4>(g, 1, st);
+  if (epi == EPI_SWIGLU) return small ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_SWIGLU, 4, 4, 1, 4>(g, 1, st);
+  const int ns = g.K / GBK;
+  const int nsplit = (ns % 4 == 0 && ns >= 8) ? 4 : (ns % 2 == 0 && ns >= 4) ? 2 : 1;
+  if (nsplit == 1 || !part) return small ? launch_gemm_t<EPI_RESID, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_RESID, 4, 4, 1, 4>(g, 1, st);
+  g.kper = g.K / nsplit;
+  g.part = part;
+  g.part_stride = (size_t)MK_PT * g.ldc;
+  hipError_t e = small ? launch_gemm_t<EPI_PART, 2, 2, 2, 2>(g, nsplit, st) : launch_gemm_t<EPI_PART, 4, 4, 1, 4>(g, nsplit, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pf_split_reduce, dim3(g.M), dim3(PF_THREADS), 0, st, g.c, (const float *)part, nsplit, g.part_stride, g.N, g.M);
+  return hipGetLastError();
 }
 
 static size_t chunk_prep_lds(int dk) { return (size_t)(2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 2 * MK_CHUNK) * 4; }
@@ -920,7 +969,7 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         g.wb[0] = g.wb[1] = g.wb[2] = L.dn_in; g.wend[0] = g.wend[1] = g.wend[2] = g.N;
         g.ks = H; g.kstride = 0;
         g.c = pf->P; g.ldc = pf->NP;
-        hipError_t e = launch_gemm(EPI_STORE, false, g, st);
+        hipError_t e = launch_gemm(EPI_STORE, false, g, nullptr, st);
         if (e != hipSuccess) return e;
         PfDn dn{};
         dn.P = pf->P; dn.NP = pf->NP; dn.T = T; dn.conv = L.dn_conv; dn.ring = L.ring; dn.ctl = d->ctl;
@@ -940,7 +989,7 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         go.wb[0] = go.wb[1] = go.wb[2] = L.dn_out; go.wend[0] = go.wend[1] = go.wend[2] = H;
         go.ks = dv; go.kstride = H * dv;
         go.c = pf->X; go.ldc = H;
-        if ((e = launch_gemm(EPI_RESID, true, go, st)) != hipSuccess) return e;
+        if ((e = launch_gemm(EPI_RESID, true, go, pf->part, st)) != hipSuccess) return e;
       } else {
         g.N = (nq + 2 * nkv) * hd; g.K = H;
         g.wb[0] = L.at_q; g.wend[0] = nq * hd;
@@ -948,7 +997,7 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         g.wb[2] = L.at_v; g.wend[2] = g.N;
         g.ks = H; g.kstride = 0;
         g.c = pf->P; g.ldc = pf->NP;
-        hipError_t e = launch_gemm(EPI_STORE, false, g, st);
+        hipError_t e = launch_gemm(EPI_STORE, false, g, nullptr, st);
         if (e != hipSuccess) return e;
         PfAtt at{};
         at.P = pf->P; at.NP = pf->NP; at.T = T; at.rope = d->rope; at.page_table = d->page_table; at.ctl = d->ctl;
@@ -961,7 +1010,7 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         go.wb[0] = go.wb[1] = go.wb[2] = L.at_o; go.wend[0] = go.wend[1] = go.wend[2] = H;
         go.ks = hd; go.kstride = H * hd;
         go.c = pf->X; go.ldc = H;
-        if ((e = launch_gemm(EPI_RESID, true, go, st)) != hipSuccess) return e;
+        if ((e = launch_gemm(EPI_RESID, true, go, pf->part, st)) != hipSuccess) return e;
       }
       hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->X, L.ln2, H, d->rms_eps,
                          pf->a1h, pf->a1l, pf->K1);
@@ -970,14 +1019,14 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
       gu.wb[0] = gu.wb[1] = gu.wb[2] = L.ffn_gu; gu.wend[0] = gu.wend[1] = gu.wend[2] = 2 * I;
       gu.ks = H; gu.kstride = 0;
       gu.oh = pf->a2h; gu.ol = pf->a2l; gu.ldo = I;
-      hipError_t e = launch_gemm(EPI_SWIGLU, false, gu, st);
+      hipError_t e = launch_gemm(EPI_SWIGLU, false, gu, nullptr, st);
       if (e != hipSuccess) return e;
       PfGemm gd{};
       gd.ah = pf->a2h; gd.al = pf->a2l; gd.lda = I; gd.M = T; gd.N = H; gd.K = I;
       gd.wb[0] = gd.wb[1] = gd.wb[2] = L.ffn_dn; gd.wend[0] = gd.wend[1] = gd.wend[2] = H;
       gd.ks = J; gd.kstride = H * J;
       gd.c = pf->X; gd.ldc = H;
-      if ((e = launch_gemm(EPI_RESID, true, gd, st)) != hipSuccess) return e;
+      if ((e = launch_gemm(EPI_RESID, true, gd, pf->part, st)) != hipSuccess) return e;
     }
     if (last) {
       hipLaunchKernelGGL(pf_lm, dim3(MK_NWG), dim3(PF_THREADS), 0, st, (const float *)pf->X, T - 1, d->lnf, d->rms_eps,
