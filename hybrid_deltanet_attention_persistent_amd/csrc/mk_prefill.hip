@@ -38,7 +38,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int PF_THREADS = 256;
-constexpr int RB = 8;          // state rows per scan workgroup
+constexpr int RB = 4;          // state rows per scan workgroup (one per wave)
 constexpr int QB = 16;         // queries per attention workgroup
 constexpr int KB = 64;         // keys per attention block
 
@@ -362,20 +362,42 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_prep(PfDn d) {
   extern __shared__ float buf[];  // [C] conv outputs, then [2 nh] norms
   const int t = blockIdx.x;
   const int p0 = d.ctl[MK_CTL_POS];
-  for (int ch = threadIdx.x; ch < d.C; ch += PF_THREADS) {
-    const int col = dn_col(d, ch);
-    const float4 wt = *reinterpret_cast<const float4 *>(d.conv + ch * 4);
-    const float wv[4] = {wt.x, wt.y, wt.z, wt.w};
-    float acc = 0.f;
+  {  // every thread handles up to CPT channels; all their loads of one tap are issued together
+    constexpr int CPT = 12;   // C <= 3072
+    int col[CPT];
+    float4 wt[CPT];
+    float acc[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int ch = threadIdx.x + j * PF_THREADS;
+      col[j] = ch < d.C ? dn_col(d, ch) : 0;
+      wt[j] = ch < d.C ? *reinterpret_cast<const float4 *>(d.conv + ch * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      acc[j] = 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tt = t - 3 + i;     // tap i meets the token 3 - i steps before
-      float x = 0.f;
-      if (tt >= 0) x = d.P[(size_t)tt * d.NP + col];
-      else if (p0 + tt >= 0) x = d.ring[((p0 + tt) & (MK_RING - 1)) * d.C + ch];
-      acc = fmaf(wv[i], x, acc);
+      float x[CPT];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int ch = threadIdx.x + j * PF_THREADS;
+        x[j] = 0.f;
+        if (ch < d.C) {
+          if (tt >= 0) x[j] = d.P[(size_t)tt * d.NP + col[j]];
+          else if (p0 + tt >= 0) x[j] = d.ring[((p0 + tt) & (MK_RING - 1)) * d.C + ch];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const float wi = i == 0 ? wt[j].x : i == 1 ? wt[j].y : i == 2 ? wt[j].z : wt[j].w;
+        acc[j] = fmaf(wi, x[j], acc[j]);
+      }
     }
-    buf[ch] = siluf_(acc);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int ch = threadIdx.x + j * PF_THREADS;
+      if (ch < d.C) buf[ch] = siluf_(acc[j]);
+    }
   }
   __syncthreads();
   float *nrm = buf + d.C;
@@ -565,18 +587,35 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
   }
   __syncthreads();
   const size_t hb = (size_t)h * MK_PT;
-  const int ti = tid & 63, rp = (tid >> 6) * 2;    // token of this thread, its first state row (RB == 8)
+  const int ti = tid & 63, rp = tid >> 6;          // token and state row of this thread (RB == 4)
   // the next chunk's inputs, loaded into registers while the current chunk is computed
   float4 pK[8], pQ[8], pT[4], pM[4], pV[1];
   float pg = 0.f, pd = 0.f, pb = 0.f;
+  // per-thread element offsets of the chunk copies, the same for every chunk
+  int kq_row[8], kq_src[8], kq_dst[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int e = b * PF_THREADS + tid, r = e / (dk / 4), c4 = e - r * (dk / 4);
+    kq_row[b] = e < MK_CHUNK * dk / 4 ? r : MK_CHUNK;     // MK_CHUNK: no such element
+    kq_src[b] = r * dk + c4 * 4;
+    kq_dst[b] = r * ks + c4 * 4;
+  }
   auto fetch = [&](int c) {
     const int t0 = c * MK_CHUNK, Cn = min(MK_CHUNK, s.T - t0);
     const size_t cb = ((size_t)h * nch + c);
-    g2r<8>(pK, s.k + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
-    g2r<8>(pQ, s.q + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
-    g2r<4>(pT, s.cT + cb * MK_CHUNK * MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK);
-    g2r<4>(pM, s.cM + cb * MK_CHUNK * MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK, MK_CHUNK);
-    g2r<1>(pV, s.v + (hb + t0) * dv + r0, dv, MK_CHUNK, RB, Cn);
+    const float *kb = s.k + (hb + t0) * dk, *qb = s.q + (hb + t0) * dk;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool ok = kq_row[b] < Cn;
+      pK[b] = ok ? ld4(kb + kq_src[b]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      pQ[b] = ok ? ld4(qb + kq_src[b]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      pT[b] = ld4(s.cT + cb * MK_CHUNK * MK_CHUNK + (b * PF_THREADS + tid) * 4);
+      pM[b] = ld4(s.cM + cb * MK_CHUNK * MK_CHUNK + (b * PF_THREADS + tid) * 4);
+    }
+    pV[0] = (tid < Cn) ? ld4(s.v + (hb + t0 + tid) * dv + r0) : make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid < MK_CHUNK) {
       pg = s.cg[cb * MK_CHUNK + tid];
       pd = s.cd[cb * MK_CHUNK + tid];
@@ -586,55 +625,54 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
   fetch(0);
   for (int c = 0; c < nchunk; ++c) {
     const int t0 = c * MK_CHUNK, Cn = min(MK_CHUNK, s.T - t0);
-    r2l<8>(pK, Ks, ks, MK_CHUNK, dk);
-    r2l<8>(pQ, Qs, ks, MK_CHUNK, dk);
-    r2l<4>(pT, Tm, CS, MK_CHUNK, MK_CHUNK);
-    r2l<4>(pM, Mm, CS, MK_CHUNK, MK_CHUNK);
-    r2l<1>(pV, Vr, RB, MK_CHUNK, RB);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      if (kq_row[b] < MK_CHUNK) {
+        *reinterpret_cast<float4 *>(Ks + kq_dst[b]) = pK[b];
+        *reinterpret_cast<float4 *>(Qs + kq_dst[b]) = pQ[b];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int e = b * PF_THREADS + tid, i = e / (MK_CHUNK / 4), j4 = e % (MK_CHUNK / 4);
+      *reinterpret_cast<float4 *>(Tm + i * CS + j4 * 4) = pT[b];
+      *reinterpret_cast<float4 *>(Mm + i * CS + j4 * 4) = pM[b];
+    }
+    if (tid < MK_CHUNK) *reinterpret_cast<float4 *>(Vr + tid * RB) = pV[0];
     if (tid < MK_CHUNK) { gs[tid] = pg; ds[tid] = pd; bs[tid] = pb; }
     __syncthreads();
     if (c + 1 < nchunk) fetch(c + 1);
-    {  // S0 k_i and S0 q_i for rows rp, rp+1 -> B and SQ
-      float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+    {  // S0 k_i and S0 q_i for row rp -> B and SQ
+      float a0 = 0.f, b0 = 0.f;
+#pragma unroll 8
       for (int d = 0; d < dk; d += 4) {
-        const float4 k4 = ld4(Ks + ti * ks + d), q4 = ld4(Qs + ti * ks + d);
-        const float4 s0 = ld4(Sr + rp * dk + d), s1 = ld4(Sr + (rp + 1) * dk + d);
-        a0 = dot4(s0, k4, a0); b0 = dot4(s0, q4, b0);
-        a1 = dot4(s1, k4, a1); b1 = dot4(s1, q4, b1);
+        const float4 s0 = ld4(Sr + rp * dk + d);
+        a0 = dot4(s0, ld4(Ks + ti * ks + d), a0);
+        b0 = dot4(s0, ld4(Qs + ti * ks + d), b0);
       }
       Bm[rp * CS + ti] = bs[ti] * (Vr[ti * RB + rp] - gs[ti] * a0);
-      Bm[(rp + 1) * CS + ti] = bs[ti] * (Vr[ti * RB + rp + 1] - gs[ti] * a1);
       SQ[rp * CS + ti] = b0;
-      SQ[(rp + 1) * CS + ti] = b1;
     }
     __syncthreads();
     {  // U = (I + A)^-1 B  (the inverse is zero above the diagonal)
-      float u0 = 0.f, u1 = 0.f;
-      for (int j = 0; j <= ti; j += 4) {
-        const float4 t4 = ld4(Tm + ti * CS + j);
-        u0 = dot4(t4, ld4(Bm + rp * CS + j), u0);
-        u1 = dot4(t4, ld4(Bm + (rp + 1) * CS + j), u1);
-      }
+      float u0 = 0.f;
+#pragma unroll 4
+      for (int j = 0; j <= ti; j += 4) u0 = dot4(ld4(Tm + ti * CS + j), ld4(Bm + rp * CS + j), u0);
       U[rp * CS + ti] = u0;
-      U[(rp + 1) * CS + ti] = u1;
     }
     __syncthreads();
     if (ti < Cn) {  // outputs (the decay-weighted q.k matrix is zero above the diagonal)
-      float o0 = gs[ti] * SQ[rp * CS + ti], o1 = gs[ti] * SQ[(rp + 1) * CS + ti];
-      for (int j = 0; j <= ti; j += 4) {
-        const float4 m4 = ld4(Mm + ti * CS + j);
-        o0 = dot4(m4, ld4(U + rp * CS + j), o0);
-        o1 = dot4(m4, ld4(U + (rp + 1) * CS + j), o1);
-      }
-      float *op = s.o + (size_t)(t0 + ti) * s.nh * dv + h * dv + r0 + rp;
-      op[0] = o0;
-      op[1] = o1;
+      float o0 = gs[ti] * SQ[rp * CS + ti];
+#pragma unroll 4
+      for (int j = 0; j <= ti; j += 4) o0 = dot4(ld4(Mm + ti * CS + j), ld4(U + rp * CS + j), o0);
+      s.o[(size_t)(t0 + ti) * s.nh * dv + h * dv + r0 + rp] = o0;
     }
     {  // end-of-chunk state: thread -> row tid / 32, columns 4 (tid % 32) .. +4
       const float gl = gs[Cn - 1];
       for (int e = tid; e < RB * (dk / 4); e += PF_THREADS) {
         const int r = e / (dk / 4), d = (e % (dk / 4)) * 4;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
         for (int j = 0; j < Cn; ++j) {
           const float cf = ds[j] * U[r * CS + j];
           const float4 k4 = ld4(Ks + j * ks + d);
@@ -772,32 +810,43 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att(PfAtt a) {
       float s = -INFINITY;
       if (r < nqr && kp <= qp) {
         float dd = 0.f;
+#pragma unroll 8
         for (int d = 0; d < hd; d += 4) dd = dot4(ld4(Qs + r * hd + d), ld4(Ks + j * kh + d), dd);
         s = dd * scale;
       }
       Ps[e] = s;
     }
     __syncthreads();
-    if (tid < QB) {  // online softmax bookkeeping for row tid
-      const int r = tid;
-      float mx = mrow[r];
-      for (int j = 0; j < KB; ++j) mx = fmaxf(mx, Ps[r * KB + j]);
+    {  // online softmax bookkeeping: 16 lanes per query row, 4 keys per lane
+      const int r = tid / 16, j0 = (tid % 16) * 4;
+      const float4 s4 = ld4(Ps + r * KB + j0);
+      float mx = fmaxf(fmaxf(s4.x, s4.y), fmaxf(s4.z, s4.w));
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+      mx = fmaxf(mx, mrow[r]);
       const float al = (mx == -INFINITY) ? 1.f : expf(mrow[r] - mx);
-      float l = lrow[r] * al;
-      for (int j = 0; j < KB; ++j) {
-        const float p = (Ps[r * KB + j] == -INFINITY) ? 0.f : expf(Ps[r * KB + j] - mx);
-        Ps[r * KB + j] = p;
-        l += p;
+      float4 p4;
+      p4.x = (s4.x == -INFINITY) ? 0.f : expf(s4.x - mx);
+      p4.y = (s4.y == -INFINITY) ? 0.f : expf(s4.y - mx);
+      p4.z = (s4.z == -INFINITY) ? 0.f : expf(s4.z - mx);
+      p4.w = (s4.w == -INFINITY) ? 0.f : expf(s4.w - mx);
+      *reinterpret_cast<float4 *>(Ps + r * KB + j0) = p4;
+      float l = (p4.x + p4.y) + (p4.z + p4.w);
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) l += __shfl_xor(l, o, 16);
+      __syncthreads();   // every lane of the row has read mrow / lrow before lane 0 updates them
+      if ((tid % 16) == 0) {
+        lrow[r] = lrow[r] * al + l;
+        mrow[r] = mx;
+        alpha[r] = al;
       }
-      mrow[r] = mx;
-      lrow[r] = l;
-      alpha[r] = al;
     }
     __syncthreads();
     {
       const float al = alpha[aq_];
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] *= al;
+#pragma unroll 8
       for (int kk = 0; kk < KB; ++kk) {
         const float pk = Ps[aq_ * KB + kk];
         const float *vp = Vs + kk * hd + d0;
@@ -849,24 +898,40 @@ __global__ void __launch_bounds__(PF_THREADS) pf_lm(const float *X, int row, con
   const int r0 = (int)((long long)b * V / gridDim.x), r1 = (int)((long long)(b + 1) * V / gridDim.x);
   unsigned long long mybest = 0;
   int bad = 0;
-  for (int r = r0 + w; r < r1; r += PF_THREADS / 64) {
-    const uint16_t *er = embed + (size_t)r * H;
-    float p = 0.f;
-    for (int i = lane * 8; i < H; i += 512) {
-      const uint4 wv = *reinterpret_cast<const uint4 *>(er + i);
-      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+  constexpr int RBATCH = 8;   // rows per wave whose loads are in flight together
+  for (int rb = r0 + w * RBATCH; rb < r1; rb += (PF_THREADS / 64) * RBATCH) {
+    uint4 wv[RBATCH][2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p = fmaf(__uint_as_float(ww[e] << 16), hn[i + 2 * e], p);
-        p = fmaf(__uint_as_float(ww[e] & 0xffff0000u), hn[i + 2 * e + 1], p);
+    for (int q = 0; q < RBATCH; ++q)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int i = lane * 8 + h2 * 512;
+        wv[q][h2] = make_uint4(0u, 0u, 0u, 0u);
+        if (rb + q < r1 && i < H) wv[q][h2] = *reinterpret_cast<const uint4 *>(embed + (size_t)(rb + q) * H + i);
       }
-    }
-    const float tot = wave_sum(p);
-    if (lane == 0) {
-      if (logits) logits[r] = tot;
-      if (!(tot == tot) || isinf(tot)) bad = 1;
-      const unsigned long long k = pack_best(tot, r);
-      if (k > mybest) mybest = k;
+#pragma unroll
+    for (int q = 0; q < RBATCH; ++q) {
+      float p = 0.f;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int i = lane * 8 + h2 * 512;
+        if (i < H) {
+          const uint32_t ww[4] = {wv[q][h2].x, wv[q][h2].y, wv[q][h2].z, wv[q][h2].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p = fmaf(__uint_as_float(ww[e] << 16), hn[i + 2 * e], p);
+            p = fmaf(__uint_as_float(ww[e] & 0xffff0000u), hn[i + 2 * e + 1], p);
+          }
+        }
+      }
+      const float tot = wave_sum(p);
+      const int r = rb + q;
+      if (lane == 0 && r < r1) {
+        if (logits) logits[r] = tot;
+        if (!(tot == tot) || isinf(tot)) bad = 1;
+        const unsigned long long kk = pack_best(tot, r);
+        if (kk > mybest) mybest = kk;
+      }
     }
   }
   if (lane == 0) wb[w] = mybest;
