@@ -260,13 +260,17 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
 #pragma unroll
       for (int ni = 0; ni < NT; ++ni)
         fb[ni] = *reinterpret_cast<const bf16x8 *>(Bb + (wn * NT * 16 + ni * 16 + (lane & 15)) * GLD + kc);
+      // all hi terms first, then all lo terms: consecutive MFMAs never share an accumulator
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NT; ++ni) {
+        for (int ni = 0; ni < NT; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-        }
     }
   };
   // Stage st sits in LDS buffer st & 1 while stage st + 1 is in one register set and stage st + 2
@@ -568,6 +572,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
   float *SQ = Mm + MK_CHUNK * CS, *Bm = SQ + RB * CS, *U = Bm + RB * CS;
   float *Vr = U + RB * CS;                         // [64][RB]: token-major, as stored
   float *gs = Vr + MK_CHUNK * RB, *ds = gs + MK_CHUNK, *bs = ds + MK_CHUNK;
+  float *Sp = bs + MK_CHUNK;                       // [RB][dk] partial state update (second half of a chunk)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   float *Sg = s.S + ((size_t)h * dv + r0) * dk;
   g2l<4>(Sr, dk, Sg, dk, RB, dk, RB);
@@ -667,18 +672,28 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
       for (int j = 0; j <= ti; j += 4) o0 = dot4(ld4(Mm + ti * CS + j), ld4(U + rp * CS + j), o0);
       s.o[(size_t)(t0 + ti) * s.nh * dv + h * dv + r0 + rp] = o0;
     }
-    {  // end-of-chunk state: thread -> row tid / 32, columns 4 (tid % 32) .. +4
+    {  // end-of-chunk state: output e = (row, 4 columns); the two halves of the workgroup sum
+       // tokens [0, 32) and [32, Cn), the second half hands its partial over through LDS
       const float gl = gs[Cn - 1];
-      for (int e = tid; e < RB * (dk / 4); e += PF_THREADS) {
+      const int nout = RB * (dk / 4), half = tid / nout, e = tid - half * nout;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (half < 2) {
         const int r = e / (dk / 4), d = (e % (dk / 4)) * 4;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int j0 = half * (MK_CHUNK / 2), j1 = min(Cn, j0 + MK_CHUNK / 2);
 #pragma unroll 8
-        for (int j = 0; j < Cn; ++j) {
+        for (int j = j0; j < j1; ++j) {
           const float cf = ds[j] * U[r * CS + j];
           const float4 k4 = ld4(Ks + j * ks + d);
           acc.x = fmaf(cf, k4.x, acc.x); acc.y = fmaf(cf, k4.y, acc.y);
           acc.z = fmaf(cf, k4.z, acc.z); acc.w = fmaf(cf, k4.w, acc.w);
         }
+        if (half == 1) *reinterpret_cast<float4 *>(Sp + e * 4) = acc;
+      }
+      __syncthreads();
+      if (half == 0) {
+        const int r = e / (dk / 4), d = (e % (dk / 4)) * 4;
+        const float4 p2 = ld4(Sp + e * 4);
+        acc.x += p2.x; acc.y += p2.y; acc.z += p2.z; acc.w += p2.w;
         float4 *sp = reinterpret_cast<float4 *>(Sr + r * dk + d);
         const float4 sv = *sp;
         *sp = make_float4(fmaf(gl, sv.x, acc.x), fmaf(gl, sv.y, acc.y), fmaf(gl, sv.z, acc.z), fmaf(gl, sv.w, acc.w));
@@ -1002,7 +1017,7 @@ static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStr
 
 static size_t chunk_prep_lds(int dk) { return (size_t)(2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 2 * MK_CHUNK) * 4; }
 static size_t scan_lds(int dk) {
-  return (size_t)(RB * dk + 2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 3 * RB * CS + MK_CHUNK * RB + 3 * MK_CHUNK) * 4;
+  return (size_t)(2 * RB * dk + 2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 3 * RB * CS + MK_CHUNK * RB + 3 * MK_CHUNK) * 4;
 }
 static size_t att_lds(int hd) { return (size_t)(QB * hd + KB * (hd + 4) + KB * hd + QB * KB + 3 * QB) * 4; }
 
