@@ -347,7 +347,7 @@ static int check_device(int *dev) {
   if (prop.multiProcessorCount != MK_NWG)
     return fail(MK_ELAUNCH, "device has " + std::to_string(prop.multiProcessorCount) + " CUs, need 256 (8 XCDs x 32)");
   if (!prop.cooperativeLaunch) return fail(MK_ELAUNCH, "device has no cooperative launch");
-  for (int tmpl : {0, 1, MK_MAXCOL}) {  // 0: the prompt kernel
+  for (int tmpl : {1, MK_MAXCOL}) {
     int per_cu = 0;
     HIPCHECK(mk_forward_occupancy(tmpl, &per_cu));
     if (per_cu < 1) return fail(MK_ELAUNCH, "persistent kernel does not fit on a CU");
@@ -616,7 +616,6 @@ extern "C" int mk_decode_step(mk_model *m, const int32_t *d_tokens, int32_t n_to
   a.m = m->dev;
   a.tokens = d_tokens;
   a.n = n_tokens;
-  a.prefill = 0;
   a.tag0 = m->tag;
   a.argmax = d_argmax;
   a.logits = d_logits;

@@ -1,6 +1,6 @@
 // mk_forward.hip -- persistent single-launch forward pass of the hybrid Gated-DeltaNet +
-// attention decoder on MI355X (gfx950): one decode step, one multi-token verify
-// forward, or a prompt processed token by token, each in one cooperative launch.
+// attention decoder on MI355X (gfx950): one decode step or one multi-token verify
+// forward, each in one cooperative launch (prompts go through mk_prefill.hip).
 //
 // What it computes: the launch page "OS Megakernel that match M5 Max Tok/w at 2x
 // the Throughput on RTX 3090" (section "We wrote a single CUDA kernel that runs
@@ -22,7 +22,10 @@
 //     by a reduce-scatter (over XCDs) + all-gather (inside the XCD) per sublayer.
 //   * Weights stream once per forward in a tile layout that makes every wave load
 //     a contiguous 1 KiB (mk_layout.h), and each phase's weight rows are loaded
-//     into registers one phase ahead, so HBM latency overlaps the hand-off wait.
+//     into registers one phase ahead, so HBM latency overlaps the hand-off wait:
+//     in decode, waves 0-6 hold the weight loads and wave 7 alone polls (a poll
+//     waits for every older load of its wave), and workgroup barriers fence LDS
+//     only (a full fence would drain the weight loads at every barrier).
 //   * Decode and verify use the same per-column arithmetic in the same order, so
 //     a verify forward's logits are bit-identical to sequential decode steps.
 #include <hip/hip_runtime.h>
@@ -423,7 +426,7 @@ __device__ void rmsnorm_cols_r(const float *src, float *dst, float g0, float g1,
 typedef const __attribute__((address_space(4))) MkLayerDev ConstLayer;
 
 // ------------------------------------------------------------------------------ the kernel
-template <int NCOL, bool PROMPT>
+template <int NCOL>
 __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   extern __shared__ float lds_raw[];
   const MkDev &m = a.m;
@@ -432,7 +435,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // index derived from it is scalar too
   const int w8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = lane_id(), tid = threadIdx.x, tid0 = threadIdx.x;
-  // Decode and prompt: waves 0..6 stream weight rows, wave 7 polls the hand-offs (it holds no
+  // Decode: waves 0..6 stream weight rows, wave 7 polls the hand-offs (it holds no
   // weight loads, so its polls never wait behind them).  Verify: all 8 waves do both.
   constexpr int CW = (NCOL == 1) ? MK_WAVES - 1 : MK_WAVES;   // weight-streaming waves
   constexpr int NPW = (CW < MK_WAVES) ? MK_WAVES - CW : MK_WAVES;   // polling waves
@@ -460,9 +463,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   const int ctl_pos = __hip_atomic_load(m.ctl + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int pend_n = __hip_atomic_load(m.ctl + MK_CTL_PEND, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int par = __hip_atomic_load(m.ctl + MK_CTL_PAR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool verify = !PROMPT && a.n > 1;
-  const int nsteps = PROMPT ? a.n : 1;
-  const int ncol = PROMPT ? 1 : a.n;
+  const bool verify = a.n > 1;
+  const int ncol = a.n;
   const int G_h = mk_tile_G(H), L_h = H / 8 / G_h, RG_h = 64 / G_h;
   const int SL = H / MK_NL;  // residual slice per workgroup in the reductions
   const int nh = m.nh, dk = m.dk, dv = m.dv, nq = m.nq, nkv = m.nkv, hd = m.hd, J = m.J;
@@ -522,10 +524,10 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     keep_issued();
   };
 
-  for (int step = 0; step < nsteps; ++step) {
-    const uint32_t tg = a.tag0 + step;
-    const int pos0 = ctl_pos + step;       // position of column 0
-    const bool last_step = step == nsteps - 1;
+  {
+    const int step = 0;                    // (the watchdog's site code keeps a step field)
+    const uint32_t tg = a.tag0;
+    const int pos0 = ctl_pos;              // position of column 0
     int li = 0;
 
     float g1a = ld_gain(layers[0].ln1, H, tid);            // gains of the next RMSNorm
@@ -533,7 +535,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     issue_in(0);
     // ---- embedding rows
     for (int c = 0; c < ncol; ++c) {
-      int t = a.tokens[PROMPT ? step : c];
+      int t = a.tokens[c];
       if (t < 0 || t >= m.V) {
         if (tid == 0) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         t = 0;
@@ -715,10 +717,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               if (tid < RW) pc[dk + r0 + tid] = vr[c * RW + tid];
             }
           }
-          lbar();
-          // a prompt's next token reads the ring written here (other workgroups of the XCD); decode
-          // and verify state is read by the next launch only
-          if (PROMPT) wait_stores();
+          lbar();   // (the ring, S and pending updates written here are read by the next launch only)
           if (tid < ncol * RW) {
             const int c = tid / RW, r = tid - (tid / RW) * RW;
             pub(xo + c * m.x_o_len + r0 + r, outo[c * RW + r], tg);
@@ -840,8 +839,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                   float kf[8];
                   if (tpos < pos0) {
                     const uint32_t off = (uint32_t)((((size_t)m.page_table[tpos / MK_PAGE] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + d0) * 2;
-                    const u32x4 kw = PROMPT ? __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, AUX_DEV)
-                                            : __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+                    const u32x4 kw = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
                     unpack8(kw, kf);
                   } else {
                     const float *kk = qkv + (tpos - pos0) * 3 * hd + hd + d0;
@@ -879,8 +877,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                   float vvv;
                   if (tpos < pos0) {
                     const uint32_t off = (uint32_t)((((size_t)m.page_table[tpos / MK_PAGE] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + d) * 2;
-                    const uint32_t raw = PROMPT ? __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, AUX_DEV)
-                                                : __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, 0);
+                    const uint32_t raw = __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, 0);
                     vvv = __uint_as_float(raw << 16);
                   } else {
                     vvv = qkv[(tpos - pos0) * 3 * hd + 2 * hd + d];
@@ -1038,10 +1035,6 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       }
     }  // layers
 
-    if (!last_step) {
-      pend_n = 0;   // the pending updates were applied (and stored) during this token
-      continue;
-    }
     // ================================================================ LM head + greedy argmax
     rmsnorm_cols_r<NCOL>(xres, hn, g1a, g1b, H, m.rms_eps, ncol, red, tid0);
     {
@@ -1208,32 +1201,30 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             if (c < ncol) a.argmax[c] = gsel[c];
           if (a.n_acc) a.n_acc[0] = nacc;
           if (anynan) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_NAN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const int consumed = PROMPT ? a.n : (verify ? nacc : 1);
+          const int consumed = verify ? nacc : 1;
           __hip_atomic_store(m.ctl + MK_CTL_POS, ctl_pos + consumed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(m.ctl + MK_CTL_PEND, verify ? nacc : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(m.ctl + MK_CTL_PAR, verify ? (par ^ 1) : par, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
-  }  // steps
+  }
 }
 
 // ------------------------------------------------------------------------------ host-side launchers
-// Instantiations: one decode column, up to MK_MAXCOL verify columns, and the prompt
-// processed token by token (a distinct kernel so that profiles separate it).
-static const void *forward_fn(int ncol_template, int prompt) {
-  if (prompt) return (const void *)mk_forward<1, true>;
-  return (ncol_template == 1) ? (const void *)mk_forward<1, false> : (const void *)mk_forward<MK_MAXCOL, false>;
+// Instantiations: one decode column, and up to MK_MAXCOL verify columns.
+static const void *forward_fn(int ncol_template) {
+  return (ncol_template == 1) ? (const void *)mk_forward<1> : (const void *)mk_forward<MK_MAXCOL>;
 }
 
 extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, hipStream_t stream) {
   void *args[] = {const_cast<MkLaunch *>(a)};
-  return hipLaunchCooperativeKernel(forward_fn(ncol_template, a->prefill), dim3(MK_NWG), dim3(MK_THREADS), args,
+  return hipLaunchCooperativeKernel(forward_fn(ncol_template), dim3(MK_NWG), dim3(MK_THREADS), args,
                                     MK_LDS_BYTES, stream);
 }
 
 extern "C" hipError_t mk_forward_occupancy(int ncol_template, int *blocks_per_cu) {
-  const void *fn = forward_fn(ncol_template, ncol_template == 0);
+  const void *fn = forward_fn(ncol_template);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, MK_LDS_BYTES);
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, MK_THREADS, MK_LDS_BYTES);

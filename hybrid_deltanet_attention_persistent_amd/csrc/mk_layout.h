@@ -91,12 +91,11 @@ struct MkDev {
 // Arguments of one persistent-kernel launch.
 struct MkLaunch {
   MkDev m;
-  const int32_t *tokens;  // device: [n] (decode / verify) or the prompt (prefill)
-  int32_t n;              // columns (decode / verify) or prompt tokens (prefill)
-  int32_t prefill;        // 1: process the tokens one by one (prompt), 0: decode / verify columns
+  const int32_t *tokens;  // device: [n]
+  int32_t n;              // columns: 1 (decode) or 2..MK_MAXCOL (verify)
   uint32_t tag0;          // exchange tag of the first forward pass of this launch
-  int32_t *argmax;        // device: [n] (prefill: [1])
-  float *logits;          // device, nullable: [n][V] (prefill: [V])
+  int32_t *argmax;        // device: [n]
+  float *logits;          // device, nullable: [n][V]
   int32_t *n_acc;         // device, nullable
 };
 

@@ -119,10 +119,13 @@ int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, int32_t n_te
  * and position to zero, pending verify updates dropped, device error word cleared. */
 int mk_reset_state(mk_model *m, void *stream);
 
-/* Prefill: append d_tokens[0..n_tokens) (device int32) at the current position in
- * one launch, leave the state ready for decode, write the greedy token after the
- * last prompt token to d_next_token[0] (device int32) and, if d_last_logits is not
- * NULL, that position's logits to d_last_logits[0..vocab) (device float).        */
+/* Prefill: append d_tokens[0..n_tokens) (device int32) at the current position,
+ * leave the state ready for decode, write the greedy token after the last prompt
+ * token to d_next_token[0] (device int32) and, if d_last_logits is not NULL, that
+ * position's logits to d_last_logits[0..vocab) (device float).  The prompt runs in
+ * passes of up to 1024 tokens, each a stream-ordered sequence of kernels (MFMA
+ * projections, the delta rule in chunks of 64); nothing returns to the host
+ * between them.  Pending verify updates are applied first.                        */
 int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_next_token,
                float *d_last_logits, void *stream);
 
