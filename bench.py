@@ -122,6 +122,59 @@ def cpu_baseline(seconds: float = 15.0) -> dict:
                       f"one thread ({el:.1f} s)"}
 
 
+def extras(model, cfg, stream) -> dict:
+    """Secondary measurements on the same model: multi-token verify forwards after the pp520
+    prompt (1 accepted + 4 seeded random drafts each, state rolled back to the accepted prefix),
+    and decode at long context after an 8192-token prompt."""
+    import torch
+    dev = stream.device
+    out = {}
+    # verify: 64 forwards of [last accepted, 4 drafts]
+    prompt = torch.tensor(W.make_prompt(cfg, 520, seed=1), dtype=torch.int32, device=dev)
+    drafts = torch.tensor(W.make_drafts(cfg, 64, 5, seed=2), dtype=torch.int32, device=dev)
+    am = torch.zeros((64, 5), dtype=torch.int32, device=dev)
+    nacc = torch.zeros(64, dtype=torch.int32, device=dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    model.reset()
+    model.prefill(prompt, tok)
+    model.sync()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for f in range(64):
+        model.decode_step(drafts[f], am[f], None, nacc[f:f + 1])
+    e1.record(stream)
+    model.sync()
+    ms = e0.elapsed_time(e1)
+    acc = int(nacc.sum().item())
+    out["verify"] = {"forwards": 64, "tokens_per_forward": 5, "us_per_forward": round(ms * 1e3 / 64, 1),
+                     "forwards_per_s": round(64 / (ms * 1e-3), 1), "positions_per_s": round(5 * 64 / (ms * 1e-3), 1),
+                     "committed_tok_per_s_random_drafts": round(acc / (ms * 1e-3), 1),
+                     "accepted_per_forward_random_drafts": round(acc / 64, 3)}
+    # long context: 8192-token prompt, 128 decode steps
+    prompt = torch.tensor(W.make_prompt(cfg, 8192, seed=1), dtype=torch.int32, device=dev)
+    toks = torch.zeros(129, dtype=torch.int32, device=dev)
+    model.reset()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    model.prefill(prompt, toks[0:1])
+    p1.record(stream)
+    e0.record(stream)
+    for i in range(128):
+        model.decode_step(toks[i:i + 1], toks[i + 1:i + 2])
+    e1.record(stream)
+    model.sync()
+    pf_ms, dec_ms = p0.elapsed_time(p1), e0.elapsed_time(e1)
+    by = decode_bytes_per_token(cfg, 8192 + 63.5)
+    us = dec_ms * 1e3 / 128
+    pf = prefill_flops(cfg, 8192)
+    out["long_context_8192"] = {"decode_tok_s": round(128 / (dec_ms * 1e-3), 1), "decode_us_per_token": round(us, 1),
+                                "hbm_frac_all_bytes": round(by["all"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "hbm_frac_weights_only": round(by["weights"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "prefill_ms": round(pf_ms, 2), "prefill_tok_s": round(8192 / (pf_ms * 1e-3), 1),
+                                "prefill_mfma_frac": round(pf["all"] / (pf_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +183,8 @@ def main():
     ap.add_argument("--workload", default="24L-pp520-tg128", choices=WORKLOAD_CHOICES)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the secondary measurements (verify forwards, 8192-token context)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -218,6 +273,8 @@ def main():
                      "kernel": kernel, "bytes_per_launch": int(by["all"]),
                      "launch_us": round(launch_us, 2)},
     }
+    if not args.no_extras and wl.name == "24L-pp520-tg128":
+        line["extras"] = extras(model, cfg, stream)
     del model
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
