@@ -1001,8 +1001,8 @@ static hipError_t launch_gemm_t(const PfGemm &g, int nsplit, hipStream_t st) {
 static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStream_t st) {
   if (g.K % GBK != 0) return hipErrorInvalidValue;
   g.kper = g.K;
-  if (epi == EPI_STORE) return small ? launch_gemm_t<EPI_STORE, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_STORE, 4, 4, 1, 4>(g, 1, st);
-  if (epi == EPI_SWIGLU) return small ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_SWIGLU, 4, 4, 1, 4>(g, 1, st);
+  if (epi == EPI_STORE) return small ? launch_gemm_t<EPI_STORE, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_STORE, 4, 2, 1, 4>(g, 1, st);
+  if (epi == EPI_SWIGLU) return small ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_SWIGLU, 4, 2, 1, 4>(g, 1, st);
   const int ns = g.K / GBK;
   const int nsplit = (ns % 4 == 0 && ns >= 8) ? 4 : (ns % 2 == 0 && ns >= 4) ? 2 : 1;
   if (nsplit == 1 || !part) return small ? launch_gemm_t<EPI_RESID, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_RESID, 4, 4, 1, 4>(g, 1, st);
