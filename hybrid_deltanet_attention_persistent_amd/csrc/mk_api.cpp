@@ -80,7 +80,7 @@ struct LayerRegions {
 };
 
 struct Plan {
-  int H, V, I, J, nh, dk, dv, C, r_in, nq, nkv, hd, r_in_max, x_o_len, max_pages;
+  int H, V, I, J, nh, dk, dv, C, r_in, nq, nkv, hd, r_in_max, x_o_len, xm_len, max_pages;
   Region embed, lnf, rope, page_table, layer_table, ctl, x_arg;
   std::vector<LayerRegions> layers;
   // prefill scratch (one pass of MK_PT tokens)
@@ -153,6 +153,7 @@ Plan make_plan(const mk_config *c) {
   // attention: 32 partials {max, sum, acc[hd]}
   p.x_o_len = std::max(has_dn ? p.dv : 0, has_at ? MK_NL * (p.hd + 2) : 0);
   p.x_o_len = (p.x_o_len + 31) & ~31;
+  p.xm_len = (p.J + 31) & ~31;
   p.max_pages = c->max_ctx / MK_PAGE;
   const size_t H = p.H;
   Layout L;
@@ -193,7 +194,7 @@ Plan make_plan(const mk_config *c) {
     r.x_o = L.add((size_t)MK_NX * MK_MAXCOL * p.x_o_len * 8);
     r.x_mix = L.add((size_t)MK_MAXCOL * MK_NX * H * 8);
     r.x_r1 = L.add((size_t)MK_NX * MK_MAXCOL * H * 8);
-    r.x_m = L.add((size_t)MK_NX * MK_MAXCOL * p.J * 8);
+    r.x_m = L.add((size_t)MK_NX * MK_MAXCOL * p.xm_len * 8);
     r.x_ffn = L.add((size_t)MK_MAXCOL * MK_NX * H * 8);
     r.x_r2 = L.add((size_t)MK_NX * MK_MAXCOL * H * 8);
   }
@@ -395,7 +396,7 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   MkDev d{};
   d.n_layers = cfg->n_layers; d.H = p.H; d.V = p.V; d.I = p.I; d.J = p.J;
   d.nh = p.nh; d.dk = p.dk; d.dv = p.dv; d.C = p.C; d.r_in = p.r_in;
-  d.nq = p.nq; d.nkv = p.nkv; d.hd = p.hd; d.r_in_max = p.r_in_max; d.x_o_len = p.x_o_len;
+  d.nq = p.nq; d.nkv = p.nkv; d.hd = p.hd; d.r_in_max = p.r_in_max; d.x_o_len = p.x_o_len; d.xm_len = p.xm_len;
   d.max_ctx = cfg->max_ctx; d.max_pages = p.max_pages;
   d.rms_eps = cfg->rms_eps; d.l2_eps = cfg->l2_eps;
   d.embed = (const uint16_t *)(A + p.embed.off);

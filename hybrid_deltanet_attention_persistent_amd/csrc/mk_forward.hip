@@ -13,8 +13,9 @@
 //   * 256 workgroups x 512 threads, one per CU; workgroup b lives on XCD b % 8.
 //   * No grid barrier.  Every hand-off is a tagged exchange slot {value, tag}
 //     written once per forward; a consumer polls the slots it needs until every
-//     tag equals the forward's tag.  Slots are written and read with
-//     device-coherent (sc1) 64-bit stores and loads.
+//     tag equals the forward's tag.  Slots are read with device-coherent (sc1)
+//     loads, which skip the per-CU L1; a slot read by other XCDs is written through
+//     to memory, a slot read only inside the writer's XCD stops in that XCD's L2.
 //   * XCD x owns DeltaNet head x / query head x and FFN intermediate slice x, so
 //     in-projection -> conv -> delta rule -> gated norm -> out-projection stay
 //     inside one XCD; the out-projection and the FFN down-projection are split
@@ -135,9 +136,18 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 }
 
 // tagged exchange slot: 8 bytes {float bits, tag}, written with one device-coherent 64-bit store
+// (written through to memory, where the other XCDs' polls see it)
 __device__ __forceinline__ void pub(uint2 *p, float v, uint32_t tag) {
   __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), ((unsigned long long)tag << 32) | __float_as_uint(v),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A slot read only by workgroups of the writer's own XCD: the 64-bit store stops in that XCD's
+// L2, which the consumers' device-coherent loads (they skip the per-CU L1) read directly.  The
+// round trip is about half that of a store written through to memory.  Every such slot region is
+// owned by one XCD and padded to whole 256-byte blocks, so no cache line holds two XCDs' slots.
+__device__ __forceinline__ void pub_xcd(uint2 *p, float v, uint32_t tag) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), ((unsigned long long)tag << 32) | __float_as_uint(v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Watchdog expiry inside a gather: flag the workgroup and record the first failing site.
@@ -573,7 +583,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               rg_dot<NCOL, 2>(w_in[r], L_h, G_h, hn, H, ncol, o);
               if ((lane & (G_h - 1)) == 0) {
                 const int row = rg * RG_h + lane / G_h;
-                FOR_COL(c) pub(xin + c * m.r_in_max + row, o[c], tg);
+                FOR_COL(c) pub_xcd(xin + c * m.r_in_max + row, o[c], tg);
               }
             }
           }
@@ -720,7 +730,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           lbar();   // (the ring, S and pending updates written here are read by the next launch only)
           if (tid < ncol * RW) {
             const int c = tid / RW, r = tid - (tid / RW) * RW;
-            pub(xo + c * m.x_o_len + r0 + r, outo[c * RW + r], tg);
+            pub_xcd(xo + c * m.x_o_len + r0 + r, outo[c * RW + r], tg);
           }
         }
         // ---- D3: gated RMSNorm + out-projection columns of head x
@@ -772,7 +782,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               rg_dot<NCOL, 2>(w_in[r], L_h, G_h, hn, H, ncol, o);
               if ((lane & (G_h - 1)) == 0) {
                 const int row = t * hd + rg * RG_h + lane / G_h;
-                FOR_COL(c) pub(xin + c * m.r_in_max + row, o[c], tg);
+                FOR_COL(c) pub_xcd(xin + c * m.r_in_max + row, o[c], tg);
               }
             }
           }
@@ -893,11 +903,11 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 float acc = pv[d];
 #pragma unroll 1
                 for (int ww = 1; ww < MK_WAVES; ++ww) acc += pv[ww * hd + d];
-                pub(dst + 2 + d, acc, tg);
+                pub_xcd(dst + 2 + d, acc, tg);
               }
               if (tid == 0) {
-                pub(dst + 0, nk > 0 ? mx[0] : -INFINITY, tg);
-                pub(dst + 1, nk > 0 ? mx[1] : 0.f, tg);
+                pub_xcd(dst + 0, nk > 0 ? mx[0] : -INFINITY, tg);
+                pub_xcd(dst + 1, nk > 0 ? mx[1] : 0.f, tg);
               }
               lbar();
             }
@@ -965,14 +975,14 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           float sm = tmp[(c * MK_NX) * SL + k];
 #pragma unroll
           for (int g = 1; g < MK_NX; ++g) sm += tmp[(c * MK_NX + g) * SL + k];
-          pub(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, tg);
+          pub_xcd(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, tg);
         }
         if (!gather2d<MCL, NPW>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(9), tid)) MK_BAIL();
       }
       // ================================================================ FFN
       rmsnorm_cols_r<NCOL>(xres, hn, g2a, g2b, H, m.rms_eps, ncol, red, tid);
       {
-        uint2 *xm = ly.x_m + (size_t)x * MK_MAXCOL * J;
+        uint2 *xm = ly.x_m + (size_t)x * MK_MAXCOL * m.xm_len;
         // ---- F1: gate/up pairs j -> m_j = SiLU(g_j) * u_j (weights already in flight)
 #pragma unroll
         for (int pr = 0; pr < NPAIR; ++pr) {
@@ -990,7 +1000,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
 #pragma unroll
               for (int c = 0; c < NCOL; ++c) u[c] = __shfl_xor(g[c], 32, 64);
             }
-            if (lane == 0) FOR_COL(c) pub(xm + c * J + j, siluf_(g[c]) * u[c], tg);
+            if (lane == 0) FOR_COL(c) pub_xcd(xm + c * m.xm_len + j, siluf_(g[c]) * u[c], tg);
           }
         }
         // prefetch: down-projection rows (F2), in flight during the m hand-off
@@ -1000,7 +1010,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         keep_issued();
         // ---- F2: down-projection columns of slice x
         float *mv = work;  // [NCOL][J]
-        if (!gather2d<MCS, NPW>(xm, ncol, J, J, tg, mv, flag, m.ctl, SITE(11), tid)) MK_BAIL();
+        if (!gather2d<MCS, NPW>(xm, ncol, J, m.xm_len, tg, mv, flag, m.ctl, SITE(11), tid)) MK_BAIL();
         if (wx < nrg) {
           float oo[NCOL];
           rg_dot<NCOL, LMAX_D>(w_dn[0], L_d, G_d, mv, J, ncol, oo);
@@ -1029,7 +1039,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           float sm = tmp[(c * MK_NX) * SL + k];
 #pragma unroll
           for (int g = 1; g < MK_NX; ++g) sm += tmp[(c * MK_NX + g) * SL + k];
-          pub(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, tg);
+          pub_xcd(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, tg);
         }
         if (!gather2d<MCL, NPW>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(13), tid)) MK_BAIL();
       }

@@ -76,7 +76,7 @@ struct MkDev {
   int32_t n_layers, H, V, I, J;
   int32_t nh, dk, dv, C, r_in;        // r_in = 2dk + 2dv + 2
   int32_t nq, nkv, hd;
-  int32_t r_in_max, x_o_len;
+  int32_t r_in_max, x_o_len, xm_len;  // exchange row lengths (slots), multiples of 32: 256-byte blocks
   int32_t max_ctx, max_pages;
   float rms_eps, l2_eps;
   const uint16_t *embed;              // [V][H] (tile format with L == 1 or G == 64: row-major)
