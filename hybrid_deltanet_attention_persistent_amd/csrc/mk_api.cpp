@@ -16,8 +16,8 @@
 #include "mk.h"
 #include "mk_layout.h"
 
-extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, hipStream_t stream);
-extern "C" hipError_t mk_forward_occupancy(int ncol_template, int *blocks_per_cu);
+extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, int shape, hipStream_t stream);
+extern "C" hipError_t mk_forward_occupancy(int ncol_template, int shape, int *blocks_per_cu);
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
                                          const int32_t *tokens, int n, int32_t *argmax, float *logits,
                                          hipStream_t st);
@@ -348,11 +348,12 @@ static int check_device(int *dev) {
   if (prop.multiProcessorCount != MK_NWG)
     return fail(MK_ELAUNCH, "device has " + std::to_string(prop.multiProcessorCount) + " CUs, need 256 (8 XCDs x 32)");
   if (!prop.cooperativeLaunch) return fail(MK_ELAUNCH, "device has no cooperative launch");
-  for (int tmpl : {1, MK_MAXCOL}) {
-    int per_cu = 0;
-    HIPCHECK(mk_forward_occupancy(tmpl, &per_cu));
-    if (per_cu < 1) return fail(MK_ELAUNCH, "persistent kernel does not fit on a CU");
-  }
+  for (int shape : {MK_SHAPE_ANY, MK_SHAPE_H1024})
+    for (int tmpl : {1, MK_MAXCOL}) {
+      int per_cu = 0;
+      HIPCHECK(mk_forward_occupancy(tmpl, shape, &per_cu));
+      if (per_cu < 1) return fail(MK_ELAUNCH, "persistent kernel does not fit on a CU");
+    }
   return MK_OK;
 }
 
@@ -621,7 +622,7 @@ extern "C" int mk_decode_step(mk_model *m, const int32_t *d_tokens, int32_t n_to
   a.argmax = d_argmax;
   a.logits = d_logits;
   a.n_acc = d_n_accepted;
-  HIPCHECK(mk_launch_forward(&a, n_tokens == 1 ? 1 : MK_MAXCOL, st));
+  HIPCHECK(mk_launch_forward(&a, n_tokens == 1 ? 1 : MK_MAXCOL, mk_shape_of(m->dev), st));
   m->tag += 1;
   m->pos_hi += n_tokens;
   return MK_OK;

@@ -436,7 +436,7 @@ __device__ void rmsnorm_cols_r(const float *src, float *dst, float g0, float g1,
 typedef const __attribute__((address_space(4))) MkLayerDev ConstLayer;
 
 // ------------------------------------------------------------------------------ the kernel
-template <int NCOL>
+template <int NCOL, int SH>
 __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   extern __shared__ float lds_raw[];
   const MkDev &m = a.m;
@@ -452,7 +452,12 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   constexpr int NRG_O = (CW < MK_WAVES) ? 2 : 1;               // out-projection row groups per wave
   const int wx = (w8 < CW) ? lw * CW + w8 : (1 << 24);        // streaming-wave index inside the XCD
   const int XW = MK_NL * CW;                                   // streaming waves per XCD
-  const int H = m.H;
+  // SH == MK_SHAPE_H1024 fixes every dimension of the hidden-1024 model (8 DeltaNet heads with
+  // d_k = d_v = 128, 8 query and 2 KV heads of 128, FFN 3584) at compile time: tile strides,
+  // row-group counts and reduction widths fold into straight-line code.  SH == MK_SHAPE_ANY reads
+  // them from the launch arguments.
+  constexpr bool FX = SH == MK_SHAPE_H1024;
+  const int H = FX ? 1024 : m.H;
   // the layer table is read-only: reading it through the constant address space gives
   // scalar loads, so every pointer taken from it is known to be wave-uniform
   ConstLayer *const layers = (ConstLayer *)(uintptr_t)m.layers;
@@ -477,7 +482,10 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   const int ncol = a.n;
   const int G_h = mk_tile_G(H), L_h = H / 8 / G_h, RG_h = 64 / G_h;
   const int SL = H / MK_NL;  // residual slice per workgroup in the reductions
-  const int nh = m.nh, dk = m.dk, dv = m.dv, nq = m.nq, nkv = m.nkv, hd = m.hd, J = m.J;
+  const int nh = FX ? 8 : m.nh, dk = FX ? 128 : m.dk, dv = FX ? 128 : m.dv;
+  const int nq = FX ? 8 : m.nq, nkv = FX ? 2 : m.nkv, hd = FX ? 128 : m.hd, J = FX ? 448 : m.J;
+  const int r_in = FX ? 514 : m.r_in, nconv = FX ? 3072 : m.C;
+  const int r_in_max = FX ? 544 : m.r_in_max, x_o_len = FX ? 4160 : m.x_o_len, xm_len = FX ? 448 : m.xm_len;
   const int G_o = mk_tile_G(dv), RG_o = 64 / G_o;        // out-projection columns of one head: L == 1
   const int G_a = mk_tile_G(hd), RG_a = 64 / G_a;        // o-projection columns of one head: L == 1
   const int G_d = mk_tile_G(J), L_d = J / 8 / G_d, RG_d = 64 / G_d;
@@ -497,12 +505,12 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     ConstLayer &ly = layers[live ? li : 0];
     const bool dn = ly.kind == 0;
     const int per = hd / RG_h;                     // row groups of one attention head
-    const int nrg = !live ? 0 : dn ? ((x < nh) ? m.r_in / RG_h : 0) : ((x < nq) ? 3 * per : 0);
+    const int nrg = !live ? 0 : dn ? ((x < nh) ? r_in / RG_h : 0) : ((x < nq) ? 3 * per : 0);
 #pragma unroll
     for (int r = 0; r < NRG_IN; ++r) {
       const int u = wx + r * XW;
       const int t = dn ? 0 : min(u / per, 2), rg = dn ? u : u - t * per;
-      const uint16_t *tile = dn ? ly.dn_in + (size_t)x * m.r_in * H
+      const uint16_t *tile = dn ? ly.dn_in + (size_t)x * r_in * H
                            : (t == 0) ? ly.at_q + (size_t)x * hd * H
                            : (t == 1) ? ly.at_k + (size_t)(x * nkv / nq) * hd * H
                                       : ly.at_v + (size_t)(x * nkv / nq) * hd * H;
@@ -569,12 +577,12 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       rmsnorm_cols_r<NCOL>(xres, hn, g1a, g1b, H, m.rms_eps, ncol, red, tid);
       if (ly.kind == 0) {
         // ================================================ DeltaNet layer
-        uint2 *xin = ly.x_in + (size_t)x * MK_MAXCOL * m.r_in_max;
-        uint2 *xo = ly.x_o + (size_t)x * MK_MAXCOL * m.x_o_len;
+        uint2 *xin = ly.x_in + (size_t)x * MK_MAXCOL * r_in_max;
+        uint2 *xo = ly.x_o + (size_t)x * MK_MAXCOL * x_o_len;
         const int RW = dv / MK_NL, r0 = lw * RW;
         // ---- D1: in-projection rows of head x (weights already in flight)
         if (x < nh) {
-          const int nrg = m.r_in / RG_h;
+          const int nrg = r_in / RG_h;
 #pragma unroll
           for (int r = 0; r < NRG_IN; ++r) {
             const int rg = wx + r * XW;
@@ -583,7 +591,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               rg_dot<NCOL, 2>(w_in[r], L_h, G_h, hn, H, ncol, o);
               if ((lane & (G_h - 1)) == 0) {
                 const int row = rg * RG_h + lane / G_h;
-                FOR_COL(c) pub_xcd(xin + c * m.r_in_max + row, o[c], tg);
+                FOR_COL(c) pub_xcd(xin + c * r_in_max + row, o[c], tg);
               }
             }
           }
@@ -618,18 +626,18 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           gn = (tid < dv) ? ly.dn_gnorm[tid] : 0.f;   // gated-norm gain, used in D3
           if (tid < nch) {
             wt = *reinterpret_cast<const float4 *>(ly.dn_conv + ch * 4);
-            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(ly.ring, 0, MK_RING * m.C * 4, RSRC_W3);
+            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(ly.ring, 0, MK_RING * nconv * 4, RSRC_W3);
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
               const int pp = pos0 - 3 + i;
               if (pp >= 0)
-                hist[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, ((pp & (MK_RING - 1)) * m.C + ch) * 4, 0, AUX_DEV));
+                hist[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, ((pp & (MK_RING - 1)) * nconv + ch) * 4, 0, AUX_DEV));
             }
           }
           {
-            const GSeg sg[3] = {{0, ncol, 2 * dk, m.r_in_max, qk},                 // q, k pre-conv
-                                {2 * dk + r0, ncol, RW, m.r_in_max, vr},           // my v rows
-                                {2 * dk + 2 * dv, ncol, 2, m.r_in_max, ab}};       // a, b
+            const GSeg sg[3] = {{0, ncol, 2 * dk, r_in_max, qk},                 // q, k pre-conv
+                                {2 * dk + r0, ncol, RW, r_in_max, vr},           // my v rows
+                                {2 * dk + 2 * dv, ncol, 2, r_in_max, ab}};       // a, b
             if (!gather_segs<MCS, NPW, 3>(xin, sg, tg, flag, m.ctl, SITE(1), tid)) MK_BAIL();
           }
           // conv + SiLU: threads [0, 2dk) are the q/k channels of head x, [2dk, 2dk+RW) my v channels
@@ -659,7 +667,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 cur[c * cstride] = siluf_(sacc);
               }
               if (tid >= 2 * dk || lw == 0)
-                FOR_COL(c) ly.ring[((pos0 + c) & (MK_RING - 1)) * m.C + ch] = raw[c];
+                FOR_COL(c) ly.ring[((pos0 + c) & (MK_RING - 1)) * nconv + ch] = raw[c];
             }
           }
           lbar();
@@ -730,7 +738,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           lbar();   // (the ring, S and pending updates written here are read by the next launch only)
           if (tid < ncol * RW) {
             const int c = tid / RW, r = tid - (tid / RW) * RW;
-            pub_xcd(xo + c * m.x_o_len + r0 + r, outo[c * RW + r], tg);
+            pub_xcd(xo + c * x_o_len + r0 + r, outo[c * RW + r], tg);
           }
         }
         // ---- D3: gated RMSNorm + out-projection columns of head x
@@ -738,8 +746,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           float *o = work;                 // [NCOL][dv]
           float *z = o + NCOL * dv;        // [NCOL][dv]
           {
-            const GSeg sg[2] = {{(int)(xo - xin), ncol, dv, m.x_o_len, o},       // o rows of the head
-                                {2 * dk + dv, ncol, dv, m.r_in_max, z}};         // z of the head
+            const GSeg sg[2] = {{(int)(xo - xin), ncol, dv, x_o_len, o},       // o rows of the head
+                                {2 * dk + dv, ncol, dv, r_in_max, z}};         // z of the head
             if (!gather_segs<MCS, NPW, 2>(xin, sg, tg, flag, m.ctl, SITE(4), tid)) MK_BAIL();
           }
           for (int c = 0; c < ncol; ++c) {
@@ -768,8 +776,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       } else {
         // ================================================ attention layer
         const int kvh = x * nkv / nq;
-        uint2 *xin = ly.x_in + (size_t)x * MK_MAXCOL * m.r_in_max;
-        uint2 *xo = ly.x_o + (size_t)x * MK_MAXCOL * m.x_o_len;
+        uint2 *xin = ly.x_in + (size_t)x * MK_MAXCOL * r_in_max;
+        uint2 *xo = ly.x_o + (size_t)x * MK_MAXCOL * x_o_len;
         if (x < nq) {
           // ---- A1: q rows of head x, k/v rows of its kv head (weights already in flight)
           const int per = hd / RG_h;
@@ -782,7 +790,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               rg_dot<NCOL, 2>(w_in[r], L_h, G_h, hn, H, ncol, o);
               if ((lane & (G_h - 1)) == 0) {
                 const int row = t * hd + rg * RG_h + lane / G_h;
-                FOR_COL(c) pub_xcd(xin + c * m.r_in_max + row, o[c], tg);
+                FOR_COL(c) pub_xcd(xin + c * r_in_max + row, o[c], tg);
               }
             }
           }
@@ -790,7 +798,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           keep_issued();
           // ---- A2: RoPE, KV append, split-KV partials
           float *qkv = work;                    // [NCOL][3hd]
-          if (!gather2d<MCS, NPW>(xin, ncol, 3 * hd, m.r_in_max, tg, qkv, flag, m.ctl, SITE(6), tid)) MK_BAIL();
+          if (!gather2d<MCS, NPW>(xin, ncol, 3 * hd, r_in_max, tg, qkv, flag, m.ctl, SITE(6), tid)) MK_BAIL();
           {
             const int half = hd / 2;
             for (int i = tid; i < ncol * half; i += MK_THREADS) {
@@ -898,7 +906,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               }
               lbar();
               const int plen = hd + 2;
-              uint2 *dst = xo + c * m.x_o_len + lw * plen;
+              uint2 *dst = xo + c * x_o_len + lw * plen;
               for (int d = tid; d < hd; d += MK_THREADS) {
                 float acc = pv[d];
 #pragma unroll 1
@@ -918,7 +926,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             float *part = work + 2048;             // [32][plen]
             float *ov = work;                      // [NCOL][hd]
             for (int c = 0; c < ncol; ++c) {
-              if (!gather2d<5, MK_WAVES>(xo + c * m.x_o_len, 1, MK_NL * plen, 0, tg, part, flag, m.ctl, SITE(7), tid)) MK_BAIL();
+              if (!gather2d<5, MK_WAVES>(xo + c * x_o_len, 1, MK_NL * plen, 0, tg, part, flag, m.ctl, SITE(7), tid)) MK_BAIL();
               // per-partial scale exp(m_w - M) (0 for workgroups without keys), once, in wave 0
               float *scl = part + MK_NL * plen;     // [32] scales, [32] = sum of l_w * scale
               if (w8 == 0) {
@@ -982,7 +990,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       // ================================================================ FFN
       rmsnorm_cols_r<NCOL>(xres, hn, g2a, g2b, H, m.rms_eps, ncol, red, tid);
       {
-        uint2 *xm = ly.x_m + (size_t)x * MK_MAXCOL * m.xm_len;
+        uint2 *xm = ly.x_m + (size_t)x * MK_MAXCOL * xm_len;
         // ---- F1: gate/up pairs j -> m_j = SiLU(g_j) * u_j (weights already in flight)
 #pragma unroll
         for (int pr = 0; pr < NPAIR; ++pr) {
@@ -1000,7 +1008,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
 #pragma unroll
               for (int c = 0; c < NCOL; ++c) u[c] = __shfl_xor(g[c], 32, 64);
             }
-            if (lane == 0) FOR_COL(c) pub_xcd(xm + c * m.xm_len + j, siluf_(g[c]) * u[c], tg);
+            if (lane == 0) FOR_COL(c) pub_xcd(xm + c * xm_len + j, siluf_(g[c]) * u[c], tg);
           }
         }
         // prefetch: down-projection rows (F2), in flight during the m hand-off
@@ -1010,7 +1018,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         keep_issued();
         // ---- F2: down-projection columns of slice x
         float *mv = work;  // [NCOL][J]
-        if (!gather2d<MCS, NPW>(xm, ncol, J, m.xm_len, tg, mv, flag, m.ctl, SITE(11), tid)) MK_BAIL();
+        if (!gather2d<MCS, NPW>(xm, ncol, J, xm_len, tg, mv, flag, m.ctl, SITE(11), tid)) MK_BAIL();
         if (wx < nrg) {
           float oo[NCOL];
           rg_dot<NCOL, LMAX_D>(w_dn[0], L_d, G_d, mv, J, ncol, oo);
@@ -1222,19 +1230,22 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
 }
 
 // ------------------------------------------------------------------------------ host-side launchers
-// Instantiations: one decode column, and up to MK_MAXCOL verify columns.
-static const void *forward_fn(int ncol_template) {
-  return (ncol_template == 1) ? (const void *)mk_forward<1> : (const void *)mk_forward<MK_MAXCOL>;
+// Instantiations: one decode column or up to MK_MAXCOL verify columns, each for the generic and the
+// hidden-1024 shape.
+static const void *forward_fn(int ncol_template, int shape) {
+  if (shape == MK_SHAPE_H1024)
+    return (ncol_template == 1) ? (const void *)mk_forward<1, MK_SHAPE_H1024> : (const void *)mk_forward<MK_MAXCOL, MK_SHAPE_H1024>;
+  return (ncol_template == 1) ? (const void *)mk_forward<1, MK_SHAPE_ANY> : (const void *)mk_forward<MK_MAXCOL, MK_SHAPE_ANY>;
 }
 
-extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, hipStream_t stream) {
+extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, int shape, hipStream_t stream) {
   void *args[] = {const_cast<MkLaunch *>(a)};
-  return hipLaunchCooperativeKernel(forward_fn(ncol_template), dim3(MK_NWG), dim3(MK_THREADS), args,
+  return hipLaunchCooperativeKernel(forward_fn(ncol_template, shape), dim3(MK_NWG), dim3(MK_THREADS), args,
                                     MK_LDS_BYTES, stream);
 }
 
-extern "C" hipError_t mk_forward_occupancy(int ncol_template, int *blocks_per_cu) {
-  const void *fn = forward_fn(ncol_template);
+extern "C" hipError_t mk_forward_occupancy(int ncol_template, int shape, int *blocks_per_cu) {
+  const void *fn = forward_fn(ncol_template, shape);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, MK_LDS_BYTES);
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, MK_THREADS, MK_LDS_BYTES);

@@ -99,6 +99,16 @@ struct MkLaunch {
   int32_t *n_acc;         // device, nullable
 };
 
+// Instantiations of the persistent kernel: MK_SHAPE_H1024 has every dimension of the hidden-1024
+// model as a compile-time constant; MK_SHAPE_ANY reads them from MkDev.
+enum { MK_SHAPE_ANY = 0, MK_SHAPE_H1024 = 1 };
+static inline int mk_shape_of(const MkDev &d) {
+  const bool h1024 = d.H == 1024 && d.nh == 8 && d.dk == 128 && d.dv == 128 && d.nq == 8 && d.nkv == 2 &&
+                     d.hd == 128 && d.J == 448 && d.r_in == 514 && d.C == 3072 && d.r_in_max == 544 &&
+                     d.x_o_len == 4160 && d.xm_len == 448;
+  return h1024 ? MK_SHAPE_H1024 : MK_SHAPE_ANY;
+}
+
 __host__ __device__ static inline int mk_tile_G(int K) {
   int c = K / 8, g = 64;
   while (g > 1 && (c % g) != 0) g >>= 1;
