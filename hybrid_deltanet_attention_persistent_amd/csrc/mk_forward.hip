@@ -106,13 +106,27 @@ __device__ __forceinline__ float row_sum16(float v) {
   v = dpp_add<DPP_HALF_MIRROR>(v);
   return dpp_add<DPP_MIRROR>(v);
 }
+// Sum over the 64 lanes in a fixed order: lane pairs (l, l ^ 32) through a permlane32 swap, then
+// (l, l ^ 16) through a permlane16 swap, then the 16-lane row tree above.  Every lane gets the
+// total.  Each swap returns {low half, high half} operands, so every add is (lower lane) + (upper).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float swap_add32(float a, float b) {  // lanes < 32: a[l] + a[l+32]; >= 32: b[l-32] + b[l]
+  const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(p.x) + __uint_as_float(p.y);
+}
+__device__ __forceinline__ float swap_add16(float a, float b) {  // rows {0,1,2,3} <- a r0+r1, b r0+r1, a r2+r3, b r2+r3
+  const u32x2 p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(p.x) + __uint_as_float(p.y);
+}
 __device__ __forceinline__ float wave_sum(float v) {
-  v = row_sum16(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (r0 + r1) + (r2 + r3);
+  v = swap_add32(v, v);
+  v = swap_add16(v, v);
+  return row_sum16(v);
+}
+// Four wave sums at once, each with exactly wave_sum's additions: lanes [0,16) get the total of a,
+// [16,32) of c, [32,48) of b, [48,64) of d.
+__device__ __forceinline__ float wave_sum4(float a, float b, float c, float d) {
+  return row_sum16(swap_add16(swap_add32(a, b), swap_add32(c, d)));
 }
 __device__ __forceinline__ float group_sum(float v, int G) {  // sum over aligned groups of G lanes
   if (G == 64) return wave_sum(v);
@@ -352,6 +366,12 @@ __device__ __forceinline__ float dot16(const u32x4 &w0, const u32x4 &w1, const f
   return s;
 }
 
+// Decode: dot product of one loaded row group with the activations in registers (rmsnorm_regs
+// layout), summed over each row's G lanes: the same products, order and tree as rg_dot.
+__device__ __forceinline__ float rg_dot_regs(const u32x4 &w0, const u32x4 &w1, int G, const float (&a)[16]) {
+  return group_sum(dot16(w0, w1, a), G);
+}
+
 // Sum each of 8 per-lane partials over the 64 lanes: a transposing butterfly that moves half of
 // the partials at each of the first three steps.  Returns, in lane l, the total of partial l >> 3.
 __device__ __forceinline__ float reduce8(const float (&p)[8]) {
@@ -389,35 +409,67 @@ __device__ __forceinline__ float wave_sum_lm(float t) {
   return dpp_add<DPP_HALF_MIRROR>(t);
 }
 
-// RMSNorm of src[c][H] into dst[c][H] with gain g.
+// RMSNorm.  The sum of squares of a hidden vector x[H] is taken the way the GEMV lanes hold the
+// vector: lane l owns elements (i G + l % G) 8 + e (i < L, e < 8; G, L: the tile layout of a
+// row of H), summed in that order, then over G lanes.  Every wave computes it itself, so the
+// norm needs no exchange between waves; decode and verify use this one order.
+__device__ __forceinline__ float col_sumsq(const float *x, int G, int L) {
+  const int kl = (lane_id() & (G - 1)) * 8;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i < L) {
+      const float4 a0 = *reinterpret_cast<const float4 *>(x + i * G * 8 + kl);
+      const float4 a1 = *reinterpret_cast<const float4 *>(x + i * G * 8 + kl + 4);
+      ss = fmaf(a0.x, a0.x, ss); ss = fmaf(a0.y, a0.y, ss); ss = fmaf(a0.z, a0.z, ss); ss = fmaf(a0.w, a0.w, ss);
+      ss = fmaf(a1.x, a1.x, ss); ss = fmaf(a1.y, a1.y, ss); ss = fmaf(a1.z, a1.z, ss); ss = fmaf(a1.w, a1.w, ss);
+    }
+  }
+  return group_sum(ss, G);
+}
+__device__ __forceinline__ float rms_scale(float sumsq, int H, float eps) { return 1.f / sqrtf(sumsq / (float)H + eps); }
+
+// RMSNorm of src[c][H] into dst[c][H] (LDS); thread t scales elements t and t + 512 (H <= 1024)
+// with the gains g0, g1 it holds.  Ends with a barrier.
 template <int NCOL>
-__device__ void rmsnorm_cols(const float *src, float *dst, const float *g, int H, float eps, int n, float *red) {
+__device__ void rmsnorm_cols_r(const float *src, float *dst, float g0, float g1, int H, int G, int L, float eps,
+                               int n, int tid) {
   for (int c = 0; c < NCOL; ++c) {
     if (c >= n) break;
-    float s = 0.f;
-    for (int k = threadIdx.x; k < H; k += MK_THREADS) s = fmaf(src[c * H + k], src[c * H + k], s);
-    const float tot = block_sum(s, red);
-    const float den = sqrtf(tot / (float)H + eps);
-    for (int k = threadIdx.x; k < H; k += MK_THREADS) dst[c * H + k] = src[c * H + k] / den * g[k];
+    const float r = rms_scale(col_sumsq(src + c * H, G, L), H, eps);
+    if (tid < H) dst[c * H + tid] = src[c * H + tid] * r * g0;
+    if (tid + MK_THREADS < H) dst[c * H + tid + MK_THREADS] = src[c * H + tid + MK_THREADS] * r * g1;
   }
   lbar();
 }
 
-// RMSNorm with the gains already in registers: thread t owns elements t and t + 512 (H <= 1024).
-template <int NCOL>
-__device__ void rmsnorm_cols_r(const float *src, float *dst, float g0, float g1, int H, float eps, int n,
-                               float *red, int tid) {
-  for (int c = 0; c < NCOL; ++c) {
-    if (c >= n) break;
-    float s = 0.f;
-    if (tid < H) s = fmaf(src[c * H + tid], src[c * H + tid], s);
-    if (tid + MK_THREADS < H) s = fmaf(src[c * H + tid + MK_THREADS], src[c * H + tid + MK_THREADS], s);
-    const float tot = block_sum(s, red);
-    const float den = sqrtf(tot / (float)H + eps);
-    if (tid < H) dst[c * H + tid] = src[c * H + tid] / den * g0;
-    if (tid + MK_THREADS < H) dst[c * H + tid + MK_THREADS] = src[c * H + tid + MK_THREADS] / den * g1;
-  }
-  lbar();
+// Decode: this lane's normalised activations of a hidden vector, in registers: element
+// (i G + l % G) 8 + e goes to a[i * 8 + e] (the operand layout of a tile row), with the gains the
+// lane holds in the same layout.  The same values as rmsnorm_cols_r, without LDS or barriers.
+__device__ __forceinline__ void rmsnorm_regs(const float *x, const float (&g)[16], int H, int G, int L, float eps,
+                                             float (&a)[16]) {
+  const float r = rms_scale(col_sumsq(x, G, L), H, eps);
+  const int kl = (lane_id() & (G - 1)) * 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[i * 8 + e] = (i < L) ? x[i * G * 8 + kl + e] * r * g[i * 8 + e] : 0.f;
+}
+// The gains of one RMSNorm in the operand layout of rmsnorm_regs (zeros past L), four 16-byte loads.
+// Branch-free: a wave that needs none passes live = false.
+__device__ __forceinline__ void ld_gain16(const float *p, int H, int G, bool live, float (&g)[16]) {
+  const __amdgpu_buffer_rsrc_t rs = tile_rsrc(p, live ? (uint32_t)(H * 4) : 0u);   // not live: zeros, no traffic
+  const int kl = (lane_id() & (G - 1)) * 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((i * G * 8 + kl + h * 4) * 4), 0, 0);
+      g[i * 8 + h * 4 + 0] = __uint_as_float(v.x);
+      g[i * 8 + h * 4 + 1] = __uint_as_float(v.y);
+      g[i * 8 + h * 4 + 2] = __uint_as_float(v.z);
+      g[i * 8 + h * 4 + 3] = __uint_as_float(v.w);
+    }
 }
 
 // loop over the live columns with compile-time indices (register arrays stay in registers)
@@ -548,8 +600,15 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     const int pos0 = ctl_pos;              // position of column 0
     int li = 0;
 
-    float g1a = ld_gain(layers[0].ln1, H, tid);            // gains of the next RMSNorm
-    float g1b = ld_gain(layers[0].ln1, H, tid + MK_THREADS);
+    // gains of the next RMSNorm: decode's weight-streaming lanes hold them in the operand layout of
+    // their tile rows (rmsnorm_regs), verify's threads hold elements t and t + 512
+    float g1v[16], g1a = 0.f, g1b = 0.f;
+    if constexpr (NCOL == 1) {
+      ld_gain16(layers[0].ln1, H, G_h, w8 < CW, g1v);
+    } else {
+      g1a = ld_gain(layers[0].ln1, H, tid);
+      g1b = ld_gain(layers[0].ln1, H, tid + MK_THREADS);
+    }
     issue_in(0);
     // ---- embedding rows
     for (int c = 0; c < ncol; ++c) {
@@ -572,9 +631,21 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       asm volatile("" : "+v"(tid));
       const int lane = tid & 63;
       // gains of this layer's FFN norm, needed after the mixer
-      const float g2a = ld_gain(ly.ln2, H, tid);
-      const float g2b = ld_gain(ly.ln2, H, tid + MK_THREADS);
-      rmsnorm_cols_r<NCOL>(xres, hn, g1a, g1b, H, m.rms_eps, ncol, red, tid);
+      float g2v[16], g2a = 0.f, g2b = 0.f;
+      if constexpr (NCOL == 1) {
+        ld_gain16(ly.ln2, H, G_h, w8 < CW, g2v);
+      } else {
+        g2a = ld_gain(ly.ln2, H, tid);
+        g2b = ld_gain(ly.ln2, H, tid + MK_THREADS);
+      }
+      // decode: each weight-streaming wave normalises the residual into registers itself (no LDS
+      // pass, no barrier); verify: into hn
+      float av[16];
+      if constexpr (NCOL == 1) {
+        if (w8 < CW) rmsnorm_regs(xres, g1v, H, G_h, L_h, m.rms_eps, av);
+      } else {
+        rmsnorm_cols_r<NCOL>(xres, hn, g1a, g1b, H, G_h, L_h, m.rms_eps, ncol, tid);
+      }
       if (ly.kind == 0) {
         // ================================================ DeltaNet layer
         uint2 *xin = ly.x_in + (size_t)x * MK_MAXCOL * r_in_max;
@@ -583,15 +654,31 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         // ---- D1: in-projection rows of head x (weights already in flight)
         if (x < nh) {
           const int nrg = r_in / RG_h;
+          if constexpr (NCOL == 1) {
+            if (G_h == 64) {  // one row per row group: the three rows of this wave reduced together
+              const float t = wave_sum4(dot16(w_in[0][0], w_in[0][1], av), dot16(w_in[1][0], w_in[1][1], av),
+                                        dot16(w_in[2][0], w_in[2][1], av), 0.f);
+              const int r = (lane == 0) ? 0 : (lane == 32) ? 1 : (lane == 16) ? 2 : NRG_IN;   // lanes holding row r
+              if (r < NRG_IN && wx + r * XW < nrg) pub_xcd(xin + (wx + r * XW), t, tg);
+            } else {
 #pragma unroll
-          for (int r = 0; r < NRG_IN; ++r) {
-            const int rg = wx + r * XW;
-            if (rg < nrg) {
-              float o[NCOL];
-              rg_dot<NCOL, 2>(w_in[r], L_h, G_h, hn, H, ncol, o);
-              if ((lane & (G_h - 1)) == 0) {
-                const int row = rg * RG_h + lane / G_h;
-                FOR_COL(c) pub_xcd(xin + c * r_in_max + row, o[c], tg);
+              for (int r = 0; r < NRG_IN; ++r) {
+                const int rg = wx + r * XW;
+                const float o = rg_dot_regs(w_in[r][0], w_in[r][1], G_h, av);
+                if (rg < nrg && (lane & (G_h - 1)) == 0) pub_xcd(xin + rg * RG_h + lane / G_h, o, tg);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < NRG_IN; ++r) {
+              const int rg = wx + r * XW;
+              if (rg < nrg) {
+                float o[NCOL];
+                rg_dot<NCOL, 2>(w_in[r], L_h, G_h, hn, H, ncol, o);
+                if ((lane & (G_h - 1)) == 0) {
+                  const int row = rg * RG_h + lane / G_h;
+                  FOR_COL(c) pub_xcd(xin + c * r_in_max + row, o[c], tg);
+                }
               }
             }
           }
@@ -781,16 +868,36 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         if (x < nq) {
           // ---- A1: q rows of head x, k/v rows of its kv head (weights already in flight)
           const int per = hd / RG_h;
+          if constexpr (NCOL == 1) {
+            if (G_h == 64) {  // as D1: three rows reduced together (row group u is row u)
+              const float tt = wave_sum4(dot16(w_in[0][0], w_in[0][1], av), dot16(w_in[1][0], w_in[1][1], av),
+                                         dot16(w_in[2][0], w_in[2][1], av), 0.f);
+              const int r = (lane == 0) ? 0 : (lane == 32) ? 1 : (lane == 16) ? 2 : NRG_IN;
+              const int u = wx + r * XW;
+              if (r < NRG_IN && u < 3 * per) pub_xcd(xin + u, tt, tg);   // row t hd + rg == u when per == hd
+            } else {
 #pragma unroll
-          for (int r = 0; r < NRG_IN; ++r) {
-            const int u = wx + r * XW;
-            if (u < 3 * per) {
-              const int t = u / per, rg = u - t * per;
-              float o[NCOL];
-              rg_dot<NCOL, 2>(w_in[r], L_h, G_h, hn, H, ncol, o);
-              if ((lane & (G_h - 1)) == 0) {
-                const int row = t * hd + rg * RG_h + lane / G_h;
-                FOR_COL(c) pub_xcd(xin + c * r_in_max + row, o[c], tg);
+              for (int r = 0; r < NRG_IN; ++r) {
+                const int u = wx + r * XW;
+                const float o = rg_dot_regs(w_in[r][0], w_in[r][1], G_h, av);
+                if (u < 3 * per && (lane & (G_h - 1)) == 0) {
+                  const int t = u / per, rg = u - t * per;
+                  pub_xcd(xin + t * hd + rg * RG_h + lane / G_h, o, tg);
+                }
+              }
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < NRG_IN; ++r) {
+              const int u = wx + r * XW;
+              if (u < 3 * per) {
+                const int t = u / per, rg = u - t * per;
+                float o[NCOL];
+                rg_dot<NCOL, 2>(w_in[r], L_h, G_h, hn, H, ncol, o);
+                if ((lane & (G_h - 1)) == 0) {
+                  const int row = t * hd + rg * RG_h + lane / G_h;
+                  FOR_COL(c) pub_xcd(xin + c * r_in_max + row, o[c], tg);
+                }
               }
             }
           }
@@ -988,27 +1095,57 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         if (!gather2d<MCL, NPW>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(9), tid)) MK_BAIL();
       }
       // ================================================================ FFN
-      rmsnorm_cols_r<NCOL>(xres, hn, g2a, g2b, H, m.rms_eps, ncol, red, tid);
+      if constexpr (NCOL == 1) {
+        if (w8 < CW) rmsnorm_regs(xres, g2v, H, G_h, L_h, m.rms_eps, av);
+      } else {
+        rmsnorm_cols_r<NCOL>(xres, hn, g2a, g2b, H, G_h, L_h, m.rms_eps, ncol, tid);
+      }
       {
         uint2 *xm = ly.x_m + (size_t)x * MK_MAXCOL * xm_len;
         // ---- F1: gate/up pairs j -> m_j = SiLU(g_j) * u_j (weights already in flight)
+        if constexpr (NCOL == 1) {
+          if (RG_h == 1 && L_h == 2) {
+            // both pairs at once: lanes [0,16) gate 0, [16,32) gate 1, [32,48) up 0, [48,64) up 1;
+            // the permlane32 swap then puts gate and up of pair 0 in lane 0 and of pair 1 in lane 16
+            const float t = wave_sum4(dot16(w_gu[0][0], w_gu[0][1], av), dot16(w_gu[0][2], w_gu[0][3], av),
+                                      dot16(w_gu[1][0], w_gu[1][1], av), dot16(w_gu[1][2], w_gu[1][3], av));
+            const u32x2 gu = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+            const int j = wx + (lane >> 4) * XW;
+            if ((lane == 0 || lane == 16) && j < J) pub_xcd(xm + j, siluf_(__uint_as_float(gu.x)) * __uint_as_float(gu.y), tg);
+          } else {
 #pragma unroll
-        for (int pr = 0; pr < NPAIR; ++pr) {
-          const int j = wx + pr * XW;
-          if (j < J) {
-            float g[NCOL], u[NCOL];
-            if (RG_h == 1) {  // gate = loads [0, L_h), up = loads [L_h, 2 L_h)
-              const u32x4 wg[2] = {w_gu[pr][0], w_gu[pr][1]};
-              const u32x4 wu[2] = {L_h == 2 ? w_gu[pr][2] : w_gu[pr][1], w_gu[pr][3]};
-              rg_dot<NCOL, 2>(wg, L_h, G_h, hn, H, ncol, g);
-              rg_dot<NCOL, 2>(wu, L_h, G_h, hn, H, ncol, u);
-            } else {  // one row group holds the pair: lanes [0,32) compute g_j, lanes [32,64) u_j
-              const u32x4 wg[2] = {w_gu[pr][0], w_gu[pr][1]};
-              rg_dot<NCOL, 2>(wg, L_h, G_h, hn, H, ncol, g);
-#pragma unroll
-              for (int c = 0; c < NCOL; ++c) u[c] = __shfl_xor(g[c], 32, 64);
+            for (int pr = 0; pr < NPAIR; ++pr) {
+              const int j = wx + pr * XW;
+              float g, u;
+              if (RG_h == 1) {  // gate = loads [0, L_h), up = loads [L_h, 2 L_h)
+                g = rg_dot_regs(w_gu[pr][0], L_h == 2 ? w_gu[pr][1] : u32x4{0u, 0u, 0u, 0u}, G_h, av);
+                u = rg_dot_regs(L_h == 2 ? w_gu[pr][2] : w_gu[pr][1], L_h == 2 ? w_gu[pr][3] : u32x4{0u, 0u, 0u, 0u}, G_h, av);
+              } else {  // one row group holds the pair: lanes [0,32) compute g_j, lanes [32,64) u_j
+                g = rg_dot_regs(w_gu[pr][0], w_gu[pr][1], G_h, av);
+                u = __shfl_xor(g, 32, 64);
+              }
+              if (lane == 0 && j < J) pub_xcd(xm + j, siluf_(g) * u, tg);
             }
-            if (lane == 0) FOR_COL(c) pub_xcd(xm + c * xm_len + j, siluf_(g[c]) * u[c], tg);
+          }
+        } else {
+#pragma unroll
+          for (int pr = 0; pr < NPAIR; ++pr) {
+            const int j = wx + pr * XW;
+            if (j < J) {
+              float g[NCOL], u[NCOL];
+              if (RG_h == 1) {  // gate = loads [0, L_h), up = loads [L_h, 2 L_h)
+                const u32x4 wg[2] = {w_gu[pr][0], w_gu[pr][1]};
+                const u32x4 wu[2] = {L_h == 2 ? w_gu[pr][2] : w_gu[pr][1], w_gu[pr][3]};
+                rg_dot<NCOL, 2>(wg, L_h, G_h, hn, H, ncol, g);
+                rg_dot<NCOL, 2>(wu, L_h, G_h, hn, H, ncol, u);
+              } else {  // one row group holds the pair: lanes [0,32) compute g_j, lanes [32,64) u_j
+                const u32x4 wg[2] = {w_gu[pr][0], w_gu[pr][1]};
+                rg_dot<NCOL, 2>(wg, L_h, G_h, hn, H, ncol, g);
+#pragma unroll
+                for (int c = 0; c < NCOL; ++c) u[c] = __shfl_xor(g[c], 32, 64);
+              }
+              if (lane == 0) FOR_COL(c) pub_xcd(xm + c * xm_len + j, siluf_(g[c]) * u[c], tg);
+            }
           }
         }
         // prefetch: down-projection rows (F2), in flight during the m hand-off
@@ -1033,8 +1170,12 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       {
         const bool more = li + 1 < m.n_layers;
         const float *gsrc = more ? layers[li + 1].ln1 : m.lnf;   // else the final norm's gains
-        g1a = ld_gain(gsrc, H, tid);
-        g1b = ld_gain(gsrc, H, tid + MK_THREADS);
+        if constexpr (NCOL == 1) {
+          ld_gain16(gsrc, H, G_h, w8 < CW || !more, g1v);   // every wave takes part in the LM head
+        } else {
+          g1a = ld_gain(gsrc, H, tid);
+          g1b = ld_gain(gsrc, H, tid + MK_THREADS);
+        }
         issue_in(li + 1);
       }
       // ---- R2: residual += sum of the 8 FFN slices
@@ -1054,7 +1195,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     }  // layers
 
     // ================================================================ LM head + greedy argmax
-    rmsnorm_cols_r<NCOL>(xres, hn, g1a, g1b, H, m.rms_eps, ncol, red, tid0);
+    float avf[16];   // decode: the final norm in registers (every wave)
+    if constexpr (NCOL == 1) rmsnorm_regs(xres, g1v, H, G_h, L_h, m.rms_eps, avf);
+    else rmsnorm_cols_r<NCOL>(xres, hn, g1a, g1b, H, G_h, L_h, m.rms_eps, ncol, tid0);
     {
       const int nrg_all = m.V / RG_h;
       const int g0 = (int)((long long)b * nrg_all / MK_NWG), g1 = (int)((long long)(b + 1) * nrg_all / MK_NWG);
@@ -1076,7 +1219,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              av[c][i * 8 + e] = (c < ncol && i < L_h) ? hn[c * H + i * G_h * 8 + kl + e] : 0.f;
+              av[c][i * 8 + e] = (NCOL == 1) ? avf[i * 8 + e] : (c < ncol && i < L_h) ? hn[c * H + i * G_h * 8 + kl + e] : 0.f;
       }
       for (int rb = wg0; rb < wg1; rb += B) {
         u32x4 wr[B][2];
