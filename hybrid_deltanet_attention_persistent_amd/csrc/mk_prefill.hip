@@ -889,6 +889,179 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att(PfAtt a) {
   }
 }
 
+// Causal attention on the matrix cores.  Workgroup = 4 waves x 16 queries of one head; key blocks
+// of 32 positions come from the paged bf16 cache into LDS (K row-major, V transposed), shared by
+// the 4 waves.  Per wave and block: S = Q K^T with v_mfma_f32_16x16x32_bf16 (Q in FP32 enters as
+// bf16 hi + lo, K is exactly bf16), online softmax in FP32 on the result layout (lane l holds
+// rows 4 (l / 16) + i of key l % 16), P written to LDS as hi + lo and read back as the A operand,
+// O += P V (V exact bf16).  Same arithmetic contract as the rest of the prefill: operands with 16
+// significant bits, FP32 accumulation and softmax.
+constexpr int AKB = 32;                  // keys per block
+template <int HD>
+__global__ void __launch_bounds__(PF_THREADS) pf_att_mfma(PfAtt a) {
+  constexpr int KS = HD / 32;            // 32-wide k steps of Q K^T
+  constexpr int NDB = HD / 16;           // 16-wide output column blocks
+  constexpr int KLD = HD + 8, VLD = AKB + 8, PLD = AKB + 8;   // padded LDS rows (bf16 elements)
+  __shared__ uint16_t Ks[AKB * KLD];     // [key][dim]
+  __shared__ uint16_t Vt[HD * VLD];      // [dim][key]
+  __shared__ uint16_t Pw[4][2][16 * PLD];  // per wave: hi, lo [query][key]
+  __shared__ int pages[10240 / MK_PAGE];  // the page table of every cached position (checked on the host)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hq = blockIdx.y, kvh = hq * a.nkv / a.nq;
+  const int p0 = a.ctl[MK_CTL_POS];
+  const int t0 = blockIdx.x * 64, tw = t0 + w * 16;          // first query row of the workgroup / wave
+  const int nq_wg = min(64, a.T - t0);
+  const int last = p0 + t0 + nq_wg - 1;                      // largest query position of the workgroup
+  const int wlast = p0 + min(tw + 15, a.T - 1);              // ... of this wave
+  const bool wlive = tw < a.T;
+  const float scale = 1.f / sqrtf((float)HD);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  // Q fragments of this wave: row r16, dims 32 s + 8 g4 .. +8, as hi and lo
+  bf16x8 qh[KS], ql[KS];
+  {
+    const bool ok = tw + r16 < a.T;
+    const float *qrow = a.aq + (size_t)(tw + r16) * a.nq * HD + hq * HD;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = 0.f;
+      if (ok) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(qrow + s2 * 32 + g4 * 8);
+        const float4 x1 = *reinterpret_cast<const float4 *>(qrow + s2 * 32 + g4 * 8 + 4);
+        f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w; f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
+      }
+      u32x4 h, l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h0 = f2bf(f[2 * e]), h1 = f2bf(f[2 * e + 1]);
+        h[e] = h0 | (h1 << 16);
+        l[e] = f2bf(f[2 * e] - bf2f(h0)) | (f2bf(f[2 * e + 1] - bf2f(h1)) << 16);
+      }
+      qh[s2] = __builtin_bit_cast(bf16x8, h);
+      ql[s2] = __builtin_bit_cast(bf16x8, l);
+    }
+  }
+  f32x4 o[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { mrow[i] = -INFINITY; lrow[i] = 0.f; }
+  constexpr int CPR = HD / 8;                            // 16-byte chunks per key row
+  constexpr int NCH = AKB * CPR / PF_THREADS;            // chunks per thread and tile
+  const int nkb = last / AKB + 1;
+  for (int i = tid; i <= last / MK_PAGE; i += PF_THREADS) pages[i] = a.page_table[i];
+  __syncthreads();
+  // K and V rows of block kb into registers (positions past `last` read as zeros); the next
+  // block's loads are in flight while the current block is multiplied
+  uint4 kr[NCH], vr[NCH];
+  auto load_kv = [&](int kb) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e = c * PF_THREADS + tid, r = e % AKB, cc = e / AKB, pp = kb * AKB + r;
+      kr[c] = make_uint4(0u, 0u, 0u, 0u);
+      vr[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (pp <= last) {
+        const size_t off = (((size_t)pages[pp / MK_PAGE] * a.nkv + kvh) * MK_PAGE + (pp % MK_PAGE)) * HD + cc * 8;
+        kr[c] = *reinterpret_cast<const uint4 *>(a.kc + off);
+        vr[c] = *reinterpret_cast<const uint4 *>(a.vc + off);
+      }
+    }
+  };
+  load_kv(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int k0 = kb * AKB;
+    __syncthreads();   // every wave is done with the previous tiles
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e = c * PF_THREADS + tid, r = e % AKB, cc = e / AKB;
+      *reinterpret_cast<uint4 *>(Ks + r * KLD + cc * 8) = kr[c];
+      const uint32_t vw[4] = {vr[c].x, vr[c].y, vr[c].z, vr[c].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        Vt[(cc * 8 + 2 * q) * VLD + r] = (uint16_t)(vw[q] & 0xffffu);
+        Vt[(cc * 8 + 2 * q + 1) * VLD + r] = (uint16_t)(vw[q] >> 16);
+      }
+    }
+    __syncthreads();
+    if (kb + 1 < nkb) load_kv(kb + 1);
+    if (!wlive || k0 > wlast) continue;                  // wave-uniform: no key of this block is visible
+    // S = Q K^T for keys k0 + 16 cb + r16
+    f32x4 sc[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      sc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (cb * 16 + r16) * KLD + s2 * 32 + g4 * 8);
+        sc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[s2], kf, sc[cb], 0, 0, 0);
+        sc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[s2], kf, sc[cb], 0, 0, 0);
+      }
+    }
+    // online softmax: lane holds rows 4 g4 + i, keys k0 + 16 cb + r16
+    float pv[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qrow = tw + 4 * g4 + i, qp = p0 + qrow;
+      float sv[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int kp = k0 + cb * 16 + r16;
+        sv[cb] = (qrow < a.T && kp <= qp) ? sc[cb][i] * scale : -INFINITY;
+      }
+      float mx = fmaxf(sv[0], sv[1]);
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+      const float mn = fmaxf(mrow[i], mx);
+      const float al = (mn == -INFINITY) ? 1.f : expf(mrow[i] - mn);
+      float rs = 0.f;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        pv[cb][i] = (sv[cb] == -INFINITY) ? 0.f : expf(sv[cb] - mn);
+        rs += pv[cb][i];
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) rs += __shfl_xor(rs, off, 16);
+      lrow[i] = lrow[i] * al + rs;
+      mrow[i] = mn;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) o[d][i] *= al;
+    }
+    // P to LDS (hi, lo), read back as the A operand: row r16, keys 8 g4 .. +8
+    uint16_t *ph = Pw[w][0], *pl = Pw[w][1];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t h = f2bf(pv[cb][i]);
+        ph[(4 * g4 + i) * PLD + cb * 16 + r16] = (uint16_t)h;
+        pl[(4 * g4 + i) * PLD + cb * 16 + r16] = (uint16_t)f2bf(pv[cb][i] - bf2f(h));
+      }
+    const bf16x8 pah = *reinterpret_cast<const bf16x8 *>(ph + r16 * PLD + g4 * 8);   // (one wave writes and reads:
+    const bf16x8 pal = *reinterpret_cast<const bf16x8 *>(pl + r16 * PLD + g4 * 8);   //  its LDS accesses stay in order)
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vt + (d * 16 + r16) * VLD + g4 * 8);
+      o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, vf, o[d], 0, 0, 0);
+      o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, vf, o[d], 0, 0, 0);
+    }
+  }
+  // O / l, as hi + lo: row tw + 4 g4 + i, dims 16 d + r16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qrow = tw + 4 * g4 + i;
+    if (qrow < a.T) {
+      const float inv = lrow[i];
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        const size_t off = (size_t)qrow * a.ld + hq * HD + d * 16 + r16;
+        split_store(o[d][i] / inv, a.oh + off, a.ol + off);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------ LM head
 __device__ __forceinline__ unsigned long long pack_best(float v, int idx) {
   uint32_t u = __float_as_uint(v);
@@ -1084,7 +1257,9 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         at.kc = L.kc; at.vc = L.vc; at.aq = pf->aq; at.nq = nq; at.nkv = nkv; at.hd = hd;
         at.oh = pf->a1h; at.ol = pf->a1l; at.ld = pf->K1;
         hipLaunchKernelGGL(pf_att_rope, dim3(T), dim3(PF_THREADS), 0, st, at);
-        hipLaunchKernelGGL(pf_att, dim3((T + QB - 1) / QB, nq), dim3(PF_THREADS), att_lds(hd), st, at);
+        if (hd == 128) hipLaunchKernelGGL(pf_att_mfma<128>, dim3((T + 63) / 64, nq), dim3(PF_THREADS), 0, st, at);
+        else if (hd == 64) hipLaunchKernelGGL(pf_att_mfma<64>, dim3((T + 63) / 64, nq), dim3(PF_THREADS), 0, st, at);
+        else hipLaunchKernelGGL(pf_att, dim3((T + QB - 1) / QB, nq), dim3(PF_THREADS), att_lds(hd), st, at);
         PfGemm go{};
         go.ah = pf->a1h; go.al = pf->a1l; go.lda = pf->K1; go.M = T; go.N = H; go.K = nq * hd;
         go.wb[0] = go.wb[1] = go.wb[2] = L.at_o; go.wend[0] = go.wend[1] = go.wend[2] = H;
