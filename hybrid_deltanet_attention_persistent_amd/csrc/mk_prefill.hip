@@ -16,8 +16,9 @@
 // Precision.  Weights are BF16 and activations FP32 (the contract of the decode kernel).  A
 // GEMM operand a (FP32) enters the bf16 MFMA as two terms, hi = bf16(a) and lo = bf16(a - hi),
 // both multiplied by the exact bf16 weight and accumulated in FP32: the operand keeps 16
-// significant bits (relative error below 2^-17).  The delta rule, conv, norms and attention
-// run in FP32 on the vector ALUs.
+// significant bits (relative error below 2^-17).  Attention multiplies on the matrix cores the
+// same way (Q and the softmax weights as hi + lo, K and V exactly bf16), softmax in FP32.  The
+// delta rule, conv and norms run in FP32 on the vector ALUs.
 //
 // The chunked delta rule follows from unrolling the recurrence S_i = alpha_i S_{i-1} +
 // u_i k_i^T, u_i = beta_i (v_i - alpha_i S_{i-1} k_i) over a chunk that starts from S0.  With
@@ -34,13 +35,14 @@
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 namespace {
 
 constexpr int PF_THREADS = 256;
 constexpr int RB = 4;          // state rows per scan workgroup (one per wave)
-constexpr int QB = 16;         // queries per attention workgroup
-constexpr int KB = 64;         // keys per attention block
 
 __device__ __forceinline__ uint32_t f2bf(float f) {  // round to nearest even
   uint32_t u = __float_as_uint(f);
@@ -61,6 +63,24 @@ __device__ __forceinline__ float sigmoidf_(float x) {
 __device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
 __device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
 
+// Max / sum over each 16-lane row with DPP (xor 1, xor 2, half-row mirror, row mirror): every lane
+// of the row gets the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  return fmaxf(v, dpp_mov<0x140>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  return v + dpp_mov<0x140>(v);
+}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -764,147 +784,60 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att_rope(PfAtt a) {
   }
 }
 
-// causal attention of QB queries of one head over keys 0 .. position, online softmax (FP32)
-__global__ void __launch_bounds__(PF_THREADS) pf_att(PfAtt a) {
-  extern __shared__ float sm[];
-  const int qb = blockIdx.x, hq = blockIdx.y, hd = a.hd, kvh = hq * a.nkv / a.nq;
-  const int p0 = a.ctl[MK_CTL_POS];
-  const int t0 = qb * QB, nqr = min(QB, a.T - t0);
-  const int kh = hd + 4;                // padded rows: float4 reads stay conflict-free
-  float *Qs = sm;                       // [QB][hd]
-  float *Ks = Qs + QB * hd;             // [KB][hd+4]
-  float *Vs = Ks + KB * kh;             // [KB][hd]
-  float *Ps = Vs + KB * hd;             // [QB][KB]
-  float *mrow = Ps + QB * KB, *lrow = mrow + QB, *alpha = lrow + QB;
-  const int tid = threadIdx.x;
-  const float scale = 1.f / sqrtf((float)hd);
-  g2l<2>(Qs, hd, a.aq + (size_t)t0 * a.nq * hd + hq * hd, (size_t)a.nq * hd, QB, hd, nqr);
-  if (tid < QB) { mrow[tid] = -INFINITY; lrow[tid] = 0.f; }
-  // accumulator: thread -> query tid / 16, dims dpt (tid % 16) .. +dpt, dpt = hd / 16
-  const int aq_ = tid / 16, dpt = hd / 16, d0 = (tid % 16) * dpt;
-  float acc[8];
+// Causal attention on the matrix cores, computed transposed so that each lane owns one query:
+// S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_16x16x32_bf16 (result layout: lane l holds rows
+// 4 (l / 16) + i of column l % 16, i.e. four keys / four dims of query l % 16).  Workgroup = 4
+// waves x 16 queries of one head; key blocks of 64 positions come from the paged bf16 cache into
+// LDS (row-major K and V), shared by the 4 waves.  V fragments are read with the transposing LDS
+// load (ds_read_b64_tr_b16: in each 16-lane group, lanes 4r .. 4r+3 supply the 16 elements of row
+// r and lane i receives column i of the four rows).  Q (FP32) and P enter as bf16 hi + lo, K
+// and V are exactly bf16; the online softmax runs in FP32 per lane, with the column reductions
+// over the four lane groups done by permlane swaps, and P moves from the result layout to the
+// operand layout by two permlane swaps, without LDS.
+constexpr int AKB = 64;                  // keys per block
+
+// v[0..3] of two 16-key result tiles X (keys 0..15 of a 32-key step) and Y (16..31), each lane
+// group g holding keys 4 g .. 4 g + 3 of its query -> the operand layout of that step: lane group
+// g gets keys 8 g .. 8 g + 7 (first four in lo[], last four in hi[]).
+__device__ __forceinline__ void p_to_operand(const f32x4 &X, const f32x4 &Y, float (&lo)[4], float (&hi)[4]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  const int last = p0 + t0 + nqr - 1;   // largest query position
-  const int nkb = last / KB + 1;
-  const int cpr = hd / 8;               // 16-byte chunks per K/V row
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * KB;
-    {  // K and V rows of this block: 16-byte loads, all issued before any store
-      constexpr int NL = 4;             // chunks per thread (KB * 128 / 8 / 256)
-      uint4 kr[NL], vr[NL];
-#pragma unroll
-      for (int b = 0; b < NL; ++b) {
-        const int e = b * PF_THREADS + tid, r = e / cpr, cc = e % cpr, p = k0 + r;
-        kr[b] = make_uint4(0u, 0u, 0u, 0u);
-        vr[b] = make_uint4(0u, 0u, 0u, 0u);
-        if (r < KB && p <= last) {
-          const size_t o = kv_off(a, p, kvh) + cc * 8;
-          kr[b] = *reinterpret_cast<const uint4 *>(a.kc + o);
-          vr[b] = *reinterpret_cast<const uint4 *>(a.vc + o);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < NL; ++b) {
-        const int e = b * PF_THREADS + tid, r = e / cpr, cc = e % cpr;
-        if (r < KB) {
-          float *kd = Ks + r * kh + cc * 8, *vd = Vs + r * hd + cc * 8;
-          const uint32_t kw[4] = {kr[b].x, kr[b].y, kr[b].z, kr[b].w}, vw[4] = {vr[b].x, vr[b].y, vr[b].z, vr[b].w};
-          *reinterpret_cast<float4 *>(kd) = make_float4(bf2f(kw[0] & 0xffffu), bf2f(kw[0] >> 16), bf2f(kw[1] & 0xffffu), bf2f(kw[1] >> 16));
-          *reinterpret_cast<float4 *>(kd + 4) = make_float4(bf2f(kw[2] & 0xffffu), bf2f(kw[2] >> 16), bf2f(kw[3] & 0xffffu), bf2f(kw[3] >> 16));
-          *reinterpret_cast<float4 *>(vd) = make_float4(bf2f(vw[0] & 0xffffu), bf2f(vw[0] >> 16), bf2f(vw[1] & 0xffffu), bf2f(vw[1] >> 16));
-          *reinterpret_cast<float4 *>(vd + 4) = make_float4(bf2f(vw[2] & 0xffffu), bf2f(vw[2] >> 16), bf2f(vw[3] & 0xffffu), bf2f(vw[3] >> 16));
-        }
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < QB * KB; e += PF_THREADS) {
-      const int r = e / KB, j = e % KB;
-      const int qp = p0 + t0 + r, kp = k0 + j;
-      float s = -INFINITY;
-      if (r < nqr && kp <= qp) {
-        float dd = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < hd; d += 4) dd = dot4(ld4(Qs + r * hd + d), ld4(Ks + j * kh + d), dd);
-        s = dd * scale;
-      }
-      Ps[e] = s;
-    }
-    __syncthreads();
-    {  // online softmax bookkeeping: 16 lanes per query row, 4 keys per lane
-      const int r = tid / 16, j0 = (tid % 16) * 4;
-      const float4 s4 = ld4(Ps + r * KB + j0);
-      float mx = fmaxf(fmaxf(s4.x, s4.y), fmaxf(s4.z, s4.w));
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
-      mx = fmaxf(mx, mrow[r]);
-      const float al = (mx == -INFINITY) ? 1.f : expf(mrow[r] - mx);
-      float4 p4;
-      p4.x = (s4.x == -INFINITY) ? 0.f : expf(s4.x - mx);
-      p4.y = (s4.y == -INFINITY) ? 0.f : expf(s4.y - mx);
-      p4.z = (s4.z == -INFINITY) ? 0.f : expf(s4.z - mx);
-      p4.w = (s4.w == -INFINITY) ? 0.f : expf(s4.w - mx);
-      *reinterpret_cast<float4 *>(Ps + r * KB + j0) = p4;
-      float l = (p4.x + p4.y) + (p4.z + p4.w);
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) l += __shfl_xor(l, o, 16);
-      __syncthreads();   // every lane of the row has read mrow / lrow before lane 0 updates them
-      if ((tid % 16) == 0) {
-        lrow[r] = lrow[r] * al + l;
-        mrow[r] = mx;
-        alpha[r] = al;
-      }
-    }
-    __syncthreads();
-    {
-      const float al = alpha[aq_];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] *= al;
-#pragma unroll 8
-      for (int kk = 0; kk < KB; ++kk) {
-        const float pk = Ps[aq_ * KB + kk];
-        const float *vp = Vs + kk * hd + d0;
-        const float4 v0 = ld4(vp);
-        acc[0] = fmaf(pk, v0.x, acc[0]); acc[1] = fmaf(pk, v0.y, acc[1]);
-        acc[2] = fmaf(pk, v0.z, acc[2]); acc[3] = fmaf(pk, v0.w, acc[3]);
-        if (dpt == 8) {
-          const float4 v1 = ld4(vp + 4);
-          acc[4] = fmaf(pk, v1.x, acc[4]); acc[5] = fmaf(pk, v1.y, acc[5]);
-          acc[6] = fmaf(pk, v1.z, acc[6]); acc[7] = fmaf(pk, v1.w, acc[7]);
-        }
-      }
-    }
-    __syncthreads();
+  for (int i = 0; i < 4; ++i) {
+    const u32x2 a = __builtin_amdgcn_permlane32_swap(__float_as_uint(X[i]), __float_as_uint(Y[i]), false, false);
+    const u32x2 b = __builtin_amdgcn_permlane16_swap(a.x, a.y, false, false);
+    lo[i] = __uint_as_float(b.x);
+    hi[i] = __uint_as_float(b.y);
   }
-  if (aq_ < nqr) {
-    const float inv = lrow[aq_];
+}
+// max / sum over the four lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48): every lane gets the result
+__device__ __forceinline__ float group4_max(float v) {
+  u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+  p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p.x) + __uint_as_float(p.y);
+  p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p.x) + __uint_as_float(p.y);
+}
+// 8 FP32 values as the bf16 hi and lo operands
+__device__ __forceinline__ void split8(const float (&f)[8], bf16x8 &h, bf16x8 &l) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < dpt) {
-        const size_t o = (size_t)(t0 + aq_) * a.ld + hq * hd + d0 + j;
-        split_store(acc[j] / inv, a.oh + o, a.ol + o);
-      }
-    }
+  for (int e = 0; e < 8; ++e) {
+    h[e] = (__bf16)f[e];
+    l[e] = (__bf16)(f[e] - (float)h[e]);
   }
 }
 
-// Causal attention on the matrix cores.  Workgroup = 4 waves x 16 queries of one head; key blocks
-// of 32 positions come from the paged bf16 cache into LDS (K row-major, V transposed), shared by
-// the 4 waves.  Per wave and block: S = Q K^T with v_mfma_f32_16x16x32_bf16 (Q in FP32 enters as
-// bf16 hi + lo, K is exactly bf16), online softmax in FP32 on the result layout (lane l holds
-// rows 4 (l / 16) + i of key l % 16), P written to LDS as hi + lo and read back as the A operand,
-// O += P V (V exact bf16).  Same arithmetic contract as the rest of the prefill: operands with 16
-// significant bits, FP32 accumulation and softmax.
-constexpr int AKB = 32;                  // keys per block
 template <int HD>
 __global__ void __launch_bounds__(PF_THREADS) pf_att_mfma(PfAtt a) {
-  constexpr int KS = HD / 32;            // 32-wide k steps of Q K^T
-  constexpr int NDB = HD / 16;           // 16-wide output column blocks
-  constexpr int KLD = HD + 8, VLD = AKB + 8, PLD = AKB + 8;   // padded LDS rows (bf16 elements)
+  constexpr int KS = HD / 32;            // 32-wide dim steps of K Q^T
+  constexpr int NDB = HD / 16;           // 16-dim blocks of O^T
+  constexpr int NCB = AKB / 16;          // 16-key tiles of S^T
+  constexpr int KLD = HD + 8, VLD = HD + 16;   // padded LDS rows (bf16 elements)
   __shared__ uint16_t Ks[AKB * KLD];     // [key][dim]
-  __shared__ uint16_t Vt[HD * VLD];      // [dim][key]
-  __shared__ uint16_t Pw[4][2][16 * PLD];  // per wave: hi, lo [query][key]
+  __shared__ uint16_t Vs[AKB * VLD];     // [key][dim]
   __shared__ int pages[10240 / MK_PAGE];  // the page table of every cached position (checked on the host)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hq = blockIdx.y, kvh = hq * a.nkv / a.nq;
@@ -914,40 +847,31 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att_mfma(PfAtt a) {
   const int last = p0 + t0 + nq_wg - 1;                      // largest query position of the workgroup
   const int wlast = p0 + min(tw + 15, a.T - 1);              // ... of this wave
   const bool wlive = tw < a.T;
-  const float scale = 1.f / sqrtf((float)HD);
   const int r16 = lane & 15, g4 = lane >> 4;
-  // Q fragments of this wave: row r16, dims 32 s + 8 g4 .. +8, as hi and lo
+  const int qrow = tw + r16, qp = p0 + qrow;                 // this lane's query
+  const bool qok = qrow < a.T;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)HD);  // softmax in base 2: scale * log2(e)
+  // Q operand of this wave: query r16, dims 32 s + 8 g4 .. +8, as hi and lo
   bf16x8 qh[KS], ql[KS];
   {
-    const bool ok = tw + r16 < a.T;
-    const float *qrow = a.aq + (size_t)(tw + r16) * a.nq * HD + hq * HD;
+    const float *qr = a.aq + (size_t)qrow * a.nq * HD + hq * HD;
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
       float f[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = 0.f;
-      if (ok) {
-        const float4 x0 = *reinterpret_cast<const float4 *>(qrow + s2 * 32 + g4 * 8);
-        const float4 x1 = *reinterpret_cast<const float4 *>(qrow + s2 * 32 + g4 * 8 + 4);
+      if (qok) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(qr + s2 * 32 + g4 * 8);
+        const float4 x1 = *reinterpret_cast<const float4 *>(qr + s2 * 32 + g4 * 8 + 4);
         f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w; f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
       }
-      u32x4 h, l;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t h0 = f2bf(f[2 * e]), h1 = f2bf(f[2 * e + 1]);
-        h[e] = h0 | (h1 << 16);
-        l[e] = f2bf(f[2 * e] - bf2f(h0)) | (f2bf(f[2 * e + 1] - bf2f(h1)) << 16);
-      }
-      qh[s2] = __builtin_bit_cast(bf16x8, h);
-      ql[s2] = __builtin_bit_cast(bf16x8, l);
+      split8(f, qh[s2], ql[s2]);
     }
   }
-  f32x4 o[NDB];
+  f32x4 o[NDB];                           // O^T: dims 16 d + 4 g4 + i of this lane's query
 #pragma unroll
   for (int d = 0; d < NDB; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[4], lrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { mrow[i] = -INFINITY; lrow[i] = 0.f; }
+  float mrow = -INFINITY, lrow = 0.f;     // running max (base 2) and sum of this lane's query
   constexpr int CPR = HD / 8;                            // 16-byte chunks per key row
   constexpr int NCH = AKB * CPR / PF_THREADS;            // chunks per thread and tile
   const int nkb = last / AKB + 1;
@@ -977,88 +901,83 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att_mfma(PfAtt a) {
     for (int c = 0; c < NCH; ++c) {
       const int e = c * PF_THREADS + tid, r = e % AKB, cc = e / AKB;
       *reinterpret_cast<uint4 *>(Ks + r * KLD + cc * 8) = kr[c];
-      const uint32_t vw[4] = {vr[c].x, vr[c].y, vr[c].z, vr[c].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        Vt[(cc * 8 + 2 * q) * VLD + r] = (uint16_t)(vw[q] & 0xffffu);
-        Vt[(cc * 8 + 2 * q + 1) * VLD + r] = (uint16_t)(vw[q] >> 16);
-      }
+      *reinterpret_cast<uint4 *>(Vs + r * VLD + cc * 8) = vr[c];
     }
     __syncthreads();
     if (kb + 1 < nkb) load_kv(kb + 1);
     if (!wlive || k0 > wlast) continue;                  // wave-uniform: no key of this block is visible
-    // S = Q K^T for keys k0 + 16 cb + r16
-    f32x4 sc[2];
+    // S^T = K Q^T: tile cb holds keys k0 + 16 cb + 4 g4 + i of query r16
+    f32x4 sc[NCB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      sc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) sc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (cb * 16 + r16) * KLD + s2 * 32 + g4 * 8);
-        sc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[s2], kf, sc[cb], 0, 0, 0);
-        sc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[s2], kf, sc[cb], 0, 0, 0);
-      }
+    for (int s2 = 0; s2 < KS; ++s2) {
+      bf16x8 kf[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) kf[cb] = *reinterpret_cast<const bf16x8 *>(Ks + (cb * 16 + r16) * KLD + s2 * 32 + g4 * 8);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) sc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[cb], qh[s2], sc[cb], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) sc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[cb], ql[s2], sc[cb], 0, 0, 0);
     }
-    // online softmax: lane holds rows 4 g4 + i, keys k0 + 16 cb + r16
-    float pv[2][4];
+    // online softmax of this lane's query over its 4 NCB keys, then over the lane groups
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qrow = tw + 4 * g4 + i, qp = p0 + qrow;
-      float sv[2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int kp = k0 + cb * 16 + r16;
-        sv[cb] = (qrow < a.T && kp <= qp) ? sc[cb][i] * scale : -INFINITY;
-      }
-      float mx = fmaxf(sv[0], sv[1]);
-#pragma unroll
-      for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-      const float mn = fmaxf(mrow[i], mx);
-      const float al = (mn == -INFINITY) ? 1.f : expf(mrow[i] - mn);
-      float rs = 0.f;
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        pv[cb][i] = (sv[cb] == -INFINITY) ? 0.f : expf(sv[cb] - mn);
-        rs += pv[cb][i];
-      }
-#pragma unroll
-      for (int off = 8; off > 0; off >>= 1) rs += __shfl_xor(rs, off, 16);
-      lrow[i] = lrow[i] * al + rs;
-      mrow[i] = mn;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) o[d][i] *= al;
-    }
-    // P to LDS (hi, lo), read back as the A operand: row r16, keys 8 g4 .. +8
-    uint16_t *ph = Pw[w][0], *pl = Pw[w][1];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t h = f2bf(pv[cb][i]);
-        ph[(4 * g4 + i) * PLD + cb * 16 + r16] = (uint16_t)h;
-        pl[(4 * g4 + i) * PLD + cb * 16 + r16] = (uint16_t)f2bf(pv[cb][i] - bf2f(h));
+        const int kp = k0 + cb * 16 + 4 * g4 + i;
+        sc[cb][i] = (qok && kp <= qp) ? sc[cb][i] * sl2 : -INFINITY;
+        mx = fmaxf(mx, sc[cb][i]);
       }
-    const bf16x8 pah = *reinterpret_cast<const bf16x8 *>(ph + r16 * PLD + g4 * 8);   // (one wave writes and reads:
-    const bf16x8 pal = *reinterpret_cast<const bf16x8 *>(pl + r16 * PLD + g4 * 8);   //  its LDS accesses stay in order)
+    mx = group4_max(mx);
+    const float mn = fmaxf(mrow, mx);
+    const float al = (mn == -INFINITY) ? 1.f : exp2f(mrow - mn);
+    float rs = 0.f;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(Vt + (d * 16 + r16) * VLD + g4 * 8);
-      o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, vf, o[d], 0, 0, 0);
-      o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, vf, o[d], 0, 0, 0);
-    }
-  }
-  // O / l, as hi + lo: row tw + 4 g4 + i, dims 16 d + r16
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qrow = tw + 4 * g4 + i;
-    if (qrow < a.T) {
-      const float inv = lrow[i];
+      for (int i = 0; i < 4; ++i) {
+        sc[cb][i] = (sc[cb][i] == -INFINITY) ? 0.f : exp2f(sc[cb][i] - mn);
+        rs += sc[cb][i];
+      }
+    rs = group4_sum(rs);
+    lrow = lrow * al + rs;
+    mrow = mn;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[d][i] *= al;
+    // O^T += V^T P^T, 32 keys per step
+#pragma unroll
+    for (int h = 0; h < AKB / 32; ++h) {
+      float plo[4], phi[4];
+      p_to_operand(sc[2 * h], sc[2 * h + 1], plo, phi);
+      const float pf[8] = {plo[0], plo[1], plo[2], plo[3], phi[0], phi[1], phi[2], phi[3]};
+      bf16x8 pah, pal;
+      split8(pf, pah, pal);
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
-        const size_t off = (size_t)qrow * a.ld + hq * HD + d * 16 + r16;
-        split_store(o[d][i] / inv, a.oh + off, a.ol + off);
+        // keys h 32 + 8 g4 .. +8 of dim 16 d + r16: rows r16 / 4 and 4 + r16 / 4 of the lane group's
+        // eight keys, columns 4 (r16 % 4) .. +4
+        const uint16_t *vp = Vs + (h * 32 + g4 * 8 + (r16 >> 2)) * VLD + d * 16 + (r16 & 3) * 4;
+        const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)vp);
+        const v4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(vp + 4 * VLD));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, v8i16{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pah, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pal, o[d], 0, 0, 0);
       }
     }
+  }
+  // O / l, as hi + lo: query qrow, dims 16 d + 4 g4 + i
+  if (qok) {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t off = (size_t)qrow * a.ld + hq * HD + d * 16 + 4 * g4 + i;
+        split_store(o[d][i] / lrow, a.oh + off, a.ol + off);
+      }
   }
 }
 
@@ -1192,7 +1111,6 @@ static size_t chunk_prep_lds(int dk) { return (size_t)(2 * MK_CHUNK * (dk + 4) +
 static size_t scan_lds(int dk) {
   return (size_t)(2 * RB * dk + 2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 3 * RB * CS + MK_CHUNK * RB + 3 * MK_CHUNK) * 4;
 }
-static size_t att_lds(int hd) { return (size_t)(QB * hd + KB * (hd + 4) + KB * hd + QB * KB + 3 * QB) * 4; }
 
 // Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table.
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
@@ -1203,7 +1121,6 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
     hipError_t e;
     if ((e = hipFuncSetAttribute((const void *)pf_dn_chunk_prep, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess) return e;
     if ((e = hipFuncSetAttribute((const void *)pf_dn_scan, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess) return e;
-    if ((e = hipFuncSetAttribute((const void *)pf_att, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess) return e;
     attr_done = true;
   }
   const int H = d->H, nh = d->nh, dk = d->dk, dv = d->dv, nq = d->nq, nkv = d->nkv, hd = d->hd, J = d->J, I = d->I;
@@ -1259,7 +1176,7 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         hipLaunchKernelGGL(pf_att_rope, dim3(T), dim3(PF_THREADS), 0, st, at);
         if (hd == 128) hipLaunchKernelGGL(pf_att_mfma<128>, dim3((T + 63) / 64, nq), dim3(PF_THREADS), 0, st, at);
         else if (hd == 64) hipLaunchKernelGGL(pf_att_mfma<64>, dim3((T + 63) / 64, nq), dim3(PF_THREADS), 0, st, at);
-        else hipLaunchKernelGGL(pf_att, dim3((T + QB - 1) / QB, nq), dim3(PF_THREADS), att_lds(hd), st, at);
+        else return hipErrorInvalidValue;   // head_dim is 64 or 128 (checked at load)
         PfGemm go{};
         go.ah = pf->a1h; go.al = pf->a1l; go.lda = pf->K1; go.M = T; go.N = H; go.K = nq * hd;
         go.wb[0] = go.wb[1] = go.wb[2] = L.at_o; go.wend[0] = go.wend[1] = go.wend[2] = H;
