@@ -519,6 +519,13 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   float *work = hn + NCOL * H;                  // [8192] phase scratch
   float *red = work + 8192;                     // [64] reductions
   int *flag = reinterpret_cast<int *>(red + 64);
+  // physical pages of this workgroup's attention key blocks lw, lw + 32, ... (32 keys each, two
+  // blocks per page), read once per launch: block j of the workgroup lies in page pgs[j]
+  int *pgs = flag + 16;                         // [16] (10240 positions / 32 / 32 = 10 blocks)
+  if (tid < 16) {
+    const int pi = (lw + tid * MK_NL) * MK_KBLK / MK_PAGE;
+    pgs[tid] = (pi < m.max_pages) ? m.page_table[pi] : 0;
+  }
   if (tid == 0) {
     flag[0] = 0;
     uint32_t xcc;
@@ -953,27 +960,26 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               const int myblk = (nblk > lw) ? (nblk - lw + MK_NL - 1) / MK_NL : 0;
               const int nk = (myblk == 0) ? 0 : (myblk - 1) * MK_KBLK + min(MK_KBLK, P + 1 - (lw + (myblk - 1) * MK_NL) * MK_KBLK);
               const float *q = qkv + c * 3 * hd;
-              // scores: key slot ks -> block lw + (ks / 32) * 32, offset ks % 32
-#pragma unroll 1
+              // scores: key slot ks -> block lw + (ks / 32) * 32, offset ks % 32.  Cached keys come
+              // through branch-free buffer loads (absent ones with an out-of-range offset), so the
+              // loads of several steps can be in flight together; this step's keys come from LDS.
+#pragma unroll 2
               for (int base = w8 * kpw; base < nk; base += MK_WAVES * kpw) {
-                const int ks = base + lane / lpk;
-                float sdot = 0.f;
-                if (ks < nk) {
-                  const int tpos = (lw + (ks / MK_KBLK) * MK_NL) * MK_KBLK + (ks % MK_KBLK);
-                  const int d0 = (lane % lpk) * 8;
-                  float kf[8];
-                  if (tpos < pos0) {
-                    const uint32_t off = (uint32_t)((((size_t)m.page_table[tpos / MK_PAGE] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + d0) * 2;
-                    const u32x4 kw = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-                    unpack8(kw, kf);
-                  } else {
-                    const float *kk = qkv + (tpos - pos0) * 3 * hd + hd + d0;
+                const int ks = base + lane / lpk, j = ks / MK_KBLK;
+                const int tpos = (lw + j * MK_NL) * MK_KBLK + (ks % MK_KBLK);
+                const int d0 = (lane % lpk) * 8;
+                const bool cached = ks < nk && tpos < pos0;
+                const uint32_t off = cached ? (uint32_t)((((pgs[j] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + d0) * 2) : OOB_OFF;
+                float kf[8];
+                unpack8(__builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0), kf);
+                if (ks < nk && !cached) {
+                  const float *kk = qkv + (tpos - pos0) * 3 * hd + hd + d0;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) kf[i] = kk[i];
-                  }
-#pragma unroll
-                  for (int i = 0; i < 8; ++i) sdot = fmaf(q[d0 + i], kf[i], sdot);
+                  for (int i = 0; i < 8; ++i) kf[i] = kk[i];
                 }
+                float sdot = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sdot = fmaf(q[d0 + i], kf[i], sdot);
                 sdot = group_sum(sdot, lpk);
                 if (ks < nk && (lane % lpk) == 0) sc[ks] = sdot * scale;
               }
@@ -993,23 +999,36 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 if (lane == 0) { mx[0] = mv; mx[1] = ls; }
               }
               lbar();
-              // P.V: wave w takes keys w, w+8, ...; lanes take dims
-              for (int d = lane; d < hd; d += 64) {
-                float acc = 0.f;
-#pragma unroll 1
+              // P.V: wave w takes keys w, w+8, ...; lane l takes dims l dpl .. +dpl (one 2- or 4-byte
+              // load per key, branch-free as above)
+              {
+                const int dpl = hd / 64;   // 1 or 2
+                float acc[2] = {0.f, 0.f};
+#pragma unroll 4
                 for (int ks = w8; ks < nk; ks += MK_WAVES) {
-                  const int tpos = (lw + (ks / MK_KBLK) * MK_NL) * MK_KBLK + (ks % MK_KBLK);
-                  float vvv;
-                  if (tpos < pos0) {
-                    const uint32_t off = (uint32_t)((((size_t)m.page_table[tpos / MK_PAGE] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + d) * 2;
-                    const uint32_t raw = __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, 0);
-                    vvv = __uint_as_float(raw << 16);
+                  const int j = ks / MK_KBLK, tpos = (lw + j * MK_NL) * MK_KBLK + (ks % MK_KBLK);
+                  const bool cached = tpos < pos0;
+                  const uint32_t off = cached ? (uint32_t)((((pgs[j] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + lane * dpl) * 2) : OOB_OFF;
+                  float v0, v1;
+                  if (dpl == 2) {
+                    const uint32_t raw = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, 0);
+                    v0 = __uint_as_float(raw << 16);
+                    v1 = __uint_as_float(raw & 0xffff0000u);
                   } else {
-                    vvv = qkv[(tpos - pos0) * 3 * hd + 2 * hd + d];
+                    v0 = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, 0) << 16);
+                    v1 = 0.f;
                   }
-                  acc = fmaf(sc[ks], vvv, acc);
+                  if (!cached) {
+                    const float *vv = qkv + (tpos - pos0) * 3 * hd + 2 * hd + lane * dpl;
+                    v0 = vv[0];
+                    if (dpl == 2) v1 = vv[1];
+                  }
+                  const float p = sc[ks];
+                  acc[0] = fmaf(p, v0, acc[0]);
+                  acc[1] = fmaf(p, v1, acc[1]);
                 }
-                pv[w8 * hd + d] = acc;
+                pv[w8 * hd + lane * dpl] = acc[0];
+                if (dpl == 2) pv[w8 * hd + lane * dpl + 1] = acc[1];
               }
               lbar();
               const int plen = hd + 2;
