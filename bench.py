@@ -244,7 +244,7 @@ def main():
     pf = prefill_flops(cfg, wl.prompt_len)
     pf_s = float(np.median(pre_ms)) * 1e-3
     pf_tflops = pf["all"] / pf_s / 1e12
-    kernel = "mk_forward<1>"
+    kernel = "mk_forward<1, 1>"
     traffic = load_traffic(kernel)
     line = {
         "metric": "decode tok/s (batch 1, tg128 after pp520)" if wl.name != "tiny-pp16-tg16" else "decode tok/s",
