@@ -343,20 +343,38 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
       }
 }
 
-// X += sum over the splits of the split-K partials, in split order (deterministic)
-__global__ void __launch_bounds__(PF_THREADS) pf_split_reduce(float *X, const float *part, int nsplit, size_t stride,
-                                                              int N, int M) {
-  const int row = blockIdx.x;
-  if (row >= M) return;
-  for (int n4 = threadIdx.x; n4 < N / 4; n4 += PF_THREADS) {
-    float4 acc = reinterpret_cast<const float4 *>(part + (size_t)row * N)[n4];
+// X += sum of the split-K partials (split order), then, when g is given, the RMSNorm of the new row
+// as a bf16 hi + lo pair (the operand of the next projection): one pass over the row instead of
+// a reduction kernel and a norm kernel.  One workgroup per row, float4 per thread (H <= 1024).
+__global__ void __launch_bounds__(PF_THREADS) pf_reduce_norm(float *X, const float *part, int nsplit, size_t stride,
+                                                             int H, const float *g, float eps, uint16_t *oh,
+                                                             uint16_t *ol, int ld) {
+  __shared__ float red[4];
+  const int row = blockIdx.x, n4 = threadIdx.x;
+  const bool on = n4 < H / 4;
+  float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (on) {
+    float4 acc = reinterpret_cast<const float4 *>(part + (size_t)row * H)[n4];
     for (int z = 1; z < nsplit; ++z) {
-      const float4 p = reinterpret_cast<const float4 *>(part + z * stride + (size_t)row * N)[n4];
+      const float4 p = reinterpret_cast<const float4 *>(part + z * stride + (size_t)row * H)[n4];
       acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
     }
-    float4 *xp = reinterpret_cast<float4 *>(X + (size_t)row * N) + n4;
-    const float4 xv = *xp;
-    *xp = make_float4(xv.x + acc.x, xv.y + acc.y, xv.z + acc.z, xv.w + acc.w);
+    float4 *xp = reinterpret_cast<float4 *>(X + (size_t)row * H) + n4;
+    const float4 x0 = *xp;
+    xv = make_float4(x0.x + acc.x, x0.y + acc.y, x0.z + acc.z, x0.w + acc.w);
+    *xp = xv;
+  }
+  if (!g) return;   // uniform over the grid
+  float sq = fmaf(xv.x, xv.x, 0.f);
+  sq = fmaf(xv.y, xv.y, sq); sq = fmaf(xv.z, xv.z, sq); sq = fmaf(xv.w, xv.w, sq);
+  const float den = sqrtf(block_sum(sq, red) / (float)H + eps);
+  if (on) {
+    const float4 gv = reinterpret_cast<const float4 *>(g)[n4];
+    const size_t o = (size_t)row * ld + n4 * 4;
+    split_store(xv.x / den * gv.x, oh + o, ol + o);
+    split_store(xv.y / den * gv.y, oh + o + 1, ol + o + 1);
+    split_store(xv.z / den * gv.z, oh + o + 2, ol + o + 2);
+    split_store(xv.w / den * gv.w, oh + o + 3, ol + o + 3);
   }
 }
 
@@ -1090,20 +1108,36 @@ static hipError_t launch_gemm_t(const PfGemm &g, int nsplit, hipStream_t st) {
 // Wide projections: 64 x 256 workgroup tiles (4 waves of 64 x 64).  The 1024-wide outputs that
 // add into the residual stream: 64 x 64 tiles and split-K (partials reduced in split order), so
 // that the grid fills the chip and each K stream is short.
-static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStream_t st) {
+// The RMSNorm that follows a projection adding into the residual stream, fused into the split-K
+// reduction when there is one (gain g; output as hi + lo into oh / ol with row stride ld).
+struct PfNext {
+  const float *g;
+  float eps;
+  uint16_t *oh, *ol;
+  int ld;
+};
+static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStream_t st, const PfNext *next = nullptr) {
   if (g.K % GBK != 0) return hipErrorInvalidValue;
   g.kper = g.K;
   if (epi == EPI_STORE) return small ? launch_gemm_t<EPI_STORE, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_STORE, 4, 2, 1, 4>(g, 1, st);
   if (epi == EPI_SWIGLU) return small ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_SWIGLU, 4, 2, 1, 4>(g, 1, st);
   const int ns = g.K / GBK;
   const int nsplit = (ns % 4 == 0 && ns >= 8) ? 4 : (ns % 2 == 0 && ns >= 4) ? 2 : 1;
-  if (nsplit == 1 || !part) return small ? launch_gemm_t<EPI_RESID, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_RESID, 4, 4, 1, 4>(g, 1, st);
+  if (nsplit == 1 || !part || g.N > 4 * PF_THREADS || g.N % 4 != 0) {
+    hipError_t e = small ? launch_gemm_t<EPI_RESID, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_RESID, 4, 4, 1, 4>(g, 1, st);
+    if (e != hipSuccess || !next) return e;
+    hipLaunchKernelGGL(pf_norm_split, dim3(g.M), dim3(PF_THREADS), 0, st, (const float *)g.c, next->g, g.N, next->eps,
+                       next->oh, next->ol, next->ld);
+    return hipGetLastError();
+  }
   g.kper = g.K / nsplit;
   g.part = part;
   g.part_stride = (size_t)MK_PT * g.ldc;
   hipError_t e = small ? launch_gemm_t<EPI_PART, 2, 2, 2, 2>(g, nsplit, st) : launch_gemm_t<EPI_PART, 4, 4, 1, 4>(g, nsplit, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pf_split_reduce, dim3(g.M), dim3(PF_THREADS), 0, st, g.c, (const float *)part, nsplit, g.part_stride, g.N, g.M);
+  hipLaunchKernelGGL(pf_reduce_norm, dim3(g.M), dim3(PF_THREADS), 0, st, g.c, (const float *)part, nsplit, g.part_stride,
+                     g.N, next ? next->g : (const float *)nullptr, next ? next->eps : 0.f,
+                     next ? next->oh : (uint16_t *)nullptr, next ? next->ol : (uint16_t *)nullptr, next ? next->ld : 0);
   return hipGetLastError();
 }
 
@@ -1128,10 +1162,14 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
     const int T = n - s0 < MK_PT ? n - s0 : MK_PT;
     const bool last = s0 + T == n;
     hipLaunchKernelGGL(pf_embed, dim3(T), dim3(PF_THREADS), 0, st, d->embed, tokens + s0, H, d->V, pf->X, d->ctl);
+    hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->X, layers_host[0].ln1, H,
+                       d->rms_eps, pf->a1h, pf->a1l, pf->K1);
     for (int li = 0; li < d->n_layers; ++li) {
       const MkLayerDev &L = layers_host[li];
-      hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->X, L.ln1, H, d->rms_eps,
-                         pf->a1h, pf->a1l, pf->K1);
+      // the norm after the mixer (FFN input) and after the FFN (next layer's input) run inside
+      // the split-K reductions of the projections that add into the residual stream
+      const PfNext n2{L.ln2, d->rms_eps, pf->a1h, pf->a1l, pf->K1};
+      const PfNext n1{li + 1 < d->n_layers ? layers_host[li + 1].ln1 : nullptr, d->rms_eps, pf->a1h, pf->a1l, pf->K1};
       PfGemm g{};
       g.ah = pf->a1h; g.al = pf->a1l; g.lda = pf->K1; g.M = T;
       if (L.kind == 0) {
@@ -1159,7 +1197,7 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         go.wb[0] = go.wb[1] = go.wb[2] = L.dn_out; go.wend[0] = go.wend[1] = go.wend[2] = H;
         go.ks = dv; go.kstride = H * dv;
         go.c = pf->X; go.ldc = H;
-        if ((e = launch_gemm(EPI_RESID, true, go, pf->part, st)) != hipSuccess) return e;
+        if ((e = launch_gemm(EPI_RESID, true, go, pf->part, st, &n2)) != hipSuccess) return e;
       } else {
         g.N = (nq + 2 * nkv) * hd; g.K = H;
         g.wb[0] = L.at_q; g.wend[0] = nq * hd;
@@ -1182,10 +1220,8 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         go.wb[0] = go.wb[1] = go.wb[2] = L.at_o; go.wend[0] = go.wend[1] = go.wend[2] = H;
         go.ks = hd; go.kstride = H * hd;
         go.c = pf->X; go.ldc = H;
-        if ((e = launch_gemm(EPI_RESID, true, go, pf->part, st)) != hipSuccess) return e;
+        if ((e = launch_gemm(EPI_RESID, true, go, pf->part, st, &n2)) != hipSuccess) return e;
       }
-      hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->X, L.ln2, H, d->rms_eps,
-                         pf->a1h, pf->a1l, pf->K1);
       PfGemm gu{};
       gu.ah = pf->a1h; gu.al = pf->a1l; gu.lda = pf->K1; gu.M = T; gu.N = 2 * I; gu.K = H;
       gu.wb[0] = gu.wb[1] = gu.wb[2] = L.ffn_gu; gu.wend[0] = gu.wend[1] = gu.wend[2] = 2 * I;
@@ -1198,7 +1234,7 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
       gd.wb[0] = gd.wb[1] = gd.wb[2] = L.ffn_dn; gd.wend[0] = gd.wend[1] = gd.wend[2] = H;
       gd.ks = J; gd.kstride = H * J;
       gd.c = pf->X; gd.ldc = H;
-      if ((e = launch_gemm(EPI_RESID, true, gd, pf->part, st)) != hipSuccess) return e;
+      if ((e = launch_gemm(EPI_RESID, true, gd, pf->part, st, n1.g ? &n1 : nullptr)) != hipSuccess) return e;
     }
     if (last) {
       hipLaunchKernelGGL(pf_lm, dim3(MK_NWG), dim3(PF_THREADS), 0, st, (const float *)pf->X, T - 1, d->lnf, d->rms_eps,
