@@ -177,7 +177,9 @@ __device__ __noinline__ void gather_timeout(int *fail, int32_t *ctl, int site, i
 }
 
 // Poll up to MAXC 16-byte chunks per lane (two tagged slots each) until both tags equal `tag`,
-// then store the two values to LDS.  Returns false on watchdog expiry.
+// then store the two values to LDS.  Polls follow each other without a sleep: each round waits
+// for its own loads, which paces it (measured: a sleep between rounds only delays detection).
+// Returns false on watchdog expiry.
 template <int MAXC>
 __device__ __forceinline__ bool poll_chunks(__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[MAXC], float *const (&dp)[MAXC],
                                             uint32_t pend, uint32_t tag, int *fail, int32_t *ctl, int site, int tid) {
@@ -205,7 +207,6 @@ __device__ __forceinline__ bool poll_chunks(__amdgpu_buffer_rsrc_t rs, const uin
       gather_timeout(fail, ctl, site, tid, seen, tag);
       return false;
     }
-    __builtin_amdgcn_s_sleep(1);
   }
 }
 
@@ -1240,19 +1241,20 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             for (int e = 0; e < 8; ++e)
               av[c][i * 8 + e] = (NCOL == 1) ? avf[i * 8 + e] : (c < ncol && i < L_h) ? hn[c * H + i * G_h * 8 + kl + e] : 0.f;
       }
-      for (int rb = wg0; rb < wg1; rb += B) {
-        u32x4 wr[B][2];
+      // embedding rows stream through two register batches: the next batch's loads are issued
+      // before the current one is multiplied (branch-free: rows past this wave's range read zeros)
+      const __amdgpu_buffer_rsrc_t ers = tile_rsrc(m.embed, (uint32_t)((size_t)m.V * H * 2));
+      auto lm_load = [&](int rb, u32x4 (&wr)[B][2]) {
 #pragma unroll
         for (int r = 0; r < B; ++r) {
-          const u32x4 *p = reinterpret_cast<const u32x4 *>(m.embed) + (size_t)(rb + r) * L_h * 64 + lane;
-          if (rb + r < wg1) {
-            wr[r][0] = __builtin_nontemporal_load(p);
-            wr[r][1] = (L_h > 1) ? __builtin_nontemporal_load(p + 64) : u32x4{0u, 0u, 0u, 0u};
-          } else {
-            wr[r][0] = u32x4{0u, 0u, 0u, 0u};
-            wr[r][1] = u32x4{0u, 0u, 0u, 0u};
-          }
+          const bool ok = rb + r < wg1;
+          const uint32_t o0 = ok ? (uint32_t)(((size_t)(rb + r) * L_h * 64 + lane) * 16) : OOB_OFF;
+          wr[r][0] = __builtin_amdgcn_raw_buffer_load_b128(ers, o0, 0, AUX_NT);
+          wr[r][1] = (L_h > 1) ? __builtin_amdgcn_raw_buffer_load_b128(ers, ok ? o0 + 1024u : OOB_OFF, 0, AUX_NT)
+                               : u32x4{0u, 0u, 0u, 0u};
         }
+      };
+      auto lm_compute = [&](int rb, const u32x4 (&wr)[B][2]) {
 #pragma unroll
         for (int c = 0; c < NCOL; ++c) {
           if (c >= ncol) break;
@@ -1282,6 +1284,14 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             }
           }
         }
+      };
+      u32x4 wa[B][2], wb[B][2];
+      lm_load(wg0, wa);
+      for (int rb = wg0; rb < wg1; rb += 2 * B) {
+        lm_load(rb + B, wb);
+        lm_compute(rb, wa);
+        lm_load(rb + 2 * B, wa);
+        lm_compute(rb + B, wb);
       }
       // wave reduce (value desc, index asc), then across waves
       float *rv = work;                  // [NCOL][8]
