@@ -551,31 +551,59 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
       }
   }
   __syncthreads();
-  // X = (I + A)^-1 (unit lower triangular).  Column jj depends only on itself, so lane jj of
-  // wave 0 builds it alone, right-looking and held in registers: once row m of the column is
-  // final, it is eliminated from every row below (col_i -= A_im col_m).
-  if (tid < 64) {
-    const int jj = tid;
-    float col[MK_CHUNK];
-#pragma unroll
-    for (int i = 0; i < MK_CHUNK; ++i) col[i] = (i == jj) ? 1.f : 0.f;
-#pragma unroll
-    for (int m = 0; m < MK_CHUNK - 1; ++m) {
-      const float xm = col[m];
-      const float *am = A + m * CS;            // A[m][i] = A_im (transposed)
-#pragma unroll
-      for (int i4 = ((m + 1) & ~3); i4 < MK_CHUNK; i4 += 4) {
-        const float4 a4 = ld4(am + i4);
-        if (i4 + 0 > m) col[i4 + 0] = fmaf(-a4.x, xm, col[i4 + 0]);
-        if (i4 + 1 > m) col[i4 + 1] = fmaf(-a4.y, xm, col[i4 + 1]);
-        if (i4 + 2 > m) col[i4 + 2] = fmaf(-a4.z, xm, col[i4 + 2]);
-        if (i4 + 3 > m) col[i4 + 3] = fmaf(-a4.w, xm, col[i4 + 3]);
-      }
+  // X = (I + A)^-1 (unit lower triangular), by blocks of 16: the four diagonal blocks
+  // X_qq = (I + A_qq)^-1 by forward substitution, one wave each (lane c < 16 owns column c in
+  // registers); then block row by block row X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj, each 16 x 16
+  // product spread over the workgroup.  Blocks above the diagonal are zero (the scan reads four
+  // columns past the diagonal).
+  {
+    constexpr int NB = 16, NBK = MK_CHUNK / NB;
+    const int wq = tid >> 6, ln = tid & 63;
+    for (int e = tid; e < MK_CHUNK * MK_CHUNK; e += PF_THREADS) {
+      const int i = e / MK_CHUNK, jx = e % MK_CHUNK;
+      if (jx / NB > i / NB) X[i * CS + jx] = 0.f;
     }
+    if (ln < NB) {
+      const int b0 = wq * NB, jj = ln;
+      float col[NB];
 #pragma unroll
-    for (int i = 0; i < MK_CHUNK; ++i) X[i * CS + jj] = col[i];
+      for (int i = 0; i < NB; ++i) col[i] = (i == jj) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < NB - 1; ++m) {
+        const float xm = col[m];
+        const float *am = A + (b0 + m) * CS + b0;   // A[b0+m][b0+i] = A_{b0+i, b0+m}
+#pragma unroll
+        for (int i = m + 1; i < NB; ++i) col[i] = fmaf(-am[i], xm, col[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) X[(b0 + i) * CS + b0 + jj] = col[i];
+    }
+    __syncthreads();
+    float *R = Ks;   // [NBK - 1][NB][NB + 1] partial sums of one block row (K, Q are no longer needed)
+    constexpr int RS = NB + 1;
+    const int ri = (tid / NB) % NB, rj = tid % NB;   // element of a 16 x 16 block (256 threads)
+    for (int bi = 1; bi < NBK; ++bi) {
+      // R_bj = sum_{k=j}^{bi-1} A_{bi,k} X_{k,j} for every block j < bi
+      for (int bj = 0; bj < bi; ++bj) {
+        float acc = 0.f;
+        for (int bk = bj; bk < bi; ++bk)
+#pragma unroll
+          for (int t = 0; t < NB; ++t)   // A_{bi*16+ri, bk*16+t} X_{bk*16+t, bj*16+rj}
+            acc = fmaf(A[(bk * NB + t) * CS + bi * NB + ri], X[(bk * NB + t) * CS + bj * NB + rj], acc);
+        R[(bj * NB + ri) * RS + rj] = acc;
+      }
+      __syncthreads();
+      // X_{bi,j} = -X_{bi,bi} R_bj (X_bi,bi lower triangular)
+      for (int bj = 0; bj < bi; ++bj) {
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < NB; ++t)
+          if (t <= ri) acc = fmaf(X[(bi * NB + ri) * CS + bi * NB + t], R[(bj * NB + t) * RS + rj], acc);
+        X[(bi * NB + ri) * CS + bj * NB + rj] = -acc;
+      }
+      __syncthreads();
+    }
   }
-  __syncthreads();
   float *cT = c.cT + ((size_t)h * nch + ch) * MK_CHUNK * MK_CHUNK;
   for (int e4 = tid; e4 < MK_CHUNK * MK_CHUNK / 4; e4 += PF_THREADS) {
     const int i = e4 / (MK_CHUNK / 4), j = (e4 % (MK_CHUNK / 4)) * 4;
