@@ -630,7 +630,7 @@ struct PfScan {
 // carry RB rows of one head's state through every chunk of the pass
 __global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
   extern __shared__ float sm[];
-  const int h = blockIdx.y, r0 = blockIdx.x * RB, dk = s.dk, dv = s.dv, ks = dk + 4;
+  const int h = blockIdx.y, r0 = blockIdx.x * RB, dk = s.dk, dv = s.dv, ks = dk + 16;   // (row stride: see S0 k_i below)
   const int nch = MK_PT / MK_CHUNK, nchunk = (s.T + MK_CHUNK - 1) / MK_CHUNK;
   float *Sr = sm;                                  // [RB][dk]
   float *Ks = Sr + RB * dk, *Qs = Ks + MK_CHUNK * ks;
@@ -713,16 +713,34 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
     if (tid < MK_CHUNK) { gs[tid] = pg; ds[tid] = pd; bs[tid] = pb; }
     __syncthreads();
     if (c + 1 < nchunk) fetch(c + 1);
-    {  // S0 k_i and S0 q_i for row rp -> B and SQ
-      float a0 = 0.f, b0 = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < dk; d += 4) {
-        const float4 s0 = ld4(Sr + rp * dk + d);
-        a0 = dot4(s0, ld4(Ks + ti * ks + d), a0);
-        b0 = dot4(s0, ld4(Qs + ti * ks + d), b0);
+    {  // S0 k_i and S0 q_i -> B and SQ.  Thread (token tq, dim quarter dq) takes the float4 groups
+       // dq, dq + 4, ... of its token's k and q against all RB rows of S, so each k / q element
+       // is read from LDS once; the quarters are summed over the four adjacent lanes.  With the
+       // row stride dk + 16, the 16 lanes of an LDS access (4 tokens x 4 quarters) hit distinct banks.
+      const int tq = tid >> 2, dq = tid & 3;
+      float a[RB], bq[RB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) { a[r] = 0.f; bq[r] = 0.f; }
+#pragma unroll 4
+      for (int d = dq * 4; d < dk; d += 16) {
+        const float4 k4 = ld4(Ks + tq * ks + d), q4 = ld4(Qs + tq * ks + d);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const float4 s0 = ld4(Sr + r * dk + d);
+          a[r] = dot4(s0, k4, a[r]);
+          bq[r] = dot4(s0, q4, bq[r]);
+        }
       }
-      Bm[rp * CS + ti] = bs[ti] * (Vr[ti * RB + rp] - gs[ti] * a0);
-      SQ[rp * CS + ti] = b0;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        a[r] += dpp_mov<0xB1>(a[r]);  a[r] += dpp_mov<0x4E>(a[r]);
+        bq[r] += dpp_mov<0xB1>(bq[r]); bq[r] += dpp_mov<0x4E>(bq[r]);
+      }
+      // lane dq writes row dq (RB == 4)
+      const float ad = dq == 0 ? a[0] : dq == 1 ? a[1] : dq == 2 ? a[2] : a[3];
+      const float bd = dq == 0 ? bq[0] : dq == 1 ? bq[1] : dq == 2 ? bq[2] : bq[3];
+      Bm[dq * CS + tq] = bs[tq] * (Vr[tq * RB + dq] - gs[tq] * ad);
+      SQ[dq * CS + tq] = bd;
     }
     __syncthreads();
     {  // U = (I + A)^-1 B  (the inverse is zero above the diagonal)
@@ -1171,7 +1189,7 @@ static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStr
 
 static size_t chunk_prep_lds(int dk) { return (size_t)(2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 2 * MK_CHUNK) * 4; }
 static size_t scan_lds(int dk) {
-  return (size_t)(2 * RB * dk + 2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 3 * RB * CS + MK_CHUNK * RB + 3 * MK_CHUNK) * 4;
+  return (size_t)(2 * RB * dk + 2 * MK_CHUNK * (dk + 16) + 2 * MK_CHUNK * CS + 3 * RB * CS + MK_CHUNK * RB + 3 * MK_CHUNK) * 4;
 }
 
 // Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table.
