@@ -216,12 +216,12 @@ __device__ __forceinline__ bool poll_chunks(__amdgpu_buffer_rsrc_t rs, const uin
 // waves that keep weight loads in flight stay out of it.  Every thread calls it; it ends with a
 // barrier.  On watchdog expiry records the first failing site in the control block and returns false.
 template <int MAXC, int NPW>
-__device__ bool gather2d(const uint2 *src, int nrow, int ncol, int stride, uint32_t tag, float *dst, int *fail,
-                         int32_t *ctl, int site, int tid) {
+__device__ bool poll2d(const uint2 *src, int nrow, int ncol, int stride, uint32_t tag, float *dst, int *fail,
+                       int32_t *ctl, int site, int tid) {
   const int half = ncol >> 1;
   const int nchunk = nrow * half;
   const int pt = tid - (MK_WAVES - NPW) * 64;   // index among the polling threads
-  if (pt >= 0) {
+  if (pt >= 0 && *fail == 0) {   // (after a watchdog expiry in this workgroup: go straight to the barrier)
     const uint32_t bytes = (uint32_t)(((nrow - 1) * stride + ncol) * 8);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, bytes, RSRC_W3);
     for (int base = 0; base < nchunk; base += MAXC * NPW * 64) {
@@ -239,6 +239,12 @@ __device__ bool gather2d(const uint2 *src, int nrow, int ncol, int stride, uint3
       if (!poll_chunks<MAXC>(rs, off, dp, pend, tag, fail, ctl, site, tid)) break;
     }
   }
+  return *fail == 0;
+}
+template <int MAXC, int NPW>
+__device__ bool gather2d(const uint2 *src, int nrow, int ncol, int stride, uint32_t tag, float *dst, int *fail,
+                         int32_t *ctl, int site, int tid) {
+  poll2d<MAXC, NPW>(src, nrow, ncol, stride, tag, dst, fail, ctl, site, tid);
   lbar();
   return *fail == 0;
 }
@@ -600,6 +606,36 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       }
     }
     keep_issued();
+  };
+
+  // Residual slice lw of every column: xres slice + the 8 XCD partials of `part` (layout
+  // [col][8][H]), published to the XCD's residual slots `xr`.  With one polling wave (decode) that
+  // wave gathers, sums and publishes on its own, without a barrier (its own LDS writes are seen by
+  // its later reads); otherwise every wave takes part after the gather's barrier.  A watchdog
+  // expiry is reported through `flag` and acted on after the next gather.
+  auto reduce_slices = [&](const uint2 *part, uint2 *xr, float *tmp, int site) {
+    if constexpr (NPW == 1) {
+      if (w8 == MK_WAVES - 1 && poll2d<MCS, NPW>(part + lw * SL, ncol * MK_NX, SL, H, a.tag0, tmp, flag, m.ctl, site, tid0)) {
+        for (int i = lane; i < ncol * SL; i += 64) {
+          const int c = i / SL, k = i - c * SL;
+          float sm = tmp[(c * MK_NX) * SL + k];
+#pragma unroll
+          for (int g = 1; g < MK_NX; ++g) sm += tmp[(c * MK_NX + g) * SL + k];
+          pub_xcd(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, a.tag0);
+        }
+      }
+    } else {
+      gather2d<MCS, NPW>(part + lw * SL, ncol * MK_NX, SL, H, a.tag0, tmp, flag, m.ctl, site, tid0);
+      if (*flag == 0) {
+        for (int i = tid0; i < ncol * SL; i += MK_THREADS) {
+          const int c = i / SL, k = i - c * SL;
+          float sm = tmp[(c * MK_NX) * SL + k];
+#pragma unroll
+          for (int g = 1; g < MK_NX; ++g) sm += tmp[(c * MK_NX + g) * SL + k];
+          pub_xcd(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, a.tag0);
+        }
+      }
+    }
   };
 
   {
@@ -1103,15 +1139,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         // [NCOL*8][SL], apart from everything the mixer phases read: the polling wave fills it
         // while the other waves may still be reading the out-projection operand
         float *tmp = work + 6400;
-        if (!gather2d<MCS, NPW>(ly.x_mix + lw * SL, ncol * MK_NX, SL, H, tg, tmp, flag, m.ctl, SITE(8), tid)) MK_BAIL();
         uint2 *xr = ly.x_r1 + (size_t)x * MK_MAXCOL * H;
-        for (int i = tid; i < ncol * SL; i += MK_THREADS) {
-          const int c = i / SL, k = i - c * SL;
-          float sm = tmp[(c * MK_NX) * SL + k];
-#pragma unroll
-          for (int g = 1; g < MK_NX; ++g) sm += tmp[(c * MK_NX + g) * SL + k];
-          pub_xcd(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, tg);
-        }
+        reduce_slices(ly.x_mix, xr, tmp, SITE(8));
         if (!gather2d<MCL, NPW>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(9), tid)) MK_BAIL();
       }
       // ================================================================ FFN
@@ -1201,15 +1230,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       // ---- R2: residual += sum of the 8 FFN slices
       {
         float *tmp = work + 6400;  // [NCOL*8][SL], apart from the down-projection operand mv
-        if (!gather2d<MCS, NPW>(ly.x_ffn + lw * SL, ncol * MK_NX, SL, H, tg, tmp, flag, m.ctl, SITE(12), tid)) MK_BAIL();
         uint2 *xr = ly.x_r2 + (size_t)x * MK_MAXCOL * H;
-        for (int i = tid; i < ncol * SL; i += MK_THREADS) {
-          const int c = i / SL, k = i - c * SL;
-          float sm = tmp[(c * MK_NX) * SL + k];
-#pragma unroll
-          for (int g = 1; g < MK_NX; ++g) sm += tmp[(c * MK_NX + g) * SL + k];
-          pub_xcd(xr + c * H + lw * SL + k, xres[c * H + lw * SL + k] + sm, tg);
-        }
+        reduce_slices(ly.x_ffn, xr, tmp, SITE(12));
         if (!gather2d<MCL, NPW>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(13), tid)) MK_BAIL();
       }
     }  // layers

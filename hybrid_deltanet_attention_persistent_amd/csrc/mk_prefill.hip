@@ -1151,9 +1151,9 @@ static hipError_t launch_gemm_t(const PfGemm &g, int nsplit, hipStream_t st) {
   hipLaunchKernelGGL((pf_gemm<EPI, MT, NT, WGM, WGN>), grid, dim3(PF_THREADS), lds, st, g);
   return hipGetLastError();
 }
-// Wide projections: 64 x 256 workgroup tiles (4 waves of 64 x 64).  The 1024-wide outputs that
-// add into the residual stream: 64 x 64 tiles and split-K (partials reduced in split order), so
-// that the grid fills the chip and each K stream is short.
+// Wide projections: 64 x 128 workgroup tiles (4 waves of 64 x 32, two workgroups per CU).  The
+// 1024-wide outputs that add into the residual stream: the same tiles with split-K (partials
+// reduced in split order), so that the grid fills the chip and each K stream is short.
 // The RMSNorm that follows a projection adding into the residual stream, fused into the split-K
 // reduction when there is one (gain g; output as hi + lo into oh / ol with row stride ld).
 struct PfNext {
@@ -1179,7 +1179,7 @@ static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStr
   g.kper = g.K / nsplit;
   g.part = part;
   g.part_stride = (size_t)MK_PT * g.ldc;
-  hipError_t e = small ? launch_gemm_t<EPI_PART, 2, 2, 2, 2>(g, nsplit, st) : launch_gemm_t<EPI_PART, 4, 4, 1, 4>(g, nsplit, st);
+  hipError_t e = small ? launch_gemm_t<EPI_PART, 4, 2, 1, 4>(g, nsplit, st) : launch_gemm_t<EPI_PART, 4, 4, 1, 4>(g, nsplit, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pf_reduce_norm, dim3(g.M), dim3(PF_THREADS), 0, st, g.c, (const float *)part, nsplit, g.part_stride,
                      g.N, next ? next->g : (const float *)nullptr, next ? next->eps : 0.f,
