@@ -258,13 +258,13 @@ struct GSeg {
 
 // Gather several blocks (all addressed from one base) in one polling loop and one barrier.
 template <int MAXC, int NPW, int NSEG>
-__device__ bool gather_segs(const uint2 *base, const GSeg (&sg)[NSEG], uint32_t tag, int *fail, int32_t *ctl,
+__device__ bool poll_segs(const uint2 *base, const GSeg (&sg)[NSEG], uint32_t tag, int *fail, int32_t *ctl,
                             int site, int tid) {
   int total = 0;
 #pragma unroll
   for (int s = 0; s < NSEG; ++s) total += sg[s].nrow * (sg[s].ncol >> 1);
   const int pt = tid - (MK_WAVES - NPW) * 64;
-  if (pt >= 0) {
+  if (pt >= 0 && *fail == 0) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, 0x7fffffff, RSRC_W3);
     for (int b0 = 0; b0 < total; b0 += MAXC * NPW * 64) {
       uint32_t off[MAXC];
@@ -292,6 +292,12 @@ __device__ bool gather_segs(const uint2 *base, const GSeg (&sg)[NSEG], uint32_t 
       if (!poll_chunks<MAXC>(rs, off, dp, pend, tag, fail, ctl, site, tid)) break;
     }
   }
+  return *fail == 0;
+}
+template <int MAXC, int NPW, int NSEG>
+__device__ bool gather_segs(const uint2 *base, const GSeg (&sg)[NSEG], uint32_t tag, int *fail, int32_t *ctl,
+                            int site, int tid) {
+  poll_segs<MAXC, NPW, NSEG>(base, sg, tag, fail, ctl, site, tid);
   lbar();
   return *fail == 0;
 }
@@ -674,6 +680,10 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       int tid = tid0;
       asm volatile("" : "+v"(tid));
       const int lane = tid & 63;
+      // gains of this layer's gated RMSNorm (DeltaNet), held by the last wave, which applies it in
+      // D3: elements lane and lane + 64
+      const int gnn = (ly.kind == 0 && w8 == MK_WAVES - 1) ? dv : 0;
+      const float gnv0 = ld_gain(ly.dn_gnorm, gnn, lane), gnv1 = ld_gain(ly.dn_gnorm, gnn, lane + 64);
       // gains of this layer's FFN norm, needed after the mixer
       float g2v[16], g2a = 0.f, g2b = 0.f;
       if constexpr (NCOL == 1) {
@@ -737,7 +747,6 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         float *nrm = ab + NCOL * 2;               // [NCOL][2]
         float *gts = nrm + NCOL * 2;              // [NCOL][2] alpha, beta
         float *outo = gts + NCOL * 2;             // [NCOL][RW]
-        float gn = 0.f;
         if (x < nh) {
           // this wave's row of S (wave w < RW owns row r0 + w; lane holds elements lane + 64 j)
           const bool act = w8 < RW;
@@ -754,7 +763,6 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           else if (tid < nch) ch = 2 * nh * dk + x * dv + r0 + (tid - 2 * dk);
           float hist[3] = {0.f, 0.f, 0.f};
           float4 wt = make_float4(0.f, 0.f, 0.f, 0.f);
-          gn = (tid < dv) ? ly.dn_gnorm[tid] : 0.f;   // gated-norm gain, used in D3
           if (tid < nch) {
             wt = *reinterpret_cast<const float4 *>(ly.dn_conv + ch * 4);
             const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(ly.ring, 0, MK_RING * nconv * 4, RSRC_W3);
@@ -879,15 +887,22 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           {
             const GSeg sg[2] = {{(int)(xo - xin), ncol, dv, x_o_len, o},       // o rows of the head
                                 {2 * dk + dv, ncol, dv, r_in_max, z}};         // z of the head
-            if (!gather_segs<MCS, NPW, 2>(xin, sg, tg, flag, m.ctl, SITE(4), tid)) MK_BAIL();
+            // with one polling wave, that wave gathers and normalises before the barrier
+            if constexpr (NPW == 1) poll_segs<MCS, NPW, 2>(xin, sg, tg, flag, m.ctl, SITE(4), tid);
+            else gather_segs<MCS, NPW, 2>(xin, sg, tg, flag, m.ctl, SITE(4), tid);
           }
-          for (int c = 0; c < ncol; ++c) {
-            float sq = 0.f;
-            for (int i = tid; i < dv; i += MK_THREADS) sq = fmaf(o[c * dv + i], o[c * dv + i], sq);
-            const float den = sqrtf(block_sum(sq, red) / (float)dv + m.rms_eps);
-            if (tid < dv) o[c * dv + tid] = o[c * dv + tid] / den * gn * siluf_(z[c * dv + tid]);
+          // gated RMSNorm of each column, by the last wave (lane: elements lane, lane + 64)
+          if (w8 == MK_WAVES - 1 && *flag == 0) {
+            FOR_COL(c) {
+              const float a0 = o[c * dv + lane], a1 = (dv > 64) ? o[c * dv + 64 + lane] : 0.f;
+              const float sq = fmaf(a1, a1, fmaf(a0, a0, 0.f));
+              const float den = sqrtf(wave_sum(sq) / (float)dv + m.rms_eps);
+              o[c * dv + lane] = a0 / den * gnv0 * siluf_(z[c * dv + lane]);
+              if (dv > 64) o[c * dv + 64 + lane] = a1 / den * gnv1 * siluf_(z[c * dv + 64 + lane]);
+            }
           }
           lbar();
+          if (*flag) MK_BAIL();
 #pragma unroll
           for (int r = 0; r < NRG_O; ++r) {
             const int rg = wx + r * XW;
