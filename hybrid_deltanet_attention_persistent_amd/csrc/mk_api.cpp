@@ -347,7 +347,6 @@ static int check_device(int *dev) {
     return fail(MK_ELAUNCH, std::string("device is ") + prop.gcnArchName + ", need gfx950 (MI355X)");
   if (prop.multiProcessorCount != MK_NWG)
     return fail(MK_ELAUNCH, "device has " + std::to_string(prop.multiProcessorCount) + " CUs, need 256 (8 XCDs x 32)");
-  if (!prop.cooperativeLaunch) return fail(MK_ELAUNCH, "device has no cooperative launch");
   for (int shape : {MK_SHAPE_ANY, MK_SHAPE_H1024})
     for (int tmpl : {1, MK_MAXCOL}) {
       int per_cu = 0;

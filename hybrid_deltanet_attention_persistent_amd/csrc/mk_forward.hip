@@ -1,6 +1,6 @@
 // mk_forward.hip -- persistent single-launch forward pass of the hybrid Gated-DeltaNet +
 // attention decoder on MI355X (gfx950): one decode step or one multi-token verify
-// forward, each in one cooperative launch (prompts go through mk_prefill.hip).
+// forward, each in one launch (prompts go through mk_prefill.hip).
 //
 // What it computes: the launch page "OS Megakernel that match M5 Max Tok/w at 2x
 // the Throughput on RTX 3090" (section "We wrote a single CUDA kernel that runs
@@ -1447,10 +1447,15 @@ static const void *forward_fn(int ncol_template, int shape) {
   return (ncol_template == 1) ? (const void *)mk_forward<1, MK_SHAPE_ANY> : (const void *)mk_forward<MK_MAXCOL, MK_SHAPE_ANY>;
 }
 
+// The workgroups wait for each other's data, so all 256 must be resident at once.  The launch does
+// not need the cooperative-launch path for that (measured: it costs about 16 us per launch): the
+// grid is one workgroup per CU (the LDS request admits one per CU, the host checks the occupancy
+// and the CU count at load), launches on one stream run one after the other, and every wait is
+// bounded -- if another process's kernel held CUs so that some workgroups could not start, the
+// resident ones report MK_EHANG after the watchdog instead of waiting forever.
 extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, int shape, hipStream_t stream) {
   void *args[] = {const_cast<MkLaunch *>(a)};
-  return hipLaunchCooperativeKernel(forward_fn(ncol_template, shape), dim3(MK_NWG), dim3(MK_THREADS), args,
-                                    MK_LDS_BYTES, stream);
+  return hipLaunchKernel(forward_fn(ncol_template, shape), dim3(MK_NWG), dim3(MK_THREADS), args, MK_LDS_BYTES, stream);
 }
 
 extern "C" hipError_t mk_forward_occupancy(int ncol_template, int shape, int *blocks_per_cu) {
