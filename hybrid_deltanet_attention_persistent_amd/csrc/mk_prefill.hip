@@ -325,11 +325,11 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
         const int col = n0 + ni * 16 + (lane & 15);
         const float v = acc[mi][ni][i];
         if (EPI == EPI_SWIGLU) {
-          // columns 2j (gate) and 2j+1 (up) of one intermediate index sit in lanes l, l^1
-          const float u = __shfl_xor(v, 1, 64);
+          // columns 2j (gate) and 2j+1 (up) of one intermediate index sit in lanes l, l^1 (DPP swap)
+          const float u = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
           if ((lane & 1) == 0 && row < g.M && col < g.N) {
             const size_t o = (size_t)row * g.ldo + (col >> 1);
-            split_store(siluf_(v) * u, g.oh + o, g.ol + o);
+            split_store(__fdividef(v, 1.f + __expf(-v)) * u, g.oh + o, g.ol + o);   // SiLU(gate) * up
           }
         } else if (row < g.M && col < g.N) {
           if (EPI == EPI_PART) {
