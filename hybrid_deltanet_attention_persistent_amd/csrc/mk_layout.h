@@ -130,7 +130,8 @@ struct MkPf {
   float *q, *k, *v;                   // [nh][PT][dk|dv] conv + SiLU (+ L2 norm for q, k), head-major
   float *z;                           // [PT][nh dv] output-gate inputs
   float *la, *be;                     // [nh][PT] log alpha, beta
-  float *cT, *cM;                     // [nh][PT/CHUNK][CHUNK][CHUNK] (I + A)^-1 and decay-weighted q.k
+  float *cW, *cQ, *cU, *cO;           // [nh][PT/CHUNK][CHUNK][dk|dv] chunk terms W, Q~, U', O' of the delta rule
+  float *cKt;                         // [nh][PT/CHUNK][dk][CHUNK] the chunk's keys, transposed
   float *cg, *cd;                     // [nh][PT/CHUNK][CHUNK] exp(G_i), exp(G_last - G_i)
   float *o;                           // [PT][nh dv] delta-rule output
   float *aq;                          // [PT][nq hd] queries after RoPE

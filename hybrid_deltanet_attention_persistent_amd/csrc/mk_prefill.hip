@@ -42,7 +42,6 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 namespace {
 
 constexpr int PF_THREADS = 256;
-constexpr int RB = 4;          // state rows per scan workgroup (one per wave)
 
 __device__ __forceinline__ uint32_t f2bf(float f) {  // round to nearest even
   uint32_t u = __float_as_uint(f);
@@ -148,6 +147,16 @@ __device__ __forceinline__ float dot4(const float4 a, const float4 b, float s) {
   s = fmaf(a.x, b.x, s); s = fmaf(a.y, b.y, s); s = fmaf(a.z, b.z, s); return fmaf(a.w, b.w, s);
 }
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+// Workgroup barrier that orders LDS only.  __syncthreads also waits for the wave's outstanding
+// global stores, and with them (one in-order counter) for every load issued before them, which
+// would drain a prefetch at each barrier; where waves exchange data through LDS only, this one
+// keeps the prefetch in flight.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ------------------------------------------------------------------------------ row kernels
 __global__ void __launch_bounds__(PF_THREADS) pf_embed(const uint16_t *embed, const int32_t *tok, int H, int V,
@@ -206,9 +215,11 @@ __device__ __forceinline__ int tileG(int K) {
 // Workgroup tile BM x BN (BM = WGM*MT*16, BN = WGN*NT*16, WGM*WGN = 4 waves), K in stages of 64.
 // Each stage of A (hi and lo) and W is copied into LDS once per workgroup (16-byte loads: 128
 // contiguous bytes per row), double-buffered: the next stage's loads are in flight while the
-// MFMAs of the current one run.  LDS rows are padded to 72 elements so the 16-byte fragment
-// reads of 8 consecutive rows hit distinct banks.
-constexpr int GBK = 64, GLD = GBK + 8;
+// MFMAs of the current one run.  LDS rows are padded to 80 elements (10 units of 16 bytes): a
+// 16-byte LDS read is served for 16 lanes at a time, and with this row stride the fragment reads
+// (16 rows, one 16-byte column per group of 16 lanes) hit distinct banks, which a 9-unit stride
+// does not (measured: twice the LDS time).
+constexpr int GBK = 64, GLD = GBK + 16;
 
 template <int EPI, int MT, int NT, int WGM, int WGN>
 __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
@@ -488,83 +499,111 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_ring(PfDn d) {
     d.ring[((p0 + t) & (MK_RING - 1)) * d.C + ch] = d.P[(size_t)t * d.NP + dn_col(d, ch)];
 }
 
+// v_mfma_f32_16x16x4f32: D += A B with A 16 x 4, B 4 x 16 (full FP32).  Lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16]; register v of lane l holds D[4 (l / 16) + v][l % 16].
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 struct PfChunk {
-  const float *q, *k, *la, *be;   // head-major [nh][PT][dk], [nh][PT]
-  float *cT, *cM, *cg, *cd;       // [nh][PT/CHUNK][CHUNK][CHUNK], [nh][PT/CHUNK][CHUNK]
-  int T, dk;
+  const float *q, *k, *v, *la, *be;   // head-major [nh][PT][dk|dv], [nh][PT]
+  float *cW, *cQ, *cU, *cO, *cKt;     // per (head, chunk), CHUNK x dk each, in the fragment orders below
+  float *cg, *cd;                     // [nh][PT/CHUNK][CHUNK] exp(G_i), exp(G_last - G_i)
+  int T;
 };
 
-// per (chunk, head): (I + A)^-1, the decay-weighted q.k matrix and the decays
+// Per (chunk, head), everything of the chunk that does not depend on the state entering it
+// (the chunked form of the gated delta rule, rewritten so that the state enters only through
+// products with it).  With G_i the in-chunk prefix sums of log alpha, gamma_i = e^{G_i},
+// A_ij = beta_i e^{G_i - G_j} k_i.k_j (j < i), T = (I + A)^-1, M_ij = e^{G_i - G_j} q_i.k_j (j <= i):
+//   W  = T diag(beta gamma) K,   U' = T diag(beta) V,
+//   Q~ = diag(gamma) Q - M W,    O' = M U'
+// so that, for the state S entering the chunk (rows = value dims):
+//   U = U' - W S^T,   O = Q~ S^T + O',   S_next = gamma_last S + (diag(d) U)^T K,  d_i = e^{G_last - G_i}
+// which is the recurrence token by token (U_i = beta_i (v_i - S_{i-1} k_i) scaled into the chunk).
+// Q~ and O' use M T, computed once.  The products run on FP32 MFMA.
 constexpr int CS = MK_CHUNK + 4;   // padded row stride of the chunk matrices in LDS
+// The chunk terms are stored in the order in which the scan's MFMA fragments read them, so that
+// each 16-byte load of a wave covers 1 KB of contiguous memory.  W, Q~, U', O' (token t, column
+// n): 16 x 16 block (t / 16, n / 16), then column quad (n % 16) / 4, token t % 16, n % 4.
+// K^T (dim d, token t): block (d / 16, t / 16), then token quad (t % 16) / 4, dim d % 16, t % 4.
+template <int DK>
+__device__ __forceinline__ int frag_tn(int t, int n) {
+  return ((((t >> 4) * (DK / 16) + (n >> 4)) * 4 + ((n & 15) >> 2)) * 16 + (t & 15)) * 4 + (n & 3);
+}
+__device__ __forceinline__ int frag_kt(int d, int t) {
+  return ((((d >> 4) * 4 + (t >> 4)) * 4 + ((t & 15) >> 2)) * 16 + (d & 15)) * 4 + (t & 3);
+}
+template <int DK>
 __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
   extern __shared__ float sm[];
-  const int ch = blockIdx.x, h = blockIdx.y, nch = MK_PT / MK_CHUNK;
+  constexpr int KS = DK + 4;                   // padded rows keep float4 reads conflict-free
+  // workgroup (head h, chunk ch) runs on XCD h % 8, like the scan workgroups of head h, which
+  // then read what it writes from their own L2
+  const int h = blockIdx.x, ch = blockIdx.y, nch = MK_PT / MK_CHUNK;
   const int t0 = ch * MK_CHUNK, Cn = min(MK_CHUNK, c.T - t0);
-  const int dk = c.dk, ks = dk + 4;           // padded rows keep float4 reads conflict-free
-  float *Ks = sm, *Qs = Ks + MK_CHUNK * ks;
-  float *A = Qs + MK_CHUNK * ks;              // [64][CS]
-  float *X = A + MK_CHUNK * CS;               // [64][CS]
-  float *Gs = X + MK_CHUNK * CS, *bs = Gs + MK_CHUNK;
+  float *Ks = sm, *Qs = Ks + MK_CHUNK * KS, *Vs = Qs + MK_CHUNK * KS;
+  float *A = Vs + MK_CHUNK * KS;               // [64][CS] A (transposed), later M T
+  float *X = A + MK_CHUNK * CS;                // [64][CS] (I + A)^-1
+  float *Mm = X + MK_CHUNK * CS;               // [64][CS] M
+  float *Gs = Mm + MK_CHUNK * CS, *bs = Gs + MK_CHUNK, *gam = bs + MK_CHUNK, *bgam = gam + MK_CHUNK;
   const size_t hb = (size_t)h * MK_PT;
-  const int tid = threadIdx.x;
-  g2l<8>(Ks, ks, c.k + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
-  g2l<8>(Qs, ks, c.q + (hb + t0) * dk, dk, MK_CHUNK, dk, Cn);
-  if (tid < MK_CHUNK) bs[tid] = tid < Cn ? c.be[hb + t0 + tid] : 0.f;
-  if (tid < 64) {  // in-chunk prefix sums of log alpha (one wave, Hillis-Steele)
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  g2l<8>(Ks, KS, c.k + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
+  g2l<8>(Qs, KS, c.q + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
+  if (tid < 64) {  // in-chunk prefix sums of log alpha (one wave, Hillis-Steele), beta, the decays
     float G = tid < Cn ? c.la[hb + t0 + tid] : 0.f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_up(G, o, 64);
       if (tid >= o) G += y;
     }
+    const float b = tid < Cn ? c.be[hb + t0 + tid] : 0.f;
     Gs[tid] = G;
+    bs[tid] = b;
+    gam[tid] = tid < Cn ? expf(G) : 0.f;
+    bgam[tid] = b * gam[tid];
   }
   __syncthreads();
-  float *cM = c.cM + ((size_t)h * nch + ch) * MK_CHUNK * MK_CHUNK;
-  {  // thread -> 4x4 block of (i, j): k_i.k_j and q_i.k_j
-    const int i0 = (tid >> 4) * 4, j0 = (tid & 15) * 4;
-    float kk[4][4], qk[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) { kk[a][b] = 0.f; qk[a][b] = 0.f; }
-    if (j0 <= i0 + 3) {
-      for (int d = 0; d < dk; d += 4) {
-        float4 ki[4], qi[4], kj[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) { ki[a] = ld4(Ks + (i0 + a) * ks + d); qi[a] = ld4(Qs + (i0 + a) * ks + d); kj[a] = ld4(Ks + (j0 + a) * ks + d); }
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) { kk[a][b] = dot4(ki[a], kj[b], kk[a][b]); qk[a][b] = dot4(qi[a], kj[b], qk[a][b]); }
+  {  // k_i.k_j and q_i.k_j on the 10 16 x 16 tiles with ti >= tj (FP32 MFMA; in the i-th group of
+     // four k steps lane group g takes the dims 16 i + 4 g ..); tiles above are never read
+#pragma unroll 1
+    for (int tt = w; tt < 10; tt += 4) {
+      const int ti = tt < 1 ? 0 : tt < 3 ? 1 : tt < 6 ? 2 : 3, tj = tt - ti * (ti + 1) / 2;
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
+      const float *ka = Ks + (16 * ti + c16) * KS + 4 * g, *qa = Qs + (16 * ti + c16) * KS + 4 * g;
+      const float *kb = Ks + (16 * tj + c16) * KS + 4 * g;
+#pragma unroll 4
+      for (int i = 0; i < DK / 16; ++i) {
+        const float4 a = ld4(ka + 16 * i), q = ld4(qa + 16 * i), b = ld4(kb + 16 * i);
+        kk = mfma4(a.x, b.x, kk); qk = mfma4(q.x, b.x, qk);
+        kk = mfma4(a.y, b.y, kk); qk = mfma4(q.y, b.y, qk);
+        kk = mfma4(a.z, b.z, kk); qk = mfma4(q.z, b.z, qk);
+        kk = mfma4(a.w, b.w, kk); qk = mfma4(q.w, b.w, qk);
       }
-    }
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int i = i0 + a, j = j0 + b;
+      for (int v = 0; v < 4; ++v) {
+        const int i = 16 * ti + 4 * g + v, j = 16 * tj + c16;
         const bool lower = j <= i && i < Cn;
         const float dec = lower ? expf(Gs[i] - Gs[j]) : 0.f;
-        A[j * CS + i] = (lower && j < i) ? bs[i] * dec * kk[a][b] : 0.f;   // transposed: A[j][i] holds A_ij
-        cM[i * MK_CHUNK + j] = dec * qk[a][b];
+        A[j * CS + i] = (lower && j < i) ? bs[i] * dec * kk[v] : 0.f;   // transposed: A[j][i] holds A_ij
+        Mm[i * CS + j] = dec * qk[v];
       }
+    }
   }
   __syncthreads();
   // X = (I + A)^-1 (unit lower triangular), by blocks of 16: the four diagonal blocks
   // X_qq = (I + A_qq)^-1 by forward substitution, one wave each (lane c < 16 owns column c in
   // registers); then block row by block row X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj, each 16 x 16
-  // product spread over the workgroup.  Blocks above the diagonal are zero (the scan reads four
-  // columns past the diagonal).
+  // product spread over the workgroup.  Blocks above the diagonal are zero.
   {
     constexpr int NB = 16, NBK = MK_CHUNK / NB;
-    const int wq = tid >> 6, ln = tid & 63;
     for (int e = tid; e < MK_CHUNK * MK_CHUNK; e += PF_THREADS) {
       const int i = e / MK_CHUNK, jx = e % MK_CHUNK;
       if (jx / NB > i / NB) X[i * CS + jx] = 0.f;
     }
-    if (ln < NB) {
-      const int b0 = wq * NB, jj = ln;
+    if (lane < NB) {
+      const int b0 = w * NB, jj = lane;
       float col[NB];
 #pragma unroll
       for (int i = 0; i < NB; ++i) col[i] = (i == jj) ? 1.f : 0.f;
@@ -579,7 +618,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
       for (int i = 0; i < NB; ++i) X[(b0 + i) * CS + b0 + jj] = col[i];
     }
     __syncthreads();
-    float *R = Ks;   // [NBK - 1][NB][NB + 1] partial sums of one block row (K, Q are no longer needed)
+    float *R = Vs;   // [NBK - 1][NB][NB + 1] partial sums of one block row (V is loaded afterwards)
     constexpr int RS = NB + 1;
     const int ri = (tid / NB) % NB, rj = tid % NB;   // element of a 16 x 16 block (256 threads)
     for (int bi = 1; bi < NBK; ++bi) {
@@ -604,15 +643,70 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
       __syncthreads();
     }
   }
-  float *cT = c.cT + ((size_t)h * nch + ch) * MK_CHUNK * MK_CHUNK;
-  for (int e4 = tid; e4 < MK_CHUNK * MK_CHUNK / 4; e4 += PF_THREADS) {
-    const int i = e4 / (MK_CHUNK / 4), j = (e4 % (MK_CHUNK / 4)) * 4;
-    *reinterpret_cast<float4 *>(cT + i * MK_CHUNK + j) = ld4(X + i * CS + j);
+  g2l<8>(Vs, KS, c.v + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
+  {  // M T into A (both lower triangular): wave w takes row block w, column blocks 0..w
+#pragma unroll 1
+    for (int nt = 0; nt <= w; ++nt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = nt; kb <= w; ++kb)
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int m = 16 * kb + 4 * k4 + g;
+          acc = mfma4(Mm[(16 * w + c16) * CS + m], X[m * CS + 16 * nt + c16], acc);
+        }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) A[(16 * w + 4 * g + v) * CS + 16 * nt + c16] = acc[v];
+    }
+  }
+  __syncthreads();
+  const size_t cb = (size_t)h * nch + ch, mo = cb * MK_CHUNK * DK;
+  {  // W, U', Q~, O': wave w takes the 16-column blocks w, w + 4, ... of all four row blocks
+     // (the k range of row block rb ends at its diagonal)
+    for (int nt = w; nt < DK / 16; nt += 4) {
+      const int d = 16 * nt + c16;
+#pragma unroll 1
+      for (int rb = 0; rb < 4; ++rb) {
+        f32x4 aw = {0.f, 0.f, 0.f, 0.f}, aq = aw, au = aw, ao = aw;
+        for (int kb = 0; kb <= rb; ++kb) {
+          float x[4], mt[4], bk[4], bv[4];
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            const int j = 16 * kb + 4 * k4 + g;
+            x[k4] = X[(16 * rb + c16) * CS + j];
+            mt[k4] = A[(16 * rb + c16) * CS + j];
+            bk[k4] = Ks[j * KS + d] * bgam[j];
+            bv[k4] = Vs[j * KS + d] * bs[j];
+          }
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            aw = mfma4(x[k4], bk[k4], aw);
+            aq = mfma4(mt[k4], bk[k4], aq);
+            au = mfma4(x[k4], bv[k4], au);
+            ao = mfma4(mt[k4], bv[k4], ao);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = 16 * rb + 4 * g + v;
+          const size_t o = mo + frag_tn<DK>(i, d);
+          c.cW[o] = aw[v];
+          c.cQ[o] = gam[i] * Qs[i * KS + d] - aq[v];
+          c.cU[o] = au[v];
+          c.cO[o] = ao[v];
+        }
+      }
+    }
+  }
+  for (int e = tid; e < DK * MK_CHUNK; e += PF_THREADS) {   // K^T in fragment order:
+    // e = (((db * 4 + tb) * 4 + tq) * 16 + dl) * 4 + te
+    const int te = e & 3, dl = (e >> 2) & 15, tq = (e >> 6) & 3, tb = (e >> 8) & 3, db = e >> 10;
+    const int d = 16 * db + dl, t = 16 * tb + 4 * tq + te;
+    c.cKt[mo + e] = Ks[t * KS + d];
   }
   if (tid < MK_CHUNK) {
     const int i = tid;
-    const size_t o = ((size_t)h * nch + ch) * MK_CHUNK + i;
-    c.cg[o] = i < Cn ? expf(Gs[i]) : 0.f;
+    const size_t o = cb * MK_CHUNK + i;
+    c.cg[o] = gam[i];
     c.cd[o] = i < Cn ? expf(Gs[Cn - 1] - Gs[i]) : 0.f;
   }
 }
@@ -621,172 +715,143 @@ struct PfScan {
   float *S;                        // [nh][dv][dk] layer state
   const float *pend;               // [2][nh][MAXCOL][dk + dv + 2] pending updates (k | v | alpha beta)
   const int32_t *ctl;
-  const float *q, *k, *v, *be;     // head-major
-  const float *cT, *cM, *cg, *cd;
+  const float *cW, *cQ, *cU, *cO, *cKt, *cg, *cd;
   float *o;                        // [PT][nh dv]
-  int T, nh, dk, dv;
+  int T, nh;
 };
 
-// carry RB rows of one head's state through every chunk of the pass
-__global__ void __launch_bounds__(PF_THREADS) pf_dn_scan(PfScan s) {
+// Carry 16 rows of one head's state through every chunk of the pass.  Per chunk, with S the
+// state entering it: P = S [W; Q~]^T (16 x 128 on FP32 MFMA: waves 0-3 take the 16-token
+// blocks of W, waves 4-7 those of Q~), U = U' - P_W^T and the outputs O = P_Q^T + O'; then
+// S <- gamma_last S + (diag(d) U)^T K (wave w takes the 16 state columns of block w).  The state
+// moves between the two MFMA layouts through LDS; the next chunk's operands are loaded into
+// registers while the current one is computed.
+constexpr int SCAN_THREADS = 512;
+template <int DK>
+__global__ void __launch_bounds__(SCAN_THREADS) pf_dn_scan(PfScan s) {
+  constexpr int SR = 16;              // state rows per workgroup
+  // MFMA k order: in the i-th group of four k steps, lane group g takes the four dims (or tokens)
+  // 16 i + 4 g .. 16 i + 4 g + 3, so that one 16-byte load per lane reads 64 contiguous bytes per row
+  constexpr int SL = DK + 4, DL = MK_CHUNK + 4;
+  constexpr int OL = SR + 4;          // row stride of the staged outputs
   extern __shared__ float sm[];
-  const int h = blockIdx.y, r0 = blockIdx.x * RB, dk = s.dk, dv = s.dv, ks = dk + 16;   // (row stride: see S0 k_i below)
+  float *Sl = sm;                     // [SR][SL] the state rows, row-major
+  float *Dl = Sl + SR * SL;           // [SR][DL] diag(d) U, transposed: [row][token]
+  float *Ol = Dl + SR * DL;           // [PT][OL] outputs of the pass (written out at the end)
+  const int h = blockIdx.x, r0 = blockIdx.y * SR;   // head h on XCD h % 8 (see the chunk terms)
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int nch = MK_PT / MK_CHUNK, nchunk = (s.T + MK_CHUNK - 1) / MK_CHUNK;
-  float *Sr = sm;                                  // [RB][dk]
-  float *Ks = Sr + RB * dk, *Qs = Ks + MK_CHUNK * ks;
-  float *Tm = Qs + MK_CHUNK * ks, *Mm = Tm + MK_CHUNK * CS;
-  float *SQ = Mm + MK_CHUNK * CS, *Bm = SQ + RB * CS, *U = Bm + RB * CS;
-  float *Vr = U + RB * CS;                         // [64][RB]: token-major, as stored
-  float *gs = Vr + MK_CHUNK * RB, *ds = gs + MK_CHUNK, *bs = ds + MK_CHUNK;
-  float *Sp = bs + MK_CHUNK;                       // [RB][dk] partial state update (second half of a chunk)
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  float *Sg = s.S + ((size_t)h * dv + r0) * dk;
-  g2l<4>(Sr, dk, Sg, dk, RB, dk, RB);
+  const bool isq = w >= 4, upd = w < DK / 16;
+  const int pt = w & 3;               // token block of the P tile
+  float *Sg = s.S + ((size_t)h * DK + r0) * DK;
+  for (int e = tid; e < SR * DK / 4; e += SCAN_THREADS) {
+    const int r = e / (DK / 4), c4 = e - r * (DK / 4);
+    *reinterpret_cast<float4 *>(Sl + r * SL + c4 * 4) = ld4(Sg + r * DK + c4 * 4);
+  }
   __syncthreads();
   // pending updates left by a verify forward (same arithmetic as the decode kernel's step)
   const int pend_n = s.ctl[MK_CTL_PEND], par = s.ctl[MK_CTL_PAR];
   for (int jp = 0; jp < pend_n; ++jp) {
-    const float *pk = s.pend + (((size_t)par * s.nh + h) * MK_MAXCOL + jp) * (dk + dv + 2);
-    const float a = pk[dk + dv], b = pk[dk + dv + 1];
-    for (int r = w; r < RB; r += PF_THREADS / 64) {
+    const float *pk = s.pend + (((size_t)par * s.nh + h) * MK_MAXCOL + jp) * (2 * DK + 2);
+    const float a = pk[2 * DK], b = pk[2 * DK + 1];
+    for (int r = w; r < SR; r += SCAN_THREADS / 64) {
       float p = 0.f;
-      for (int e = lane; e < dk; e += 64) p = fmaf(Sr[r * dk + e], pk[e], p);
+      for (int e = lane; e < DK; e += 64) p = fmaf(Sl[r * SL + e], pk[e], p);
       const float sk = wave_sum(p);
-      const float u = b * (pk[dk + r0 + r] - a * sk);
-      for (int e = lane; e < dk; e += 64) Sr[r * dk + e] = fmaf(u, pk[e], a * Sr[r * dk + e]);
+      const float u = b * (pk[DK + r0 + r] - a * sk);
+      for (int e = lane; e < DK; e += 64) Sl[r * SL + e] = fmaf(u, pk[e], a * Sl[r * SL + e]);
     }
   }
   __syncthreads();
-  const size_t hb = (size_t)h * MK_PT;
-  const int ti = tid & 63, rp = tid >> 6;          // token and state row of this thread (RB == 4)
-  // the next chunk's inputs, loaded into registers while the current chunk is computed
-  float4 pK[8], pQ[8], pT[4], pM[4], pV[1];
-  float pg = 0.f, pd = 0.f, pb = 0.f;
-  // per-thread element offsets of the chunk copies, the same for every chunk
-  int kq_row[8], kq_src[8], kq_dst[8];
+  // the state in the MFMA result layout: S[4 g + v][16 w + c16] (waves with a column block)
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  if (upd) {
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int e = b * PF_THREADS + tid, r = e / (dk / 4), c4 = e - r * (dk / 4);
-    kq_row[b] = e < MK_CHUNK * dk / 4 ? r : MK_CHUNK;     // MK_CHUNK: no such element
-    kq_src[b] = r * dk + c4 * 4;
-    kq_dst[b] = r * ks + c4 * 4;
+    for (int v = 0; v < 4; ++v) sc[v] = Sl[(4 * g + v) * SL + 16 * w + c16];
   }
-  auto fetch = [&](int c) {
-    const int t0 = c * MK_CHUNK, Cn = min(MK_CHUNK, s.T - t0);
-    const size_t cb = ((size_t)h * nch + c);
-    const float *kb = s.k + (hb + t0) * dk, *qb = s.q + (hb + t0) * dk;
+  // operands of one chunk, per lane: the P tile's B fragments (W or Q~ row 16 pt + c16), the K^T
+  // fragments of the column block (dim 16 w + c16), U' or O' (token 16 pt + c16, rows 4 g ..) and
+  // d of that token
+  struct Ops { float4 bp[DK / 16]; float4 bk[4]; float4 uo; float dd, gl; };
+  // Every wave issues the same loads for every chunk index (clamped to the last chunk), so the
+  // number of loads in flight never depends on the path taken and the compiler's waits stay exact
+  // (a load on one path only makes it wait for everything at the next join).
+  auto fetch = [&](Ops &op, int c) {
+    c = min(c, nchunk - 1);
+    const size_t cb = (size_t)h * nch + c, mo = cb * MK_CHUNK * DK;
+    const float *P = (isq ? s.cQ : s.cW) + mo + frag_tn<DK>(16 * pt + c16, 4 * g);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool ok = kq_row[b] < Cn;
-      pK[b] = ok ? ld4(kb + kq_src[b]) : make_float4(0.f, 0.f, 0.f, 0.f);
-      pQ[b] = ok ? ld4(qb + kq_src[b]) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int i = 0; i < DK / 16; ++i) op.bp[i] = ld4(P + 256 * i);
+    const float *K = s.cKt + mo + frag_kt(16 * min(w, DK / 16 - 1) + c16, 4 * g);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      pT[b] = ld4(s.cT + cb * MK_CHUNK * MK_CHUNK + (b * PF_THREADS + tid) * 4);
-      pM[b] = ld4(s.cM + cb * MK_CHUNK * MK_CHUNK + (b * PF_THREADS + tid) * 4);
-    }
-    pV[0] = (tid < Cn) ? ld4(s.v + (hb + t0 + tid) * dv + r0) : make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tid < MK_CHUNK) {
-      pg = s.cg[cb * MK_CHUNK + tid];
-      pd = s.cd[cb * MK_CHUNK + tid];
-      pb = tid < Cn ? s.be[hb + t0 + tid] : 0.f;
-    }
+    for (int i = 0; i < 4; ++i) op.bk[i] = ld4(K + 256 * i);
+    op.uo = ld4((isq ? s.cO : s.cU) + mo + frag_tn<DK>(16 * pt + c16, r0 + 4 * g));
+    op.dd = s.cd[cb * MK_CHUNK + 16 * pt + c16];
+    op.gl = s.cg[cb * MK_CHUNK + min(MK_CHUNK, s.T - c * MK_CHUNK) - 1];   // gamma of the chunk's last token
   };
-  fetch(0);
-  for (int c = 0; c < nchunk; ++c) {
+  // one chunk: operands in `cur`, while the operands of chunk c + 2 are loaded into `pre`.  A step
+  // past the last chunk (the loop runs in threes) leaves the state as it is: d = 0, gamma = 1.
+  auto step = [&](const Ops &cur, Ops &pre, int c) {
     const int t0 = c * MK_CHUNK, Cn = min(MK_CHUNK, s.T - t0);
+    const bool act = c < nchunk;
+    const float dd = act ? cur.dd : 0.f, gl = act ? cur.gl : 1.f;
+    fetch(pre, c + 2);
+    // P tile: rows 4 g + v, token 16 pt + c16
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+    {
+      const float *sr = Sl + c16 * SL + 4 * g;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      if (kq_row[b] < MK_CHUNK) {
-        *reinterpret_cast<float4 *>(Ks + kq_dst[b]) = pK[b];
-        *reinterpret_cast<float4 *>(Qs + kq_dst[b]) = pQ[b];
+      for (int i = 0; i < DK / 16; ++i) {
+        const float4 a = ld4(sr + 16 * i), b = cur.bp[i];
+        p = mfma4(a.x, b.x, p); p = mfma4(a.y, b.y, p); p = mfma4(a.z, b.z, p); p = mfma4(a.w, b.w, p);
       }
     }
+    const int tok = 16 * pt + c16;
+    if (!isq) {
+      Dl[(4 * g + 0) * DL + tok] = dd * (cur.uo.x - p[0]);
+      Dl[(4 * g + 1) * DL + tok] = dd * (cur.uo.y - p[1]);
+      Dl[(4 * g + 2) * DL + tok] = dd * (cur.uo.z - p[2]);
+      Dl[(4 * g + 3) * DL + tok] = dd * (cur.uo.w - p[3]);
+    } else if (tok < Cn) {
+      *reinterpret_cast<float4 *>(Ol + (t0 + tok) * OL + 4 * g) =
+          make_float4(p[0] + cur.uo.x, p[1] + cur.uo.y, p[2] + cur.uo.z, p[3] + cur.uo.w);
+    }
+    lds_barrier();
+    if (upd) {  // S <- gamma_last S + D K on the column block 16 w ..
+      f32x4 acc = {gl * sc[0], gl * sc[1], gl * sc[2], gl * sc[3]};
+      const float *dr = Dl + c16 * DL + 4 * g;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int e = b * PF_THREADS + tid, i = e / (MK_CHUNK / 4), j4 = e % (MK_CHUNK / 4);
-      *reinterpret_cast<float4 *>(Tm + i * CS + j4 * 4) = pT[b];
-      *reinterpret_cast<float4 *>(Mm + i * CS + j4 * 4) = pM[b];
-    }
-    if (tid < MK_CHUNK) *reinterpret_cast<float4 *>(Vr + tid * RB) = pV[0];
-    if (tid < MK_CHUNK) { gs[tid] = pg; ds[tid] = pd; bs[tid] = pb; }
-    __syncthreads();
-    if (c + 1 < nchunk) fetch(c + 1);
-    {  // S0 k_i and S0 q_i -> B and SQ.  Thread (token tq, dim quarter dq) takes the float4 groups
-       // dq, dq + 4, ... of its token's k and q against all RB rows of S, so each k / q element
-       // is read from LDS once; the quarters are summed over the four adjacent lanes.  With the
-       // row stride dk + 16, the 16 lanes of an LDS access (4 tokens x 4 quarters) hit distinct banks.
-      const int tq = tid >> 2, dq = tid & 3;
-      float a[RB], bq[RB];
+      for (int i = 0; i < 4; ++i) {
+        const float4 a = ld4(dr + 16 * i), b = cur.bk[i];
+        acc = mfma4(a.x, b.x, acc); acc = mfma4(a.y, b.y, acc); acc = mfma4(a.z, b.z, acc); acc = mfma4(a.w, b.w, acc);
+      }
+      sc = acc;
 #pragma unroll
-      for (int r = 0; r < RB; ++r) { a[r] = 0.f; bq[r] = 0.f; }
-#pragma unroll 4
-      for (int d = dq * 4; d < dk; d += 16) {
-        const float4 k4 = ld4(Ks + tq * ks + d), q4 = ld4(Qs + tq * ks + d);
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-          const float4 s0 = ld4(Sr + r * dk + d);
-          a[r] = dot4(s0, k4, a[r]);
-          bq[r] = dot4(s0, q4, bq[r]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        a[r] += dpp_mov<0xB1>(a[r]);  a[r] += dpp_mov<0x4E>(a[r]);
-        bq[r] += dpp_mov<0xB1>(bq[r]); bq[r] += dpp_mov<0x4E>(bq[r]);
-      }
-      // lane dq writes row dq (RB == 4)
-      const float ad = dq == 0 ? a[0] : dq == 1 ? a[1] : dq == 2 ? a[2] : a[3];
-      const float bd = dq == 0 ? bq[0] : dq == 1 ? bq[1] : dq == 2 ? bq[2] : bq[3];
-      Bm[dq * CS + tq] = bs[tq] * (Vr[tq * RB + dq] - gs[tq] * ad);
-      SQ[dq * CS + tq] = bd;
+      for (int v = 0; v < 4; ++v) Sl[(4 * g + v) * SL + 16 * w + c16] = sc[v];
     }
-    __syncthreads();
-    {  // U = (I + A)^-1 B  (the inverse is zero above the diagonal)
-      float u0 = 0.f;
-#pragma unroll 4
-      for (int j = 0; j <= ti; j += 4) u0 = dot4(ld4(Tm + ti * CS + j), ld4(Bm + rp * CS + j), u0);
-      U[rp * CS + ti] = u0;
-    }
-    __syncthreads();
-    if (ti < Cn) {  // outputs (the decay-weighted q.k matrix is zero above the diagonal)
-      float o0 = gs[ti] * SQ[rp * CS + ti];
-#pragma unroll 4
-      for (int j = 0; j <= ti; j += 4) o0 = dot4(ld4(Mm + ti * CS + j), ld4(U + rp * CS + j), o0);
-      s.o[(size_t)(t0 + ti) * s.nh * dv + h * dv + r0 + rp] = o0;
-    }
-    {  // end-of-chunk state: output e = (row, 4 columns); the two halves of the workgroup sum
-       // tokens [0, 32) and [32, Cn), the second half hands its partial over through LDS
-      const float gl = gs[Cn - 1];
-      const int nout = RB * (dk / 4), half = tid / nout, e = tid - half * nout;
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (half < 2) {
-        const int r = e / (dk / 4), d = (e % (dk / 4)) * 4;
-        const int j0 = half * (MK_CHUNK / 2), j1 = min(Cn, j0 + MK_CHUNK / 2);
-#pragma unroll 8
-        for (int j = j0; j < j1; ++j) {
-          const float cf = ds[j] * U[r * CS + j];
-          const float4 k4 = ld4(Ks + j * ks + d);
-          acc.x = fmaf(cf, k4.x, acc.x); acc.y = fmaf(cf, k4.y, acc.y);
-          acc.z = fmaf(cf, k4.z, acc.z); acc.w = fmaf(cf, k4.w, acc.w);
-        }
-        if (half == 1) *reinterpret_cast<float4 *>(Sp + e * 4) = acc;
-      }
-      __syncthreads();
-      if (half == 0) {
-        const int r = e / (dk / 4), d = (e % (dk / 4)) * 4;
-        const float4 p2 = ld4(Sp + e * 4);
-        acc.x += p2.x; acc.y += p2.y; acc.z += p2.z; acc.w += p2.w;
-        float4 *sp = reinterpret_cast<float4 *>(Sr + r * dk + d);
-        const float4 sv = *sp;
-        *sp = make_float4(fmaf(gl, sv.x, acc.x), fmaf(gl, sv.y, acc.y), fmaf(gl, sv.z, acc.z), fmaf(gl, sv.w, acc.w));
-      }
-    }
-    __syncthreads();
+    lds_barrier();
+  };
+  // three operand sets in rotation (no register copies, so that nothing waits on a load in
+  // flight before its chunk): each chunk's operands are loaded two chunks ahead
+  Ops o0, o1, o2;
+  fetch(o0, 0);
+  fetch(o1, 1);
+  // wait for the first two chunks' operands here: with loads still pending on the way into the
+  // loop, the compiler's waits at the loop head would also wait for the prefetch issued in it
+  wait_loads();
+  for (int c = 0; c < nchunk; c += 3) {
+    step(o0, o2, c);
+    step(o1, o0, c + 1);
+    step(o2, o1, c + 2);
   }
-  for (int i = tid; i < RB * dk / 4; i += PF_THREADS)
-    reinterpret_cast<float4 *>(Sg)[i] = reinterpret_cast<const float4 *>(Sr)[i];
+  for (int e = tid; e < s.T * (SR / 4); e += SCAN_THREADS) {   // the staged outputs, row by row
+    const int t = e / (SR / 4), q = e - t * (SR / 4);
+    *reinterpret_cast<float4 *>(s.o + (size_t)t * s.nh * DK + h * DK + r0 + 4 * q) = ld4(Ol + t * OL + 4 * q);
+  }
+  if (upd) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Sg[(size_t)(4 * g + v) * DK + 16 * w + c16] = sc[v];
+  }
 }
 
 // gated RMSNorm per (token, head): y = o / sqrt(mean(o^2) + eps) * g * SiLU(z), as bf16 hi + lo
@@ -1187,10 +1252,8 @@ static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStr
   return hipGetLastError();
 }
 
-static size_t chunk_prep_lds(int dk) { return (size_t)(2 * MK_CHUNK * (dk + 4) + 2 * MK_CHUNK * CS + 2 * MK_CHUNK) * 4; }
-static size_t scan_lds(int dk) {
-  return (size_t)(2 * RB * dk + 2 * MK_CHUNK * (dk + 16) + 2 * MK_CHUNK * CS + 3 * RB * CS + MK_CHUNK * RB + 3 * MK_CHUNK) * 4;
-}
+static size_t chunk_prep_lds(int dk) { return (size_t)(3 * MK_CHUNK * (dk + 4) + 3 * MK_CHUNK * CS + 4 * MK_CHUNK) * 4; }
+static size_t scan_lds(int dk) { return (size_t)(16 * (dk + 4) + 16 * (MK_CHUNK + 4) + MK_PT * 20) * 4; }
 
 // Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table.
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
@@ -1199,8 +1262,10 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e;
-    if ((e = hipFuncSetAttribute((const void *)pf_dn_chunk_prep, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess) return e;
-    if ((e = hipFuncSetAttribute((const void *)pf_dn_scan, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024)) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)pf_dn_chunk_prep<64>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)chunk_prep_lds(64))) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)pf_dn_chunk_prep<128>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)chunk_prep_lds(128))) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)pf_dn_scan<64>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_lds(64))) != hipSuccess) return e;
+    if ((e = hipFuncSetAttribute((const void *)pf_dn_scan<128>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_lds(128))) != hipSuccess) return e;
     attr_done = true;
   }
   const int H = d->H, nh = d->nh, dk = d->dk, dv = d->dv, nq = d->nq, nkv = d->nkv, hd = d->hd, J = d->J, I = d->I;
@@ -1232,10 +1297,16 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         hipLaunchKernelGGL(pf_dn_prep, dim3(T), dim3(PF_THREADS), (size_t)(d->C + 2 * nh) * 4, st, dn);
         hipLaunchKernelGGL(pf_dn_ring, dim3(T < MK_RING ? T : MK_RING), dim3(PF_THREADS), 0, st, dn);
         const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
-        PfChunk ck{pf->q, pf->k, pf->la, pf->be, pf->cT, pf->cM, pf->cg, pf->cd, T, dk};
-        hipLaunchKernelGGL(pf_dn_chunk_prep, dim3(nchunk, nh), dim3(PF_THREADS), chunk_prep_lds(dk), st, ck);
-        PfScan sc{L.S, L.pend, d->ctl, pf->q, pf->k, pf->v, pf->be, pf->cT, pf->cM, pf->cg, pf->cd, pf->o, T, nh, dk, dv};
-        hipLaunchKernelGGL(pf_dn_scan, dim3(dv / RB, nh), dim3(PF_THREADS), scan_lds(dk), st, sc);
+        // dk == dv in {64, 128} (checked when the model is loaded)
+        PfChunk ck{pf->q, pf->k, pf->v, pf->la, pf->be, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, T};
+        PfScan sc{L.S, L.pend, d->ctl, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, pf->o, T, nh};
+        if (dk == 128) {
+          hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk), dim3(PF_THREADS), chunk_prep_lds(128), st, ck);
+          hipLaunchKernelGGL(pf_dn_scan<128>, dim3(nh, 128 / 16), dim3(SCAN_THREADS), scan_lds(128), st, sc);
+        } else {
+          hipLaunchKernelGGL(pf_dn_chunk_prep<64>, dim3(nh, nchunk), dim3(PF_THREADS), chunk_prep_lds(64), st, ck);
+          hipLaunchKernelGGL(pf_dn_scan<64>, dim3(nh, 64 / 16), dim3(SCAN_THREADS), scan_lds(64), st, sc);
+        }
         hipLaunchKernelGGL(pf_dn_gnorm, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->o, (const float *)pf->z,
                            L.dn_gnorm, nh, dv, d->rms_eps, pf->a1h, pf->a1l, pf->K1);
         PfGemm go{};
