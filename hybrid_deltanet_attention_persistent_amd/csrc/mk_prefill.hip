@@ -99,22 +99,22 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 // multiples of 4 floats).  Rows >= nvalid read as zero.  Every thread of the workgroup calls it;
 // each issues NB 16-byte loads before storing any, so the loads overlap instead of each paying
 // the full memory latency.
-template <int NB>
+template <int NB, int NT = PF_THREADS>
 __device__ __forceinline__ void g2l(float *dst, int dstride, const float *src, size_t sstride, int rows, int cols,
                                     int nvalid) {
   const int c4 = cols >> 2, total = rows * c4;
-  for (int base = 0; base < total; base += NB * PF_THREADS) {
+  for (int base = 0; base < total; base += NB * NT) {
     float4 v[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int e = base + b * PF_THREADS + (int)threadIdx.x;
+      const int e = base + b * NT + (int)threadIdx.x;
       const int r = e / c4, c = e - r * c4;
       v[b] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (e < total && r < nvalid) v[b] = *reinterpret_cast<const float4 *>(src + (size_t)r * sstride + c * 4);
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int e = base + b * PF_THREADS + (int)threadIdx.x;
+      const int e = base + b * NT + (int)threadIdx.x;
       const int r = e / c4, c = e - r * c4;
       if (e < total) *reinterpret_cast<float4 *>(dst + r * dstride + c * 4) = v[b];
     }
@@ -122,23 +122,23 @@ __device__ __forceinline__ void g2l(float *dst, int dstride, const float *src, s
 }
 // The two halves of g2l for one batch of NB float4 per thread, so that a batch can be loaded
 // into registers well before it is stored (software prefetch).
-template <int NB>
+template <int NB, int NT = PF_THREADS>
 __device__ __forceinline__ void g2r(float4 (&v)[NB], const float *src, size_t sstride, int rows, int cols, int nvalid) {
   const int c4 = cols >> 2, total = rows * c4;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int e = b * PF_THREADS + (int)threadIdx.x;
+    const int e = b * NT + (int)threadIdx.x;
     const int r = e / c4, c = e - r * c4;
     v[b] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (e < total && r < nvalid) v[b] = *reinterpret_cast<const float4 *>(src + (size_t)r * sstride + c * 4);
   }
 }
-template <int NB>
+template <int NB, int NT = PF_THREADS>
 __device__ __forceinline__ void r2l(const float4 (&v)[NB], float *dst, int dstride, int rows, int cols) {
   const int c4 = cols >> 2, total = rows * c4;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int e = b * PF_THREADS + (int)threadIdx.x;
+    const int e = b * NT + (int)threadIdx.x;
     const int r = e / c4, c = e - r * c4;
     if (e < total) *reinterpret_cast<float4 *>(dst + r * dstride + c * 4) = v[b];
   }
@@ -534,8 +534,9 @@ __device__ __forceinline__ int frag_tn(int t, int n) {
 __device__ __forceinline__ int frag_kt(int d, int t) {
   return ((((d >> 4) * 4 + (t >> 4)) * 4 + ((t & 15) >> 2)) * 16 + (d & 15)) * 4 + (t & 3);
 }
+constexpr int CP_THREADS = 512, CP_WAVES = CP_THREADS / 64;
 template <int DK>
-__global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
+__global__ void __launch_bounds__(CP_THREADS) pf_dn_chunk_prep(PfChunk c) {
   extern __shared__ float sm[];
   constexpr int KS = DK + 4;                   // padded rows keep float4 reads conflict-free
   // workgroup (head h, chunk ch) runs on XCD h % 8, like the scan workgroups of head h, which
@@ -549,8 +550,12 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
   float *Gs = Mm + MK_CHUNK * CS, *bs = Gs + MK_CHUNK, *gam = bs + MK_CHUNK, *bgam = gam + MK_CHUNK;
   const size_t hb = (size_t)h * MK_PT;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  g2l<8>(Ks, KS, c.k + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
-  g2l<8>(Qs, KS, c.q + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
+  // V is loaded into registers now and stored to LDS after the inverse (its space holds scratch)
+  constexpr int NV = MK_CHUNK * DK / 4 / CP_THREADS;
+  float4 vr[NV];
+  g2r<NV, CP_THREADS>(vr, c.v + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
+  g2l<NV, CP_THREADS>(Ks, KS, c.k + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
+  g2l<NV, CP_THREADS>(Qs, KS, c.q + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
   if (tid < 64) {  // in-chunk prefix sums of log alpha (one wave, Hillis-Steele), beta, the decays
     float G = tid < Cn ? c.la[hb + t0 + tid] : 0.f;
 #pragma unroll
@@ -565,11 +570,14 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
     bgam[tid] = b * gam[tid];
   }
   __syncthreads();
-  {  // k_i.k_j and q_i.k_j on the 10 16 x 16 tiles with ti >= tj (FP32 MFMA; in the i-th group of
-     // four k steps lane group g takes the dims 16 i + 4 g ..); tiles above are never read
+  // the 10 16 x 16 tiles (ti, tj) with ti >= tj of a 64 x 64 lower triangular matrix
+  auto tile = [](int tt, int &ti, int &tj) { ti = tt < 1 ? 0 : tt < 3 ? 1 : tt < 6 ? 2 : 3; tj = tt - ti * (ti + 1) / 2; };
+  {  // k_i.k_j and q_i.k_j on the lower tiles (FP32 MFMA; in the i-th group of four k steps lane
+     // group g takes the dims 16 i + 4 g ..); tiles above are never read
 #pragma unroll 1
-    for (int tt = w; tt < 10; tt += 4) {
-      const int ti = tt < 1 ? 0 : tt < 3 ? 1 : tt < 6 ? 2 : 3, tj = tt - ti * (ti + 1) / 2;
+    for (int tt = w; tt < 10; tt += CP_WAVES) {
+      int ti, tj;
+      tile(tt, ti, tj);
       f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
       const float *ka = Ks + (16 * ti + c16) * KS + 4 * g, *qa = Qs + (16 * ti + c16) * KS + 4 * g;
       const float *kb = Ks + (16 * tj + c16) * KS + 4 * g;
@@ -595,14 +603,15 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
   // X = (I + A)^-1 (unit lower triangular), by blocks of 16: the four diagonal blocks
   // X_qq = (I + A_qq)^-1 by forward substitution, one wave each (lane c < 16 owns column c in
   // registers); then block row by block row X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj, each 16 x 16
-  // product spread over the workgroup.  Blocks above the diagonal are zero.
+  // product on 256 threads, the two halves of the workgroup taking alternate blocks j.
+  // Blocks above the diagonal are zero.
   {
     constexpr int NB = 16, NBK = MK_CHUNK / NB;
-    for (int e = tid; e < MK_CHUNK * MK_CHUNK; e += PF_THREADS) {
+    for (int e = tid; e < MK_CHUNK * MK_CHUNK; e += CP_THREADS) {
       const int i = e / MK_CHUNK, jx = e % MK_CHUNK;
       if (jx / NB > i / NB) X[i * CS + jx] = 0.f;
     }
-    if (lane < NB) {
+    if (w < NBK && lane < NB) {
       const int b0 = w * NB, jj = lane;
       float col[NB];
 #pragma unroll
@@ -618,12 +627,12 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
       for (int i = 0; i < NB; ++i) X[(b0 + i) * CS + b0 + jj] = col[i];
     }
     __syncthreads();
-    float *R = Vs;   // [NBK - 1][NB][NB + 1] partial sums of one block row (V is loaded afterwards)
+    float *R = Vs;   // [NBK - 1][NB][NB + 1] partial sums of one block row (V is stored afterwards)
     constexpr int RS = NB + 1;
-    const int ri = (tid / NB) % NB, rj = tid % NB;   // element of a 16 x 16 block (256 threads)
+    const int half = tid >> 8, ri = (tid >> 4) & 15, rj = tid & 15;   // element of a 16 x 16 block
     for (int bi = 1; bi < NBK; ++bi) {
       // R_bj = sum_{k=j}^{bi-1} A_{bi,k} X_{k,j} for every block j < bi
-      for (int bj = 0; bj < bi; ++bj) {
+      for (int bj = half; bj < bi; bj += 2) {
         float acc = 0.f;
         for (int bk = bj; bk < bi; ++bk)
 #pragma unroll
@@ -633,7 +642,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
       }
       __syncthreads();
       // X_{bi,j} = -X_{bi,bi} R_bj (X_bi,bi lower triangular)
-      for (int bj = 0; bj < bi; ++bj) {
+      for (int bj = half; bj < bi; bj += 2) {
         float acc = 0.f;
 #pragma unroll
         for (int t = 0; t < NB; ++t)
@@ -643,61 +652,63 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_chunk_prep(PfChunk c) {
       __syncthreads();
     }
   }
-  g2l<8>(Vs, KS, c.v + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
-  {  // M T into A (both lower triangular): wave w takes row block w, column blocks 0..w
+  r2l<NV, CP_THREADS>(vr, Vs, KS, MK_CHUNK, DK);
+  {  // M T into A (both lower triangular), by lower tiles: MT_{ti,tj} = sum_{kb=tj}^{ti} M_{ti,kb} T_{kb,tj}
 #pragma unroll 1
-    for (int nt = 0; nt <= w; ++nt) {
+    for (int tt = w; tt < 10; tt += CP_WAVES) {
+      int ti, tj;
+      tile(tt, ti, tj);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int kb = nt; kb <= w; ++kb)
+      for (int kb = tj; kb <= ti; ++kb)
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) {
           const int m = 16 * kb + 4 * k4 + g;
-          acc = mfma4(Mm[(16 * w + c16) * CS + m], X[m * CS + 16 * nt + c16], acc);
+          acc = mfma4(Mm[(16 * ti + c16) * CS + m], X[m * CS + 16 * tj + c16], acc);
         }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) A[(16 * w + 4 * g + v) * CS + 16 * nt + c16] = acc[v];
+      for (int v = 0; v < 4; ++v) A[(16 * ti + 4 * g + v) * CS + 16 * tj + c16] = acc[v];
     }
   }
   __syncthreads();
   const size_t cb = (size_t)h * nch + ch, mo = cb * MK_CHUNK * DK;
-  {  // W, U', Q~, O': wave w takes the 16-column blocks w, w + 4, ... of all four row blocks
-     // (the k range of row block rb ends at its diagonal)
-    for (int nt = w; nt < DK / 16; nt += 4) {
-      const int d = 16 * nt + c16;
+  {  // W, U', Q~, O' by 16 x 16 blocks (token block rb, column block nt), computed transposed
+     // (A operand from K or V, B operand from T or M T) so that each lane ends with four
+     // consecutive columns of one token: one 16-byte store in fragment order.  The k range of
+     // token block rb ends at its diagonal.
 #pragma unroll 1
-      for (int rb = 0; rb < 4; ++rb) {
-        f32x4 aw = {0.f, 0.f, 0.f, 0.f}, aq = aw, au = aw, ao = aw;
-        for (int kb = 0; kb <= rb; ++kb) {
-          float x[4], mt[4], bk[4], bv[4];
+    for (int u = w; u < (DK / 16) * 4; u += CP_WAVES) {
+      const int nt = u % (DK / 16), rb = u / (DK / 16), d = 16 * nt + c16;
+      f32x4 aw = {0.f, 0.f, 0.f, 0.f}, aq = aw, au = aw, ao = aw;
+      for (int kb = 0; kb <= rb; ++kb) {
+        float x[4], mt[4], bk[4], bv[4];
 #pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) {
-            const int j = 16 * kb + 4 * k4 + g;
-            x[k4] = X[(16 * rb + c16) * CS + j];
-            mt[k4] = A[(16 * rb + c16) * CS + j];
-            bk[k4] = Ks[j * KS + d] * bgam[j];
-            bv[k4] = Vs[j * KS + d] * bs[j];
-          }
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) {
-            aw = mfma4(x[k4], bk[k4], aw);
-            aq = mfma4(mt[k4], bk[k4], aq);
-            au = mfma4(x[k4], bv[k4], au);
-            ao = mfma4(mt[k4], bv[k4], ao);
-          }
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int j = 16 * kb + 4 * k4 + g;
+          x[k4] = X[(16 * rb + c16) * CS + j];
+          mt[k4] = A[(16 * rb + c16) * CS + j];
+          bk[k4] = Ks[j * KS + d] * bgam[j];
+          bv[k4] = Vs[j * KS + d] * bs[j];
         }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int i = 16 * rb + 4 * g + v;
-          const size_t o = mo + frag_tn<DK>(i, d);
-          c.cW[o] = aw[v];
-          c.cQ[o] = gam[i] * Qs[i * KS + d] - aq[v];
-          c.cU[o] = au[v];
-          c.cO[o] = ao[v];
+        for (int k4 = 0; k4 < 4; ++k4) {
+          aw = mfma4(bk[k4], x[k4], aw);
+          aq = mfma4(bk[k4], mt[k4], aq);
+          au = mfma4(bv[k4], x[k4], au);
+          ao = mfma4(bv[k4], mt[k4], ao);
         }
       }
+      // lane (g, c16), register v: token t = 16 rb + c16, column 16 nt + 4 g + v
+      const int t = 16 * rb + c16, n0 = 16 * nt + 4 * g;
+      const size_t o = mo + frag_tn<DK>(t, n0);
+      const float4 q4 = ld4(Qs + t * KS + n0);
+      const float gt = gam[t];
+      *reinterpret_cast<float4 *>(c.cW + o) = make_float4(aw[0], aw[1], aw[2], aw[3]);
+      *reinterpret_cast<float4 *>(c.cQ + o) = make_float4(gt * q4.x - aq[0], gt * q4.y - aq[1], gt * q4.z - aq[2], gt * q4.w - aq[3]);
+      *reinterpret_cast<float4 *>(c.cU + o) = make_float4(au[0], au[1], au[2], au[3]);
+      *reinterpret_cast<float4 *>(c.cO + o) = make_float4(ao[0], ao[1], ao[2], ao[3]);
     }
   }
-  for (int e = tid; e < DK * MK_CHUNK; e += PF_THREADS) {   // K^T in fragment order:
+  for (int e = tid; e < DK * MK_CHUNK; e += CP_THREADS) {   // K^T in fragment order:
     // e = (((db * 4 + tb) * 4 + tq) * 16 + dl) * 4 + te
     const int te = e & 3, dl = (e >> 2) & 15, tq = (e >> 6) & 3, tb = (e >> 8) & 3, db = e >> 10;
     const int d = 16 * db + dl, t = 16 * tb + 4 * tq + te;
@@ -1301,10 +1312,10 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         PfChunk ck{pf->q, pf->k, pf->v, pf->la, pf->be, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, T};
         PfScan sc{L.S, L.pend, d->ctl, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, pf->o, T, nh};
         if (dk == 128) {
-          hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk), dim3(PF_THREADS), chunk_prep_lds(128), st, ck);
+          hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(128), st, ck);
           hipLaunchKernelGGL(pf_dn_scan<128>, dim3(nh, 128 / 16), dim3(SCAN_THREADS), scan_lds(128), st, sc);
         } else {
-          hipLaunchKernelGGL(pf_dn_chunk_prep<64>, dim3(nh, nchunk), dim3(PF_THREADS), chunk_prep_lds(64), st, ck);
+          hipLaunchKernelGGL(pf_dn_chunk_prep<64>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(64), st, ck);
           hipLaunchKernelGGL(pf_dn_scan<64>, dim3(nh, 64 / 16), dim3(SCAN_THREADS), scan_lds(64), st, sc);
         }
         hipLaunchKernelGGL(pf_dn_gnorm, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->o, (const float *)pf->z,
