@@ -85,7 +85,7 @@ struct Plan {
   std::vector<LayerRegions> layers;
   // prefill scratch (one pass of MK_PT tokens)
   int K1, NP;
-  Region pf_X, pf_a1h, pf_a1l, pf_a2h, pf_a2l, pf_P, pf_q, pf_k, pf_v, pf_z, pf_la, pf_be, pf_cW, pf_cQ, pf_cU, pf_cO, pf_cKt, pf_cg, pf_cd,
+  Region pf_X, pf_a1h, pf_a1l, pf_a2h, pf_a2l, pf_P, pf_cW, pf_cQ, pf_cU, pf_cO, pf_cKt, pf_cg, pf_cd,
       pf_o, pf_aq, pf_lmbest, pf_part;
   size_t total;
 };
@@ -209,12 +209,6 @@ Plan make_plan(const mk_config *c) {
     p.pf_a2l = L.add(T * p.I * 2);
     p.pf_P = L.add(T * p.NP * 4);
     const size_t nhd = has_dn ? p.nh : 0;
-    p.pf_q = L.add(nhd * T * p.dk * 4);
-    p.pf_k = L.add(nhd * T * p.dk * 4);
-    p.pf_v = L.add(nhd * T * p.dv * 4);
-    p.pf_z = L.add(nhd * T * p.dv * 4);
-    p.pf_la = L.add(nhd * T * 4);
-    p.pf_be = L.add(nhd * T * 4);
     p.pf_cW = L.add(nhd * nch * MK_CHUNK * p.dk * 4);
     p.pf_cQ = L.add(nhd * nch * MK_CHUNK * p.dk * 4);
     p.pf_cU = L.add(nhd * nch * MK_CHUNK * p.dv * 4);
@@ -550,8 +544,6 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
     f.a1h = (uint16_t *)P(p.pf_a1h); f.a1l = (uint16_t *)P(p.pf_a1l);
     f.a2h = (uint16_t *)P(p.pf_a2h); f.a2l = (uint16_t *)P(p.pf_a2l);
     f.P = (float *)P(p.pf_P);
-    f.q = (float *)P(p.pf_q); f.k = (float *)P(p.pf_k); f.v = (float *)P(p.pf_v); f.z = (float *)P(p.pf_z);
-    f.la = (float *)P(p.pf_la); f.be = (float *)P(p.pf_be);
     f.cW = (float *)P(p.pf_cW); f.cQ = (float *)P(p.pf_cQ); f.cU = (float *)P(p.pf_cU); f.cO = (float *)P(p.pf_cO);
     f.cKt = (float *)P(p.pf_cKt); f.cg = (float *)P(p.pf_cg); f.cd = (float *)P(p.pf_cd);
     f.o = (float *)P(p.pf_o); f.aq = (float *)P(p.pf_aq);

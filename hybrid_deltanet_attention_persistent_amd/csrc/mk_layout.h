@@ -127,9 +127,6 @@ struct MkPf {
   uint16_t *a1h, *a1l;                // [PT][K1] GEMM operand as bf16 hi + lo, K1 = max(H, nh dv, nq hd)
   uint16_t *a2h, *a2l;                // [PT][I]  SwiGLU activations as bf16 hi + lo
   float *P;                           // [PT][NP] projection outputs, NP = max(nh r_in, (nq + 2 nkv) hd)
-  float *q, *k, *v;                   // [nh][PT][dk|dv] conv + SiLU (+ L2 norm for q, k), head-major
-  float *z;                           // [PT][nh dv] output-gate inputs
-  float *la, *be;                     // [nh][PT] log alpha, beta
   float *cW, *cQ, *cU, *cO;           // [nh][PT/CHUNK][CHUNK][dk|dv] chunk terms W, Q~, U', O' of the delta rule
   float *cKt;                         // [nh][PT/CHUNK][dk][CHUNK] the chunk's keys, transposed
   float *cg, *cd;                     // [nh][PT/CHUNK][CHUNK] exp(G_i), exp(G_last - G_i)

@@ -6,10 +6,11 @@
 // Throughput on RTX 3090", section "We wrote a single CUDA kernel ...": prefill turns the
 // projections into dense products over all prompt rows):
 //
-//   RMSNorm -> MFMA GEMM (in-projection / QKV) -> conv + SiLU + L2 norm + gates ->
-//   chunked delta rule (chunk precompute in parallel, then one sequential scan over the
-//   chunks per state row block) -> gated RMSNorm -> MFMA GEMM (out-projection, + residual) ->
-//   RMSNorm -> MFMA GEMM (gate/up, SwiGLU epilogue) -> MFMA GEMM (down, + residual)
+//   RMSNorm -> MFMA GEMM (in-projection / QKV) -> chunked delta rule (per chunk and head in
+//   parallel: conv + SiLU + L2 norm + gates and every term that does not depend on the state;
+//   then one sequential scan over the chunks per block of state rows) -> gated RMSNorm ->
+//   MFMA GEMM (out-projection, + residual) -> RMSNorm -> MFMA GEMM (gate/up, SwiGLU epilogue)
+//   -> MFMA GEMM (down, + residual)
 //
 // and for attention layers RoPE + KV append and causal attention over the cache.
 //
@@ -18,7 +19,8 @@
 // both multiplied by the exact bf16 weight and accumulated in FP32: the operand keeps 16
 // significant bits (relative error below 2^-17).  Attention multiplies on the matrix cores the
 // same way (Q and the softmax weights as hi + lo, K and V exactly bf16), softmax in FP32.  The
-// delta rule, conv and norms run in FP32 on the vector ALUs.
+// delta rule runs in full FP32: its products on the FP32 matrix cores (v_mfma_f32_16x16x4f32),
+// conv and norms on the vector ALUs.
 //
 // The chunked delta rule follows from unrolling the recurrence S_i = alpha_i S_{i-1} +
 // u_i k_i^T, u_i = beta_i (v_i - alpha_i S_{i-1} k_i) over a chunk that starts from S0.  With
@@ -26,8 +28,9 @@
 //   (I + A) U = B,  A_ij = beta_i exp(G_i - G_j) k_i.k_j (j < i),  B_i = beta_i (v_i - gamma_i S0 k_i)
 //   o_i = gamma_i S0 q_i + sum_{j <= i} exp(G_i - G_j) (k_j.q_i) u_j
 //   S_end = gamma_last S0 + sum_j exp(G_last - G_j) u_j k_j^T
-// Everything but S0 is computed for all chunks in parallel; the scan carries S0 through the
-// chunks, one block of state rows per workgroup (rows of S evolve independently).
+// Everything but S0 is computed for all chunks in parallel, arranged so that S0 enters only
+// through products with it (see pf_dn_chunk_prep); the scan carries S0 through the chunks, one
+// block of 16 state rows per workgroup (rows of S evolve independently).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include "mk_layout.h"
@@ -60,6 +63,8 @@ __device__ __forceinline__ float sigmoidf_(float x) {
   return e / (1.f + e);
 }
 __device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
+// SiLU with the hardware exponential and reciprocal (a few ulp): x / (1 + e^-x)
+__device__ __forceinline__ float silu_fast(float x) { return __fdividef(x, 1.f + __expf(-x)); }
 __device__ __forceinline__ float softplusf_(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
 
 // Max / sum over each 16-lane row with DPP (xor 1, xor 2, half-row mirror, row mirror): every lane
@@ -397,8 +402,6 @@ struct PfDn {
   float *ring;           // [MK_RING][C] pre-conv inputs by position
   const int32_t *ctl;
   int nh, dk, dv, r_in, C;
-  float l2_eps;
-  float *q, *k, *v, *z, *la, *be;
 };
 
 // source column in P of conv channel ch (q channels, then k, then v)
@@ -408,85 +411,6 @@ __device__ __forceinline__ int dn_col(const PfDn &d, int ch) {
   if (ch < 2 * nqk) return ((ch - nqk) / d.dk) * d.r_in + d.dk + ((ch - nqk) % d.dk);
   const int c2 = ch - 2 * nqk;
   return (c2 / d.dv) * d.r_in + 2 * d.dk + (c2 % d.dv);
-}
-
-// causal conv (taps over positions p-3..p) + SiLU, L2 norms of q and k per head, gates
-__global__ void __launch_bounds__(PF_THREADS) pf_dn_prep(PfDn d) {
-  extern __shared__ float buf[];  // [C] conv outputs, then [2 nh] norms
-  const int t = blockIdx.x;
-  const int p0 = d.ctl[MK_CTL_POS];
-  {  // every thread handles up to CPT channels; all their loads of one tap are issued together
-    constexpr int CPT = 12;   // C <= 3072
-    int col[CPT];
-    float4 wt[CPT];
-    float acc[CPT];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int ch = threadIdx.x + j * PF_THREADS;
-      col[j] = ch < d.C ? dn_col(d, ch) : 0;
-      wt[j] = ch < d.C ? *reinterpret_cast<const float4 *>(d.conv + ch * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      acc[j] = 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = t - 3 + i;     // tap i meets the token 3 - i steps before
-      float x[CPT];
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const int ch = threadIdx.x + j * PF_THREADS;
-        x[j] = 0.f;
-        if (ch < d.C) {
-          if (tt >= 0) x[j] = d.P[(size_t)tt * d.NP + col[j]];
-          else if (p0 + tt >= 0) x[j] = d.ring[((p0 + tt) & (MK_RING - 1)) * d.C + ch];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const float wi = i == 0 ? wt[j].x : i == 1 ? wt[j].y : i == 2 ? wt[j].z : wt[j].w;
-        acc[j] = fmaf(wi, x[j], acc[j]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int ch = threadIdx.x + j * PF_THREADS;
-      if (ch < d.C) buf[ch] = siluf_(acc[j]);
-    }
-  }
-  __syncthreads();
-  float *nrm = buf + d.C;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int r = w; r < 2 * d.nh; r += PF_THREADS / 64) {  // r = 2 head + (0: q, 1: k)
-    const float *p = buf + (r & 1) * d.nh * d.dk + (r >> 1) * d.dk;
-    float sq = 0.f;
-    for (int i = lane; i < d.dk; i += 64) sq = fmaf(p[i], p[i], sq);
-    sq = wave_sum(sq);
-    if (lane == 0) nrm[r] = sqrtf(sq + d.l2_eps);
-  }
-  __syncthreads();
-  const int nqk = d.nh * d.dk;
-  for (int ch = threadIdx.x; ch < d.C; ch += PF_THREADS) {
-    if (ch < nqk) {
-      const int h = ch / d.dk, i = ch % d.dk;
-      d.q[((size_t)h * MK_PT + t) * d.dk + i] = buf[ch] / nrm[2 * h];
-    } else if (ch < 2 * nqk) {
-      const int h = (ch - nqk) / d.dk, i = (ch - nqk) % d.dk;
-      d.k[((size_t)h * MK_PT + t) * d.dk + i] = buf[ch] / nrm[2 * h + 1];
-    } else {
-      const int h = (ch - 2 * nqk) / d.dv, i = (ch - 2 * nqk) % d.dv;
-      d.v[((size_t)h * MK_PT + t) * d.dv + i] = buf[ch];
-    }
-  }
-  for (int i = threadIdx.x; i < d.nh * d.dv; i += PF_THREADS) {
-    const int h = i / d.dv, e = i % d.dv;
-    d.z[(size_t)t * d.nh * d.dv + i] = d.P[(size_t)t * d.NP + h * d.r_in + 2 * d.dk + d.dv + e];
-  }
-  if (threadIdx.x < d.nh) {
-    const int h = threadIdx.x;
-    const float a = d.P[(size_t)t * d.NP + h * d.r_in + 2 * d.dk + 2 * d.dv];
-    const float b = d.P[(size_t)t * d.NP + h * d.r_in + 2 * d.dk + 2 * d.dv + 1];
-    d.la[(size_t)h * MK_PT + t] = -softplusf_(a);   // log alpha, alpha = exp(-softplus(a))
-    d.be[(size_t)h * MK_PT + t] = sigmoidf_(b);
-  }
 }
 
 // keep the pre-conv inputs of the last positions for the decode kernel's conv
@@ -506,7 +430,12 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 }
 
 struct PfChunk {
-  const float *q, *k, *v, *la, *be;   // head-major [nh][PT][dk|dv], [nh][PT]
+  const float *P;                     // [T][NP] in-projection outputs; per head x: [q | k | v | z | a | b]
+  int NP, r_in, C, nh;                // C: conv channels (q of all heads, then k, then v)
+  const float *conv;                  // [C][4] taps
+  const float *ring;                  // [MK_RING][C] pre-conv inputs of earlier positions
+  const int32_t *ctl;
+  float l2_eps;
   float *cW, *cQ, *cU, *cO, *cKt;     // per (head, chunk), CHUNK x dk each, in the fragment orders below
   float *cg, *cd;                     // [nh][PT/CHUNK][CHUNK] exp(G_i), exp(G_last - G_i)
   int T;
@@ -547,27 +476,77 @@ __global__ void __launch_bounds__(CP_THREADS) pf_dn_chunk_prep(PfChunk c) {
   float *A = Vs + MK_CHUNK * KS;               // [64][CS] A (transposed), later M T
   float *X = A + MK_CHUNK * CS;                // [64][CS] (I + A)^-1
   float *Mm = X + MK_CHUNK * CS;               // [64][CS] M
-  float *Gs = Mm + MK_CHUNK * CS, *bs = Gs + MK_CHUNK, *gam = bs + MK_CHUNK, *bgam = gam + MK_CHUNK;
-  const size_t hb = (size_t)h * MK_PT;
+  float *R = Mm + MK_CHUNK * CS;               // [3][16][17] partial sums of the inverse
+  float *Gs = R + 3 * 16 * 17, *bs = Gs + MK_CHUNK, *gam = bs + MK_CHUNK, *bgam = gam + MK_CHUNK;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  // V is loaded into registers now and stored to LDS after the inverse (its space holds scratch)
-  constexpr int NV = MK_CHUNK * DK / 4 / CP_THREADS;
-  float4 vr[NV];
-  g2r<NV, CP_THREADS>(vr, c.v + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
-  g2l<NV, CP_THREADS>(Ks, KS, c.k + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
-  g2l<NV, CP_THREADS>(Qs, KS, c.q + (hb + t0) * DK, DK, MK_CHUNK, DK, Cn);
-  if (tid < 64) {  // in-chunk prefix sums of log alpha (one wave, Hillis-Steele), beta, the decays
-    float G = tid < Cn ? c.la[hb + t0 + tid] : 0.f;
+  const int p0 = c.ctl[MK_CTL_POS];
+  {  // causal conv (taps over positions p-3 .. p) + SiLU of the head's q, k, v channels, straight
+     // into Ks, Qs, Vs: thread -> one channel pair and a run of tokens; all its inputs are loaded
+     // before any is used (earlier positions of the sequence come from the ring)
+    constexpr int NPAIR = 3 * DK / 2, NGRP = CP_THREADS / NPAIR, TPG = (MK_CHUNK + NGRP - 1) / NGRP;
+    const int cp = tid % NPAIR, grp = tid / NPAIR;
+    if (grp < NGRP) {
+      const int seg = cp / (DK / 2), i = (cp % (DK / 2)) * 2;   // seg 0: q, 1: k, 2: v
+      const int col = h * c.r_in + seg * DK + i, ch = seg * c.nh * DK + h * DK + i;
+      const float4 w0 = ld4(c.conv + ch * 4), w1 = ld4(c.conv + ch * 4 + 4);
+      const int j0 = grp * TPG;
+      float2 xs[TPG + 3];
+#pragma unroll
+      for (int u = 0; u < TPG + 3; ++u) {   // branch-free: every load issued, invalid ones zeroed
+        const int tt = t0 + j0 + u - 3;       // pass token
+        const bool ok = tt >= 0 ? tt < c.T : p0 + tt >= 0;
+        const float *src = tt >= 0 ? c.P + (size_t)min(tt, c.T - 1) * c.NP + col
+                                   : c.ring + ((p0 + tt) & (MK_RING - 1)) * c.C + ch;
+        const float2 x = *reinterpret_cast<const float2 *>(src);
+        xs[u] = ok ? x : make_float2(0.f, 0.f);
+      }
+      float *dst = (seg == 0 ? Qs : seg == 1 ? Ks : Vs) + i;
+#pragma unroll
+      for (int u = 0; u < TPG; ++u) {
+        const int j = j0 + u;
+        if (j < MK_CHUNK) {
+          float a0 = fmaf(w0.x, xs[u].x, 0.f), a1 = fmaf(w1.x, xs[u].y, 0.f);
+          a0 = fmaf(w0.y, xs[u + 1].x, a0); a1 = fmaf(w1.y, xs[u + 1].y, a1);
+          a0 = fmaf(w0.z, xs[u + 2].x, a0); a1 = fmaf(w1.z, xs[u + 2].y, a1);
+          a0 = fmaf(w0.w, xs[u + 3].x, a0); a1 = fmaf(w1.w, xs[u + 3].y, a1);
+          *reinterpret_cast<float2 *>(dst + j * KS) = j < Cn ? make_float2(silu_fast(a0), silu_fast(a1)) : make_float2(0.f, 0.f);
+        }
+      }
+    }
+  }
+  if (tid < 64) {  // gates, in-chunk prefix sums of log alpha (one wave, Hillis-Steele), the decays
+    const float *pa = c.P + (size_t)(t0 + tid) * c.NP + h * c.r_in + 4 * DK;   // a, b
+    const bool ok = tid < Cn;
+    float G = ok ? -softplusf_(pa[0]) : 0.f;   // log alpha, alpha = exp(-softplus(a))
+    const float b = ok ? sigmoidf_(pa[1]) : 0.f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_up(G, o, 64);
       if (tid >= o) G += y;
     }
-    const float b = tid < Cn ? c.be[hb + t0 + tid] : 0.f;
     Gs[tid] = G;
     bs[tid] = b;
-    gam[tid] = tid < Cn ? expf(G) : 0.f;
+    gam[tid] = ok ? expf(G) : 0.f;
     bgam[tid] = b * gam[tid];
+  }
+  __syncthreads();
+  {  // L2 norms of the q and k rows, four threads per row (rows past the chunk's end stay zero)
+    const int r = tid >> 2, part = tid & 3;
+    float *row = (r < MK_CHUNK ? Qs + r * KS : Ks + (r - MK_CHUNK) * KS) + part * (DK / 4);
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < DK / 4; e += 4) {
+      const float4 v = ld4(row + e);
+      sq = fmaf(v.x, v.x, sq); sq = fmaf(v.y, v.y, sq); sq = fmaf(v.z, v.z, sq); sq = fmaf(v.w, v.w, sq);
+    }
+    sq += dpp_mov<0xB1>(sq);
+    sq += dpp_mov<0x4E>(sq);
+    const float nrm = sqrtf(sq + c.l2_eps);
+#pragma unroll
+    for (int e = 0; e < DK / 4; e += 4) {
+      const float4 v = ld4(row + e);
+      *reinterpret_cast<float4 *>(row + e) = make_float4(v.x / nrm, v.y / nrm, v.z / nrm, v.w / nrm);
+    }
   }
   __syncthreads();
   // the 10 16 x 16 tiles (ti, tj) with ti >= tj of a 64 x 64 lower triangular matrix
@@ -627,8 +606,7 @@ __global__ void __launch_bounds__(CP_THREADS) pf_dn_chunk_prep(PfChunk c) {
       for (int i = 0; i < NB; ++i) X[(b0 + i) * CS + b0 + jj] = col[i];
     }
     __syncthreads();
-    float *R = Vs;   // [NBK - 1][NB][NB + 1] partial sums of one block row (V is stored afterwards)
-    constexpr int RS = NB + 1;
+    constexpr int RS = NB + 1;   // R: [NBK - 1][NB][RS] partial sums of one block row
     const int half = tid >> 8, ri = (tid >> 4) & 15, rj = tid & 15;   // element of a 16 x 16 block
     for (int bi = 1; bi < NBK; ++bi) {
       // R_bj = sum_{k=j}^{bi-1} A_{bi,k} X_{k,j} for every block j < bi
@@ -652,7 +630,6 @@ __global__ void __launch_bounds__(CP_THREADS) pf_dn_chunk_prep(PfChunk c) {
       __syncthreads();
     }
   }
-  r2l<NV, CP_THREADS>(vr, Vs, KS, MK_CHUNK, DK);
   {  // M T into A (both lower triangular), by lower tiles: MT_{ti,tj} = sum_{kb=tj}^{ti} M_{ti,kb} T_{kb,tj}
 #pragma unroll 1
     for (int tt = w; tt < 10; tt += CP_WAVES) {
@@ -866,12 +843,13 @@ __global__ void __launch_bounds__(SCAN_THREADS) pf_dn_scan(PfScan s) {
 }
 
 // gated RMSNorm per (token, head): y = o / sqrt(mean(o^2) + eps) * g * SiLU(z), as bf16 hi + lo
-__global__ void __launch_bounds__(PF_THREADS) pf_dn_gnorm(const float *o, const float *z, const float *gn, int nh, int dv,
-                                                          float eps, uint16_t *oh, uint16_t *ol, int ld) {
+// (z of head h, token t: Pz[t NP + h r_in + i], straight from the in-projection outputs)
+__global__ void __launch_bounds__(PF_THREADS) pf_dn_gnorm(const float *o, const float *Pz, int NP, int r_in, const float *gn,
+                                                          int nh, int dv, float eps, uint16_t *oh, uint16_t *ol, int ld) {
   const int t = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int h = w; h < nh; h += PF_THREADS / 64) {
     const float *oo = o + (size_t)t * nh * dv + h * dv;
-    const float *zz = z + (size_t)t * nh * dv + h * dv;
+    const float *zz = Pz + (size_t)t * NP + h * r_in;
     float sq = 0.f;
     for (int i = lane; i < dv; i += 64) sq = fmaf(oo[i], oo[i], sq);
     const float den = sqrtf(wave_sum(sq) / (float)dv + eps);
@@ -1263,7 +1241,7 @@ static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStr
   return hipGetLastError();
 }
 
-static size_t chunk_prep_lds(int dk) { return (size_t)(3 * MK_CHUNK * (dk + 4) + 3 * MK_CHUNK * CS + 4 * MK_CHUNK) * 4; }
+static size_t chunk_prep_lds(int dk) { return (size_t)(3 * MK_CHUNK * (dk + 4) + 3 * MK_CHUNK * CS + 3 * 16 * 17 + 4 * MK_CHUNK) * 4; }
 static size_t scan_lds(int dk) { return (size_t)(16 * (dk + 4) + 16 * (MK_CHUNK + 4) + MK_PT * 20) * 4; }
 
 // Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table.
@@ -1301,25 +1279,27 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         g.c = pf->P; g.ldc = pf->NP;
         hipError_t e = launch_gemm(EPI_STORE, false, g, nullptr, st);
         if (e != hipSuccess) return e;
-        PfDn dn{};
-        dn.P = pf->P; dn.NP = pf->NP; dn.T = T; dn.conv = L.dn_conv; dn.ring = L.ring; dn.ctl = d->ctl;
-        dn.nh = nh; dn.dk = dk; dn.dv = dv; dn.r_in = d->r_in; dn.C = d->C; dn.l2_eps = d->l2_eps;
-        dn.q = pf->q; dn.k = pf->k; dn.v = pf->v; dn.z = pf->z; dn.la = pf->la; dn.be = pf->be;
-        hipLaunchKernelGGL(pf_dn_prep, dim3(T), dim3(PF_THREADS), (size_t)(d->C + 2 * nh) * 4, st, dn);
-        hipLaunchKernelGGL(pf_dn_ring, dim3(T < MK_RING ? T : MK_RING), dim3(PF_THREADS), 0, st, dn);
         const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
-        // dk == dv in {64, 128} (checked when the model is loaded)
-        PfChunk ck{pf->q, pf->k, pf->v, pf->la, pf->be, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, T};
+        // dk == dv in {64, 128} (checked when the model is loaded).  The chunk terms read the ring
+        // (conv inputs of earlier positions) before pf_dn_ring overwrites it with this pass's last ones.
+        PfChunk ck{pf->P, pf->NP, d->r_in, d->C, nh, L.dn_conv, L.ring, d->ctl, d->l2_eps,
+                   pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, T};
         PfScan sc{L.S, L.pend, d->ctl, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, pf->o, T, nh};
-        if (dk == 128) {
+        if (dk == 128)
           hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(128), st, ck);
-          hipLaunchKernelGGL(pf_dn_scan<128>, dim3(nh, 128 / 16), dim3(SCAN_THREADS), scan_lds(128), st, sc);
-        } else {
+        else
           hipLaunchKernelGGL(pf_dn_chunk_prep<64>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(64), st, ck);
+        PfDn dn{};
+        dn.P = pf->P; dn.NP = pf->NP; dn.T = T; dn.ring = L.ring; dn.ctl = d->ctl;
+        dn.nh = nh; dn.dk = dk; dn.dv = dv; dn.r_in = d->r_in; dn.C = d->C;
+        hipLaunchKernelGGL(pf_dn_ring, dim3(T < MK_RING ? T : MK_RING), dim3(PF_THREADS), 0, st, dn);
+        if (dk == 128)
+          hipLaunchKernelGGL(pf_dn_scan<128>, dim3(nh, 128 / 16), dim3(SCAN_THREADS), scan_lds(128), st, sc);
+        else
           hipLaunchKernelGGL(pf_dn_scan<64>, dim3(nh, 64 / 16), dim3(SCAN_THREADS), scan_lds(64), st, sc);
-        }
-        hipLaunchKernelGGL(pf_dn_gnorm, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->o, (const float *)pf->z,
-                           L.dn_gnorm, nh, dv, d->rms_eps, pf->a1h, pf->a1l, pf->K1);
+        hipLaunchKernelGGL(pf_dn_gnorm, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->o,
+                           (const float *)pf->P + 2 * dk + dv, pf->NP, d->r_in, L.dn_gnorm, nh, dv, d->rms_eps,
+                           pf->a1h, pf->a1l, pf->K1);
         PfGemm go{};
         go.ah = pf->a1h; go.al = pf->a1l; go.lda = pf->K1; go.M = T; go.N = H; go.K = nh * dv;
         go.wb[0] = go.wb[1] = go.wb[2] = L.dn_out; go.wend[0] = go.wend[1] = go.wend[2] = H;
