@@ -217,7 +217,7 @@ __device__ __forceinline__ int tileG(int K) {
   return g;
 }
 
-// Workgroup tile BM x BN (BM = WGM*MT*16, BN = WGN*NT*16, WGM*WGN = 4 waves), K in stages of 64.
+// Workgroup tile BM x BN (BM = WGM*MT*16, BN = WGN*NT*16, WGM*WGN waves), K in stages of 64.
 // Each stage of A (hi and lo) and W is copied into LDS once per workgroup (16-byte loads: 128
 // contiguous bytes per row), double-buffered: the next stage's loads are in flight while the
 // MFMAs of the current one run.  LDS rows are padded to 80 elements (10 units of 16 bytes): a
@@ -227,9 +227,9 @@ __device__ __forceinline__ int tileG(int K) {
 constexpr int GBK = 64, GLD = GBK + 16;
 
 template <int EPI, int MT, int NT, int WGM, int WGN>
-__global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
-  constexpr int BM = WGM * MT * 16, BN = WGN * NT * 16;
-  constexpr int NA = 2 * BM * 8 / PF_THREADS, NB = BN * 8 / PF_THREADS;   // 16-byte loads per thread and stage
+__global__ void __launch_bounds__(WGM * WGN * 64) pf_gemm(PfGemm g) {
+  constexpr int BM = WGM * MT * 16, BN = WGN * NT * 16, NTHR = WGM * WGN * 64;
+  constexpr int NA = 2 * BM * 8 / NTHR, NB = BN * 8 / NTHR;   // 16-byte loads per thread and stage
   extern __shared__ uint16_t gsm[];
   // stage buffer b: A at gsm + b * 2 BM GLD ([hi/lo][BM][GLD]), W at gsm + 4 BM GLD + b * BN GLD
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -241,7 +241,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
   int aoff[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int c = tid + i * PF_THREADS, hl = c / (BM * 8), rem = c % (BM * 8), row = rem / 8, kg = rem % 8;
+    const int c = tid + i * NTHR, hl = c / (BM * 8), rem = c % (BM * 8), row = rem / 8, kg = rem % 8;
     asrc[i] = (hl ? g.al : g.ah) + (size_t)(bm0 + row) * g.lda + kg * 8;
     aoff[i] = (hl * BM + row) * GLD + kg * 8;
   }
@@ -249,7 +249,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_gemm(PfGemm g) {
   int brow[NB], bkg[NB], boff[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int c = tid + i * PF_THREADS, row = c / 8, kg = c % 8;
+    const int c = tid + i * NTHR, row = c / 8, kg = c % 8;
     const int n = min(bn0 + row, g.N - 1);
     const int s = n < g.wend[0] ? 0 : (n < g.wend[1] ? 1 : 2);
     const int r = n - (s == 0 ? 0 : g.wend[s - 1]);
@@ -1190,7 +1190,6 @@ struct MkPfHost {
   MkPf pf;
 };
 
-// wide projections: 64 x 256 workgroup tiles (4 waves of 64 x 64); 1024-wide outputs: 64 x 64
 template <int EPI, int MT, int NT, int WGM, int WGN>
 static hipError_t launch_gemm_t(const PfGemm &g, int nsplit, hipStream_t st) {
   constexpr int BM = WGM * MT * 16, BN = WGN * NT * 16;
@@ -1202,10 +1201,11 @@ static hipError_t launch_gemm_t(const PfGemm &g, int nsplit, hipStream_t st) {
     attr = true;
   }
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, nsplit);
-  hipLaunchKernelGGL((pf_gemm<EPI, MT, NT, WGM, WGN>), grid, dim3(PF_THREADS), lds, st, g);
+  hipLaunchKernelGGL((pf_gemm<EPI, MT, NT, WGM, WGN>), grid, dim3(WGM * WGN * 64), lds, st, g);
   return hipGetLastError();
 }
-// Wide projections: 64 x 128 workgroup tiles (4 waves of 64 x 32, two workgroups per CU).  The
+// Wide projections: 64 x 128 workgroup tiles (8 waves of 32 x 32, two workgroups per CU: 16
+// waves hide the LDS and memory latency better than 8 waves of 64 x 32 did).  The
 // 1024-wide outputs that add into the residual stream: the same tiles with split-K (partials
 // reduced in split order), so that the grid fills the chip and each K stream is short.
 // The RMSNorm that follows a projection adding into the residual stream, fused into the split-K
@@ -1219,8 +1219,8 @@ struct PfNext {
 static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStream_t st, const PfNext *next = nullptr) {
   if (g.K % GBK != 0) return hipErrorInvalidValue;
   g.kper = g.K;
-  if (epi == EPI_STORE) return small ? launch_gemm_t<EPI_STORE, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_STORE, 4, 2, 1, 4>(g, 1, st);
-  if (epi == EPI_SWIGLU) return small ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_SWIGLU, 4, 2, 1, 4>(g, 1, st);
+  if (epi == EPI_STORE) return small ? launch_gemm_t<EPI_STORE, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_STORE, 2, 2, 2, 4>(g, 1, st);
+  if (epi == EPI_SWIGLU) return small ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 4>(g, 1, st);
   const int ns = g.K / GBK;
   const int nsplit = (ns % 4 == 0 && ns >= 8) ? 4 : (ns % 2 == 0 && ns >= 4) ? 2 : 1;
   if (nsplit == 1 || !part || g.N > 4 * PF_THREADS || g.N % 4 != 0) {
@@ -1233,7 +1233,7 @@ static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStr
   g.kper = g.K / nsplit;
   g.part = part;
   g.part_stride = (size_t)MK_PT * g.ldc;
-  hipError_t e = small ? launch_gemm_t<EPI_PART, 4, 2, 1, 4>(g, nsplit, st) : launch_gemm_t<EPI_PART, 4, 4, 1, 4>(g, nsplit, st);
+  hipError_t e = small ? launch_gemm_t<EPI_PART, 2, 2, 2, 4>(g, nsplit, st) : launch_gemm_t<EPI_PART, 4, 4, 1, 4>(g, nsplit, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pf_reduce_norm, dim3(g.M), dim3(PF_THREADS), 0, st, g.c, (const float *)part, nsplit, g.part_stride,
                      g.N, next ? next->g : (const float *)nullptr, next ? next->eps : 0.f,
