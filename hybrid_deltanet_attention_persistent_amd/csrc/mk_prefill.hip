@@ -57,6 +57,13 @@ __device__ __forceinline__ void split_store(float v, uint16_t *hi, uint16_t *lo)
   *hi = (uint16_t)h;
   *lo = (uint16_t)f2bf(v - bf2f(h));
 }
+// four consecutive elements (8-byte aligned) as hi and lo bf16 in one 8-byte store each
+__device__ __forceinline__ void split_store4(float4 v, uint16_t *hi, uint16_t *lo) {
+  const uint32_t h0 = f2bf(v.x), h1 = f2bf(v.y), h2 = f2bf(v.z), h3 = f2bf(v.w);
+  const uint32_t l0 = f2bf(v.x - bf2f(h0)), l1 = f2bf(v.y - bf2f(h1)), l2 = f2bf(v.z - bf2f(h2)), l3 = f2bf(v.w - bf2f(h3));
+  *reinterpret_cast<uint2 *>(hi) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+  *reinterpret_cast<uint2 *>(lo) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+}
 __device__ __forceinline__ float sigmoidf_(float x) {
   if (x >= 0.f) return 1.f / (1.f + expf(-x));
   const float e = expf(x);
@@ -369,14 +376,17 @@ __global__ void __launch_bounds__(PF_THREADS) pf_reduce_norm(float *X, const flo
   const int row = blockIdx.x, n4 = threadIdx.x;
   const bool on = n4 < H / 4;
   float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (on) {
-    float4 acc = reinterpret_cast<const float4 *>(part + (size_t)row * H)[n4];
-    for (int z = 1; z < nsplit; ++z) {
-      const float4 p = reinterpret_cast<const float4 *>(part + z * stride + (size_t)row * H)[n4];
-      acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
-    }
+  if (on) {   // (nsplit <= 4: all loads issued before the first add)
+    float4 p[4];
+#pragma unroll
+    for (int z = 0; z < 4; ++z)
+      p[z] = reinterpret_cast<const float4 *>(part + min(z, nsplit - 1) * stride + (size_t)row * H)[n4];
     float4 *xp = reinterpret_cast<float4 *>(X + (size_t)row * H) + n4;
     const float4 x0 = *xp;
+    float4 acc = p[0];
+#pragma unroll
+    for (int z = 1; z < 4; ++z)
+      if (z < nsplit) { acc.x += p[z].x; acc.y += p[z].y; acc.z += p[z].z; acc.w += p[z].w; }
     xv = make_float4(x0.x + acc.x, x0.y + acc.y, x0.z + acc.z, x0.w + acc.w);
     *xp = xv;
   }
@@ -387,42 +397,11 @@ __global__ void __launch_bounds__(PF_THREADS) pf_reduce_norm(float *X, const flo
   if (on) {
     const float4 gv = reinterpret_cast<const float4 *>(g)[n4];
     const size_t o = (size_t)row * ld + n4 * 4;
-    split_store(xv.x / den * gv.x, oh + o, ol + o);
-    split_store(xv.y / den * gv.y, oh + o + 1, ol + o + 1);
-    split_store(xv.z / den * gv.z, oh + o + 2, ol + o + 2);
-    split_store(xv.w / den * gv.w, oh + o + 3, ol + o + 3);
+    split_store4(make_float4(xv.x / den * gv.x, xv.y / den * gv.y, xv.z / den * gv.z, xv.w / den * gv.w), oh + o, ol + o);
   }
 }
 
 // ------------------------------------------------------------------------------ DeltaNet
-struct PfDn {
-  const float *P;        // [T][NP]: per head x, columns x*r_in + [q | k | v | z | a | b]
-  int NP, T;
-  const float *conv;     // [C][4] taps
-  float *ring;           // [MK_RING][C] pre-conv inputs by position
-  const int32_t *ctl;
-  int nh, dk, dv, r_in, C;
-};
-
-// source column in P of conv channel ch (q channels, then k, then v)
-__device__ __forceinline__ int dn_col(const PfDn &d, int ch) {
-  const int nqk = d.nh * d.dk;
-  if (ch < nqk) return (ch / d.dk) * d.r_in + (ch % d.dk);
-  if (ch < 2 * nqk) return ((ch - nqk) / d.dk) * d.r_in + d.dk + ((ch - nqk) % d.dk);
-  const int c2 = ch - 2 * nqk;
-  return (c2 / d.dv) * d.r_in + 2 * d.dk + (c2 % d.dv);
-}
-
-// keep the pre-conv inputs of the last positions for the decode kernel's conv
-__global__ void __launch_bounds__(PF_THREADS) pf_dn_ring(PfDn d) {
-  const int p0 = d.ctl[MK_CTL_POS];
-  const int first = max(0, d.T - MK_RING);
-  const int t = first + blockIdx.x;
-  if (t >= d.T) return;
-  for (int ch = threadIdx.x; ch < d.C; ch += PF_THREADS)
-    d.ring[((p0 + t) & (MK_RING - 1)) * d.C + ch] = d.P[(size_t)t * d.NP + dn_col(d, ch)];
-}
-
 // v_mfma_f32_16x16x4f32: D += A B with A 16 x 4, B 4 x 16 (full FP32).  Lane l supplies
 // A[l % 16][l / 16] and B[l / 16][l % 16]; register v of lane l holds D[4 (l / 16) + v][l % 16].
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -706,6 +685,9 @@ struct PfScan {
   const float *cW, *cQ, *cU, *cO, *cKt, *cg, *cd;
   float *o;                        // [PT][nh dv]
   int T, nh;
+  const float *P;                  // [T][NP] in-projection outputs (conv inputs of the pass)
+  int NP, r_in, C;
+  float *ring;                     // [MK_RING][C] conv inputs by position, for the decode kernel
 };
 
 // Carry 16 rows of one head's state through every chunk of the pass.  Per chunk, with S the
@@ -732,6 +714,15 @@ __global__ void __launch_bounds__(SCAN_THREADS) pf_dn_scan(PfScan s) {
   const bool isq = w >= 4, upd = w < DK / 16;
   const int pt = w & 3;               // token block of the P tile
   float *Sg = s.S + ((size_t)h * DK + r0) * DK;
+  if (blockIdx.y == 0) {  // the head's conv inputs of the pass's last positions into the ring
+    // (the chunk terms have read the earlier positions they need from it already)
+    const int n = min(s.T, MK_RING), p0 = s.ctl[MK_CTL_POS];
+    for (int e = tid; e < n * 3 * DK; e += SCAN_THREADS) {
+      const int t = s.T - n + e / (3 * DK), q = e % (3 * DK), seg = q / DK;
+      s.ring[((p0 + t) & (MK_RING - 1)) * s.C + seg * s.nh * DK + h * DK + (q - seg * DK)] =
+          s.P[(size_t)t * s.NP + h * s.r_in + q];
+    }
+  }
   for (int e = tid; e < SR * DK / 4; e += SCAN_THREADS) {
     const int r = e / (DK / 4), c4 = e - r * (DK / 4);
     *reinterpret_cast<float4 *>(Sl + r * SL + c4 * 4) = ld4(Sg + r * DK + c4 * 4);
@@ -1281,18 +1272,15 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         if (e != hipSuccess) return e;
         const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
         // dk == dv in {64, 128} (checked when the model is loaded).  The chunk terms read the ring
-        // (conv inputs of earlier positions) before pf_dn_ring overwrites it with this pass's last ones.
+        // (conv inputs of earlier positions) before the scan overwrites it with this pass's last ones.
         PfChunk ck{pf->P, pf->NP, d->r_in, d->C, nh, L.dn_conv, L.ring, d->ctl, d->l2_eps,
                    pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, T};
-        PfScan sc{L.S, L.pend, d->ctl, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, pf->o, T, nh};
+        PfScan sc{L.S, L.pend, d->ctl, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, pf->o, T, nh,
+                  pf->P, pf->NP, d->r_in, d->C, L.ring};
         if (dk == 128)
           hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(128), st, ck);
         else
           hipLaunchKernelGGL(pf_dn_chunk_prep<64>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(64), st, ck);
-        PfDn dn{};
-        dn.P = pf->P; dn.NP = pf->NP; dn.T = T; dn.ring = L.ring; dn.ctl = d->ctl;
-        dn.nh = nh; dn.dk = dk; dn.dv = dv; dn.r_in = d->r_in; dn.C = d->C;
-        hipLaunchKernelGGL(pf_dn_ring, dim3(T < MK_RING ? T : MK_RING), dim3(PF_THREADS), 0, st, dn);
         if (dk == 128)
           hipLaunchKernelGGL(pf_dn_scan<128>, dim3(nh, 128 / 16), dim3(SCAN_THREADS), scan_lds(128), st, sc);
         else
