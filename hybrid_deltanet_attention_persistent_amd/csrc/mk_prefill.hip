@@ -1114,17 +1114,21 @@ __global__ void __launch_bounds__(PF_THREADS) pf_lm(const float *X, int row, con
   const int r0 = (int)((long long)b * V / gridDim.x), r1 = (int)((long long)(b + 1) * V / gridDim.x);
   unsigned long long mybest = 0;
   int bad = 0;
-  constexpr int RBATCH = 8;   // rows per wave whose loads are in flight together
-  for (int rb = r0 + w * RBATCH; rb < r1; rb += (PF_THREADS / 64) * RBATCH) {
-    uint4 wv[RBATCH][2];
+  // Each wave streams batches of RBATCH rows, the next batch's loads in flight while the current
+  // one is reduced.  Every load is issued (rows past the range and lanes past H read valid memory
+  // and are masked), so the compiler's waits stay exact.
+  constexpr int RBATCH = 8;
+  const int stride = (PF_THREADS / 64) * RBATCH;
+  auto load = [&](uint4 (&wv)[RBATCH][2], int rb) {
 #pragma unroll
     for (int q = 0; q < RBATCH; ++q)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int i = lane * 8 + h2 * 512;
-        wv[q][h2] = make_uint4(0u, 0u, 0u, 0u);
-        if (rb + q < r1 && i < H) wv[q][h2] = *reinterpret_cast<const uint4 *>(embed + (size_t)(rb + q) * H + i);
+        wv[q][h2] = *reinterpret_cast<const uint4 *>(embed + (size_t)min(rb + q, r1 - 1) * H + (i < H ? i : 0));
       }
+  };
+  auto reduce = [&](const uint4 (&wv)[RBATCH][2], int rb) {
 #pragma unroll
     for (int q = 0; q < RBATCH; ++q) {
       float p = 0.f;
@@ -1149,6 +1153,15 @@ __global__ void __launch_bounds__(PF_THREADS) pf_lm(const float *X, int row, con
         if (kk > mybest) mybest = kk;
       }
     }
+  };
+  uint4 wa[RBATCH][2], wc[RBATCH][2];
+  int rb = r0 + w * RBATCH;
+  load(wa, rb);
+  for (; rb < r1; rb += 2 * stride) {
+    load(wc, rb + stride);
+    reduce(wa, rb);
+    load(wa, rb + 2 * stride);
+    reduce(wc, rb + stride);
   }
   if (lane == 0) wb[w] = mybest;
   if (bad) __hip_atomic_fetch_or(ctl + MK_CTL_ERR, MK_DERR_NAN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1161,15 +1174,23 @@ __global__ void __launch_bounds__(PF_THREADS) pf_lm(const float *X, int row, con
 }
 
 // end of a pass: the greedy token (last pass), the position, pending updates consumed
+// (one wave: each lane takes every 64th candidate, then a butterfly maximum over the lanes)
 __global__ void pf_finish(const unsigned long long *best, int nbest, int32_t *argmax, int32_t *ctl, int T) {
-  if (threadIdx.x != 0) return;
+  const int lane = threadIdx.x;
   if (argmax) {
     unsigned long long m = 0;
-    for (int i = 0; i < nbest; ++i) m = best[i] > m ? best[i] : m;
-    argmax[0] = (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFu));
+    for (int i = lane; i < nbest; i += 64) m = best[i] > m ? best[i] : m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long y = __shfl_xor(m, o, 64);
+      m = y > m ? y : m;
+    }
+    if (lane == 0) argmax[0] = (int32_t)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFu));
   }
-  ctl[MK_CTL_POS] += T;
-  ctl[MK_CTL_PEND] = 0;
+  if (lane == 0) {
+    ctl[MK_CTL_POS] += T;
+    ctl[MK_CTL_PEND] = 0;
+  }
 }
 
 }  // namespace
