@@ -367,6 +367,43 @@ __device__ __forceinline__ void rg_dot(const u32x4 (&w)[LMAX], int L, int G, con
   for (int c = 0; c < NCOL; ++c) out[c] = group_sum(out[c], G);
 }
 
+// rg_dot for the down projection (up to 8 loads per lane): every activation load of a column is
+// issued before its products, and the products alternate between two accumulators, so the loads
+// overlap and the dependent chain is half as long.  Decode and verify both use it (same order).
+template <int NCOL, int LMAX>
+__device__ __forceinline__ void rg_dot_dn(const u32x4 (&w)[LMAX], int L, int G, const float *act, int astride, int n,
+                                          float (&out)[NCOL]) {
+  const int kl = (lane_id() & (G - 1)) * 8;
+#pragma unroll
+  for (int c = 0; c < NCOL; ++c) {
+    out[c] = 0.f;
+    if (c < n) {
+      float4 a[LMAX][2];
+#pragma unroll
+      for (int i = 0; i < LMAX; ++i) {   // (past L: a valid re-read, unused)
+        const int k0 = (i < L ? i : 0) * G * 8 + kl;
+        a[i][0] = *reinterpret_cast<const float4 *>(act + c * astride + k0);
+        a[i][1] = *reinterpret_cast<const float4 *>(act + c * astride + k0 + 4);
+      }
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < LMAX; ++i) {
+        if (i < L) {
+          float f[8];
+          unpack8(w[i], f);
+          s0 = fmaf(f[0], a[i][0].x, s0); s1 = fmaf(f[1], a[i][0].y, s1);
+          s0 = fmaf(f[2], a[i][0].z, s0); s1 = fmaf(f[3], a[i][0].w, s1);
+          s0 = fmaf(f[4], a[i][1].x, s0); s1 = fmaf(f[5], a[i][1].y, s1);
+          s0 = fmaf(f[6], a[i][1].z, s0); s1 = fmaf(f[7], a[i][1].w, s1);
+        }
+      }
+      out[c] = s0 + s1;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NCOL; ++c) out[c] = group_sum(out[c], G);
+}
+
 // Per-lane partial dot of 16 bf16 weights (two 16-byte loads) with 16 cached activations.
 __device__ __forceinline__ float dot16(const u32x4 &w0, const u32x4 &w1, const float (&a)[16]) {
   float f[8], s = 0.f;
@@ -1222,7 +1259,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         if (!gather2d<MCS, NPW>(xm, ncol, J, xm_len, tg, mv, flag, m.ctl, SITE(11), tid)) MK_BAIL();
         if (wx < nrg) {
           float oo[NCOL];
-          rg_dot<NCOL, LMAX_D>(w_dn[0], L_d, G_d, mv, J, ncol, oo);
+          rg_dot_dn<NCOL, LMAX_D>(w_dn[0], L_d, G_d, mv, J, ncol, oo);
           if ((lane & (G_d - 1)) == 0) {
             const int row = wx * RG_d + lane / G_d;
             FOR_COL(c) pub(ly.x_ffn + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
