@@ -572,6 +572,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // physical pages of this workgroup's attention key blocks lw, lw + 32, ... (32 keys each, two
   // blocks per page), read once per launch: block j of the workgroup lies in page pgs[j]
   int *pgs = flag + 16;                         // [16] (10240 positions / 32 / 32 = 10 blocks)
+  // RoPE cos / sin of this launch's positions [NCOL][hd / 2][2] (hd <= 128), loaded with the
+  // embedding rows so that no attention layer waits for them
+  float *rl = reinterpret_cast<float *>(pgs + 16);
   if (tid < 16) {
     const int pi = (lw + tid * MK_NL) * MK_KBLK / MK_PAGE;
     pgs[tid] = (pi < m.max_pages) ? m.page_table[pi] : 0;
@@ -706,6 +709,15 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       }
       const uint16_t *row = m.embed + (size_t)t * H;
       for (int k = tid; k < H; k += MK_THREADS) xres[c * H + k] = bfv(row[k]);
+    }
+    if (m.nq > 0) {
+      const int half = hd / 2;
+      for (int i = tid; i < ncol * half; i += MK_THREADS) {
+        const int c = i / half, d = i - c * half;
+        const float2 r = *reinterpret_cast<const float2 *>(m.rope + ((size_t)(pos0 + c) * half + d) * 2);
+        rl[i * 2 + 0] = r.x;
+        rl[i * 2 + 1] = r.y;
+      }
     }
     lbar();
 
@@ -1006,8 +1018,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             const int half = hd / 2;
             for (int i = tid; i < ncol * half; i += MK_THREADS) {
               const int c = i / half, d = i - c * half;
-              const float cs = m.rope[((size_t)(pos0 + c) * half + d) * 2 + 0];
-              const float sn = m.rope[((size_t)(pos0 + c) * half + d) * 2 + 1];
+              const float cs = rl[i * 2 + 0], sn = rl[i * 2 + 1];
               float *q = qkv + c * 3 * hd, *k = q + hd, *v = k + hd;
               const float q1 = q[d], q2 = q[d + half], k1 = k[d], k2 = k[d + half];
               q[d] = q1 * cs - q2 * sn;
