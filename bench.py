@@ -72,7 +72,7 @@ def prefill_flops(cfg: W.ModelConfig, T: int, p0: int = 0) -> dict:
 
 def source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("mk_forward.hip", "mk_layout.h"):
+    for f in ("mk_forward_kernel.h", "mk_forward.hip", "mk_layout.h"):
         h.update(open(os.path.join(ROOT, "hybrid_deltanet_attention_persistent_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmk.so")
-SOURCES = ["mk_api.cpp", "mk_forward.hip", "mk_prefill.hip"]
+SOURCES = ["mk_api.cpp", "mk_forward.hip", "mk_verify.hip", "mk_prefill.hip"]
 
 # -ffp-contract=off: every fused multiply-add in the kernels is an explicit fmaf, so the
 # arithmetic (and the bit-identity of decode and verify) is fixed by the source.
