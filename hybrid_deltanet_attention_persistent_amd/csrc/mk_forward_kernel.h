@@ -1082,11 +1082,12 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 const uint32_t off = cached ? (uint32_t)((((pgs[j] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + d0) * 2) : OOB_OFF;
                 float kf[8];
                 unpack8(__builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0), kf);
-                if (ks < nk && !cached) {
-                  const float *kk = qkv + (tpos - pos0) * 3 * hd + hd + d0;
+                // this step's keys: read from LDS for every slot (row 0 where unused) and selected,
+                // so the loop body stays one block and the loads of several steps issue together
+                const bool cur = ks < nk && !cached;
+                const float *kk = qkv + (cur ? tpos - pos0 : 0) * 3 * hd + hd + d0;
 #pragma unroll
-                  for (int i = 0; i < 8; ++i) kf[i] = kk[i];
-                }
+                for (int i = 0; i < 8; ++i) kf[i] = cur ? kk[i] : kf[i];
                 float sdot = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) sdot = fmaf(q[d0 + i], kf[i], sdot);
@@ -1128,11 +1129,10 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                     v0 = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, 0) << 16);
                     v1 = 0.f;
                   }
-                  if (!cached) {
-                    const float *vv = qkv + (tpos - pos0) * 3 * hd + 2 * hd + lane * dpl;
-                    v0 = vv[0];
-                    if (dpl == 2) v1 = vv[1];
-                  }
+                  const float *vv = qkv + (cached ? 0 : tpos - pos0) * 3 * hd + 2 * hd + lane * dpl;
+                  const float l0 = vv[0], l1 = (dpl == 2) ? vv[1] : 0.f;
+                  v0 = cached ? v0 : l0;
+                  v1 = cached ? v1 : l1;
                   const float p = sc[ks];
                   acc[0] = fmaf(p, v0, acc[0]);
                   acc[1] = fmaf(p, v1, acc[1]);
@@ -1495,4 +1495,3 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     }
   }
 }
-
