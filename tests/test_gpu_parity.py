@@ -203,6 +203,35 @@ def test_tiny_reset_reproduces_bits(dev, tiny):
     r.close()
 
 
+@pytest.mark.parametrize("width,n_good", [(2, 1), (3, 0), (3, 2), (4, 1), (4, 3)])
+def test_tiny_verify_narrower_than_five(dev, tiny, width, n_good):
+    """A verify forward of 2..4 tokens: per-position argmax and logits bit-identical to sequential
+    decode steps, n_accepted = 1 + the drafts that match, position advanced by n_accepted."""
+    cfg = W.TINY
+    prompt = W.make_prompt(cfg, 13, seed=12)
+    seq = Runner(cfg, tiny, dev)
+    g0, _ = seq.prefill(prompt)
+    ref = OracleModel(cfg, tiny, C2)
+    ref.prefill(prompt)
+    drafts, t = [], g0
+    for _ in range(width - 1):
+        t = argmax_lowest(ref.decode(t))
+        drafts.append(t)
+    if n_good < width - 1:
+        drafts[n_good] = (drafts[n_good] + 1) % cfg.vocab
+    toks = [g0] + drafts
+    s = [seq.decode(x) for x in toks]
+    ver = Runner(cfg, tiny, dev)
+    ver.prefill(prompt)
+    vg, n_acc, vl = ver.verify(toks)
+    assert vg == [x[0] for x in s]
+    assert np.array_equal(vl.view(np.uint32), np.stack([x[1] for x in s]).view(np.uint32))
+    assert n_acc == n_good + 1
+    assert ver.m.sync() == len(prompt) + n_acc
+    seq.close()
+    ver.close()
+
+
 @pytest.mark.parametrize("n_good", [0, 1, 2, 3, 4])
 def test_tiny_verify_is_bit_identical_to_sequential_decode(dev, tiny, n_good):
     cfg = W.TINY
