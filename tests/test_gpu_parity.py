@@ -433,6 +433,29 @@ def test_24L_verify5(dev, big_weights):
     r.close()
 
 
+@pytest.mark.parametrize("plen", [1, 67, 130])
+def test_24L_ragged_prompt_matches_live_oracle(dev, big_weights, plen):
+    """The hidden-1024 kernels against the live oracle at prompt lengths off the 64-token chunk
+    grid (one token, one chunk + 3, two chunks + 2), then three chained greedy steps."""
+    cfg = W.HYBRID_24L
+    prompt = W.make_prompt(cfg, plen, seed=41)
+    ref_toks, ref_logits = OracleModel(cfg, big_weights, C2).generate(prompt, 3)
+    r = Runner(cfg, big_weights, dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    logits = torch.zeros((4, cfg.vocab), dtype=torch.float32, device=dev)
+    r.m.prefill(i32(prompt, dev), nxt, logits[0])
+    outs = [nxt]
+    for i in range(3):
+        o = torch.zeros(1, dtype=torch.int32, device=dev)
+        r.m.decode_step(outs[-1], o, logits[i + 1])
+        outs.append(o)
+    assert r.m.sync() == plen + 3
+    assert [int(o.item()) for o in outs] == list(ref_toks)
+    for i in range(4):
+        close(logits[i].cpu().numpy(), ref_logits[i], f"prompt {plen}, position {i}")
+    r.close()
+
+
 def test_24L_verify_bit_identical_to_decode(dev, big_weights):
     cfg = W.HYBRID_24L
     prompt = W.make_prompt(cfg, 70, seed=31)
