@@ -186,6 +186,30 @@ def test_tiny_context_limit_and_bad_token(dev, tiny):
     r.close()
 
 
+def test_tiny_rejects_empty_and_oversized_calls(dev, tiny):
+    """Zero tokens, or a decode/verify wider than max_verify, is MK_EINVAL before anything is
+    enqueued: the position stays where it was and the model keeps working."""
+    cfg = W.TINY
+    import hybrid_deltanet_attention_persistent_amd as pkg
+    r = Runner(cfg, tiny, dev)
+    buf = i32(list(range(cfg.max_verify + 1)), dev)
+    out = torch.zeros(cfg.max_verify + 1, dtype=torch.int32, device=dev)
+    for n in (0, cfg.max_verify + 1):
+        with pytest.raises(pkg.MkError) as e:
+            r.m.decode_step(buf, out, None, None, n_tokens=n)
+        assert e.value.status == pkg.lib.MK_EINVAL
+    with pytest.raises(pkg.MkError) as e:
+        r.m.prefill(buf[:0], out[:1])
+    assert e.value.status == pkg.lib.MK_EINVAL
+    assert r.m.sync() == 0
+    prompt = W.make_prompt(cfg, 4, seed=3)
+    g, lg = r.prefill(prompt)
+    ref = OracleModel(cfg, tiny, C2)
+    close(lg, ref.prefill(prompt), "prefill after rejected calls")
+    assert r.m.sync() == 4
+    r.close()
+
+
 def test_tiny_reset_reproduces_bits(dev, tiny):
     cfg = W.TINY
     prompt = W.make_prompt(cfg, 16, seed=1)
