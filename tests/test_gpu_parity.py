@@ -480,6 +480,31 @@ def test_24L_ragged_prompt_matches_live_oracle(dev, big_weights, plen):
     r.close()
 
 
+def test_24L_appended_prompt_matches_live_oracle(dev, big_weights):
+    """A second prompt appended at an unaligned position (after a prompt and two decode steps):
+    the prefill picks up the conv history, the delta-rule state and the KV cache where decode left
+    them, on the hidden-1024 kernels."""
+    cfg = W.HYBRID_24L
+    p1, p2 = W.make_prompt(cfg, 67, seed=43), W.make_prompt(cfg, 45, seed=44)
+    ref = OracleModel(cfg, big_weights, C2)
+    r = Runner(cfg, big_weights, dev)
+    checks = [(r.prefill(p1), ref.prefill(p1))]
+    t = checks[-1][0][0]
+    for _ in range(2):
+        checks.append((r.decode(t), ref.decode(t)))
+        t = checks[-1][0][0]
+    checks.append((r.prefill(p2), ref.prefill(p2)))
+    t = checks[-1][0][0]
+    for _ in range(2):
+        checks.append((r.decode(t), ref.decode(t)))
+        t = checks[-1][0][0]
+    for i, ((g, lg), rl) in enumerate(checks):
+        assert g == argmax_lowest(rl), f"call {i}"
+        close(lg, rl, f"call {i}")
+    assert r.m.sync() == 67 + 2 + 45 + 2
+    r.close()
+
+
 def test_24L_verify_bit_identical_to_decode(dev, big_weights):
     cfg = W.HYBRID_24L
     prompt = W.make_prompt(cfg, 70, seed=31)
