@@ -558,3 +558,95 @@ def test_24L_long_context(dev, big_weights):
     for i in range(n):
         check_golden_logits(lg[i], gd, i)
     r.close()
+
+
+def test_24L_pp520_full_vocab_live_oracle(dev, big_weights):
+    """The headline workload's prompt (520 seeded tokens) and two chained greedy steps on the
+    hidden-1024 kernels, every one of the 151,936 logits against the live oracle."""
+    cfg = W.HYBRID_24L
+    prompt = W.make_prompt(cfg, 520, seed=1)
+    ref_toks, ref_logits = OracleModel(cfg, big_weights, C2).generate(prompt, 2)
+    r = Runner(cfg, big_weights, dev)
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    logits = torch.zeros((3, cfg.vocab), dtype=torch.float32, device=dev)
+    r.m.prefill(i32(prompt, dev), nxt, logits[0])
+    outs = [nxt]
+    for i in range(2):
+        o = torch.zeros(1, dtype=torch.int32, device=dev)
+        r.m.decode_step(outs[-1], o, logits[i + 1])
+        outs.append(o)
+    assert r.m.sync() == 522
+    assert [int(o.item()) for o in outs] == list(ref_toks)
+    lg = logits.cpu().numpy()
+    for i in range(3):
+        close(lg[i], ref_logits[i], f"position {i} (all {cfg.vocab} logits)")
+    r.close()
+
+
+class SeqReplay:
+    """Sequential single-token decode from the prompt over a given token history: the reference a
+    verify forward must reproduce bit for bit."""
+
+    def __init__(self, cfg, weights, dev, prompt):
+        self.r = Runner(cfg, weights, dev)
+        self.prompt = prompt
+
+    def run(self, history, toks):
+        """Reset, prefill the prompt, decode `history` (the committed tokens), then decode `toks`
+        one at a time; returns [(greedy, logits)] for `toks`."""
+        self.r.m.reset()
+        self.r.prefill(self.prompt)
+        for x in history:
+            self.r.decode(x)
+        return [self.r.decode(x) for x in toks]
+
+    def close(self):
+        self.r.close()
+
+
+@pytest.mark.parametrize("n_acc1", [1, 2, 3, 4, 5])
+def test_24L_planted_draft_verify(dev, big_weights, n_acc1):
+    """Verify forwards on the hidden-1024 kernels with drafts planted from the oracle's greedy
+    continuation, corrupted at one position, so that every n_accepted in 1..5 occurs: the first
+    forward accepts n_acc1 tokens, the second (which first replays the n_acc1 pending delta-rule
+    updates) accepts 6 - n_acc1 (5 when n_acc1 is 1).  Per position, argmax and logits must equal
+    sequential decode steps bit for bit, and the oracle within the parity bar; after the second
+    forward a decode step continues from exactly the accepted prefix."""
+    cfg = W.HYBRID_24L
+    prompt = W.make_prompt(cfg, 70, seed=31)
+    ref = OracleModel(cfg, big_weights, C2)
+    g_ref, _ = ref.generate(prompt, 11)            # g0 .. g11, the oracle's greedy continuation
+    g_ref = [int(t) for t in g_ref]
+    ver = Runner(cfg, big_weights, dev)
+    seq = SeqReplay(cfg, big_weights, dev, prompt)
+    g0, _ = ver.prefill(prompt)
+    assert g0 == g_ref[0]
+    ref = OracleModel(cfg, big_weights, C2)
+    ref.prefill(prompt)
+    committed = []                                   # tokens consumed after the prompt
+    for f, want in enumerate([n_acc1, 6 - n_acc1 if n_acc1 > 1 else 5]):
+        base = len(committed)
+        toks = g_ref[base:base + 5]                  # [last accepted, 4 greedy drafts]
+        if want < 5:                                 # corrupt draft `want` -> n_accepted == want
+            toks[want] = (toks[want] + 1 + f) % cfg.vocab
+        vg, n_acc, vl = ver.verify(toks)
+        s = seq.run(committed, toks)
+        assert vg == [x[0] for x in s], f"forward {f}"
+        assert np.array_equal(vl.view(np.uint32), np.stack([x[1] for x in s]).view(np.uint32)), f"forward {f}"
+        rg, rn, rl = ref.verify(toks)
+        assert n_acc == rn == want, f"forward {f}: n_accepted {n_acc}, oracle {rn}, planted {want}"
+        assert vg[:n_acc] == rg[:n_acc]
+        for j in range(5):
+            close(vl[j], rl[j], f"forward {f} position {j}")
+        committed += toks[:n_acc]
+        assert vg[n_acc - 1] == g_ref[len(committed)]
+    assert ver.m.sync() == len(prompt) + len(committed)
+    nxt = g_ref[len(committed)]
+    a = ver.decode(nxt)
+    b = seq.run(committed, [nxt])[0]
+    assert a[0] == b[0] and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    rl = ref.decode(nxt)
+    close(a[1], rl, "decode after the rollback")
+    assert a[0] == argmax_lowest(rl)
+    ver.close()
+    seq.close()
