@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -18,6 +19,7 @@
 
 extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, int shape, hipStream_t stream);
 extern "C" hipError_t mk_forward_occupancy(int ncol_template, int shape, int *blocks_per_cu);
+extern "C" hipError_t mk_static_scratch(void **ptr);
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
                                          const int32_t *tokens, int n, int32_t *argmax, float *logits,
                                          hipStream_t st);
@@ -47,6 +49,8 @@ struct mk_model {
   MkPf pf;                              // prefill scratch
   char *arena;
   size_t arena_bytes;
+  uint2 *xch;                           // exchange slots of mk_decode_step (in the arena)
+  uint2 *static_xch;                    // device address of the static slots (mk_decode_step_static)
   // regions cleared by mk_reset_state
   std::vector<std::pair<size_t, size_t>> state_regions;
   int32_t pos_hi;  // upper bound of the device position (exact unless a verify ran)
@@ -76,12 +80,11 @@ struct LayerRegions {
   Region dn_in, dn_conv, dn_gnorm, dn_out, S, ring, pend;
   Region at_q, at_k, at_v, at_o, kc, vc;
   Region ffn_gu, ffn_dn;
-  Region x_in, x_o, x_mix, x_r1, x_m, x_ffn, x_r2;
 };
 
 struct Plan {
   int H, V, I, J, nh, dk, dv, C, r_in, nq, nkv, hd, r_in_max, x_o_len, xm_len, max_pages;
-  Region embed, lnf, rope, page_table, layer_table, ctl, x_arg;
+  Region embed, lnf, rope, page_table, layer_table, ctl, xch;
   std::vector<LayerRegions> layers;
   // prefill scratch (one pass of MK_PT tokens)
   int K1, NP;
@@ -163,7 +166,6 @@ Plan make_plan(const mk_config *c) {
   p.page_table = L.add((size_t)p.max_pages * 4);
   p.layer_table = L.add(sizeof(MkLayerDev) * c->n_layers);
   p.ctl = L.add(MK_CTL_WORDS * 4);
-  p.x_arg = L.add((size_t)MK_MAXCOL * MK_NWG * 16);
   p.layers.resize(c->n_layers);
   for (int i = 0; i < c->n_layers; ++i) {
     LayerRegions &r = p.layers[i];
@@ -188,16 +190,8 @@ Plan make_plan(const mk_config *c) {
     r.ffn_gu = L.add((size_t)2 * p.I * H * 2);
     r.ffn_dn = L.add((size_t)H * p.I * 2);
   }
-  for (int i = 0; i < c->n_layers; ++i) {
-    LayerRegions &r = p.layers[i];
-    r.x_in = L.add((size_t)MK_NX * MK_MAXCOL * p.r_in_max * 8);
-    r.x_o = L.add((size_t)MK_NX * MK_MAXCOL * p.x_o_len * 8);
-    r.x_mix = L.add((size_t)MK_MAXCOL * MK_NX * H * 8);
-    r.x_r1 = L.add((size_t)MK_NX * MK_MAXCOL * H * 8);
-    r.x_m = L.add((size_t)MK_NX * MK_MAXCOL * p.xm_len * 8);
-    r.x_ffn = L.add((size_t)MK_MAXCOL * MK_NX * H * 8);
-    r.x_r2 = L.add((size_t)MK_NX * MK_MAXCOL * H * 8);
-  }
+  // exchange slots, sized for the widest launch (verify, MK_MAXCOL columns)
+  p.xch = L.add(mk_xch_bytes(MK_MAXCOL, c->n_layers, p.H, p.r_in_max, p.x_o_len, p.xm_len));
   {
     const size_t T = MK_PT, nch = MK_PT / MK_CHUNK;
     p.K1 = std::max(p.H, std::max(p.nh * p.dv, p.nq * p.hd));
@@ -371,6 +365,8 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   int dev = 0;
   s = check_device(&dev);
   if (s != MK_OK) return s;
+  void *static_xch = nullptr;   // the static exchange slots of this device (looked up once per device)
+  HIPCHECK(mk_static_scratch(&static_xch));
   hipStream_t st = (hipStream_t)stream;
   char *A = (char *)d_arena;
   auto T = [&](const std::string &name) { return (const uint16_t *)exp[name].t->data; };
@@ -402,7 +398,6 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   d.page_table = (const int32_t *)(A + p.page_table.off);
   d.layers = (const MkLayerDev *)(A + p.layer_table.off);
   d.ctl = (int32_t *)(A + p.ctl.off);
-  d.x_arg = (uint4 *)(A + p.x_arg.off);
 
   if (p.rope.bytes) {  // rotary table in double precision, stored as float
     std::vector<float> rt((size_t)cfg->max_ctx * (p.hd / 2) * 2);
@@ -510,19 +505,11 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
       L.ffn_gu = (const uint16_t *)(A + r.ffn_gu.off);
       L.ffn_dn = (const uint16_t *)(A + r.ffn_dn.off);
     }
-    L.x_in = (uint2 *)(A + r.x_in.off);
-    L.x_o = (uint2 *)(A + r.x_o.off);
-    L.x_mix = (uint2 *)(A + r.x_mix.off);
-    L.x_r1 = (uint2 *)(A + r.x_r1.off);
-    L.x_m = (uint2 *)(A + r.x_m.off);
-    L.x_ffn = (uint2 *)(A + r.x_ffn.off);
-    L.x_r2 = (uint2 *)(A + r.x_r2.off);
   }
   HIPCHECK(put(p.layer_table, lt.data()));
   // exchange slots start with tag 0 (never used); control words and state start at zero
-  HIPCHECK(hipMemsetAsync(A + p.x_arg.off, 0, p.x_arg.bytes, st));
   {
-    const size_t x0 = p.layers[0].x_in.off;
+    const size_t x0 = p.xch.off;
     HIPCHECK(hipMemsetAsync(A + x0, 0, p.total - x0, st));
   }
   state.push_back({p.ctl.off, p.ctl.bytes});
@@ -553,6 +540,8 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   }
   mm->arena = A;
   mm->arena_bytes = arena_bytes;
+  mm->xch = (uint2 *)(A + p.xch.off);
+  mm->static_xch = (uint2 *)static_xch;
   mm->state_regions = state;
   mm->pos_hi = 0;
   mm->tag = 1;
@@ -601,11 +590,24 @@ extern "C" int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens
   return MK_OK;
 }
 
-extern "C" int mk_decode_step(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_argmax,
-                              float *d_logits, int32_t *d_n_accepted, void *stream) {
+// Sequence numbers of the static exchange slots, one counter per device: every launch that uses
+// them tags its slots with a number no earlier launch on the device used.
+static std::mutex g_static_mu;
+static uint32_t g_static_tag[256];
+
+static int decode_launch(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_argmax, float *d_logits,
+                         int32_t *d_n_accepted, void *stream, bool use_static) {
   if (!live(m)) return fail(MK_ESTATE, "model not loaded");
   if (!d_tokens || !d_argmax) return fail(MK_EINVAL, "token buffers must not be NULL");
   if (n_tokens < 1 || n_tokens > m->cfg.max_verify) return fail(MK_EINVAL, "n_tokens must be in [1, max_verify]");
+  const int tmpl = n_tokens == 1 ? 1 : MK_MAXCOL;
+  if (use_static) {
+    const size_t need = mk_xch_bytes(tmpl, m->dev.n_layers, m->dev.H, m->dev.r_in_max, m->dev.x_o_len, m->dev.xm_len);
+    if (need > (size_t)MK_STATIC_SCRATCH_BYTES)
+      return fail(MK_EINVAL, "the exchange slots of this launch need " + std::to_string(need) +
+                                 " bytes, more than the static array's " + std::to_string((size_t)MK_STATIC_SCRATCH_BYTES));
+    if (m->device < 0 || m->device >= 256) return fail(MK_EINVAL, "device index out of range");
+  }
   hipStream_t st = (hipStream_t)stream;
   int s = ensure_ctx(m, n_tokens, st);
   if (s != MK_OK) return s;
@@ -613,14 +615,33 @@ extern "C" int mk_decode_step(mk_model *m, const int32_t *d_tokens, int32_t n_to
   a.m = m->dev;
   a.tokens = d_tokens;
   a.n = n_tokens;
-  a.tag0 = m->tag;
   a.argmax = d_argmax;
   a.logits = d_logits;
   a.n_acc = d_n_accepted;
-  HIPCHECK(mk_launch_forward(&a, n_tokens == 1 ? 1 : MK_MAXCOL, mk_shape_of(m->dev), st));
-  m->tag += 1;
+  if (use_static) {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    uint32_t &t = g_static_tag[m->device];
+    if (++t == 0) t = 1;                   // 0 is the tag of never-written slots
+    a.tag0 = t;
+    a.xch = m->static_xch;
+  } else {
+    a.tag0 = m->tag;
+    a.xch = m->xch;
+  }
+  HIPCHECK(mk_launch_forward(&a, tmpl, mk_shape_of(m->dev), st));
+  if (!use_static) m->tag += 1;
   m->pos_hi += n_tokens;
   return MK_OK;
+}
+
+extern "C" int mk_decode_step(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_argmax,
+                              float *d_logits, int32_t *d_n_accepted, void *stream) {
+  return decode_launch(m, d_tokens, n_tokens, d_argmax, d_logits, d_n_accepted, stream, false);
+}
+
+extern "C" int mk_decode_step_static(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_argmax,
+                                     float *d_logits, int32_t *d_n_accepted, void *stream) {
+  return decode_launch(m, d_tokens, n_tokens, d_argmax, d_logits, d_n_accepted, stream, true);
 }
 
 extern "C" int mk_sync_status(mk_model *m, void *stream, int32_t *pos) {

@@ -1,6 +1,38 @@
 // mk_forward.hip -- decode instantiations of the persistent forward kernel (one column per
 // launch) and the host-side launch entry points for both decode and verify.
+#include <mutex>
+
+#include "mk.h"
 #include "mk_forward_kernel.h"
+
+// ------------------------------------------------------------------------------ static exchange slots
+// The exchange slots of mk_decode_step_static, for callers that cannot allocate: one array per
+// device (each device holds its own copy of the code object's globals), kept until the process
+// ends.  Zero at load, so every slot starts with tag 0, which no launch uses.  Host code must not
+// pass `scratch` itself to a kernel (on the host it names a stand-in, not device memory): it takes
+// the device address from mk_static_scratch and passes that.
+static __device__ __align__(256) unsigned char scratch[MK_STATIC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device (the library's
+// load call does it with the model's device current).
+extern "C" hipError_t mk_static_scratch(void **ptr) {
+  static std::mutex mu;
+  static void *addr[256] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 256) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || ((uintptr_t)p & 255) != 0) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------------------ host-side launchers
 // Instantiations: one decode column (here) or up to MK_MAXCOL verify columns (mk_verify.hip), each

@@ -739,6 +739,14 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       int tid = tid0;
       asm volatile("" : "+v"(tid));
       const int lane = tid & 63;
+      // this layer's exchange slots (layout in mk_layout.h)
+      uint2 *const x_in_l = a.xch + (size_t)li * mk_xch_layer_slots(NCOL, H, r_in_max, x_o_len, xm_len);
+      uint2 *const x_o_l = x_in_l + NCOL * MK_NX * r_in_max;
+      uint2 *const x_mix_l = x_o_l + NCOL * MK_NX * x_o_len;
+      uint2 *const x_r1_l = x_mix_l + NCOL * MK_NX * H;
+      uint2 *const x_m_l = x_r1_l + NCOL * MK_NX * H;
+      uint2 *const x_ffn_l = x_m_l + NCOL * MK_NX * xm_len;
+      uint2 *const x_r2_l = x_ffn_l + NCOL * MK_NX * H;
       // gains of this layer's gated RMSNorm (DeltaNet), held by the last wave, which applies it in
       // D3: elements lane and lane + 64
       const int gnn = (ly.kind == 0 && w8 == MK_WAVES - 1) ? dv : 0;
@@ -761,8 +769,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       }
       if (ly.kind == 0) {
         // ================================================ DeltaNet layer
-        uint2 *xin = ly.x_in + (size_t)x * MK_MAXCOL * r_in_max;
-        uint2 *xo = ly.x_o + (size_t)x * MK_MAXCOL * x_o_len;
+        uint2 *xin = x_in_l + (size_t)x * NCOL * r_in_max;
+        uint2 *xo = x_o_l + (size_t)x * NCOL * x_o_len;
         const int RW = dv / MK_NL, r0 = lw * RW;
         // ---- D1: in-projection rows of head x (weights already in flight)
         if (x < nh) {
@@ -970,19 +978,19 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               rg_dot<NCOL, 1>(w_out[r], 1, G_o, o, dv, ncol, oo);
               if ((lane & (G_o - 1)) == 0) {
                 const int row = rg * RG_o + lane / G_o;
-                FOR_COL(c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
+                FOR_COL(c) pub(x_mix_l + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
               }
             }
           }
         } else {
           for (int i = tid + lw * MK_THREADS; i < H; i += MK_NL * MK_THREADS)
-            for (int c = 0; c < ncol; ++c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + i, 0.f, tg);
+            for (int c = 0; c < ncol; ++c) pub(x_mix_l + ((size_t)c * MK_NX + x) * H + i, 0.f, tg);
         }
       } else {
         // ================================================ attention layer
         const int kvh = x * nkv / nq;
-        uint2 *xin = ly.x_in + (size_t)x * MK_MAXCOL * r_in_max;
-        uint2 *xo = ly.x_o + (size_t)x * MK_MAXCOL * x_o_len;
+        uint2 *xin = x_in_l + (size_t)x * NCOL * r_in_max;
+        uint2 *xo = x_o_l + (size_t)x * NCOL * x_o_len;
         if (x < nq) {
           // ---- A1: q rows of head x, k/v rows of its kv head (weights already in flight)
           const int per = hd / RG_h;
@@ -1195,14 +1203,14 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 rg_dot<NCOL, 1>(w_out[r], 1, G_a, ov, hd, ncol, oo);
                 if ((lane & (G_a - 1)) == 0) {
                   const int row = rg * RG_a + lane / G_a;
-                  FOR_COL(c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
+                  FOR_COL(c) pub(x_mix_l + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
                 }
               }
             }
           }
         } else {
           for (int i = tid + lw * MK_THREADS; i < H; i += MK_NL * MK_THREADS)
-            for (int c = 0; c < ncol; ++c) pub(ly.x_mix + ((size_t)c * MK_NX + x) * H + i, 0.f, tg);
+            for (int c = 0; c < ncol; ++c) pub(x_mix_l + ((size_t)c * MK_NX + x) * H + i, 0.f, tg);
         }
       }
       // prefetch: gate/up rows of FFN slice x (F1), in flight during the residual reduction
@@ -1212,8 +1220,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         // [NCOL*8][SL], apart from everything the mixer phases read: the polling wave fills it
         // while the other waves may still be reading the out-projection operand
         float *tmp = work + 6400;
-        uint2 *xr = ly.x_r1 + (size_t)x * MK_MAXCOL * H;
-        reduce_slices(ly.x_mix, xr, tmp, SITE(8));
+        uint2 *xr = x_r1_l + (size_t)x * NCOL * H;
+        reduce_slices(x_mix_l, xr, tmp, SITE(8));
         if (!gather2d<MCL, NPW>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(9), tid)) MK_BAIL();
       }
       // ================================================================ FFN
@@ -1223,7 +1231,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         rmsnorm_cols_r<NCOL>(xres, hn, g2a, g2b, H, G_h, L_h, m.rms_eps, ncol, tid);
       }
       {
-        uint2 *xm = ly.x_m + (size_t)x * MK_MAXCOL * xm_len;
+        uint2 *xm = x_m_l + (size_t)x * NCOL * xm_len;
         // ---- F1: gate/up pairs j -> m_j = SiLU(g_j) * u_j (weights already in flight)
         if constexpr (NCOL == 1) {
           if (RG_h == 1 && L_h == 2) {
@@ -1283,7 +1291,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           rg_dot_dn<NCOL, LMAX_D>(w_dn[0], L_d, G_d, mv, J, ncol, oo);
           if ((lane & (G_d - 1)) == 0) {
             const int row = wx * RG_d + lane / G_d;
-            FOR_COL(c) pub(ly.x_ffn + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
+            FOR_COL(c) pub(x_ffn_l + ((size_t)c * MK_NX + x) * H + row, oo[c], tg);
           }
         }
       }
@@ -1303,13 +1311,14 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       // ---- R2: residual += sum of the 8 FFN slices
       {
         float *tmp = work + 6400;  // [NCOL*8][SL], apart from the down-projection operand mv
-        uint2 *xr = ly.x_r2 + (size_t)x * MK_MAXCOL * H;
-        reduce_slices(ly.x_ffn, xr, tmp, SITE(12));
+        uint2 *xr = x_r2_l + (size_t)x * NCOL * H;
+        reduce_slices(x_ffn_l, xr, tmp, SITE(12));
         if (!gather2d<MCL, NPW>(xr, ncol, H, H, tg, xres, flag, m.ctl, SITE(13), tid)) MK_BAIL();
       }
     }  // layers
 
     // ================================================================ LM head + greedy argmax
+    uint4 *const x_arg = reinterpret_cast<uint4 *>(a.xch + (size_t)m.n_layers * mk_xch_layer_slots(NCOL, H, r_in_max, x_o_len, xm_len));
     float avf[16];   // decode: the final norm in registers (every wave)
     if constexpr (NCOL == 1) rmsnorm_regs(xres, g1v, H, G_h, L_h, m.rms_eps, avf);
     else rmsnorm_cols_r<NCOL>(xres, hn, g1a, g1b, H, G_h, L_h, m.rms_eps, ncol, tid0);
@@ -1416,7 +1425,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           nn |= rn[ww];
           if (rv[c * 8 + ww] > bv || (rv[c * 8 + ww] == bv && ri[c * 8 + ww] < bi)) { bv = rv[c * 8 + ww]; bi = ri[c * 8 + ww]; }
         }
-        unsigned long long *rec = reinterpret_cast<unsigned long long *>(m.x_arg + c * MK_NWG + b);
+        unsigned long long *rec = reinterpret_cast<unsigned long long *>(x_arg + c * MK_NWG + b);
         __hip_atomic_store(rec, ((unsigned long long)(uint32_t)bi << 32) | __float_as_uint(bv), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         wait_stores();  // value and index land before the tag word
@@ -1431,7 +1440,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       float *cv = work;                         // [NCOL][256]
       int *ci = reinterpret_cast<int *>(work + NCOL * MK_NWG);
       int *cn = reinterpret_cast<int *>(work + 2 * NCOL * MK_NWG);
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(m.x_arg, 0, MK_MAXCOL * MK_NWG * 16, RSRC_W3);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(x_arg, 0, NCOL * MK_NWG * 16, RSRC_W3);
       for (int i = tid; i < ncol * MK_NWG; i += MK_THREADS) {
         const unsigned long long deadline = wall_clock64() + MK_WAIT_TICKS;
         while (true) {

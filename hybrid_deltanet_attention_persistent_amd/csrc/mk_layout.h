@@ -62,15 +62,27 @@ struct MkLayerDev {
   // FFN (XCD x owns intermediate rows [x*J, (x+1)*J))
   const uint16_t *ffn_gu;             // [8] tiles [2J][H]: rows g_j, u_j interleaved
   const uint16_t *ffn_dn;             // [8] tiles [H][J]
-  // tagged exchange buffers: uint2 {float bits, tag}
-  uint2 *x_in;                        // [8][MAXCOL][r_in_max]   XCD-local
-  uint2 *x_o;                         // [8][MAXCOL][x_o_len]    XCD-local (o rows / attention partials)
-  uint2 *x_mix;                       // [MAXCOL][8][H]          grid (mixer split-K partials)
-  uint2 *x_r1;                        // [8][MAXCOL][H]          XCD-local (residual after mixer)
-  uint2 *x_m;                         // [8][MAXCOL][J]          XCD-local (SwiGLU activations)
-  uint2 *x_ffn;                       // [MAXCOL][8][H]          grid (down-projection partials)
-  uint2 *x_r2;                        // [8][MAXCOL][H]          XCD-local (residual after FFN)
 };
+
+// Tagged exchange slots (uint2 {float bits, tag}) of one launch with n columns: per layer, in this
+// order,
+//   x_in  [8][n][r_in_max]   XCD-local (in-projection / QKV rows)
+//   x_o   [8][n][x_o_len]    XCD-local (o rows / attention partials)
+//   x_mix [n][8][H]          grid      (mixer split-K partials)
+//   x_r1  [8][n][H]          XCD-local (residual after the mixer)
+//   x_m   [8][n][xm_len]     XCD-local (SwiGLU activations)
+//   x_ffn [n][8][H]          grid      (down-projection partials)
+//   x_r2  [8][n][H]          XCD-local (residual after the FFN)
+// then, after the last layer, the argmax candidates: uint4 {value, index, tag, nan} [n][256].
+// Every length is a multiple of 32 slots, so with a 256-byte aligned base no 256-byte block holds
+// two XCDs' slots.  The layout depends on n: decode (n = 1) and verify (n = 5) launches place the
+// same value at different slots, which is harmless because every launch has tags of its own.
+__host__ __device__ static inline size_t mk_xch_layer_slots(int n, int H, int r_in_max, int x_o_len, int xm_len) {
+  return (size_t)n * 8 * (size_t)(r_in_max + x_o_len + xm_len + 4 * H);
+}
+__host__ __device__ static inline size_t mk_xch_bytes(int n, int n_layers, int H, int r_in_max, int x_o_len, int xm_len) {
+  return (size_t)n_layers * mk_xch_layer_slots(n, H, r_in_max, x_o_len, xm_len) * 8 + (size_t)n * MK_NWG * 16;
+}
 
 struct MkDev {
   int32_t n_layers, H, V, I, J;
@@ -85,7 +97,6 @@ struct MkDev {
   const int32_t *page_table;          // [max_pages] logical -> physical page
   const MkLayerDev *layers;           // [n_layers]
   int32_t *ctl;                       // [MK_CTL_WORDS]
-  uint4 *x_arg;                       // [MAXCOL][256] {value, index, tag, 0}  grid
 };
 
 // Arguments of one persistent-kernel launch.
@@ -97,6 +108,7 @@ struct MkLaunch {
   int32_t *argmax;        // device: [n]
   float *logits;          // device, nullable: [n][V]
   int32_t *n_acc;         // device, nullable
+  uint2 *xch;             // device: exchange slots of this launch (mk_xch_bytes(n_template, ...) bytes, 256-byte aligned)
 };
 
 // Instantiations of the persistent kernel: MK_SHAPE_H1024 has every dimension of the hidden-1024

@@ -24,7 +24,8 @@ MK_LAYER_DELTANET, MK_LAYER_ATTENTION = 0, 1
 MK_DTYPE_BF16, MK_DTYPE_F16, MK_DTYPE_F32 = 1, 2, 3
 
 EXPORTED = ["mk_required_bytes", "mk_load_weights", "mk_reset_state", "mk_prefill", "mk_decode_step",
-            "mk_sync_status", "mk_free", "mk_status_string", "mk_last_error"]
+            "mk_decode_step_static", "mk_sync_status", "mk_free", "mk_status_string", "mk_last_error"]
+MK_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class MkError(RuntimeError):
@@ -68,6 +69,7 @@ def load_library() -> ctypes.CDLL:
     lib.mk_reset_state.argtypes = [vp, vp]
     lib.mk_prefill.argtypes = [vp, vp, i32, vp, vp, vp]
     lib.mk_decode_step.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.mk_decode_step_static.argtypes = [vp, vp, i32, vp, vp, vp, vp]
     lib.mk_sync_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.mk_free.argtypes = [vp]
     lib.mk_free.restype = None
@@ -76,7 +78,7 @@ def load_library() -> ctypes.CDLL:
     lib.mk_last_error.argtypes = []
     lib.mk_last_error.restype = ctypes.c_char_p
     for f in ("mk_required_bytes", "mk_load_weights", "mk_reset_state", "mk_prefill", "mk_decode_step",
-              "mk_sync_status"):
+              "mk_decode_step_static", "mk_sync_status"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -158,6 +160,12 @@ def mk_prefill(handle: int, tokens, next_token, last_logits=None, stream=None) -
 def mk_decode_step(handle: int, tokens, n_tokens: int, argmax, logits=None, n_accepted=None, stream=None) -> None:
     _check(load_library().mk_decode_step(handle, _ptr(tokens), int(n_tokens), _ptr(argmax), _ptr(logits),
                                          _ptr(n_accepted), _stream(stream)), "mk_decode_step")
+
+
+def mk_decode_step_static(handle: int, tokens, n_tokens: int, argmax, logits=None, n_accepted=None,
+                          stream=None) -> None:
+    _check(load_library().mk_decode_step_static(handle, _ptr(tokens), int(n_tokens), _ptr(argmax), _ptr(logits),
+                                                _ptr(n_accepted), _stream(stream)), "mk_decode_step_static")
 
 
 def mk_sync_status(handle: int, stream=None) -> int:

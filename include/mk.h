@@ -141,6 +141,26 @@ int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *
 int mk_decode_step(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_argmax,
                    float *d_logits, int32_t *d_n_accepted, void *stream);
 
+/* Size of the static exchange-slot array of mk_decode_step_static (one per device).        */
+enum { MK_STATIC_SCRATCH_BYTES = 16 << 20 };
+
+/* mk_decode_step for callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, results and errors as mk_decode_step, but the launch's exchange slots (the
+ * tagged partial results the workgroups hand each other) live in a static device array of
+ * MK_STATIC_SCRATCH_BYTES per device, held until the process ends, instead of the model's
+ * arena.  The slots of one launch take n_layers * n * 8 * (r_in_max + x_o_len + xm_len +
+ * 4 * hidden) * 8 + n * 4096 bytes, with n = 1 for a decode step and n = 5 for a verify
+ * forward (r_in_max, x_o_len, xm_len: the exchange row lengths, for the 24-layer hidden-1024
+ * model 544, 4160 and 448, so a decode step needs 14.2 MiB); a call whose slots do not fit is
+ * rejected with MK_EINVAL before anything is enqueued.  Calls no allocating routine.  All
+ * calls on one device share the array: calls that overlap in time on one device (any models,
+ * streams or threads) race and their results are undefined; calls ordered one after another
+ * are independent (each launch tags its slots with a device-wide sequence number, so nothing
+ * needs clearing between calls).                                                          */
+int mk_decode_step_static(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_argmax,
+                          float *d_logits, int32_t *d_n_accepted, void *stream);
+
 /* Synchronise `stream`, then report the device-side status of the work done so
  * far (MK_OK, MK_EHANG, MK_ETOKEN or MK_ENAN) and, if pos is not NULL, the number
  * of tokens the state holds.  A device error stays set until mk_reset_state.      */

@@ -142,7 +142,14 @@ def test_calls_on_unloaded_model_are_rejected(so):
     buf = ctypes.c_void_p(4096)
     assert so.mk_prefill(None, buf, 4, buf, None, None) == L.MK_ESTATE
     assert so.mk_decode_step(None, buf, 1, buf, None, None, None) == L.MK_ESTATE
+    assert so.mk_decode_step_static(None, buf, 1, buf, None, None, None) == L.MK_ESTATE
     assert so.mk_reset_state(None, None) == L.MK_ESTATE
     pos = ctypes.c_int32(0)
     assert so.mk_sync_status(None, None, ctypes.byref(pos)) == L.MK_ESTATE
     so.mk_free(None)  # no-op
+
+
+def test_static_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "mk.h")).read()
+    m = re.search(r"MK_STATIC_SCRATCH_BYTES\s*=\s*(\d+)\s*<<\s*(\d+)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.MK_STATIC_SCRATCH_BYTES
