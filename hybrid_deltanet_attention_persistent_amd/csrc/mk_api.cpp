@@ -127,15 +127,15 @@ int check_config(const mk_config *c, std::string &why) {
   if (c->max_ctx <= 0 || c->max_ctx % MK_PAGE != 0 || c->max_ctx > 10240) { why = "max_ctx must be a multiple of 64 in [64, 10240]"; return MK_EINVAL; }
   if (c->prefill_chunk != 64) { why = "prefill_chunk must be 64"; return MK_EINVAL; }
   if (c->max_verify < 1 || c->max_verify > MK_MAXCOL) { why = "max_verify must be in [1, 5]"; return MK_EINVAL; }
-  {  // per-wave register budgets of the persistent kernel (prefetched weight rows per phase); in
-     // decode 7 of the 8 waves of a workgroup stream weights
-    const int Gh = mk_tile_G(c->hidden), RGh = 64 / Gh, XW = MK_NL * (MK_WAVES - 1);
+  {  // per-wave register budgets of the persistent kernel (weight rows held per phase): each role
+     // (token mixer, FFN) has MK_NG workgroups of 8 weight-streaming waves per XCD
+    const int Gh = mk_tile_G(c->hidden), RGh = 64 / Gh, XW = MK_NG * MK_WAVES;
     const int J = c->ffn / MK_NX, Gd = mk_tile_G(J);
     if (nd > 0 && c->hidden / (64 / mk_tile_G(c->dn_dv)) > 2 * XW) { why = "DeltaNet out-projection too wide"; return MK_EINVAL; }
     if (na > 0 && c->hidden / (64 / mk_tile_G(c->at_head_dim)) > 2 * XW) { why = "attention o-projection too wide"; return MK_EINVAL; }
-    if (nd > 0 && (2 * c->dn_dk + 2 * c->dn_dv + 2) / RGh > 3 * XW) { why = "DeltaNet in-projection too tall"; return MK_EINVAL; }
-    if (na > 0 && 3 * c->at_head_dim / RGh > 3 * XW) { why = "QKV projection too tall"; return MK_EINVAL; }
-    if (J > 2 * XW) { why = "ffn too large for the gate/up prefetch"; return MK_EINVAL; }
+    if (nd > 0 && (2 * c->dn_dk + 2 * c->dn_dv + 2) / RGh > 5 * XW) { why = "DeltaNet in-projection too tall"; return MK_EINVAL; }
+    if (na > 0 && 3 * c->at_head_dim / RGh > 5 * XW) { why = "QKV projection too tall"; return MK_EINVAL; }
+    if (J > 4 * XW) { why = "ffn too large for the gate/up prefetch"; return MK_EINVAL; }
     if (c->hidden / (64 / Gd) > XW) { why = "down-projection tiles too many for one per wave"; return MK_EINVAL; }
   }
   return MK_OK;
@@ -153,8 +153,8 @@ Plan make_plan(const mk_config *c) {
   p.r_in_max = std::max(has_dn ? p.r_in : 0, has_at ? 3 * p.hd : 0);
   p.r_in_max = (p.r_in_max + 31) & ~31;  // 256-byte aligned per-column blocks: no cache line is shared
 
-  // attention: 32 partials {max, sum, acc[hd]}
-  p.x_o_len = std::max(has_dn ? p.dv : 0, has_at ? MK_NL * (p.hd + 2) : 0);
+  // DeltaNet: o and o g silu(z) of the head; attention: 16 partials {max, sum, acc[hd]}
+  p.x_o_len = std::max(has_dn ? 2 * p.dv : 0, has_at ? MK_NG * (p.hd + 2) : 0);
   p.x_o_len = (p.x_o_len + 31) & ~31;
   p.xm_len = (p.J + 31) & ~31;
   p.max_pages = c->max_ctx / MK_PAGE;

@@ -6,13 +6,15 @@
 // dispatches workgroups to the 8 XCDs round-robin; the kernel checks this at
 // start).  Each XCD ("group" x) owns one DeltaNet head / one query head and one
 // slice of the FFN intermediate dimension, so most hand-offs stay inside one XCD
-// and go through its L2; only the residual-stream reductions cross XCDs.
+// and go through its L2; only the residual-stream reductions cross XCDs.  Inside an
+// XCD, workgroups b >> 3 < MK_NG run the token mixers and the others the FFNs.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #define MK_NX 8                      // XCDs = head groups
 #define MK_NL 32                     // workgroups per XCD
+#define MK_NG 16                     // workgroups per XCD in each of the two roles (token mixer, FFN)
 #define MK_NWG (MK_NX * MK_NL)       // persistent grid size
 #define MK_THREADS 512               // threads per workgroup
 #define MK_WAVES (MK_THREADS / 64)   // wave64 per workgroup
@@ -67,7 +69,7 @@ struct MkLayerDev {
 // Tagged exchange slots (uint2 {float bits, tag}) of one launch with n columns: per layer, in this
 // order,
 //   x_in  [8][n][r_in_max]   XCD-local (in-projection / QKV rows)
-//   x_o   [8][n][x_o_len]    XCD-local (o rows / attention partials)
+//   x_o   [8][n][x_o_len]    XCD-local (DeltaNet o and o g silu(z) rows / attention partials)
 //   x_mix [n][8][H]          grid      (mixer split-K partials)
 //   x_r1  [8][n][H]          XCD-local (residual after the mixer)
 //   x_m   [8][n][xm_len]     XCD-local (SwiGLU activations)
@@ -117,7 +119,7 @@ enum { MK_SHAPE_ANY = 0, MK_SHAPE_H1024 = 1 };
 static inline int mk_shape_of(const MkDev &d) {
   const bool h1024 = d.H == 1024 && d.nh == 8 && d.dk == 128 && d.dv == 128 && d.nq == 8 && d.nkv == 2 &&
                      d.hd == 128 && d.J == 448 && d.r_in == 514 && d.C == 3072 && d.r_in_max == 544 &&
-                     d.x_o_len == 4160 && d.xm_len == 448;
+                     d.x_o_len == 2080 && d.xm_len == 448;
   return h1024 ? MK_SHAPE_H1024 : MK_SHAPE_ANY;
 }
 
