@@ -53,6 +53,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define NPAIR 4    // FFN role: gate/up row pairs per wave (four loads each)
 #define LMAX_D 8   // FFN role: loads per lane of one down-projection row group
 #define NWR 24     // registers (u32x4) of the larger role: 4 NPAIR + LMAX_D >= 2 NRG_IN + NRG_O
+#define NKV_PRE 6  // mixer role: attention key steps whose cached K and V rows are prefetched (2 NKV_PRE spare registers)
 #define LM_BATCH(NCOL) ((NCOL) == 1 ? 8 : 4)
 
 // ------------------------------------------------------------------------------ helpers
@@ -463,6 +464,12 @@ __device__ __forceinline__ void ld_gain16(const float *p, int H, int G, bool liv
 
 typedef const __attribute__((address_space(4))) MkLayerDev ConstLayer;
 
+// Byte offset of elements [d, d + 8) of the cached key or value row of position k, kv head kvh,
+// in the paged cache [page][kv head][MK_PAGE][hd] (page table in LDS).
+__device__ __forceinline__ uint32_t kv_off(const int *ptl, int k, int kvh, int nkv, int hd, int d) {
+  return (uint32_t)((((ptl[k / MK_PAGE] * nkv + kvh) * MK_PAGE + (k % MK_PAGE)) * hd + d) * 2);
+}
+
 // ------------------------------------------------------------------------------ the kernel
 template <int NCOL, int SH>
 __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
@@ -493,16 +500,12 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   float *work = xres + NCOL * H;                // [8192] phase scratch
   float *red = work + 8192;                     // [64] reductions
   int *flag = reinterpret_cast<int *>(red + 64);
-  // physical pages of this workgroup's attention key blocks lg, lg + 16, ... (32 keys each, two
-  // blocks per page), read once per launch: block j of the workgroup lies in page pgs[j]
-  int *pgs = flag + 16;                         // [32] (10240 positions / 32 / 16 = 20 blocks)
+  // the page table of the KV cache (logical page -> physical page), read once per launch
+  int *ptl = flag + 16;                         // [160] (10240 positions / 64)
   // RoPE cos / sin of this launch's positions [NCOL][hd / 2][2] (hd <= 128), loaded with the
   // embedding rows so that no attention layer waits for them
-  float *rl = reinterpret_cast<float *>(pgs + 32);
-  if (tid0 < 32) {
-    const int pi = (lg + tid0 * MK_NG) * MK_KBLK / MK_PAGE;
-    pgs[tid0] = (pi < m.max_pages) ? m.page_table[pi] : 0;
-  }
+  float *rl = reinterpret_cast<float *>(ptl + 160);
+  for (int i = tid0; i < m.max_pages; i += MK_THREADS) ptl[i] = m.page_table[i];
   if (tid0 == 0) {
     flag[0] = 0;
     uint32_t xcc;
@@ -541,11 +544,13 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // DeltaNet state of this wave for the next mixer phase, loaded with its weights
   float srow[2] = {0.f, 0.f}, hist[3] = {0.f, 0.f, 0.f}, grow = 0.f;
   float4 cwt = make_float4(0.f, 0.f, 0.f, 0.f);
-  // this lane's conv channel in D2: q/k channel w8 CPW + lane (lane < CPW) or, in lane 63, the v
-  // channel of the wave's row of S
-  const bool qkl = lane < CPW, vl = lane == 63 && w8 < RW;
-  const int chq = w8 * CPW + lane;
-  const int conv_ch = qkl ? ((chq < dk) ? x * dk + chq : nh * dk + x * dk + (chq - dk)) : 2 * nh * dk + x * dv + r0 + w8;
+  // A lane's conv channel in D2: q/k channel w8 CPW + lane (lane < CPW) or, in lane 63, the v
+  // channel of the wave's row of S.  (Computed where used from a lane index the compiler cannot
+  // see through, so that nothing derived from it is hoisted out of the layer loop.)
+  auto conv_channel = [&](int ln) {
+    const int cq = w8 * CPW + ln;
+    return (ln < CPW) ? ((cq < dk) ? x * dk + cq : nh * dk + x * dk + (cq - dk)) : 2 * nh * dk + x * dv + r0 + w8;
+  };
 
   // (each issue computes its per-lane offsets from a lane index the compiler cannot see through,
   // so they are not hoisted out of the layer loop and kept live -- and spilled -- across it)
@@ -553,7 +558,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     const bool live = l < m.n_layers;
-    ConstLayer &ly = layers[live ? l : 0];
+    // (read through readfirstlane: the layer index stays in a scalar register, so the table is
+    // read with scalar loads and every tile descriptor is wave-uniform)
+    ConstLayer &ly = layers[__builtin_amdgcn_readfirstlane(live ? l : 0)];
     const bool dn = ly.kind == 0;
     const int per = hd / RG_h;                     // row groups of one attention head
     const int nrg = !live ? 0 : dn ? ((x < nh) ? r_in / RG_h : 0) : ((x < nq) ? 3 * per : 0);
@@ -584,6 +591,21 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       const int rg = wx + r * XW;
       wr[2 * NRG_IN + r] = __builtin_amdgcn_raw_buffer_load_b128(ro, rg < ngo ? (uint32_t)((rg * 64 + lane) * 16) : OOB_OFF, 0, AUX_NT);
     }
+    // attention: this lane's cached K and V rows of the first NKV_PRE key steps (keys lg + 16 ks,
+    // slot ks = step * MK_WAVES * kpw + w8 * kpw + lane / lpk; 16 bytes of one row per lane)
+    {
+      const bool at = live && !dn && x < nq;
+      const int lpk = hd / 8, kpw = 64 / lpk;
+      const __amdgpu_buffer_rsrc_t krs = tile_rsrc(ly.kc, at ? 0x7fffffffu : 0u);
+      const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(ly.vc, at ? 0x7fffffffu : 0u);
+#pragma unroll
+      for (int st = 0; st < NKV_PRE; ++st) {
+        const int ks = st * MK_WAVES * kpw + w8 * kpw + lane / lpk, k = lg + MK_NG * ks;
+        const uint32_t off = (k < pos0) ? kv_off(ptl, k, kvh, nkv, hd, (lane % lpk) * 8) : OOB_OFF;
+        wr[2 * NRG_IN + NRG_O + 2 * st] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+        wr[2 * NRG_IN + NRG_O + 2 * st + 1] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+      }
+    }
     // this wave's DeltaNet state: its row of S, the conv taps and history of its lane's channel,
     // the gated-norm gain of its row
     const bool sdn = live && dn && x < nh;
@@ -593,7 +615,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     srow[1] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsS, (64 + lane) * 4, 0, AUX_DEV));
     // (the descriptors are wave-uniform; a lane without a channel reads zeros through an
     // out-of-range offset)
-    const bool chl = qkl || vl;
+    const bool chl = lane < CPW || (lane == 63 && w8 < RW);
+    const int conv_ch = conv_channel(lane);
     const __amdgpu_buffer_rsrc_t rc = tile_rsrc(ly.dn_conv, sdn ? (uint32_t)(nconv * 16) : 0u);
     const u32x4 wt = __builtin_amdgcn_raw_buffer_load_b128(rc, chl ? (uint32_t)(conv_ch * 16) : OOB_OFF, 0, 0);
     cwt = make_float4(__uint_as_float(wt.x), __uint_as_float(wt.y), __uint_as_float(wt.z), __uint_as_float(wt.w));
@@ -612,7 +635,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     const bool live = l < m.n_layers;
-    ConstLayer &ly = layers[live ? l : 0];
+    // (read through readfirstlane: the layer index stays in a scalar register, so the table is
+    // read with scalar loads and every tile descriptor is wave-uniform)
+    ConstLayer &ly = layers[__builtin_amdgcn_readfirstlane(live ? l : 0)];
     // gate/up pairs j = wx + pr XW of FFN slice x: rows 2j, 2j + 1 of the slice's tile, contiguous
     // (two row groups when a row group is one row, one when it is two): nl loads per lane
     const int nl = 2 * L_h / RG_h;
@@ -674,11 +699,12 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       rl[i * 2 + 1] = r.y;
     }
   }
+  lbar();   // (the first mixer issue reads the page table from LDS)
   if (mixer) issue_mixer(0);
   else issue_ffn(0);
-  lbar();
 
   for (li = 0; li < m.n_layers; ++li) {
+    li = __builtin_amdgcn_readfirstlane(li);   // keep the layer index (and all derived from it) scalar
     ConstLayer &ly = layers[li];
     // A per-layer copy of the thread index the compiler cannot see through: address
     // arithmetic derived from it stays inside the layer loop instead of being hoisted out
@@ -750,6 +776,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           MK_TRACE_POINT(li, 3);
           // conv + SiLU of this lane's channel for every column: tap i meets the token 3 - i steps
           // before the column (earlier columns of this forward, else the history)
+          const bool qkl = lane < CPW, vl = lane == 63 && w8 < RW;
+          const int chq = w8 * CPW + lane, conv_ch = conv_channel(lane);
           float raw[NCOL], cv[NCOL];
 #pragma unroll
           for (int c = 0; c < NCOL; ++c) raw[c] = (c < ncol) ? (qkl ? gqk[c * 2 * dk + chq] : vl ? gvv[c * RW + w8] : 0.f) : 0.f;
@@ -931,44 +959,62 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             }
           }
           {
+            // Split-KV partials: this workgroup takes keys lg, lg + 16, lg + 32, ... of each query
+            // position (balanced over the 16 workgroups).  Key slot ks is key lg + 16 ks; a step of
+            // the workgroup covers MK_WAVES * kpw slots, kpw per wave, lpk lanes per key with 8
+            // dimensions each.  Cached keys and values of the first NKV_PRE steps are in registers
+            // (loaded with this layer's weights), later steps load them here.  This forward's own
+            // positions (at most one per column in this workgroup, as ncol < 16) come from LDS.
             float *sc = work + NCOL * 3 * hd;      // scores of my keys [<= 640]
             float *pv = sc + 640;                  // [MK_WAVES][hd] partial P.V per wave
             float *mx = pv + MK_WAVES * hd;        // [2]: max, sum
             const float scale = 1.f / sqrtf((float)hd);
-            const int lpk = hd / 8;                // lanes per key
-            const int kpw = 64 / lpk;              // keys per wave step
+            const int lpk = hd / 8, kpw = 64 / lpk, spw = MK_WAVES * kpw;
+            const int d0 = (lane % lpk) * 8, kslot = w8 * kpw + lane / lpk;
             const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
             const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
+            // cached keys of this workgroup: slots [0, ncache)
+            const int ncache = (pos0 > lg) ? (pos0 - 1 - lg) / MK_NG + 1 : 0;
+            const int nstc = (ncache + spw - 1) / spw;
 #pragma unroll 1
             for (int c = 0; c < ncol; ++c) {
               const int P = pos0 + c;             // query position; keys 0..P
-              const int nblk = P / MK_KBLK + 1;
-              const int myblk = (nblk > lg) ? (nblk - lg + MK_NG - 1) / MK_NG : 0;
-              const int nk = (myblk == 0) ? 0 : (myblk - 1) * MK_KBLK + min(MK_KBLK, P + 1 - (lg + (myblk - 1) * MK_NG) * MK_KBLK);
-              const float *q = qkv + c * 3 * hd;
-              // scores: key slot ks -> block lg + (ks / 32) * 16, offset ks % 32.  Cached keys come
-              // through branch-free buffer loads (absent ones with an out-of-range offset), so the
-              // loads of several steps can be in flight together; this forward's keys come from LDS.
-#pragma unroll 2
-              for (int base = w8 * kpw; base < nk; base += MK_WAVES * kpw) {
-                const int ks = base + lane / lpk, j = ks / MK_KBLK;
-                const int tpos = (lg + j * MK_NG) * MK_KBLK + (ks % MK_KBLK);
-                const int d0 = (lane % lpk) * 8;
-                const bool cached = ks < nk && tpos < pos0;
-                const uint32_t off = cached ? (uint32_t)((((pgs[j] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + d0) * 2) : OOB_OFF;
-                float kf[8];
-                unpack8(__builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0), kf);
-                // this forward's keys: read from LDS for every slot (row 0 where unused) and selected,
-                // so the loop body stays one block and the loads of several steps issue together
-                const bool cur = ks < nk && !cached;
-                const float *kk = qkv + (cur ? tpos - pos0 : 0) * 3 * hd + hd + d0;
+              const int nk = (P >= lg) ? (P - lg) / MK_NG + 1 : 0;
+              // this forward's key of this workgroup, if any: position kc_ in [pos0, P], slot nk - 1
+              const int kc_ = lg + MK_NG * (nk - 1);
+              const bool hascur = nk > 0 && kc_ >= pos0;
+              float qv[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) kf[i] = cur ? kk[i] : kf[i];
+              for (int i = 0; i < 8; ++i) qv[i] = qkv[c * 3 * hd + d0 + i];
+              auto score = [&](int ks, const float (&kf)[8]) {
                 float sdot = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) sdot = fmaf(q[d0 + i], kf[i], sdot);
+                for (int i = 0; i < 8; ++i) sdot = fmaf(qv[i], kf[i], sdot);
                 sdot = group_sum(sdot, lpk);
-                if (ks < nk && (lane % lpk) == 0) sc[ks] = sdot * scale;
+                if (ks < ncache && (lane % lpk) == 0) sc[ks] = sdot * scale;
+              };
+#pragma unroll
+              for (int st = 0; st < NKV_PRE; ++st) {
+                if (st < nstc) {
+                  float kf[8];
+                  unpack8(wr[2 * NRG_IN + NRG_O + 2 * st], kf);
+                  score(st * spw + kslot, kf);
+                }
+              }
+#pragma unroll 1
+              for (int st = NKV_PRE; st < nstc; ++st) {
+                const int ks = st * spw + kslot;
+                float kf[8];
+                unpack8(__builtin_amdgcn_raw_buffer_load_b128(krs, ks < ncache ? kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : OOB_OFF, 0, 0), kf);
+                score(ks, kf);
+              }
+              if (hascur && w8 == 0 && lane < lpk) {   // this forward's key: from LDS
+                const float *kk = qkv + (kc_ - pos0) * 3 * hd + hd + d0;
+                float sdot = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sdot = fmaf(qv[i], kk[i], sdot);
+                sdot = group_sum(sdot, lpk);
+                if (lane == 0) sc[nk - 1] = sdot * scale;
               }
               lbar();
               if (w8 == 0) {
@@ -978,52 +1024,72 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 for (int off = 32; off > 0; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off, 64));
                 float ls = 0.f;
                 for (int i = lane; i < nk; i += 64) {
-                  const float p = __expf(sc[i] - mv);
-                  sc[i] = p;
-                  ls += p;
+                  const float pe = __expf(sc[i] - mv);
+                  sc[i] = pe;
+                  ls += pe;
                 }
                 ls = wave_sum(ls);
                 if (lane == 0) { mx[0] = mv; mx[1] = ls; }
               }
               lbar();
-              // P.V: wave w takes keys w, w+8, ...; lane l takes dims l dpl .. +dpl (one 2- or 4-byte
-              // load per key, branch-free as above)
-              {
-                const int dpl = hd / 64;   // 1 or 2
-                float acc[2] = {0.f, 0.f};
-#pragma unroll 4
-                for (int ks = w8; ks < nk; ks += MK_WAVES) {
-                  const int j = ks / MK_KBLK, tpos = (lg + j * MK_NG) * MK_KBLK + (ks % MK_KBLK);
-                  const bool cached = tpos < pos0;
-                  const uint32_t off = cached ? (uint32_t)((((pgs[j] * nkv + kvh) * MK_PAGE + (tpos % MK_PAGE)) * hd + lane * dpl) * 2) : OOB_OFF;
-                  float v0, v1;
-                  if (dpl == 2) {
-                    const uint32_t raw2 = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, 0);
-                    v0 = __uint_as_float(raw2 << 16);
-                    v1 = __uint_as_float(raw2 & 0xffff0000u);
-                  } else {
-                    v0 = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, 0) << 16);
-                    v1 = 0.f;
-                  }
-                  const float *vv = qkv + (cached ? 0 : tpos - pos0) * 3 * hd + 2 * hd + lane * dpl;
-                  const float l0 = vv[0], l1 = (dpl == 2) ? vv[1] : 0.f;
-                  v0 = cached ? v0 : l0;
-                  v1 = cached ? v1 : l1;
-                  const float p = sc[ks];
-                  acc[0] = fmaf(p, v0, acc[0]);
-                  acc[1] = fmaf(p, v1, acc[1]);
+              // P.V over the same slots: each lane accumulates its 8 dimensions
+              float acc[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+              auto pvacc = [&](int ks, const float (&vf)[8]) {
+                const float pe = (ks < ncache) ? sc[ks < ncache ? ks : 0] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(pe, vf[i], acc[i]);
+              };
+#pragma unroll
+              for (int st = 0; st < NKV_PRE; ++st) {
+                if (st < nstc) {
+                  float vf[8];
+                  unpack8(wr[2 * NRG_IN + NRG_O + 2 * st + 1], vf);
+                  pvacc(st * spw + kslot, vf);
                 }
-                pv[w8 * hd + lane * dpl] = acc[0];
-                if (dpl == 2) pv[w8 * hd + lane * dpl + 1] = acc[1];
+              }
+#pragma unroll 1
+              for (int st = NKV_PRE; st < nstc; ++st) {
+                const int ks = st * spw + kslot;
+                float vf[8];
+                unpack8(__builtin_amdgcn_raw_buffer_load_b128(vrs, ks < ncache ? kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : OOB_OFF, 0, 0), vf);
+                pvacc(ks, vf);
+              }
+              // this forward's value, from LDS, added by the lanes that own its slot in the step order
+              // (as a cached key of a later decode step it is accumulated there: same additions, same
+              // order, so verify and sequential decode agree bit for bit)
+              const int kcs = (nk - 1) % spw;
+              if (hascur && w8 == kcs / kpw && lane / lpk == kcs % kpw) {
+                const float pe = sc[nk - 1];
+                const float *vv = qkv + (kc_ - pos0) * 3 * hd + 2 * hd + d0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(pe, vv[i], acc[i]);
+              }
+              // sum over the kpw key groups of the wave (lanes l, l + lpk, ...), then over the waves
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                float v = acc[i];
+                if (lpk == 16) {
+                  v = swap_add32(v, v);
+                  v = swap_add16(v, v);
+                } else {
+                  for (int o = lpk; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+                }
+                acc[i] = v;
+              }
+              if (lane < lpk) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pv[w8 * hd + d0 + i] = acc[i];
               }
               lbar();
               const int plen = hd + 2;
               uint2 *dst = xo + c * x_o_len + lg * plen;
               for (int d = tid; d < hd; d += MK_THREADS) {
-                float acc = pv[d];
+                float a2 = pv[d];
 #pragma unroll 1
-                for (int ww = 1; ww < MK_WAVES; ++ww) acc += pv[ww * hd + d];
-                pub_xcd(dst + 2 + d, acc, tg);
+                for (int ww = 1; ww < MK_WAVES; ++ww) a2 += pv[ww * hd + d];
+                pub_xcd(dst + 2 + d, a2, tg);
               }
               if (tid == 0) {
                 pub_xcd(dst + 0, nk > 0 ? mx[0] : -INFINITY, tg);
