@@ -64,6 +64,14 @@ __device__ __forceinline__ void split_store4(float4 v, uint16_t *hi, uint16_t *l
   *reinterpret_cast<uint2 *>(hi) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
   *reinterpret_cast<uint2 *>(lo) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
 }
+// GEMM operand layout (the A operand of every prefill projection): a [rows][Kc] bf16 matrix (Kc a
+// multiple of 32) as 16 x 32 blocks of 1 KiB, block (rows 16 rb .., columns 32 kb ..) at element
+// (rb Kc / 32 + kb) 512; within a block, row r's 8-element group q (columns 8 q ..) at 16-byte slot
+// 4 r + (q ^ ((r >> 1) & 3)).  Rows are padded to a multiple of 16 (pad rows are never used).
+__device__ __forceinline__ size_t ablk(int t, int k, int Kc) {
+  const int r = t & 15, q = (k >> 3) & 3;
+  return ((size_t)(t >> 4) * (Kc >> 5) + (k >> 5)) * 512 + (r * 4 + (q ^ ((r >> 1) & 3))) * 8 + (k & 7);
+}
 __device__ __forceinline__ float sigmoidf_(float x) {
   if (x >= 0.f) return 1.f / (1.f + expf(-x));
   const float e = expf(x);
@@ -182,9 +190,9 @@ __global__ void __launch_bounds__(PF_THREADS) pf_embed(const uint16_t *embed, co
   for (int i = threadIdx.x; i < H; i += PF_THREADS) X[(size_t)t * H + i] = bf2f(embed[(size_t)id * H + i]);
 }
 
-// h = x / sqrt(mean(x^2) + eps) * g, written as a bf16 hi + lo pair (row stride ld)
+// h = x / sqrt(mean(x^2) + eps) * g, written as a bf16 hi + lo pair in the operand block layout (Kc = H)
 __global__ void __launch_bounds__(PF_THREADS) pf_norm_split(const float *X, const float *g, int H, float eps,
-                                                            uint16_t *oh, uint16_t *ol, int ld) {
+                                                            uint16_t *oh, uint16_t *ol) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   const float *x = X + (size_t)t * H;
@@ -192,29 +200,30 @@ __global__ void __launch_bounds__(PF_THREADS) pf_norm_split(const float *X, cons
   for (int i = threadIdx.x; i < H; i += PF_THREADS) s = fmaf(x[i], x[i], s);
   const float den = sqrtf(block_sum(s, red) / (float)H + eps);
   for (int i = threadIdx.x; i < H; i += PF_THREADS)
-    split_store(x[i] / den * g[i], oh + (size_t)t * ld + i, ol + (size_t)t * ld + i);
+    split_store(x[i] / den * g[i], oh + ablk(t, i, H), ol + ablk(t, i, H));
 }
 
 // ------------------------------------------------------------------------------ MFMA GEMM
-// C[M][N] = A[M][K] . W[N][K]^T with A given as bf16 hi + lo ([M][lda]) and W in the tile
+// C[M][N] = A[M][K] . W[N][K]^T with A given as bf16 hi + lo (operand block layout) and W in the tile
 // format of mk_layout.h.  W rows come from up to three row segments (tile wb[s] holds rows
 // [wend[s-1], wend[s]) ), and along K from segments of ks columns, kstride elements apart
 // (one tile [rows][ks] per segment).  One wave computes MT x NT 16x16 blocks with
 // v_mfma_f32_16x16x32_bf16 (lane l: A row l%16 and B column l%16 with k = 8 (l/16) .. +8;
 // result rows 4 (l/16) .. +4 of column l%16).
 struct PfGemm {
-  const uint16_t *ah, *al;
-  int lda, M, N, K;
+  const uint16_t *ah, *al;            // A as bf16 hi + lo in the GEMM operand block layout (Kc = K)
+  int M, N, K;
   const uint16_t *wb[3];
   int wend[3];
   int ks, kstride;
   float *c;
   int ldc;
-  uint16_t *oh, *ol;
+  uint16_t *oh, *ol;                  // EPI_SWIGLU: output in the operand block layout, Kc = ldo
   int ldo;
-  int kper;            // K columns per split (blockIdx.z); == K without split-K
+  int kper;            // K columns per split; == K without split-K
   float *part;         // EPI_PART: split z writes part[z][row][ldc]
   size_t part_stride;  // elements per split
+  int tn, tm, tz;      // tiles along N, along M, and K splits (the grid is their product)
 };
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PART = 3 };
 
@@ -224,118 +233,138 @@ __device__ __forceinline__ int tileG(int K) {
   return g;
 }
 
-// Workgroup tile BM x BN (BM = WGM*MT*16, BN = WGN*NT*16, WGM*WGN waves), K in stages of 64.
-// Each stage of A (hi and lo) and W is copied into LDS once per workgroup (16-byte loads: 128
-// contiguous bytes per row), double-buffered: the next stage's loads are in flight while the
-// MFMAs of the current one run.  LDS rows are padded to 80 elements (10 units of 16 bytes): a
-// 16-byte LDS read is served for 16 lanes at a time, and with this row stride the fragment reads
-// (16 rows, one 16-byte column per group of 16 lanes) hit distinct banks, which a 9-unit stride
-// does not (measured: twice the LDS time).
-constexpr int GBK = 64, GLD = GBK + 16;
+// Workgroup tile BM x BN (BM = WGM*MT*16, BN = WGN*NT*16, WGM*WGN waves), K in stages of 32.
+// Each stage of A (hi and lo) and W is copied into LDS by direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l of a wave writes 16 bytes at LDS base + 16 l), in 1 KiB blocks of
+// 16 rows x 32 k, in a ring of NS stages: the loads of stage st + NS are issued while stage st + 1
+// is read, so NS - 1 stages are in flight and no register holds a load in flight.  Within a block,
+// row r's 8-element group q sits at slot 4 r + (q ^ ((r >> 1) & 3)): the fragment reads (lane l:
+// row l % 16, group l / 16) of each 8 consecutive lanes then cover all 32 banks once.  A arrives in
+// that block layout already (written so by the kernels producing GEMM operands); W rows are
+// gathered from the tile format (4 lanes per row, 64 contiguous bytes each).
+constexpr int GBK = 32;
 
-template <int EPI, int MT, int NT, int WGM, int WGN>
+template <int EPI, int MT, int NT, int WGM, int WGN, int NS>
 __global__ void __launch_bounds__(WGM * WGN * 64) pf_gemm(PfGemm g) {
-  constexpr int BM = WGM * MT * 16, BN = WGN * NT * 16, NTHR = WGM * WGN * 64;
-  constexpr int NA = 2 * BM * 8 / NTHR, NB = BN * 8 / NTHR;   // 16-byte loads per thread and stage
-  extern __shared__ uint16_t gsm[];
-  // stage buffer b: A at gsm + b * 2 BM GLD ([hi/lo][BM][GLD]), W at gsm + 4 BM GLD + b * BN GLD
+  constexpr int NW = WGM * WGN, BM = WGM * MT * 16, BN = WGN * NT * 16;
+  constexpr int NBA = BM / 16, NBB = BN / 16, NBLK = 2 * NBA + NBB;   // 1 KiB blocks per stage
+  static_assert(NBLK % NW == 0, "every wave issues the same number of block loads");
+  constexpr int DPW = NBLK / NW;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char gsm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / WGN, wn = w % WGN;
-  const int bm0 = blockIdx.y * BM, bn0 = blockIdx.x * BN;
-  const int G = tileG(g.ks), L = g.ks / 8 / G, RG = 64 / G, G8 = G * 8;
-  // staging: thread -> chunks c = tid + i*256 of A ([hi/lo][row][kg]) and of B ([row][kg])
-  const uint16_t *asrc[NA];
-  int aoff[NA];
+  // Workgroup b runs on XCD b % 8.  XCD x takes a contiguous block of the tiles ordered (split,
+  // N tile, M tile), so that each weight slice (and, with split-K, each activation slab) is pulled
+  // into one XCD's L2 only.
+  const int ntile = g.tn * g.tm * g.tz, xcd = blockIdx.x & 7, q8 = ntile >> 3, r8 = ntile & 7;
+  const int tile = xcd * q8 + min(xcd, r8) + (int)(blockIdx.x >> 3);
+  const int tmi = tile % g.tm, tni = (tile / g.tm) % g.tn, tzi = tile / (g.tm * g.tn);
+  const int bm0 = tmi * BM, bn0 = tni * BN;
+  const int kbeg = tzi * g.kper, nst = g.kper / GBK, kb0 = kbeg / GBK, kbn = g.K / GBK;
+  // this lane's loads: block b = w + i NW of a stage (A hi blocks, A lo blocks, then W blocks)
+  const int drow = lane >> 2, dkg = (lane & 3) ^ ((drow >> 1) & 3);
+  const uint16_t *src[DPW];
+  const int G = tileG(g.ks), L = g.ks / 8 / G, RG = 64 / G, G8 = G * 8, lg8 = __builtin_ctz(G8);
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int c = tid + i * NTHR, hl = c / (BM * 8), rem = c % (BM * 8), row = rem / 8, kg = rem % 8;
-    asrc[i] = (hl ? g.al : g.ah) + (size_t)(bm0 + row) * g.lda + kg * 8;
-    aoff[i] = (hl * BM + row) * GLD + kg * 8;
+  for (int i = 0; i < DPW; ++i) {
+    const int b = w + i * NW;
+    if (b < 2 * NBA) {
+      const int hl = b / NBA, rb = b % NBA;
+      src[i] = (hl ? g.al : g.ah) + ((size_t)(bm0 / 16 + rb) * kbn + kb0) * 512 + lane * 8;
+    } else {
+      const int n = min(bn0 + (b - 2 * NBA) * 16 + drow, g.N - 1);
+      const int s = n < g.wend[0] ? 0 : (n < g.wend[1] ? 1 : 2);
+      const int r = n - (s == 0 ? 0 : g.wend[s - 1]);
+      src[i] = g.wb[s] + (r / RG) * L * 512 + (r % RG) * G8;
+    }
   }
-  const uint16_t *bsrc[NB];
-  int brow[NB], bkg[NB], boff[NB];
+  int bj = kbeg + dkg * 8, bksg = bj / g.ks;   // k position of this lane's next W load
+  bj -= bksg * g.ks;
+  auto issue = [&](int st) {
+    const int buf = st % NS, sa = min(st, nst - 1);
+    const size_t boff = (size_t)bksg * g.kstride + ((bj >> lg8) << 9) + (bj & (G8 - 1));
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int c = tid + i * NTHR, row = c / 8, kg = c % 8;
-    const int n = min(bn0 + row, g.N - 1);
-    const int s = n < g.wend[0] ? 0 : (n < g.wend[1] ? 1 : 2);
-    const int r = n - (s == 0 ? 0 : g.wend[s - 1]);
-    bsrc[i] = g.wb[s] + (r / RG) * L * 512 + (r % RG) * G8;
-    brow[i] = r;
-    bkg[i] = kg * 8;
-    boff[i] = row * GLD + kg * 8;
-  }
-  (void)brow;
-  u32x4 ra0[NA], rb0[NB], ra1[NA], rb1[NB];
-  auto fetch = [&](int k0, u32x4 (&ra)[NA], u32x4 (&rb)[NB]) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(asrc[i] + k0);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int k = k0 + bkg[i];
-      const int ksg = k / g.ks, j = k - ksg * g.ks;
-      rb[i] = *reinterpret_cast<const u32x4 *>(bsrc[i] + (size_t)ksg * g.kstride + (j / G8) * 512 + (j & (G8 - 1)));
+    for (int i = 0; i < DPW; ++i) {
+      const int b = w + i * NW;
+      const uint16_t *p = b < 2 * NBA ? src[i] + (size_t)sa * 512 : src[i] + boff;
+      __builtin_amdgcn_global_load_lds((const void *)p,
+                                       (__attribute__((address_space(3))) void *)(gsm + (buf * NBLK + b) * 1024), 16, 0, 0);
+    }
+    if (st < nst - 1) {
+      bj += GBK;
+      if (bj >= g.ks) { bj -= g.ks; ++bksg; }
     }
   };
-  auto stash = [&](int buf, const u32x4 (&ra)[NA], const u32x4 (&rb)[NB]) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) *reinterpret_cast<u32x4 *>(gsm + buf * 2 * BM * GLD + aoff[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4 *>(gsm + 4 * BM * GLD + buf * BN * GLD + boff[i]) = rb[i];
-  };
-  f32x4 acc[MT][NT];
+  f32x4 acc[MT][NT], acl[MT][NT];   // hi and lo products in separate accumulators (no MFMA waits on its neighbour)
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf) {
-    const uint16_t *Ab = gsm + buf * 2 * BM * GLD, *Bb = gsm + 4 * BM * GLD + buf * BN * GLD;
+    for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = acl[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fpos = ((lane & 15) * 4 + ((lane >> 4) ^ (((lane & 15) >> 1) & 3))) * 16;
+  typedef bf16x8 FragM[MT];
+  typedef bf16x8 FragN[NT];
+  // Per stage, in this order with nothing moved across: the next stage's fragment reads one at a
+  // time, each followed by MPR of the current stage's MFMAs (the loads of a later stage after the
+  // second read), so that no wave queues all its LDS reads ahead of its first MFMA.
+  constexpr int NRD = 2 * MT + NT, NMF = 2 * MT * NT, MPR = NMF / NRD;
+  auto step = [&](int stn, int sti, FragM &fan, FragM &fln, FragN &fbn, const FragM &fa, const FragM &fl, const FragN &fb) {
+    const unsigned char *sb = gsm + (stn % NS) * NBLK * 1024 + fpos;
+    int mf = 0;
 #pragma unroll
-    for (int kk = 0; kk < GBK; kk += 32) {
-      const int kc = kk + (lane >> 4) * 8;
-      bf16x8 fa[MT], fl[MT], fb[NT];
+    for (int j = 0; j < NRD; ++j) {
+      if (j < MT) fan[j] = *reinterpret_cast<const bf16x8 *>(sb + (wm * MT + j) * 1024);
+      else if (j < 2 * MT) fln[j - MT] = *reinterpret_cast<const bf16x8 *>(sb + (NBA + wm * MT + j - MT) * 1024);
+      else fbn[j - 2 * MT] = *reinterpret_cast<const bf16x8 *>(sb + (2 * NBA + wn * NT + j - 2 * MT) * 1024);
+      if (j == 1) issue(sti);
+      const int mend = (j == NRD - 1) ? NMF : mf + MPR;
 #pragma unroll
-      for (int mi = 0; mi < MT; ++mi) {
-        const int row = wm * MT * 16 + mi * 16 + (lane & 15);
-        fa[mi] = *reinterpret_cast<const bf16x8 *>(Ab + row * GLD + kc);
-        fl[mi] = *reinterpret_cast<const bf16x8 *>(Ab + (BM + row) * GLD + kc);
+      for (; mf < mend; ++mf) {
+        const int lo = mf >= MT * NT, q = lo ? mf - MT * NT : mf, mi = q / NT, ni = q % NT;
+        if (lo) acl[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[mi], fb[ni], acl[mi][ni], 0, 0, 0);
+        else acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
       }
-#pragma unroll
-      for (int ni = 0; ni < NT; ++ni)
-        fb[ni] = *reinterpret_cast<const bf16x8 *>(Bb + (wn * NT * 16 + ni * 16 + (lane & 15)) * GLD + kc);
-      // all hi terms first, then all lo terms: consecutive MFMAs never share an accumulator
-#pragma unroll
-      for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NT; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-#pragma unroll
-      for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NT; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fl[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Stage st sits in LDS buffer st & 1 while stage st + 1 is in one register set and stage st + 2
-  // is being loaded into the other: each load has two stages of MFMAs to land.  Past the last
-  // stage the fetches re-read it (branch-free) and are never used.
-  const int kbeg = blockIdx.z * g.kper, nst = g.kper / GBK;
-  auto kof = [&](int st) { return kbeg + min(st, nst - 1) * GBK; };
-  fetch(kof(0), ra0, rb0);
-  stash(0, ra0, rb0);
-  fetch(kof(1), ra1, rb1);
-  __syncthreads();
-  for (int st = 0; st < nst; st += 2) {
-    fetch(kof(st + 2), ra0, rb0);
-    compute(0);
-    stash(1, ra1, rb1);
-    __syncthreads();
-    if (st + 1 >= nst) break;
-    fetch(kof(st + 3), ra1, rb1);
-    compute(1);
-    stash(0, ra0, rb0);
-    __syncthreads();
+  // vmcnt(n) with lgkmcnt(0): the encoding is vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  constexpr int WPRO = (NS - 1) * DPW, WLOOP = (NS - 2) * DPW;
+  constexpr int ENC_PRO = 0x0070 | (WPRO & 15) | ((WPRO >> 4) << 14);
+  constexpr int ENC_LOOP = 0x0070 | (WLOOP & 15) | ((WLOOP >> 4) << 14);
+  static_assert(WPRO < 64, "vmcnt range");
+#pragma unroll
+  for (int s = 0; s < NS; ++s) issue(s);
+  __builtin_amdgcn_s_waitcnt(ENC_PRO);
+  __builtin_amdgcn_s_barrier();
+  FragM a0, l0, a1, l1;
+  FragN b0, b1;
+  {
+    const unsigned char *sb = gsm + fpos;
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      a0[j] = *reinterpret_cast<const bf16x8 *>(sb + (wm * MT + j) * 1024);
+      l0[j] = *reinterpret_cast<const bf16x8 *>(sb + (NBA + wm * MT + j) * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) b0[j] = *reinterpret_cast<const bf16x8 *>(sb + (2 * NBA + wn * NT + j) * 1024);
   }
+  // Iteration st: wait until stage st + 1 has landed (every wave's loads: vmcnt, then the barrier)
+  // and every wave holds stage st in registers (lgkmcnt(0) before the barrier); read stage st + 1,
+  // refill stage st's buffer with stage st + NS, multiply stage st.  Loads past the last stage
+  // re-read it and are never used.
+  for (int st = 0; st < nst; st += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(ENC_LOOP);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    step(st + 1, st + NS, a1, l1, b1, a0, l0, b0);
+    if (st + 1 >= nst) break;
+    __builtin_amdgcn_s_waitcnt(ENC_LOOP);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    step(st + 2, st + NS + 1, a0, l0, b0, a1, l1, b1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no load into LDS may outlive the workgroup
   // epilogue
   const int m0 = bm0 + wm * MT * 16, n0 = bn0 + wn * NT * 16;
 #pragma unroll
@@ -346,17 +375,17 @@ __global__ void __launch_bounds__(WGM * WGN * 64) pf_gemm(PfGemm g) {
       for (int i = 0; i < 4; ++i) {
         const int row = m0 + mi * 16 + (lane >> 4) * 4 + i;
         const int col = n0 + ni * 16 + (lane & 15);
-        const float v = acc[mi][ni][i];
+        const float v = acc[mi][ni][i] + acl[mi][ni][i];
         if (EPI == EPI_SWIGLU) {
           // columns 2j (gate) and 2j+1 (up) of one intermediate index sit in lanes l, l^1 (DPP swap)
           const float u = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
           if ((lane & 1) == 0 && row < g.M && col < g.N) {
-            const size_t o = (size_t)row * g.ldo + (col >> 1);
+            const size_t o = ablk(row, col >> 1, g.ldo);
             split_store(__fdividef(v, 1.f + __expf(-v)) * u, g.oh + o, g.ol + o);   // SiLU(gate) * up
           }
         } else if (row < g.M && col < g.N) {
           if (EPI == EPI_PART) {
-            g.part[blockIdx.z * g.part_stride + (size_t)row * g.ldc + col] = v;
+            g.part[tzi * g.part_stride + (size_t)row * g.ldc + col] = v;
           } else {
             float *cp = g.c + (size_t)row * g.ldc + col;
             if (EPI == EPI_RESID) *cp = *cp + v;
@@ -367,11 +396,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64) pf_gemm(PfGemm g) {
 }
 
 // X += sum of the split-K partials (split order), then, when g is given, the RMSNorm of the new row
-// as a bf16 hi + lo pair (the operand of the next projection): one pass over the row instead of
-// a reduction kernel and a norm kernel.  One workgroup per row, float4 per thread (H <= 1024).
+// as a bf16 hi + lo pair in the operand block layout (Kc = H, the operand of the next projection):
+// one pass over the row instead of a reduction kernel and a norm kernel.  One workgroup per row,
+// float4 per thread (H <= 1024).
 __global__ void __launch_bounds__(PF_THREADS) pf_reduce_norm(float *X, const float *part, int nsplit, size_t stride,
                                                              int H, const float *g, float eps, uint16_t *oh,
-                                                             uint16_t *ol, int ld) {
+                                                             uint16_t *ol) {
   __shared__ float red[4];
   const int row = blockIdx.x, n4 = threadIdx.x;
   const bool on = n4 < H / 4;
@@ -396,7 +426,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_reduce_norm(float *X, const flo
   const float den = sqrtf(block_sum(sq, red) / (float)H + eps);
   if (on) {
     const float4 gv = reinterpret_cast<const float4 *>(g)[n4];
-    const size_t o = (size_t)row * ld + n4 * 4;
+    const size_t o = ablk(row, n4 * 4, H);
     split_store4(make_float4(xv.x / den * gv.x, xv.y / den * gv.y, xv.z / den * gv.z, xv.w / den * gv.w), oh + o, ol + o);
   }
 }
@@ -833,10 +863,11 @@ __global__ void __launch_bounds__(SCAN_THREADS) pf_dn_scan(PfScan s) {
   }
 }
 
-// gated RMSNorm per (token, head): y = o / sqrt(mean(o^2) + eps) * g * SiLU(z), as bf16 hi + lo
-// (z of head h, token t: Pz[t NP + h r_in + i], straight from the in-projection outputs)
+// gated RMSNorm per (token, head): y = o / sqrt(mean(o^2) + eps) * g * SiLU(z), as bf16 hi + lo in
+// the operand block layout (Kc = nh dv; z of head h, token t: Pz[t NP + h r_in + i], straight from
+// the in-projection outputs)
 __global__ void __launch_bounds__(PF_THREADS) pf_dn_gnorm(const float *o, const float *Pz, int NP, int r_in, const float *gn,
-                                                          int nh, int dv, float eps, uint16_t *oh, uint16_t *ol, int ld) {
+                                                          int nh, int dv, float eps, uint16_t *oh, uint16_t *ol) {
   const int t = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int h = w; h < nh; h += PF_THREADS / 64) {
     const float *oo = o + (size_t)t * nh * dv + h * dv;
@@ -845,7 +876,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_dn_gnorm(const float *o, const 
     for (int i = lane; i < dv; i += 64) sq = fmaf(oo[i], oo[i], sq);
     const float den = sqrtf(wave_sum(sq) / (float)dv + eps);
     for (int i = lane; i < dv; i += 64)
-      split_store(oo[i] / den * gn[i] * siluf_(zz[i]), oh + (size_t)t * ld + h * dv + i, ol + (size_t)t * ld + h * dv + i);
+      split_store(oo[i] / den * gn[i] * siluf_(zz[i]), oh + ablk(t, h * dv + i, nh * dv), ol + ablk(t, h * dv + i, nh * dv));
   }
 }
 
@@ -859,8 +890,7 @@ struct PfAtt {
   uint16_t *kc, *vc;          // [pages][nkv][PAGE][hd]
   float *aq;                  // [PT][nq hd]
   int nq, nkv, hd;
-  uint16_t *oh, *ol;          // [PT][ld]
-  int ld;
+  uint16_t *oh, *ol;          // output, operand block layout with Kc = nq hd
 };
 
 __device__ __forceinline__ size_t kv_off(const PfAtt &a, int p, int kvh) {
@@ -1084,7 +1114,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att_mfma(PfAtt a) {
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const size_t off = (size_t)qrow * a.ld + hq * HD + d * 16 + 4 * g4 + i;
+        const size_t off = ablk(qrow, hq * HD + d * 16 + 4 * g4 + i, a.nq * HD);
         split_store(o[d][i] / lrow, a.oh + off, a.ol + off);
       }
   }
@@ -1202,54 +1232,57 @@ struct MkPfHost {
   MkPf pf;
 };
 
-template <int EPI, int MT, int NT, int WGM, int WGN>
-static hipError_t launch_gemm_t(const PfGemm &g, int nsplit, hipStream_t st) {
+template <int EPI, int MT, int NT, int WGM, int WGN, int NS>
+static hipError_t launch_gemm_t(PfGemm g, int nsplit, hipStream_t st) {
   constexpr int BM = WGM * MT * 16, BN = WGN * NT * 16;
-  const size_t lds = (size_t)(4 * BM + 2 * BN) * GLD * 2;
+  g.tn = (g.N + BN - 1) / BN;
+  g.tm = (g.M + BM - 1) / BM;
+  g.tz = nsplit;
+  const size_t lds = (size_t)NS * (2 * BM / 16 + BN / 16) * 1024;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)pf_gemm<EPI, MT, NT, WGM, WGN>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void *)pf_gemm<EPI, MT, NT, WGM, WGN, NS>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, nsplit);
-  hipLaunchKernelGGL((pf_gemm<EPI, MT, NT, WGM, WGN>), grid, dim3(WGM * WGN * 64), lds, st, g);
+  hipLaunchKernelGGL((pf_gemm<EPI, MT, NT, WGM, WGN, NS>), dim3(g.tn * g.tm * g.tz), dim3(WGM * WGN * 64), lds, st, g);
   return hipGetLastError();
 }
-// Wide projections: 64 x 128 workgroup tiles (8 waves of 32 x 32, two workgroups per CU: 16
-// waves hide the LDS and memory latency better than 8 waves of 64 x 32 did).  The
-// 1024-wide outputs that add into the residual stream: the same tiles with split-K (partials
-// reduced in split order), so that the grid fills the chip and each K stream is short.
+// Tiles (measured at 520 rows): outputs wider than 2048 columns take 64 x 256 workgroup tiles
+// (8 waves of 32 x 64, 96 KiB of LDS, one workgroup per CU); narrower ones 64 x 64 tiles (4 waves
+// of 32 x 32) so that the grid still fills the chip.  The 1024-wide outputs that add into the
+// residual stream use 64 x 128 tiles (8 waves of 32 x 32) with split-K (partials reduced in split
+// order), so that the grid fills the chip and each K stream is short.
 // The RMSNorm that follows a projection adding into the residual stream, fused into the split-K
-// reduction when there is one (gain g; output as hi + lo into oh / ol with row stride ld).
+// reduction when there is one (gain g; output as hi + lo in the operand block layout, Kc = N).
 struct PfNext {
   const float *g;
   float eps;
   uint16_t *oh, *ol;
-  int ld;
 };
-static hipError_t launch_gemm(int epi, bool small, PfGemm g, float *part, hipStream_t st, const PfNext *next = nullptr) {
+static hipError_t launch_gemm(int epi, PfGemm g, float *part, hipStream_t st, const PfNext *next = nullptr) {
   if (g.K % GBK != 0) return hipErrorInvalidValue;
   g.kper = g.K;
-  if (epi == EPI_STORE) return small ? launch_gemm_t<EPI_STORE, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_STORE, 2, 2, 2, 4>(g, 1, st);
-  if (epi == EPI_SWIGLU) return small ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 4>(g, 1, st);
+  const bool wide = g.N > 2048;
+  if (epi == EPI_STORE) return wide ? launch_gemm_t<EPI_STORE, 2, 4, 2, 4, 4>(g, 1, st) : launch_gemm_t<EPI_STORE, 2, 2, 2, 2, 4>(g, 1, st);
+  if (epi == EPI_SWIGLU) return wide ? launch_gemm_t<EPI_SWIGLU, 2, 4, 2, 4, 4>(g, 1, st) : launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2, 4>(g, 1, st);
   const int ns = g.K / GBK;
-  const int nsplit = (ns % 4 == 0 && ns >= 8) ? 4 : (ns % 2 == 0 && ns >= 4) ? 2 : 1;
+  const int nsplit = (ns % 4 == 0 && ns >= 16) ? 4 : (ns % 2 == 0 && ns >= 8) ? 2 : 1;
   if (nsplit == 1 || !part || g.N > 4 * PF_THREADS || g.N % 4 != 0) {
-    hipError_t e = small ? launch_gemm_t<EPI_RESID, 2, 2, 2, 2>(g, 1, st) : launch_gemm_t<EPI_RESID, 4, 4, 1, 4>(g, 1, st);
+    hipError_t e = launch_gemm_t<EPI_RESID, 2, 2, 2, 2, 4>(g, 1, st);
     if (e != hipSuccess || !next) return e;
     hipLaunchKernelGGL(pf_norm_split, dim3(g.M), dim3(PF_THREADS), 0, st, (const float *)g.c, next->g, g.N, next->eps,
-                       next->oh, next->ol, next->ld);
+                       next->oh, next->ol);
     return hipGetLastError();
   }
   g.kper = g.K / nsplit;
   g.part = part;
   g.part_stride = (size_t)MK_PT * g.ldc;
-  hipError_t e = small ? launch_gemm_t<EPI_PART, 2, 2, 2, 4>(g, nsplit, st) : launch_gemm_t<EPI_PART, 4, 4, 1, 4>(g, nsplit, st);
+  hipError_t e = launch_gemm_t<EPI_PART, 2, 2, 2, 4, 4>(g, nsplit, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pf_reduce_norm, dim3(g.M), dim3(PF_THREADS), 0, st, g.c, (const float *)part, nsplit, g.part_stride,
                      g.N, next ? next->g : (const float *)nullptr, next ? next->eps : 0.f,
-                     next ? next->oh : (uint16_t *)nullptr, next ? next->ol : (uint16_t *)nullptr, next ? next->ld : 0);
+                     next ? next->oh : (uint16_t *)nullptr, next ? next->ol : (uint16_t *)nullptr);
   return hipGetLastError();
 }
 
@@ -1275,21 +1308,21 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
     const bool last = s0 + T == n;
     hipLaunchKernelGGL(pf_embed, dim3(T), dim3(PF_THREADS), 0, st, d->embed, tokens + s0, H, d->V, pf->X, d->ctl);
     hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->X, layers_host[0].ln1, H,
-                       d->rms_eps, pf->a1h, pf->a1l, pf->K1);
+                       d->rms_eps, pf->a1h, pf->a1l);
     for (int li = 0; li < d->n_layers; ++li) {
       const MkLayerDev &L = layers_host[li];
       // the norm after the mixer (FFN input) and after the FFN (next layer's input) run inside
       // the split-K reductions of the projections that add into the residual stream
-      const PfNext n2{L.ln2, d->rms_eps, pf->a1h, pf->a1l, pf->K1};
-      const PfNext n1{li + 1 < d->n_layers ? layers_host[li + 1].ln1 : nullptr, d->rms_eps, pf->a1h, pf->a1l, pf->K1};
+      const PfNext n2{L.ln2, d->rms_eps, pf->a1h, pf->a1l};
+      const PfNext n1{li + 1 < d->n_layers ? layers_host[li + 1].ln1 : nullptr, d->rms_eps, pf->a1h, pf->a1l};
       PfGemm g{};
-      g.ah = pf->a1h; g.al = pf->a1l; g.lda = pf->K1; g.M = T;
+      g.ah = pf->a1h; g.al = pf->a1l; g.M = T;
       if (L.kind == 0) {
         g.N = nh * d->r_in; g.K = H;
         g.wb[0] = g.wb[1] = g.wb[2] = L.dn_in; g.wend[0] = g.wend[1] = g.wend[2] = g.N;
         g.ks = H; g.kstride = 0;
         g.c = pf->P; g.ldc = pf->NP;
-        hipError_t e = launch_gemm(EPI_STORE, false, g, nullptr, st);
+        hipError_t e = launch_gemm(EPI_STORE, g, nullptr, st);
         if (e != hipSuccess) return e;
         const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
         // dk == dv in {64, 128} (checked when the model is loaded).  The chunk terms read the ring
@@ -1308,13 +1341,13 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
           hipLaunchKernelGGL(pf_dn_scan<64>, dim3(nh, 64 / 16), dim3(SCAN_THREADS), scan_lds(64), st, sc);
         hipLaunchKernelGGL(pf_dn_gnorm, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->o,
                            (const float *)pf->P + 2 * dk + dv, pf->NP, d->r_in, L.dn_gnorm, nh, dv, d->rms_eps,
-                           pf->a1h, pf->a1l, pf->K1);
+                           pf->a1h, pf->a1l);
         PfGemm go{};
-        go.ah = pf->a1h; go.al = pf->a1l; go.lda = pf->K1; go.M = T; go.N = H; go.K = nh * dv;
+        go.ah = pf->a1h; go.al = pf->a1l; go.M = T; go.N = H; go.K = nh * dv;
         go.wb[0] = go.wb[1] = go.wb[2] = L.dn_out; go.wend[0] = go.wend[1] = go.wend[2] = H;
         go.ks = dv; go.kstride = H * dv;
         go.c = pf->X; go.ldc = H;
-        if ((e = launch_gemm(EPI_RESID, true, go, pf->part, st, &n2)) != hipSuccess) return e;
+        if ((e = launch_gemm(EPI_RESID, go, pf->part, st, &n2)) != hipSuccess) return e;
       } else {
         g.N = (nq + 2 * nkv) * hd; g.K = H;
         g.wb[0] = L.at_q; g.wend[0] = nq * hd;
@@ -1322,36 +1355,36 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         g.wb[2] = L.at_v; g.wend[2] = g.N;
         g.ks = H; g.kstride = 0;
         g.c = pf->P; g.ldc = pf->NP;
-        hipError_t e = launch_gemm(EPI_STORE, false, g, nullptr, st);
+        hipError_t e = launch_gemm(EPI_STORE, g, nullptr, st);
         if (e != hipSuccess) return e;
         PfAtt at{};
         at.P = pf->P; at.NP = pf->NP; at.T = T; at.rope = d->rope; at.page_table = d->page_table; at.ctl = d->ctl;
         at.kc = L.kc; at.vc = L.vc; at.aq = pf->aq; at.nq = nq; at.nkv = nkv; at.hd = hd;
-        at.oh = pf->a1h; at.ol = pf->a1l; at.ld = pf->K1;
+        at.oh = pf->a1h; at.ol = pf->a1l;
         hipLaunchKernelGGL(pf_att_rope, dim3(T), dim3(PF_THREADS), 0, st, at);
         if (hd == 128) hipLaunchKernelGGL(pf_att_mfma<128>, dim3((T + 63) / 64, nq), dim3(PF_THREADS), 0, st, at);
         else if (hd == 64) hipLaunchKernelGGL(pf_att_mfma<64>, dim3((T + 63) / 64, nq), dim3(PF_THREADS), 0, st, at);
         else return hipErrorInvalidValue;   // head_dim is 64 or 128 (checked at load)
         PfGemm go{};
-        go.ah = pf->a1h; go.al = pf->a1l; go.lda = pf->K1; go.M = T; go.N = H; go.K = nq * hd;
+        go.ah = pf->a1h; go.al = pf->a1l; go.M = T; go.N = H; go.K = nq * hd;
         go.wb[0] = go.wb[1] = go.wb[2] = L.at_o; go.wend[0] = go.wend[1] = go.wend[2] = H;
         go.ks = hd; go.kstride = H * hd;
         go.c = pf->X; go.ldc = H;
-        if ((e = launch_gemm(EPI_RESID, true, go, pf->part, st, &n2)) != hipSuccess) return e;
+        if ((e = launch_gemm(EPI_RESID, go, pf->part, st, &n2)) != hipSuccess) return e;
       }
       PfGemm gu{};
-      gu.ah = pf->a1h; gu.al = pf->a1l; gu.lda = pf->K1; gu.M = T; gu.N = 2 * I; gu.K = H;
+      gu.ah = pf->a1h; gu.al = pf->a1l; gu.M = T; gu.N = 2 * I; gu.K = H;
       gu.wb[0] = gu.wb[1] = gu.wb[2] = L.ffn_gu; gu.wend[0] = gu.wend[1] = gu.wend[2] = 2 * I;
       gu.ks = H; gu.kstride = 0;
       gu.oh = pf->a2h; gu.ol = pf->a2l; gu.ldo = I;
-      hipError_t e = launch_gemm(EPI_SWIGLU, false, gu, nullptr, st);
+      hipError_t e = launch_gemm(EPI_SWIGLU, gu, nullptr, st);
       if (e != hipSuccess) return e;
       PfGemm gd{};
-      gd.ah = pf->a2h; gd.al = pf->a2l; gd.lda = I; gd.M = T; gd.N = H; gd.K = I;
+      gd.ah = pf->a2h; gd.al = pf->a2l; gd.M = T; gd.N = H; gd.K = I;
       gd.wb[0] = gd.wb[1] = gd.wb[2] = L.ffn_dn; gd.wend[0] = gd.wend[1] = gd.wend[2] = H;
       gd.ks = J; gd.kstride = H * J;
       gd.c = pf->X; gd.ldc = H;
-      if ((e = launch_gemm(EPI_RESID, true, gd, pf->part, st, n1.g ? &n1 : nullptr)) != hipSuccess) return e;
+      if ((e = launch_gemm(EPI_RESID, gd, pf->part, st, n1.g ? &n1 : nullptr)) != hipSuccess) return e;
     }
     if (last) {
       hipLaunchKernelGGL(pf_lm, dim3(MK_NWG), dim3(PF_THREADS), 0, st, (const float *)pf->X, T - 1, d->lnf, d->rms_eps,
