@@ -438,13 +438,88 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-struct PfChunk {
+// Per (16-token block, head): the causal conv (taps over positions p-3 .. p) + SiLU of the head's
+// q, k, v channels, the L2 norms of q and k, and the gates log alpha = -softplus(a), beta =
+// sigmoid(b): everything of the delta rule that is local to one token.  Thread = channel (3 dk of
+// them); all of its 19 inputs are loaded before any is used (earlier positions of the sequence
+// come from the ring).
+struct PfPrep {
   const float *P;                     // [T][NP] in-projection outputs; per head x: [q | k | v | z | a | b]
   int NP, r_in, C, nh;                // C: conv channels (q of all heads, then k, then v)
   const float *conv;                  // [C][4] taps
   const float *ring;                  // [MK_RING][C] pre-conv inputs of earlier positions
   const int32_t *ctl;
   float l2_eps;
+  float *qkv;                         // [nh][PT][3 dk]: q / |q|, k / |k|, v
+  float *gb;                          // [nh][PT][2]: log alpha, beta
+  int T;
+};
+constexpr int PREP_TB = 16;
+template <int DK>
+__global__ void __launch_bounds__(3 * DK) pf_dn_prep(PfPrep c) {
+  constexpr int NCH = 3 * DK, XL = NCH + 4;
+  __shared__ float xs[PREP_TB * XL];
+  const int h = blockIdx.y, t0 = blockIdx.x * PREP_TB, ch = threadIdx.x, w = ch >> 6, lane = ch & 63;
+  const int seg = ch / DK, i = ch - seg * DK;
+  const int col = h * c.r_in + ch, cch = seg * c.nh * DK + h * DK + i;
+  const int p0 = c.ctl[MK_CTL_POS];
+  const float4 wt = ld4(c.conv + cch * 4);
+  float x[PREP_TB + 3];
+#pragma unroll
+  for (int u = 0; u < PREP_TB + 3; ++u) {   // branch-free: every load issued, invalid ones zeroed
+    const int tt = t0 + u - 3;              // pass token
+    const bool ok = tt >= 0 ? tt < c.T : p0 + tt >= 0;
+    const float *src = tt >= 0 ? c.P + (size_t)min(tt, c.T - 1) * c.NP + col
+                               : c.ring + ((p0 + tt) & (MK_RING - 1)) * c.C + cch;
+    const float v = *src;
+    x[u] = ok ? v : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < PREP_TB; ++j) {
+    float a = fmaf(wt.x, x[j], 0.f);
+    a = fmaf(wt.y, x[j + 1], a);
+    a = fmaf(wt.z, x[j + 2], a);
+    a = fmaf(wt.w, x[j + 3], a);
+    xs[j * XL + ch] = silu_fast(a);
+  }
+  if (ch < PREP_TB && t0 + ch < c.T) {   // gates of token t0 + ch
+    const float *pa = c.P + (size_t)(t0 + ch) * c.NP + h * c.r_in + 4 * DK;   // a, b
+    *reinterpret_cast<float2 *>(c.gb + ((size_t)h * MK_PT + t0 + ch) * 2) = make_float2(-softplusf_(pa[0]), sigmoidf_(pa[1]));
+  }
+  __syncthreads();
+  // norms: 16 lanes per row (token j, segment q or k), DK / 16 elements per lane, summed with DPP
+  float *dst = c.qkv + ((size_t)h * MK_PT + t0) * NCH;
+  {
+    constexpr int EPL = DK / 16, RPW = 4, NR = 2 * PREP_TB;   // rows per wave at a time
+    for (int r = w * RPW + (lane >> 4); r < NR; r += (NCH / 64) * RPW) {
+      const int j = r >> 1, sg = r & 1, e0 = (lane & 15) * EPL;
+      float v[EPL];
+#pragma unroll
+      for (int q = 0; q < EPL; q += 4) {
+        const float4 x4 = ld4(xs + j * XL + sg * DK + e0 + q);
+        v[q] = x4.x; v[q + 1] = x4.y; v[q + 2] = x4.z; v[q + 3] = x4.w;
+      }
+      float sq = 0.f;
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) sq = fmaf(v[q], v[q], sq);
+      const float nrm = sqrtf(row_sum16(sq) + c.l2_eps);
+      if (t0 + j < c.T) {
+#pragma unroll
+        for (int q = 0; q < EPL; q += 4)
+          *reinterpret_cast<float4 *>(dst + (size_t)j * NCH + sg * DK + e0 + q) =
+              make_float4(v[q] / nrm, v[q + 1] / nrm, v[q + 2] / nrm, v[q + 3] / nrm);
+      }
+    }
+  }
+  for (int e = ch; e < PREP_TB * DK; e += NCH) {
+    const int j = e / DK, q = e - j * DK;
+    if (t0 + j < c.T) dst[(size_t)j * NCH + 2 * DK + q] = xs[j * XL + 2 * DK + q];
+  }
+}
+
+struct PfChunk {
+  const float *qkv;                   // [nh][PT][3 dk] from pf_dn_prep
+  const float *gb;                    // [nh][PT][2] log alpha, beta
   float *cW, *cQ, *cU, *cO, *cKt;     // per (head, chunk), CHUNK x dk each, in the fragment orders below
   float *cg, *cd;                     // [nh][PT/CHUNK][CHUNK] exp(G_i), exp(G_last - G_i)
   int T;
@@ -488,46 +563,26 @@ __global__ void __launch_bounds__(CP_THREADS) pf_dn_chunk_prep(PfChunk c) {
   float *R = Mm + MK_CHUNK * CS;               // [3][16][17] partial sums of the inverse
   float *Gs = R + 3 * 16 * 17, *bs = Gs + MK_CHUNK, *gam = bs + MK_CHUNK, *bgam = gam + MK_CHUNK;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  const int p0 = c.ctl[MK_CTL_POS];
-  {  // causal conv (taps over positions p-3 .. p) + SiLU of the head's q, k, v channels, straight
-     // into Ks, Qs, Vs: thread -> one channel pair and a run of tokens; all its inputs are loaded
-     // before any is used (earlier positions of the sequence come from the ring)
-    constexpr int NPAIR = 3 * DK / 2, NGRP = CP_THREADS / NPAIR, TPG = (MK_CHUNK + NGRP - 1) / NGRP;
-    const int cp = tid % NPAIR, grp = tid / NPAIR;
-    if (grp < NGRP) {
-      const int seg = cp / (DK / 2), i = (cp % (DK / 2)) * 2;   // seg 0: q, 1: k, 2: v
-      const int col = h * c.r_in + seg * DK + i, ch = seg * c.nh * DK + h * DK + i;
-      const float4 w0 = ld4(c.conv + ch * 4), w1 = ld4(c.conv + ch * 4 + 4);
-      const int j0 = grp * TPG;
-      float2 xs[TPG + 3];
+  {  // the chunk's normalized q, k and v rows into Qs, Ks, Vs (rows past the chunk's end: zero)
+    constexpr int C4 = 3 * DK / 4, NL = (MK_CHUNK * C4 + CP_THREADS - 1) / CP_THREADS;
+    const float *src = c.qkv + ((size_t)h * MK_PT + t0) * 3 * DK;
+    float4 v[NL];
 #pragma unroll
-      for (int u = 0; u < TPG + 3; ++u) {   // branch-free: every load issued, invalid ones zeroed
-        const int tt = t0 + j0 + u - 3;       // pass token
-        const bool ok = tt >= 0 ? tt < c.T : p0 + tt >= 0;
-        const float *src = tt >= 0 ? c.P + (size_t)min(tt, c.T - 1) * c.NP + col
-                                   : c.ring + ((p0 + tt) & (MK_RING - 1)) * c.C + ch;
-        const float2 x = *reinterpret_cast<const float2 *>(src);
-        xs[u] = ok ? x : make_float2(0.f, 0.f);
-      }
-      float *dst = (seg == 0 ? Qs : seg == 1 ? Ks : Vs) + i;
+    for (int u = 0; u < NL; ++u) {
+      const int e = tid + u * CP_THREADS, j = e / C4;
+      v[u] = (e < MK_CHUNK * C4 && j < Cn) ? ld4(src + (size_t)e * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
-      for (int u = 0; u < TPG; ++u) {
-        const int j = j0 + u;
-        if (j < MK_CHUNK) {
-          float a0 = fmaf(w0.x, xs[u].x, 0.f), a1 = fmaf(w1.x, xs[u].y, 0.f);
-          a0 = fmaf(w0.y, xs[u + 1].x, a0); a1 = fmaf(w1.y, xs[u + 1].y, a1);
-          a0 = fmaf(w0.z, xs[u + 2].x, a0); a1 = fmaf(w1.z, xs[u + 2].y, a1);
-          a0 = fmaf(w0.w, xs[u + 3].x, a0); a1 = fmaf(w1.w, xs[u + 3].y, a1);
-          *reinterpret_cast<float2 *>(dst + j * KS) = j < Cn ? make_float2(silu_fast(a0), silu_fast(a1)) : make_float2(0.f, 0.f);
-        }
-      }
+    for (int u = 0; u < NL; ++u) {
+      const int e = tid + u * CP_THREADS, j = e / C4, q4 = (e - j * C4) * 4, sg = q4 / DK;
+      if (e < MK_CHUNK * C4) *reinterpret_cast<float4 *>((sg == 0 ? Qs : sg == 1 ? Ks : Vs) + j * KS + (q4 - sg * DK)) = v[u];
     }
   }
-  if (tid < 64) {  // gates, in-chunk prefix sums of log alpha (one wave, Hillis-Steele), the decays
-    const float *pa = c.P + (size_t)(t0 + tid) * c.NP + h * c.r_in + 4 * DK;   // a, b
+  if (tid < 64) {  // in-chunk prefix sums of log alpha (one wave, Hillis-Steele), the decays
     const bool ok = tid < Cn;
-    float G = ok ? -softplusf_(pa[0]) : 0.f;   // log alpha, alpha = exp(-softplus(a))
-    const float b = ok ? sigmoidf_(pa[1]) : 0.f;
+    const float2 ab = ok ? *reinterpret_cast<const float2 *>(c.gb + ((size_t)h * MK_PT + t0 + tid) * 2) : make_float2(0.f, 0.f);
+    float G = ab.x;
+    const float b = ab.y;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_up(G, o, 64);
@@ -537,25 +592,6 @@ __global__ void __launch_bounds__(CP_THREADS) pf_dn_chunk_prep(PfChunk c) {
     bs[tid] = b;
     gam[tid] = ok ? expf(G) : 0.f;
     bgam[tid] = b * gam[tid];
-  }
-  __syncthreads();
-  {  // L2 norms of the q and k rows, four threads per row (rows past the chunk's end stay zero)
-    const int r = tid >> 2, part = tid & 3;
-    float *row = (r < MK_CHUNK ? Qs + r * KS : Ks + (r - MK_CHUNK) * KS) + part * (DK / 4);
-    float sq = 0.f;
-#pragma unroll
-    for (int e = 0; e < DK / 4; e += 4) {
-      const float4 v = ld4(row + e);
-      sq = fmaf(v.x, v.x, sq); sq = fmaf(v.y, v.y, sq); sq = fmaf(v.z, v.z, sq); sq = fmaf(v.w, v.w, sq);
-    }
-    sq += dpp_mov<0xB1>(sq);
-    sq += dpp_mov<0x4E>(sq);
-    const float nrm = sqrtf(sq + c.l2_eps);
-#pragma unroll
-    for (int e = 0; e < DK / 4; e += 4) {
-      const float4 v = ld4(row + e);
-      *reinterpret_cast<float4 *>(row + e) = make_float4(v.x / nrm, v.y / nrm, v.z / nrm, v.w / nrm);
-    }
   }
   __syncthreads();
   // the 10 16 x 16 tiles (ti, tj) with ti >= tj of a 64 x 64 lower triangular matrix
@@ -712,8 +748,8 @@ struct PfScan {
   float *S;                        // [nh][dv][dk] layer state
   const float *pend;               // [2][nh][MAXCOL][dk + dv + 2] pending updates (k | v | alpha beta)
   const int32_t *ctl;
-  const float *cW, *cQ, *cU, *cO, *cKt, *cg, *cd;
-  float *o;                        // [PT][nh dv]
+  const float *cW, *cU, *cKt, *cg, *cd;
+  float *snap;                     // [nh][PT/CHUNK][dv][dk] the state entering each chunk
   int T, nh;
   const float *P;                  // [T][NP] in-projection outputs (conv inputs of the pass)
   int NP, r_in, C;
@@ -721,9 +757,11 @@ struct PfScan {
 };
 
 // Carry 16 rows of one head's state through every chunk of the pass.  Per chunk, with S the
-// state entering it: P = S [W; Q~]^T (16 x 128 on FP32 MFMA: waves 0-3 take the 16-token
-// blocks of W, waves 4-7 those of Q~), U = U' - P_W^T and the outputs O = P_Q^T + O'; then
-// S <- gamma_last S + (diag(d) U)^T K (wave w takes the 16 state columns of block w).  The state
+// state entering it (first stored as the chunk's snapshot for the outputs): P = S W^T (16 x 64
+// on FP32 MFMA: wave w takes token block w % 4 over half w / 4 of the key dims, the halves
+// summed through LDS), U = U' - P^T; then S <- gamma_last S + (diag(d) U)^T K (wave w takes the
+// 16 state columns of block w).  The outputs O = Q~ S^T + O' need only the snapshots and are
+// computed afterwards for all chunks at once (pf_dn_out), off this sequential path.  The state
 // moves between the two MFMA layouts through LDS; the next chunk's operands are loaded into
 // registers while the current one is computed.
 constexpr int SCAN_THREADS = 512;
@@ -733,19 +771,18 @@ __global__ void __launch_bounds__(SCAN_THREADS) pf_dn_scan(PfScan s) {
   // MFMA k order: in the i-th group of four k steps, lane group g takes the four dims (or tokens)
   // 16 i + 4 g .. 16 i + 4 g + 3, so that one 16-byte load per lane reads 64 contiguous bytes per row
   constexpr int SL = DK + 4, DL = MK_CHUNK + 4;
-  constexpr int OL = SR + 4;          // row stride of the staged outputs
   extern __shared__ float sm[];
   float *Sl = sm;                     // [SR][SL] the state rows, row-major
   float *Dl = Sl + SR * SL;           // [SR][DL] diag(d) U, transposed: [row][token]
-  float *Ol = Dl + SR * DL;           // [PT][OL] outputs of the pass (written out at the end)
+  float *Pl = Dl + SR * DL;           // [4][64][4] second halves of the P tiles, per (token block, lane)
   const int h = blockIdx.x, r0 = blockIdx.y * SR;   // head h on XCD h % 8 (see the chunk terms)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int nch = MK_PT / MK_CHUNK, nchunk = (s.T + MK_CHUNK - 1) / MK_CHUNK;
-  const bool isq = w >= 4, upd = w < DK / 16;
-  const int pt = w & 3;               // token block of the P tile
+  const bool upd = w < DK / 16, lo = w < 4;
+  const int pt = w & 3, kh = w >> 2;  // token block and key-dim half of the P tile
   float *Sg = s.S + ((size_t)h * DK + r0) * DK;
   if (blockIdx.y == 0) {  // the head's conv inputs of the pass's last positions into the ring
-    // (the chunk terms have read the earlier positions they need from it already)
+    // (the conv of this pass has read the earlier positions it needs from it already)
     const int n = min(s.T, MK_RING), p0 = s.ctl[MK_CTL_POS];
     for (int e = tid; e < n * 3 * DK; e += SCAN_THREADS) {
       const int t = s.T - n + e / (3 * DK), q = e % (3 * DK), seg = q / DK;
@@ -778,52 +815,63 @@ __global__ void __launch_bounds__(SCAN_THREADS) pf_dn_scan(PfScan s) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) sc[v] = Sl[(4 * g + v) * SL + 16 * w + c16];
   }
-  // operands of one chunk, per lane: the P tile's B fragments (W or Q~ row 16 pt + c16), the K^T
-  // fragments of the column block (dim 16 w + c16), U' or O' (token 16 pt + c16, rows 4 g ..) and
-  // d of that token
-  struct Ops { float4 bp[DK / 16]; float4 bk[4]; float4 uo; float dd, gl; };
+  // operands of one chunk, per lane: the P tile's B fragments (W row 16 pt + c16, the lane's half
+  // of the dims), the K^T fragments of the column block (dim 16 w + c16), U' (token 16 pt + c16,
+  // rows 4 g ..) and d of that token
+  constexpr int NBP = DK / 32;
+  struct Ops { float4 bp[NBP]; float4 bk[4]; float4 uo; float dd, gl; };
   // Every wave issues the same loads for every chunk index (clamped to the last chunk), so the
-  // number of loads in flight never depends on the path taken and the compiler's waits stay exact
-  // (a load on one path only makes it wait for everything at the next join).
+  // number of loads in flight never depends on the path taken and the compiler's waits stay exact.
   auto fetch = [&](Ops &op, int c) {
     c = min(c, nchunk - 1);
     const size_t cb = (size_t)h * nch + c, mo = cb * MK_CHUNK * DK;
-    const float *P = (isq ? s.cQ : s.cW) + mo + frag_tn<DK>(16 * pt + c16, 4 * g);
+    const float *P = s.cW + mo + frag_tn<DK>(16 * pt + c16, 4 * g);
 #pragma unroll
-    for (int i = 0; i < DK / 16; ++i) op.bp[i] = ld4(P + 256 * i);
+    for (int i = 0; i < NBP; ++i) op.bp[i] = ld4(P + 256 * (kh * NBP + i));
     const float *K = s.cKt + mo + frag_kt(16 * min(w, DK / 16 - 1) + c16, 4 * g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) op.bk[i] = ld4(K + 256 * i);
-    op.uo = ld4((isq ? s.cO : s.cU) + mo + frag_tn<DK>(16 * pt + c16, r0 + 4 * g));
+    op.uo = ld4(s.cU + mo + frag_tn<DK>(16 * pt + c16, r0 + 4 * g));
     op.dd = s.cd[cb * MK_CHUNK + 16 * pt + c16];
     op.gl = s.cg[cb * MK_CHUNK + min(MK_CHUNK, s.T - c * MK_CHUNK) - 1];   // gamma of the chunk's last token
   };
   // one chunk: operands in `cur`, while the operands of chunk c + 2 are loaded into `pre`.  A step
   // past the last chunk (the loop runs in threes) leaves the state as it is: d = 0, gamma = 1.
   auto step = [&](const Ops &cur, Ops &pre, int c) {
-    const int t0 = c * MK_CHUNK, Cn = min(MK_CHUNK, s.T - t0);
     const bool act = c < nchunk;
     const float dd = act ? cur.dd : 0.f, gl = act ? cur.gl : 1.f;
-    fetch(pre, c + 2);
-    // P tile: rows 4 g + v, token 16 pt + c16
-    f32x4 p = {0.f, 0.f, 0.f, 0.f};
-    {
-      const float *sr = Sl + c16 * SL + 4 * g;
-#pragma unroll
-      for (int i = 0; i < DK / 16; ++i) {
-        const float4 a = ld4(sr + 16 * i), b = cur.bp[i];
-        p = mfma4(a.x, b.x, p); p = mfma4(a.y, b.y, p); p = mfma4(a.z, b.z, p); p = mfma4(a.w, b.w, p);
+    if (act) {   // snapshot of the state entering chunk c (uniform branch)
+      float *sn = s.snap + (((size_t)h * nch + c) * DK + r0) * DK;
+      for (int e = tid; e < SR * DK / 4; e += SCAN_THREADS) {
+        const int r = e / (DK / 4), c4 = e - r * (DK / 4);
+        *reinterpret_cast<float4 *>(sn + r * DK + c4 * 4) = ld4(Sl + r * SL + c4 * 4);
       }
     }
-    const int tok = 16 * pt + c16;
-    if (!isq) {
-      Dl[(4 * g + 0) * DL + tok] = dd * (cur.uo.x - p[0]);
-      Dl[(4 * g + 1) * DL + tok] = dd * (cur.uo.y - p[1]);
-      Dl[(4 * g + 2) * DL + tok] = dd * (cur.uo.z - p[2]);
-      Dl[(4 * g + 3) * DL + tok] = dd * (cur.uo.w - p[3]);
-    } else if (tok < Cn) {
-      *reinterpret_cast<float4 *>(Ol + (t0 + tok) * OL + 4 * g) =
-          make_float4(p[0] + cur.uo.x, p[1] + cur.uo.y, p[2] + cur.uo.z, p[3] + cur.uo.w);
+    fetch(pre, c + 2);
+    // P tile half: rows 4 g + v, token 16 pt + c16, dims of half kh; two chains of MFMAs
+    f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
+    {
+      const float *sr = Sl + c16 * SL + 4 * g + kh * (DK / 2);
+#pragma unroll
+      for (int i = 0; i < NBP; i += 2) {
+        const float4 a = ld4(sr + 16 * i), b = cur.bp[i];
+        const float4 a2 = ld4(sr + 16 * (i + 1)), b2 = cur.bp[i + 1];
+        p0 = mfma4(a.x, b.x, p0); p1 = mfma4(a2.x, b2.x, p1);
+        p0 = mfma4(a.y, b.y, p0); p1 = mfma4(a2.y, b2.y, p1);
+        p0 = mfma4(a.z, b.z, p0); p1 = mfma4(a2.z, b2.z, p1);
+        p0 = mfma4(a.w, b.w, p0); p1 = mfma4(a2.w, b2.w, p1);
+      }
+    }
+    const f32x4 p = p0 + p1;
+    if (!lo) *reinterpret_cast<f32x4 *>(Pl + (pt * 64 + lane) * 4) = p;
+    lds_barrier();
+    if (lo) {
+      const f32x4 q = *reinterpret_cast<const f32x4 *>(Pl + (pt * 64 + lane) * 4);
+      const int tok = 16 * pt + c16;
+      Dl[(4 * g + 0) * DL + tok] = dd * (cur.uo.x - (p[0] + q[0]));
+      Dl[(4 * g + 1) * DL + tok] = dd * (cur.uo.y - (p[1] + q[1]));
+      Dl[(4 * g + 2) * DL + tok] = dd * (cur.uo.z - (p[2] + q[2]));
+      Dl[(4 * g + 3) * DL + tok] = dd * (cur.uo.w - (p[3] + q[3]));
     }
     lds_barrier();
     if (upd) {  // S <- gamma_last S + D K on the column block 16 w ..
@@ -853,30 +901,79 @@ __global__ void __launch_bounds__(SCAN_THREADS) pf_dn_scan(PfScan s) {
     step(o1, o0, c + 1);
     step(o2, o1, c + 2);
   }
-  for (int e = tid; e < s.T * (SR / 4); e += SCAN_THREADS) {   // the staged outputs, row by row
-    const int t = e / (SR / 4), q = e - t * (SR / 4);
-    *reinterpret_cast<float4 *>(s.o + (size_t)t * s.nh * DK + h * DK + r0 + 4 * q) = ld4(Ol + t * OL + 4 * q);
-  }
   if (upd) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) Sg[(size_t)(4 * g + v) * DK + 16 * w + c16] = sc[v];
   }
 }
 
-// gated RMSNorm per (token, head): y = o / sqrt(mean(o^2) + eps) * g * SiLU(z), as bf16 hi + lo in
-// the operand block layout (Kc = nh dv; z of head h, token t: Pz[t NP + h r_in + i], straight from
-// the in-projection outputs)
-__global__ void __launch_bounds__(PF_THREADS) pf_dn_gnorm(const float *o, const float *Pz, int NP, int r_in, const float *gn,
-                                                          int nh, int dv, float eps, uint16_t *oh, uint16_t *ol) {
-  const int t = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int h = w; h < nh; h += PF_THREADS / 64) {
-    const float *oo = o + (size_t)t * nh * dv + h * dv;
-    const float *zz = Pz + (size_t)t * NP + h * r_in;
-    float sq = 0.f;
-    for (int i = lane; i < dv; i += 64) sq = fmaf(oo[i], oo[i], sq);
-    const float den = sqrtf(wave_sum(sq) / (float)dv + eps);
-    for (int i = lane; i < dv; i += 64)
-      split_store(oo[i] / den * gn[i] * siluf_(zz[i]), oh + ablk(t, h * dv + i, nh * dv), ol + ablk(t, h * dv + i, nh * dv));
+// Outputs of the delta rule for 16 tokens of one head, from the snapshot S of the state entering
+// their chunk: O = Q~ S^T + O' (FP32 MFMA, wave w: value columns 16 w ..), then the gated RMSNorm
+// y = O / sqrt(mean(O^2) + eps) * g * SiLU(z) per token, written as bf16 hi + lo in the operand
+// block layout (Kc = nh dv) for the out-projection.  z of head h, token t: P[t NP + h r_in + 2 dk + dv + i].
+struct PfOut {
+  const float *cQ, *cO, *snap;
+  const float *P;
+  int NP, r_in;
+  const float *gn;
+  int nh;
+  float eps;
+  uint16_t *oh, *ol;
+  int T;
+};
+template <int DK>
+__global__ void __launch_bounds__(DK * 4) pf_dn_out(PfOut o) {
+  constexpr int NWV = DK / 16;
+  __shared__ float red[NWV][16];
+  const int h = blockIdx.y, t0 = blockIdx.x * 16, c = t0 / MK_CHUNK, nch = MK_PT / MK_CHUNK;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const size_t cb = (size_t)h * nch + c, mo = cb * MK_CHUNK * DK;
+  const int tc = t0 - c * MK_CHUNK;   // token offset inside the chunk
+  const float *qa = o.cQ + mo + frag_tn<DK>(tc + c16, 4 * g);
+  const float *sb = o.snap + (cb * DK + 16 * w + c16) * DK + 4 * g;
+  float4 qf[DK / 16], sf[DK / 16];
+#pragma unroll
+  for (int i = 0; i < DK / 16; ++i) { qf[i] = ld4(qa + 256 * i); sf[i] = ld4(sb + 16 * i); }
+  float op[4], zv[4];
+  const int n = 16 * w + c16;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    op[v] = o.cO[mo + frag_tn<DK>(tc + 4 * g + v, n)];
+    zv[v] = o.P[(size_t)min(t0 + 4 * g + v, o.T - 1) * o.NP + h * o.r_in + 3 * DK + n];
+  }
+  const float gnv = o.gn[n];
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+  for (int i = 0; i < DK / 16; i += 2) {
+    a0 = mfma4(qf[i].x, sf[i].x, a0); a1 = mfma4(qf[i + 1].x, sf[i + 1].x, a1);
+    a0 = mfma4(qf[i].y, sf[i].y, a0); a1 = mfma4(qf[i + 1].y, sf[i + 1].y, a1);
+    a0 = mfma4(qf[i].z, sf[i].z, a0); a1 = mfma4(qf[i + 1].z, sf[i + 1].z, a1);
+    a0 = mfma4(qf[i].w, sf[i].w, a0); a1 = mfma4(qf[i + 1].w, sf[i + 1].w, a1);
+  }
+  // lane (g, c16), register v: token t0 + 4 g + v, value column 16 w + c16
+  float ov[4], sq[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    ov[v] = a0[v] + a1[v] + op[v];
+    sq[v] = row_sum16(ov[v] * ov[v]);
+  }
+  if (c16 == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[w][4 * g + v] = sq[v];
+  }
+  __syncthreads();
+  const int Kc = o.nh * DK;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int tl = 4 * g + v, t = t0 + tl;
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < NWV; ++q) ss += red[q][tl];
+    if (t < o.T) {
+      const float den = sqrtf(ss / (float)DK + o.eps);
+      const size_t off = ablk(t, h * DK + n, Kc);
+      split_store(ov[v] / den * gnv * siluf_(zv[v]), o.oh + off, o.ol + off);
+    }
   }
 }
 
@@ -1287,7 +1384,7 @@ static hipError_t launch_gemm(int epi, PfGemm g, float *part, hipStream_t st, co
 }
 
 static size_t chunk_prep_lds(int dk) { return (size_t)(3 * MK_CHUNK * (dk + 4) + 3 * MK_CHUNK * CS + 3 * 16 * 17 + 4 * MK_CHUNK) * 4; }
-static size_t scan_lds(int dk) { return (size_t)(16 * (dk + 4) + 16 * (MK_CHUNK + 4) + MK_PT * 20) * 4; }
+static size_t scan_lds(int dk) { return (size_t)(16 * (dk + 4) + 16 * (MK_CHUNK + 4) + 4 * 64 * 4) * 4; }
 
 // Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table.
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
@@ -1325,23 +1422,25 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         hipError_t e = launch_gemm(EPI_STORE, g, nullptr, st);
         if (e != hipSuccess) return e;
         const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
-        // dk == dv in {64, 128} (checked when the model is loaded).  The chunk terms read the ring
-        // (conv inputs of earlier positions) before the scan overwrites it with this pass's last ones.
-        PfChunk ck{pf->P, pf->NP, d->r_in, d->C, nh, L.dn_conv, L.ring, d->ctl, d->l2_eps,
-                   pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, T};
-        PfScan sc{L.S, L.pend, d->ctl, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, pf->o, T, nh,
+        // dk == dv in {64, 128} (checked when the model is loaded).  The conv reads the ring (conv
+        // inputs of earlier positions) before the scan overwrites it with this pass's last ones.
+        PfPrep pp{pf->P, pf->NP, d->r_in, d->C, nh, L.dn_conv, L.ring, d->ctl, d->l2_eps, pf->qkv, pf->gb, T};
+        PfChunk ck{pf->qkv, pf->gb, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, T};
+        PfScan sc{L.S, L.pend, d->ctl, pf->cW, pf->cU, pf->cKt, pf->cg, pf->cd, pf->snap, T, nh,
                   pf->P, pf->NP, d->r_in, d->C, L.ring};
-        if (dk == 128)
+        PfOut po{pf->cQ, pf->cO, pf->snap, pf->P, pf->NP, d->r_in, L.dn_gnorm, nh, d->rms_eps, pf->a1h, pf->a1l, T};
+        const dim3 gtok((T + PREP_TB - 1) / PREP_TB, nh);
+        if (dk == 128) {
+          hipLaunchKernelGGL(pf_dn_prep<128>, gtok, dim3(3 * 128), 0, st, pp);
           hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(128), st, ck);
-        else
-          hipLaunchKernelGGL(pf_dn_chunk_prep<64>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(64), st, ck);
-        if (dk == 128)
           hipLaunchKernelGGL(pf_dn_scan<128>, dim3(nh, 128 / 16), dim3(SCAN_THREADS), scan_lds(128), st, sc);
-        else
+          hipLaunchKernelGGL(pf_dn_out<128>, gtok, dim3(128 * 4), 0, st, po);
+        } else {
+          hipLaunchKernelGGL(pf_dn_prep<64>, gtok, dim3(3 * 64), 0, st, pp);
+          hipLaunchKernelGGL(pf_dn_chunk_prep<64>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(64), st, ck);
           hipLaunchKernelGGL(pf_dn_scan<64>, dim3(nh, 64 / 16), dim3(SCAN_THREADS), scan_lds(64), st, sc);
-        hipLaunchKernelGGL(pf_dn_gnorm, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->o,
-                           (const float *)pf->P + 2 * dk + dv, pf->NP, d->r_in, L.dn_gnorm, nh, dv, d->rms_eps,
-                           pf->a1h, pf->a1l);
+          hipLaunchKernelGGL(pf_dn_out<64>, gtok, dim3(64 * 4), 0, st, po);
+        }
         PfGemm go{};
         go.ah = pf->a1h; go.al = pf->a1l; go.M = T; go.N = H; go.K = nh * dv;
         go.wb[0] = go.wb[1] = go.wb[2] = L.dn_out; go.wend[0] = go.wend[1] = go.wend[2] = H;
