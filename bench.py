@@ -135,7 +135,8 @@ def cpu_baseline(decode_seconds: float = 10.0) -> dict:
 def extras(model, cfg, stream) -> dict:
     """Secondary measurements on the same model: multi-token verify forwards after the pp520
     prompt (1 accepted + 4 seeded random drafts each, state rolled back to the accepted prefix),
-    and decode at long context after an 8192-token prompt."""
+    greedy generation with lookup drafts after the same prompt, and decode at long context after
+    an 8192-token prompt."""
     import torch
     dev = stream.device
     out = {}
@@ -167,6 +168,54 @@ def extras(model, cfg, stream) -> dict:
                      "forwards_per_s": round(1e6 / launch_us, 1), "positions_per_s": round(5e6 / launch_us, 1),
                      "committed_tok_per_s_random_drafts": round(acc / (ms * 1e-3), 1),
                      "accepted_per_forward_random_drafts": round(acc / nf, 3)}
+    # lookup drafts: 128 greedy tokens after the pp520 prompt, each launch verifying the last token
+    # plus the n-gram drafts found in the prompt and the tokens generated so far (one host round
+    # trip per launch), against 128 chained decode steps on the same state
+    pnp = W.make_prompt(cfg, 520, seed=1)
+    first = torch.zeros(1, dtype=torch.int32, device=dev)
+    model.reset()
+    model.prefill(prompt, first)
+    model.sync()
+    t_first = int(first.item())
+    t0 = time.perf_counter()
+    toks_lk, st = model.generate_lookup(pnp, t_first, 128, 1, 3)
+    lk_s = time.perf_counter() - t0
+    model.reset()
+    model.prefill(prompt, first)
+    model.sync()
+    chain = torch.zeros(129, dtype=torch.int32, device=dev)
+    chain[0:1] = first
+    t0 = time.perf_counter()
+    for i in range(128):
+        model.decode_step(chain[i:i + 1], chain[i + 1:i + 2])
+    model.sync()
+    dec_s = time.perf_counter() - t0
+    same = toks_lk == chain[1:].cpu().numpy().tolist()
+    # the same 128 tokens with perfect drafts (the greedy continuation just computed, 4 per verify
+    # forward, chained on the device): what verify commits when every draft is right
+    model.reset()
+    model.prefill(prompt, first)
+    nfw = 128 // 5
+    planted = torch.zeros((nfw, 5), dtype=torch.int32, device=dev)
+    for f in range(nfw):
+        planted[f] = chain[5 * f:5 * f + 5]
+    pam = torch.zeros((nfw, 5), dtype=torch.int32, device=dev)
+    pacc = torch.zeros((nfw, 1), dtype=torch.int32, device=dev)
+    model.sync()
+    e0.record(stream)
+    for f in range(nfw):
+        model.decode_step(planted[f], pam[f], None, pacc[f])
+    e1.record(stream)
+    model.sync()
+    pl_ms = e0.elapsed_time(e1)
+    pl_ok = bool(torch.equal(pam[:, :4], planted[:, 1:])) and int(pacc.min().item()) == 5
+    out["lookup_decode"] = {"tokens": 128, "launches": st["forwards"], "drafted": st["drafted"],
+                            "accepted_drafts": st["accepted"], "tokens_per_launch": round(128 / st["forwards"], 3),
+                            "committed_tok_per_s": round(128 / lk_s, 1), "plain_decode_tok_per_s": round(128 / dec_s, 1),
+                            "speedup": round(dec_s / lk_s, 3), "tokens_equal_plain_decode": bool(same),
+                            "note": "host clock around each loop; the lookup loop synchronises once per launch",
+                            "perfect_drafts": {"forwards": nfw, "accepted_per_forward": 5, "all_accepted": pl_ok,
+                                               "committed_tok_per_s": round(5 * nfw / (pl_ms * 1e-3), 1)}}
     # long context: 8192-token prompt, 128 decode steps
     prompt = torch.tensor(W.make_prompt(cfg, 8192, seed=1), dtype=torch.int32, device=dev)
     toks = torch.zeros(129, dtype=torch.int32, device=dev)

@@ -51,6 +51,7 @@ struct mk_model {
   size_t arena_bytes;
   uint2 *xch;                           // exchange slots of mk_decode_step (in the arena)
   uint2 *static_xch;                    // device address of the static slots (mk_decode_step_static)
+  int32_t *gen;                         // [64] device buffers of mk_generate_lookup (in the arena)
   // regions cleared by mk_reset_state
   std::vector<std::pair<size_t, size_t>> state_regions;
   int32_t pos_hi;  // upper bound of the device position (exact unless a verify ran)
@@ -84,7 +85,7 @@ struct LayerRegions {
 
 struct Plan {
   int H, V, I, J, nh, dk, dv, C, r_in, nq, nkv, hd, r_in_max, x_o_len, xm_len, max_pages;
-  Region embed, lnf, rope, page_table, layer_table, ctl, xch;
+  Region embed, lnf, rope, page_table, layer_table, ctl, xch, gen;
   std::vector<LayerRegions> layers;
   // prefill scratch (one pass of MK_PT tokens)
   int K1, NP;
@@ -192,6 +193,7 @@ Plan make_plan(const mk_config *c) {
   }
   // exchange slots, sized for the widest launch (verify, MK_MAXCOL columns)
   p.xch = L.add(mk_xch_bytes(MK_MAXCOL, c->n_layers, p.H, p.r_in_max, p.x_o_len, p.xm_len));
+  p.gen = L.add(256);   // tokens in, greedy tokens out, n_accepted, error word of mk_generate_lookup
   {
     const size_t T = MK_PT, nch = MK_PT / MK_CHUNK;
     p.K1 = std::max(p.H, std::max(p.nh * p.dv, p.nq * p.hd));
@@ -544,6 +546,7 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   mm->arena = A;
   mm->arena_bytes = arena_bytes;
   mm->xch = (uint2 *)(A + p.xch.off);
+  mm->gen = (int32_t *)(A + p.gen.off);
   mm->static_xch = (uint2 *)static_xch;
   mm->state_regions = state;
   mm->pos_hi = 0;
@@ -665,6 +668,74 @@ extern "C" int mk_sync_status(mk_model *m, void *stream, int32_t *pos) {
   }
   if (e & MK_DERR_TOKEN) return fail(MK_ETOKEN, "a token id was out of range");
   if (e & MK_DERR_NAN) return fail(MK_ENAN, "non-finite logits");
+  return MK_OK;
+}
+
+// ------------------------------------------------------------------------------ lookup drafts
+extern "C" int mk_lookup_draft(const int32_t *history, int32_t n_history, int32_t ngram_min, int32_t ngram_max,
+                               int32_t max_draft, int32_t *out_draft) {
+  if (n_history < 0 || max_draft < 0 || ngram_min < 1 || ngram_max < ngram_min)
+    return fail(MK_EINVAL, "mk_lookup_draft: need n_history >= 0, max_draft >= 0, 1 <= ngram_min <= ngram_max");
+  if (max_draft == 0 || n_history < 2) return 0;
+  if (!history || !out_draft) return fail(MK_EINVAL, "mk_lookup_draft: NULL buffer");
+  for (int32_t g = std::min(ngram_max, n_history - 1); g >= ngram_min; --g) {
+    const int32_t *suf = history + (n_history - g);
+    // most recent earlier occurrence: start i with i + g < n_history (at least one token follows it)
+    for (int32_t i = n_history - g - 1; i >= 0; --i) {
+      if (std::memcmp(history + i, suf, (size_t)g * sizeof(int32_t)) != 0) continue;
+      const int32_t nd = std::min(max_draft, n_history - (i + g));
+      std::memcpy(out_draft, history + i + g, (size_t)nd * sizeof(int32_t));
+      return nd;
+    }
+  }
+  return 0;
+}
+
+extern "C" int mk_generate_lookup(mk_model *m, const int32_t *history, int32_t n_history, int32_t last_token,
+                                  int32_t n_generate, int32_t ngram_min, int32_t ngram_max, int32_t *out_tokens,
+                                  mk_lookup_stats *stats, void *stream) {
+  if (!live(m)) return fail(MK_ESTATE, "model not loaded");
+  if (n_history < 0 || (n_history > 0 && !history)) return fail(MK_EINVAL, "history must hold n_history tokens");
+  if (n_generate < 0 || (n_generate > 0 && !out_tokens)) return fail(MK_EINVAL, "out_tokens must hold n_generate tokens");
+  if (ngram_min < 1 || ngram_max < ngram_min) return fail(MK_EINVAL, "need 1 <= ngram_min <= ngram_max");
+  if (last_token < 0 || last_token >= m->cfg.vocab) return fail(MK_EINVAL, "last_token out of range");
+  mk_lookup_stats st{0, 0, 0};
+  if (stats) *stats = st;
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<int32_t> ctx(history, history + n_history);
+  ctx.push_back(last_token);
+  int32_t *d_tok = m->gen, *d_arg = m->gen + 16, *d_nacc = m->gen + 32;
+  int32_t cur = last_token, done = 0;
+  int32_t tok[MK_MAXCOL], arg[MK_MAXCOL], draft[MK_MAXCOL];
+  while (done < n_generate) {
+    const int32_t rem = n_generate - done;
+    const int32_t dmax = std::min(m->cfg.max_verify - 1, rem - 1);
+    int32_t nd = dmax > 0 ? mk_lookup_draft(ctx.data(), (int32_t)ctx.size(), ngram_min, ngram_max, dmax, draft) : 0;
+    if (nd < 0) return nd;
+    tok[0] = cur;
+    for (int32_t i = 0; i < nd; ++i) tok[1 + i] = draft[i];
+    HIPCHECK(hipMemcpyAsync(d_tok, tok, (size_t)(1 + nd) * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    int r = decode_launch(m, d_tok, 1 + nd, d_arg, nullptr, nd > 0 ? d_nacc : nullptr, stream, false);
+    if (r != MK_OK) return r;
+    int32_t nacc = 1, ctl[MK_CTL_WORDS];
+    HIPCHECK(hipMemcpyAsync(arg, d_arg, (size_t)(1 + nd) * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    if (nd > 0) HIPCHECK(hipMemcpyAsync(&nacc, d_nacc, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    HIPCHECK(hipMemcpyAsync(ctl, m->dev.ctl, sizeof(ctl), hipMemcpyDeviceToHost, s));
+    HIPCHECK(hipStreamSynchronize(s));
+    m->pos_hi = ctl[MK_CTL_POS];
+    if (ctl[MK_CTL_ERR] != 0) return mk_sync_status(m, stream, nullptr);   // reports the device error
+    if (nacc < 1 || nacc > 1 + nd) return fail(MK_EHIP, "n_accepted out of range");
+    for (int32_t i = 0; i < nacc; ++i) {
+      out_tokens[done + i] = arg[i];
+      ctx.push_back(arg[i]);
+    }
+    done += nacc;
+    cur = arg[nacc - 1];
+    st.forwards += 1;
+    st.drafted += nd;
+    st.accepted += nacc - 1;
+    if (stats) *stats = st;
+  }
   return MK_OK;
 }
 

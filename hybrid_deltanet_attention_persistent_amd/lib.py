@@ -24,7 +24,8 @@ MK_LAYER_DELTANET, MK_LAYER_ATTENTION = 0, 1
 MK_DTYPE_BF16, MK_DTYPE_F16, MK_DTYPE_F32 = 1, 2, 3
 
 EXPORTED = ["mk_required_bytes", "mk_load_weights", "mk_reset_state", "mk_prefill", "mk_decode_step",
-            "mk_decode_step_static", "mk_sync_status", "mk_free", "mk_status_string", "mk_last_error"]
+            "mk_decode_step_static", "mk_sync_status", "mk_free", "mk_status_string", "mk_last_error",
+            "mk_lookup_draft", "mk_generate_lookup"]
 MK_STATIC_SCRATCH_BYTES = 16 << 20
 
 
@@ -44,6 +45,10 @@ class MkConfig(ctypes.Structure):
         ("tied_embedding", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("prefill_chunk", ctypes.c_int32),
         ("max_verify", ctypes.c_int32),
     ]
+
+
+class MkLookupStats(ctypes.Structure):
+    _fields_ = [("forwards", ctypes.c_int32), ("drafted", ctypes.c_int32), ("accepted", ctypes.c_int32)]
 
 
 class MkTensor(ctypes.Structure):
@@ -71,6 +76,8 @@ def load_library() -> ctypes.CDLL:
     lib.mk_decode_step.argtypes = [vp, vp, i32, vp, vp, vp, vp]
     lib.mk_decode_step_static.argtypes = [vp, vp, i32, vp, vp, vp, vp]
     lib.mk_sync_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
+    lib.mk_lookup_draft.argtypes = [vp, i32, i32, i32, i32, vp]
+    lib.mk_generate_lookup.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, ctypes.POINTER(MkLookupStats), vp]
     lib.mk_free.argtypes = [vp]
     lib.mk_free.restype = None
     lib.mk_status_string.argtypes = [ctypes.c_int]
@@ -78,7 +85,7 @@ def load_library() -> ctypes.CDLL:
     lib.mk_last_error.argtypes = []
     lib.mk_last_error.restype = ctypes.c_char_p
     for f in ("mk_required_bytes", "mk_load_weights", "mk_reset_state", "mk_prefill", "mk_decode_step",
-              "mk_decode_step_static", "mk_sync_status"):
+              "mk_decode_step_static", "mk_sync_status", "mk_lookup_draft", "mk_generate_lookup"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -175,6 +182,29 @@ def mk_sync_status(handle: int, stream=None) -> int:
     return pos.value
 
 
+def mk_lookup_draft(history, ngram_min: int, ngram_max: int, max_draft: int) -> list:
+    """Lookup draft tokens for `history` (host ints); see include/mk.h."""
+    h = np.ascontiguousarray(np.asarray(history, dtype=np.int32))
+    out = np.zeros(max(int(max_draft), 1), dtype=np.int32)
+    n = load_library().mk_lookup_draft(h.ctypes.data if h.size else None, int(h.size), int(ngram_min), int(ngram_max),
+                                       int(max_draft), out.ctypes.data)
+    if n < 0:
+        _check(n, "mk_lookup_draft")
+    return out[:n].tolist()
+
+
+def mk_generate_lookup(handle: int, history, last_token: int, n_generate: int, ngram_min: int = 1,
+                       ngram_max: int = 3, stream=None) -> tuple:
+    """Greedy tokens generated with lookup drafts: (tokens, {"forwards", "drafted", "accepted"})."""
+    h = np.ascontiguousarray(np.asarray(history, dtype=np.int32))
+    out = np.zeros(max(int(n_generate), 1), dtype=np.int32)
+    st = MkLookupStats()
+    _check(load_library().mk_generate_lookup(handle, h.ctypes.data if h.size else None, int(h.size), int(last_token),
+                                             int(n_generate), int(ngram_min), int(ngram_max), out.ctypes.data,
+                                             ctypes.byref(st), _stream(stream)), "mk_generate_lookup")
+    return out[:n_generate].tolist(), {"forwards": st.forwards, "drafted": st.drafted, "accepted": st.accepted}
+
+
 def mk_free(handle: int) -> None:
     load_library().mk_free(handle)
 
@@ -205,6 +235,9 @@ class Model:
 
     def sync(self) -> int:
         return mk_sync_status(self.handle)
+
+    def generate_lookup(self, history, last_token: int, n_generate: int, ngram_min: int = 1, ngram_max: int = 3):
+        return mk_generate_lookup(self.handle, history, last_token, n_generate, ngram_min, ngram_max)
 
     def close(self):
         if self.handle:

@@ -161,6 +161,41 @@ enum { MK_STATIC_SCRATCH_BYTES = 16 << 20 };
 int mk_decode_step_static(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_argmax,
                           float *d_logits, int32_t *d_n_accepted, void *stream);
 
+/* Weight-free draft tokens for speculative decoding ("lookup-augmented draft" on the RTX 3090 tag
+ * page; several drafts checked per weight pass with greedy output unchanged, speed section of the
+ * Korean update page): the longest suffix of history[0..n_history) of length g, for g from ngram_max
+ * down to ngram_min, that also occurs earlier in the history; at its most recent earlier occurrence
+ * the tokens that followed it (at most max_draft, fewer where the history ends) are copied to
+ * out_draft.  Returns the number of draft tokens (0 when no such suffix recurs), or MK_EINVAL
+ * (NULL pointer with a non-empty request, 1 <= ngram_min <= ngram_max violated, max_draft < 0).
+ * Host memory only; no model or GPU involved.                                                     */
+int mk_lookup_draft(const int32_t *history, int32_t n_history, int32_t ngram_min, int32_t ngram_max,
+                    int32_t max_draft, int32_t *out_draft);
+
+/* Counters of one mk_generate_lookup call.                                                         */
+typedef struct mk_lookup_stats {
+  int32_t forwards;   /* launches (decode steps and verify forwards)                              */
+  int32_t drafted;    /* draft tokens sent to verify forwards                                     */
+  int32_t accepted;   /* draft tokens accepted (committed without a launch of their own)          */
+} mk_lookup_stats;
+
+/* Greedy generation driven by lookup drafts.  The state holds history[0..n_history) (host; the
+ * prompt and whatever was appended since) and last_token is the greedy token after it (as
+ * mk_prefill or the last decode step returned it, not yet appended).  Generates n_generate tokens
+ * into out_tokens[0..n_generate) (host): each launch takes last_token plus the drafts
+ * mk_lookup_draft finds in history + generated tokens (at most max_verify - 1, and never more than
+ * the tokens still to generate), as a verify forward, or as a decode step when there are none;
+ * the accepted drafts and the greedy token after them are committed.  The result equals
+ * n_generate chained mk_decode_step calls token for token (verify is bit-identical to decode), in
+ * fewer launches when drafts are accepted.  The state is left after last_token and
+ * out_tokens[0..n_generate - 1), with out_tokens[n_generate - 1] the next last_token.  stats may
+ * be NULL.  Synchronises `stream` after every launch (the next drafts depend on the accepted
+ * tokens); device-side errors (MK_EHANG, MK_ETOKEN, MK_ENAN) end the call with that status and the
+ * tokens generated so far.  Its small device buffers live in the model's arena.                   */
+int mk_generate_lookup(mk_model *m, const int32_t *history, int32_t n_history, int32_t last_token,
+                       int32_t n_generate, int32_t ngram_min, int32_t ngram_max, int32_t *out_tokens,
+                       mk_lookup_stats *stats, void *stream);
+
 /* Synchronise `stream`, then report the device-side status of the work done so
  * far (MK_OK, MK_EHANG, MK_ETOKEN or MK_ENAN) and, if pos is not NULL, the number
  * of tokens the state holds.  A device error stays set until mk_reset_state.      */
