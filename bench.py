@@ -241,6 +241,74 @@ def extras(model, cfg, stream) -> dict:
     return out
 
 
+def energy(model, cfg, stream, seconds: float = 4.0) -> dict:
+    """Energy per token from the GPU's own energy accumulator (amdsmi), accelerator socket only,
+    like the launch page's method (section "Measurement:": NVML energy counters, accelerator power
+    only), at the power cap the GPU runs with: the page's power-limit sweep (section "Then we
+    turned the power down") needs privileges this run does not have.  The driver refreshes the
+    accumulator only every so often, so energy is read around windows of several seconds (timed by
+    the accumulator's own timestamp): window A repeats (reset, pp520 prompt, 128 chained decode
+    steps), window B repeats (reset, pp520 prompt); decode energy per token = (A per round - B per
+    round) / 128."""
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:  # noqa: BLE001 -- reported, not fatal
+        return {"error": f"amdsmi unavailable: {e}"}
+    try:
+        h = amdsmi.amdsmi_get_processor_handles()[0]   # the one visible GPU
+
+        def read():
+            e = amdsmi.amdsmi_get_energy_count(h)
+            return e["energy_accumulator"] * e["counter_resolution"] * 1e-6, e["timestamp"] * 1e-9
+
+        cap = amdsmi.amdsmi_get_power_cap_info(h)
+        dev = stream.device
+        prompt = torch.tensor(W.make_prompt(cfg, 520, seed=1), dtype=torch.int32, device=dev)
+        toks = torch.zeros(129, dtype=torch.int32, device=dev)
+
+        def window(decode: bool):
+            model.sync()
+            j0, s0 = read()
+            t0, n = time.perf_counter(), 0
+            while time.perf_counter() - t0 < seconds:
+                model.reset()
+                model.prefill(prompt, toks[0:1])
+                if decode:
+                    for i in range(128):
+                        model.decode_step(toks[i:i + 1], toks[i + 1:i + 2])
+                model.sync()
+                n += 1
+            j1, s1 = read()
+            return j1 - j0, s1 - s0, n
+
+        ea, sa, na = window(True)
+        eb, sb, nb = window(False)
+        if ea <= 0 or eb <= 0 or sa <= 0 or sb <= 0:
+            return {"error": f"energy accumulator did not advance (A {ea} J over {sa} s, B {eb} J over {sb} s)"}
+        e_pf = eb / nb
+        e_tok = (ea / na - e_pf) / 128
+        t_tok = (sa / na - sb / nb) / 128
+        w = lambda v: round(v * 1e-6, 1) if v > 1e5 else v   # caps are reported in microwatts
+        return {"decode_tok_per_j": round(1 / e_tok, 3), "decode_j_per_tok": round(e_tok, 4),
+                "decode_avg_power_w": round(e_tok / t_tok, 1), "decode_tok_s_in_window": round(1 / t_tok, 1),
+                "prefill_pp520_j": round(e_pf, 3), "prefill_tok_per_j": round(520 / e_pf, 1),
+                "prefill_avg_power_w": round(eb / sb, 1),
+                "window_a": {"rounds": na, "seconds": round(sa, 3), "joules": round(ea, 1)},
+                "window_b": {"rounds": nb, "seconds": round(sb, 3), "joules": round(eb, 1)},
+                "power_cap_w": w(cap["power_cap"]),
+                "note": "socket energy accumulator (15.3 uJ units) and its timestamp; the host synchronises "
+                        "after every round, so idle gaps between launches are inside the windows"}
+    except Exception as e:  # noqa: BLE001
+        return {"error": f"energy read failed: {e}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +317,7 @@ def main():
     ap.add_argument("--workload", default="24L-pp520-tg128", choices=WORKLOAD_CHOICES)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-energy", action="store_true", help="skip the energy-per-token windows of the extras")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the secondary measurements (verify forwards, 8192-token context)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -341,6 +410,8 @@ def main():
     }
     if not args.no_extras and wl.name == "24L-pp520-tg128":
         line["extras"] = extras(model, cfg, stream)
+        if not args.no_energy:
+            line["extras"]["energy"] = energy(model, cfg, stream)
     del model
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
