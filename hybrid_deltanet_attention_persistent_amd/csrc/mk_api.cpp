@@ -179,7 +179,7 @@ Plan make_plan(const mk_config *c) {
       r.dn_out = L.add((size_t)p.nh * H * p.dv * 2);
       r.S = L.add((size_t)p.nh * p.dv * p.dk * 4);
       r.ring = L.add((size_t)MK_RING * p.C * 4);
-      r.pend = L.add((size_t)2 * p.nh * MK_MAXCOL * (p.dk + p.dv + 2) * 4);
+      r.pend = L.add((size_t)2 * p.nh * MK_MAXCOL * mk_pend_stride(p.dv) * 4);
     } else {
       r.at_q = L.add((size_t)p.nq * p.hd * H * 2);
       r.at_k = L.add((size_t)p.nkv * p.hd * H * 2);

@@ -592,18 +592,28 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       wr[2 * NRG_IN + r] = __builtin_amdgcn_raw_buffer_load_b128(ro, rg < ngo ? (uint32_t)((rg * 64 + lane) * 16) : OOB_OFF, 0, AUX_NT);
     }
     // attention: this lane's cached K and V rows of the first NKV_PRE key steps (keys lg + 16 ks,
-    // slot ks = step * MK_WAVES * kpw + w8 * kpw + lane / lpk; 16 bytes of one row per lane)
+    // slot ks = step * MK_WAVES * kpw + w8 * kpw + lane / lpk; 16 bytes of one row per lane).
+    // DeltaNet: the same registers take the pending updates left by a verify forward, update j in
+    // slots 2 j (v, alpha, beta of this wave's row) and 2 j + 1 (this lane's key quad), so that
+    // D2 replays them without a memory round trip per update.
     {
       const bool at = live && !dn && x < nq;
-      const int lpk = hd / 8, kpw = 64 / lpk;
+      const bool pdn = live && dn && x < nh && pend_n > 0;
+      const int lpk = hd / 8, kpw = 64 / lpk, pks = mk_pend_stride(dv);
       const __amdgpu_buffer_rsrc_t krs = tile_rsrc(ly.kc, at ? 0x7fffffffu : 0u);
       const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(ly.vc, at ? 0x7fffffffu : 0u);
+      const __amdgpu_buffer_rsrc_t prs =
+          tile_rsrc(ly.pend + ((size_t)par * nh + (pdn ? x : 0)) * MK_MAXCOL * pks, pdn ? (uint32_t)(MK_MAXCOL * pks * 4) : 0u);
+      const int prow = (w8 < RW) ? r0 + w8 : -1;
 #pragma unroll
       for (int st = 0; st < NKV_PRE; ++st) {
         const int ks = st * MK_WAVES * kpw + w8 * kpw + lane / lpk, k = lg + MK_NG * ks;
         const uint32_t off = (k < pos0) ? kv_off(ptl, k, kvh, nkv, hd, (lane % lpk) * 8) : OOB_OFF;
-        wr[2 * NRG_IN + NRG_O + 2 * st] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-        wr[2 * NRG_IN + NRG_O + 2 * st + 1] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+        const bool pj = st < pend_n;
+        const uint32_t pv = (pj && prow >= 0) ? (uint32_t)((st * pks + MK_PEND_K + 4 * prow) * 4) : OOB_OFF;
+        const uint32_t pk = pj ? (uint32_t)((st * pks + 4 * lane) * 4) : OOB_OFF;
+        wr[2 * NRG_IN + NRG_O + 2 * st] = __builtin_amdgcn_raw_buffer_load_b128(dn ? prs : krs, dn ? pv : off, 0, 0);
+        wr[2 * NRG_IN + NRG_O + 2 * st + 1] = __builtin_amdgcn_raw_buffer_load_b128(dn ? prs : vrs, dn ? pk : off, 0, 0);
       }
     }
     // this wave's DeltaNet state: its row of S, the conv taps and history of its lane's channel,
@@ -813,11 +823,12 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               if (J2 > 1) p = fmaf(srow[1], e1, p);
               return wave_sum(p);
             };
-            const float *pk_base = ly.pend + ((size_t)par * nh + x) * MK_MAXCOL * (dk + dv + 2);
-            for (int j = 0; j < pend_n; ++j) {  // pending updates left by a verify forward
-              const float *pk = pk_base + j * (dk + dv + 2);
-              const float aj = pk[dk + dv], bj = pk[dk + dv + 1], vj = pk[dk + r0 + w8];
-              const float k0 = pk[lane], k1 = (J2 > 1) ? pk[64 + lane] : 0.f;
+#pragma unroll
+            for (int j = 0; j < MK_MAXCOL; ++j) {  // pending updates left by a verify forward (in registers)
+              if (j >= pend_n) break;
+              const u32x4 pvj = wr[2 * NRG_IN + NRG_O + 2 * j], pkj = wr[2 * NRG_IN + NRG_O + 2 * j + 1];
+              const float vj = __uint_as_float(pvj.x), aj = __uint_as_float(pvj.y), bj = __uint_as_float(pvj.z);
+              const float k0 = __uint_as_float(pkj.x), k1 = (J2 > 1) ? __uint_as_float(pkj.y) : 0.f;
               const float u = bj * (vj - aj * rowdot(k0, k1));
               srow[0] = fmaf(u, k0, aj * srow[0]);
               if (J2 > 1) srow[1] = fmaf(u, k1, aj * srow[1]);
@@ -827,7 +838,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               Srow[lane] = srow[0];
               if (J2 > 1) Srow[64 + lane] = srow[1];
             }
-            float *pw = ly.pend + ((size_t)(par ^ 1) * nh + x) * MK_MAXCOL * (dk + dv + 2);
+            float *pw = ly.pend + ((size_t)(par ^ 1) * nh + x) * MK_MAXCOL * mk_pend_stride(dv);
             FOR_COL(c) {
               const float qr = rsqrtf(((rsq[c * 8 + 0] + rsq[c * 8 + 1]) + rsq[c * 8 + 2]) + rsq[c * 8 + 3] + m.l2_eps);
               const float kr = rsqrtf(((rsq[c * 8 + 4] + rsq[c * 8 + 5]) + rsq[c * 8 + 6]) + rsq[c * 8 + 7] + m.l2_eps);
@@ -847,13 +858,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 pub_xcd(xo + c * x_o_len + dv + r0 + w8, uo, tg);
               }
               if (verify) {  // (k, v, alpha, beta) of this column become a pending update
-                float *pc = pw + c * (dk + dv + 2);
-                if (lg == 0 && w8 == 0) {
-                  pc[lane] = k0;
-                  if (J2 > 1) pc[64 + lane] = k1;
-                  if (lane == 0) { pc[dk + dv] = al; pc[dk + dv + 1] = be; }
-                }
-                if (lane == 0) pc[dk + r0 + w8] = vr;
+                float *pc = pw + c * mk_pend_stride(dv);
+                if (lg == 0 && w8 == 0) *reinterpret_cast<float4 *>(pc + 4 * lane) = make_float4(k0, k1, 0.f, 0.f);
+                if (lane == 0) *reinterpret_cast<float4 *>(pc + MK_PEND_K + 4 * (r0 + w8)) = make_float4(vr, al, be, 0.f);
               }
             }
             if (!verify) {

@@ -44,6 +44,12 @@ struct MkTile {
   int32_t rows, K, G, L;
 };
 
+// Pending delta-rule updates of a verify forward, per (parity, head, column): the key as 64 lane
+// quads (k[l], k[64 + l], 0, 0) (MK_PEND_K floats; dk <= 128), then one quad per value row
+// (v_r, alpha, beta, 0).  Every part is a 16-byte load per lane for the kernels that replay them.
+#define MK_PEND_K 256
+__host__ __device__ static inline int mk_pend_stride(int dv) { return MK_PEND_K + 4 * dv; }
+
 struct MkLayerDev {
   int32_t kind;                       // 0 DeltaNet, 1 attention
   int32_t idx;                        // index among layers of the same kind
@@ -55,7 +61,7 @@ struct MkLayerDev {
   const uint16_t *dn_out;             // [nh] tiles [H][dv]   (columns of head h of W_out)
   float *S;                           // [nh][dv][dk]
   float *ring;                        // [MK_RING][C] pre-conv inputs by position % MK_RING
-  float *pend;                        // [2][nh][MK_MAXCOL][dk + dv + 2]: k | v | alpha beta
+  float *pend;                        // [2][nh][MK_MAXCOL][mk_pend_stride(dv)] pending updates (layout below)
   // attention
   const uint16_t *at_q;               // [nq] tiles [hd][H]
   const uint16_t *at_k, *at_v;        // [nkv] tiles [hd][H]

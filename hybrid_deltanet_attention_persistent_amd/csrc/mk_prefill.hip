@@ -746,7 +746,7 @@ __global__ void __launch_bounds__(CP_THREADS) pf_dn_chunk_prep(PfChunk c) {
 
 struct PfScan {
   float *S;                        // [nh][dv][dk] layer state
-  const float *pend;               // [2][nh][MAXCOL][dk + dv + 2] pending updates (k | v | alpha beta)
+  const float *pend;               // [2][nh][MAXCOL][mk_pend_stride(dv)] pending updates (mk_layout.h)
   const int32_t *ctl;
   const float *cW, *cU, *cKt, *cg, *cd;
   float *snap;                     // [nh][PT/CHUNK][dv][dk] the state entering each chunk
@@ -798,14 +798,15 @@ __global__ void __launch_bounds__(SCAN_THREADS) pf_dn_scan(PfScan s) {
   // pending updates left by a verify forward (same arithmetic as the decode kernel's step)
   const int pend_n = s.ctl[MK_CTL_PEND], par = s.ctl[MK_CTL_PAR];
   for (int jp = 0; jp < pend_n; ++jp) {
-    const float *pk = s.pend + (((size_t)par * s.nh + h) * MK_MAXCOL + jp) * (2 * DK + 2);
-    const float a = pk[2 * DK], b = pk[2 * DK + 1];
+    const float *pk = s.pend + (((size_t)par * s.nh + h) * MK_MAXCOL + jp) * mk_pend_stride(DK);
+    const float *pv = pk + MK_PEND_K;   // (v_r, alpha, beta, 0) per value row
+    const float a = pv[1], b = pv[2];
     for (int r = w; r < SR; r += SCAN_THREADS / 64) {
       float p = 0.f;
-      for (int e = lane; e < DK; e += 64) p = fmaf(Sl[r * SL + e], pk[e], p);
+      for (int e = lane; e < DK; e += 64) p = fmaf(Sl[r * SL + e], pk[4 * (e & 63) + (e >> 6)], p);
       const float sk = wave_sum(p);
-      const float u = b * (pk[DK + r0 + r] - a * sk);
-      for (int e = lane; e < DK; e += 64) Sl[r * SL + e] = fmaf(u, pk[e], a * Sl[r * SL + e]);
+      const float u = b * (pv[4 * (r0 + r)] - a * sk);
+      for (int e = lane; e < DK; e += 64) Sl[r * SL + e] = fmaf(u, pk[4 * (e & 63) + (e >> 6)], a * Sl[r * SL + e]);
     }
   }
   __syncthreads();
