@@ -54,6 +54,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LMAX_D 8   // FFN role: loads per lane of one down-projection row group
 #define NWR 24     // registers (u32x4) of the larger role: 4 NPAIR + LMAX_D >= 2 NRG_IN + NRG_O
 #define NKV_PRE 6  // mixer role: attention key steps whose cached K and V rows are prefetched (2 NKV_PRE spare registers)
+#define KV_GRP 4   // later key steps whose loads are issued together
 #define LM_BATCH(NCOL) ((NCOL) == 1 ? 8 : 4)
 
 // ------------------------------------------------------------------------------ helpers
@@ -1008,12 +1009,23 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                   score(st * spw + kslot, kf);
                 }
               }
+              // later steps: KV_GRP steps' loads issued together, then used in step order
 #pragma unroll 1
-              for (int st = NKV_PRE; st < nstc; ++st) {
-                const int ks = st * spw + kslot;
-                float kf[8];
-                unpack8(__builtin_amdgcn_raw_buffer_load_b128(krs, ks < ncache ? kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : OOB_OFF, 0, 0), kf);
-                score(ks, kf);
+              for (int st = NKV_PRE; st < nstc; st += KV_GRP) {
+                u32x4 kr[KV_GRP];
+#pragma unroll
+                for (int u = 0; u < KV_GRP; ++u) {
+                  const int ks = (st + u) * spw + kslot;
+                  kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, ks < ncache ? kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : OOB_OFF, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < KV_GRP; ++u) {
+                  if (st + u < nstc) {
+                    float kf[8];
+                    unpack8(kr[u], kf);
+                    score((st + u) * spw + kslot, kf);
+                  }
+                }
               }
               if (hascur && w8 == 0 && lane < lpk) {   // this forward's key: from LDS
                 const float *kk = qkv + (kc_ - pos0) * 3 * hd + hd + d0;
@@ -1057,11 +1069,21 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 }
               }
 #pragma unroll 1
-              for (int st = NKV_PRE; st < nstc; ++st) {
-                const int ks = st * spw + kslot;
-                float vf[8];
-                unpack8(__builtin_amdgcn_raw_buffer_load_b128(vrs, ks < ncache ? kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : OOB_OFF, 0, 0), vf);
-                pvacc(ks, vf);
+              for (int st = NKV_PRE; st < nstc; st += KV_GRP) {
+                u32x4 vr[KV_GRP];
+#pragma unroll
+                for (int u = 0; u < KV_GRP; ++u) {
+                  const int ks = (st + u) * spw + kslot;
+                  vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ks < ncache ? kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : OOB_OFF, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < KV_GRP; ++u) {
+                  if (st + u < nstc) {
+                    float vf[8];
+                    unpack8(vr[u], vf);
+                    pvacc((st + u) * spw + kslot, vf);
+                  }
+                }
               }
               // this forward's value, from LDS, added by the lanes that own its slot in the step order
               // (as a cached key of a later decode step it is accumulated there: same additions, same
