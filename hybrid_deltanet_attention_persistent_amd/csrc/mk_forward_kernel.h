@@ -498,8 +498,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   ConstLayer *const layers = (ConstLayer *)(uintptr_t)m.layers;
 
   float *xres = lds_raw;                        // [NCOL][H] residual stream
-  float *work = xres + NCOL * H;                // [8192] phase scratch
-  float *red = work + 8192;                     // [64] reductions
+  constexpr int WORK = NCOL == 1 ? 8192 : 12288;  // phase scratch (verify: the merge of all columns' partials)
+  float *work = xres + NCOL * H;                // [WORK] phase scratch
+  float *red = work + WORK;                     // [64] reductions
   int *flag = reinterpret_cast<int *>(red + 64);
   // the page table of the KV cache (logical page -> physical page), read once per launch
   int *ptl = flag + 16;                         // [160] (10240 positions / 64)
@@ -1130,35 +1131,41 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           MK_TRACE_POINT(li, 4);
           // ---- A3: merge the 16 partials + o-projection columns of head x
           {
+            // every column's partials in one gather; the scales of column c in wave c; then the
+            // merged outputs of all columns (per column the same arithmetic as one column alone)
             const int plen = hd + 2;
-            float *part = work + 2048;             // [16][plen]
-            float *ov = work;                      // [NCOL][hd]
-            for (int c = 0; c < ncol; ++c) {
-              if (!gather2d<3, MK_WAVES>(xo + c * x_o_len, 1, MK_NG * plen, 0, tg, part, flag, m.ctl, SITE(7), tid)) MK_BAIL();
-              // per-partial scale exp(m_w - M) (0 for workgroups without keys), once, in wave 0
-              float *scl = part + MK_NG * plen;     // [16] scales, [16] = sum of l_w * scale
-              if (w8 == 0) {
-                const bool has = lane < MK_NG && part[lane * plen + 1] > 0.f;
-                float M = has ? part[lane * plen] : -INFINITY;
+            float *ov = work;                        // [NCOL][hd]
+            float *part = work + NCOL * hd;          // [NCOL][16][plen]
+            float *scl = part + NCOL * MK_NG * plen; // [NCOL][17]: per-partial scales, [16] = sum of l_w * scale
+            constexpr int A3C = NCOL == 1 ? 3 : 6;
+            if (!gather2d<A3C, MK_WAVES>(xo, ncol, MK_NG * plen, x_o_len, tg, part, flag, m.ctl, SITE(7), tid)) MK_BAIL();
+            // per-partial scale exp(m_w - M) (0 for workgroups without keys)
+            if (w8 < ncol) {
+              const float *pc = part + w8 * MK_NG * plen;
+              float *sc = scl + w8 * (MK_NG + 1);
+              const bool has = lane < MK_NG && pc[lane * plen + 1] > 0.f;
+              float M = has ? pc[lane * plen] : -INFINITY;
 #pragma unroll
-                for (int off = MK_NG / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-                const float sv = has ? __expf(part[lane * plen] - M) : 0.f;
-                if (lane < MK_NG) scl[lane] = sv;
-                if (lane == 0) {  // (LDS writes of one wave are seen by its later reads)
-                  float Ls = 0.f;
-                  for (int ww = 0; ww < MK_NG; ++ww) Ls = fmaf(part[ww * plen + 1], scl[ww], Ls);
-                  scl[MK_NG] = Ls;
-                }
+              for (int off = MK_NG / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+              const float sv = has ? __expf(pc[lane * plen] - M) : 0.f;
+              if (lane < MK_NG) sc[lane] = sv;
+              if (lane == 0) {  // (LDS writes of one wave are seen by its later reads)
+                float Ls = 0.f;
+                for (int ww = 0; ww < MK_NG; ++ww) Ls = fmaf(pc[ww * plen + 1], sc[ww], Ls);
+                sc[MK_NG] = Ls;
               }
-              lbar();
-              for (int d = tid; d < hd; d += MK_THREADS) {
-                float acc = 0.f;
-#pragma unroll 8
-                for (int ww = 0; ww < MK_NG; ++ww) acc = fmaf(part[ww * plen + 2 + d], scl[ww], acc);
-                ov[c * hd + d] = acc / scl[MK_NG];
-              }
-              lbar();
             }
+            lbar();
+            for (int i = tid; i < ncol * hd; i += MK_THREADS) {
+              const int c = i / hd, d = i - c * hd;
+              const float *pc = part + c * MK_NG * plen;
+              const float *sc = scl + c * (MK_NG + 1);
+              float acc = 0.f;
+#pragma unroll 8
+              for (int ww = 0; ww < MK_NG; ++ww) acc = fmaf(pc[ww * plen + 2 + d], sc[ww], acc);
+              ov[c * hd + d] = acc / sc[MK_NG];
+            }
+            lbar();
             MK_TRACE_POINT(li, 5);
             const int kl = (lane & (G_a - 1)) * 8;
             FOR_COL(c) {
