@@ -37,7 +37,7 @@ from typing import Dict, List, Tuple
 import numpy as np
 
 from workloads import ModelConfig, DELTANET
-from .ops import (round_bf16, bf16_bits_to_f64, rmsnorm, silu, l2norm, gates, causal_conv,
+from .ops import (round_bf16, kv_q8_rows, bf16_bits_to_f64, rmsnorm, silu, l2norm, gates, causal_conv,
                   delta_rule_step, rope, gated_rmsnorm, swiglu, argmax_lowest)
 
 
@@ -144,7 +144,9 @@ class OracleModel:
         q = rope((h @ w[p + "wq"].T).reshape(T, c.at_q_heads, d), pos[:, None], c.rope_theta)
         k = rope((h @ w[p + "wk"].T).reshape(T, c.at_kv_heads, d), pos[:, None], c.rope_theta)
         v = (h @ w[p + "wv"].T).reshape(T, c.at_kv_heads, d)
-        if self.contract.kv_bf16:
+        if c.kv_quant:                  # 8-bit codes, power-of-two scale per cached row
+            k, v = kv_q8_rows(k)[2], kv_q8_rows(v)[2]
+        elif self.contract.kv_bf16:
             k, v = round_bf16(k), round_bf16(v)
         self.Kc[li][self.pos:self.pos + T] = k
         self.Vc[li][self.pos:self.pos + T] = v

@@ -34,7 +34,7 @@ __all__ = [
     "round_bf16", "bf16_bits_to_f64", "rmsnorm", "sigmoid", "silu", "softplus", "l2norm",
     "gates", "causal_conv", "delta_rule_step", "delta_rule_step_literal", "delta_rule_chunked",
     "rope", "rope_inv_freq", "attention_masked_dense", "attention_one_query", "gated_rmsnorm",
-    "swiglu", "argmax_lowest",
+    "swiglu", "argmax_lowest", "kv_q8_rows",
 ]
 
 
@@ -53,6 +53,27 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     hi = hi + up.astype(np.uint64)
     out = (hi << np.uint64(16)).astype(np.uint32).view(np.float32)
     return out.astype(np.float64)
+
+
+def kv_q8_rows(x: np.ndarray):
+    """8-bit KV-cache quantisation with one power-of-two scale per row (the last axis).
+
+    The pages name an 8-bit KV cache ("q8" on the Korean update page, limits section; block-quantised
+    KV caches on the RTX 3090 tag page) without defining its format; the reading used here: per
+    cached row (one position of one KV head), in float32, a = max |x_i|, e = the smallest integer
+    with a <= 127 * 2^e (e = -7 for an all-zero row), codes q_i = round-half-even(x_i * 2^-e) in
+    [-127, 127], stored value q_i * 2^e.  A power-of-two scale keeps every stored value exactly a
+    bfloat16 number (|q| <= 127 needs 7 significant bits).
+
+    Returns (codes int8 [..., d], exponents int32 [...], values float64 [..., d])."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    a = np.max(np.abs(x32), axis=-1)
+    _, E = np.frexp(a.astype(np.float64))                   # a in [2^(E-1), 2^E), E = 0 for a == 0
+    E = E.astype(np.int64)
+    e = np.where(a.astype(np.float64) <= np.ldexp(127.0, E - 7), E - 7, E - 6)
+    scaled = np.ldexp(x32.astype(np.float64), -e[..., None])  # exact: a power-of-two rescaling
+    q = np.clip(np.rint(scaled), -127, 127).astype(np.int64)  # rint: ties to even
+    return q.astype(np.int8), e.astype(np.int32), np.ldexp(q.astype(np.float64), e[..., None])
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -50,6 +50,7 @@ class ModelConfig:
     max_ctx: int = 8448
     prefill_chunk: int = 64
     max_verify: int = 5
+    kv_quant: int = 0          # 0: K/V cache in bfloat16; 1: 8-bit codes with a power-of-two scale per row
 
     @property
     def n_layers(self) -> int:
@@ -82,7 +83,11 @@ HYBRID_24L = ModelConfig(
     dn_heads=8, dn_dk=128, dn_dv=128, conv_k=4,
     at_q_heads=8, at_kv_heads=2, at_head_dim=128, max_ctx=8448)
 
-MODELS = {TINY.name: TINY, HYBRID_24L.name: HYBRID_24L}
+# the same models with the 8-bit K/V cache (codes + a power-of-two scale per cached row)
+TINY_Q8 = dataclasses.replace(TINY, name="tiny-hybrid-4L-q8", kv_quant=1)
+HYBRID_24L_Q8 = dataclasses.replace(HYBRID_24L, name="hybrid-24L-h1024-q8", kv_quant=1)
+
+MODELS = {m.name: m for m in (TINY, HYBRID_24L, TINY_Q8, HYBRID_24L_Q8)}
 
 
 @dataclass(frozen=True)
