@@ -10,6 +10,7 @@ this host as a reported baseline.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -46,7 +47,8 @@ def decode_bytes_per_token(cfg: W.ModelConfig, ctx: float) -> dict:
     small = 4 * (n_dn * (cfg.conv_channels * cfg.conv_k + cfg.dn_dv) + 2 * cfg.n_layers * H + H)
     state = n_dn * cfg.dn_heads * cfg.dn_dv * cfg.dn_dk * 4 * 2
     conv = n_dn * cfg.conv_channels * 4 * (cfg.conv_k - 1 + 1)
-    kv_row = cfg.at_kv_heads * cfg.at_head_dim * 2 * 2      # K and V of one position, bf16
+    # K and V of one position: bf16, or (8-bit cache) one byte per element plus one exponent byte per row
+    kv_row = cfg.at_kv_heads * 2 * ((cfg.at_head_dim + 1) if cfg.kv_quant else cfg.at_head_dim * 2)
     kv = n_at * kv_row * (ctx + 1)
     return dict(weights=weights, all=weights + small + state + conv + kv)
 
@@ -132,11 +134,39 @@ def cpu_baseline(decode_seconds: float = 10.0) -> dict:
             "os_cpu_count": os.cpu_count()}
 
 
-def extras(model, cfg, stream) -> dict:
+def long_context(model, cfg, stream, n_prompt: int = 8192, n_decode: int = 128) -> dict:
+    """Prefill of an n_prompt-token seeded prompt, then n_decode chained greedy decode steps."""
+    import torch
+    dev = stream.device
+    prompt = torch.tensor(W.make_prompt(cfg, n_prompt, seed=1), dtype=torch.int32, device=dev)
+    toks = torch.zeros(n_decode + 1, dtype=torch.int32, device=dev)
+    model.reset()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    model.prefill(prompt, toks[0:1])
+    p1.record(stream)
+    e0.record(stream)
+    for i in range(n_decode):
+        model.decode_step(toks[i:i + 1], toks[i + 1:i + 2])
+    e1.record(stream)
+    model.sync()
+    pf_ms, dec_ms = p0.elapsed_time(p1), e0.elapsed_time(e1)
+    by = decode_bytes_per_token(cfg, n_prompt + (n_decode - 1) / 2.0)
+    us = dec_ms * 1e3 / n_decode
+    pf = prefill_flops(cfg, n_prompt)
+    return {"decode_tok_s": round(n_decode / (dec_ms * 1e-3), 1), "decode_us_per_token": round(us, 1),
+            "hbm_frac_all_bytes": round(by["all"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "hbm_frac_weights_only": round(by["weights"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "prefill_ms": round(pf_ms, 2), "prefill_tok_s": round(n_prompt / (pf_ms * 1e-3), 1),
+            "prefill_mfma_frac": round(pf["all"] / (pf_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def extras(model, cfg, stream, weights=None) -> dict:
     """Secondary measurements on the same model: multi-token verify forwards after the pp520
     prompt (1 accepted + 4 seeded random drafts each, state rolled back to the accepted prefix),
     greedy generation with lookup drafts after the same prompt, and decode at long context after
-    an 8192-token prompt."""
+    an 8192-token prompt, with the bf16 KV cache and (given the weights) with the 8-bit one."""
     import torch
     dev = stream.device
     out = {}
@@ -217,27 +247,15 @@ def extras(model, cfg, stream) -> dict:
                             "perfect_drafts": {"forwards": nfw, "accepted_per_forward": 5, "all_accepted": pl_ok,
                                                "committed_tok_per_s": round(5 * nfw / (pl_ms * 1e-3), 1)}}
     # long context: 8192-token prompt, 128 decode steps
-    prompt = torch.tensor(W.make_prompt(cfg, 8192, seed=1), dtype=torch.int32, device=dev)
-    toks = torch.zeros(129, dtype=torch.int32, device=dev)
-    model.reset()
-    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    p0.record(stream)
-    model.prefill(prompt, toks[0:1])
-    p1.record(stream)
-    e0.record(stream)
-    for i in range(128):
-        model.decode_step(toks[i:i + 1], toks[i + 1:i + 2])
-    e1.record(stream)
-    model.sync()
-    pf_ms, dec_ms = p0.elapsed_time(p1), e0.elapsed_time(e1)
-    by = decode_bytes_per_token(cfg, 8192 + 63.5)
-    us = dec_ms * 1e3 / 128
-    pf = prefill_flops(cfg, 8192)
-    out["long_context_8192"] = {"decode_tok_s": round(128 / (dec_ms * 1e-3), 1), "decode_us_per_token": round(us, 1),
-                                "hbm_frac_all_bytes": round(by["all"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                "hbm_frac_weights_only": round(by["weights"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                "prefill_ms": round(pf_ms, 2), "prefill_tok_s": round(8192 / (pf_ms * 1e-3), 1),
-                                "prefill_mfma_frac": round(pf["all"] / (pf_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    out["long_context_8192"] = long_context(model, cfg, stream)
+    if weights is not None:
+        import hybrid_deltanet_attention_persistent_amd as pkg
+        cfg8 = dataclasses.replace(cfg, name=cfg.name + "-q8", kv_quant=1)
+        m8 = pkg.Model(cfg8, weights, device=str(dev))
+        long_context(m8, cfg8, stream, 1024, 8)      # warm-up of the 8-bit instantiations
+        out["long_context_8192_kv8"] = long_context(m8, cfg8, stream)
+        out["long_context_8192_kv8"]["kv_cache"] = "int8 codes + power-of-two scale per row"
+        m8.close()
     return out
 
 
@@ -338,7 +356,6 @@ def main():
     weights = W.make_weights(cfg, seed=wl.weight_seed)
     prompt = torch.tensor(W.make_prompt(cfg, wl.prompt_len, seed=wl.prompt_seed), dtype=torch.int32, device=dev)
     model = pkg.Model(cfg, weights, device="cuda:0")
-    del weights
     T = wl.decode_steps
     tok = torch.zeros(T + 1, dtype=torch.int32, device=dev)
 
@@ -409,7 +426,7 @@ def main():
                      "launch_us": round(launch_us, 2)},
     }
     if not args.no_extras and wl.name == "24L-pp520-tg128":
-        line["extras"] = extras(model, cfg, stream)
+        line["extras"] = extras(model, cfg, stream, weights)
         if not args.no_energy:
             line["extras"]["energy"] = energy(model, cfg, stream)
     del model

@@ -17,8 +17,8 @@
 #include "mk.h"
 #include "mk_layout.h"
 
-extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, int shape, hipStream_t stream);
-extern "C" hipError_t mk_forward_occupancy(int ncol_template, int shape, int *blocks_per_cu);
+extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, int variant, hipStream_t stream);
+extern "C" hipError_t mk_forward_occupancy(int ncol_template, int variant, int *blocks_per_cu);
 extern "C" hipError_t mk_static_scratch(void **ptr);
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
                                          const int32_t *tokens, int n, int32_t *argmax, float *logits,
@@ -79,7 +79,7 @@ struct Layout {
 struct LayerRegions {
   Region ln1, ln2;
   Region dn_in, dn_conv, dn_gnorm, dn_out, S, ring, pend;
-  Region at_q, at_k, at_v, at_o, kc, vc;
+  Region at_q, at_k, at_v, at_o, kc, vc, kve;
   Region ffn_gu, ffn_dn;
 };
 
@@ -128,6 +128,7 @@ int check_config(const mk_config *c, std::string &why) {
   if (c->max_ctx <= 0 || c->max_ctx % MK_PAGE != 0 || c->max_ctx > 10240) { why = "max_ctx must be a multiple of 64 in [64, 10240]"; return MK_EINVAL; }
   if (c->prefill_chunk != 64) { why = "prefill_chunk must be 64"; return MK_EINVAL; }
   if (c->max_verify < 1 || c->max_verify > MK_MAXCOL) { why = "max_verify must be in [1, 5]"; return MK_EINVAL; }
+  if (c->kv_quant != 0 && c->kv_quant != 1) { why = "kv_quant must be 0 (bf16 cache) or 1 (8-bit codes)"; return MK_EINVAL; }
   {  // per-wave register budgets of the persistent kernel (weight rows held per phase): each role
      // (token mixer, FFN) has MK_NG workgroups of 8 weight-streaming waves per XCD
     const int Gh = mk_tile_G(c->hidden), RGh = 64 / Gh, XW = MK_NG * MK_WAVES;
@@ -185,8 +186,10 @@ Plan make_plan(const mk_config *c) {
       r.at_k = L.add((size_t)p.nkv * p.hd * H * 2);
       r.at_v = L.add((size_t)p.nkv * p.hd * H * 2);
       r.at_o = L.add((size_t)p.nq * H * p.hd * 2);
-      r.kc = L.add((size_t)p.max_pages * p.nkv * MK_PAGE * p.hd * 2);
-      r.vc = L.add((size_t)p.max_pages * p.nkv * MK_PAGE * p.hd * 2);
+      const size_t cb = c->kv_quant ? 1 : 2;   // bytes per cached element: int8 code or bf16
+      r.kc = L.add((size_t)p.max_pages * p.nkv * MK_PAGE * p.hd * cb);
+      r.vc = L.add((size_t)p.max_pages * p.nkv * MK_PAGE * p.hd * cb);
+      r.kve = L.add(c->kv_quant ? (size_t)p.max_pages * p.nkv * MK_PAGE * 2 : 0);
     }
     r.ffn_gu = L.add((size_t)2 * p.I * H * 2);
     r.ffn_dn = L.add((size_t)H * p.I * 2);
@@ -342,10 +345,10 @@ static int check_device(int *dev) {
     return fail(MK_ELAUNCH, std::string("device is ") + prop.gcnArchName + ", need gfx950 (MI355X)");
   if (prop.multiProcessorCount != MK_NWG)
     return fail(MK_ELAUNCH, "device has " + std::to_string(prop.multiProcessorCount) + " CUs, need 256 (8 XCDs x 32)");
-  for (int shape : {MK_SHAPE_ANY, MK_SHAPE_H1024})
+  for (int variant = 0; variant < MK_N_VARIANTS; ++variant)
     for (int tmpl : {1, MK_MAXCOL}) {
       int per_cu = 0;
-      HIPCHECK(mk_forward_occupancy(tmpl, shape, &per_cu));
+      HIPCHECK(mk_forward_occupancy(tmpl, variant, &per_cu));
       if (per_cu < 1) return fail(MK_ELAUNCH, "persistent kernel does not fit on a CU");
     }
   return MK_OK;
@@ -395,6 +398,7 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   d.nh = p.nh; d.dk = p.dk; d.dv = p.dv; d.C = p.C; d.r_in = p.r_in;
   d.nq = p.nq; d.nkv = p.nkv; d.hd = p.hd; d.r_in_max = p.r_in_max; d.x_o_len = p.x_o_len; d.xm_len = p.xm_len;
   d.max_ctx = cfg->max_ctx; d.max_pages = p.max_pages;
+  d.kv_quant = cfg->kv_quant;
   d.rms_eps = cfg->rms_eps; d.l2_eps = cfg->l2_eps;
   d.embed = (const uint16_t *)(A + p.embed.off);
   d.lnf = (const float *)(A + p.lnf.off);
@@ -487,8 +491,9 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
       L.at_k = (const uint16_t *)(A + r.at_k.off);
       L.at_v = (const uint16_t *)(A + r.at_v.off);
       L.at_o = (const uint16_t *)(A + r.at_o.off);
-      L.kc = (uint16_t *)(A + r.kc.off);
-      L.vc = (uint16_t *)(A + r.vc.off);
+      L.kc = A + r.kc.off;
+      L.vc = A + r.vc.off;
+      L.kve = cfg->kv_quant ? (int8_t *)(A + r.kve.off) : nullptr;
     }
     {
       const int J = p.J;
@@ -634,7 +639,7 @@ static int decode_launch(mk_model *m, const int32_t *d_tokens, int32_t n_tokens,
     a.tag0 = m->tag;
     a.xch = m->xch;
   }
-  HIPCHECK(mk_launch_forward(&a, tmpl, mk_shape_of(m->dev), st));
+  HIPCHECK(mk_launch_forward(&a, tmpl, mk_variant_of(m->dev), st));
   if (!use_static) m->tag += 1;
   m->pos_hi += n_tokens;
   return MK_OK;

@@ -36,12 +36,17 @@ extern "C" hipError_t mk_static_scratch(void **ptr) {
 
 // ------------------------------------------------------------------------------ host-side launchers
 // Instantiations: one decode column (here) or up to MK_MAXCOL verify columns (mk_verify.hip), each
-// for the generic and the hidden-1024 shape.
-const void *mk_verify_kernel(int shape);
+// for the generic and the hidden-1024 shape, with a bf16 or an 8-bit KV cache.
+const void *mk_verify_kernel(int variant);
 
-static const void *forward_fn(int ncol_template, int shape) {
-  if (ncol_template != 1) return mk_verify_kernel(shape);
-  return (shape == MK_SHAPE_H1024) ? (const void *)mk_forward<1, MK_SHAPE_H1024> : (const void *)mk_forward<1, MK_SHAPE_ANY>;
+static const void *forward_fn(int ncol_template, int variant) {
+  if (ncol_template != 1) return mk_verify_kernel(variant);
+  switch (variant) {
+    case MK_SHAPE_H1024: return (const void *)mk_forward<1, MK_SHAPE_H1024>;
+    case MK_SHAPE_ANY | MK_KV_Q8: return (const void *)mk_forward<1, MK_SHAPE_ANY | MK_KV_Q8>;
+    case MK_SHAPE_H1024 | MK_KV_Q8: return (const void *)mk_forward<1, MK_SHAPE_H1024 | MK_KV_Q8>;
+    default: return (const void *)mk_forward<1, MK_SHAPE_ANY>;
+  }
 }
 
 // The workgroups wait for each other's data, so all 256 must be resident at once.  The launch does
@@ -50,13 +55,13 @@ static const void *forward_fn(int ncol_template, int shape) {
 // and the CU count at load), launches on one stream run one after the other, and every wait is
 // bounded -- if another process's kernel held CUs so that some workgroups could not start, the
 // resident ones report MK_EHANG after the watchdog instead of waiting forever.
-extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, int shape, hipStream_t stream) {
+extern "C" hipError_t mk_launch_forward(const MkLaunch *a, int ncol_template, int variant, hipStream_t stream) {
   void *args[] = {const_cast<MkLaunch *>(a)};
-  return hipLaunchKernel(forward_fn(ncol_template, shape), dim3(MK_NWG), dim3(MK_THREADS), args, MK_LDS_BYTES, stream);
+  return hipLaunchKernel(forward_fn(ncol_template, variant), dim3(MK_NWG), dim3(MK_THREADS), args, MK_LDS_BYTES, stream);
 }
 
-extern "C" hipError_t mk_forward_occupancy(int ncol_template, int shape, int *blocks_per_cu) {
-  const void *fn = forward_fn(ncol_template, shape);
+extern "C" hipError_t mk_forward_occupancy(int ncol_template, int variant, int *blocks_per_cu) {
+  const void *fn = forward_fn(ncol_template, variant);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, MK_LDS_BYTES);
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, MK_THREADS, MK_LDS_BYTES);

@@ -471,6 +471,39 @@ __device__ __forceinline__ uint32_t kv_off(const int *ptl, int k, int kvh, int n
   return (uint32_t)((((ptl[k / MK_PAGE] * nkv + kvh) * MK_PAGE + (k % MK_PAGE)) * hd + d) * 2);
 }
 
+// 8-bit cache: byte offset of codes [d, d + 16) of a cached row, and of the row's exponent pair
+// (K exponent, V exponent) in [page][kv head][MK_PAGE][2].
+__device__ __forceinline__ uint32_t kv8_off(const int *ptl, int k, int kvh, int nkv, int hd, int d) {
+  return (uint32_t)(((ptl[k / MK_PAGE] * nkv + kvh) * MK_PAGE + (k % MK_PAGE)) * hd + d);
+}
+__device__ __forceinline__ uint32_t kve_off(const int *ptl, int k, int kvh, int nkv) {
+  return (uint32_t)(((ptl[k / MK_PAGE] * nkv + kvh) * MK_PAGE + (k % MK_PAGE)) * 2);
+}
+// 16 int8 codes (two's complement, lowest byte first) times 2^e, e in [-126, 127]: the biased code
+// c + 128 (a flipped sign bit) converts straight to FP32, and (c + 128) 2^e - 128 2^e is exact in
+// one FMA, so each result is exactly c * 2^e.
+__device__ __forceinline__ void deq16(const u32x4 &w, int e, float f[16]) {
+  const float s = __uint_as_float((uint32_t)(e + 127) << 23), nb = -128.f * s;
+  const uint32_t u[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u, w.w ^ 0x80808080u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[4 * i + j] = fmaf((float)((u[i] >> (8 * j)) & 0xffu), s, nb);
+}
+// A cached row's dims [d0, d0 + DPL) as FP32: 8 bf16 (DPL 8) or 16 codes with exponent e (DPL 16).
+// (The 16 converted values are made where used: hoisted out of the column loop, every prefetched
+// row's would be live at once.)
+template <int DPL>
+__device__ __forceinline__ void kv_unpack(const u32x4 &w, int e, float (&f)[DPL]) {
+  if constexpr (DPL == 16) {
+    u32x4 v = w;
+    asm volatile("" : "+v"(v), "+v"(e));
+    deq16(v, e, f);
+  } else {
+    unpack8(w, f);
+  }
+}
+
 // ------------------------------------------------------------------------------ the kernel
 template <int NCOL, int SH>
 __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
@@ -491,7 +524,11 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // d_k = d_v = 128, 8 query and 2 KV heads of 128, FFN 3584) at compile time: tile strides,
   // row-group counts and reduction widths fold into straight-line code.  SH == MK_SHAPE_ANY reads
   // them from the launch arguments.
-  constexpr bool FX = SH == MK_SHAPE_H1024;
+  constexpr bool FX = (SH & MK_SHAPE_H1024) != 0;
+  // MK_KV_Q8: the KV cache holds int8 codes with one exponent per row; a lane then takes 16
+  // dimensions of a cached row per 16-byte load instead of 8
+  constexpr bool KVQ = (SH & MK_KV_Q8) != 0;
+  constexpr int DPL = KVQ ? 16 : 8;
   const int H = FX ? 1024 : m.H;
   // the layer table is read-only: reading it through the constant address space gives
   // scalar loads, so every pointer taken from it is known to be wave-uniform
@@ -601,7 +638,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     {
       const bool at = live && !dn && x < nq;
       const bool pdn = live && dn && x < nh && pend_n > 0;
-      const int lpk = hd / 8, kpw = 64 / lpk, pks = mk_pend_stride(dv);
+      const int lpk = hd / DPL, kpw = 64 / lpk, pks = mk_pend_stride(dv);
       const __amdgpu_buffer_rsrc_t krs = tile_rsrc(ly.kc, at ? 0x7fffffffu : 0u);
       const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(ly.vc, at ? 0x7fffffffu : 0u);
       const __amdgpu_buffer_rsrc_t prs =
@@ -610,7 +647,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
 #pragma unroll
       for (int st = 0; st < NKV_PRE; ++st) {
         const int ks = st * MK_WAVES * kpw + w8 * kpw + lane / lpk, k = lg + MK_NG * ks;
-        const uint32_t off = (k < pos0) ? kv_off(ptl, k, kvh, nkv, hd, (lane % lpk) * 8) : OOB_OFF;
+        const uint32_t off = (k >= pos0) ? OOB_OFF
+                             : KVQ ? kv8_off(ptl, k, kvh, nkv, hd, (lane % lpk) * DPL) : kv_off(ptl, k, kvh, nkv, hd, (lane % lpk) * 8);
         const bool pj = st < pend_n;
         const uint32_t pv = (pj && prow >= 0) ? (uint32_t)((st * pks + MK_PEND_K + 4 * prow) * 4) : OOB_OFF;
         const uint32_t pk = pj ? (uint32_t)((st * pks + 4 * lane) * 4) : OOB_OFF;
@@ -935,6 +973,18 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           }
           MK_TRACE_POINT(li, 2);
           // ---- A2: RoPE, KV append, split-KV partials
+          // 8-bit cache: the exponent pairs of the prefetched rows, loaded here (not with the rows:
+          // held across the layer they would not fit in registers) and in flight during the gather
+          uint32_t kvx[NKV_PRE];
+          if constexpr (KVQ) {
+            const int lpk = hd / DPL, kpw = 64 / lpk;
+            const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(ly.kve, 0, 0x7fffffff, RSRC_W3);
+#pragma unroll
+            for (int st = 0; st < NKV_PRE; ++st) {
+              const int k = lg + MK_NG * (st * MK_WAVES * kpw + w8 * kpw + lane / lpk);
+              kvx[st] = __builtin_amdgcn_raw_buffer_load_b16(ers, (k < pos0) ? kve_off(ptl, k, kvh, nkv) : OOB_OFF, 0, 0);
+            }
+          }
           float *qkv = work;                    // [NCOL][3hd]
           if (!gather2d<MCS, MK_WAVES>(xin, ncol, 3 * hd, r_in_max, tg, qkv, flag, m.ctl, SITE(6), tid)) MK_BAIL();
           MK_TRACE_POINT(li, 3);
@@ -947,14 +997,48 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               const float q1 = q[d], q2 = q[d + half], k1 = k[d], k2 = k[d + half];
               q[d] = q1 * cs - q2 * sn;
               q[d + half] = q2 * cs + q1 * sn;
-              k[d] = rbf(k1 * cs - k2 * sn); k[d + half] = rbf(k2 * cs + k1 * sn);
-              v[d] = rbf(v[d]); v[d + half] = rbf(v[d + half]);
+              if constexpr (KVQ) {
+                k[d] = k1 * cs - k2 * sn; k[d + half] = k2 * cs + k1 * sn;
+              } else {
+                k[d] = rbf(k1 * cs - k2 * sn); k[d + half] = rbf(k2 * cs + k1 * sn);
+                v[d] = rbf(v[d]); v[d + half] = rbf(v[d + half]);
+              }
             }
           }
           lbar();
-          // the first query head of the kv group appends K, V (read by later launches only: this
-          // launch takes its own positions' keys and values from LDS)
-          if (lg == 0 && (x * nkv) % nq == 0) {
+          if constexpr (KVQ) {
+            // 8-bit cache: each K and V row of this forward (one wave per row) becomes codes and an
+            // exponent; LDS keeps the values they stand for, which is what later forwards read back
+            // from the cache.  The first query head of the kv group appends the rows.
+            const bool app = lg == 0 && (x * nkv) % nq == 0;
+            const __amdgpu_buffer_rsrc_t cst = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
+            const __amdgpu_buffer_rsrc_t vst = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
+            const __amdgpu_buffer_rsrc_t est = __builtin_amdgcn_make_buffer_rsrc(ly.kve, 0, 0x7fffffff, RSRC_W3);
+            for (int r = w8; r < 2 * ncol; r += MK_WAVES) {
+              const int c = r >> 1, isv = r & 1;
+              float *row = qkv + c * 3 * hd + (1 + isv) * hd;
+              const float x0 = lane < hd ? row[lane] : 0.f, x1 = lane + 64 < hd ? row[lane + 64] : 0.f;
+              float am = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+              for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+              const int e = mk_q8_exp(am);
+              const float q0 = rintf(ldexpf(x0, -e)), q1 = rintf(ldexpf(x1, -e));
+              const int p = pos0 + c;
+              const uint32_t rix = ((uint32_t)ptl[p / MK_PAGE] * nkv + kvh) * MK_PAGE + (p % MK_PAGE);
+              if (lane < hd) {
+                row[lane] = ldexpf(q0, e);
+                if (app) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int)q0, isv ? vst : cst, rix * hd + lane, 0, AUX_DEV);
+              }
+              if (lane + 64 < hd) {
+                row[lane + 64] = ldexpf(q1, e);
+                if (app) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int)q1, isv ? vst : cst, rix * hd + lane + 64, 0, AUX_DEV);
+              }
+              if (app && lane == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e, est, rix * 2 + isv, 0, AUX_DEV);
+            }
+            lbar();
+          } else if (lg == 0 && (x * nkv) % nq == 0) {
+            // the first query head of the kv group appends K, V (read by later launches only: this
+            // launch takes its own positions' keys and values from LDS)
             const __amdgpu_buffer_rsrc_t kst = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
             const __amdgpu_buffer_rsrc_t vst = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
             for (int i = tid; i < ncol * hd; i += MK_THREADS) {
@@ -978,10 +1062,15 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             float *pv = sc + 640;                  // [MK_WAVES][hd] partial P.V per wave
             float *mx = pv + MK_WAVES * hd;        // [2]: max, sum
             const float scale = 1.f / sqrtf((float)hd);
-            const int lpk = hd / 8, kpw = 64 / lpk, spw = MK_WAVES * kpw;
-            const int d0 = (lane % lpk) * 8, kslot = w8 * kpw + lane / lpk;
+            const int lpk = hd / DPL, kpw = 64 / lpk, spw = MK_WAVES * kpw;
+            const int d0 = (lane % lpk) * DPL, kslot = w8 * kpw + lane / lpk;
             const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
             const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
+            const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(KVQ ? (void *)ly.kve : nullptr, 0, KVQ ? 0x7fffffff : 0, RSRC_W3);
+            // byte offset of this lane's part of cached row ks (a slot below ncache), and of its exponents
+            auto row_off = [&](int ks) {
+              return KVQ ? kv8_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0);
+            };
             // cached keys of this workgroup: slots [0, ncache)
             const int ncache = (pos0 > lg) ? (pos0 - 1 - lg) / MK_NG + 1 : 0;
             const int nstc = (ncache + spw - 1) / spw;
@@ -992,21 +1081,21 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               // this forward's key of this workgroup, if any: position kc_ in [pos0, P], slot nk - 1
               const int kc_ = lg + MK_NG * (nk - 1);
               const bool hascur = nk > 0 && kc_ >= pos0;
-              float qv[8];
+              float qv[DPL];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) qv[i] = qkv[c * 3 * hd + d0 + i];
-              auto score = [&](int ks, const float (&kf)[8]) {
+              for (int i = 0; i < DPL; ++i) qv[i] = qkv[c * 3 * hd + d0 + i];
+              auto score = [&](int ks, const float (&kf)[DPL]) {
                 float sdot = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) sdot = fmaf(qv[i], kf[i], sdot);
+                for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kf[i], sdot);
                 sdot = group_sum(sdot, lpk);
                 if (ks < ncache && (lane % lpk) == 0) sc[ks] = sdot * scale;
               };
 #pragma unroll
               for (int st = 0; st < NKV_PRE; ++st) {
                 if (st < nstc) {
-                  float kf[8];
-                  unpack8(wr[2 * NRG_IN + NRG_O + 2 * st], kf);
+                  float kf[DPL];
+                  kv_unpack<DPL>(wr[2 * NRG_IN + NRG_O + 2 * st], (int)(int8_t)(kvx[st] & 0xffu), kf);
                   score(st * spw + kslot, kf);
                 }
               }
@@ -1014,16 +1103,19 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
 #pragma unroll 1
               for (int st = NKV_PRE; st < nstc; st += KV_GRP) {
                 u32x4 kr[KV_GRP];
+                uint32_t ke[KV_GRP];
 #pragma unroll
                 for (int u = 0; u < KV_GRP; ++u) {
                   const int ks = (st + u) * spw + kslot;
-                  kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, ks < ncache ? kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : OOB_OFF, 0, 0);
+                  kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, ks < ncache ? row_off(ks) : OOB_OFF, 0, 0);
+                  if constexpr (KVQ) ke[u] = __builtin_amdgcn_raw_buffer_load_b8(ers, ks < ncache ? kve_off(ptl, lg + MK_NG * ks, kvh, nkv) : OOB_OFF, 0, 0);
+                  else ke[u] = 0;
                 }
 #pragma unroll
                 for (int u = 0; u < KV_GRP; ++u) {
                   if (st + u < nstc) {
-                    float kf[8];
-                    unpack8(kr[u], kf);
+                    float kf[DPL];
+                    kv_unpack<DPL>(kr[u], (int)(int8_t)ke[u], kf);
                     score((st + u) * spw + kslot, kf);
                   }
                 }
@@ -1032,7 +1124,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 const float *kk = qkv + (kc_ - pos0) * 3 * hd + hd + d0;
                 float sdot = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) sdot = fmaf(qv[i], kk[i], sdot);
+                for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kk[i], sdot);
                 sdot = group_sum(sdot, lpk);
                 if (lane == 0) sc[nk - 1] = sdot * scale;
               }
@@ -1053,35 +1145,38 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               }
               lbar();
               // P.V over the same slots: each lane accumulates its 8 dimensions
-              float acc[8];
+              float acc[DPL];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-              auto pvacc = [&](int ks, const float (&vf)[8]) {
+              for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+              auto pvacc = [&](int ks, const float (&vf)[DPL]) {
                 const float pe = (ks < ncache) ? sc[ks < ncache ? ks : 0] : 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = fmaf(pe, vf[i], acc[i]);
+                for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vf[i], acc[i]);
               };
 #pragma unroll
               for (int st = 0; st < NKV_PRE; ++st) {
                 if (st < nstc) {
-                  float vf[8];
-                  unpack8(wr[2 * NRG_IN + NRG_O + 2 * st + 1], vf);
+                  float vf[DPL];
+                  kv_unpack<DPL>(wr[2 * NRG_IN + NRG_O + 2 * st + 1], (int)(int8_t)(kvx[st] >> 8), vf);
                   pvacc(st * spw + kslot, vf);
                 }
               }
 #pragma unroll 1
               for (int st = NKV_PRE; st < nstc; st += KV_GRP) {
                 u32x4 vr[KV_GRP];
+                uint32_t ve[KV_GRP];
 #pragma unroll
                 for (int u = 0; u < KV_GRP; ++u) {
                   const int ks = (st + u) * spw + kslot;
-                  vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ks < ncache ? kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : OOB_OFF, 0, 0);
+                  vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ks < ncache ? row_off(ks) : OOB_OFF, 0, 0);
+                  if constexpr (KVQ) ve[u] = __builtin_amdgcn_raw_buffer_load_b8(ers, ks < ncache ? kve_off(ptl, lg + MK_NG * ks, kvh, nkv) + 1 : OOB_OFF, 0, 0);
+                  else ve[u] = 0;
                 }
 #pragma unroll
                 for (int u = 0; u < KV_GRP; ++u) {
                   if (st + u < nstc) {
-                    float vf[8];
-                    unpack8(vr[u], vf);
+                    float vf[DPL];
+                    kv_unpack<DPL>(vr[u], (int)(int8_t)ve[u], vf);
                     pvacc((st + u) * spw + kslot, vf);
                   }
                 }
@@ -1094,11 +1189,11 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 const float pe = sc[nk - 1];
                 const float *vv = qkv + (kc_ - pos0) * 3 * hd + 2 * hd + d0;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = fmaf(pe, vv[i], acc[i]);
+                for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vv[i], acc[i]);
               }
               // sum over the kpw key groups of the wave (lanes l, l + lpk, ...), then over the waves
 #pragma unroll
-              for (int i = 0; i < 8; ++i) {
+              for (int i = 0; i < DPL; ++i) {
                 float v = acc[i];
                 if (lpk == 16) {
                   v = swap_add32(v, v);
@@ -1110,7 +1205,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               }
               if (lane < lpk) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pv[w8 * hd + d0 + i] = acc[i];
+                for (int i = 0; i < DPL; ++i) pv[w8 * hd + d0 + i] = acc[i];
               }
               lbar();
               const int plen = hd + 2;

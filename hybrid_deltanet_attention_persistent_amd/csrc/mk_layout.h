@@ -66,7 +66,8 @@ struct MkLayerDev {
   const uint16_t *at_q;               // [nq] tiles [hd][H]
   const uint16_t *at_k, *at_v;        // [nkv] tiles [hd][H]
   const uint16_t *at_o;               // [nq] tiles [H][hd]   (columns of head i of W_o)
-  uint16_t *kc, *vc;                  // [pages][nkv][MK_PAGE][hd] bf16
+  void *kc, *vc;                      // [pages][nkv][MK_PAGE][hd] bf16, or int8 codes with kv_quant
+  int8_t *kve;                        // kv_quant: [pages][nkv][MK_PAGE][2] exponents e of the K, V row
   // FFN (XCD x owns intermediate rows [x*J, (x+1)*J))
   const uint16_t *ffn_gu;             // [8] tiles [2J][H]: rows g_j, u_j interleaved
   const uint16_t *ffn_dn;             // [8] tiles [H][J]
@@ -98,6 +99,7 @@ struct MkDev {
   int32_t nq, nkv, hd;
   int32_t r_in_max, x_o_len, xm_len;  // exchange row lengths (slots), multiples of 32: 256-byte blocks
   int32_t max_ctx, max_pages;
+  int32_t kv_quant;                   // 0: bf16 cache; 1: int8 codes q, row value q * 2^e (e per row)
   float rms_eps, l2_eps;
   const uint16_t *embed;              // [V][H] (tile format with L == 1 or G == 64: row-major)
   const float *lnf;                   // [H]
@@ -120,13 +122,25 @@ struct MkLaunch {
 };
 
 // Instantiations of the persistent kernel: MK_SHAPE_H1024 has every dimension of the hidden-1024
-// model as a compile-time constant; MK_SHAPE_ANY reads them from MkDev.
-enum { MK_SHAPE_ANY = 0, MK_SHAPE_H1024 = 1 };
+// model as a compile-time constant; MK_SHAPE_ANY reads them from MkDev.  MK_KV_Q8 is or-ed in for
+// a model whose KV cache holds 8-bit codes.
+enum { MK_SHAPE_ANY = 0, MK_SHAPE_H1024 = 1, MK_KV_Q8 = 2, MK_N_VARIANTS = 4 };
 static inline int mk_shape_of(const MkDev &d) {
   const bool h1024 = d.H == 1024 && d.nh == 8 && d.dk == 128 && d.dv == 128 && d.nq == 8 && d.nkv == 2 &&
                      d.hd == 128 && d.J == 448 && d.r_in == 514 && d.C == 3072 && d.r_in_max == 544 &&
                      d.x_o_len == 2080 && d.xm_len == 448;
   return h1024 ? MK_SHAPE_H1024 : MK_SHAPE_ANY;
+}
+static inline int mk_variant_of(const MkDev &d) { return mk_shape_of(d) | (d.kv_quant ? MK_KV_Q8 : 0); }
+
+// 8-bit KV cache row: the exponent e of a row whose largest magnitude is a (FP32): the smallest
+// integer with a <= 127 * 2^e, but at least -126 (every nonzero q * 2^e is then a normal number).
+// The codes are round-half-even(x * 2^-e) in [-127, 127].
+__host__ __device__ static inline int mk_q8_exp(float a) {
+  union { float f; uint32_t u; } c;
+  c.f = a;
+  const int e = (int)(c.u >> 23) - 133 + ((c.u & 0x7fffffu) > 0x7e0000u ? 1 : 0);
+  return e < -126 ? -126 : e;
 }
 
 __host__ __device__ static inline int mk_tile_G(int K) {

@@ -979,13 +979,28 @@ __global__ void __launch_bounds__(DK * 4) pf_dn_out(PfOut o) {
 }
 
 // ------------------------------------------------------------------------------ attention
+// 8 int8 codes (lowest byte first) times 2^e as 8 bf16 (exact: a code needs 7 significant bits and
+// e is in [-126, 127], so each value is a normal bf16 number or zero)
+__device__ __forceinline__ uint4 deq8_bf16(uint2 q, int e) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = i < 2 ? q.x : q.y, sh = 16 * (i & 1);
+    const float lo = ldexpf((float)(int8_t)(w >> sh), e), hi = ldexpf((float)(int8_t)(w >> (sh + 8)), e);
+    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 struct PfAtt {
   const float *P;             // [T][NP]: q (nq hd) | k (nkv hd) | v (nkv hd)
   int NP, T;
   const float *rope;          // [max_ctx][hd/2][2]
   const int32_t *page_table;
   const int32_t *ctl;
-  uint16_t *kc, *vc;          // [pages][nkv][PAGE][hd]
+  void *kc, *vc;              // [pages][nkv][PAGE][hd] bf16, or int8 codes with kvq
+  int8_t *kve;                // kvq: [pages][nkv][PAGE][2] exponents of the K, V rows
+  int kvq;                    // 8-bit cache
   float *aq;                  // [PT][nq hd]
   int nq, nkv, hd;
   uint16_t *oh, *ol;          // output, operand block layout with Kc = nq hd
@@ -995,10 +1010,14 @@ __device__ __forceinline__ size_t kv_off(const PfAtt &a, int p, int kvh) {
   return (((size_t)a.page_table[p / MK_PAGE] * a.nkv + kvh) * MK_PAGE + (p % MK_PAGE)) * a.hd;
 }
 
-// RoPE on q and k at position p0 + t; K and V appended to the cache as bf16
+// RoPE on q and k at position p0 + t; K and V appended to the cache as bf16, or (8-bit cache) as
+// codes q and an exponent e per row, q = round-half-even(x 2^-e) with e the smallest integer
+// (>= -126) that keeps |q| <= 127
 __global__ void __launch_bounds__(PF_THREADS) pf_att_rope(PfAtt a) {
+  __shared__ float kv8[2 * MK_NX * 128];   // 8-bit cache: the rows to quantise [K|V][kv head][hd]
   const int t = blockIdx.x, p = a.ctl[MK_CTL_POS] + t, half = a.hd / 2;
   const float *row = a.P + (size_t)t * a.NP;
+  uint16_t *kc = static_cast<uint16_t *>(a.kc), *vc = static_cast<uint16_t *>(a.vc);
   for (int e = threadIdx.x; e < (a.nq + a.nkv) * half; e += PF_THREADS) {
     const int hh = e / half, d = e % half;
     const float cs = a.rope[((size_t)p * half + d) * 2 + 0], sn = a.rope[((size_t)p * half + d) * 2 + 1];
@@ -1010,14 +1029,40 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att_rope(PfAtt a) {
       const int kvh = hh - a.nq;
       const float *kr = row + a.nq * a.hd + kvh * a.hd;
       const float k1 = kr[d], k2 = kr[d + half];
-      const size_t o = kv_off(a, p, kvh);
-      a.kc[o + d] = (uint16_t)f2bf(k1 * cs - k2 * sn);
-      a.kc[o + d + half] = (uint16_t)f2bf(k2 * cs + k1 * sn);
+      if (a.kvq) {
+        kv8[kvh * a.hd + d] = k1 * cs - k2 * sn;
+        kv8[kvh * a.hd + d + half] = k2 * cs + k1 * sn;
+      } else {
+        const size_t o = kv_off(a, p, kvh);
+        kc[o + d] = (uint16_t)f2bf(k1 * cs - k2 * sn);
+        kc[o + d + half] = (uint16_t)f2bf(k2 * cs + k1 * sn);
+      }
     }
   }
-  for (int e = threadIdx.x; e < a.nkv * a.hd; e += PF_THREADS) {
-    const int kvh = e / a.hd, d = e % a.hd;
-    a.vc[kv_off(a, p, kvh) + d] = (uint16_t)f2bf(row[(a.nq + a.nkv) * a.hd + e]);
+  if (!a.kvq) {
+    for (int e = threadIdx.x; e < a.nkv * a.hd; e += PF_THREADS) {
+      const int kvh = e / a.hd, d = e % a.hd;
+      vc[kv_off(a, p, kvh) + d] = (uint16_t)f2bf(row[(a.nq + a.nkv) * a.hd + e]);
+    }
+    return;
+  }
+  for (int e = threadIdx.x; e < a.nkv * a.hd; e += PF_THREADS) kv8[MK_NX * 128 + e] = row[(a.nq + a.nkv) * a.hd + e];
+  __syncthreads();
+  // one wave per row: K rows of every kv head, then V rows
+  const int lane = threadIdx.x & 63;
+  for (int r = threadIdx.x >> 6; r < 2 * a.nkv; r += PF_THREADS / 64) {
+    const int isv = r / a.nkv, kvh = r % a.nkv;
+    const float *x = kv8 + isv * MK_NX * 128 + kvh * a.hd;
+    const float x0 = lane < a.hd ? x[lane] : 0.f, x1 = lane + 64 < a.hd ? x[lane + 64] : 0.f;
+    float am = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    const int ex = mk_q8_exp(am);
+    const size_t rix = kv_off(a, p, kvh) / a.hd;
+    int8_t *dst = static_cast<int8_t *>(isv ? a.vc : a.kc) + rix * a.hd;
+    if (lane < a.hd) dst[lane] = (int8_t)(int)rintf(ldexpf(x0, -ex));
+    if (lane + 64 < a.hd) dst[lane + 64] = (int8_t)(int)rintf(ldexpf(x1, -ex));
+    if (lane == 0) a.kve[rix * 2 + isv] = (int8_t)ex;
   }
 }
 
@@ -1067,7 +1112,7 @@ __device__ __forceinline__ void split8(const float (&f)[8], bf16x8 &h, bf16x8 &l
   }
 }
 
-template <int HD>
+template <int HD, bool KVQ>
 __global__ void __launch_bounds__(PF_THREADS) pf_att_mfma(PfAtt a) {
   constexpr int KS = HD / 32;            // 32-wide dim steps of K Q^T
   constexpr int NDB = HD / 16;           // 16-dim blocks of O^T
@@ -1124,9 +1169,17 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att_mfma(PfAtt a) {
       kr[c] = make_uint4(0u, 0u, 0u, 0u);
       vr[c] = make_uint4(0u, 0u, 0u, 0u);
       if (pp <= last) {
-        const size_t off = (((size_t)pages[pp / MK_PAGE] * a.nkv + kvh) * MK_PAGE + (pp % MK_PAGE)) * HD + cc * 8;
-        kr[c] = *reinterpret_cast<const uint4 *>(a.kc + off);
-        vr[c] = *reinterpret_cast<const uint4 *>(a.vc + off);
+        const size_t rix = ((size_t)pages[pp / MK_PAGE] * a.nkv + kvh) * MK_PAGE + (pp % MK_PAGE), off = rix * HD + cc * 8;
+        if constexpr (KVQ) {   // 8 codes and the row's exponent -> 8 bf16 (exactly: |code| <= 127)
+          const uint2 kq = *reinterpret_cast<const uint2 *>(static_cast<const int8_t *>(a.kc) + off);
+          const uint2 vq = *reinterpret_cast<const uint2 *>(static_cast<const int8_t *>(a.vc) + off);
+          const char2 ex = *reinterpret_cast<const char2 *>(a.kve + rix * 2);
+          kr[c] = deq8_bf16(kq, ex.x);
+          vr[c] = deq8_bf16(vq, ex.y);
+        } else {
+          kr[c] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.kc) + off);
+          vr[c] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.vc) + off);
+        }
       }
     }
   };
@@ -1459,11 +1512,15 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
         if (e != hipSuccess) return e;
         PfAtt at{};
         at.P = pf->P; at.NP = pf->NP; at.T = T; at.rope = d->rope; at.page_table = d->page_table; at.ctl = d->ctl;
-        at.kc = L.kc; at.vc = L.vc; at.aq = pf->aq; at.nq = nq; at.nkv = nkv; at.hd = hd;
+        at.kc = L.kc; at.vc = L.vc; at.kve = L.kve; at.kvq = d->kv_quant;
+        at.aq = pf->aq; at.nq = nq; at.nkv = nkv; at.hd = hd;
         at.oh = pf->a1h; at.ol = pf->a1l;
         hipLaunchKernelGGL(pf_att_rope, dim3(T), dim3(PF_THREADS), 0, st, at);
-        if (hd == 128) hipLaunchKernelGGL(pf_att_mfma<128>, dim3((T + 63) / 64, nq), dim3(PF_THREADS), 0, st, at);
-        else if (hd == 64) hipLaunchKernelGGL(pf_att_mfma<64>, dim3((T + 63) / 64, nq), dim3(PF_THREADS), 0, st, at);
+        const dim3 ga((T + 63) / 64, nq);
+        if (hd == 128 && !at.kvq) hipLaunchKernelGGL((pf_att_mfma<128, false>), ga, dim3(PF_THREADS), 0, st, at);
+        else if (hd == 128) hipLaunchKernelGGL((pf_att_mfma<128, true>), ga, dim3(PF_THREADS), 0, st, at);
+        else if (hd == 64 && !at.kvq) hipLaunchKernelGGL((pf_att_mfma<64, false>), ga, dim3(PF_THREADS), 0, st, at);
+        else if (hd == 64) hipLaunchKernelGGL((pf_att_mfma<64, true>), ga, dim3(PF_THREADS), 0, st, at);
         else return hipErrorInvalidValue;   // head_dim is 64 or 128 (checked at load)
         PfGemm go{};
         go.ah = pf->a1h; go.al = pf->a1l; go.M = T; go.N = H; go.K = nq * hd;

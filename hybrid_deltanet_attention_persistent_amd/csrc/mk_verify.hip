@@ -4,7 +4,11 @@
 #define MK_SEG_INLINE __forceinline__
 #include "mk_forward_kernel.h"
 
-const void *mk_verify_kernel(int shape) {
-  return (shape == MK_SHAPE_H1024) ? (const void *)mk_forward<MK_MAXCOL, MK_SHAPE_H1024>
-                                   : (const void *)mk_forward<MK_MAXCOL, MK_SHAPE_ANY>;
+const void *mk_verify_kernel(int variant) {
+  switch (variant) {
+    case MK_SHAPE_H1024: return (const void *)mk_forward<MK_MAXCOL, MK_SHAPE_H1024>;
+    case MK_SHAPE_ANY | MK_KV_Q8: return (const void *)mk_forward<MK_MAXCOL, MK_SHAPE_ANY | MK_KV_Q8>;
+    case MK_SHAPE_H1024 | MK_KV_Q8: return (const void *)mk_forward<MK_MAXCOL, MK_SHAPE_H1024 | MK_KV_Q8>;
+    default: return (const void *)mk_forward<MK_MAXCOL, MK_SHAPE_ANY>;
+  }
 }

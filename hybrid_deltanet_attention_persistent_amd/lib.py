@@ -43,7 +43,7 @@ class MkConfig(ctypes.Structure):
         ("at_q_heads", ctypes.c_int32), ("at_kv_heads", ctypes.c_int32), ("at_head_dim", ctypes.c_int32),
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("l2_eps", ctypes.c_float),
         ("tied_embedding", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("prefill_chunk", ctypes.c_int32),
-        ("max_verify", ctypes.c_int32),
+        ("max_verify", ctypes.c_int32), ("kv_quant", ctypes.c_int32),
     ]
 
 
@@ -104,7 +104,7 @@ def make_config(cfg) -> tuple:
     c = MkConfig(cfg.n_layers, ctypes.cast(kinds, ctypes.POINTER(ctypes.c_uint8)), cfg.hidden, cfg.vocab, cfg.ffn,
                  cfg.dn_heads, cfg.dn_dk, cfg.dn_dv, cfg.conv_k, cfg.at_q_heads, cfg.at_kv_heads, cfg.at_head_dim,
                  cfg.rope_theta, cfg.rms_eps, cfg.l2_eps, 1 if cfg.tied_embedding else 0, cfg.max_ctx,
-                 cfg.prefill_chunk, cfg.max_verify)
+                 cfg.prefill_chunk, cfg.max_verify, int(getattr(cfg, "kv_quant", 0)))
     return c, kinds
 
 

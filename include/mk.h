@@ -71,7 +71,14 @@ enum { MK_DTYPE_BF16 = 1, MK_DTYPE_F16 = 2, MK_DTYPE_F32 = 3 };
  * a config): hidden % 256 == 0; dn_dk == dn_dv in {64, 128}; dn_heads <= 8;
  * conv_k == 4; at_head_dim in {64, 128}; at_q_heads <= 8 and a multiple of
  * at_kv_heads; ffn % 64 == 0; max_ctx a multiple of 64; prefill_chunk == 64;
- * 1 <= max_verify <= 5; tied_embedding == 1.                                      */
+ * 1 <= max_verify <= 5; tied_embedding == 1; kv_quant in {0, 1}.
+ *
+ * kv_quant selects the KV-cache format (the launch page of the 8-bit cache: "8-bit KV cache"
+ * limits of the Korean write-up, and the RTX 3090 tag page).  0: rows stored as bf16.  1: every
+ * cached row (one position, one KV head, K or V) stored as hd int8 codes q plus one int8 exponent
+ * e, standing for q * 2^e: e is the smallest integer with max|x| <= 127 * 2^e (at least -126),
+ * q = round-half-even(x * 2^-e).  Each q * 2^e is exactly a bf16 number, so the attention
+ * arithmetic after the cache is the same in both formats; the cache takes half the bytes.      */
 typedef struct mk_config {
   int32_t n_layers;
   const uint8_t *layer_kind; /* host array [n_layers] of MK_LAYER_*                  */
@@ -80,6 +87,7 @@ typedef struct mk_config {
   int32_t at_q_heads, at_kv_heads, at_head_dim;
   float rope_theta, rms_eps, l2_eps;
   int32_t tied_embedding, max_ctx, prefill_chunk, max_verify;
+  int32_t kv_quant;          /* 0: bf16 KV cache; 1: 8-bit codes with a power-of-two scale per row */
 } mk_config;
 
 /* One weight tensor in host memory.  Names and shapes ([out, in] for matrices):

@@ -61,7 +61,8 @@ def kv_q8_rows(x: np.ndarray):
     The pages name an 8-bit KV cache ("q8" on the Korean update page, limits section; block-quantised
     KV caches on the RTX 3090 tag page) without defining its format; the reading used here: per
     cached row (one position of one KV head), in float32, a = max |x_i|, e = the smallest integer
-    with a <= 127 * 2^e (e = -7 for an all-zero row), codes q_i = round-half-even(x_i * 2^-e) in
+    >= -126 with a <= 127 * 2^e (so e = -126 for an all-zero or tiny row, and every nonzero stored
+    value is a normal number; e fits one signed byte), codes q_i = round-half-even(x_i * 2^-e) in
     [-127, 127], stored value q_i * 2^e.  A power-of-two scale keeps every stored value exactly a
     bfloat16 number (|q| <= 127 needs 7 significant bits).
 
@@ -71,6 +72,7 @@ def kv_q8_rows(x: np.ndarray):
     _, E = np.frexp(a.astype(np.float64))                   # a in [2^(E-1), 2^E), E = 0 for a == 0
     E = E.astype(np.int64)
     e = np.where(a.astype(np.float64) <= np.ldexp(127.0, E - 7), E - 7, E - 6)
+    e = np.maximum(np.where(a == 0, -126, e), -126)
     scaled = np.ldexp(x32.astype(np.float64), -e[..., None])  # exact: a power-of-two rescaling
     q = np.clip(np.rint(scaled), -127, 127).astype(np.int64)  # rint: ties to even
     return q.astype(np.int8), e.astype(np.int32), np.ldexp(q.astype(np.float64), e[..., None])

@@ -65,7 +65,19 @@ def test_required_bytes_scales_with_context(so):
     assert kv + rope <= a - b <= kv + rope + 65536
 
 
+def test_required_bytes_with_8bit_cache(so):
+    """The 8-bit cache holds one byte per element plus two exponent bytes (K, V) per position and
+    kv head: half the bf16 cache's element bytes."""
+    a = L.mk_required_bytes(W.HYBRID_24L)
+    b = L.mk_required_bytes(W.HYBRID_24L_Q8)
+    pos = 8448 * 2                                # positions x kv heads
+    saved = 6 * 2 * pos * 128                     # 6 layers x K,V x one byte less per element
+    exps = 6 * pos * 2                            # 6 layers x (K, V) exponent bytes
+    assert saved - exps - 65536 <= a - b <= saved - exps + 65536
+
+
 @pytest.mark.parametrize("change", [
+    dict(kv_quant=2), dict(kv_quant=-1),
     dict(hidden=300), dict(dn_heads=9), dict(dn_dk=96, dn_dv=96), dict(at_head_dim=32),
     dict(at_q_heads=6, at_kv_heads=4), dict(max_verify=6), dict(max_verify=0), dict(max_ctx=100),
     dict(max_ctx=20480), dict(prefill_chunk=32), dict(conv_k=3), dict(tied_embedding=False), dict(ffn=100),

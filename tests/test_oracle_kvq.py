@@ -52,13 +52,25 @@ def test_exponent_boundary():
 
 def test_zero_row_and_sign_symmetry():
     codes, e, val = kv_q8_rows(np.zeros((2, 16)))
-    assert not np.any(codes) and not np.any(val)
+    assert not np.any(codes) and not np.any(val) and np.all(e == -126)
     rng = np.random.default_rng(3)
     x = rng.standard_normal((20, 64))
     c1, e1, v1 = kv_q8_rows(x)
     c2, e2, v2 = kv_q8_rows(-x)
     assert np.array_equal(e1, e2) and np.array_equal(c2.astype(np.int64), -c1.astype(np.int64))
     assert np.array_equal(v2, -v1)
+
+
+def test_lowest_exponent():
+    """Rows below 127 * 2^-126 keep e = -126: codes are x * 2^126 rounded (a normal-number floor)."""
+    x = np.array([[np.ldexp(3.0, -127), np.ldexp(-1.0, -130), np.ldexp(5.0, -126)]])
+    codes, e, val = kv_q8_rows(x)
+    assert e[0] == -126
+    assert codes[0].tolist() == [2, 0, 5]            # 1.5 rounds to even 2; 2^-4 rounds to 0
+    assert np.array_equal(val[0], np.ldexp(np.array([2.0, 0.0, 5.0]), -126))
+    big = np.array([[np.ldexp(127.0, -126), 0.0]])
+    assert kv_q8_rows(big)[1][0] == -126
+    assert kv_q8_rows(np.array([[np.ldexp(128.0, -126)]]))[1][0] == -125
 
 
 def test_stored_values_are_bfloat16_numbers():

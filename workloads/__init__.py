@@ -109,6 +109,8 @@ WORKLOADS = {
     "24L-pp520": Workload("24L-pp520", HYBRID_24L, 520, 0),
     "24L-pp8192-tg128": Workload("24L-pp8192-tg128", HYBRID_24L, 8192, 128),
     "24L-pp520-verify5": Workload("24L-pp520-verify5", HYBRID_24L, 520, 128, verify_width=5),
+    # 8-bit KV cache: a context long enough that decode reads cached rows past the prefetched ones
+    "24L-q8-pp8192-tg32": Workload("24L-q8-pp8192-tg32", HYBRID_24L_Q8, 8192, 32),
 }
 
 
@@ -194,7 +196,7 @@ def param_count(cfg: ModelConfig) -> int:
 
 
 __all__ = [
-    "ModelConfig", "Workload", "TINY", "HYBRID_24L", "MODELS", "WORKLOADS", "DELTANET", "ATTENTION",
+    "ModelConfig", "Workload", "TINY", "HYBRID_24L", "TINY_Q8", "HYBRID_24L_Q8", "MODELS", "WORKLOADS", "DELTANET", "ATTENTION",
     "tensor_specs", "make_weights", "make_prompt", "make_drafts", "f32_to_bf16_bits",
     "bf16_bits_to_f32", "param_count",
 ]
