@@ -107,6 +107,7 @@ __device__ __forceinline__ float decay_f(float a) { return __fdividef(1.f, 1.f +
 #define DPP_XOR2 0x4E       // quad_perm [2,3,0,1]
 #define DPP_HALF_MIRROR 0x141
 #define DPP_MIRROR 0x140
+#define DPP_ROR8 0x128      // row_ror:8
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float v) {
   return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -479,30 +480,26 @@ __device__ __forceinline__ uint32_t kv8_off(const int *ptl, int k, int kvh, int 
 __device__ __forceinline__ uint32_t kve_off(const int *ptl, int k, int kvh, int nkv) {
   return (uint32_t)(((ptl[k / MK_PAGE] * nkv + kvh) * MK_PAGE + (k % MK_PAGE)) * 2);
 }
-// 16 int8 codes (two's complement, lowest byte first) times 2^e, e in [-126, 127]: the biased code
-// c + 128 (a flipped sign bit) converts straight to FP32, and (c + 128) 2^e - 128 2^e is exact in
-// one FMA, so each result is exactly c * 2^e.
-__device__ __forceinline__ void deq16(const u32x4 &w, int e, float f[16]) {
-  const float s = __uint_as_float((uint32_t)(e + 127) << 23), nb = -128.f * s;
-  const uint32_t u[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u, w.w ^ 0x80808080u};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f[4 * i + j] = fmaf((float)((u[i] >> (8 * j)) & 0xffu), s, nb);
-}
-// A cached row's dims [d0, d0 + DPL) as FP32: 8 bf16 (DPL 8) or 16 codes with exponent e (DPL 16).
-// (The 16 converted values are made where used: hoisted out of the column loop, every prefetched
-// row's would be live at once.)
+// A cached row's dims [d0, d0 + DPL) as FP32: 8 bf16 values (DPL 8), or 16 int8 codes (DPL 16,
+// two's complement, lowest byte first; one sign-extending convert each), whose row scale 2^e the
+// caller applies once per dot product / per probability.  (The codes are converted where used:
+// hoisted out of the column loop, every prefetched row's would be live at once.)
 template <int DPL>
-__device__ __forceinline__ void kv_unpack(const u32x4 &w, int e, float (&f)[DPL]) {
+__device__ __forceinline__ void kv_unpack(const u32x4 &w, float (&f)[DPL]) {
   if constexpr (DPL == 16) {
     u32x4 v = w;
-    asm volatile("" : "+v"(v), "+v"(e));
-    deq16(v, e, f);
+    asm volatile("" : "+v"(v));
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[4 * i + j] = (float)(int)(int8_t)(u[i] >> (8 * j));
   } else {
     unpack8(w, f);
   }
 }
+// 2^e as FP32 for an 8-bit cache exponent e in [-126, 127] (given as its byte)
+__device__ __forceinline__ float q8_scale(uint32_t eb) { return __uint_as_float((uint32_t)((int)(int8_t)eb + 127) << 23); }
 
 // ------------------------------------------------------------------------------ the kernel
 template <int NCOL, int SH>
@@ -529,6 +526,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // dimensions of a cached row per 16-byte load instead of 8
   constexpr bool KVQ = (SH & MK_KV_Q8) != 0;
   constexpr int DPL = KVQ ? 16 : 8;
+  constexpr int NPRE = KVQ ? 3 : NKV_PRE;   // attention key steps prefetched with the weights
   const int H = FX ? 1024 : m.H;
   // the layer table is read-only: reading it through the constant address space gives
   // scalar loads, so every pointer taken from it is known to be wave-uniform
@@ -647,7 +645,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
 #pragma unroll
       for (int st = 0; st < NKV_PRE; ++st) {
         const int ks = st * MK_WAVES * kpw + w8 * kpw + lane / lpk, k = lg + MK_NG * ks;
-        const uint32_t off = (k >= pos0) ? OOB_OFF
+        const uint32_t off = (k >= pos0 || st >= NPRE) ? OOB_OFF
                              : KVQ ? kv8_off(ptl, k, kvh, nkv, hd, (lane % lpk) * DPL) : kv_off(ptl, k, kvh, nkv, hd, (lane % lpk) * 8);
         const bool pj = st < pend_n;
         const uint32_t pv = (pj && prow >= 0) ? (uint32_t)((st * pks + MK_PEND_K + 4 * prow) * 4) : OOB_OFF;
@@ -975,17 +973,19 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           // ---- A2: RoPE, KV append, split-KV partials
           // 8-bit cache: the exponent pairs of the prefetched rows, loaded here (not with the rows:
           // held across the layer they would not fit in registers) and in flight during the gather
-          uint32_t kvx[NKV_PRE];
+          uint32_t kvx[NPRE];
           if constexpr (KVQ) {
             const int lpk = hd / DPL, kpw = 64 / lpk;
             const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(ly.kve, 0, 0x7fffffff, RSRC_W3);
 #pragma unroll
-            for (int st = 0; st < NKV_PRE; ++st) {
+            for (int st = 0; st < NPRE; ++st) {
               const int k = lg + MK_NG * (st * MK_WAVES * kpw + w8 * kpw + lane / lpk);
               kvx[st] = __builtin_amdgcn_raw_buffer_load_b16(ers, (k < pos0) ? kve_off(ptl, k, kvh, nkv) : OOB_OFF, 0, 0);
             }
           }
           float *qkv = work;                    // [NCOL][3hd]
+          // 8-bit cache: scales 2^e of this forward's K, V rows [NCOL][2] (past the split-KV buffers below)
+          float *kvs = work + NCOL * 3 * hd + 640 + MK_WAVES * hd + 2;
           if (!gather2d<MCS, MK_WAVES>(xin, ncol, 3 * hd, r_in_max, tg, qkv, flag, m.ctl, SITE(6), tid)) MK_BAIL();
           MK_TRACE_POINT(li, 3);
           {
@@ -1008,8 +1008,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           lbar();
           if constexpr (KVQ) {
             // 8-bit cache: each K and V row of this forward (one wave per row) becomes codes and an
-            // exponent; LDS keeps the values they stand for, which is what later forwards read back
-            // from the cache.  The first query head of the kv group appends the rows.
+            // exponent; LDS keeps the codes (as FP32) and the row scales 2^e, in the form later
+            // forwards read them from the cache.  The first query head of the kv group appends the rows.
             const bool app = lg == 0 && (x * nkv) % nq == 0;
             const __amdgpu_buffer_rsrc_t cst = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
             const __amdgpu_buffer_rsrc_t vst = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
@@ -1022,15 +1022,17 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
 #pragma unroll
               for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
               const int e = mk_q8_exp(am);
-              const float q0 = rintf(ldexpf(x0, -e)), q1 = rintf(ldexpf(x1, -e));
+              // (through int: a code of zero is +0, as the cache's byte converts)
+              const float q0 = (float)(int)rintf(ldexpf(x0, -e)), q1 = (float)(int)rintf(ldexpf(x1, -e));
               const int p = pos0 + c;
               const uint32_t rix = ((uint32_t)ptl[p / MK_PAGE] * nkv + kvh) * MK_PAGE + (p % MK_PAGE);
+              if (lane == 0) kvs[r] = q8_scale((uint32_t)e);
               if (lane < hd) {
-                row[lane] = ldexpf(q0, e);
+                row[lane] = q0;
                 if (app) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int)q0, isv ? vst : cst, rix * hd + lane, 0, AUX_DEV);
               }
               if (lane + 64 < hd) {
-                row[lane + 64] = ldexpf(q1, e);
+                row[lane + 64] = q1;
                 if (app) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int)q1, isv ? vst : cst, rix * hd + lane + 64, 0, AUX_DEV);
               }
               if (app && lane == 0) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e, est, rix * 2 + isv, 0, AUX_DEV);
@@ -1084,24 +1086,25 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               float qv[DPL];
 #pragma unroll
               for (int i = 0; i < DPL; ++i) qv[i] = qkv[c * 3 * hd + d0 + i];
-              auto score = [&](int ks, const float (&kf)[DPL]) {
+              auto score = [&](int ks, const float (&kf)[DPL], float ksc) {
                 float sdot = 0.f;
 #pragma unroll
                 for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kf[i], sdot);
+                if constexpr (KVQ) sdot *= ksc;
                 sdot = group_sum(sdot, lpk);
                 if (ks < ncache && (lane % lpk) == 0) sc[ks] = sdot * scale;
               };
 #pragma unroll
-              for (int st = 0; st < NKV_PRE; ++st) {
+              for (int st = 0; st < NPRE; ++st) {
                 if (st < nstc) {
                   float kf[DPL];
-                  kv_unpack<DPL>(wr[2 * NRG_IN + NRG_O + 2 * st], (int)(int8_t)(kvx[st] & 0xffu), kf);
-                  score(st * spw + kslot, kf);
+                  kv_unpack<DPL>(wr[2 * NRG_IN + NRG_O + 2 * st], kf);
+                  score(st * spw + kslot, kf, KVQ ? q8_scale(kvx[st] & 0xffu) : 1.f);
                 }
               }
               // later steps: KV_GRP steps' loads issued together, then used in step order
 #pragma unroll 1
-              for (int st = NKV_PRE; st < nstc; st += KV_GRP) {
+              for (int st = NPRE; st < nstc; st += KV_GRP) {
                 u32x4 kr[KV_GRP];
                 uint32_t ke[KV_GRP];
 #pragma unroll
@@ -1115,8 +1118,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 for (int u = 0; u < KV_GRP; ++u) {
                   if (st + u < nstc) {
                     float kf[DPL];
-                    kv_unpack<DPL>(kr[u], (int)(int8_t)ke[u], kf);
-                    score((st + u) * spw + kslot, kf);
+                    kv_unpack<DPL>(kr[u], kf);
+                    score((st + u) * spw + kslot, kf, KVQ ? q8_scale(ke[u]) : 1.f);
                   }
                 }
               }
@@ -1125,6 +1128,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 float sdot = 0.f;
 #pragma unroll
                 for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kk[i], sdot);
+                if constexpr (KVQ) sdot *= kvs[(kc_ - pos0) * 2];
                 sdot = group_sum(sdot, lpk);
                 if (lane == 0) sc[nk - 1] = sdot * scale;
               }
@@ -1148,21 +1152,22 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               float acc[DPL];
 #pragma unroll
               for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-              auto pvacc = [&](int ks, const float (&vf)[DPL]) {
-                const float pe = (ks < ncache) ? sc[ks < ncache ? ks : 0] : 0.f;
+              auto pvacc = [&](int ks, const float (&vf)[DPL], float vsc) {
+                float pe = (ks < ncache) ? sc[ks < ncache ? ks : 0] : 0.f;
+                if constexpr (KVQ) pe *= vsc;
 #pragma unroll
                 for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vf[i], acc[i]);
               };
 #pragma unroll
-              for (int st = 0; st < NKV_PRE; ++st) {
+              for (int st = 0; st < NPRE; ++st) {
                 if (st < nstc) {
                   float vf[DPL];
-                  kv_unpack<DPL>(wr[2 * NRG_IN + NRG_O + 2 * st + 1], (int)(int8_t)(kvx[st] >> 8), vf);
-                  pvacc(st * spw + kslot, vf);
+                  kv_unpack<DPL>(wr[2 * NRG_IN + NRG_O + 2 * st + 1], vf);
+                  pvacc(st * spw + kslot, vf, KVQ ? q8_scale(kvx[st] >> 8) : 1.f);
                 }
               }
 #pragma unroll 1
-              for (int st = NKV_PRE; st < nstc; st += KV_GRP) {
+              for (int st = NPRE; st < nstc; st += KV_GRP) {
                 u32x4 vr[KV_GRP];
                 uint32_t ve[KV_GRP];
 #pragma unroll
@@ -1176,8 +1181,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 for (int u = 0; u < KV_GRP; ++u) {
                   if (st + u < nstc) {
                     float vf[DPL];
-                    kv_unpack<DPL>(vr[u], (int)(int8_t)ve[u], vf);
-                    pvacc((st + u) * spw + kslot, vf);
+                    kv_unpack<DPL>(vr[u], vf);
+                    pvacc((st + u) * spw + kslot, vf, KVQ ? q8_scale(ve[u]) : 1.f);
                   }
                 }
               }
@@ -1186,7 +1191,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               // order, so verify and sequential decode agree bit for bit)
               const int kcs = (nk - 1) % spw;
               if (hascur && w8 == kcs / kpw && lane / lpk == kcs % kpw) {
-                const float pe = sc[nk - 1];
+                float pe = sc[nk - 1];
+                if constexpr (KVQ) pe *= kvs[(kc_ - pos0) * 2 + 1];
                 const float *vv = qkv + (kc_ - pos0) * 3 * hd + 2 * hd + d0;
 #pragma unroll
                 for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vv[i], acc[i]);
@@ -1196,6 +1202,10 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               for (int i = 0; i < DPL; ++i) {
                 float v = acc[i];
                 if (lpk == 16) {
+                  v = swap_add32(v, v);
+                  v = swap_add16(v, v);
+                } else if (lpk == 8) {
+                  v = dpp_add<DPP_ROR8>(v);   // (l, l ^ 8) within each row of 16 lanes
                   v = swap_add32(v, v);
                   v = swap_add16(v, v);
                 } else {
