@@ -44,8 +44,15 @@ struct mk_model {
   int device;
   mk_config cfg;
   std::vector<uint8_t> kinds;
-  MkDev dev;
-  std::vector<MkLayerDev> layers_host;  // the layer table (host copy) for the prefill driver
+  MkDev dev;                            // the selected sequence's view (state, KV cache, control words)
+  std::vector<MkLayerDev> layers_host;  // its layer table (host copy) for the prefill driver
+  // sequences (mk_config.n_seq): each has its own layer table (shared weights, own state and
+  // KV cache) and control block; calls other than mk_decode_batch act on the selected one
+  int cur = 0;
+  std::vector<MkDev> seq_dev;
+  std::vector<std::vector<MkLayerDev>> seq_layers_host;
+  std::vector<int32_t> seq_pos_hi;      // per sequence: upper bound of its device position
+  std::vector<uint8_t> seq_verified;    // per sequence: its last forward was a verify (updates may be pending)
   MkPf pf;                              // prefill scratch
   char *arena;
   size_t arena_bytes;
@@ -54,7 +61,7 @@ struct mk_model {
   int32_t *gen;                         // [64] device buffers of mk_generate_lookup (in the arena)
   // regions cleared by mk_reset_state
   std::vector<std::pair<size_t, size_t>> state_regions;
-  int32_t pos_hi;  // upper bound of the device position (exact unless a verify ran)
+  int32_t pos_hi;  // the selected sequence's upper bound of the device position (exact unless a verify ran)
   uint32_t tag;    // next exchange tag
 };
 
@@ -83,10 +90,20 @@ struct LayerRegions {
   Region ffn_gu, ffn_dn;
 };
 
+// The state of sequences 1 .. n_seq - 1 (sequence 0's lives in LayerRegions)
+struct SeqLayer {
+  Region S, ring, pend, kc, vc, kve;
+};
+struct SeqRegions {
+  Region ctl, layer_table;
+  std::vector<SeqLayer> layers;
+};
+
 struct Plan {
-  int H, V, I, J, nh, dk, dv, C, r_in, nq, nkv, hd, r_in_max, x_o_len, xm_len, max_pages;
+  int H, V, I, J, nh, dk, dv, C, r_in, nq, nkv, hd, r_in_max, x_o_len, xm_len, max_pages, n_seq;
   Region embed, lnf, rope, page_table, layer_table, ctl, xch, gen;
   std::vector<LayerRegions> layers;
+  std::vector<SeqRegions> seq;        // [n_seq - 1]
   // prefill scratch (one pass of MK_PT tokens)
   int K1, NP;
   Region pf_X, pf_a1h, pf_a1l, pf_a2h, pf_a2l, pf_P, pf_cW, pf_cQ, pf_cU, pf_cO, pf_cKt, pf_cg, pf_cd,
@@ -129,6 +146,7 @@ int check_config(const mk_config *c, std::string &why) {
   if (c->prefill_chunk != 64) { why = "prefill_chunk must be 64"; return MK_EINVAL; }
   if (c->max_verify < 1 || c->max_verify > MK_MAXCOL) { why = "max_verify must be in [1, 5]"; return MK_EINVAL; }
   if (c->kv_quant != 0 && c->kv_quant != 1) { why = "kv_quant must be 0 (bf16 cache) or 1 (8-bit codes)"; return MK_EINVAL; }
+  if (c->n_seq < 0 || c->n_seq > MK_MAXCOL) { why = "n_seq must be in [1, 5] (0 means 1)"; return MK_EINVAL; }
   {  // per-wave register budgets of the persistent kernel (weight rows held per phase): each role
      // (token mixer, FFN) has MK_NG workgroups of 8 weight-streaming waves per XCD
     const int Gh = mk_tile_G(c->hidden), RGh = 64 / Gh, XW = MK_NG * MK_WAVES;
@@ -193,6 +211,27 @@ Plan make_plan(const mk_config *c) {
     }
     r.ffn_gu = L.add((size_t)2 * p.I * H * 2);
     r.ffn_dn = L.add((size_t)H * p.I * 2);
+  }
+  // sequences 1 .. n_seq - 1: control block, layer table, and per layer the state / KV regions
+  p.n_seq = c->n_seq > 0 ? c->n_seq : 1;
+  p.seq.resize(p.n_seq - 1);
+  for (auto &sq : p.seq) {
+    sq.ctl = L.add(MK_CTL_WORDS * 4);
+    sq.layer_table = L.add(sizeof(MkLayerDev) * c->n_layers);
+    sq.layers.resize(c->n_layers);
+    for (int i = 0; i < c->n_layers; ++i) {
+      SeqLayer &r = sq.layers[i];
+      if (c->layer_kind[i] == MK_LAYER_DELTANET) {
+        r.S = L.add((size_t)p.nh * p.dv * p.dk * 4);
+        r.ring = L.add((size_t)MK_RING * p.C * 4);
+        r.pend = L.add((size_t)2 * p.nh * MK_MAXCOL * mk_pend_stride(p.dv) * 4);
+      } else {
+        const size_t cb = c->kv_quant ? 1 : 2;
+        r.kc = L.add((size_t)p.max_pages * p.nkv * MK_PAGE * p.hd * cb);
+        r.vc = L.add((size_t)p.max_pages * p.nkv * MK_PAGE * p.hd * cb);
+        r.kve = L.add(c->kv_quant ? (size_t)p.max_pages * p.nkv * MK_PAGE * 2 : 0);
+      }
+    }
   }
   // exchange slots, sized for the widest launch (verify, MK_MAXCOL columns)
   p.xch = L.add(mk_xch_bytes(MK_MAXCOL, c->n_layers, p.H, p.r_in_max, p.x_o_len, p.xm_len));
@@ -345,10 +384,13 @@ static int check_device(int *dev) {
     return fail(MK_ELAUNCH, std::string("device is ") + prop.gcnArchName + ", need gfx950 (MI355X)");
   if (prop.multiProcessorCount != MK_NWG)
     return fail(MK_ELAUNCH, "device has " + std::to_string(prop.multiProcessorCount) + " CUs, need 256 (8 XCDs x 32)");
-  for (int variant = 0; variant < MK_N_VARIANTS; ++variant)
+  for (int variant = 0; variant < MK_N_VARIANTS + 2; ++variant)
     for (int tmpl : {1, MK_MAXCOL}) {
+      // (variants past MK_N_VARIANTS: the batch instantiations, MK_MAXCOL columns only)
+      const int v = variant < MK_N_VARIANTS ? variant : MK_BATCH | (variant - MK_N_VARIANTS);
+      if (v >= MK_N_VARIANTS && tmpl == 1) continue;
       int per_cu = 0;
-      HIPCHECK(mk_forward_occupancy(tmpl, variant, &per_cu));
+      HIPCHECK(mk_forward_occupancy(tmpl, v, &per_cu));
       if (per_cu < 1) return fail(MK_ELAUNCH, "persistent kernel does not fit on a CU");
     }
   return MK_OK;
@@ -516,6 +558,32 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
     }
   }
   HIPCHECK(put(p.layer_table, lt.data()));
+  // the other sequences: the same weights, their own state and KV cache
+  std::vector<MkDev> seq_dev(p.n_seq, d);
+  std::vector<std::vector<MkLayerDev>> seq_lt(p.n_seq, lt);
+  for (int sq = 1; sq < p.n_seq; ++sq) {
+    const SeqRegions &R = p.seq[sq - 1];
+    for (int li = 0; li < cfg->n_layers; ++li) {
+      MkLayerDev &L = seq_lt[sq][li];
+      const SeqLayer &r = R.layers[li];
+      if (L.kind == 0) {
+        L.S = (float *)(A + r.S.off);
+        L.ring = (float *)(A + r.ring.off);
+        L.pend = (float *)(A + r.pend.off);
+        state.push_back({r.S.off, r.S.bytes});
+        state.push_back({r.ring.off, r.ring.bytes});
+        state.push_back({r.pend.off, r.pend.bytes});
+      } else {
+        L.kc = A + r.kc.off;
+        L.vc = A + r.vc.off;
+        L.kve = cfg->kv_quant ? (int8_t *)(A + r.kve.off) : nullptr;
+      }
+    }
+    HIPCHECK(put(R.layer_table, seq_lt[sq].data()));
+    seq_dev[sq].layers = (const MkLayerDev *)(A + R.layer_table.off);
+    seq_dev[sq].ctl = (int32_t *)(A + R.ctl.off);
+    state.push_back({R.ctl.off, R.ctl.bytes});
+  }
   // exchange slots start with tag 0 (never used); control words and state start at zero
   {
     const size_t x0 = p.xch.off;
@@ -533,6 +601,11 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   mm->cfg.layer_kind = mm->kinds.data();
   mm->dev = d;
   mm->layers_host = lt;
+  mm->cur = 0;
+  mm->seq_dev = seq_dev;
+  mm->seq_layers_host = seq_lt;
+  mm->seq_pos_hi.assign(p.n_seq, 0);
+  mm->seq_verified.assign(p.n_seq, 0);
   {
     MkPf &f = mm->pf;
     auto P = [&](const Region &r) { return (void *)(A + r.off); };
@@ -567,6 +640,8 @@ extern "C" int mk_reset_state(mk_model *m, void *stream) {
   hipStream_t st = (hipStream_t)stream;
   for (auto &r : m->state_regions) HIPCHECK(hipMemsetAsync(m->arena + r.first, 0, r.second, st));
   m->pos_hi = 0;
+  m->seq_pos_hi.assign(m->seq_pos_hi.size(), 0);
+  m->seq_verified.assign(m->seq_verified.size(), 0);
   return MK_OK;
 }
 
@@ -598,6 +673,7 @@ extern "C" int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens
   if (s != MK_OK) return s;
   HIPCHECK(mk_prefill_enqueue(&m->dev, m->layers_host.data(), &m->pf, d_tokens, n_tokens, d_next_token, d_last_logits, st));
   m->pos_hi += n_tokens;
+  m->seq_verified[m->cur] = 0;   // the prefill applies any pending updates first
   return MK_OK;
 }
 
@@ -622,7 +698,7 @@ static int decode_launch(mk_model *m, const int32_t *d_tokens, int32_t n_tokens,
   hipStream_t st = (hipStream_t)stream;
   int s = ensure_ctx(m, n_tokens, st);
   if (s != MK_OK) return s;
-  MkLaunch a;
+  MkLaunch a{};
   a.m = m->dev;
   a.tokens = d_tokens;
   a.n = n_tokens;
@@ -642,6 +718,7 @@ static int decode_launch(mk_model *m, const int32_t *d_tokens, int32_t n_tokens,
   HIPCHECK(mk_launch_forward(&a, tmpl, mk_variant_of(m->dev), st));
   if (!use_static) m->tag += 1;
   m->pos_hi += n_tokens;
+  m->seq_verified[m->cur] = n_tokens > 1;
   return MK_OK;
 }
 
@@ -661,6 +738,16 @@ extern "C" int mk_sync_status(mk_model *m, void *stream, int32_t *pos) {
   int s = sync_pos(m, (hipStream_t)stream, ctl);
   if (s != MK_OK) return s;
   if (pos) *pos = ctl[MK_CTL_POS];
+  // device errors of a batch launch land in the control block of its first column's sequence:
+  // report the first sequence with one (the selected sequence first)
+  for (size_t q = 0; q < m->seq_dev.size() && ctl[MK_CTL_ERR] == 0; ++q) {
+    if ((int)q == m->cur) continue;
+    int32_t other[MK_CTL_WORDS];
+    HIPCHECK(hipMemcpy(other, m->seq_dev[q].ctl, sizeof(other), hipMemcpyDeviceToHost));
+    if (other[MK_CTL_ERR] != 0) {
+      for (int w = MK_CTL_ERR; w < MK_CTL_WHERE + 4; ++w) ctl[w] = other[w];
+    }
+  }
   const int e = ctl[MK_CTL_ERR];
   if (e & MK_DERR_XCD) return fail(MK_ELAUNCH, "workgroups were not placed round-robin over the XCDs");
   if (e & MK_DERR_HANG) {
@@ -673,6 +760,65 @@ extern "C" int mk_sync_status(mk_model *m, void *stream, int32_t *pos) {
   }
   if (e & MK_DERR_TOKEN) return fail(MK_ETOKEN, "a token id was out of range");
   if (e & MK_DERR_NAN) return fail(MK_ENAN, "non-finite logits");
+  return MK_OK;
+}
+
+// ------------------------------------------------------------------------------ sequences
+extern "C" int mk_select_seq(mk_model *m, int32_t seq) {
+  if (!live(m)) return fail(MK_ESTATE, "model not loaded");
+  if (seq < 0 || seq >= (int32_t)m->seq_dev.size())
+    return fail(MK_EINVAL, "seq " + std::to_string(seq) + " out of range [0, " + std::to_string(m->seq_dev.size()) + ")");
+  m->seq_pos_hi[m->cur] = m->pos_hi;
+  m->cur = seq;
+  m->dev = m->seq_dev[seq];
+  m->layers_host = m->seq_layers_host[seq];
+  m->pos_hi = m->seq_pos_hi[seq];
+  return MK_OK;
+}
+
+extern "C" int mk_decode_batch(mk_model *m, const int32_t *seqs, int32_t n, const int32_t *d_tokens, int32_t *d_argmax,
+                               float *d_logits, void *stream) {
+  if (!live(m)) return fail(MK_ESTATE, "model not loaded");
+  if (!seqs || !d_tokens || !d_argmax) return fail(MK_EINVAL, "seqs and token buffers must not be NULL");
+  const int nseq = (int)m->seq_dev.size();
+  if (n < 1 || n > nseq) return fail(MK_EINVAL, "n must be in [1, n_seq]");
+  if (m->cfg.kv_quant) return fail(MK_EINVAL, "batch decode needs the bf16 KV cache (kv_quant = 0)");
+  m->seq_pos_hi[m->cur] = m->pos_hi;
+  hipStream_t st = (hipStream_t)stream;
+  for (int32_t c = 0; c < n; ++c) {
+    const int q = seqs[c];
+    if (q < 0 || q >= nseq) return fail(MK_EINVAL, "seqs[" + std::to_string(c) + "] out of range");
+    for (int32_t j = 0; j < c; ++j)
+      if (seqs[j] == q) return fail(MK_EINVAL, "seqs must be distinct");
+    if (m->seq_verified[q])
+      return fail(MK_EINVAL, "sequence " + std::to_string(q) +
+                                 " last ran a verify forward: a decode step or prefill on it must settle it first");
+    if ((int64_t)m->seq_pos_hi[q] + 1 > m->cfg.max_ctx) {
+      int32_t ctl[MK_CTL_WORDS];
+      HIPCHECK(hipStreamSynchronize(st));
+      HIPCHECK(hipMemcpy(ctl, m->seq_dev[q].ctl, sizeof(ctl), hipMemcpyDeviceToHost));
+      m->seq_pos_hi[q] = ctl[MK_CTL_POS];
+      if ((int64_t)m->seq_pos_hi[q] + 1 > m->cfg.max_ctx)
+        return fail(MK_ECTX, "sequence " + std::to_string(q) + " is at max_ctx");
+    }
+  }
+  MkLaunch a{};
+  a.m = m->seq_dev[seqs[0]];
+  a.tokens = d_tokens;
+  a.n = n;
+  a.argmax = d_argmax;
+  a.logits = d_logits;
+  a.n_acc = nullptr;
+  for (int32_t c = 0; c < n; ++c) {
+    a.seq_layers[c] = m->seq_dev[seqs[c]].layers;
+    a.seq_ctl[c] = m->seq_dev[seqs[c]].ctl;
+  }
+  a.tag0 = m->tag;
+  a.xch = m->xch;
+  HIPCHECK(mk_launch_forward(&a, MK_MAXCOL, mk_shape_of(m->dev) | MK_BATCH, st));
+  m->tag += 1;
+  for (int32_t c = 0; c < n; ++c) m->seq_pos_hi[seqs[c]] += 1;
+  m->pos_hi = m->seq_pos_hi[m->cur];
   return MK_OK;
 }
 

@@ -526,7 +526,12 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // dimensions of a cached row per 16-byte load instead of 8
   constexpr bool KVQ = (SH & MK_KV_Q8) != 0;
   constexpr int DPL = KVQ ? 16 : 8;
-  constexpr int NPRE = KVQ ? 3 : NKV_PRE;   // attention key steps prefetched with the weights
+  // MK_BATCH: column c is a decode step of its own sequence (state and KV cache through
+  // a.seq_layers[c], position a.seq_ctl[c][MK_CTL_POS]); no verify semantics, no pending updates
+  constexpr bool BAT = (SH & MK_BATCH) != 0;
+  static_assert(!BAT || (NCOL == MK_MAXCOL && !KVQ), "batch launches: MK_MAXCOL columns, bf16 cache");
+  // attention key steps prefetched with the weights (batch: none, every column reads its own cache)
+  constexpr int NPRE = BAT ? 0 : KVQ ? 3 : NKV_PRE;
   const int H = FX ? 1024 : m.H;
   // the layer table is read-only: reading it through the constant address space gives
   // scalar loads, so every pointer taken from it is known to be wave-uniform
@@ -550,10 +555,25 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     if ((int)(xcc & 7) != x) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_XCD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  const int ctl_pos = __hip_atomic_load(m.ctl + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int pend_n = __hip_atomic_load(m.ctl + MK_CTL_PEND, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int par = __hip_atomic_load(m.ctl + MK_CTL_PAR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool verify = a.n > 1;
+  const int ctl_pos = BAT ? 0 : __hip_atomic_load(m.ctl + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int pend_n = BAT ? 0 : __hip_atomic_load(m.ctl + MK_CTL_PEND, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int par = BAT ? 0 : __hip_atomic_load(m.ctl + MK_CTL_PAR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool verify = !BAT && a.n > 1;
+  // batch: every column's sequence position (wave-uniform); bsel picks column c's entry of a
+  // per-column array for a c that is not a compile-time constant, without indexing registers
+  int bpos[NCOL];
+#pragma unroll
+  for (int c = 0; c < NCOL; ++c)
+    bpos[c] = (BAT && c < a.n) ? __builtin_amdgcn_readfirstlane(
+                                     __hip_atomic_load(a.seq_ctl[c] + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                               : 0;
+  auto bsel = [&](const auto (&arr)[NCOL], int c) {
+    auto v = arr[0];
+#pragma unroll
+    for (int j = 1; j < NCOL; ++j)
+      if (c == j) v = arr[j];
+    return v;
+  };
   const int ncol = a.n;
   const int G_h = mk_tile_G(H), L_h = H / 8 / G_h, RG_h = 64 / G_h;
   const int SL = H / MK_NG;  // residual slice per workgroup in the reductions
@@ -633,7 +653,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     // DeltaNet: the same registers take the pending updates left by a verify forward, update j in
     // slots 2 j (v, alpha, beta of this wave's row) and 2 j + 1 (this lane's key quad), so that
     // D2 replays them without a memory round trip per update.
-    {
+    if constexpr (!BAT) {
       const bool at = live && !dn && x < nq;
       const bool pdn = live && dn && x < nh && pend_n > 0;
       const int lpk = hd / DPL, kpw = 64 / lpk, pks = mk_pend_stride(dv);
@@ -655,9 +675,10 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       }
     }
     // this wave's DeltaNet state: its row of S, the conv taps and history of its lane's channel,
-    // the gated-norm gain of its row
+    // the gated-norm gain of its row (batch: the conv taps and the gain; each column's S row and
+    // history are its own sequence's, loaded in D2)
     const bool sdn = live && dn && x < nh;
-    const bool own = sdn && w8 < RW;
+    const bool own = sdn && w8 < RW && !BAT;
     const __amdgpu_buffer_rsrc_t rsS = tile_rsrc(ly.S + ((size_t)x * dv + r0 + (own ? w8 : 0)) * dk, own ? (uint32_t)(dk * 4) : 0u);
     srow[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsS, lane * 4, 0, AUX_DEV));
     srow[1] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsS, (64 + lane) * 4, 0, AUX_DEV));
@@ -668,14 +689,14 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     const __amdgpu_buffer_rsrc_t rc = tile_rsrc(ly.dn_conv, sdn ? (uint32_t)(nconv * 16) : 0u);
     const u32x4 wt = __builtin_amdgcn_raw_buffer_load_b128(rc, chl ? (uint32_t)(conv_ch * 16) : OOB_OFF, 0, 0);
     cwt = make_float4(__uint_as_float(wt.x), __uint_as_float(wt.y), __uint_as_float(wt.z), __uint_as_float(wt.w));
-    const __amdgpu_buffer_rsrc_t rr = tile_rsrc(ly.ring, sdn ? (uint32_t)(MK_RING * nconv * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t rr = tile_rsrc(ly.ring, (sdn && !BAT) ? (uint32_t)(MK_RING * nconv * 4) : 0u);
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int pp = pos0 - 3 + i;
       hist[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           rr, (chl && pp >= 0) ? (uint32_t)(((pp & (MK_RING - 1)) * nconv + conv_ch) * 4) : OOB_OFF, 0, AUX_DEV));
     }
-    grow = ld_gain(ly.dn_gnorm, own ? dv : 0, r0 + w8);
+    grow = ld_gain(ly.dn_gnorm, (sdn && w8 < RW) ? dv : 0, r0 + w8);
     ld_gain16(ly.ln1, H, G_h, live, gv);
     keep_issued();
   };
@@ -742,7 +763,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     const int half = hd / 2;
     for (int i = tid0; i < ncol * half; i += MK_THREADS) {
       const int c = i / half, d = i - c * half;
-      const float2 r = *reinterpret_cast<const float2 *>(m.rope + ((size_t)(pos0 + c) * half + d) * 2);
+      const int pc = BAT ? bsel(bpos, c) : pos0 + c;
+      const float2 r = *reinterpret_cast<const float2 *>(m.rope + ((size_t)pc * half + d) * 2);
       rl[i * 2 + 0] = r.x;
       rl[i * 2 + 1] = r.y;
     }
@@ -814,6 +836,29 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           float *gab = gz + NCOL * RW;            // [NCOL][2]    a, b
           float *qkc = gab + NCOL * 2;            // [NCOL][2dk]  q, k after conv + SiLU
           float *rsq = qkc + NCOL * 2 * dk;       // [NCOL][8]    per-wave sums of squares
+          // batch: each column's conv history (this lane's channel) and S row (this wave's row)
+          // come from its own sequence's state; loaded here, in flight during the gather
+          float hb[NCOL][3], sb[NCOL][2];
+          if constexpr (BAT) {
+            const bool chl = lane < CPW || (lane == 63 && w8 < RW);
+            const int conv_ch = conv_channel(lane);
+#pragma unroll
+            for (int c = 0; c < NCOL; ++c) {
+              const bool lc = c < ncol;
+              ConstLayer &lc_ly = ((ConstLayer *)(uintptr_t)a.seq_layers[lc ? c : 0])[li];
+              const __amdgpu_buffer_rsrc_t rr = tile_rsrc(lc_ly.ring, lc ? (uint32_t)(MK_RING * nconv * 4) : 0u);
+#pragma unroll
+              for (int i = 0; i < 3; ++i) {
+                const int pp = bpos[c] - 3 + i;
+                hb[c][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    rr, (chl && pp >= 0) ? (uint32_t)(((pp & (MK_RING - 1)) * nconv + conv_ch) * 4) : OOB_OFF, 0, AUX_DEV));
+              }
+              const bool ow = lc && w8 < RW;
+              const __amdgpu_buffer_rsrc_t rs = tile_rsrc(lc_ly.S + ((size_t)x * dv + r0 + (ow ? w8 : 0)) * dk, ow ? (uint32_t)(dk * 4) : 0u);
+              sb[c][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, AUX_DEV));
+              sb[c][1] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (64 + lane) * 4, 0, AUX_DEV));
+            }
+          }
           {
             const GSeg sg[4] = {{0, ncol, 2 * dk, r_in_max, gqk},
                                 {2 * dk + r0, ncol, RW, r_in_max, gvv},
@@ -837,7 +882,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int cc = c - (3 - i);
-                const float v = (cc >= 0) ? raw[cc < 0 ? 0 : cc] : hist[cc + 3 < 0 ? 0 : cc + 3];
+                // (batch: every column is the newest token of its own sequence, as in decode)
+                const float v = BAT ? (i < 3 ? hb[c][i < 3 ? i : 0] : raw[c])
+                                    : (cc >= 0) ? raw[cc < 0 ? 0 : cc] : hist[cc + 3 < 0 ? 0 : cc + 3];
                 sacc = fmaf(wv[i], v, sacc);
               }
               cv[c] = silu_f(sacc);
@@ -850,8 +897,13 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             if (lane == 0) rsq[c * MK_WAVES + w8] = sq;
           }
           // this forward's pre-conv inputs into the ring (q/k by workgroup 0 of the role, v by the owner)
-          if ((qkl && lg == 0) || vl)
-            FOR_COL(c) ly.ring[((pos0 + c) & (MK_RING - 1)) * nconv + conv_ch] = raw[c];
+          if ((qkl && lg == 0) || vl) {
+            if constexpr (BAT) {
+              FOR_COL(c) ((ConstLayer *)(uintptr_t)a.seq_layers[c])[li].ring[(bpos[c] & (MK_RING - 1)) * nconv + conv_ch] = raw[c];
+            } else {
+              FOR_COL(c) ly.ring[((pos0 + c) & (MK_RING - 1)) * nconv + conv_ch] = raw[c];
+            }
+          }
           lbar();
           if (w8 < RW) {
             // delta rule on row r0 + w8: S_r <- alpha S_r + beta (v_r - alpha S_r.k) k ; o_r = S_r.q
@@ -878,6 +930,10 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             }
             float *pw = ly.pend + ((size_t)(par ^ 1) * nh + x) * MK_MAXCOL * mk_pend_stride(dv);
             FOR_COL(c) {
+              if constexpr (BAT) {   // this column's sequence's row of S
+                srow[0] = sb[c][0];
+                srow[1] = sb[c][1];
+              }
               const float qr = rsqrtf(((rsq[c * 8 + 0] + rsq[c * 8 + 1]) + rsq[c * 8 + 2]) + rsq[c * 8 + 3] + m.l2_eps);
               const float kr = rsqrtf(((rsq[c * 8 + 4] + rsq[c * 8 + 5]) + rsq[c * 8 + 6]) + rsq[c * 8 + 7] + m.l2_eps);
               const float *qc = qkc + c * 2 * dk;
@@ -900,8 +956,13 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 if (lg == 0 && w8 == 0) *reinterpret_cast<float4 *>(pc + 4 * lane) = make_float4(k0, k1, 0.f, 0.f);
                 if (lane == 0) *reinterpret_cast<float4 *>(pc + MK_PEND_K + 4 * (r0 + w8)) = make_float4(vr, al, be, 0.f);
               }
+              if constexpr (BAT) {
+                float *Sc = ((ConstLayer *)(uintptr_t)a.seq_layers[c])[li].S + ((size_t)x * dv + r0 + w8) * dk;
+                Sc[lane] = srow[0];
+                if (J2 > 1) Sc[64 + lane] = srow[1];
+              }
             }
-            if (!verify) {
+            if (!verify && !BAT) {
               Srow[lane] = srow[0];
               if (J2 > 1) Srow[64 + lane] = srow[1];
             }
@@ -973,7 +1034,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           // ---- A2: RoPE, KV append, split-KV partials
           // 8-bit cache: the exponent pairs of the prefetched rows, loaded here (not with the rows:
           // held across the layer they would not fit in registers) and in flight during the gather
-          uint32_t kvx[NPRE];
+          uint32_t kvx[NPRE > 0 ? NPRE : 1];
           if constexpr (KVQ) {
             const int lpk = hd / DPL, kpw = 64 / lpk;
             const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(ly.kve, 0, 0x7fffffff, RSRC_W3);
@@ -1041,16 +1102,32 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           } else if (lg == 0 && (x * nkv) % nq == 0) {
             // the first query head of the kv group appends K, V (read by later launches only: this
             // launch takes its own positions' keys and values from LDS)
-            const __amdgpu_buffer_rsrc_t kst = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
-            const __amdgpu_buffer_rsrc_t vst = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
-            for (int i = tid; i < ncol * hd; i += MK_THREADS) {
-              const int c = i / hd, d = i - c * hd;
-              const int p = pos0 + c;
-              const size_t off = (((size_t)m.page_table[p / MK_PAGE] * nkv + kvh) * MK_PAGE + (p % MK_PAGE)) * hd + d;
-              const uint16_t kb = (uint16_t)(__float_as_uint(qkv[c * 3 * hd + hd + d]) >> 16);
-              const uint16_t vb = (uint16_t)(__float_as_uint(qkv[c * 3 * hd + 2 * hd + d]) >> 16);
-              __builtin_amdgcn_raw_buffer_store_b16(kb, kst, (uint32_t)(off * 2), 0, AUX_DEV);
-              __builtin_amdgcn_raw_buffer_store_b16(vb, vst, (uint32_t)(off * 2), 0, AUX_DEV);
+            if constexpr (BAT) {   // column c into its own sequence's cache, at its position
+              FOR_COL(c) {
+                ConstLayer &cl = ((ConstLayer *)(uintptr_t)a.seq_layers[c])[li];
+                const __amdgpu_buffer_rsrc_t kst = __builtin_amdgcn_make_buffer_rsrc(cl.kc, 0, 0x7fffffff, RSRC_W3);
+                const __amdgpu_buffer_rsrc_t vst = __builtin_amdgcn_make_buffer_rsrc(cl.vc, 0, 0x7fffffff, RSRC_W3);
+                const int p = bpos[c];
+                for (int d = tid; d < hd; d += MK_THREADS) {
+                  const size_t off = (((size_t)ptl[p / MK_PAGE] * nkv + kvh) * MK_PAGE + (p % MK_PAGE)) * hd + d;
+                  const uint16_t kb = (uint16_t)(__float_as_uint(qkv[c * 3 * hd + hd + d]) >> 16);
+                  const uint16_t vb = (uint16_t)(__float_as_uint(qkv[c * 3 * hd + 2 * hd + d]) >> 16);
+                  __builtin_amdgcn_raw_buffer_store_b16(kb, kst, (uint32_t)(off * 2), 0, AUX_DEV);
+                  __builtin_amdgcn_raw_buffer_store_b16(vb, vst, (uint32_t)(off * 2), 0, AUX_DEV);
+                }
+              }
+            } else {
+              const __amdgpu_buffer_rsrc_t kst = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
+              const __amdgpu_buffer_rsrc_t vst = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
+              for (int i = tid; i < ncol * hd; i += MK_THREADS) {
+                const int c = i / hd, d = i - c * hd;
+                const int p = pos0 + c;
+                const size_t off = (((size_t)m.page_table[p / MK_PAGE] * nkv + kvh) * MK_PAGE + (p % MK_PAGE)) * hd + d;
+                const uint16_t kb = (uint16_t)(__float_as_uint(qkv[c * 3 * hd + hd + d]) >> 16);
+                const uint16_t vb = (uint16_t)(__float_as_uint(qkv[c * 3 * hd + 2 * hd + d]) >> 16);
+                __builtin_amdgcn_raw_buffer_store_b16(kb, kst, (uint32_t)(off * 2), 0, AUX_DEV);
+                __builtin_amdgcn_raw_buffer_store_b16(vb, vst, (uint32_t)(off * 2), 0, AUX_DEV);
+              }
             }
           }
           {
@@ -1066,23 +1143,36 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             const float scale = 1.f / sqrtf((float)hd);
             const int lpk = hd / DPL, kpw = 64 / lpk, spw = MK_WAVES * kpw;
             const int d0 = (lane % lpk) * DPL, kslot = w8 * kpw + lane / lpk;
-            const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
-            const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
+            const __amdgpu_buffer_rsrc_t krs0 = __builtin_amdgcn_make_buffer_rsrc(ly.kc, 0, 0x7fffffff, RSRC_W3);
+            const __amdgpu_buffer_rsrc_t vrs0 = __builtin_amdgcn_make_buffer_rsrc(ly.vc, 0, 0x7fffffff, RSRC_W3);
             const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(KVQ ? (void *)ly.kve : nullptr, 0, KVQ ? 0x7fffffff : 0, RSRC_W3);
             // byte offset of this lane's part of cached row ks (a slot below ncache), and of its exponents
             auto row_off = [&](int ks) {
               return KVQ ? kv8_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0);
             };
-            // cached keys of this workgroup: slots [0, ncache)
-            const int ncache = (pos0 > lg) ? (pos0 - 1 - lg) / MK_NG + 1 : 0;
-            const int nstc = (ncache + spw - 1) / spw;
+            // batch: each column's own cache (its sequence's K and V of this layer)
+            const void *bkc[NCOL], *bvc[NCOL];
+#pragma unroll
+            for (int c = 0; c < NCOL; ++c) {
+              ConstLayer &cl = ((ConstLayer *)(uintptr_t)a.seq_layers[(BAT && c < ncol) ? c : 0])[li];
+              bkc[c] = BAT ? cl.kc : nullptr;
+              bvc[c] = BAT ? cl.vc : nullptr;
+            }
 #pragma unroll 1
             for (int c = 0; c < ncol; ++c) {
-              const int P = pos0 + c;             // query position; keys 0..P
+              // first position of this forward in column c's sequence: cached keys are below it
+              const int base = BAT ? bsel(bpos, c) : pos0;
+              const int P = BAT ? base : pos0 + c;  // query position; keys 0..P
+              // cached keys of this workgroup: slots [0, ncache)
+              const int ncache = (base > lg) ? (base - 1 - lg) / MK_NG + 1 : 0;
+              const int nstc = (ncache + spw - 1) / spw;
+              const __amdgpu_buffer_rsrc_t krs = BAT ? __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(bsel(bkc, c)), 0, 0x7fffffff, RSRC_W3) : krs0;
+              const __amdgpu_buffer_rsrc_t vrs = BAT ? __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(bsel(bvc, c)), 0, 0x7fffffff, RSRC_W3) : vrs0;
               const int nk = (P >= lg) ? (P - lg) / MK_NG + 1 : 0;
-              // this forward's key of this workgroup, if any: position kc_ in [pos0, P], slot nk - 1
+              // this forward's key of this workgroup, if any: position kc_ in [base, P], slot nk - 1
               const int kc_ = lg + MK_NG * (nk - 1);
-              const bool hascur = nk > 0 && kc_ >= pos0;
+              const bool hascur = nk > 0 && kc_ >= base;
+              const int crow = BAT ? c : kc_ - pos0;   // its row of this forward's K, V in LDS
               float qv[DPL];
 #pragma unroll
               for (int i = 0; i < DPL; ++i) qv[i] = qkv[c * 3 * hd + d0 + i];
@@ -1124,11 +1214,11 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 }
               }
               if (hascur && w8 == 0 && lane < lpk) {   // this forward's key: from LDS
-                const float *kk = qkv + (kc_ - pos0) * 3 * hd + hd + d0;
+                const float *kk = qkv + crow * 3 * hd + hd + d0;
                 float sdot = 0.f;
 #pragma unroll
                 for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kk[i], sdot);
-                if constexpr (KVQ) sdot *= kvs[(kc_ - pos0) * 2];
+                if constexpr (KVQ) sdot *= kvs[crow * 2];
                 sdot = group_sum(sdot, lpk);
                 if (lane == 0) sc[nk - 1] = sdot * scale;
               }
@@ -1192,8 +1282,8 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               const int kcs = (nk - 1) % spw;
               if (hascur && w8 == kcs / kpw && lane / lpk == kcs % kpw) {
                 float pe = sc[nk - 1];
-                if constexpr (KVQ) pe *= kvs[(kc_ - pos0) * 2 + 1];
-                const float *vv = qkv + (kc_ - pos0) * 3 * hd + 2 * hd + d0;
+                if constexpr (KVQ) pe *= kvs[crow * 2 + 1];
+                const float *vv = qkv + crow * 3 * hd + 2 * hd + d0;
 #pragma unroll
                 for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vv[i], acc[i]);
               }
@@ -1568,10 +1658,16 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           if (c < ncol) a.argmax[c] = gsel[c];
         if (a.n_acc) a.n_acc[0] = nacc;
         if (anynan) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_NAN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int consumed = verify ? nacc : 1;
-        __hip_atomic_store(m.ctl + MK_CTL_POS, ctl_pos + consumed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(m.ctl + MK_CTL_PEND, verify ? nacc : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(m.ctl + MK_CTL_PAR, verify ? (par ^ 1) : par, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (BAT) {   // every sequence of the batch advances by its one token
+#pragma unroll
+          for (int c = 0; c < NCOL; ++c)
+            if (c < ncol) __hip_atomic_store(a.seq_ctl[c] + MK_CTL_POS, bpos[c] + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          const int consumed = verify ? nacc : 1;
+          __hip_atomic_store(m.ctl + MK_CTL_POS, ctl_pos + consumed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(m.ctl + MK_CTL_PEND, verify ? nacc : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(m.ctl + MK_CTL_PAR, verify ? (par ^ 1) : par, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   }

@@ -119,12 +119,18 @@ struct MkLaunch {
   float *logits;          // device, nullable: [n][V]
   int32_t *n_acc;         // device, nullable
   uint2 *xch;             // device: exchange slots of this launch (mk_xch_bytes(n_template, ...) bytes, 256-byte aligned)
+  // batch launches (MK_BATCH): column c is one decode step of its own sequence, whose state
+  // (DeltaNet S, conv ring, KV cache) the layer table seq_layers[c] points at and whose position
+  // is seq_ctl[c][MK_CTL_POS]; m.layers / m.ctl are those of column 0's sequence
+  const MkLayerDev *seq_layers[MK_MAXCOL];
+  int32_t *seq_ctl[MK_MAXCOL];
 };
 
 // Instantiations of the persistent kernel: MK_SHAPE_H1024 has every dimension of the hidden-1024
 // model as a compile-time constant; MK_SHAPE_ANY reads them from MkDev.  MK_KV_Q8 is or-ed in for
-// a model whose KV cache holds 8-bit codes.
-enum { MK_SHAPE_ANY = 0, MK_SHAPE_H1024 = 1, MK_KV_Q8 = 2, MK_N_VARIANTS = 4 };
+// a model whose KV cache holds 8-bit codes, MK_BATCH for a batch launch (MK_MAXCOL columns, one
+// sequence each; bf16 cache).
+enum { MK_SHAPE_ANY = 0, MK_SHAPE_H1024 = 1, MK_KV_Q8 = 2, MK_N_VARIANTS = 4, MK_BATCH = 4 };
 static inline int mk_shape_of(const MkDev &d) {
   const bool h1024 = d.H == 1024 && d.nh == 8 && d.dk == 128 && d.dv == 128 && d.nq == 8 && d.nkv == 2 &&
                      d.hd == 128 && d.J == 448 && d.r_in == 514 && d.C == 3072 && d.r_in_max == 544 &&

@@ -25,7 +25,7 @@ MK_DTYPE_BF16, MK_DTYPE_F16, MK_DTYPE_F32 = 1, 2, 3
 
 EXPORTED = ["mk_required_bytes", "mk_load_weights", "mk_reset_state", "mk_prefill", "mk_decode_step",
             "mk_decode_step_static", "mk_sync_status", "mk_free", "mk_status_string", "mk_last_error",
-            "mk_lookup_draft", "mk_generate_lookup"]
+            "mk_lookup_draft", "mk_generate_lookup", "mk_select_seq", "mk_decode_batch"]
 MK_STATIC_SCRATCH_BYTES = 16 << 20
 
 
@@ -43,7 +43,7 @@ class MkConfig(ctypes.Structure):
         ("at_q_heads", ctypes.c_int32), ("at_kv_heads", ctypes.c_int32), ("at_head_dim", ctypes.c_int32),
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("l2_eps", ctypes.c_float),
         ("tied_embedding", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("prefill_chunk", ctypes.c_int32),
-        ("max_verify", ctypes.c_int32), ("kv_quant", ctypes.c_int32),
+        ("max_verify", ctypes.c_int32), ("kv_quant", ctypes.c_int32), ("n_seq", ctypes.c_int32),
     ]
 
 
@@ -78,6 +78,8 @@ def load_library() -> ctypes.CDLL:
     lib.mk_sync_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.mk_lookup_draft.argtypes = [vp, i32, i32, i32, i32, vp]
     lib.mk_generate_lookup.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, ctypes.POINTER(MkLookupStats), vp]
+    lib.mk_select_seq.argtypes = [vp, i32]
+    lib.mk_decode_batch.argtypes = [vp, vp, i32, vp, vp, vp, vp]
     lib.mk_free.argtypes = [vp]
     lib.mk_free.restype = None
     lib.mk_status_string.argtypes = [ctypes.c_int]
@@ -85,7 +87,8 @@ def load_library() -> ctypes.CDLL:
     lib.mk_last_error.argtypes = []
     lib.mk_last_error.restype = ctypes.c_char_p
     for f in ("mk_required_bytes", "mk_load_weights", "mk_reset_state", "mk_prefill", "mk_decode_step",
-              "mk_decode_step_static", "mk_sync_status", "mk_lookup_draft", "mk_generate_lookup"):
+              "mk_decode_step_static", "mk_sync_status", "mk_lookup_draft", "mk_generate_lookup", "mk_select_seq",
+              "mk_decode_batch"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -104,7 +107,7 @@ def make_config(cfg) -> tuple:
     c = MkConfig(cfg.n_layers, ctypes.cast(kinds, ctypes.POINTER(ctypes.c_uint8)), cfg.hidden, cfg.vocab, cfg.ffn,
                  cfg.dn_heads, cfg.dn_dk, cfg.dn_dv, cfg.conv_k, cfg.at_q_heads, cfg.at_kv_heads, cfg.at_head_dim,
                  cfg.rope_theta, cfg.rms_eps, cfg.l2_eps, 1 if cfg.tied_embedding else 0, cfg.max_ctx,
-                 cfg.prefill_chunk, cfg.max_verify, int(getattr(cfg, "kv_quant", 0)))
+                 cfg.prefill_chunk, cfg.max_verify, int(getattr(cfg, "kv_quant", 0)), int(getattr(cfg, "n_seq", 1)))
     return c, kinds
 
 
@@ -205,6 +208,17 @@ def mk_generate_lookup(handle: int, history, last_token: int, n_generate: int, n
     return out[:n_generate].tolist(), {"forwards": st.forwards, "drafted": st.drafted, "accepted": st.accepted}
 
 
+def mk_select_seq(handle: int, seq: int) -> None:
+    _check(load_library().mk_select_seq(handle, int(seq)), "mk_select_seq")
+
+
+def mk_decode_batch(handle: int, seqs, tokens, argmax, logits=None, stream=None) -> None:
+    """One decode step for each sequence in `seqs` (host ints); tokens / argmax / logits are device buffers."""
+    sq = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+    _check(load_library().mk_decode_batch(handle, sq.ctypes.data if sq.size else None, int(sq.size), _ptr(tokens),
+                                          _ptr(argmax), _ptr(logits), _stream(stream)), "mk_decode_batch")
+
+
 def mk_free(handle: int) -> None:
     load_library().mk_free(handle)
 
@@ -235,6 +249,12 @@ class Model:
 
     def sync(self) -> int:
         return mk_sync_status(self.handle)
+
+    def select(self, seq: int):
+        mk_select_seq(self.handle, seq)
+
+    def decode_batch(self, seqs, tokens, argmax, logits=None):
+        mk_decode_batch(self.handle, seqs, tokens, argmax, logits)
 
     def generate_lookup(self, history, last_token: int, n_generate: int, ngram_min: int = 1, ngram_max: int = 3):
         return mk_generate_lookup(self.handle, history, last_token, n_generate, ngram_min, ngram_max)

@@ -71,7 +71,7 @@ enum { MK_DTYPE_BF16 = 1, MK_DTYPE_F16 = 2, MK_DTYPE_F32 = 3 };
  * a config): hidden % 256 == 0; dn_dk == dn_dv in {64, 128}; dn_heads <= 8;
  * conv_k == 4; at_head_dim in {64, 128}; at_q_heads <= 8 and a multiple of
  * at_kv_heads; ffn % 64 == 0; max_ctx a multiple of 64; prefill_chunk == 64;
- * 1 <= max_verify <= 5; tied_embedding == 1; kv_quant in {0, 1}.
+ * 1 <= max_verify <= 5; tied_embedding == 1; kv_quant in {0, 1}; 0 <= n_seq <= 5.
  *
  * kv_quant selects the KV-cache format (the launch page of the 8-bit cache: "8-bit KV cache"
  * limits of the Korean write-up, and the RTX 3090 tag page).  0: rows stored as bf16.  1: every
@@ -88,6 +88,7 @@ typedef struct mk_config {
   float rope_theta, rms_eps, l2_eps;
   int32_t tied_embedding, max_ctx, prefill_chunk, max_verify;
   int32_t kv_quant;          /* 0: bf16 KV cache; 1: 8-bit codes with a power-of-two scale per row */
+  int32_t n_seq;             /* sequences held at once, 1..5 (0 means 1); see mk_decode_batch     */
 } mk_config;
 
 /* One weight tensor in host memory.  Names and shapes ([out, in] for matrices):
@@ -123,8 +124,9 @@ int mk_required_bytes(const mk_config *cfg, size_t *arena_bytes);
 int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, int32_t n_tensors,
                     void *d_arena, size_t arena_bytes, void *stream, mk_model **out);
 
-/* Clear the recurrent state: DeltaNet states and conv history to zero, KV length
- * and position to zero, pending verify updates dropped, device error word cleared. */
+/* Clear the recurrent state of every sequence: DeltaNet states and conv history to
+ * zero, KV length and position to zero, pending verify updates dropped, device error
+ * words cleared.  The selected sequence stays selected.                            */
 int mk_reset_state(mk_model *m, void *stream);
 
 /* Prefill: append d_tokens[0..n_tokens) (device int32) at the current position,
@@ -168,6 +170,26 @@ enum { MK_STATIC_SCRATCH_BYTES = 16 << 20 };
  * needs clearing between calls).                                                          */
 int mk_decode_step_static(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_argmax,
                           float *d_logits, int32_t *d_n_accepted, void *stream);
+
+/* Sequences.  A model holds mk_config.n_seq sequences, each with its own DeltaNet states, conv
+ * history, KV cache, position and error word; the weights are shared.  mk_prefill, mk_decode_step,
+ * mk_decode_step_static, mk_generate_lookup, mk_sync_status (position) act on the selected
+ * sequence, 0 after loading.  mk_select_seq changes it (host-side only, nothing is enqueued); it
+ * fails with MK_EINVAL for seq outside [0, n_seq).                                         */
+int mk_select_seq(mk_model *m, int32_t seq);
+
+/* Batch decode (B sequences share one weight pass; concurrency section of the RTX 3090 tag page's
+ * Dflash2 item): one greedy decode step for each of the n distinct sequences seqs[0..n) (host
+ * array, 1 <= n <= n_seq), in one launch.  d_tokens[c] (device int32) is the last token of
+ * sequence seqs[c]; the greedy next token goes to d_argmax[c] and, if d_logits is not NULL, the
+ * logits to d_logits[c][vocab].  Each sequence's results equal those of mk_decode_step on that
+ * sequence alone, bit for bit; each position advances by one.  Rejected with MK_EINVAL (before
+ * anything is enqueued) for a bad or repeated sequence index, a model with kv_quant = 1, or a
+ * sequence whose last forward was a verify (a decode step or prefill on it applies its pending
+ * updates first); MK_ECTX if a sequence is at max_ctx.  Device errors are reported by the next
+ * mk_sync_status.                                                                            */
+int mk_decode_batch(mk_model *m, const int32_t *seqs, int32_t n, const int32_t *d_tokens, int32_t *d_argmax,
+                    float *d_logits, void *stream);
 
 /* Weight-free draft tokens for speculative decoding ("lookup-augmented draft" on the RTX 3090 tag
  * page; several drafts checked per weight pass with greedy output unchanged, speed section of the

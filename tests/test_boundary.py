@@ -76,8 +76,24 @@ def test_required_bytes_with_8bit_cache(so):
     assert saved - exps - 65536 <= a - b <= saved - exps + 65536
 
 
+def test_required_bytes_per_sequence(so):
+    """Each sequence past the first adds its own DeltaNet states, conv rings, pending buffers, KV
+    cache, control block and layer table; the weights are shared."""
+    cfg = W.HYBRID_24L
+    a = L.mk_required_bytes(cfg)
+    b = L.mk_required_bytes(dataclasses.replace(cfg, n_seq=3))
+    assert L.mk_required_bytes(dataclasses.replace(cfg, n_seq=0)) == a == L.mk_required_bytes(dataclasses.replace(cfg, n_seq=1))
+    n_dn, n_at = 18, 6
+    S = 8 * 128 * 128 * 4
+    ring = 8 * cfg.conv_channels * 4
+    pend = 2 * 8 * 5 * (256 + 4 * 128) * 4
+    kv = 2 * cfg.max_ctx * 2 * 128 * 2
+    per_seq = n_dn * (S + ring + pend) + n_at * kv
+    assert 2 * per_seq <= b - a <= 2 * per_seq + 2 * (cfg.n_layers * 3 + 2) * 256 + 2 * cfg.n_layers * 256
+
+
 @pytest.mark.parametrize("change", [
-    dict(kv_quant=2), dict(kv_quant=-1),
+    dict(kv_quant=2), dict(kv_quant=-1), dict(n_seq=6), dict(n_seq=-1),
     dict(hidden=300), dict(dn_heads=9), dict(dn_dk=96, dn_dv=96), dict(at_head_dim=32),
     dict(at_q_heads=6, at_kv_heads=4), dict(max_verify=6), dict(max_verify=0), dict(max_ctx=100),
     dict(max_ctx=20480), dict(prefill_chunk=32), dict(conv_k=3), dict(tied_embedding=False), dict(ffn=100),
@@ -156,6 +172,9 @@ def test_calls_on_unloaded_model_are_rejected(so):
     assert so.mk_decode_step(None, buf, 1, buf, None, None, None) == L.MK_ESTATE
     assert so.mk_decode_step_static(None, buf, 1, buf, None, None, None) == L.MK_ESTATE
     assert so.mk_reset_state(None, None) == L.MK_ESTATE
+    assert so.mk_select_seq(None, 0) == L.MK_ESTATE
+    seqs = (ctypes.c_int32 * 2)(0, 1)
+    assert so.mk_decode_batch(None, seqs, 2, buf, buf, None, None) == L.MK_ESTATE
     pos = ctypes.c_int32(0)
     assert so.mk_sync_status(None, None, ctypes.byref(pos)) == L.MK_ESTATE
     so.mk_free(None)  # no-op

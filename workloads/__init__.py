@@ -51,6 +51,7 @@ class ModelConfig:
     prefill_chunk: int = 64
     max_verify: int = 5
     kv_quant: int = 0          # 0: K/V cache in bfloat16; 1: 8-bit codes with a power-of-two scale per row
+    n_seq: int = 1             # sequences held at once (batch decode serves up to this many per launch)
 
     @property
     def n_layers(self) -> int:
