@@ -162,6 +162,43 @@ def long_context(model, cfg, stream, n_prompt: int = 8192, n_decode: int = 128) 
             "prefill_mfma_frac": round(pf["all"] / (pf_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def batch_decode(pkg, cfg, weights, stream, n_steps: int = 64) -> dict:
+    """Batch decode: B sequences (B = 1..5), each after its own 520-token seeded prompt, share one
+    weight pass per launch; n_steps launches chained on the device.  Aggregate tok/s counts every
+    sequence's token."""
+    import torch
+    dev = stream.device
+    nmax = 5
+    cfgb = dataclasses.replace(cfg, n_seq=nmax)
+    m = pkg.Model(cfgb, weights, device=str(dev))
+    prompts = [torch.tensor(W.make_prompt(cfg, 520, seed=1 + s), dtype=torch.int32, device=dev) for s in range(nmax)]
+    res = {}
+    for B in range(1, nmax + 1):
+        seqs = list(range(B))
+        tok = torch.zeros((n_steps + 1, B), dtype=torch.int32, device=dev)
+        for rep in range(2):          # the first pass warms the batch instantiation up
+            m.reset()
+            for s in seqs:
+                m.select(s)
+                m.prefill(prompts[s], tok[0, s:s + 1])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(n_steps):
+                m.decode_batch(seqs, tok[i], tok[i + 1])
+            e1.record(stream)
+            m.sync()
+        us = e0.elapsed_time(e1) * 1e3 / n_steps
+        by = decode_bytes_per_token(cfg, 520 + (n_steps - 1) / 2.0)
+        kv_state = by["all"] - by["weights"]
+        launch_bytes = by["weights"] + B * kv_state
+        res[f"B{B}"] = {"us_per_launch": round(us, 1), "aggregate_tok_s": round(B * 1e6 / us, 1),
+                        "hbm_frac": round(launch_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    m.close()
+    res["note"] = ("mk_decode_batch over sequences 0..B-1 of one model (n_seq = 5), each after its own pp520 prompt; "
+                   "B = 1 runs the five-column batch kernel with one column")
+    return res
+
+
 def extras(model, cfg, stream, weights=None) -> dict:
     """Secondary measurements on the same model: multi-token verify forwards after the pp520
     prompt (1 accepted + 4 seeded random drafts each, state rolled back to the accepted prefix),
@@ -250,6 +287,7 @@ def extras(model, cfg, stream, weights=None) -> dict:
     out["long_context_8192"] = long_context(model, cfg, stream)
     if weights is not None:
         import hybrid_deltanet_attention_persistent_amd as pkg
+        out["batch_decode"] = batch_decode(pkg, cfg, weights, stream)
         cfg8 = dataclasses.replace(cfg, name=cfg.name + "-q8", kv_quant=1)
         m8 = pkg.Model(cfg8, weights, device=str(dev))
         long_context(m8, cfg8, stream, 1024, 8)      # warm-up of the 8-bit instantiations

@@ -815,7 +815,9 @@ extern "C" int mk_decode_batch(mk_model *m, const int32_t *seqs, int32_t n, cons
   }
   a.tag0 = m->tag;
   a.xch = m->xch;
-  HIPCHECK(mk_launch_forward(&a, MK_MAXCOL, mk_shape_of(m->dev) | MK_BATCH, st));
+  // a batch of one is a decode step of that sequence: the one-column kernel (same arithmetic)
+  if (n == 1) HIPCHECK(mk_launch_forward(&a, 1, mk_variant_of(a.m), st));
+  else HIPCHECK(mk_launch_forward(&a, MK_MAXCOL, mk_shape_of(m->dev) | MK_BATCH, st));
   m->tag += 1;
   for (int32_t c = 0; c < n; ++c) m->seq_pos_hi[seqs[c]] += 1;
   m->pos_hi = m->seq_pos_hi[m->cur];

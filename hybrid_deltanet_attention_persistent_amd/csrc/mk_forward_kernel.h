@@ -38,6 +38,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <type_traits>
 #include "mk_layout.h"
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -530,8 +531,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // a.seq_layers[c], position a.seq_ctl[c][MK_CTL_POS]); no verify semantics, no pending updates
   constexpr bool BAT = (SH & MK_BATCH) != 0;
   static_assert(!BAT || (NCOL == MK_MAXCOL && !KVQ), "batch launches: MK_MAXCOL columns, bf16 cache");
-  // attention key steps prefetched with the weights (batch: none, every column reads its own cache)
-  constexpr int NPRE = BAT ? 0 : KVQ ? 3 : NKV_PRE;
+  // attention key steps prefetched with the weights (batch: the first step of every column, from
+  // its own cache: slots 2c, 2c + 1 of the prefetch registers)
+  constexpr int NPRE = BAT ? 1 : KVQ ? 3 : NKV_PRE;
   const int H = FX ? 1024 : m.H;
   // the layer table is read-only: reading it through the constant address space gives
   // scalar loads, so every pointer taken from it is known to be wave-uniform
@@ -597,6 +599,22 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // wr[2 NRG_IN, 2 NRG_IN + NRG_O); the FFN role its gate/up pairs in wr[0, 4 NPAIR) and its
   // down-projection row group in wr[4 NPAIR, 4 NPAIR + LMAX_D).
   u32x4 wr[NWR];
+  // batch: column c's prefetched K (KV false) or V (KV true) row, for a c that is not a
+  // compile-time constant.  (Each candidate passes an empty asm first: a select between loads of
+  // the register array could otherwise be folded into one load at a computed index, which would
+  // move the whole array to scratch memory.)
+  auto wsel = [&](int c, auto kvc) {
+    constexpr int kv = decltype(kvc)::value;
+    u32x4 v = wr[2 * NRG_IN + NRG_O + kv];
+    asm volatile("" : "+v"(v));
+#pragma unroll
+    for (int j = 1; j < NCOL; ++j) {
+      u32x4 t = wr[2 * NRG_IN + NRG_O + 2 * j + kv];
+      asm volatile("" : "+v"(t));
+      v = (c == j) ? t : v;
+    }
+    return v;
+  };
   float gv[16];                                          // gains of the role's RMSNorm (operand layout)
   // DeltaNet state of this wave for the next mixer phase, loaded with its weights
   float srow[2] = {0.f, 0.f}, hist[3] = {0.f, 0.f, 0.f}, grow = 0.f;
@@ -672,6 +690,43 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         const uint32_t pk = pj ? (uint32_t)((st * pks + 4 * lane) * 4) : OOB_OFF;
         wr[2 * NRG_IN + NRG_O + 2 * st] = __builtin_amdgcn_raw_buffer_load_b128(dn ? prs : krs, dn ? pv : off, 0, 0);
         wr[2 * NRG_IN + NRG_O + 2 * st + 1] = __builtin_amdgcn_raw_buffer_load_b128(dn ? prs : vrs, dn ? pk : off, 0, 0);
+      }
+    }
+    if constexpr (BAT) {
+      // batch: per column c, in slots 2c and 2c + 1 of the prefetch registers, that column's own
+      // sequence's DeltaNet state (S row of this wave: x, y; conv history of this lane's channel:
+      // z, w and the second slot's x) or its cached K and V rows of the first key step
+      const bool sdn = live && dn && x < nh, at = live && !dn && x < nq;
+      const bool chl = lane < CPW || (lane == 63 && w8 < RW);
+      const int conv_ch = conv_channel(lane);
+      const int lpk = hd / DPL, kpw = 64 / lpk, k = lg + MK_NG * (w8 * kpw + lane / lpk);
+#pragma unroll
+      for (int j = 0; j < NCOL; ++j) {
+        const bool lj = j < ncol;
+        ConstLayer &lyj = ((ConstLayer *)(uintptr_t)a.seq_layers[lj ? j : 0])[__builtin_amdgcn_readfirstlane(live ? l : 0)];
+        u32x4 &s0 = wr[2 * NRG_IN + NRG_O + 2 * j];
+        u32x4 &s1 = wr[2 * NRG_IN + NRG_O + 2 * j + 1];
+        if (dn) {
+          const bool ow = sdn && lj && w8 < RW;
+          const __amdgpu_buffer_rsrc_t rs = tile_rsrc(lyj.S + ((size_t)x * dv + r0 + (ow ? w8 : 0)) * dk, ow ? (uint32_t)(dk * 4) : 0u);
+          const __amdgpu_buffer_rsrc_t rr = tile_rsrc(lyj.ring, (sdn && lj) ? (uint32_t)(MK_RING * nconv * 4) : 0u);
+          uint32_t h[3];
+#pragma unroll
+          for (int i = 0; i < 3; ++i) {
+            const int pp = bpos[j] - 3 + i;
+            h[i] = __builtin_amdgcn_raw_buffer_load_b32(
+                rr, (chl && pp >= 0) ? (uint32_t)(((pp & (MK_RING - 1)) * nconv + conv_ch) * 4) : OOB_OFF, 0, AUX_DEV);
+          }
+          s0 = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, AUX_DEV),
+                     __builtin_amdgcn_raw_buffer_load_b32(rs, (64 + lane) * 4, 0, AUX_DEV), h[0], h[1]};
+          s1 = u32x4{h[2], 0u, 0u, 0u};
+        } else {
+          const __amdgpu_buffer_rsrc_t krs = tile_rsrc(lyj.kc, (at && lj) ? 0x7fffffffu : 0u);
+          const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(lyj.vc, (at && lj) ? 0x7fffffffu : 0u);
+          const uint32_t off = (k < bpos[j]) ? kv_off(ptl, k, kvh, nkv, hd, (lane % lpk) * 8) : OOB_OFF;
+          s0 = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+          s1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+        }
       }
     }
     // this wave's DeltaNet state: its row of S, the conv taps and history of its lane's channel,
@@ -838,25 +893,17 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           float *rsq = qkc + NCOL * 2 * dk;       // [NCOL][8]    per-wave sums of squares
           // batch: each column's conv history (this lane's channel) and S row (this wave's row)
           // come from its own sequence's state; loaded here, in flight during the gather
+          // (prefetched with the layer's weights, slots 2c and 2c + 1)
           float hb[NCOL][3], sb[NCOL][2];
           if constexpr (BAT) {
-            const bool chl = lane < CPW || (lane == 63 && w8 < RW);
-            const int conv_ch = conv_channel(lane);
 #pragma unroll
             for (int c = 0; c < NCOL; ++c) {
-              const bool lc = c < ncol;
-              ConstLayer &lc_ly = ((ConstLayer *)(uintptr_t)a.seq_layers[lc ? c : 0])[li];
-              const __amdgpu_buffer_rsrc_t rr = tile_rsrc(lc_ly.ring, lc ? (uint32_t)(MK_RING * nconv * 4) : 0u);
-#pragma unroll
-              for (int i = 0; i < 3; ++i) {
-                const int pp = bpos[c] - 3 + i;
-                hb[c][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    rr, (chl && pp >= 0) ? (uint32_t)(((pp & (MK_RING - 1)) * nconv + conv_ch) * 4) : OOB_OFF, 0, AUX_DEV));
-              }
-              const bool ow = lc && w8 < RW;
-              const __amdgpu_buffer_rsrc_t rs = tile_rsrc(lc_ly.S + ((size_t)x * dv + r0 + (ow ? w8 : 0)) * dk, ow ? (uint32_t)(dk * 4) : 0u);
-              sb[c][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, AUX_DEV));
-              sb[c][1] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (64 + lane) * 4, 0, AUX_DEV));
+              const u32x4 s0 = wr[2 * NRG_IN + NRG_O + 2 * c], s1 = wr[2 * NRG_IN + NRG_O + 2 * c + 1];
+              sb[c][0] = __uint_as_float(s0.x);
+              sb[c][1] = __uint_as_float(s0.y);
+              hb[c][0] = __uint_as_float(s0.z);
+              hb[c][1] = __uint_as_float(s0.w);
+              hb[c][2] = __uint_as_float(s1.x);
             }
           }
           {
@@ -1188,7 +1235,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               for (int st = 0; st < NPRE; ++st) {
                 if (st < nstc) {
                   float kf[DPL];
-                  kv_unpack<DPL>(wr[2 * NRG_IN + NRG_O + 2 * st], kf);
+                  kv_unpack<DPL>(BAT ? wsel(c, std::integral_constant<int, 0>{}) : wr[2 * NRG_IN + NRG_O + 2 * st], kf);
                   score(st * spw + kslot, kf, KVQ ? q8_scale(kvx[st] & 0xffu) : 1.f);
                 }
               }
@@ -1252,7 +1299,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               for (int st = 0; st < NPRE; ++st) {
                 if (st < nstc) {
                   float vf[DPL];
-                  kv_unpack<DPL>(wr[2 * NRG_IN + NRG_O + 2 * st + 1], vf);
+                  kv_unpack<DPL>(BAT ? wsel(c, std::integral_constant<int, 1>{}) : wr[2 * NRG_IN + NRG_O + 2 * st + 1], vf);
                   pvacc(st * spw + kslot, vf, KVQ ? q8_scale(kvx[st] >> 8) : 1.f);
                 }
               }
