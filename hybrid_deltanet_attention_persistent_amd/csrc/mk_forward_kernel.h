@@ -531,9 +531,10 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // a.seq_layers[c], position a.seq_ctl[c][MK_CTL_POS]); no verify semantics, no pending updates
   constexpr bool BAT = (SH & MK_BATCH) != 0;
   static_assert(!BAT || (NCOL == MK_MAXCOL && !KVQ), "batch launches: MK_MAXCOL columns, bf16 cache");
-  // attention key steps prefetched with the weights (batch: the first step of every column, from
-  // its own cache: slots 2c, 2c + 1 of the prefetch registers)
-  constexpr int NPRE = BAT ? 1 : KVQ ? 3 : NKV_PRE;
+  // attention key steps prefetched with the weights (batch: the first two steps of every column,
+  // from its own cache: step 0 in slots 2c, 2c + 1 of the prefetch registers, loaded with the
+  // weights; step 1 in registers 2c, 2c + 1, loaded at the start of A2)
+  constexpr int NPRE = BAT ? 2 : KVQ ? 3 : NKV_PRE;
   const int H = FX ? 1024 : m.H;
   // the layer table is read-only: reading it through the constant address space gives
   // scalar loads, so every pointer taken from it is known to be wave-uniform
@@ -603,13 +604,15 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   // compile-time constant.  (Each candidate passes an empty asm first: a select between loads of
   // the register array could otherwise be folded into one load at a computed index, which would
   // move the whole array to scratch memory.)
-  auto wsel = [&](int c, auto kvc) {
-    constexpr int kv = decltype(kvc)::value;
-    u32x4 v = wr[2 * NRG_IN + NRG_O + kv];
+  // Step 0 sits in the prefetch slots, step 1 in the slots of the in-projection rows (free once
+  // A1 has used them).
+  auto wsel = [&](int c, auto kvc, auto stc) {
+    constexpr int kv = decltype(kvc)::value, base = decltype(stc)::value == 0 ? 2 * NRG_IN + NRG_O : 0;
+    u32x4 v = wr[base + kv];
     asm volatile("" : "+v"(v));
 #pragma unroll
     for (int j = 1; j < NCOL; ++j) {
-      u32x4 t = wr[2 * NRG_IN + NRG_O + 2 * j + kv];
+      u32x4 t = wr[base + 2 * j + kv];
       asm volatile("" : "+v"(t));
       v = (c == j) ? t : v;
     }
@@ -1095,6 +1098,22 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           // 8-bit cache: scales 2^e of this forward's K, V rows [NCOL][2] (past the split-KV buffers below)
           float *kvs = work + NCOL * 3 * hd + 640 + MK_WAVES * hd + 2;
           if (!gather2d<MCS, MK_WAVES>(xin, ncol, 3 * hd, r_in_max, tg, qkv, flag, m.ctl, SITE(6), tid)) MK_BAIL();
+          if constexpr (BAT) {
+            // every column's cached K and V rows of key step 1 (see NPRE), issued after the gather (a
+            // wave's loads complete in order: issued before it, they would delay its polls)
+            const int lpk = hd / DPL, kpw = 64 / lpk;
+            const int k = lg + MK_NG * (MK_WAVES * kpw + w8 * kpw + lane / lpk);
+#pragma unroll
+            for (int j = 0; j < NCOL; ++j) {
+              const bool lj = j < ncol;
+              ConstLayer &lyj = ((ConstLayer *)(uintptr_t)a.seq_layers[lj ? j : 0])[li];
+              const __amdgpu_buffer_rsrc_t krs = tile_rsrc(lyj.kc, lj ? 0x7fffffffu : 0u);
+              const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(lyj.vc, lj ? 0x7fffffffu : 0u);
+              const uint32_t off = (k < bpos[j]) ? kv_off(ptl, k, kvh, nkv, hd, (lane % lpk) * 8) : OOB_OFF;
+              wr[2 * j] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+              wr[2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+            }
+          }
           MK_TRACE_POINT(li, 3);
           {
             const int half = hd / 2;
@@ -1235,7 +1254,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               for (int st = 0; st < NPRE; ++st) {
                 if (st < nstc) {
                   float kf[DPL];
-                  kv_unpack<DPL>(BAT ? wsel(c, std::integral_constant<int, 0>{}) : wr[2 * NRG_IN + NRG_O + 2 * st], kf);
+                  kv_unpack<DPL>(!BAT ? wr[2 * NRG_IN + NRG_O + 2 * st]
+                                 : st == 0 ? wsel(c, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{})
+                                           : wsel(c, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}), kf);
                   score(st * spw + kslot, kf, KVQ ? q8_scale(kvx[st] & 0xffu) : 1.f);
                 }
               }
@@ -1299,7 +1320,9 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               for (int st = 0; st < NPRE; ++st) {
                 if (st < nstc) {
                   float vf[DPL];
-                  kv_unpack<DPL>(BAT ? wsel(c, std::integral_constant<int, 1>{}) : wr[2 * NRG_IN + NRG_O + 2 * st + 1], vf);
+                  kv_unpack<DPL>(!BAT ? wr[2 * NRG_IN + NRG_O + 2 * st + 1]
+                                 : st == 0 ? wsel(c, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{})
+                                           : wsel(c, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}), vf);
                   pvacc(st * spw + kslot, vf, KVQ ? q8_scale(kvx[st] >> 8) : 1.f);
                 }
               }
