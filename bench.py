@@ -195,7 +195,7 @@ def batch_decode(pkg, cfg, weights, stream, n_steps: int = 64) -> dict:
                         "hbm_frac": round(launch_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     m.close()
     res["note"] = ("mk_decode_batch over sequences 0..B-1 of one model (n_seq = 5), each after its own pp520 prompt; "
-                   "B = 1 runs the five-column batch kernel with one column")
+                   "B = 1 runs the one-column decode kernel, B >= 2 the five-column batch kernel")
     return res
 
 
