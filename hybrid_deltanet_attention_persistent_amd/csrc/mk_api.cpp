@@ -368,6 +368,7 @@ static int validate_tensors(const mk_config *cfg, const mk_tensor *t, int32_t n,
     for (size_t d = 0; ok && d < sh.size(); ++d) ok = t[i].shape[d] == sh[d];
     if (!ok) return fail(MK_ESHAPE, "tensor '" + name + "' has the wrong shape");
     if (!t[i].data) return fail(MK_EINVAL, "tensor '" + name + "' has no data");
+    if (t[i].on_device != 0 && t[i].on_device != 1) return fail(MK_EINVAL, "tensor '" + name + "': on_device must be 0 or 1");
     it->second.t = &t[i];
   }
   for (auto &kv : exp)
@@ -418,7 +419,22 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   HIPCHECK(mk_static_scratch(&static_xch));
   hipStream_t st = (hipStream_t)stream;
   char *A = (char *)d_arena;
-  auto T = [&](const std::string &name) { return (const uint16_t *)exp[name].t->data; };
+  // tensors in device memory: host copies for the re-tiling below
+  std::map<std::string, std::vector<uint16_t>> host_copy;
+  HIPCHECK(hipStreamSynchronize(st));
+  for (auto &kv : exp) {
+    const mk_tensor *t = kv.second.t;
+    if (!t->on_device) continue;
+    size_t n = 1;
+    for (int64_t d : kv.second.shape) n *= (size_t)d;
+    std::vector<uint16_t> &h = host_copy[kv.first];
+    h.resize(n);
+    HIPCHECK(hipMemcpy(h.data(), t->data, n * 2, hipMemcpyDeviceToHost));
+  }
+  auto T = [&](const std::string &name) {
+    auto it = host_copy.find(name);
+    return it != host_copy.end() ? (const uint16_t *)it->second.data() : (const uint16_t *)exp[name].t->data;
+  };
   auto put = [&](const Region &r, const void *host) -> hipError_t {
     hipError_t e = hipMemcpyAsync(A + r.off, host, r.bytes, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return e;

@@ -53,7 +53,7 @@ class MkLookupStats(ctypes.Structure):
 
 class MkTensor(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
-                ("shape", ctypes.c_int64 * 4), ("data", ctypes.c_void_p)]
+                ("shape", ctypes.c_int64 * 4), ("data", ctypes.c_void_p), ("on_device", ctypes.c_int32)]
 
 
 _lib = None
@@ -112,16 +112,22 @@ def make_config(cfg) -> tuple:
 
 
 def make_tensors(weights: Dict[str, np.ndarray], dtype: int = MK_DTYPE_BF16):
-    """mk_tensor array over host numpy arrays (uint16 bf16 bit patterns); returns (array, keep-alive)."""
+    """mk_tensor array over the weights (bf16 bit patterns as uint16: host numpy arrays, or contiguous
+    torch tensors, which may live on the GPU); returns (array, keep-alive)."""
     keep = []
     arr = (MkTensor * len(weights))()
     for i, (name, a) in enumerate(weights.items()):
-        a = np.ascontiguousarray(a)
+        if hasattr(a, "data_ptr"):           # torch tensor (host or device memory)
+            a = a.contiguous()
+            ptr, on_dev, shp = a.data_ptr(), 1 if a.is_cuda else 0, tuple(a.shape)
+        else:
+            a = np.ascontiguousarray(a)
+            ptr, on_dev, shp = a.ctypes.data, 0, a.shape
         keep.append(a)
         nm = name.encode()
         keep.append(nm)
-        shape = (ctypes.c_int64 * 4)(*(list(a.shape) + [0] * (4 - a.ndim)))
-        arr[i] = MkTensor(nm, dtype, a.ndim, shape, a.ctypes.data)
+        shape = (ctypes.c_int64 * 4)(*(list(shp) + [0] * (4 - len(shp))))
+        arr[i] = MkTensor(nm, dtype, len(shp), shape, ptr, on_dev)
     return arr, keep
 
 

@@ -107,7 +107,9 @@ typedef struct mk_tensor {
   int32_t dtype;
   int32_t ndim;
   int64_t shape[4];
-  const void *data; /* host pointer; only read during mk_load_weights             */
+  const void *data; /* only read during mk_load_weights                            */
+  int32_t on_device; /* 0: data is host memory; 1: device memory of the current device
+                        (copied to the host for re-tiling, after the stream is synchronised) */
 } mk_tensor;
 
 typedef struct mk_model mk_model; /* opaque */

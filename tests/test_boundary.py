@@ -138,6 +138,14 @@ def test_loader_checks_every_tensor_type(so, tiny_weights):
         assert name in so.mk_last_error().decode()
 
 
+def test_loader_rejects_bad_on_device_flag(so, tiny_weights):
+    arr, keep = L.make_tensors(tiny_weights)
+    arr[3].on_device = 2
+    st, h = _load(so, W.TINY, tiny_weights, tensors=(arr, keep))
+    assert st == L.MK_EINVAL and h is None
+    assert "on_device" in so.mk_last_error().decode()
+
+
 def test_loader_rejects_shape_missing_unknown_duplicate(so, tiny_weights):
     w = dict(tiny_weights)
     w["layers.0.dn.wq"] = w["layers.0.dn.wq"][:, :128]

@@ -121,6 +121,24 @@ def test_tiny_teacher_forced_random_tokens(dev, tiny):
     r.close()
 
 
+def test_tiny_weights_from_device_memory(dev, tiny):
+    """mk_tensor.on_device = 1: weights handed over as GPU tensors load to the same model, bit for bit."""
+    cfg = W.TINY
+    prompt = W.make_prompt(cfg, 16, seed=1)
+    dw = {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).to(dev) for k, v in tiny.items()}
+    outs = []
+    for weights in (tiny, dw):
+        r = Runner(cfg, weights, dev)
+        g, lg = r.prefill(prompt)
+        g2, lg2 = r.decode(g)
+        outs.append((g, lg, g2, lg2))
+        r.close()
+    a, b = outs
+    assert a[0] == b[0] and a[2] == b[2]
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32))
+
+
 def test_tiny_nonunit_gains(dev):
     cfg = W.TINY
     w = W.make_weights(cfg, seed=3, gain_std=0.1)
