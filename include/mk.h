@@ -177,7 +177,8 @@ int mk_decode_step_static(mk_model *m, const int32_t *d_tokens, int32_t n_tokens
  * history, KV cache, position and error word; the weights are shared.  mk_prefill, mk_decode_step,
  * mk_decode_step_static, mk_generate_lookup, mk_sync_status (position) act on the selected
  * sequence, 0 after loading.  mk_select_seq changes it (host-side only, nothing is enqueued); it
- * fails with MK_EINVAL for seq outside [0, n_seq).                                         */
+ * fails with MK_EINVAL for seq outside [0, n_seq).  All sequences of a model share its prefill
+ * scratch and exchange slots: calls on one model, whatever the sequence, are ordered on one stream. */
 int mk_select_seq(mk_model *m, int32_t seq);
 
 /* Batch decode (B sequences share one weight pass; concurrency section of the RTX 3090 tag page's
