@@ -449,6 +449,10 @@ __device__ __forceinline__ void ld_gain16(const float *p, int H, int G, bool liv
 
 // loop over the live columns with compile-time indices (register arrays stay in registers)
 #define FOR_COL(c) _Pragma("unroll") for (int c = 0; c < NCOL; ++c) if (c < ncol)
+// loop over the live columns at run time, for bodies that index no register array by column: one
+// copy of the body.  (Measured: 8 KB of code that never runs made decode 4 % slower, so the
+// multi-column kernels keep one copy of each GEMV phase instead of NCOL.)
+#define FOR_COL_R(c) _Pragma("unroll 1") for (int c = 0; c < NCOL && c < ncol; ++c)
 
 // On a watchdog expiry the whole workgroup records the error and leaves; the other
 // workgroups then time out on its missing outputs and leave too.
@@ -545,12 +549,17 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   float *work = xres + NCOL * H;                // [WORK] phase scratch
   float *red = work + WORK;                     // [64] reductions
   int *flag = reinterpret_cast<int *>(red + 64);
+  // batch: the columns' sequence positions, for loops whose column index is not a compile-time
+  // constant (written at start, first read after many barriers)
+  int *bposl = flag + 8;                        // [NCOL] (flag[8 .. 8 + NCOL))
   // the page table of the KV cache (logical page -> physical page), read once per launch
   int *ptl = flag + 16;                         // [160] (10240 positions / 64)
   // RoPE cos / sin of this launch's positions [NCOL][hd / 2][2] (hd <= 128), loaded with the
   // embedding rows so that no attention layer waits for them
   float *rl = reinterpret_cast<float *>(ptl + 160);
   for (int i = tid0; i < m.max_pages; i += MK_THREADS) ptl[i] = m.page_table[i];
+  if (BAT && tid0 < NCOL)
+    bposl[tid0] = tid0 < a.n ? __hip_atomic_load(a.seq_ctl[tid0] + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
   if (tid0 == 0) {
     flag[0] = 0;
     uint32_t xcc;
@@ -570,13 +579,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     bpos[c] = (BAT && c < a.n) ? __builtin_amdgcn_readfirstlane(
                                      __hip_atomic_load(a.seq_ctl[c] + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
                                : 0;
-  auto bsel = [&](const auto (&arr)[NCOL], int c) {
-    auto v = arr[0];
-#pragma unroll
-    for (int j = 1; j < NCOL; ++j)
-      if (c == j) v = arr[j];
-    return v;
-  };
+
   const int ncol = a.n;
   const int G_h = mk_tile_G(H), L_h = H / 8 / G_h, RG_h = 64 / G_h;
   const int SL = H / MK_NG;  // residual slice per workgroup in the reductions
@@ -821,7 +824,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
     const int half = hd / 2;
     for (int i = tid0; i < ncol * half; i += MK_THREADS) {
       const int c = i / half, d = i - c * half;
-      const int pc = BAT ? bsel(bpos, c) : pos0 + c;
+      const int pc = BAT ? __hip_atomic_load(a.seq_ctl[c] + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : pos0 + c;
       const float2 r = *reinterpret_cast<const float2 *>(m.rope + ((size_t)pc * half + d) * 2);
       rl[i * 2 + 0] = r.x;
       rl[i * 2 + 1] = r.y;
@@ -863,7 +866,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         // ---- D1: in-projection rows u = wx + r XW of head x (weights already in registers)
         if (x < nh) {
           const int nrg = r_in / RG_h;
-          FOR_COL(c) {
+          FOR_COL_R(c) {
             float av[16];
             rmsnorm_regs(xres + c * H, gv, H, G_h, L_h, m.rms_eps, av);
             if (G_h == 64) {  // one row per row group: rows 0-3 of this wave reduced together, then row 4
@@ -1025,7 +1028,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
           if (!gather2d<MCS, MK_WAVES>(xo, ncol, 2 * dv, x_o_len, tg, d3, flag, m.ctl, SITE(4), tid)) MK_BAIL();
           MK_TRACE_POINT(li, 5);
           const int kl = (lane & (G_o - 1)) * 8;
-          FOR_COL(c) {
+          FOR_COL_R(c) {
             float ss = 0.f, uu[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -1056,7 +1059,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         if (x < nq) {
           // ---- A1: q rows of head x, k / v rows of its kv head (weights already in registers)
           const int per = hd / RG_h;
-          FOR_COL(c) {
+          FOR_COL_R(c) {
             float av[16];
             rmsnorm_regs(xres + c * H, gv, H, G_h, L_h, m.rms_eps, av);
             if (G_h == 64) {  // row group u is row u (t hd + rg == u)
@@ -1216,24 +1219,18 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             auto row_off = [&](int ks) {
               return KVQ ? kv8_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0);
             };
-            // batch: each column's own cache (its sequence's K and V of this layer)
-            const void *bkc[NCOL], *bvc[NCOL];
-#pragma unroll
-            for (int c = 0; c < NCOL; ++c) {
-              ConstLayer &cl = ((ConstLayer *)(uintptr_t)a.seq_layers[(BAT && c < ncol) ? c : 0])[li];
-              bkc[c] = BAT ? cl.kc : nullptr;
-              bvc[c] = BAT ? cl.vc : nullptr;
-            }
 #pragma unroll 1
             for (int c = 0; c < ncol; ++c) {
               // first position of this forward in column c's sequence: cached keys are below it
-              const int base = BAT ? bsel(bpos, c) : pos0;
+              const int base = BAT ? bposl[c] : pos0;
               const int P = BAT ? base : pos0 + c;  // query position; keys 0..P
               // cached keys of this workgroup: slots [0, ncache)
               const int ncache = (base > lg) ? (base - 1 - lg) / MK_NG + 1 : 0;
               const int nstc = (ncache + spw - 1) / spw;
-              const __amdgpu_buffer_rsrc_t krs = BAT ? __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(bsel(bkc, c)), 0, 0x7fffffff, RSRC_W3) : krs0;
-              const __amdgpu_buffer_rsrc_t vrs = BAT ? __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(bsel(bvc, c)), 0, 0x7fffffff, RSRC_W3) : vrs0;
+              // (batch: column c's own cache, its sequence's K and V of this layer)
+              ConstLayer &cl = ((ConstLayer *)(uintptr_t)a.seq_layers[BAT ? c : 0])[li];
+              const __amdgpu_buffer_rsrc_t krs = BAT ? __builtin_amdgcn_make_buffer_rsrc(cl.kc, 0, 0x7fffffff, RSRC_W3) : krs0;
+              const __amdgpu_buffer_rsrc_t vrs = BAT ? __builtin_amdgcn_make_buffer_rsrc(cl.vc, 0, 0x7fffffff, RSRC_W3) : vrs0;
               const int nk = (P >= lg) ? (P - lg) / MK_NG + 1 : 0;
               // this forward's key of this workgroup, if any: position kc_ in [base, P], slot nk - 1
               const int kc_ = lg + MK_NG * (nk - 1);
@@ -1433,7 +1430,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             lbar();
             MK_TRACE_POINT(li, 5);
             const int kl = (lane & (G_a - 1)) * 8;
-            FOR_COL(c) {
+            FOR_COL_R(c) {
 #pragma unroll
               for (int r = 0; r < NRG_O; ++r) {
                 const int rg = wx + r * XW;
@@ -1467,7 +1464,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
       MK_TRACE_POINT(li, 9);
       uint2 *xm = x_m_l + (size_t)x * NCOL * xm_len;
       // ---- F1: gate/up pairs j = wx + pr XW -> m_j = SiLU(g_j) u_j (weights already in registers)
-      FOR_COL(c) {
+      FOR_COL_R(c) {
         float av[16];
         rmsnorm_regs(xres + c * H, gv, H, G_h, L_h, m.rms_eps, av);
         if (RG_h == 1 && L_h == 2) {
@@ -1506,7 +1503,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
         MK_TRACE_POINT(li, 11);
         if (wx < H / RG_d) {
           const int kl = (lane & (G_d - 1)) * 8;
-          FOR_COL(c) {
+          FOR_COL_R(c) {
             // every activation load of the column first, then the products alternating between two
             // accumulators (the loads overlap, the dependent chain is half as long)
             float4 av[LMAX_D][2];
