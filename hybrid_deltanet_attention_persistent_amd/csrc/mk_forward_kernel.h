@@ -1219,175 +1219,345 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
             auto row_off = [&](int ks) {
               return KVQ ? kv8_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0) : kv_off(ptl, lg + MK_NG * ks, kvh, nkv, hd, d0);
             };
-#pragma unroll 1
-            for (int c = 0; c < ncol; ++c) {
-              // first position of this forward in column c's sequence: cached keys are below it
-              const int base = BAT ? bposl[c] : pos0;
-              const int P = BAT ? base : pos0 + c;  // query position; keys 0..P
-              // cached keys of this workgroup: slots [0, ncache)
-              const int ncache = (base > lg) ? (base - 1 - lg) / MK_NG + 1 : 0;
+if constexpr (NCOL > 1 && !BAT && !KVQ) {
+              // Verify: every column reads the same cached keys and values (the sequence's, below
+              // pos0), so each cached row is converted once and used for all columns, and the phase
+              // has four barriers instead of four per column.  Per column the products, sums and their
+              // order are those of the one-column loop below, so the results equal decode's bit for
+              // bit.  Column c: scores at scv + 640 c, P.V partials at pvv + MK_WAVES hd c, max and sum
+              // at mxv[2 c], mxv[2 c + 1].
+              float *scv = sc;                                 // [NCOL][640]
+              float *pvv = scv + NCOL * 640;                   // [NCOL][MK_WAVES][hd]
+              float *mxv = pvv + NCOL * MK_WAVES * hd;         // [NCOL][2]
+              const int ncache = (pos0 > lg) ? (pos0 - 1 - lg) / MK_NG + 1 : 0;
               const int nstc = (ncache + spw - 1) / spw;
-              // (batch: column c's own cache, its sequence's K and V of this layer)
-              ConstLayer &cl = ((ConstLayer *)(uintptr_t)a.seq_layers[BAT ? c : 0])[li];
-              const __amdgpu_buffer_rsrc_t krs = BAT ? __builtin_amdgcn_make_buffer_rsrc(cl.kc, 0, 0x7fffffff, RSRC_W3) : krs0;
-              const __amdgpu_buffer_rsrc_t vrs = BAT ? __builtin_amdgcn_make_buffer_rsrc(cl.vc, 0, 0x7fffffff, RSRC_W3) : vrs0;
-              const int nk = (P >= lg) ? (P - lg) / MK_NG + 1 : 0;
-              // this forward's key of this workgroup, if any: position kc_ in [base, P], slot nk - 1
-              const int kc_ = lg + MK_NG * (nk - 1);
-              const bool hascur = nk > 0 && kc_ >= base;
-              const int crow = BAT ? c : kc_ - pos0;   // its row of this forward's K, V in LDS
-              float qv[DPL];
+              // keys of this workgroup up to column c's position, and its own key (at most one)
+              auto nkc = [&](int c) { const int P = pos0 + c; return (P >= lg) ? (P - lg) / MK_NG + 1 : 0; };
+              float qv[NCOL][DPL];   // (columns past ncol: zeros, computed and never stored)
 #pragma unroll
-              for (int i = 0; i < DPL; ++i) qv[i] = qkv[c * 3 * hd + d0 + i];
-              auto score = [&](int ks, const float (&kf)[DPL], float ksc) {
-                float sdot = 0.f;
+              for (int c = 0; c < NCOL; ++c)
 #pragma unroll
-                for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kf[i], sdot);
-                if constexpr (KVQ) sdot *= ksc;
-                sdot = group_sum(sdot, lpk);
-                if (ks < ncache && (lane % lpk) == 0) sc[ks] = sdot * scale;
+                for (int i = 0; i < DPL; ++i) qv[c][i] = (c < ncol) ? qkv[c * 3 * hd + d0 + i] : 0.f;
+              auto score_all = [&](int ks, const float (&kf)[DPL]) {
+#pragma unroll
+                for (int c = 0; c < NCOL; ++c) {
+                  float sdot = 0.f;
+#pragma unroll
+                  for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[c][i], kf[i], sdot);
+                  sdot = group_sum(sdot, lpk);
+                  if (c < ncol && ks < ncache && (lane % lpk) == 0) scv[c * 640 + ks] = sdot * scale;
+                }
               };
 #pragma unroll
               for (int st = 0; st < NPRE; ++st) {
                 if (st < nstc) {
                   float kf[DPL];
-                  kv_unpack<DPL>(!BAT ? wr[2 * NRG_IN + NRG_O + 2 * st]
-                                 : st == 0 ? wsel(c, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{})
-                                           : wsel(c, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}), kf);
-                  score(st * spw + kslot, kf, KVQ ? q8_scale(kvx[st] & 0xffu) : 1.f);
+                  kv_unpack<DPL>(wr[2 * NRG_IN + NRG_O + 2 * st], kf);
+                  score_all(st * spw + kslot, kf);
                 }
               }
-              // later steps: KV_GRP steps' loads issued together, then used in step order
 #pragma unroll 1
               for (int st = NPRE; st < nstc; st += KV_GRP) {
                 u32x4 kr[KV_GRP];
-                uint32_t ke[KV_GRP];
 #pragma unroll
                 for (int u = 0; u < KV_GRP; ++u) {
                   const int ks = (st + u) * spw + kslot;
-                  kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, ks < ncache ? row_off(ks) : OOB_OFF, 0, 0);
-                  if constexpr (KVQ) ke[u] = __builtin_amdgcn_raw_buffer_load_b8(ers, ks < ncache ? kve_off(ptl, lg + MK_NG * ks, kvh, nkv) : OOB_OFF, 0, 0);
-                  else ke[u] = 0;
+                  kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs0, ks < ncache ? row_off(ks) : OOB_OFF, 0, 0);
                 }
 #pragma unroll
                 for (int u = 0; u < KV_GRP; ++u) {
                   if (st + u < nstc) {
                     float kf[DPL];
                     kv_unpack<DPL>(kr[u], kf);
-                    score((st + u) * spw + kslot, kf, KVQ ? q8_scale(ke[u]) : 1.f);
+                    score_all((st + u) * spw + kslot, kf);
                   }
                 }
               }
-              if (hascur && w8 == 0 && lane < lpk) {   // this forward's key: from LDS
-                const float *kk = qkv + crow * 3 * hd + hd + d0;
-                float sdot = 0.f;
+              if (w8 == 0 && lane < lpk) {   // this forward's keys: from LDS
 #pragma unroll
-                for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kk[i], sdot);
-                if constexpr (KVQ) sdot *= kvs[crow * 2];
-                sdot = group_sum(sdot, lpk);
-                if (lane == 0) sc[nk - 1] = sdot * scale;
+                for (int c = 0; c < NCOL; ++c) {
+                  const int nk = nkc(c), kc_ = lg + MK_NG * (nk - 1);
+                  if (c < ncol && nk > 0 && kc_ >= pos0) {
+                    const float *kk = qkv + (kc_ - pos0) * 3 * hd + hd + d0;
+                    float sdot = 0.f;
+#pragma unroll
+                    for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[c][i], kk[i], sdot);
+                    sdot = group_sum(sdot, lpk);
+                    if (lane == 0) scv[c * 640 + nk - 1] = sdot * scale;
+                  }
+                }
               }
               lbar();
-              if (w8 == 0) {
+              if (w8 < ncol) {   // softmax of column w8
+                const int c = w8, nk = nkc(c);
+                float *scc = scv + c * 640;
                 float mv = -INFINITY;
-                for (int i = lane; i < nk; i += 64) mv = fmaxf(mv, sc[i]);
+                for (int i = lane; i < nk; i += 64) mv = fmaxf(mv, scc[i]);
 #pragma unroll
                 for (int off = 32; off > 0; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off, 64));
                 float ls = 0.f;
                 for (int i = lane; i < nk; i += 64) {
-                  const float pe = __expf(sc[i] - mv);
-                  sc[i] = pe;
+                  const float pe = __expf(scc[i] - mv);
+                  scc[i] = pe;
                   ls += pe;
                 }
                 ls = wave_sum(ls);
-                if (lane == 0) { mx[0] = mv; mx[1] = ls; }
+                if (lane == 0) { mxv[2 * c] = mv; mxv[2 * c + 1] = ls; }
               }
               lbar();
-              // P.V over the same slots: each lane accumulates its 8 dimensions
-              float acc[DPL];
+              float acc[NCOL][DPL];
 #pragma unroll
-              for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-              auto pvacc = [&](int ks, const float (&vf)[DPL], float vsc) {
-                float pe = (ks < ncache) ? sc[ks < ncache ? ks : 0] : 0.f;
-                if constexpr (KVQ) pe *= vsc;
+              for (int c = 0; c < NCOL; ++c)
 #pragma unroll
-                for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vf[i], acc[i]);
+                for (int i = 0; i < DPL; ++i) acc[c][i] = 0.f;
+              auto pvacc_all = [&](int ks, const float (&vf)[DPL]) {
+#pragma unroll
+                for (int c = 0; c < NCOL; ++c) {
+                  const float pe = (ks < ncache) ? scv[c * 640 + (ks < ncache ? ks : 0)] : 0.f;
+#pragma unroll
+                  for (int i = 0; i < DPL; ++i) acc[c][i] = fmaf(pe, vf[i], acc[c][i]);
+                }
               };
 #pragma unroll
               for (int st = 0; st < NPRE; ++st) {
                 if (st < nstc) {
                   float vf[DPL];
-                  kv_unpack<DPL>(!BAT ? wr[2 * NRG_IN + NRG_O + 2 * st + 1]
-                                 : st == 0 ? wsel(c, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{})
-                                           : wsel(c, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}), vf);
-                  pvacc(st * spw + kslot, vf, KVQ ? q8_scale(kvx[st] >> 8) : 1.f);
+                  kv_unpack<DPL>(wr[2 * NRG_IN + NRG_O + 2 * st + 1], vf);
+                  pvacc_all(st * spw + kslot, vf);
                 }
               }
 #pragma unroll 1
               for (int st = NPRE; st < nstc; st += KV_GRP) {
                 u32x4 vr[KV_GRP];
-                uint32_t ve[KV_GRP];
 #pragma unroll
                 for (int u = 0; u < KV_GRP; ++u) {
                   const int ks = (st + u) * spw + kslot;
-                  vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ks < ncache ? row_off(ks) : OOB_OFF, 0, 0);
-                  if constexpr (KVQ) ve[u] = __builtin_amdgcn_raw_buffer_load_b8(ers, ks < ncache ? kve_off(ptl, lg + MK_NG * ks, kvh, nkv) + 1 : OOB_OFF, 0, 0);
-                  else ve[u] = 0;
+                  vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs0, ks < ncache ? row_off(ks) : OOB_OFF, 0, 0);
                 }
 #pragma unroll
                 for (int u = 0; u < KV_GRP; ++u) {
                   if (st + u < nstc) {
                     float vf[DPL];
                     kv_unpack<DPL>(vr[u], vf);
-                    pvacc((st + u) * spw + kslot, vf, KVQ ? q8_scale(ve[u]) : 1.f);
+                    pvacc_all((st + u) * spw + kslot, vf);
                   }
                 }
               }
-              // this forward's value, from LDS, added by the lanes that own its slot in the step order
-              // (as a cached key of a later decode step it is accumulated there: same additions, same
-              // order, so verify and sequential decode agree bit for bit)
-              const int kcs = (nk - 1) % spw;
-              if (hascur && w8 == kcs / kpw && lane / lpk == kcs % kpw) {
-                float pe = sc[nk - 1];
-                if constexpr (KVQ) pe *= kvs[crow * 2 + 1];
-                const float *vv = qkv + crow * 3 * hd + 2 * hd + d0;
 #pragma unroll
-                for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vv[i], acc[i]);
-              }
-              // sum over the kpw key groups of the wave (lanes l, l + lpk, ...), then over the waves
+              for (int c = 0; c < NCOL; ++c) {
+                // this forward's value, added by the lanes that own its slot in the step order
+                const int nk = nkc(c), kc_ = lg + MK_NG * (nk - 1), kcs = (nk - 1) % spw;
+                if (c < ncol && nk > 0 && kc_ >= pos0 && w8 == kcs / kpw && lane / lpk == kcs % kpw) {
+                  const float pe = scv[c * 640 + nk - 1];
+                  const float *vv = qkv + (kc_ - pos0) * 3 * hd + 2 * hd + d0;
 #pragma unroll
-              for (int i = 0; i < DPL; ++i) {
-                float v = acc[i];
-                if (lpk == 16) {
-                  v = swap_add32(v, v);
-                  v = swap_add16(v, v);
-                } else if (lpk == 8) {
-                  v = dpp_add<DPP_ROR8>(v);   // (l, l ^ 8) within each row of 16 lanes
-                  v = swap_add32(v, v);
-                  v = swap_add16(v, v);
-                } else {
-                  for (int o = lpk; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+                  for (int i = 0; i < DPL; ++i) acc[c][i] = fmaf(pe, vv[i], acc[c][i]);
                 }
-                acc[i] = v;
-              }
-              if (lane < lpk) {
+                // sum over the kpw key groups of the wave, as in the one-column loop
 #pragma unroll
-                for (int i = 0; i < DPL; ++i) pv[w8 * hd + d0 + i] = acc[i];
+                for (int i = 0; i < DPL; ++i) {
+                  float v = acc[c][i];
+                  if (lpk == 16) {
+                    v = swap_add32(v, v);
+                    v = swap_add16(v, v);
+                  } else {
+                    for (int o = lpk; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+                  }
+                  acc[c][i] = v;
+                }
+                if (c < ncol && lane < lpk) {
+#pragma unroll
+                  for (int i = 0; i < DPL; ++i) pvv[(c * MK_WAVES + w8) * hd + d0 + i] = acc[c][i];
+                }
               }
               lbar();
               const int plen = hd + 2;
-              uint2 *dst = xo + c * x_o_len + lg * plen;
-              for (int d = tid; d < hd; d += MK_THREADS) {
-                float a2 = pv[d];
+              for (int i = tid; i < ncol * hd; i += MK_THREADS) {
+                const int c = i / hd, d = i - c * hd;
+                const float *pc = pvv + c * MK_WAVES * hd;
+                float a2 = pc[d];
 #pragma unroll 1
-                for (int ww = 1; ww < MK_WAVES; ++ww) a2 += pv[ww * hd + d];
-                pub_xcd(dst + 2 + d, a2, tg);
+                for (int ww = 1; ww < MK_WAVES; ++ww) a2 += pc[ww * hd + d];
+                pub_xcd(xo + c * x_o_len + lg * plen + 2 + d, a2, tg);
               }
-              if (tid == 0) {
-                pub_xcd(dst + 0, nk > 0 ? mx[0] : -INFINITY, tg);
-                pub_xcd(dst + 1, nk > 0 ? mx[1] : 0.f, tg);
+              if (tid < ncol) {
+                const int c = tid, nk = nkc(c);
+                uint2 *dst = xo + c * x_o_len + lg * plen;
+                pub_xcd(dst + 0, nk > 0 ? mxv[2 * c] : -INFINITY, tg);
+                pub_xcd(dst + 1, nk > 0 ? mxv[2 * c + 1] : 0.f, tg);
               }
               lbar();
+            } else {
+#pragma unroll 1
+              for (int c = 0; c < ncol; ++c) {
+                // first position of this forward in column c's sequence: cached keys are below it
+                const int base = BAT ? bposl[c] : pos0;
+                const int P = BAT ? base : pos0 + c;  // query position; keys 0..P
+                // cached keys of this workgroup: slots [0, ncache)
+                const int ncache = (base > lg) ? (base - 1 - lg) / MK_NG + 1 : 0;
+                const int nstc = (ncache + spw - 1) / spw;
+                // (batch: column c's own cache, its sequence's K and V of this layer)
+                ConstLayer &cl = ((ConstLayer *)(uintptr_t)a.seq_layers[BAT ? c : 0])[li];
+                const __amdgpu_buffer_rsrc_t krs = BAT ? __builtin_amdgcn_make_buffer_rsrc(cl.kc, 0, 0x7fffffff, RSRC_W3) : krs0;
+                const __amdgpu_buffer_rsrc_t vrs = BAT ? __builtin_amdgcn_make_buffer_rsrc(cl.vc, 0, 0x7fffffff, RSRC_W3) : vrs0;
+                const int nk = (P >= lg) ? (P - lg) / MK_NG + 1 : 0;
+                // this forward's key of this workgroup, if any: position kc_ in [base, P], slot nk - 1
+                const int kc_ = lg + MK_NG * (nk - 1);
+                const bool hascur = nk > 0 && kc_ >= base;
+                const int crow = BAT ? c : kc_ - pos0;   // its row of this forward's K, V in LDS
+                float qv[DPL];
+  #pragma unroll
+                for (int i = 0; i < DPL; ++i) qv[i] = qkv[c * 3 * hd + d0 + i];
+                auto score = [&](int ks, const float (&kf)[DPL], float ksc) {
+                  float sdot = 0.f;
+  #pragma unroll
+                  for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kf[i], sdot);
+                  if constexpr (KVQ) sdot *= ksc;
+                  sdot = group_sum(sdot, lpk);
+                  if (ks < ncache && (lane % lpk) == 0) sc[ks] = sdot * scale;
+                };
+  #pragma unroll
+                for (int st = 0; st < NPRE; ++st) {
+                  if (st < nstc) {
+                    float kf[DPL];
+                    kv_unpack<DPL>(!BAT ? wr[2 * NRG_IN + NRG_O + 2 * st]
+                                   : st == 0 ? wsel(c, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{})
+                                             : wsel(c, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}), kf);
+                    score(st * spw + kslot, kf, KVQ ? q8_scale(kvx[st] & 0xffu) : 1.f);
+                  }
+                }
+                // later steps: KV_GRP steps' loads issued together, then used in step order
+  #pragma unroll 1
+                for (int st = NPRE; st < nstc; st += KV_GRP) {
+                  u32x4 kr[KV_GRP];
+                  uint32_t ke[KV_GRP];
+  #pragma unroll
+                  for (int u = 0; u < KV_GRP; ++u) {
+                    const int ks = (st + u) * spw + kslot;
+                    kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, ks < ncache ? row_off(ks) : OOB_OFF, 0, 0);
+                    if constexpr (KVQ) ke[u] = __builtin_amdgcn_raw_buffer_load_b8(ers, ks < ncache ? kve_off(ptl, lg + MK_NG * ks, kvh, nkv) : OOB_OFF, 0, 0);
+                    else ke[u] = 0;
+                  }
+  #pragma unroll
+                  for (int u = 0; u < KV_GRP; ++u) {
+                    if (st + u < nstc) {
+                      float kf[DPL];
+                      kv_unpack<DPL>(kr[u], kf);
+                      score((st + u) * spw + kslot, kf, KVQ ? q8_scale(ke[u]) : 1.f);
+                    }
+                  }
+                }
+                if (hascur && w8 == 0 && lane < lpk) {   // this forward's key: from LDS
+                  const float *kk = qkv + crow * 3 * hd + hd + d0;
+                  float sdot = 0.f;
+  #pragma unroll
+                  for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kk[i], sdot);
+                  if constexpr (KVQ) sdot *= kvs[crow * 2];
+                  sdot = group_sum(sdot, lpk);
+                  if (lane == 0) sc[nk - 1] = sdot * scale;
+                }
+                lbar();
+                if (w8 == 0) {
+                  float mv = -INFINITY;
+                  for (int i = lane; i < nk; i += 64) mv = fmaxf(mv, sc[i]);
+  #pragma unroll
+                  for (int off = 32; off > 0; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off, 64));
+                  float ls = 0.f;
+                  for (int i = lane; i < nk; i += 64) {
+                    const float pe = __expf(sc[i] - mv);
+                    sc[i] = pe;
+                    ls += pe;
+                  }
+                  ls = wave_sum(ls);
+                  if (lane == 0) { mx[0] = mv; mx[1] = ls; }
+                }
+                lbar();
+                // P.V over the same slots: each lane accumulates its 8 dimensions
+                float acc[DPL];
+  #pragma unroll
+                for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+                auto pvacc = [&](int ks, const float (&vf)[DPL], float vsc) {
+                  float pe = (ks < ncache) ? sc[ks < ncache ? ks : 0] : 0.f;
+                  if constexpr (KVQ) pe *= vsc;
+  #pragma unroll
+                  for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vf[i], acc[i]);
+                };
+  #pragma unroll
+                for (int st = 0; st < NPRE; ++st) {
+                  if (st < nstc) {
+                    float vf[DPL];
+                    kv_unpack<DPL>(!BAT ? wr[2 * NRG_IN + NRG_O + 2 * st + 1]
+                                   : st == 0 ? wsel(c, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{})
+                                             : wsel(c, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}), vf);
+                    pvacc(st * spw + kslot, vf, KVQ ? q8_scale(kvx[st] >> 8) : 1.f);
+                  }
+                }
+  #pragma unroll 1
+                for (int st = NPRE; st < nstc; st += KV_GRP) {
+                  u32x4 vr[KV_GRP];
+                  uint32_t ve[KV_GRP];
+  #pragma unroll
+                  for (int u = 0; u < KV_GRP; ++u) {
+                    const int ks = (st + u) * spw + kslot;
+                    vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ks < ncache ? row_off(ks) : OOB_OFF, 0, 0);
+                    if constexpr (KVQ) ve[u] = __builtin_amdgcn_raw_buffer_load_b8(ers, ks < ncache ? kve_off(ptl, lg + MK_NG * ks, kvh, nkv) + 1 : OOB_OFF, 0, 0);
+                    else ve[u] = 0;
+                  }
+  #pragma unroll
+                  for (int u = 0; u < KV_GRP; ++u) {
+                    if (st + u < nstc) {
+                      float vf[DPL];
+                      kv_unpack<DPL>(vr[u], vf);
+                      pvacc((st + u) * spw + kslot, vf, KVQ ? q8_scale(ve[u]) : 1.f);
+                    }
+                  }
+                }
+                // this forward's value, from LDS, added by the lanes that own its slot in the step order
+                // (as a cached key of a later decode step it is accumulated there: same additions, same
+                // order, so verify and sequential decode agree bit for bit)
+                const int kcs = (nk - 1) % spw;
+                if (hascur && w8 == kcs / kpw && lane / lpk == kcs % kpw) {
+                  float pe = sc[nk - 1];
+                  if constexpr (KVQ) pe *= kvs[crow * 2 + 1];
+                  const float *vv = qkv + crow * 3 * hd + 2 * hd + d0;
+  #pragma unroll
+                  for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vv[i], acc[i]);
+                }
+                // sum over the kpw key groups of the wave (lanes l, l + lpk, ...), then over the waves
+  #pragma unroll
+                for (int i = 0; i < DPL; ++i) {
+                  float v = acc[i];
+                  if (lpk == 16) {
+                    v = swap_add32(v, v);
+                    v = swap_add16(v, v);
+                  } else if (lpk == 8) {
+                    v = dpp_add<DPP_ROR8>(v);   // (l, l ^ 8) within each row of 16 lanes
+                    v = swap_add32(v, v);
+                    v = swap_add16(v, v);
+                  } else {
+                    for (int o = lpk; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+                  }
+                  acc[i] = v;
+                }
+                if (lane < lpk) {
+  #pragma unroll
+                  for (int i = 0; i < DPL; ++i) pv[w8 * hd + d0 + i] = acc[i];
+                }
+                lbar();
+                const int plen = hd + 2;
+                uint2 *dst = xo + c * x_o_len + lg * plen;
+                for (int d = tid; d < hd; d += MK_THREADS) {
+                  float a2 = pv[d];
+  #pragma unroll 1
+                  for (int ww = 1; ww < MK_WAVES; ++ww) a2 += pv[ww * hd + d];
+                  pub_xcd(dst + 2 + d, a2, tg);
+                }
+                if (tid == 0) {
+                  pub_xcd(dst + 0, nk > 0 ? mx[0] : -INFINITY, tg);
+                  pub_xcd(dst + 1, nk > 0 ? mx[1] : 0.f, tg);
+                }
+                lbar();
+              }
             }
           }
           MK_TRACE_POINT(li, 4);
