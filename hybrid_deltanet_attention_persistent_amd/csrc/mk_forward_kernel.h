@@ -1387,6 +1387,168 @@ if constexpr (NCOL > 1 && !BAT && !KVQ) {
                 pub_xcd(dst + 1, nk > 0 ? mxv[2 * c + 1] : 0.f, tg);
               }
               lbar();
+            } else if constexpr (BAT) {
+              // Batch: each column reads its own sequence's cache; the columns' scores, softmaxes and
+              // P.V partials are each one pass over the columns (four barriers per attention layer
+              // instead of four per column), each column with decode's arithmetic and order.
+              float *scv = sc;                                 // [NCOL][640]
+              float *pvv = scv + NCOL * 640;                   // [NCOL][MK_WAVES][hd]
+              float *mxv = pvv + NCOL * MK_WAVES * hd;         // [NCOL][2]
+              auto ncache_of = [&](int P) { return (P > lg) ? (P - 1 - lg) / MK_NG + 1 : 0; };
+              auto nk_of = [&](int P) { return (P >= lg) ? (P - lg) / MK_NG + 1 : 0; };
+#pragma unroll 1
+              for (int c = 0; c < ncol; ++c) {   // scores
+                const int P = bposl[c], ncache = ncache_of(P), nstc = (ncache + spw - 1) / spw, nk = nk_of(P);
+                const int kc_ = lg + MK_NG * (nk - 1);
+                ConstLayer &cl = ((ConstLayer *)(uintptr_t)a.seq_layers[c])[li];
+                const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(cl.kc, 0, 0x7fffffff, RSRC_W3);
+                float *scc = scv + c * 640;
+                float qv[DPL];
+#pragma unroll
+                for (int i = 0; i < DPL; ++i) qv[i] = qkv[c * 3 * hd + d0 + i];
+                auto score = [&](int ks, const float (&kf)[DPL]) {
+                  float sdot = 0.f;
+#pragma unroll
+                  for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kf[i], sdot);
+                  sdot = group_sum(sdot, lpk);
+                  if (ks < ncache && (lane % lpk) == 0) scc[ks] = sdot * scale;
+                };
+                if (nstc > 0) {
+                  float kf[DPL];
+                  kv_unpack<DPL>(wsel(c, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}), kf);
+                  score(kslot, kf);
+                }
+                if (nstc > 1) {
+                  float kf[DPL];
+                  kv_unpack<DPL>(wsel(c, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}), kf);
+                  score(spw + kslot, kf);
+                }
+#pragma unroll 1
+                for (int st = NPRE; st < nstc; st += KV_GRP) {
+                  u32x4 kr[KV_GRP];
+#pragma unroll
+                  for (int u = 0; u < KV_GRP; ++u) {
+                    const int ks = (st + u) * spw + kslot;
+                    kr[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, ks < ncache ? row_off(ks) : OOB_OFF, 0, 0);
+                  }
+#pragma unroll
+                  for (int u = 0; u < KV_GRP; ++u) {
+                    if (st + u < nstc) {
+                      float kf[DPL];
+                      kv_unpack<DPL>(kr[u], kf);
+                      score((st + u) * spw + kslot, kf);
+                    }
+                  }
+                }
+                if (nk > 0 && kc_ >= P && w8 == 0 && lane < lpk) {   // the column's own key: from LDS
+                  const float *kk = qkv + c * 3 * hd + hd + d0;
+                  float sdot = 0.f;
+#pragma unroll
+                  for (int i = 0; i < DPL; ++i) sdot = fmaf(qv[i], kk[i], sdot);
+                  sdot = group_sum(sdot, lpk);
+                  if (lane == 0) scc[nk - 1] = sdot * scale;
+                }
+              }
+              lbar();
+              if (w8 < ncol) {   // softmax of column w8
+                const int c = w8, nk = nk_of(bposl[c]);
+                float *scc = scv + c * 640;
+                float mv = -INFINITY;
+                for (int i = lane; i < nk; i += 64) mv = fmaxf(mv, scc[i]);
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off, 64));
+                float ls = 0.f;
+                for (int i = lane; i < nk; i += 64) {
+                  const float pe = __expf(scc[i] - mv);
+                  scc[i] = pe;
+                  ls += pe;
+                }
+                ls = wave_sum(ls);
+                if (lane == 0) { mxv[2 * c] = mv; mxv[2 * c + 1] = ls; }
+              }
+              lbar();
+#pragma unroll 1
+              for (int c = 0; c < ncol; ++c) {   // P.V
+                const int P = bposl[c], ncache = ncache_of(P), nstc = (ncache + spw - 1) / spw, nk = nk_of(P);
+                const int kc_ = lg + MK_NG * (nk - 1);
+                ConstLayer &cl = ((ConstLayer *)(uintptr_t)a.seq_layers[c])[li];
+                const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(cl.vc, 0, 0x7fffffff, RSRC_W3);
+                const float *scc = scv + c * 640;
+                float acc[DPL];
+#pragma unroll
+                for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+                auto pvacc = [&](int ks, const float (&vf)[DPL]) {
+                  const float pe = (ks < ncache) ? scc[ks < ncache ? ks : 0] : 0.f;
+#pragma unroll
+                  for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vf[i], acc[i]);
+                };
+                if (nstc > 0) {
+                  float vf[DPL];
+                  kv_unpack<DPL>(wsel(c, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}), vf);
+                  pvacc(kslot, vf);
+                }
+                if (nstc > 1) {
+                  float vf[DPL];
+                  kv_unpack<DPL>(wsel(c, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}), vf);
+                  pvacc(spw + kslot, vf);
+                }
+#pragma unroll 1
+                for (int st = NPRE; st < nstc; st += KV_GRP) {
+                  u32x4 vr[KV_GRP];
+#pragma unroll
+                  for (int u = 0; u < KV_GRP; ++u) {
+                    const int ks = (st + u) * spw + kslot;
+                    vr[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ks < ncache ? row_off(ks) : OOB_OFF, 0, 0);
+                  }
+#pragma unroll
+                  for (int u = 0; u < KV_GRP; ++u) {
+                    if (st + u < nstc) {
+                      float vf[DPL];
+                      kv_unpack<DPL>(vr[u], vf);
+                      pvacc((st + u) * spw + kslot, vf);
+                    }
+                  }
+                }
+                const int kcs = (nk - 1) % spw;
+                if (nk > 0 && kc_ >= P && w8 == kcs / kpw && lane / lpk == kcs % kpw) {   // own value, in step order
+                  const float pe = scc[nk - 1];
+                  const float *vv = qkv + c * 3 * hd + 2 * hd + d0;
+#pragma unroll
+                  for (int i = 0; i < DPL; ++i) acc[i] = fmaf(pe, vv[i], acc[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < DPL; ++i) {
+                  float v = acc[i];
+                  if (lpk == 16) {
+                    v = swap_add32(v, v);
+                    v = swap_add16(v, v);
+                  } else {
+                    for (int o = lpk; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+                  }
+                  acc[i] = v;
+                }
+                if (lane < lpk) {
+#pragma unroll
+                  for (int i = 0; i < DPL; ++i) pvv[(c * MK_WAVES + w8) * hd + d0 + i] = acc[i];
+                }
+              }
+              lbar();
+              const int plen = hd + 2;
+              for (int i = tid; i < ncol * hd; i += MK_THREADS) {
+                const int c = i / hd, d = i - c * hd;
+                const float *pc = pvv + c * MK_WAVES * hd;
+                float a2 = pc[d];
+#pragma unroll 1
+                for (int ww = 1; ww < MK_WAVES; ++ww) a2 += pc[ww * hd + d];
+                pub_xcd(xo + c * x_o_len + lg * plen + 2 + d, a2, tg);
+              }
+              if (tid < ncol) {
+                const int c = tid, nk = nk_of(bposl[c]);
+                uint2 *dst = xo + c * x_o_len + lg * plen;
+                pub_xcd(dst + 0, nk > 0 ? mxv[2 * c] : -INFINITY, tg);
+                pub_xcd(dst + 1, nk > 0 ? mxv[2 * c + 1] : 0.f, tg);
+              }
+              lbar();
             } else {
 #pragma unroll 1
               for (int c = 0; c < ncol; ++c) {
