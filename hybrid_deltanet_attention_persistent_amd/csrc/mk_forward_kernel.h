@@ -982,28 +982,35 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               if (J2 > 1) Srow[64 + lane] = srow[1];
             }
             float *pw = ly.pend + ((size_t)(par ^ 1) * nh + x) * MK_MAXCOL * mk_pend_stride(dv);
-            FOR_COL(c) {
-              if constexpr (BAT) {   // this column's sequence's row of S
-                srow[0] = sb[c][0];
-                srow[1] = sb[c][1];
-              }
+            // the readout o = S q of column c from its updated state row, and o's gated numerator
+            auto readout = [&](int c, float s0, float s1) {
               const float qr = rsqrtf(((rsq[c * 8 + 0] + rsq[c * 8 + 1]) + rsq[c * 8 + 2]) + rsq[c * 8 + 3] + m.l2_eps);
-              const float kr = rsqrtf(((rsq[c * 8 + 4] + rsq[c * 8 + 5]) + rsq[c * 8 + 6]) + rsq[c * 8 + 7] + m.l2_eps);
               const float *qc = qkc + c * 2 * dk;
               const float q0 = qc[lane] * qr, q1 = (J2 > 1) ? qc[64 + lane] * qr : 0.f;
-              const float k0 = qc[dk + lane] * kr, k1 = (J2 > 1) ? qc[dk + 64 + lane] * kr : 0.f;
-              const float vr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[c]), 63));
-              const float al = decay_f(gab[c * 2 + 0]), be = sigmoid_f(gab[c * 2 + 1]);
-              const float u = be * (vr - al * rowdot(k0, k1));
-              srow[0] = fmaf(u, k0, al * srow[0]);
-              if (J2 > 1) srow[1] = fmaf(u, k1, al * srow[1]);
-              const float o = rowdot(q0, q1);
+              float p = fmaf(s0, q0, 0.f);   // o = S_c . q (rowdot on the column's state row)
+              if (J2 > 1) p = fmaf(s1, q1, p);
+              const float o = wave_sum(p);
               // the gated norm's numerator o g silu(z); D3 divides by the RMS of the head's o
               const float uo = o * grow * silu_f(gz[c * RW + w8]);
               if (lane == 0) {
                 pub_xcd(xo + c * x_o_len + r0 + w8, o, tg);
                 pub_xcd(xo + c * x_o_len + dv + r0 + w8, uo, tg);
               }
+            };
+            FOR_COL(c) {
+              if constexpr (BAT) {   // this column's sequence's row of S
+                srow[0] = sb[c][0];
+                srow[1] = sb[c][1];
+              }
+              const float kr = rsqrtf(((rsq[c * 8 + 4] + rsq[c * 8 + 5]) + rsq[c * 8 + 6]) + rsq[c * 8 + 7] + m.l2_eps);
+              const float *qc = qkc + c * 2 * dk;
+              const float k0 = qc[dk + lane] * kr, k1 = (J2 > 1) ? qc[dk + 64 + lane] * kr : 0.f;
+              const float vr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[c]), 63));
+              const float al = decay_f(gab[c * 2 + 0]), be = sigmoid_f(gab[c * 2 + 1]);
+              const float u = be * (vr - al * rowdot(k0, k1));
+              srow[0] = fmaf(u, k0, al * srow[0]);
+              if (J2 > 1) srow[1] = fmaf(u, k1, al * srow[1]);
+              readout(c, srow[0], srow[1]);
               if (verify) {  // (k, v, alpha, beta) of this column become a pending update
                 float *pc = pw + c * mk_pend_stride(dv);
                 if (lg == 0 && w8 == 0) *reinterpret_cast<float4 *>(pc + 4 * lane) = make_float4(k0, k1, 0.f, 0.f);
