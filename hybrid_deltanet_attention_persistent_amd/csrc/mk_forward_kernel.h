@@ -982,16 +982,33 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
               if (J2 > 1) Srow[64 + lane] = srow[1];
             }
             float *pw = ly.pend + ((size_t)(par ^ 1) * nh + x) * MK_MAXCOL * mk_pend_stride(dv);
+            // several columns: lane c computes column c's norm scales of k and q, its gates and its
+            // SiLU(z) (the same operations on the same values as the column's own lanes would) into
+            // this wave's LDS table, so each column's chain below reads them in one LDS round trip
+            // (written and read by this wave only: no barrier; apart from D3's gather buffer)
+            float *csc = work + 4096 + w8 * (MK_MAXCOL * 8);   // [NCOL][8]: k scale, q scale, alpha, beta, SiLU(z)
+            if constexpr (NCOL > 1) {
+              if (lane < NCOL) {
+                const float *rc = rsq + lane * 8;
+                const float ka = rc[4], kb = rc[5], kc = rc[6], kd = rc[7], qa = rc[0], qb = rc[1], qc = rc[2], qd = rc[3];
+                const float ga = gab[lane * 2 + 0], gb = gab[lane * 2 + 1], zz = gz[lane * RW + w8];
+                *reinterpret_cast<float4 *>(csc + lane * 8) =
+                    make_float4(rsqrtf(((ka + kb) + kc) + kd + m.l2_eps), rsqrtf(((qa + qb) + qc) + qd + m.l2_eps), decay_f(ga),
+                                sigmoid_f(gb));
+                csc[lane * 8 + 4] = silu_f(zz);
+              }
+            }
             // the readout o = S q of column c from its updated state row, and o's gated numerator
             auto readout = [&](int c, float s0, float s1) {
-              const float qr = rsqrtf(((rsq[c * 8 + 0] + rsq[c * 8 + 1]) + rsq[c * 8 + 2]) + rsq[c * 8 + 3] + m.l2_eps);
+              const float qr = NCOL > 1 ? csc[c * 8 + 1]
+                                        : rsqrtf(((rsq[c * 8 + 0] + rsq[c * 8 + 1]) + rsq[c * 8 + 2]) + rsq[c * 8 + 3] + m.l2_eps);
               const float *qc = qkc + c * 2 * dk;
               const float q0 = qc[lane] * qr, q1 = (J2 > 1) ? qc[64 + lane] * qr : 0.f;
               float p = fmaf(s0, q0, 0.f);   // o = S_c . q (rowdot on the column's state row)
               if (J2 > 1) p = fmaf(s1, q1, p);
               const float o = wave_sum(p);
               // the gated norm's numerator o g silu(z); D3 divides by the RMS of the head's o
-              const float uo = o * grow * silu_f(gz[c * RW + w8]);
+              const float uo = o * grow * (NCOL > 1 ? csc[c * 8 + 4] : silu_f(gz[c * RW + w8]));
               if (lane == 0) {
                 pub_xcd(xo + c * x_o_len + r0 + w8, o, tg);
                 pub_xcd(xo + c * x_o_len + dv + r0 + w8, uo, tg);
@@ -1002,11 +1019,13 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
                 srow[0] = sb[c][0];
                 srow[1] = sb[c][1];
               }
-              const float kr = rsqrtf(((rsq[c * 8 + 4] + rsq[c * 8 + 5]) + rsq[c * 8 + 6]) + rsq[c * 8 + 7] + m.l2_eps);
+              const float kr = NCOL > 1 ? csc[c * 8 + 0]
+                                        : rsqrtf(((rsq[c * 8 + 4] + rsq[c * 8 + 5]) + rsq[c * 8 + 6]) + rsq[c * 8 + 7] + m.l2_eps);
               const float *qc = qkc + c * 2 * dk;
               const float k0 = qc[dk + lane] * kr, k1 = (J2 > 1) ? qc[dk + 64 + lane] * kr : 0.f;
               const float vr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cv[c]), 63));
-              const float al = decay_f(gab[c * 2 + 0]), be = sigmoid_f(gab[c * 2 + 1]);
+              const float al = NCOL > 1 ? csc[c * 8 + 2] : decay_f(gab[c * 2 + 0]);
+              const float be = NCOL > 1 ? csc[c * 8 + 3] : sigmoid_f(gab[c * 2 + 1]);
               const float u = be * (vr - al * rowdot(k0, k1));
               srow[0] = fmaf(u, k0, al * srow[0]);
               if (J2 > 1) srow[1] = fmaf(u, k1, al * srow[1]);
