@@ -9,5 +9,5 @@ model on the host: without the library every entry point raises ImportError.
 from .lib import (  # noqa: F401
     Model, MkError, load_library, mk_required_bytes, mk_load_weights, mk_reset_state, mk_prefill,
     mk_decode_step, mk_decode_step_static, mk_sync_status, mk_free, mk_lookup_draft, mk_generate_lookup,
-    mk_select_seq, mk_decode_batch, make_config, make_tensors, LIB_PATH, EXPORTED,
+    mk_select_seq, mk_decode_batch, mk_set_prefill_blocks, make_config, make_tensors, LIB_PATH, EXPORTED,
 )

@@ -22,7 +22,7 @@ extern "C" hipError_t mk_forward_occupancy(int ncol_template, int variant, int *
 extern "C" hipError_t mk_static_scratch(void **ptr);
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
                                          const int32_t *tokens, int n, int32_t *argmax, float *logits,
-                                         hipStream_t st);
+                                         hipStream_t st, hipStream_t side, hipEvent_t *ev, int max_blocks);
 
 static thread_local std::string g_err;
 
@@ -63,6 +63,11 @@ struct mk_model {
   std::vector<std::pair<size_t, size_t>> state_regions;
   int32_t pos_hi;  // the selected sequence's upper bound of the device position (exact unless a verify ran)
   uint32_t tag;    // next exchange tag
+  // prefill in two row blocks: the second block's kernels run on a side stream (created on first
+  // use, default priority), ordered against the caller's stream by events (n_layers + 2)
+  int pf_blocks = 2;
+  hipStream_t pf_side = nullptr;
+  std::vector<hipEvent_t> pf_ev;
 };
 
 // ------------------------------------------------------------------------------ layout
@@ -687,7 +692,22 @@ extern "C" int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens
   hipStream_t st = (hipStream_t)stream;
   int s = ensure_ctx(m, n_tokens, st);
   if (s != MK_OK) return s;
-  HIPCHECK(mk_prefill_enqueue(&m->dev, m->layers_host.data(), &m->pf, d_tokens, n_tokens, d_next_token, d_last_logits, st));
+  if (m->pf_blocks >= 2 && !m->pf_side) {
+    int cur = 0;
+    HIPCHECK(hipGetDevice(&cur));
+    HIPCHECK(hipSetDevice(m->device));
+    hipError_t e = hipStreamCreateWithFlags(&m->pf_side, hipStreamNonBlocking);
+    for (int i = 0; e == hipSuccess && i < m->dev.n_layers + 2; ++i) {
+      hipEvent_t ev;
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e == hipSuccess) m->pf_ev.push_back(ev);
+    }
+    (void)hipSetDevice(cur);
+    HIPCHECK(e);
+  }
+  const bool two = m->pf_blocks >= 2 && m->pf_side;
+  HIPCHECK(mk_prefill_enqueue(&m->dev, m->layers_host.data(), &m->pf, d_tokens, n_tokens, d_next_token, d_last_logits, st,
+                              two ? m->pf_side : nullptr, two ? m->pf_ev.data() : nullptr, m->pf_blocks));
   m->pos_hi += n_tokens;
   m->seq_verified[m->cur] = 0;   // the prefill applies any pending updates first
   return MK_OK;
@@ -765,7 +785,7 @@ extern "C" int mk_sync_status(mk_model *m, void *stream, int32_t *pos) {
     }
   }
   const int e = ctl[MK_CTL_ERR];
-  if (e & MK_DERR_XCD) return fail(MK_ELAUNCH, "workgroups were not placed round-robin over the XCDs");
+  if (e & MK_DERR_XCD) return fail(MK_ELAUNCH, "workgroups were not placed round-robin over the XCDs from one starting XCD");
   if (e & MK_DERR_HANG) {
     char buf[160];
     std::snprintf(buf, sizeof(buf), "a device-side wait timed out (step %d layer %d phase %d, block %d thread %d, tag seen %u wanted %u)",
@@ -908,8 +928,20 @@ extern "C" int mk_generate_lookup(mk_model *m, const int32_t *history, int32_t n
   return MK_OK;
 }
 
+extern "C" int mk_set_prefill_blocks(mk_model *m, int32_t max_blocks) {
+  if (!live(m)) return fail(MK_ESTATE, "model not loaded");
+  if (max_blocks != 1 && max_blocks != 2) return fail(MK_EINVAL, "max_blocks must be 1 or 2");
+  m->pf_blocks = max_blocks;
+  return MK_OK;
+}
+
 extern "C" void mk_free(mk_model *m) {
   if (!live(m)) return;
   m->magic = 0;
+  if (m->pf_side) {   // its work is ordered before later work on the caller's stream; let it drain
+    (void)hipStreamSynchronize(m->pf_side);
+    for (hipEvent_t e : m->pf_ev) (void)hipEventDestroy(e);
+    (void)hipStreamDestroy(m->pf_side);
+  }
   delete m;
 }

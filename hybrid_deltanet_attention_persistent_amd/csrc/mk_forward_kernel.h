@@ -511,7 +511,22 @@ template <int NCOL, int SH>
 __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   extern __shared__ float lds_raw[];
   const MkDev &m = a.m;
-  const int b = blockIdx.x, x = b & (MK_NX - 1), lw = b >> 3;
+  // Placement: the dispatcher puts workgroup blockIdx.x on XCD (blockIdx.x + r) mod 8, round-robin
+  // from a starting XCD r that work on other hardware queues moves (measured on the device: r = 0
+  // when only one queue has run kernels, other values after kernels on a second stream).  So the
+  // XCD is read from the hardware and the index inside the XCD is blockIdx.x / 8, which names each
+  // (XCD, index) pair once for any r and keeps which compute units take which role; b is the
+  // logical workgroup index used for every partition of the work.  The final gather checks that
+  // every workgroup saw the same r.
+  const int lw = (int)(blockIdx.x >> 3);
+  int x, rot;
+  {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    x = (int)(xcc & (MK_NX - 1));
+    rot = (x - (int)blockIdx.x) & (MK_NX - 1);
+  }
+  const int b = x + MK_NX * lw;
   // role of this workgroup: the first MK_NG workgroups of an XCD run the token mixer (DeltaNet
   // or attention) of every layer, the other MK_NG the FFN; lg is the index inside the role
   const bool mixer = lw < MK_NG;
@@ -560,12 +575,7 @@ __global__ void __launch_bounds__(MK_THREADS, 1) mk_forward(MkLaunch a) {
   for (int i = tid0; i < m.max_pages; i += MK_THREADS) ptl[i] = m.page_table[i];
   if (BAT && tid0 < NCOL)
     bposl[tid0] = tid0 < a.n ? __hip_atomic_load(a.seq_ctl[tid0] + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-  if (tid0 == 0) {
-    flag[0] = 0;
-    uint32_t xcc;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-    if ((int)(xcc & 7) != x) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_XCD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tid0 == 0) flag[0] = flag[1] = 0;
 
   const int ctl_pos = BAT ? 0 : __hip_atomic_load(m.ctl + MK_CTL_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int pend_n = BAT ? 0 : __hip_atomic_load(m.ctl + MK_CTL_PEND, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2015,7 +2025,7 @@ if constexpr (NCOL > 1 && !BAT && !KVQ) {
       __hip_atomic_store(rec, ((unsigned long long)(uint32_t)bi << 32) | __float_as_uint(bv), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       wait_stores();  // value and index land before the tag word
-      __hip_atomic_store(rec + 1, ((unsigned long long)(uint32_t)nn << 32) | tg, __ATOMIC_RELAXED,
+      __hip_atomic_store(rec + 1, ((unsigned long long)(uint32_t)(nn | rot << 8) << 32) | tg, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -2039,7 +2049,8 @@ if constexpr (NCOL > 1 && !BAT && !KVQ) {
       const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, 0, AUX_DEV);
       cv[i] = __uint_as_float(v.x);
       ci[i] = (int)v.y;
-      cn[i] = (int)v.w;
+      cn[i] = (int)(v.w & 0xffu);
+      if ((int)(v.w >> 8) != rot) flag[1] = 1;   // placement rotation of workgroup i % 256
     }
     lbar();
     if (flag[0]) MK_BAIL();
@@ -2083,6 +2094,7 @@ if constexpr (NCOL > 1 && !BAT && !KVQ) {
           if (c < ncol) a.argmax[c] = gsel[c];
         if (a.n_acc) a.n_acc[0] = nacc;
         if (anynan) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_NAN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (flag[1]) __hip_atomic_fetch_or(m.ctl + MK_CTL_ERR, MK_DERR_XCD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if constexpr (BAT) {   // every sequence of the batch advances by its one token
 #pragma unroll
           for (int c = 0; c < NCOL; ++c)

@@ -2,9 +2,10 @@
 // builds the arena and by the persistent kernels that read it.
 //
 // Work mapping of the persistent grid on MI355X: 256 workgroups, one per compute
-// unit, 512 threads (8 wave64) each.  Workgroup b runs on XCD b % 8 (the hardware
-// dispatches workgroups to the 8 XCDs round-robin; the kernel checks this at
-// start).  Each XCD ("group" x) owns one DeltaNet head / one query head and one
+// unit, 512 threads (8 wave64) each, so every XCD hosts exactly 32 of them.  The
+// dispatcher places them round-robin over the 8 XCDs from a starting XCD that can
+// differ between launches; a workgroup reads its XCD x from the hardware and is
+// workgroup x + 8 * (blockIdx.x / 8) of the grid's partition.  Each XCD ("group" x) owns one DeltaNet head / one query head and one
 // slice of the FFN intermediate dimension, so most hand-offs stay inside one XCD
 // and go through its L2; only the residual-stream reductions cross XCDs.  Inside an
 // XCD, workgroups b >> 3 < MK_NG run the token mixers and the others the FFNs.

@@ -453,6 +453,7 @@ struct PfPrep {
   float *qkv;                         // [nh][PT][3 dk]: q / |q|, k / |k|, v
   float *gb;                          // [nh][PT][2]: log alpha, beta
   int T;
+  int pofs;                           // position of row 0 = control-block position + pofs
 };
 constexpr int PREP_TB = 16;
 template <int DK>
@@ -462,7 +463,7 @@ __global__ void __launch_bounds__(3 * DK) pf_dn_prep(PfPrep c) {
   const int h = blockIdx.y, t0 = blockIdx.x * PREP_TB, ch = threadIdx.x, w = ch >> 6, lane = ch & 63;
   const int seg = ch / DK, i = ch - seg * DK;
   const int col = h * c.r_in + ch, cch = seg * c.nh * DK + h * DK + i;
-  const int p0 = c.ctl[MK_CTL_POS];
+  const int p0 = c.ctl[MK_CTL_POS] + c.pofs;
   const float4 wt = ld4(c.conv + cch * 4);
   float x[PREP_TB + 3];
 #pragma unroll
@@ -754,6 +755,9 @@ struct PfScan {
   const float *P;                  // [T][NP] in-projection outputs (conv inputs of the pass)
   int NP, r_in, C;
   float *ring;                     // [MK_RING][C] conv inputs by position, for the decode kernel
+  int pofs;                        // position of row 0 = control-block position + pofs
+  int replay;                      // 1: apply the pending updates of a verify forward first (the
+                                   // first row block of a pass; a later block finds them applied)
 };
 
 // Carry 16 rows of one head's state through every chunk of the pass.  Per chunk, with S the
@@ -783,7 +787,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) pf_dn_scan(PfScan s) {
   float *Sg = s.S + ((size_t)h * DK + r0) * DK;
   if (blockIdx.y == 0) {  // the head's conv inputs of the pass's last positions into the ring
     // (the conv of this pass has read the earlier positions it needs from it already)
-    const int n = min(s.T, MK_RING), p0 = s.ctl[MK_CTL_POS];
+    const int n = min(s.T, MK_RING), p0 = s.ctl[MK_CTL_POS] + s.pofs;
     for (int e = tid; e < n * 3 * DK; e += SCAN_THREADS) {
       const int t = s.T - n + e / (3 * DK), q = e % (3 * DK), seg = q / DK;
       s.ring[((p0 + t) & (MK_RING - 1)) * s.C + seg * s.nh * DK + h * DK + (q - seg * DK)] =
@@ -796,7 +800,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) pf_dn_scan(PfScan s) {
   }
   __syncthreads();
   // pending updates left by a verify forward (same arithmetic as the decode kernel's step)
-  const int pend_n = s.ctl[MK_CTL_PEND], par = s.ctl[MK_CTL_PAR];
+  const int pend_n = s.replay ? s.ctl[MK_CTL_PEND] : 0, par = s.ctl[MK_CTL_PAR];
   for (int jp = 0; jp < pend_n; ++jp) {
     const float *pk = s.pend + (((size_t)par * s.nh + h) * MK_MAXCOL + jp) * mk_pend_stride(DK);
     const float *pv = pk + MK_PEND_K;   // (v_r, alpha, beta, 0) per value row
@@ -1004,6 +1008,7 @@ struct PfAtt {
   float *aq;                  // [PT][nq hd]
   int nq, nkv, hd;
   uint16_t *oh, *ol;          // output, operand block layout with Kc = nq hd
+  int pofs;                   // position of row 0 = control-block position + pofs
 };
 
 __device__ __forceinline__ size_t kv_off(const PfAtt &a, int p, int kvh) {
@@ -1015,7 +1020,7 @@ __device__ __forceinline__ size_t kv_off(const PfAtt &a, int p, int kvh) {
 // (>= -126) that keeps |q| <= 127
 __global__ void __launch_bounds__(PF_THREADS) pf_att_rope(PfAtt a) {
   __shared__ float kv8[2 * MK_NX * 128];   // 8-bit cache: the rows to quantise [K|V][kv head][hd]
-  const int t = blockIdx.x, p = a.ctl[MK_CTL_POS] + t, half = a.hd / 2;
+  const int t = blockIdx.x, p = a.ctl[MK_CTL_POS] + a.pofs + t, half = a.hd / 2;
   const float *row = a.P + (size_t)t * a.NP;
   uint16_t *kc = static_cast<uint16_t *>(a.kc), *vc = static_cast<uint16_t *>(a.vc);
   for (int e = threadIdx.x; e < (a.nq + a.nkv) * half; e += PF_THREADS) {
@@ -1123,7 +1128,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_att_mfma(PfAtt a) {
   __shared__ int pages[10240 / MK_PAGE];  // the page table of every cached position (checked on the host)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hq = blockIdx.y, kvh = hq * a.nkv / a.nq;
-  const int p0 = a.ctl[MK_CTL_POS];
+  const int p0 = a.ctl[MK_CTL_POS] + a.pofs;
   const int t0 = blockIdx.x * 64, tw = t0 + w * 16;          // first query row of the workgroup / wave
   const int nq_wg = min(64, a.T - t0);
   const int last = p0 + t0 + nq_wg - 1;                      // largest query position of the workgroup
@@ -1440,10 +1445,121 @@ static hipError_t launch_gemm(int epi, PfGemm g, float *part, hipStream_t st, co
 static size_t chunk_prep_lds(int dk) { return (size_t)(3 * MK_CHUNK * (dk + 4) + 3 * MK_CHUNK * CS + 3 * 16 * 17 + 4 * MK_CHUNK) * 4; }
 static size_t scan_lds(int dk) { return (size_t)(16 * (dk + 4) + 16 * (MK_CHUNK + 4) + 4 * 64 * 4) * 4; }
 
+// One pass of a prompt is enqueued as row blocks: block b holds pass rows [r0, r0 + T) and its
+// kernels see pointers into the pass buffers offset to row r0 and positions offset by r0.  With
+// two blocks the second runs on a side stream one step behind the first: its layer l waits only
+// for the first block's state of layer l (after the delta-rule scan: the state S and the conv
+// inputs in the ring; after the KV append: the keys and values of the earlier rows), so the two
+// blocks' kernels overlap.  Every buffer of a pass is indexed by row (or by chunk, or in 16-row
+// operand blocks), so the blocks touch disjoint parts of it; r0 is a multiple of the delta-rule
+// chunk, which keeps the chunk boundaries, and with them every result, those of one block.
+struct PfBlk {
+  int r0, T;
+  bool first;   // the pass's first block (replays the pending updates of a verify forward)
+};
+enum { PF_NONE = 0, PF_RECORD = 1, PF_WAIT = 2 };
+
+static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkLayerDev *next, const MkPf *pf,
+                                const PfBlk &b, hipStream_t st, int sync, hipEvent_t ev) {
+  const int H = d->H, nh = d->nh, dk = d->dk, dv = d->dv, nq = d->nq, nkv = d->nkv, hd = d->hd, J = d->J, I = d->I;
+  const int r0 = b.r0, T = b.T;
+  const size_t rH = (size_t)r0 * H, rK = (size_t)r0 * pf->K1;
+  uint16_t *a1h = pf->a1h + rK, *a1l = pf->a1l + rK;   // operand blocks of width H, nh dv or nq hd (<= K1)
+  float *P = pf->P + (size_t)r0 * pf->NP, *X = pf->X + rH, *part = pf->part + rH;
+  // the norm after the mixer (FFN input) and after the FFN (next layer's input) run inside the
+  // split-K reductions of the projections that add into the residual stream
+  const PfNext n2{L.ln2, d->rms_eps, a1h, a1l};
+  const PfNext n1{next ? next->ln1 : nullptr, d->rms_eps, a1h, a1l};
+  PfGemm g{};
+  g.ah = a1h; g.al = a1l; g.M = T;
+  hipError_t e;
+  if (L.kind == 0) {
+    g.N = nh * d->r_in; g.K = H;
+    g.wb[0] = g.wb[1] = g.wb[2] = L.dn_in; g.wend[0] = g.wend[1] = g.wend[2] = g.N;
+    g.ks = H; g.kstride = 0;
+    g.c = P; g.ldc = pf->NP;
+    if ((e = launch_gemm(EPI_STORE, g, nullptr, st)) != hipSuccess) return e;
+    if (sync == PF_WAIT && (e = hipStreamWaitEvent(st, ev, 0)) != hipSuccess) return e;
+    const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
+    const size_t rc = (size_t)r0 * dk;   // chunk terms: (r0 / CHUNK) chunks of CHUNK x dk
+    float *qkv = pf->qkv + (size_t)r0 * 3 * dk, *gb = pf->gb + (size_t)r0 * 2;
+    // dk == dv in {64, 128} (checked when the model is loaded).  The conv reads the ring (conv
+    // inputs of earlier positions) before the scan overwrites it with this block's last ones.
+    PfPrep pp{P, pf->NP, d->r_in, d->C, nh, L.dn_conv, L.ring, d->ctl, d->l2_eps, qkv, gb, T, r0};
+    PfChunk ck{qkv, gb, pf->cW + rc, pf->cQ + rc, pf->cU + rc, pf->cO + rc, pf->cKt + rc, pf->cg + r0, pf->cd + r0, T};
+    PfScan sc{L.S, L.pend, d->ctl, pf->cW + rc, pf->cU + rc, pf->cKt + rc, pf->cg + r0, pf->cd + r0,
+              pf->snap + (size_t)(r0 / MK_CHUNK) * dv * dk, T, nh, P, pf->NP, d->r_in, d->C, L.ring, r0, b.first ? 1 : 0};
+    PfOut po{pf->cQ + rc, pf->cO + rc, pf->snap + (size_t)(r0 / MK_CHUNK) * dv * dk, P, pf->NP, d->r_in, L.dn_gnorm, nh,
+             d->rms_eps, a1h, a1l, T};
+    const dim3 gtok((T + PREP_TB - 1) / PREP_TB, nh);
+    if (dk == 128) {
+      hipLaunchKernelGGL(pf_dn_prep<128>, gtok, dim3(3 * 128), 0, st, pp);
+      hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(128), st, ck);
+      hipLaunchKernelGGL(pf_dn_scan<128>, dim3(nh, 128 / 16), dim3(SCAN_THREADS), scan_lds(128), st, sc);
+    } else {
+      hipLaunchKernelGGL(pf_dn_prep<64>, gtok, dim3(3 * 64), 0, st, pp);
+      hipLaunchKernelGGL(pf_dn_chunk_prep<64>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(64), st, ck);
+      hipLaunchKernelGGL(pf_dn_scan<64>, dim3(nh, 64 / 16), dim3(SCAN_THREADS), scan_lds(64), st, sc);
+    }
+    if (sync == PF_RECORD && (e = hipEventRecord(ev, st)) != hipSuccess) return e;
+    if (dk == 128) hipLaunchKernelGGL(pf_dn_out<128>, gtok, dim3(128 * 4), 0, st, po);
+    else hipLaunchKernelGGL(pf_dn_out<64>, gtok, dim3(64 * 4), 0, st, po);
+    PfGemm go{};
+    go.ah = a1h; go.al = a1l; go.M = T; go.N = H; go.K = nh * dv;
+    go.wb[0] = go.wb[1] = go.wb[2] = L.dn_out; go.wend[0] = go.wend[1] = go.wend[2] = H;
+    go.ks = dv; go.kstride = H * dv;
+    go.c = X; go.ldc = H;
+    if ((e = launch_gemm(EPI_RESID, go, part, st, &n2)) != hipSuccess) return e;
+  } else {
+    g.N = (nq + 2 * nkv) * hd; g.K = H;
+    g.wb[0] = L.at_q; g.wend[0] = nq * hd;
+    g.wb[1] = L.at_k; g.wend[1] = (nq + nkv) * hd;
+    g.wb[2] = L.at_v; g.wend[2] = g.N;
+    g.ks = H; g.kstride = 0;
+    g.c = P; g.ldc = pf->NP;
+    if ((e = launch_gemm(EPI_STORE, g, nullptr, st)) != hipSuccess) return e;
+    PfAtt at{};
+    at.P = P; at.NP = pf->NP; at.T = T; at.rope = d->rope; at.page_table = d->page_table; at.ctl = d->ctl;
+    at.kc = L.kc; at.vc = L.vc; at.kve = L.kve; at.kvq = d->kv_quant;
+    at.aq = pf->aq + (size_t)r0 * nq * hd; at.nq = nq; at.nkv = nkv; at.hd = hd;
+    at.oh = a1h; at.ol = a1l; at.pofs = r0;
+    hipLaunchKernelGGL(pf_att_rope, dim3(T), dim3(PF_THREADS), 0, st, at);
+    if (sync == PF_RECORD && (e = hipEventRecord(ev, st)) != hipSuccess) return e;
+    if (sync == PF_WAIT && (e = hipStreamWaitEvent(st, ev, 0)) != hipSuccess) return e;
+    const dim3 ga((T + 63) / 64, nq);
+    if (hd == 128 && !at.kvq) hipLaunchKernelGGL((pf_att_mfma<128, false>), ga, dim3(PF_THREADS), 0, st, at);
+    else if (hd == 128) hipLaunchKernelGGL((pf_att_mfma<128, true>), ga, dim3(PF_THREADS), 0, st, at);
+    else if (hd == 64 && !at.kvq) hipLaunchKernelGGL((pf_att_mfma<64, false>), ga, dim3(PF_THREADS), 0, st, at);
+    else if (hd == 64) hipLaunchKernelGGL((pf_att_mfma<64, true>), ga, dim3(PF_THREADS), 0, st, at);
+    else return hipErrorInvalidValue;   // head_dim is 64 or 128 (checked at load)
+    PfGemm go{};
+    go.ah = a1h; go.al = a1l; go.M = T; go.N = H; go.K = nq * hd;
+    go.wb[0] = go.wb[1] = go.wb[2] = L.at_o; go.wend[0] = go.wend[1] = go.wend[2] = H;
+    go.ks = hd; go.kstride = H * hd;
+    go.c = X; go.ldc = H;
+    if ((e = launch_gemm(EPI_RESID, go, part, st, &n2)) != hipSuccess) return e;
+  }
+  PfGemm gu{};
+  gu.ah = a1h; gu.al = a1l; gu.M = T; gu.N = 2 * I; gu.K = H;
+  gu.wb[0] = gu.wb[1] = gu.wb[2] = L.ffn_gu; gu.wend[0] = gu.wend[1] = gu.wend[2] = 2 * I;
+  gu.ks = H; gu.kstride = 0;
+  gu.oh = pf->a2h + (size_t)r0 * I; gu.ol = pf->a2l + (size_t)r0 * I; gu.ldo = I;
+  if ((e = launch_gemm(EPI_SWIGLU, gu, nullptr, st)) != hipSuccess) return e;
+  PfGemm gd{};
+  gd.ah = gu.oh; gd.al = gu.ol; gd.M = T; gd.N = H; gd.K = I;
+  gd.wb[0] = gd.wb[1] = gd.wb[2] = L.ffn_dn; gd.wend[0] = gd.wend[1] = gd.wend[2] = H;
+  gd.ks = J; gd.kstride = H * J;
+  gd.c = X; gd.ldc = H;
+  return launch_gemm(EPI_RESID, gd, part, st, n1.g ? &n1 : nullptr);
+}
+
 // Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table.
+// side / ev (nullable): a second stream and d->n_layers + 2 events for the two-block form; a
+// pass of fewer than PF_SPLIT_MIN rows, or max_blocks 1, runs as one block on st.
+constexpr int PF_SPLIT_MIN = 256;
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
                                          const int32_t *tokens, int n, int32_t *argmax, float *logits,
-                                         hipStream_t st) {
+                                         hipStream_t st, hipStream_t side, hipEvent_t *ev, int max_blocks) {
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e;
@@ -1453,95 +1569,41 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
     if ((e = hipFuncSetAttribute((const void *)pf_dn_scan<128>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_lds(128))) != hipSuccess) return e;
     attr_done = true;
   }
-  const int H = d->H, nh = d->nh, dk = d->dk, dv = d->dv, nq = d->nq, nkv = d->nkv, hd = d->hd, J = d->J, I = d->I;
+  const int H = d->H, NL = d->n_layers;
   for (int s0 = 0; s0 < n; s0 += MK_PT) {
     const int T = n - s0 < MK_PT ? n - s0 : MK_PT;
     const bool last = s0 + T == n;
-    hipLaunchKernelGGL(pf_embed, dim3(T), dim3(PF_THREADS), 0, st, d->embed, tokens + s0, H, d->V, pf->X, d->ctl);
-    hipLaunchKernelGGL(pf_norm_split, dim3(T), dim3(PF_THREADS), 0, st, (const float *)pf->X, layers_host[0].ln1, H,
-                       d->rms_eps, pf->a1h, pf->a1l);
-    for (int li = 0; li < d->n_layers; ++li) {
-      const MkLayerDev &L = layers_host[li];
-      // the norm after the mixer (FFN input) and after the FFN (next layer's input) run inside
-      // the split-K reductions of the projections that add into the residual stream
-      const PfNext n2{L.ln2, d->rms_eps, pf->a1h, pf->a1l};
-      const PfNext n1{li + 1 < d->n_layers ? layers_host[li + 1].ln1 : nullptr, d->rms_eps, pf->a1h, pf->a1l};
-      PfGemm g{};
-      g.ah = pf->a1h; g.al = pf->a1l; g.M = T;
-      if (L.kind == 0) {
-        g.N = nh * d->r_in; g.K = H;
-        g.wb[0] = g.wb[1] = g.wb[2] = L.dn_in; g.wend[0] = g.wend[1] = g.wend[2] = g.N;
-        g.ks = H; g.kstride = 0;
-        g.c = pf->P; g.ldc = pf->NP;
-        hipError_t e = launch_gemm(EPI_STORE, g, nullptr, st);
-        if (e != hipSuccess) return e;
-        const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
-        // dk == dv in {64, 128} (checked when the model is loaded).  The conv reads the ring (conv
-        // inputs of earlier positions) before the scan overwrites it with this pass's last ones.
-        PfPrep pp{pf->P, pf->NP, d->r_in, d->C, nh, L.dn_conv, L.ring, d->ctl, d->l2_eps, pf->qkv, pf->gb, T};
-        PfChunk ck{pf->qkv, pf->gb, pf->cW, pf->cQ, pf->cU, pf->cO, pf->cKt, pf->cg, pf->cd, T};
-        PfScan sc{L.S, L.pend, d->ctl, pf->cW, pf->cU, pf->cKt, pf->cg, pf->cd, pf->snap, T, nh,
-                  pf->P, pf->NP, d->r_in, d->C, L.ring};
-        PfOut po{pf->cQ, pf->cO, pf->snap, pf->P, pf->NP, d->r_in, L.dn_gnorm, nh, d->rms_eps, pf->a1h, pf->a1l, T};
-        const dim3 gtok((T + PREP_TB - 1) / PREP_TB, nh);
-        if (dk == 128) {
-          hipLaunchKernelGGL(pf_dn_prep<128>, gtok, dim3(3 * 128), 0, st, pp);
-          hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(128), st, ck);
-          hipLaunchKernelGGL(pf_dn_scan<128>, dim3(nh, 128 / 16), dim3(SCAN_THREADS), scan_lds(128), st, sc);
-          hipLaunchKernelGGL(pf_dn_out<128>, gtok, dim3(128 * 4), 0, st, po);
-        } else {
-          hipLaunchKernelGGL(pf_dn_prep<64>, gtok, dim3(3 * 64), 0, st, pp);
-          hipLaunchKernelGGL(pf_dn_chunk_prep<64>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(64), st, ck);
-          hipLaunchKernelGGL(pf_dn_scan<64>, dim3(nh, 64 / 16), dim3(SCAN_THREADS), scan_lds(64), st, sc);
-          hipLaunchKernelGGL(pf_dn_out<64>, gtok, dim3(64 * 4), 0, st, po);
-        }
-        PfGemm go{};
-        go.ah = pf->a1h; go.al = pf->a1l; go.M = T; go.N = H; go.K = nh * dv;
-        go.wb[0] = go.wb[1] = go.wb[2] = L.dn_out; go.wend[0] = go.wend[1] = go.wend[2] = H;
-        go.ks = dv; go.kstride = H * dv;
-        go.c = pf->X; go.ldc = H;
-        if ((e = launch_gemm(EPI_RESID, go, pf->part, st, &n2)) != hipSuccess) return e;
-      } else {
-        g.N = (nq + 2 * nkv) * hd; g.K = H;
-        g.wb[0] = L.at_q; g.wend[0] = nq * hd;
-        g.wb[1] = L.at_k; g.wend[1] = (nq + nkv) * hd;
-        g.wb[2] = L.at_v; g.wend[2] = g.N;
-        g.ks = H; g.kstride = 0;
-        g.c = pf->P; g.ldc = pf->NP;
-        hipError_t e = launch_gemm(EPI_STORE, g, nullptr, st);
-        if (e != hipSuccess) return e;
-        PfAtt at{};
-        at.P = pf->P; at.NP = pf->NP; at.T = T; at.rope = d->rope; at.page_table = d->page_table; at.ctl = d->ctl;
-        at.kc = L.kc; at.vc = L.vc; at.kve = L.kve; at.kvq = d->kv_quant;
-        at.aq = pf->aq; at.nq = nq; at.nkv = nkv; at.hd = hd;
-        at.oh = pf->a1h; at.ol = pf->a1l;
-        hipLaunchKernelGGL(pf_att_rope, dim3(T), dim3(PF_THREADS), 0, st, at);
-        const dim3 ga((T + 63) / 64, nq);
-        if (hd == 128 && !at.kvq) hipLaunchKernelGGL((pf_att_mfma<128, false>), ga, dim3(PF_THREADS), 0, st, at);
-        else if (hd == 128) hipLaunchKernelGGL((pf_att_mfma<128, true>), ga, dim3(PF_THREADS), 0, st, at);
-        else if (hd == 64 && !at.kvq) hipLaunchKernelGGL((pf_att_mfma<64, false>), ga, dim3(PF_THREADS), 0, st, at);
-        else if (hd == 64) hipLaunchKernelGGL((pf_att_mfma<64, true>), ga, dim3(PF_THREADS), 0, st, at);
-        else return hipErrorInvalidValue;   // head_dim is 64 or 128 (checked at load)
-        PfGemm go{};
-        go.ah = pf->a1h; go.al = pf->a1l; go.M = T; go.N = H; go.K = nq * hd;
-        go.wb[0] = go.wb[1] = go.wb[2] = L.at_o; go.wend[0] = go.wend[1] = go.wend[2] = H;
-        go.ks = hd; go.kstride = H * hd;
-        go.c = pf->X; go.ldc = H;
-        if ((e = launch_gemm(EPI_RESID, go, pf->part, st, &n2)) != hipSuccess) return e;
+    const bool two = side && ev && max_blocks >= 2 && T >= PF_SPLIT_MIN;
+    // split at a chunk boundary near the middle (both blocks >= 128 rows)
+    const int r1 = two ? (T / 2) / MK_CHUNK * MK_CHUNK : T;
+    PfBlk blk[2] = {{0, r1, true}, {r1, T - r1, false}};
+    const int nb = two ? 2 : 1;
+    hipError_t e;
+    if (two) {   // the side stream starts after everything enqueued on st before this pass
+      if ((e = hipEventRecord(ev[NL], st)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(side, ev[NL], 0)) != hipSuccess) return e;
+    }
+    for (int bi = 0; bi < nb; ++bi) {
+      const PfBlk &b = blk[bi];
+      hipStream_t sb = bi ? side : st;
+      hipLaunchKernelGGL(pf_embed, dim3(b.T), dim3(PF_THREADS), 0, sb, d->embed, tokens + s0 + b.r0, H, d->V,
+                         pf->X + (size_t)b.r0 * H, d->ctl);
+      hipLaunchKernelGGL(pf_norm_split, dim3(b.T), dim3(PF_THREADS), 0, sb, (const float *)pf->X + (size_t)b.r0 * H,
+                         layers_host[0].ln1, H, d->rms_eps, pf->a1h + (size_t)b.r0 * pf->K1,
+                         pf->a1l + (size_t)b.r0 * pf->K1);
+    }
+    for (int li = 0; li < NL; ++li) {
+      const MkLayerDev *next = li + 1 < NL ? &layers_host[li + 1] : nullptr;
+      for (int bi = 0; bi < nb; ++bi) {
+        const int sync = !two ? PF_NONE : bi == 0 ? PF_RECORD : PF_WAIT;
+        if ((e = enqueue_layer(d, layers_host[li], next, pf, blk[bi], bi ? side : st, sync,
+                               two ? ev[li] : nullptr)) != hipSuccess)
+          return e;
       }
-      PfGemm gu{};
-      gu.ah = pf->a1h; gu.al = pf->a1l; gu.M = T; gu.N = 2 * I; gu.K = H;
-      gu.wb[0] = gu.wb[1] = gu.wb[2] = L.ffn_gu; gu.wend[0] = gu.wend[1] = gu.wend[2] = 2 * I;
-      gu.ks = H; gu.kstride = 0;
-      gu.oh = pf->a2h; gu.ol = pf->a2l; gu.ldo = I;
-      hipError_t e = launch_gemm(EPI_SWIGLU, gu, nullptr, st);
-      if (e != hipSuccess) return e;
-      PfGemm gd{};
-      gd.ah = pf->a2h; gd.al = pf->a2l; gd.M = T; gd.N = H; gd.K = I;
-      gd.wb[0] = gd.wb[1] = gd.wb[2] = L.ffn_dn; gd.wend[0] = gd.wend[1] = gd.wend[2] = H;
-      gd.ks = J; gd.kstride = H * J;
-      gd.c = pf->X; gd.ldc = H;
-      if ((e = launch_gemm(EPI_RESID, gd, pf->part, st, n1.g ? &n1 : nullptr)) != hipSuccess) return e;
+    }
+    if (two) {   // st continues after the side stream's last layer
+      if ((e = hipEventRecord(ev[NL + 1], side)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(st, ev[NL + 1], 0)) != hipSuccess) return e;
     }
     if (last) {
       hipLaunchKernelGGL(pf_lm, dim3(MK_NWG), dim3(PF_THREADS), 0, st, (const float *)pf->X, T - 1, d->lnf, d->rms_eps,
@@ -1552,8 +1614,7 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
       hipLaunchKernelGGL(pf_finish, dim3(1), dim3(64), 0, st, (const unsigned long long *)pf->lmbest, 0,
                          (int32_t *)nullptr, d->ctl, T);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }

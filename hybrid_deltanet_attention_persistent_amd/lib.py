@@ -25,7 +25,7 @@ MK_DTYPE_BF16, MK_DTYPE_F16, MK_DTYPE_F32 = 1, 2, 3
 
 EXPORTED = ["mk_required_bytes", "mk_load_weights", "mk_reset_state", "mk_prefill", "mk_decode_step",
             "mk_decode_step_static", "mk_sync_status", "mk_free", "mk_status_string", "mk_last_error",
-            "mk_lookup_draft", "mk_generate_lookup", "mk_select_seq", "mk_decode_batch"]
+            "mk_lookup_draft", "mk_generate_lookup", "mk_select_seq", "mk_decode_batch", "mk_set_prefill_blocks"]
 MK_STATIC_SCRATCH_BYTES = 16 << 20
 
 
@@ -80,6 +80,7 @@ def load_library() -> ctypes.CDLL:
     lib.mk_generate_lookup.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, ctypes.POINTER(MkLookupStats), vp]
     lib.mk_select_seq.argtypes = [vp, i32]
     lib.mk_decode_batch.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.mk_set_prefill_blocks.argtypes = [vp, i32]
     lib.mk_free.argtypes = [vp]
     lib.mk_free.restype = None
     lib.mk_status_string.argtypes = [ctypes.c_int]
@@ -88,7 +89,7 @@ def load_library() -> ctypes.CDLL:
     lib.mk_last_error.restype = ctypes.c_char_p
     for f in ("mk_required_bytes", "mk_load_weights", "mk_reset_state", "mk_prefill", "mk_decode_step",
               "mk_decode_step_static", "mk_sync_status", "mk_lookup_draft", "mk_generate_lookup", "mk_select_seq",
-              "mk_decode_batch"):
+              "mk_decode_batch", "mk_set_prefill_blocks"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -173,6 +174,10 @@ def mk_prefill(handle: int, tokens, next_token, last_logits=None, stream=None) -
                                      _ptr(last_logits), _stream(stream)), "mk_prefill")
 
 
+def mk_set_prefill_blocks(handle: int, max_blocks: int) -> None:
+    _check(load_library().mk_set_prefill_blocks(handle, int(max_blocks)), "mk_set_prefill_blocks")
+
+
 def mk_decode_step(handle: int, tokens, n_tokens: int, argmax, logits=None, n_accepted=None, stream=None) -> None:
     _check(load_library().mk_decode_step(handle, _ptr(tokens), int(n_tokens), _ptr(argmax), _ptr(logits),
                                          _ptr(n_accepted), _stream(stream)), "mk_decode_step")
@@ -248,6 +253,9 @@ class Model:
 
     def prefill(self, tokens, next_token, last_logits=None):
         mk_prefill(self.handle, tokens, next_token, last_logits)
+
+    def set_prefill_blocks(self, max_blocks: int):
+        mk_set_prefill_blocks(self.handle, max_blocks)
 
     def decode_step(self, tokens, argmax, logits=None, n_accepted=None, n_tokens: Optional[int] = None):
         mk_decode_step(self.handle, tokens, int(tokens.numel() if n_tokens is None else n_tokens), argmax, logits,

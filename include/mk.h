@@ -141,6 +141,18 @@ int mk_reset_state(mk_model *m, void *stream);
 int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens, int32_t *d_next_token,
                float *d_last_logits, void *stream);
 
+/* Row blocks of a prefill pass (launch page "OS Megakernel that match M5 Max Tok/w at 2x the
+ * Throughput on RTX 3090": one prompt, every layer, no host round trip).  max_blocks 2 (the
+ * default): a pass of at least 256 tokens is split at a 64-token boundary near its middle and
+ * the second block's kernels run on a side stream of the model (created on the first prefill,
+ * default priority, destroyed by mk_free), one step behind the first block: its layer waits only
+ * for the first block's state of that layer (delta-rule state and conv history, or keys and
+ * values), so the two blocks' kernels overlap.  The side stream starts after everything enqueued
+ * on `stream` before the call, and `stream` continues only after the side stream's last kernel,
+ * so ordering for the caller is that of one stream.  Results are bit-identical to max_blocks 1
+ * (one block on `stream`).  Returns MK_EINVAL for other values, MK_ESTATE for a freed model.  */
+int mk_set_prefill_blocks(mk_model *m, int32_t max_blocks);
+
 /* Decode step (n_tokens == 1) or verify forward (2 <= n_tokens <= max_verify), one
  * launch.  d_tokens[0] is the last accepted token; for verify d_tokens[1..] are
  * draft tokens.  Writes the greedy token after each position to d_argmax[0..n)

@@ -181,6 +181,7 @@ def test_calls_on_unloaded_model_are_rejected(so):
     assert so.mk_decode_step_static(None, buf, 1, buf, None, None, None) == L.MK_ESTATE
     assert so.mk_reset_state(None, None) == L.MK_ESTATE
     assert so.mk_select_seq(None, 0) == L.MK_ESTATE
+    assert so.mk_set_prefill_blocks(None, 2) == L.MK_ESTATE
     seqs = (ctypes.c_int32 * 2)(0, 1)
     assert so.mk_decode_batch(None, seqs, 2, buf, buf, None, None) == L.MK_ESTATE
     pos = ctypes.c_int32(0)
