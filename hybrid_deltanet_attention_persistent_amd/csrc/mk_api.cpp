@@ -22,7 +22,8 @@ extern "C" hipError_t mk_forward_occupancy(int ncol_template, int variant, int *
 extern "C" hipError_t mk_static_scratch(void **ptr);
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
                                          const int32_t *tokens, int n, int32_t *argmax, float *logits,
-                                         hipStream_t st, hipStream_t side, hipEvent_t *ev, int max_blocks);
+                                         hipStream_t st, hipStream_t side, hipEvent_t *ev, int max_blocks,
+                                         const MkPfW *pfw);
 
 static thread_local std::string g_err;
 
@@ -54,6 +55,7 @@ struct mk_model {
   std::vector<int32_t> seq_pos_hi;      // per sequence: upper bound of its device position
   std::vector<uint8_t> seq_verified;    // per sequence: its last forward was a verify (updates may be pending)
   MkPf pf;                              // prefill scratch
+  std::vector<MkPfW> pfw;               // per layer: prefill copies of the projection weights
   char *arena;
   size_t arena_bytes;
   uint2 *xch;                           // exchange slots of mk_decode_step (in the arena)
@@ -88,11 +90,14 @@ struct Layout {
   }
 };
 
+size_t blk_bytes(int N, int K) { return (size_t)((N + 15) / 16 * 16) * K * 2; }
+
 struct LayerRegions {
   Region ln1, ln2;
   Region dn_in, dn_conv, dn_gnorm, dn_out, S, ring, pend;
   Region at_q, at_k, at_v, at_o, kc, vc, kve;
   Region ffn_gu, ffn_dn;
+  Region pf_in, pf_out, pf_qkv, pf_o, pf_gu, pf_dn;   // prefill copies (MkPfW)
 };
 
 // The state of sequences 1 .. n_seq - 1 (sequence 0's lives in LayerRegions)
@@ -204,7 +209,11 @@ Plan make_plan(const mk_config *c) {
       r.S = L.add((size_t)p.nh * p.dv * p.dk * 4);
       r.ring = L.add((size_t)MK_RING * p.C * 4);
       r.pend = L.add((size_t)2 * p.nh * MK_MAXCOL * mk_pend_stride(p.dv) * 4);
+      r.pf_in = L.add(blk_bytes(p.nh * p.r_in, p.H));
+      r.pf_out = L.add(blk_bytes(p.H, p.nh * p.dv));
     } else {
+      r.pf_qkv = L.add(blk_bytes((p.nq + 2 * p.nkv) * p.hd, p.H));
+      r.pf_o = L.add(blk_bytes(p.H, p.nq * p.hd));
       r.at_q = L.add((size_t)p.nq * p.hd * H * 2);
       r.at_k = L.add((size_t)p.nkv * p.hd * H * 2);
       r.at_v = L.add((size_t)p.nkv * p.hd * H * 2);
@@ -216,6 +225,8 @@ Plan make_plan(const mk_config *c) {
     }
     r.ffn_gu = L.add((size_t)2 * p.I * H * 2);
     r.ffn_dn = L.add((size_t)H * p.I * 2);
+    r.pf_gu = L.add(blk_bytes(2 * p.I, p.H));
+    r.pf_dn = L.add(blk_bytes(p.H, p.I));
   }
   // sequences 1 .. n_seq - 1: control block, layer table, and per layer the state / KV regions
   p.n_seq = c->n_seq > 0 ? c->n_seq : 1;
@@ -318,6 +329,24 @@ void tile_pack(const uint16_t *src, int rows, int K, size_t src_stride, uint16_t
         const int row = rg * RG + l / G, chunk = i * G + (l % G);
         std::memcpy(dst + (((size_t)rg * L + i) * 64 + l) * 8, src + (size_t)row * src_stride + (size_t)chunk * 8, 16);
       }
+}
+
+// Pack rows [N][K] (row stride src_stride elements) into the GEMM operand block layout of the
+// prefill weight copies: 1 KiB blocks of 16 rows x 32 k, block (n / 16, k / 32) at element
+// ((n / 16) * (K / 32) + k / 32) * 512; inside a block, row r's 8-element group q sits at 16-byte
+// slot 4 r + (q ^ ((r >> 1) & 3)) (the layout in which the GEMM's fragment reads are conflict-free).
+// Rows past N are zero.
+void blk_pack(const uint16_t *src, int N, int K, size_t src_stride, uint16_t *dst) {
+  const int kbn = K / 32, nbn = (N + 15) / 16;
+  for (int nb = 0; nb < nbn; ++nb)
+    for (int kb = 0; kb < kbn; ++kb)
+      for (int r = 0; r < 16; ++r)
+        for (int q = 0; q < 4; ++q) {
+          const int row = nb * 16 + r, slot = 4 * r + (q ^ ((r >> 1) & 3));
+          uint16_t *d = dst + (((size_t)nb * kbn + kb) * 64 + slot) * 8;
+          if (row < N) std::memcpy(d, src + (size_t)row * src_stride + (size_t)kb * 32 + q * 8, 16);
+          else std::memset(d, 0, 16);
+        }
 }
 
 inline float bf2f(uint16_t b) {
@@ -488,7 +517,14 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   }
 
   std::vector<MkLayerDev> lt(cfg->n_layers);
+  std::vector<MkPfW> pfw(cfg->n_layers);
   std::vector<std::pair<size_t, size_t>> state;
+  // a prefill weight copy: rows [N][K] packed into the GEMM block layout and uploaded
+  auto put_blk = [&](const Region &r, const uint16_t *src, int N, int K, size_t src_stride) -> hipError_t {
+    stage.assign(r.bytes / 2, 0);
+    blk_pack(src, N, K, src_stride, stage.data());
+    return put(r, stage.data());
+  };
   int nd = 0, na = 0;
   for (int li = 0; li < cfg->n_layers; ++li) {
     const LayerRegions &r = p.layers[li];
@@ -504,7 +540,7 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
     if (L.kind == 0) {
       const int nh = p.nh, dk = p.dk, dv = p.dv;
       stage.assign(r.dn_in.bytes / 2, 0);
-      std::vector<uint16_t> rows((size_t)p.r_in * H);
+      std::vector<uint16_t> rows((size_t)p.r_in * H), all((size_t)nh * p.r_in * H);
       for (int h = 0; h < nh; ++h) {
         size_t o = 0;
         auto take = [&](const uint16_t *src, int r0, int nr) {
@@ -518,8 +554,13 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
         take(T(pre + "dn.wa"), h, 1);
         take(T(pre + "dn.wb"), h, 1);
         tile_pack(rows.data(), p.r_in, p.H, H, stage.data() + (size_t)h * p.r_in * H);
+        std::memcpy(all.data() + (size_t)h * p.r_in * H, rows.data(), rows.size() * 2);
       }
       HIPCHECK(put(r.dn_in, stage.data()));
+      HIPCHECK(put_blk(r.pf_in, all.data(), nh * p.r_in, p.H, H));
+      HIPCHECK(put_blk(r.pf_out, T(pre + "dn.wo"), p.H, nh * dv, (size_t)nh * dv));
+      pfw[li].in = (const uint16_t *)(A + r.pf_in.off);
+      pfw[li].out = (const uint16_t *)(A + r.pf_out.off);
       { auto g = gains(T(pre + "dn.conv"), (size_t)p.C * 4); HIPCHECK(put(r.dn_conv, g.data())); }
       { auto g = gains(T(pre + "dn.gnorm"), dv); HIPCHECK(put(r.dn_gnorm, g.data())); }
       stage.assign(r.dn_out.bytes / 2, 0);
@@ -550,6 +591,16 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
       stage.assign(r.at_o.bytes / 2, 0);
       for (int i = 0; i < nq; ++i) tile_pack(T(pre + "attn.wo") + (size_t)i * hd, p.H, hd, (size_t)nq * hd, stage.data() + (size_t)i * H * hd);
       HIPCHECK(put(r.at_o, stage.data()));
+      {
+        std::vector<uint16_t> qkv((size_t)(nq + 2 * nkv) * hd * H);
+        std::memcpy(qkv.data(), T(pre + "attn.wq"), (size_t)nq * hd * H * 2);
+        std::memcpy(qkv.data() + (size_t)nq * hd * H, T(pre + "attn.wk"), (size_t)nkv * hd * H * 2);
+        std::memcpy(qkv.data() + (size_t)(nq + nkv) * hd * H, T(pre + "attn.wv"), (size_t)nkv * hd * H * 2);
+        HIPCHECK(put_blk(r.pf_qkv, qkv.data(), (nq + 2 * nkv) * hd, p.H, H));
+      }
+      HIPCHECK(put_blk(r.pf_o, T(pre + "attn.wo"), p.H, nq * hd, (size_t)nq * hd));
+      pfw[li].qkv = (const uint16_t *)(A + r.pf_qkv.off);
+      pfw[li].o = (const uint16_t *)(A + r.pf_o.off);
       L.at_q = (const uint16_t *)(A + r.at_q.off);
       L.at_k = (const uint16_t *)(A + r.at_k.off);
       L.at_v = (const uint16_t *)(A + r.at_v.off);
@@ -574,6 +625,17 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
       for (int xg = 0; xg < MK_NX; ++xg)
         tile_pack(T(pre + "ffn.wd") + (size_t)xg * J, p.H, J, (size_t)p.I, stage.data() + (size_t)xg * H * J);
       HIPCHECK(put(r.ffn_dn, stage.data()));
+      {
+        std::vector<uint16_t> gu((size_t)2 * p.I * H);
+        for (int i = 0; i < p.I; ++i) {
+          std::memcpy(gu.data() + (size_t)(2 * i) * H, T(pre + "ffn.wg") + (size_t)i * H, H * 2);
+          std::memcpy(gu.data() + (size_t)(2 * i + 1) * H, T(pre + "ffn.wu") + (size_t)i * H, H * 2);
+        }
+        HIPCHECK(put_blk(r.pf_gu, gu.data(), 2 * p.I, p.H, H));
+      }
+      HIPCHECK(put_blk(r.pf_dn, T(pre + "ffn.wd"), p.H, p.I, (size_t)p.I));
+      pfw[li].gu = (const uint16_t *)(A + r.pf_gu.off);
+      pfw[li].dn = (const uint16_t *)(A + r.pf_dn.off);
       L.ffn_gu = (const uint16_t *)(A + r.ffn_gu.off);
       L.ffn_dn = (const uint16_t *)(A + r.ffn_dn.off);
     }
@@ -622,6 +684,7 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
   mm->cfg.layer_kind = mm->kinds.data();
   mm->dev = d;
   mm->layers_host = lt;
+  mm->pfw = pfw;
   mm->cur = 0;
   mm->seq_dev = seq_dev;
   mm->seq_layers_host = seq_lt;
@@ -707,7 +770,8 @@ extern "C" int mk_prefill(mk_model *m, const int32_t *d_tokens, int32_t n_tokens
   }
   const bool two = m->pf_blocks >= 2 && m->pf_side;
   HIPCHECK(mk_prefill_enqueue(&m->dev, m->layers_host.data(), &m->pf, d_tokens, n_tokens, d_next_token, d_last_logits, st,
-                              two ? m->pf_side : nullptr, two ? m->pf_ev.data() : nullptr, m->pf_blocks));
+                              two ? m->pf_side : nullptr, two ? m->pf_ev.data() : nullptr, m->pf_blocks,
+                              m->pfw.data()));
   m->pos_hi += n_tokens;
   m->seq_verified[m->cur] = 0;   // the prefill applies any pending updates first
   return MK_OK;

@@ -163,6 +163,18 @@ __host__ __device__ static inline int mk_tile_G(int K) {
 #define MK_PT 1024                   // tokens per prefill pass (multiple of MK_CHUNK)
 #define MK_CHUNK 64                  // delta-rule chunk
 
+// Prefill copies of one layer's projection weights, each a matrix [N][K] in the GEMM operand
+// block layout (1 KiB blocks of 16 rows x 32 k; rows padded with zeros to a multiple of 16), read
+// only by the prefill GEMMs so that every weight block they load is 1 KiB of contiguous memory.
+struct MkPfW {
+  const uint16_t *in;                 // DeltaNet in-projection, rows of head h: q k v z a b  [nh r_in][H]
+  const uint16_t *out;                // DeltaNet out-projection [H][nh dv]
+  const uint16_t *qkv;                // attention q | k | v [(nq + 2 nkv) hd][H]
+  const uint16_t *o;                  // attention o-projection [H][nq hd]
+  const uint16_t *gu;                 // FFN gate and up rows interleaved (g_i row 2 i, u_i row 2 i + 1) [2 I][H]
+  const uint16_t *dn;                 // FFN down-projection [H][I]
+};
+
 struct MkPf {
   float *X;                           // [PT][H] residual stream (FP32)
   uint16_t *a1h, *a1l;                // [PT][K1] GEMM operand as bf16 hi + lo, K1 = max(H, nh dv, nq hd)

@@ -213,6 +213,7 @@ __global__ void __launch_bounds__(PF_THREADS) pf_norm_split(const float *X, cons
 struct PfGemm {
   const uint16_t *ah, *al;            // A as bf16 hi + lo in the GEMM operand block layout (Kc = K)
   int M, N, K;
+  const uint16_t *wblk;               // if set: W [N][K] in the operand block layout (rows padded to 16)
   const uint16_t *wb[3];
   int wend[3];
   int ks, kstride;
@@ -271,6 +272,9 @@ __global__ void __launch_bounds__(WGM * WGN * 64) pf_gemm(PfGemm g) {
     if (b < 2 * NBA) {
       const int hl = b / NBA, rb = b % NBA;
       src[i] = (hl ? g.al : g.ah) + ((size_t)(bm0 / 16 + rb) * kbn + kb0) * 512 + lane * 8;
+    } else if (g.wblk) {   // 1 KiB contiguous, like the A blocks
+      const int nb = min(bn0 / 16 + (b - 2 * NBA), (g.N + 15) / 16 - 1);
+      src[i] = g.wblk + ((size_t)nb * kbn + kb0) * 512 + lane * 8;
     } else {
       const int n = min(bn0 + (b - 2 * NBA) * 16 + drow, g.N - 1);
       const int s = n < g.wend[0] ? 0 : (n < g.wend[1] ? 1 : 2);
@@ -286,7 +290,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) pf_gemm(PfGemm g) {
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int b = w + i * NW;
-      const uint16_t *p = b < 2 * NBA ? src[i] + (size_t)sa * 512 : src[i] + boff;
+      const uint16_t *p = (b < 2 * NBA || g.wblk) ? src[i] + (size_t)sa * 512 : src[i] + boff;
       __builtin_amdgcn_global_load_lds((const void *)p,
                                        (__attribute__((address_space(3))) void *)(gsm + (buf * NBLK + b) * 1024), 16, 0, 0);
     }
@@ -1459,8 +1463,8 @@ struct PfBlk {
 };
 enum { PF_NONE = 0, PF_RECORD = 1, PF_WAIT = 2 };
 
-static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkLayerDev *next, const MkPf *pf,
-                                const PfBlk &b, hipStream_t st, int sync, hipEvent_t ev) {
+static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkPfW &PW, const MkLayerDev *next,
+                                const MkPf *pf, const PfBlk &b, hipStream_t st, int sync, hipEvent_t ev) {
   const int H = d->H, nh = d->nh, dk = d->dk, dv = d->dv, nq = d->nq, nkv = d->nkv, hd = d->hd, J = d->J, I = d->I;
   const int r0 = b.r0, T = b.T;
   const size_t rH = (size_t)r0 * H, rK = (size_t)r0 * pf->K1;
@@ -1477,7 +1481,7 @@ static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkLay
     g.N = nh * d->r_in; g.K = H;
     g.wb[0] = g.wb[1] = g.wb[2] = L.dn_in; g.wend[0] = g.wend[1] = g.wend[2] = g.N;
     g.ks = H; g.kstride = 0;
-    g.c = P; g.ldc = pf->NP;
+    g.c = P; g.ldc = pf->NP; g.wblk = PW.in;
     if ((e = launch_gemm(EPI_STORE, g, nullptr, st)) != hipSuccess) return e;
     if (sync == PF_WAIT && (e = hipStreamWaitEvent(st, ev, 0)) != hipSuccess) return e;
     const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
@@ -1508,7 +1512,7 @@ static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkLay
     go.ah = a1h; go.al = a1l; go.M = T; go.N = H; go.K = nh * dv;
     go.wb[0] = go.wb[1] = go.wb[2] = L.dn_out; go.wend[0] = go.wend[1] = go.wend[2] = H;
     go.ks = dv; go.kstride = H * dv;
-    go.c = X; go.ldc = H;
+    go.c = X; go.ldc = H; go.wblk = PW.out;
     if ((e = launch_gemm(EPI_RESID, go, part, st, &n2)) != hipSuccess) return e;
   } else {
     g.N = (nq + 2 * nkv) * hd; g.K = H;
@@ -1516,7 +1520,7 @@ static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkLay
     g.wb[1] = L.at_k; g.wend[1] = (nq + nkv) * hd;
     g.wb[2] = L.at_v; g.wend[2] = g.N;
     g.ks = H; g.kstride = 0;
-    g.c = P; g.ldc = pf->NP;
+    g.c = P; g.ldc = pf->NP; g.wblk = PW.qkv;
     if ((e = launch_gemm(EPI_STORE, g, nullptr, st)) != hipSuccess) return e;
     PfAtt at{};
     at.P = P; at.NP = pf->NP; at.T = T; at.rope = d->rope; at.page_table = d->page_table; at.ctl = d->ctl;
@@ -1536,30 +1540,33 @@ static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkLay
     go.ah = a1h; go.al = a1l; go.M = T; go.N = H; go.K = nq * hd;
     go.wb[0] = go.wb[1] = go.wb[2] = L.at_o; go.wend[0] = go.wend[1] = go.wend[2] = H;
     go.ks = hd; go.kstride = H * hd;
-    go.c = X; go.ldc = H;
+    go.c = X; go.ldc = H; go.wblk = PW.o;
     if ((e = launch_gemm(EPI_RESID, go, part, st, &n2)) != hipSuccess) return e;
   }
   PfGemm gu{};
   gu.ah = a1h; gu.al = a1l; gu.M = T; gu.N = 2 * I; gu.K = H;
   gu.wb[0] = gu.wb[1] = gu.wb[2] = L.ffn_gu; gu.wend[0] = gu.wend[1] = gu.wend[2] = 2 * I;
-  gu.ks = H; gu.kstride = 0;
+  gu.ks = H; gu.kstride = 0; gu.wblk = PW.gu;
   gu.oh = pf->a2h + (size_t)r0 * I; gu.ol = pf->a2l + (size_t)r0 * I; gu.ldo = I;
   if ((e = launch_gemm(EPI_SWIGLU, gu, nullptr, st)) != hipSuccess) return e;
   PfGemm gd{};
   gd.ah = gu.oh; gd.al = gu.ol; gd.M = T; gd.N = H; gd.K = I;
   gd.wb[0] = gd.wb[1] = gd.wb[2] = L.ffn_dn; gd.wend[0] = gd.wend[1] = gd.wend[2] = H;
-  gd.ks = J; gd.kstride = H * J;
+  gd.ks = J; gd.kstride = H * J; gd.wblk = PW.dn;
   gd.c = X; gd.ldc = H;
   return launch_gemm(EPI_RESID, gd, part, st, n1.g ? &n1 : nullptr);
 }
 
-// Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table.
+// Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table;
+// pfw: per layer, the prefill copies of its projection weights (null pointers: the GEMMs gather
+// the weights from the decode tiles instead).
 // side / ev (nullable): a second stream and d->n_layers + 2 events for the two-block form; a
 // pass of fewer than PF_SPLIT_MIN rows, or max_blocks 1, runs as one block on st.
 constexpr int PF_SPLIT_MIN = 256;
 extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layers_host, const MkPf *pf,
                                          const int32_t *tokens, int n, int32_t *argmax, float *logits,
-                                         hipStream_t st, hipStream_t side, hipEvent_t *ev, int max_blocks) {
+                                         hipStream_t st, hipStream_t side, hipEvent_t *ev, int max_blocks,
+                                         const MkPfW *pfw) {
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e;
@@ -1596,7 +1603,7 @@ extern "C" hipError_t mk_prefill_enqueue(const MkDev *d, const MkLayerDev *layer
       const MkLayerDev *next = li + 1 < NL ? &layers_host[li + 1] : nullptr;
       for (int bi = 0; bi < nb; ++bi) {
         const int sync = !two ? PF_NONE : bi == 0 ? PF_RECORD : PF_WAIT;
-        if ((e = enqueue_layer(d, layers_host[li], next, pf, blk[bi], bi ? side : st, sync,
+        if ((e = enqueue_layer(d, layers_host[li], pfw[li], next, pf, blk[bi], bi ? side : st, sync,
                                two ? ev[li] : nullptr)) != hipSuccess)
           return e;
       }
