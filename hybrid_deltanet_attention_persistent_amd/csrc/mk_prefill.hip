@@ -204,19 +204,14 @@ __global__ void __launch_bounds__(PF_THREADS) pf_norm_split(const float *X, cons
 }
 
 // ------------------------------------------------------------------------------ MFMA GEMM
-// C[M][N] = A[M][K] . W[N][K]^T with A given as bf16 hi + lo (operand block layout) and W in the tile
-// format of mk_layout.h.  W rows come from up to three row segments (tile wb[s] holds rows
-// [wend[s-1], wend[s]) ), and along K from segments of ks columns, kstride elements apart
-// (one tile [rows][ks] per segment).  One wave computes MT x NT 16x16 blocks with
+// C[M][N] = A[M][K] . W[N][K]^T with A given as bf16 hi + lo and W as bf16, both in the operand
+// block layout (W: the prefill weight copies of mk_layout.h).  One wave computes MT x NT 16x16 blocks with
 // v_mfma_f32_16x16x32_bf16 (lane l: A row l%16 and B column l%16 with k = 8 (l/16) .. +8;
 // result rows 4 (l/16) .. +4 of column l%16).
 struct PfGemm {
   const uint16_t *ah, *al;            // A as bf16 hi + lo in the GEMM operand block layout (Kc = K)
   int M, N, K;
-  const uint16_t *wblk;               // if set: W [N][K] in the operand block layout (rows padded to 16)
-  const uint16_t *wb[3];
-  int wend[3];
-  int ks, kstride;
+  const uint16_t *w;                  // W [N][K] in the operand block layout (rows padded to a multiple of 16)
   float *c;
   int ldc;
   uint16_t *oh, *ol;                  // EPI_SWIGLU: output in the operand block layout, Kc = ldo
@@ -228,11 +223,6 @@ struct PfGemm {
 };
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PART = 3 };
 
-__device__ __forceinline__ int tileG(int K) {
-  int c = K / 8, g = 64;
-  while (g > 1 && (c % g) != 0) g >>= 1;
-  return g;
-}
 
 // Workgroup tile BM x BN (BM = WGM*MT*16, BN = WGN*NT*16, WGM*WGN waves), K in stages of 32.
 // Each stage of A (hi and lo) and W is copied into LDS by direct-to-LDS loads
@@ -241,8 +231,8 @@ __device__ __forceinline__ int tileG(int K) {
 // is read, so NS - 1 stages are in flight and no register holds a load in flight.  Within a block,
 // row r's 8-element group q sits at slot 4 r + (q ^ ((r >> 1) & 3)): the fragment reads (lane l:
 // row l % 16, group l / 16) of each 8 consecutive lanes then cover all 32 banks once.  A arrives in
-// that block layout already (written so by the kernels producing GEMM operands); W rows are
-// gathered from the tile format (4 lanes per row, 64 contiguous bytes each).
+// that block layout already (written so by the kernels producing GEMM operands), W from the prefill
+// weight copies in the same layout: every block load is 1 KiB of contiguous memory.
 constexpr int GBK = 32;
 
 template <int EPI, int MT, int NT, int WGM, int WGN, int NS>
@@ -262,41 +252,27 @@ __global__ void __launch_bounds__(WGM * WGN * 64) pf_gemm(PfGemm g) {
   const int tmi = tile % g.tm, tni = (tile / g.tm) % g.tn, tzi = tile / (g.tm * g.tn);
   const int bm0 = tmi * BM, bn0 = tni * BN;
   const int kbeg = tzi * g.kper, nst = g.kper / GBK, kb0 = kbeg / GBK, kbn = g.K / GBK;
-  // this lane's loads: block b = w + i NW of a stage (A hi blocks, A lo blocks, then W blocks)
-  const int drow = lane >> 2, dkg = (lane & 3) ^ ((drow >> 1) & 3);
+  // this lane's loads: block b = w + i NW of a stage (A hi blocks, A lo blocks, then W blocks; W
+  // blocks past the last row block of N are clamped to it, their products never stored)
   const uint16_t *src[DPW];
-  const int G = tileG(g.ks), L = g.ks / 8 / G, RG = 64 / G, G8 = G * 8, lg8 = __builtin_ctz(G8);
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
     const int b = w + i * NW;
     if (b < 2 * NBA) {
       const int hl = b / NBA, rb = b % NBA;
       src[i] = (hl ? g.al : g.ah) + ((size_t)(bm0 / 16 + rb) * kbn + kb0) * 512 + lane * 8;
-    } else if (g.wblk) {   // 1 KiB contiguous, like the A blocks
-      const int nb = min(bn0 / 16 + (b - 2 * NBA), (g.N + 15) / 16 - 1);
-      src[i] = g.wblk + ((size_t)nb * kbn + kb0) * 512 + lane * 8;
     } else {
-      const int n = min(bn0 + (b - 2 * NBA) * 16 + drow, g.N - 1);
-      const int s = n < g.wend[0] ? 0 : (n < g.wend[1] ? 1 : 2);
-      const int r = n - (s == 0 ? 0 : g.wend[s - 1]);
-      src[i] = g.wb[s] + (r / RG) * L * 512 + (r % RG) * G8;
+      const int nb = min(bn0 / 16 + (b - 2 * NBA), (g.N + 15) / 16 - 1);
+      src[i] = g.w + ((size_t)nb * kbn + kb0) * 512 + lane * 8;
     }
   }
-  int bj = kbeg + dkg * 8, bksg = bj / g.ks;   // k position of this lane's next W load
-  bj -= bksg * g.ks;
   auto issue = [&](int st) {
     const int buf = st % NS, sa = min(st, nst - 1);
-    const size_t boff = (size_t)bksg * g.kstride + ((bj >> lg8) << 9) + (bj & (G8 - 1));
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int b = w + i * NW;
-      const uint16_t *p = (b < 2 * NBA || g.wblk) ? src[i] + (size_t)sa * 512 : src[i] + boff;
-      __builtin_amdgcn_global_load_lds((const void *)p,
+      __builtin_amdgcn_global_load_lds((const void *)(src[i] + (size_t)sa * 512),
                                        (__attribute__((address_space(3))) void *)(gsm + (buf * NBLK + b) * 1024), 16, 0, 0);
-    }
-    if (st < nst - 1) {
-      bj += GBK;
-      if (bj >= g.ks) { bj -= g.ks; ++bksg; }
     }
   };
   f32x4 acc[MT][NT], acl[MT][NT];   // hi and lo products in separate accumulators (no MFMA waits on its neighbour)
@@ -1465,7 +1441,7 @@ enum { PF_NONE = 0, PF_RECORD = 1, PF_WAIT = 2 };
 
 static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkPfW &PW, const MkLayerDev *next,
                                 const MkPf *pf, const PfBlk &b, hipStream_t st, int sync, hipEvent_t ev) {
-  const int H = d->H, nh = d->nh, dk = d->dk, dv = d->dv, nq = d->nq, nkv = d->nkv, hd = d->hd, J = d->J, I = d->I;
+  const int H = d->H, nh = d->nh, dk = d->dk, dv = d->dv, nq = d->nq, nkv = d->nkv, hd = d->hd, I = d->I;
   const int r0 = b.r0, T = b.T;
   const size_t rH = (size_t)r0 * H, rK = (size_t)r0 * pf->K1;
   uint16_t *a1h = pf->a1h + rK, *a1l = pf->a1l + rK;   // operand blocks of width H, nh dv or nq hd (<= K1)
@@ -1479,9 +1455,7 @@ static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkPfW
   hipError_t e;
   if (L.kind == 0) {
     g.N = nh * d->r_in; g.K = H;
-    g.wb[0] = g.wb[1] = g.wb[2] = L.dn_in; g.wend[0] = g.wend[1] = g.wend[2] = g.N;
-    g.ks = H; g.kstride = 0;
-    g.c = P; g.ldc = pf->NP; g.wblk = PW.in;
+    g.c = P; g.ldc = pf->NP; g.w = PW.in;
     if ((e = launch_gemm(EPI_STORE, g, nullptr, st)) != hipSuccess) return e;
     if (sync == PF_WAIT && (e = hipStreamWaitEvent(st, ev, 0)) != hipSuccess) return e;
     const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
@@ -1510,17 +1484,11 @@ static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkPfW
     else hipLaunchKernelGGL(pf_dn_out<64>, gtok, dim3(64 * 4), 0, st, po);
     PfGemm go{};
     go.ah = a1h; go.al = a1l; go.M = T; go.N = H; go.K = nh * dv;
-    go.wb[0] = go.wb[1] = go.wb[2] = L.dn_out; go.wend[0] = go.wend[1] = go.wend[2] = H;
-    go.ks = dv; go.kstride = H * dv;
-    go.c = X; go.ldc = H; go.wblk = PW.out;
+    go.c = X; go.ldc = H; go.w = PW.out;
     if ((e = launch_gemm(EPI_RESID, go, part, st, &n2)) != hipSuccess) return e;
   } else {
     g.N = (nq + 2 * nkv) * hd; g.K = H;
-    g.wb[0] = L.at_q; g.wend[0] = nq * hd;
-    g.wb[1] = L.at_k; g.wend[1] = (nq + nkv) * hd;
-    g.wb[2] = L.at_v; g.wend[2] = g.N;
-    g.ks = H; g.kstride = 0;
-    g.c = P; g.ldc = pf->NP; g.wblk = PW.qkv;
+    g.c = P; g.ldc = pf->NP; g.w = PW.qkv;
     if ((e = launch_gemm(EPI_STORE, g, nullptr, st)) != hipSuccess) return e;
     PfAtt at{};
     at.P = P; at.NP = pf->NP; at.T = T; at.rope = d->rope; at.page_table = d->page_table; at.ctl = d->ctl;
@@ -1538,28 +1506,23 @@ static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkPfW
     else return hipErrorInvalidValue;   // head_dim is 64 or 128 (checked at load)
     PfGemm go{};
     go.ah = a1h; go.al = a1l; go.M = T; go.N = H; go.K = nq * hd;
-    go.wb[0] = go.wb[1] = go.wb[2] = L.at_o; go.wend[0] = go.wend[1] = go.wend[2] = H;
-    go.ks = hd; go.kstride = H * hd;
-    go.c = X; go.ldc = H; go.wblk = PW.o;
+    go.c = X; go.ldc = H; go.w = PW.o;
     if ((e = launch_gemm(EPI_RESID, go, part, st, &n2)) != hipSuccess) return e;
   }
   PfGemm gu{};
   gu.ah = a1h; gu.al = a1l; gu.M = T; gu.N = 2 * I; gu.K = H;
-  gu.wb[0] = gu.wb[1] = gu.wb[2] = L.ffn_gu; gu.wend[0] = gu.wend[1] = gu.wend[2] = 2 * I;
-  gu.ks = H; gu.kstride = 0; gu.wblk = PW.gu;
+  gu.w = PW.gu;
   gu.oh = pf->a2h + (size_t)r0 * I; gu.ol = pf->a2l + (size_t)r0 * I; gu.ldo = I;
   if ((e = launch_gemm(EPI_SWIGLU, gu, nullptr, st)) != hipSuccess) return e;
   PfGemm gd{};
   gd.ah = gu.oh; gd.al = gu.ol; gd.M = T; gd.N = H; gd.K = I;
-  gd.wb[0] = gd.wb[1] = gd.wb[2] = L.ffn_dn; gd.wend[0] = gd.wend[1] = gd.wend[2] = H;
-  gd.ks = J; gd.kstride = H * J; gd.wblk = PW.dn;
+  gd.w = PW.dn;
   gd.c = X; gd.ldc = H;
   return launch_gemm(EPI_RESID, gd, part, st, n1.g ? &n1 : nullptr);
 }
 
 // Enqueue the prefill of n tokens (device buffer) on the stream.  layers_host: the layer table;
-// pfw: per layer, the prefill copies of its projection weights (null pointers: the GEMMs gather
-// the weights from the decode tiles instead).
+// pfw: per layer, the prefill copies of its projection weights.
 // side / ev (nullable): a second stream and d->n_layers + 2 events for the two-block form; a
 // pass of fewer than PF_SPLIT_MIN rows, or max_blocks 1, runs as one block on st.
 constexpr int PF_SPLIT_MIN = 256;
