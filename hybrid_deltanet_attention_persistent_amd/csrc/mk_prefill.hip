@@ -1384,8 +1384,9 @@ static hipError_t launch_gemm_t(PfGemm g, int nsplit, hipStream_t st) {
   hipLaunchKernelGGL((pf_gemm<EPI, MT, NT, WGM, WGN, NS>), dim3(g.tn * g.tm * g.tz), dim3(WGM * WGN * 64), lds, st, g);
   return hipGetLastError();
 }
-// Tiles (measured at 520 rows): outputs wider than 2048 columns take 64 x 256 workgroup tiles
-// (8 waves of 32 x 64, 96 KiB of LDS, one workgroup per CU); narrower ones 64 x 64 tiles (4 waves
+// Tiles (measured at 520 rows, then per row block): outputs wider than 2048 columns take 64 x 256
+// workgroup tiles (8 waves of 32 x 64, 96 KiB of LDS, one workgroup per CU; 64 x 128 for row blocks
+// of at most 384 rows); narrower ones 64 x 64 tiles (4 waves
 // of 32 x 32) so that the grid still fills the chip.  The 1024-wide outputs that add into the
 // residual stream use 64 x 128 tiles (8 waves of 32 x 32) with split-K (partials reduced in split
 // order), so that the grid fills the chip and each K stream is short.
@@ -1399,9 +1400,15 @@ struct PfNext {
 static hipError_t launch_gemm(int epi, PfGemm g, float *part, hipStream_t st, const PfNext *next = nullptr) {
   if (g.K % GBK != 0) return hipErrorInvalidValue;
   g.kper = g.K;
-  const bool wide = g.N > 2048;
-  if (epi == EPI_STORE) return wide ? launch_gemm_t<EPI_STORE, 2, 4, 2, 4, 4>(g, 1, st) : launch_gemm_t<EPI_STORE, 2, 2, 2, 2, 4>(g, 1, st);
-  if (epi == EPI_SWIGLU) return wide ? launch_gemm_t<EPI_SWIGLU, 2, 4, 2, 4, 4>(g, 1, st) : launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2, 4>(g, 1, st);
+  // outputs wider than 2048 columns: 64 x 256 tiles, or 64 x 128 for a row block of at most 384
+  // rows (measured: pp520 in two blocks 3.05 -> 3.00 ms; a 512-row block is faster with 64 x 256)
+  const bool wide = g.N > 2048, few = g.M <= 384;
+  if (epi == EPI_STORE)
+    return !wide ? launch_gemm_t<EPI_STORE, 2, 2, 2, 2, 4>(g, 1, st)
+                 : few ? launch_gemm_t<EPI_STORE, 2, 2, 2, 4, 4>(g, 1, st) : launch_gemm_t<EPI_STORE, 2, 4, 2, 4, 4>(g, 1, st);
+  if (epi == EPI_SWIGLU)
+    return !wide ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 2, 4>(g, 1, st)
+                 : few ? launch_gemm_t<EPI_SWIGLU, 2, 2, 2, 4, 4>(g, 1, st) : launch_gemm_t<EPI_SWIGLU, 2, 4, 2, 4, 4>(g, 1, st);
   const int ns = g.K / GBK;
   const int nsplit = (ns % 4 == 0 && ns >= 16) ? 4 : (ns % 2 == 0 && ns >= 8) ? 2 : 1;
   if (nsplit == 1 || !part || g.N > 4 * PF_THREADS || g.N % 4 != 0) {

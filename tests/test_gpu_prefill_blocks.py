@@ -209,3 +209,16 @@ def test_decode_after_kernels_on_another_stream(dev, tiny):
         close(lg, ref_logits[i + 1], f"decode {i}")
     assert got == list(ref_toks)
     r.close()
+
+
+def test_24L_pp1024_two_blocks_bit_identical_and_match_oracle(dev):
+    """A full 1024-token pass: two row blocks of 512 (64 x 256 GEMM tiles, grids of more than one
+    wave of workgroups), bit-identical to one block and equal to the live oracle over the whole
+    vocabulary."""
+    cfg = W.HYBRID_24L
+    weights = W.make_weights(cfg, seed=0)
+    prompt = W.make_prompt(cfg, 1024, seed=1)
+    outs = run_pair(cfg, weights, dev, [prompt], steps=1)
+    rl = OracleModel(cfg, weights, C2).prefill(prompt)
+    close(outs[0][1], rl, "pp1024 prefill logits")
+    assert outs[0][0] == argmax_lowest(rl)
