@@ -211,7 +211,9 @@ def extras(model, cfg, stream, weights=None) -> dict:
     # greedy token after its last accepted position (picked on the device: no host round trip)
     nf = 64
     prompt = torch.tensor(W.make_prompt(cfg, 520, seed=1), dtype=torch.int32, device=dev)
-    toks = torch.tensor(W.make_drafts(cfg, nf, 5, seed=2), dtype=torch.int32, device=dev)
+    # tokens [last accepted, 4 drafts] per forward (make_drafts gives the 4 drafts)
+    toks = torch.zeros((nf, 5), dtype=torch.int32, device=dev)
+    toks[:, 1:] = torch.tensor(W.make_drafts(cfg, nf, 5, seed=2), dtype=torch.int32, device=dev)
     am = torch.zeros((nf, 5), dtype=torch.int32, device=dev)
     nacc = torch.zeros((nf, 1), dtype=torch.int32, device=dev)
     model.reset()
