@@ -678,9 +678,17 @@ __global__ void __launch_bounds__(CP_THREADS) pf_dn_chunk_prep(PfChunk c) {
      // (A operand from K or V, B operand from T or M T) so that each lane ends with four
      // consecutive columns of one token: one 16-byte store in fragment order.  The k range of
      // token block rb ends at its diagonal.
+    // With two workgroups per (head, chunk) (blockIdx.z, for DK == 128) each takes half of the
+    // column blocks nt, and each wave two units whose k ranges add up to 5 blocks: token blocks 0
+    // and 3, or 1 and 2 (the work of unit (rb, nt) grows with rb).  One workgroup: every unit.
+    const bool split = DK == 128 && gridDim.z == 2;
+    const int nunit = split ? 2 : (DK / 16) * 4 / CP_WAVES;
 #pragma unroll 1
-    for (int u = w; u < (DK / 16) * 4; u += CP_WAVES) {
-      const int nt = u % (DK / 16), rb = u / (DK / 16), d = 16 * nt + c16;
+    for (int ui = 0; ui < nunit; ++ui) {
+      const int u = w + ui * CP_WAVES;
+      const int nt = split ? (int)blockIdx.z * 4 + (w & 3) : u % (DK / 16);
+      const int rb = split ? ((w >> 2) ? (ui ? 2 : 1) : (ui ? 3 : 0)) : u / (DK / 16);
+      const int d = 16 * nt + c16;
       f32x4 aw = {0.f, 0.f, 0.f, 0.f}, aq = aw, au = aw, ao = aw;
       for (int kb = 0; kb <= rb; ++kb) {
         float x[4], mt[4], bk[4], bv[4];
@@ -711,6 +719,7 @@ __global__ void __launch_bounds__(CP_THREADS) pf_dn_chunk_prep(PfChunk c) {
       *reinterpret_cast<float4 *>(c.cO + o) = make_float4(ao[0], ao[1], ao[2], ao[3]);
     }
   }
+  if (blockIdx.z != 0) return;   // the rest is written once per (head, chunk)
   for (int e = tid; e < DK * MK_CHUNK; e += CP_THREADS) {   // K^T in fragment order:
     // e = (((db * 4 + tb) * 4 + tq) * 16 + dl) * 4 + te
     const int te = e & 3, dl = (e >> 2) & 15, tq = (e >> 6) & 3, tb = (e >> 8) & 3, db = e >> 10;
@@ -1479,7 +1488,7 @@ static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkPfW
     const dim3 gtok((T + PREP_TB - 1) / PREP_TB, nh);
     if (dk == 128) {
       hipLaunchKernelGGL(pf_dn_prep<128>, gtok, dim3(3 * 128), 0, st, pp);
-      hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(128), st, ck);
+      hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk, 2), dim3(CP_THREADS), chunk_prep_lds(128), st, ck);
       hipLaunchKernelGGL(pf_dn_scan<128>, dim3(nh, 128 / 16), dim3(SCAN_THREADS), scan_lds(128), st, sc);
     } else {
       hipLaunchKernelGGL(pf_dn_prep<64>, gtok, dim3(3 * 64), 0, st, pp);
