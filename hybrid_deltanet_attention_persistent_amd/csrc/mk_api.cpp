@@ -117,7 +117,7 @@ struct Plan {
   // prefill scratch (one pass of MK_PT tokens)
   int K1, NP;
   Region pf_X, pf_a1h, pf_a1l, pf_a2h, pf_a2l, pf_P, pf_cW, pf_cQ, pf_cU, pf_cO, pf_cKt, pf_cg, pf_cd,
-      pf_snap, pf_qkv, pf_gb, pf_aq, pf_lmbest, pf_part;
+      pf_snap, pf_aq, pf_lmbest, pf_part;
   size_t total;
 };
 
@@ -271,8 +271,6 @@ Plan make_plan(const mk_config *c) {
     p.pf_cg = L.add(nhd * nch * MK_CHUNK * 4);
     p.pf_cd = L.add(nhd * nch * MK_CHUNK * 4);
     p.pf_snap = L.add(nhd * nch * p.dv * p.dk * 4);
-    p.pf_qkv = L.add(nhd * T * (2 * p.dk + p.dv) * 4);
-    p.pf_gb = L.add(nhd * T * 2 * 4);
     p.pf_aq = L.add(has_at ? T * p.nq * p.hd * 4 : 0);
     p.pf_lmbest = L.add((size_t)MK_NWG * 8);
     p.pf_part = L.add((size_t)4 * T * H * 4);
@@ -699,7 +697,7 @@ extern "C" int mk_load_weights(const mk_config *cfg, const mk_tensor *tensors, i
     f.P = (float *)P(p.pf_P);
     f.cW = (float *)P(p.pf_cW); f.cQ = (float *)P(p.pf_cQ); f.cU = (float *)P(p.pf_cU); f.cO = (float *)P(p.pf_cO);
     f.cKt = (float *)P(p.pf_cKt); f.cg = (float *)P(p.pf_cg); f.cd = (float *)P(p.pf_cd);
-    f.snap = (float *)P(p.pf_snap); f.qkv = (float *)P(p.pf_qkv); f.gb = (float *)P(p.pf_gb);
+    f.snap = (float *)P(p.pf_snap);
     f.aq = (float *)P(p.pf_aq);
     f.lmbest = (unsigned long long *)P(p.pf_lmbest);
     f.part = (float *)P(p.pf_part);

@@ -183,8 +183,6 @@ struct MkPf {
   float *cW, *cQ, *cU, *cO;           // [nh][PT/CHUNK][CHUNK][dk|dv] chunk terms W, Q~, U', O' of the delta rule
   float *cKt;                         // [nh][PT/CHUNK][dk][CHUNK] the chunk's keys, transposed
   float *cg, *cd;                     // [nh][PT/CHUNK][CHUNK] exp(G_i), exp(G_last - G_i)
-  float *qkv;                         // [nh][PT][2 dk + dv] per-token q / |q|, k / |k|, v after the conv
-  float *gb;                          // [nh][PT][2] per-token log alpha, beta
   float *snap;                        // [nh][PT/CHUNK][dv][dk] delta-rule state entering each chunk
   float *aq;                          // [PT][nq hd] queries after RoPE
   unsigned long long *lmbest;         // [MK_NWG] packed (ordered value, ~index) candidates

@@ -418,89 +418,16 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Per (16-token block, head): the causal conv (taps over positions p-3 .. p) + SiLU of the head's
-// q, k, v channels, the L2 norms of q and k, and the gates log alpha = -softplus(a), beta =
-// sigmoid(b): everything of the delta rule that is local to one token.  Thread = channel (3 dk of
-// them); all of its 19 inputs are loaded before any is used (earlier positions of the sequence
-// come from the ring).
-struct PfPrep {
+constexpr int PREP_TB = 16;   // tokens per run of the conv (and per workgroup of pf_dn_out)
+
+struct PfChunk {
   const float *P;                     // [T][NP] in-projection outputs; per head x: [q | k | v | z | a | b]
   int NP, r_in, C, nh;                // C: conv channels (q of all heads, then k, then v)
   const float *conv;                  // [C][4] taps
   const float *ring;                  // [MK_RING][C] pre-conv inputs of earlier positions
   const int32_t *ctl;
   float l2_eps;
-  float *qkv;                         // [nh][PT][3 dk]: q / |q|, k / |k|, v
-  float *gb;                          // [nh][PT][2]: log alpha, beta
-  int T;
   int pofs;                           // position of row 0 = control-block position + pofs
-};
-constexpr int PREP_TB = 16;
-template <int DK>
-__global__ void __launch_bounds__(3 * DK) pf_dn_prep(PfPrep c) {
-  constexpr int NCH = 3 * DK, XL = NCH + 4;
-  __shared__ float xs[PREP_TB * XL];
-  const int h = blockIdx.y, t0 = blockIdx.x * PREP_TB, ch = threadIdx.x, w = ch >> 6, lane = ch & 63;
-  const int seg = ch / DK, i = ch - seg * DK;
-  const int col = h * c.r_in + ch, cch = seg * c.nh * DK + h * DK + i;
-  const int p0 = c.ctl[MK_CTL_POS] + c.pofs;
-  const float4 wt = ld4(c.conv + cch * 4);
-  float x[PREP_TB + 3];
-#pragma unroll
-  for (int u = 0; u < PREP_TB + 3; ++u) {   // branch-free: every load issued, invalid ones zeroed
-    const int tt = t0 + u - 3;              // pass token
-    const bool ok = tt >= 0 ? tt < c.T : p0 + tt >= 0;
-    const float *src = tt >= 0 ? c.P + (size_t)min(tt, c.T - 1) * c.NP + col
-                               : c.ring + ((p0 + tt) & (MK_RING - 1)) * c.C + cch;
-    const float v = *src;
-    x[u] = ok ? v : 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < PREP_TB; ++j) {
-    float a = fmaf(wt.x, x[j], 0.f);
-    a = fmaf(wt.y, x[j + 1], a);
-    a = fmaf(wt.z, x[j + 2], a);
-    a = fmaf(wt.w, x[j + 3], a);
-    xs[j * XL + ch] = silu_fast(a);
-  }
-  if (ch < PREP_TB && t0 + ch < c.T) {   // gates of token t0 + ch
-    const float *pa = c.P + (size_t)(t0 + ch) * c.NP + h * c.r_in + 4 * DK;   // a, b
-    *reinterpret_cast<float2 *>(c.gb + ((size_t)h * MK_PT + t0 + ch) * 2) = make_float2(-softplusf_(pa[0]), sigmoidf_(pa[1]));
-  }
-  __syncthreads();
-  // norms: 16 lanes per row (token j, segment q or k), DK / 16 elements per lane, summed with DPP
-  float *dst = c.qkv + ((size_t)h * MK_PT + t0) * NCH;
-  {
-    constexpr int EPL = DK / 16, RPW = 4, NR = 2 * PREP_TB;   // rows per wave at a time
-    for (int r = w * RPW + (lane >> 4); r < NR; r += (NCH / 64) * RPW) {
-      const int j = r >> 1, sg = r & 1, e0 = (lane & 15) * EPL;
-      float v[EPL];
-#pragma unroll
-      for (int q = 0; q < EPL; q += 4) {
-        const float4 x4 = ld4(xs + j * XL + sg * DK + e0 + q);
-        v[q] = x4.x; v[q + 1] = x4.y; v[q + 2] = x4.z; v[q + 3] = x4.w;
-      }
-      float sq = 0.f;
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) sq = fmaf(v[q], v[q], sq);
-      const float nrm = sqrtf(row_sum16(sq) + c.l2_eps);
-      if (t0 + j < c.T) {
-#pragma unroll
-        for (int q = 0; q < EPL; q += 4)
-          *reinterpret_cast<float4 *>(dst + (size_t)j * NCH + sg * DK + e0 + q) =
-              make_float4(v[q] / nrm, v[q + 1] / nrm, v[q + 2] / nrm, v[q + 3] / nrm);
-      }
-    }
-  }
-  for (int e = ch; e < PREP_TB * DK; e += NCH) {
-    const int j = e / DK, q = e - j * DK;
-    if (t0 + j < c.T) dst[(size_t)j * NCH + 2 * DK + q] = xs[j * XL + 2 * DK + q];
-  }
-}
-
-struct PfChunk {
-  const float *qkv;                   // [nh][PT][3 dk] from pf_dn_prep
-  const float *gb;                    // [nh][PT][2] log alpha, beta
   float *cW, *cQ, *cU, *cO, *cKt;     // per (head, chunk), CHUNK x dk each, in the fragment orders below
   float *cg, *cd;                     // [nh][PT/CHUNK][CHUNK] exp(G_i), exp(G_last - G_i)
   int T;
@@ -544,26 +471,68 @@ __global__ void __launch_bounds__(CP_THREADS) pf_dn_chunk_prep(PfChunk c) {
   float *R = Mm + MK_CHUNK * CS;               // [3][16][17] partial sums of the inverse
   float *Gs = R + 3 * 16 * 17, *bs = Gs + MK_CHUNK, *gam = bs + MK_CHUNK, *bgam = gam + MK_CHUNK;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  {  // the chunk's normalized q, k and v rows into Qs, Ks, Vs (rows past the chunk's end: zero)
-    constexpr int C4 = 3 * DK / 4, NL = (MK_CHUNK * C4 + CP_THREADS - 1) / CP_THREADS;
-    const float *src = c.qkv + ((size_t)h * MK_PT + t0) * 3 * DK;
-    float4 v[NL];
+  {  // the causal conv (taps over positions p-3 .. p) + SiLU of the head's q, k and v channels
+     // into Qs, Ks, Vs (rows past the chunk's end: zero).  Item = (channel, run of PREP_TB tokens):
+     // lanes take consecutive channels, so each of its PREP_TB + 3 loads is a coalesced row
+     // segment; all of them are issued before any is used.  Positions before the pass come from
+     // the ring (the conv inputs of earlier positions).
+    constexpr int NCH = 3 * DK, NRUN = MK_CHUNK / PREP_TB;
+    const int p0 = c.ctl[MK_CTL_POS] + c.pofs;
+#pragma unroll 1
+    for (int it = tid; it < NCH * NRUN; it += CP_THREADS) {
+      const int chn = it % NCH, run = it / NCH, seg = chn / DK, i = chn - seg * DK;
+      const int col = h * c.r_in + chn, cch = seg * c.nh * DK + h * DK + i, tb = t0 + run * PREP_TB;
+      const float4 wt = ld4(c.conv + cch * 4);
+      float x[PREP_TB + 3];
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int e = tid + u * CP_THREADS, j = e / C4;
-      v[u] = (e < MK_CHUNK * C4 && j < Cn) ? ld4(src + (size_t)e * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int u = 0; u < PREP_TB + 3; ++u) {   // branch-free: every load issued, invalid ones zeroed
+        const int tt = tb + u - 3;              // pass token
+        const bool ok = tt >= 0 ? tt < c.T : p0 + tt >= 0;
+        const float *src = tt >= 0 ? c.P + (size_t)min(tt, c.T - 1) * c.NP + col
+                                   : c.ring + ((p0 + tt) & (MK_RING - 1)) * c.C + cch;
+        const float v = *src;
+        x[u] = ok ? v : 0.f;
+      }
+      float *dst = (seg == 0 ? Qs : seg == 1 ? Ks : Vs) + (run * PREP_TB) * KS + i;
+#pragma unroll
+      for (int j = 0; j < PREP_TB; ++j) {
+        float a = fmaf(wt.x, x[j], 0.f);
+        a = fmaf(wt.y, x[j + 1], a);
+        a = fmaf(wt.z, x[j + 2], a);
+        a = fmaf(wt.w, x[j + 3], a);
+        dst[j * KS] = (run * PREP_TB + j < Cn) ? silu_fast(a) : 0.f;
+      }
     }
+  }
+  __syncthreads();
+  {  // L2 norms of the q and k rows, in place: 16 lanes per row (token j, Qs or Ks), DK / 16
+     // elements per lane, summed with DPP
+    constexpr int EPL = DK / 16, RPW = 4, NR = 2 * MK_CHUNK;
+#pragma unroll 1
+    for (int r = w * RPW + (lane >> 4); r < NR; r += CP_WAVES * RPW) {
+      float *row = ((r & 1) ? Ks : Qs) + (r >> 1) * KS + (lane & 15) * EPL;
+      float v[EPL];
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int e = tid + u * CP_THREADS, j = e / C4, q4 = (e - j * C4) * 4, sg = q4 / DK;
-      if (e < MK_CHUNK * C4) *reinterpret_cast<float4 *>((sg == 0 ? Qs : sg == 1 ? Ks : Vs) + j * KS + (q4 - sg * DK)) = v[u];
+      for (int q = 0; q < EPL; q += 4) {
+        const float4 x4 = ld4(row + q);
+        v[q] = x4.x; v[q + 1] = x4.y; v[q + 2] = x4.z; v[q + 3] = x4.w;
+      }
+      float sq = 0.f;
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) sq = fmaf(v[q], v[q], sq);
+      const float nrm = sqrtf(row_sum16(sq) + c.l2_eps);
+#pragma unroll
+      for (int q = 0; q < EPL; q += 4)
+        *reinterpret_cast<float4 *>(row + q) = make_float4(v[q] / nrm, v[q + 1] / nrm, v[q + 2] / nrm, v[q + 3] / nrm);
     }
   }
   if (tid < 64) {  // in-chunk prefix sums of log alpha (one wave, Hillis-Steele), the decays
+    // gates of token t0 + tid: log alpha = -softplus(a), beta = sigmoid(b)
     const bool ok = tid < Cn;
-    const float2 ab = ok ? *reinterpret_cast<const float2 *>(c.gb + ((size_t)h * MK_PT + t0 + tid) * 2) : make_float2(0.f, 0.f);
-    float G = ab.x;
-    const float b = ab.y;
+    const float *pa = c.P + (size_t)(t0 + (ok ? tid : 0)) * c.NP + h * c.r_in + 4 * DK;   // a, b
+    const float pa0 = pa[0], pa1 = pa[1];
+    float G = ok ? -softplusf_(pa0) : 0.f;
+    const float b = ok ? sigmoidf_(pa1) : 0.f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_up(G, o, 64);
@@ -1476,22 +1445,20 @@ static hipError_t enqueue_layer(const MkDev *d, const MkLayerDev &L, const MkPfW
     if (sync == PF_WAIT && (e = hipStreamWaitEvent(st, ev, 0)) != hipSuccess) return e;
     const int nchunk = (T + MK_CHUNK - 1) / MK_CHUNK;
     const size_t rc = (size_t)r0 * dk;   // chunk terms: (r0 / CHUNK) chunks of CHUNK x dk
-    float *qkv = pf->qkv + (size_t)r0 * 3 * dk, *gb = pf->gb + (size_t)r0 * 2;
-    // dk == dv in {64, 128} (checked when the model is loaded).  The conv reads the ring (conv
-    // inputs of earlier positions) before the scan overwrites it with this block's last ones.
-    PfPrep pp{P, pf->NP, d->r_in, d->C, nh, L.dn_conv, L.ring, d->ctl, d->l2_eps, qkv, gb, T, r0};
-    PfChunk ck{qkv, gb, pf->cW + rc, pf->cQ + rc, pf->cU + rc, pf->cO + rc, pf->cKt + rc, pf->cg + r0, pf->cd + r0, T};
+    // dk == dv in {64, 128} (checked when the model is loaded).  The conv (in the chunk kernel)
+    // reads the ring (conv inputs of earlier positions) before the scan overwrites it with this
+    // block's last ones.
+    PfChunk ck{P, pf->NP, d->r_in, d->C, nh, L.dn_conv, L.ring, d->ctl, d->l2_eps, r0,
+               pf->cW + rc, pf->cQ + rc, pf->cU + rc, pf->cO + rc, pf->cKt + rc, pf->cg + r0, pf->cd + r0, T};
     PfScan sc{L.S, L.pend, d->ctl, pf->cW + rc, pf->cU + rc, pf->cKt + rc, pf->cg + r0, pf->cd + r0,
               pf->snap + (size_t)(r0 / MK_CHUNK) * dv * dk, T, nh, P, pf->NP, d->r_in, d->C, L.ring, r0, b.first ? 1 : 0};
     PfOut po{pf->cQ + rc, pf->cO + rc, pf->snap + (size_t)(r0 / MK_CHUNK) * dv * dk, P, pf->NP, d->r_in, L.dn_gnorm, nh,
              d->rms_eps, a1h, a1l, T};
     const dim3 gtok((T + PREP_TB - 1) / PREP_TB, nh);
     if (dk == 128) {
-      hipLaunchKernelGGL(pf_dn_prep<128>, gtok, dim3(3 * 128), 0, st, pp);
       hipLaunchKernelGGL(pf_dn_chunk_prep<128>, dim3(nh, nchunk, 2), dim3(CP_THREADS), chunk_prep_lds(128), st, ck);
       hipLaunchKernelGGL(pf_dn_scan<128>, dim3(nh, 128 / 16), dim3(SCAN_THREADS), scan_lds(128), st, sc);
     } else {
-      hipLaunchKernelGGL(pf_dn_prep<64>, gtok, dim3(3 * 64), 0, st, pp);
       hipLaunchKernelGGL(pf_dn_chunk_prep<64>, dim3(nh, nchunk), dim3(CP_THREADS), chunk_prep_lds(64), st, ck);
       hipLaunchKernelGGL(pf_dn_scan<64>, dim3(nh, 64 / 16), dim3(SCAN_THREADS), scan_lds(64), st, sc);
     }
