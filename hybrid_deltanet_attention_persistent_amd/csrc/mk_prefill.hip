@@ -1272,6 +1272,14 @@ __global__ void __launch_bounds__(PF_THREADS) pf_lm(const float *X, int row, con
         wv[q][h2] = *reinterpret_cast<const uint4 *>(embed + (size_t)min(rb + q, r1 - 1) * H + (i < H ? i : 0));
       }
   };
+  // a lane multiplies the same 16 hidden elements in every row: kept in registers
+  float hr[2][8];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int i = lane * 8 + h2 * 512;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hr[h2][e] = i < H ? hn[i + e] : 0.f;
+  }
   auto reduce = [&](const uint4 (&wv)[RBATCH][2], int rb) {
 #pragma unroll
     for (int q = 0; q < RBATCH; ++q) {
@@ -1283,8 +1291,8 @@ __global__ void __launch_bounds__(PF_THREADS) pf_lm(const float *X, int row, con
           const uint32_t ww[4] = {wv[q][h2].x, wv[q][h2].y, wv[q][h2].z, wv[q][h2].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            p = fmaf(__uint_as_float(ww[e] << 16), hn[i + 2 * e], p);
-            p = fmaf(__uint_as_float(ww[e] & 0xffff0000u), hn[i + 2 * e + 1], p);
+            p = fmaf(__uint_as_float(ww[e] << 16), hr[h2][2 * e], p);
+            p = fmaf(__uint_as_float(ww[e] & 0xffff0000u), hr[h2][2 * e + 1], p);
           }
         }
       }
